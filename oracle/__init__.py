@@ -1,0 +1,169 @@
+"""fp64 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the bench's CPU-baseline leg may import
+this package.  The HIP library and its Python binding never import, link or call it, and
+it imports nothing from them.
+
+``oracle.c`` holds the plain C reference (see the comments there for the passages each
+routine follows); this module compiles it with gcc (``-O2 -fopenmp``, no fast-math) into
+``liboracle.so`` next to it and wraps it with ctypes.  Inputs are float32 / complex64
+numpy arrays, exactly the arrays handed to the GPU; outputs are float64 / complex128.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_F32P = ctypes.POINTER(ctypes.c_float)
+_F64P = ctypes.POINTER(ctypes.c_double)
+_I64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` (gcc, -O2, OpenMP, IEEE double)."""
+    if not force and os.path.exists(_LIB_PATH) and \
+            os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path: str):
+    """Load a compiled oracle library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_wkv4_forward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P, _F64P]
+    lib.oracle_wkv4_backward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P,
+                                         _F32P, _F64P, _F64P, _F64P, _F64P]
+    lib.oracle_scan_real.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
+    lib.oracle_scan_complex.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
+    for name in ("oracle_wkv4_forward", "oracle_wkv4_backward", "oracle_scan_real",
+                 "oracle_scan_complex"):
+        getattr(lib, name).restype = None
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+def compile_variant(src_text: str, out_path: str):
+    """Compile C source text with the same flags into ``out_path`` and bind it.
+
+    Used by the tests that plant mistakes in a copy of ``oracle.c`` to show that the
+    pins catch them; the library built from ``oracle.c`` itself is never touched.
+    """
+    c_path = out_path + ".c"
+    with open(c_path, "w") as f:
+        f.write(src_text)
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", "-w", "-o", out_path, c_path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return _bind(out_path)
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (``OMP_NUM_THREADS`` or all cores)."""
+    return int(_load().oracle_num_threads())
+
+
+def _f32(x, shape=None):
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError("expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a
+
+
+def _c64f(x, shape):
+    a = np.ascontiguousarray(x, dtype=np.complex64)
+    if a.shape != tuple(shape):
+        raise ValueError("expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a.view(np.float32)
+
+
+def _p32(a):
+    return a.ctypes.data_as(_F32P)
+
+
+def _p64(a):
+    return a.ctypes.data_as(_F64P)
+
+
+def wkv4_forward(w, u, k, v, lib=None) -> np.ndarray:
+    """y (B,T,C) float64 of the WKV-4 operator (RWKV-LLM page, eq. (14))."""
+    k = _f32(k)
+    B, T, C = k.shape
+    v = _f32(v, (B, T, C))
+    w = _f32(w, (C,))
+    u = _f32(u, (C,))
+    y = np.empty((B, T, C), dtype=np.float64)
+    (lib or _load()).oracle_wkv4_forward(B, T, C, _p32(w), _p32(u), _p32(k), _p32(v), _p64(y))
+    return y
+
+
+def wkv4_backward(w, u, k, v, gy, lib=None):
+    """(gw (C,), gu (C,), gk (B,T,C), gv (B,T,C)) float64: chain rule of eq. (14)."""
+    k = _f32(k)
+    B, T, C = k.shape
+    v = _f32(v, (B, T, C))
+    gy = _f32(gy, (B, T, C))
+    w = _f32(w, (C,))
+    u = _f32(u, (C,))
+    gw = np.empty(C, dtype=np.float64)
+    gu = np.empty(C, dtype=np.float64)
+    gk = np.empty((B, T, C), dtype=np.float64)
+    gv = np.empty((B, T, C), dtype=np.float64)
+    (lib or _load()).oracle_wkv4_backward(B, T, C, _p32(w), _p32(u), _p32(k), _p32(v), _p32(gy),
+                                 _p64(gw), _p64(gu), _p64(gk), _p64(gv))
+    return gw, gu, gk, gv
+
+
+def scan_real(a, b, x0=None, lib=None) -> np.ndarray:
+    """x (B,T,C) float64 of x_t = a_t x_{t-1} + b_t, x_{-1} = x0 (or 0)."""
+    a = _f32(a)
+    B, T, C = a.shape
+    b = _f32(b, (B, T, C))
+    x0a = None if x0 is None else _f32(x0, (B, C))
+    x = np.empty((B, T, C), dtype=np.float64)
+    (lib or _load()).oracle_scan_real(B, T, C, _p32(a), _p32(b),
+                             None if x0a is None else _p32(x0a), _p64(x))
+    return x
+
+
+def scan_complex(lam, u, x0=None, lib=None) -> np.ndarray:
+    """x (B,T,C) complex128 of x_t = lam x_{t-1} + u_t, x_{-1} = x0 (or 0)."""
+    u = np.ascontiguousarray(u, dtype=np.complex64)
+    B, T, C = u.shape
+    lf = _c64f(lam, (C,))
+    uf = u.view(np.float32)
+    x0f = None if x0 is None else _c64f(x0, (B, C))
+    x = np.empty((B, T, C), dtype=np.complex128)
+    (lib or _load()).oracle_scan_complex(B, T, C, _p32(lf), _p32(uf),
+                                None if x0f is None else _p32(x0f),
+                                x.view(np.float64).ctypes.data_as(_F64P))
+    return x

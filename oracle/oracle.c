@@ -1,0 +1,219 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.  Plain, slow, fp64 CPU reference of the
+ * per-channel linear recurrences.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this; the product path never does.  It shares no code,
+ * header, constant or helper with the HIP library.
+ *
+ * Every routine reads the same float32 / complex64 arrays the GPU receives, widens
+ * them exactly to double, and evaluates the definition one channel at a time, time
+ * step by time step, in IEEE double with libm's exp (no fast-math).  Channels are
+ * independent, so OpenMP splits the (batch, channel) pairs over threads; each pair's
+ * arithmetic is the same sequence whatever the thread count, and the per-channel
+ * gradient sums over the batch are added in ascending batch order afterwards, so
+ * the results do not depend on the number of threads.
+ *
+ * Layout: (B,T,C) row-major, C fastest; per-channel vectors are (C,); complex
+ * values are interleaved (re, im) pairs.
+ *
+ * Valid range: the WKV routines rescale every channel by exp(-max_t k_t), which
+ * cancels exactly in the ratio; they need the per-channel spread of k below ~700
+ * and |u| below ~300 so that no used weight underflows double precision.
+ */
+#include <complex.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static double chan_max_k(const float *k, int64_t T, int64_t C, int64_t base)
+{
+    double m = -INFINITY;
+    for (int64_t t = 0; t < T; ++t) {
+        double kt = (double)k[base + t * C];
+        if (kt > m) m = kt;
+    }
+    return m;
+}
+
+/*
+ * WKV-4 forward.  RWKV-LLM page ("RWKV：基于RNN的LLM"), section "Time-mixing block",
+ * eq. (14): for one channel with decay w >= 0 and bonus u,
+ *
+ *   y_t = ( sum_{i<t} e^{-(t-1-i)w + k_i} v_i + e^{u+k_t} v_t )
+ *       / ( sum_{i<t} e^{-(t-1-i)w + k_i}     + e^{u+k_t}     ),
+ *
+ * with the time index starting at 0 and an empty past at t = 0 (so y_0 = v_0).
+ * The two past sums obey A_{t+1} = e^{-w} A_t + e^{k_t} v_t and
+ * B_{t+1} = e^{-w} B_t + e^{k_t} (the "two SLRU" reading in the LRU write-up's section
+ * on RWKV), which is how they are accumulated here.  All exponentials are taken
+ * relative to K = max_t k_t; the common factor e^{-K} cancels in the ratio.
+ */
+void oracle_wkv4_forward(int64_t B, int64_t T, int64_t C,
+                         const float *w, const float *u,
+                         const float *k, const float *v, double *y)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        const double K = chan_max_k(k, T, C, base);
+        const double decay = exp(-(double)w[c]);
+        const double uu = (double)u[c];
+        double A = 0.0, Bs = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t o = base + t * C;
+            const double kt = (double)k[o], vt = (double)v[o];
+            const double cur = exp(uu + kt - K);   /* e^{u+k_t}, rescaled */
+            y[o] = (A + cur * vt) / (Bs + cur);
+            const double past = exp(kt - K);       /* e^{k_t}, rescaled */
+            A = decay * A + past * vt;
+            Bs = decay * Bs + past;
+        }
+    }
+}
+
+/*
+ * WKV-4 backward: gradients of a scalar loss L with upstream dL/dy = gy, w.r.t. the
+ * w and u of eq. (14) as printed (summed over batch and time, since both are
+ * per-channel vectors in that section) and w.r.t. every k_t and v_t.  The pages give
+ * no backward; this is the chain rule applied to eq. (14).  With
+ *   eps = e^{-w}, alpha_i = e^{k_i}, beta_t = e^{u+k_t},
+ *   A_t = sum_{i<t} eps^{t-1-i} alpha_i v_i,   B_t = sum_{i<t} eps^{t-1-i} alpha_i,
+ *   A'_t = sum_{i<t} (t-1-i) eps^{t-1-i} alpha_i v_i,  B'_t likewise without v,
+ *   D_t = B_t + beta_t,  y_t = (A_t + beta_t v_t) / D_t,
+ *   G_s = sum_{t>s} eps^{t-1-s} gy_t / D_t,   H_s = sum_{t>s} eps^{t-1-s} gy_t y_t / D_t:
+ *
+ *   dL/du   = sum_t gy_t beta_t (v_t - y_t) / D_t
+ *   dL/dw   = - sum_t gy_t (A'_t - y_t B'_t) / D_t
+ *   dL/dv_s = gy_s beta_s / D_s + alpha_s G_s
+ *   dL/dk_s = gy_s beta_s (v_s - y_s) / D_s + alpha_s (v_s G_s - H_s)
+ *
+ * A' and B' follow A'_{t+1} = eps (A'_t + A_t); G and H run backwards with
+ * G_{s-1} = gy_s / D_s + eps G_s from G_{T-1} = 0.
+ * gw and gu are (C,); gk and gv are (B,T,C).
+ */
+void oracle_wkv4_backward(int64_t B, int64_t T, int64_t C,
+                          const float *w, const float *u,
+                          const float *k, const float *v, const float *gy,
+                          double *gw, double *gu, double *gk, double *gv)
+{
+    double *gw_bc = (double *)calloc((size_t)(B * C), sizeof(double));
+    double *gu_bc = (double *)calloc((size_t)(B * C), sizeof(double));
+#pragma omp parallel
+    {
+        double *D = (double *)malloc((size_t)T * sizeof(double));
+        double *Y = (double *)malloc((size_t)T * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t bc = 0; bc < B * C; ++bc) {
+            const int64_t b = bc / C, c = bc % C;
+            const int64_t base = b * T * C + c;
+            const double K = chan_max_k(k, T, C, base);
+            const double eps = exp(-(double)w[c]);
+            const double uu = (double)u[c];
+            double A = 0.0, Bs = 0.0, Ad = 0.0, Bd = 0.0, sgw = 0.0, sgu = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t o = base + t * C;
+                const double kt = (double)k[o], vt = (double)v[o], g = (double)gy[o];
+                const double beta = exp(uu + kt - K);
+                const double alpha = exp(kt - K);
+                const double Dt = Bs + beta;
+                const double yt = (A + beta * vt) / Dt;
+                D[t] = Dt;
+                Y[t] = yt;
+                sgu += g * beta * (vt - yt) / Dt;
+                sgw -= g * (Ad - yt * Bd) / Dt;
+                Ad = eps * (Ad + A);
+                Bd = eps * (Bd + Bs);
+                A = eps * A + alpha * vt;
+                Bs = eps * Bs + alpha;
+            }
+            gw_bc[bc] = sgw;
+            gu_bc[bc] = sgu;
+            double G = 0.0, H = 0.0; /* G_{T-1} = H_{T-1} = 0 */
+            for (int64_t s = T - 1; s >= 0; --s) {
+                const int64_t o = base + s * C;
+                const double ks = (double)k[o], vs = (double)v[o], g = (double)gy[o];
+                const double beta = exp(uu + ks - K);
+                const double alpha = exp(ks - K);
+                const double q = g / D[s];
+                gv[o] = q * beta + alpha * G;
+                gk[o] = q * beta * (vs - Y[s]) + alpha * (vs * G - H);
+                G = q + eps * G;      /* becomes G_{s-1} */
+                H = q * Y[s] + eps * H;
+            }
+        }
+        free(D);
+        free(Y);
+    }
+    for (int64_t c = 0; c < C; ++c) {
+        double sw = 0.0, su = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            sw += gw_bc[b * C + c];
+            su += gu_bc[b * C + c];
+        }
+        gw[c] = sw;
+        gu[c] = su;
+    }
+    free(gw_bc);
+    free(gu_bc);
+}
+
+/*
+ * Real diagonal scan x_t = a_t x_{t-1} + b_t, the scan form the minGRU page gives as
+ * the target of a parallel scan ("Were RNNs All We Needed?" news page, minGRU
+ * section: v_t = a_t (.) v_{t-1} + b_t).  x_{-1} = x0[b,c], or 0 when x0 is NULL.
+ */
+void oracle_scan_real(int64_t B, int64_t T, int64_t C,
+                      const float *a, const float *bb, const float *x0, double *x)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        double s = x0 ? (double)x0[b * C + c] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t o = base + t * C;
+            s = (double)a[o] * s + (double)bb[o];
+            x[o] = s;
+        }
+    }
+}
+
+/*
+ * Complex diagonal scan x_t = lambda x_{t-1} + u_t, the LRU write-up's element-wise
+ * complex recurrence (section on the diagonal linear RNN, eq. lr-xx), in complex128.
+ * lambda is (C,) complex64, u is (B,T,C) complex64, x0 is (B,C) complex64 or NULL
+ * (zero, which gives x_0 = u_0 as in the write-up's unrolled form, eq. lr-e).
+ * x is (B,T,C) complex128, interleaved.
+ */
+void oracle_scan_complex(int64_t B, int64_t T, int64_t C,
+                         const float *lam, const float *u, const float *x0, double *x)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        const double complex L = (double)lam[2 * c] + (double)lam[2 * c + 1] * I;
+        double complex s = 0.0;
+        if (x0) s = (double)x0[2 * (b * C + c)] + (double)x0[2 * (b * C + c) + 1] * I;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t o = base + t * C;
+            const double complex ut = (double)u[2 * o] + (double)u[2 * o + 1] * I;
+            s = L * s + ut;
+            x[2 * o] = creal(s);
+            x[2 * o + 1] = cimag(s);
+        }
+    }
+}

@@ -1,0 +1,140 @@
+"""O(T^2) brute-force evaluations of the defining sums, used only to pin the oracle.
+
+These are written directly from the printed sums, not from the recurrences the oracle
+uses, so a mistake in the oracle's recurrence (a dropped term, an off-by-one decay
+exponent, a swapped operand) shows up as a mismatch.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def wkv4_sums(w, u, k, v):
+    """RWKV-LLM page, eq. (14), evaluated term by term for every (b, t, c).
+
+    y_t = (sum_{i<t} e^{-(t-1-i)w+k_i} v_i + e^{u+k_t} v_t)
+        / (sum_{i<t} e^{-(t-1-i)w+k_i}     + e^{u+k_t}).
+    No rescaling: meant for tiny inputs with |k| well below 700.
+    """
+    w = np.asarray(w, np.float64)
+    u = np.asarray(u, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, T, C = k.shape
+    y = np.empty((B, T, C))
+    for b in range(B):
+        for c in range(C):
+            for t in range(T):
+                num = 0.0
+                den = 0.0
+                for i in range(t):
+                    e = np.exp(-(t - 1 - i) * w[c] + k[b, i, c])
+                    num += e * v[b, i, c]
+                    den += e
+                cur = np.exp(u[c] + k[b, t, c])
+                y[b, t, c] = (num + cur * v[b, t, c]) / (den + cur)
+    return y
+
+
+def aft_decay(w, k, v):
+    """RWKV-LLM page, eqs. (9)-(10): AFT with w_{t,i} = -(t-i) w, sums over i <= t."""
+    w = np.asarray(w, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, T, C = k.shape
+    y = np.empty((B, T, C))
+    for t in range(T):
+        i = np.arange(t + 1)
+        e = np.exp(-(t - i)[None, :, None] * w[None, None, :] + k[:, : t + 1, :])
+        y[:, t, :] = (e * v[:, : t + 1, :]).sum(1) / e.sum(1)
+    return y
+
+
+def wkv4_two_slru(w, u, k, v):
+    """LRU write-up, section on RWKV: the ratio of two SLRU recurrences,
+
+    x_t = (y_t + (g*lam - 1) e^{k_t} v_t) / (z_t + (g*lam - 1) e^{k_t}),
+    y_t = lam y_{t-1} + e^{k_t} v_t,   z_t = lam z_{t-1} + e^{k_t},
+
+    with lam = e^{-w} and g = e^{u} (the sigma(r) gate left out).
+    """
+    w = np.asarray(w, np.float64)
+    u = np.asarray(u, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, T, C = k.shape
+    lam = np.exp(-w)
+    g = np.exp(u)
+    ys = np.zeros((B, C))
+    zs = np.zeros((B, C))
+    out = np.empty((B, T, C))
+    for t in range(T):
+        ek = np.exp(k[:, t, :])
+        ys = lam * ys + ek * v[:, t, :]
+        zs = lam * zs + ek
+        out[:, t, :] = (ys + (g * lam - 1.0) * ek * v[:, t, :]) / (zs + (g * lam - 1.0) * ek)
+    return out
+
+
+def wkv4_torch(w, u, k, v):
+    """Eq. (14) as a dense masked T x T weighting in torch float64 (for autograd).
+
+    w, u: (C,), k, v: (B,T,C) torch float64 tensors.
+    """
+    import torch
+
+    B, T, C = k.shape
+    t = torch.arange(T, dtype=torch.float64)
+    dist = (t[:, None] - 1.0 - t[None, :])  # (t, i) -> t-1-i
+    mask = (t[None, :] < t[:, None])  # i < t
+    # expo[b, c, t, i] = -(t-1-i) w_c + k_{b,i,c}
+    kk = k.permute(0, 2, 1)  # (B,C,T)
+    vv = v.permute(0, 2, 1)
+    expo = -dist[None, None] * w[None, :, None, None] + kk[:, :, None, :]
+    expo = torch.where(mask[None, None], expo, torch.full_like(expo, -torch.inf))
+    E = torch.exp(expo)
+    cur = torch.exp(u[None, :, None] + kk)
+    num = (E * vv[:, :, None, :]).sum(-1) + cur * vv
+    den = E.sum(-1) + cur
+    return (num / den).permute(0, 2, 1)
+
+
+def scan_real_sums(a, b, x0=None):
+    """x_t = sum_{k<=t} (prod_{j=k+1}^{t} a_j) b_k + (prod_{j=0}^{t} a_j) x0, term by term."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    B, T, C = a.shape
+    x0 = np.zeros((B, C)) if x0 is None else np.asarray(x0, np.float64)
+    x = np.empty((B, T, C))
+    for t in range(T):
+        acc = np.prod(a[:, : t + 1, :], axis=1) * x0
+        for kk in range(t + 1):
+            acc = acc + np.prod(a[:, kk + 1: t + 1, :], axis=1) * b[:, kk, :]
+        x[:, t, :] = acc
+    return x
+
+
+def scan_complex_sums(lam, u, x0=None):
+    """LRU write-up, eq. lr-xx unrolled: x_t = sum_{k<=t} lam^{t-k} u_k (+ lam^{t+1} x0)."""
+    lam = np.asarray(lam, np.complex128)
+    u = np.asarray(u, np.complex128)
+    B, T, C = u.shape
+    x0 = np.zeros((B, C), np.complex128) if x0 is None else np.asarray(x0, np.complex128)
+    x = np.empty((B, T, C), np.complex128)
+    for t in range(T):
+        pw = lam[None, None, :] ** (t - np.arange(t + 1))[None, :, None]
+        x[:, t, :] = (pw * u[:, : t + 1, :]).sum(1) + lam ** (t + 1) * x0
+    return x
+
+
+def scan_complex_cumsum(lam, u):
+    """LRU write-up, parallelisation section: x_t = lam^t * cumsum_k(lam^{-k} u_k).
+
+    Exact in real arithmetic; only usable for short sequences (lam^{-k} grows).
+    """
+    lam = np.asarray(lam, np.complex128)
+    u = np.asarray(u, np.complex128)
+    T = u.shape[1]
+    t = np.arange(T)[None, :, None]
+    return lam ** t * np.cumsum(lam ** (-t) * u, axis=1)
