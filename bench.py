@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Throughput of the WKV-4 forward hot path on one MI355X.
+
+One step = one ``wkv4_forward`` call (the whole operator: every kernel it launches) over
+the B=8, T=1024, C=768 float32 workload (169m-style width), synthetic seeded inputs
+already resident in HBM.  Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+Input/output buffer sets are rotated so that the 256 MB last-level cache (MALL) cannot
+serve a repeated call: R = ceil(2 * 256 MB / footprint) sets.
+
+``--all`` also measures the other workloads (WKV-4 forward+backward at B=8 T=4096 C=2560,
+minGRU real scan at B=64 T=4096 C=256, LRU complex scan at B=1 T=262144 C=1024) and writes
+their lines to ``--all-out`` (they are parity workloads, not the headline line).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "WKV elements/s + achieved HBM GB/s (% peak), B=8 T=1024 C=768 fp32"
+PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+MALL_BYTES = 256 * 1024 * 1024  # MI355X Infinity Cache
+# Algorithmic bytes per element: inputs read once, outputs written once.
+BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "scan_complex": 16}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources: counter figures taken from an older build do not apply."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_recurrence_rnn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str, launches_per_step: int = 1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches
+    the current kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Row:
+    """Pre-marshalled launches of one entry point over R rotated buffer sets."""
+
+    def __init__(self, lib, kind, B, T, C, host, rotations):
+        import torch
+
+        self.kind, self.B, self.T, self.C = kind, B, T, C
+        self.elements = B * T * C
+        dev = torch.device("cuda")
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.keep = []
+        self.calls = []
+        to = lambda x: torch.from_numpy(x).to(dev)  # noqa: E731
+        if kind == "wkv4_forward":
+            w, u = to(host["w"]), to(host["u"])
+            nws = int(lib.wkv4_forward_workspace_size(B, T, C))
+            for _ in range(rotations):
+                k, v = to(host["k"]), to(host["v"])
+                y = torch.empty_like(k)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [k, v, y, ws]
+                self.calls.append((lib.wkv4_forward, (B, T, C, w.data_ptr(), u.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), y.data_ptr(), ws.data_ptr(), nws, stream)))
+            self.keep += [w, u]
+        elif kind == "wkv4_backward":
+            w, u = to(host["w"]), to(host["u"])
+            nws = int(lib.wkv4_backward_workspace_size(B, T, C))
+            for _ in range(rotations):
+                k, v, gy = to(host["k"]), to(host["v"]), to(host["gy"])
+                gk, gv = torch.empty_like(k), torch.empty_like(k)
+                gw = torch.empty(C, dtype=torch.float32, device=dev)
+                gu = torch.empty(C, dtype=torch.float32, device=dev)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [k, v, gy, gk, gv, gw, gu, ws]
+                self.calls.append((lib.wkv4_backward, (B, T, C, w.data_ptr(), u.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), gy.data_ptr(), gw.data_ptr(), gu.data_ptr(),
+                                   gk.data_ptr(), gv.data_ptr(), ws.data_ptr(), nws, stream)))
+            self.keep += [w, u]
+        elif kind == "scan_real":
+            nws = int(lib.linrec_scan_workspace_size(B, T, C, 0))
+            for _ in range(rotations):
+                a, b = to(host["a"]), to(host["b"])
+                x = torch.empty_like(a)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [a, b, x, ws]
+                self.calls.append((lib.linrec_scan_real, (B, T, C, a.data_ptr(), b.data_ptr(), None,
+                                   x.data_ptr(), ws.data_ptr(), nws, stream)))
+        elif kind == "scan_complex":
+            lam = to(host["lam"])
+            nws = int(lib.linrec_scan_workspace_size(B, T, C, 1))
+            for _ in range(rotations):
+                u = to(host["u"])
+                x = torch.empty_like(u)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [u, x, ws]
+                self.calls.append((lib.linrec_scan_complex, (B, T, C, lam.data_ptr(), u.data_ptr(), None,
+                                   x.data_ptr(), ws.data_ptr(), nws, stream)))
+            self.keep.append(lam)
+        else:
+            raise KeyError(kind)
+
+    def launch(self, i):
+        fn, args = self.calls[i % len(self.calls)]
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError("%s returned status %d" % (self.kind, st))
+
+    def run(self, steps, warmup):
+        import torch
+
+        for i in range(warmup):
+            self.launch(i)
+        stream = torch.cuda.current_stream()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            self.launch(warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, ev0.elapsed_time(ev1) / 1e3
+
+
+def rotations_for(footprint_bytes: int) -> int:
+    return max(1, math.ceil(2 * MALL_BYTES / footprint_bytes))
+
+
+def roofline(kind, elements, launch_s, traffic):
+    algo = BYTES_PER_ELEM[kind] * elements
+    achieved = algo / launch_s / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+            "algorithmic_bytes": algo}
+
+
+def cpu_baseline(kind, host, budget_s):
+    """The fp64 oracle, as it stands, on the host cores: median seconds per call."""
+    import oracle
+
+    fn = {"wkv4_forward": lambda: oracle.wkv4_forward(host["w"], host["u"], host["k"], host["v"]),
+          "wkv4_backward": lambda: oracle.wkv4_backward(host["w"], host["u"], host["k"], host["v"],
+                                                        host["gy"]),
+          "scan_real": lambda: oracle.scan_real(host["a"], host["b"]),
+          "scan_complex": lambda: oracle.scan_complex(host["lam"], host["u"])}[kind]
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s or len(times) >= 25:
+            break
+    return statistics.median(times), len(times), oracle.num_threads()
+
+
+def copy_probe():
+    """Device-to-device copy of 1 GiB: attainable-bandwidth sanity figure (read + write)."""
+    import torch
+
+    n = 1 << 28
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    reps = 20
+    for _ in range(reps):
+        b.copy_(a)
+    ev1.record()
+    torch.cuda.synchronize()
+    s = ev0.elapsed_time(ev1) / 1e3 / reps
+    del a, b
+    return round(2 * 4 * n / s / 1e9, 1)
+
+
+def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=None):
+    from linear_recurrence_rnn_amd import workloads
+
+    wl = workloads.WORKLOADS[wid]
+    B, T, C = shape or (wl.B, wl.T, wl.C)
+    host = workloads.make_inputs(wid, shape=(B, T, C))
+    elements = B * T * C
+    footprint = BYTES_PER_ELEM[kind] * elements
+    R = rotations_for(footprint)
+    log("[bench] %s %s: B=%d T=%d C=%d, %d buffer set(s) of %.1f MB" % (
+        kind, wl.label, B, T, C, R, footprint / 1e6))
+    row = Row(lib, kind, B, T, C, host, R)
+    wall, ev_s = row.run(steps, warmup)
+    per_step = wall / steps
+    per_launch = ev_s / steps
+    out = {
+        "kind": kind, "workload": wl.label, "B": B, "T": T, "C": C, "rotations": R,
+        "ms_per_step": round(per_step * 1e3, 5), "event_ms_per_step": round(per_launch * 1e3, 5),
+        "elements_per_s": elements / per_step,
+        "roofline": roofline(kind, elements, per_launch, counter_traffic(kind)),
+    }
+    del row
+    if cpu_budget > 0:
+        sample = host
+        desc = "full workload"
+        if cpu_slice is not None:
+            Ts = cpu_slice
+            sample = {k: (v[:, :Ts] if hasattr(v, "ndim") and v.ndim == 3 else v) for k, v in host.items()}
+            desc = "first %d of %d time steps, all batch rows and channels" % (Ts, T)
+        med, reps, cores = cpu_baseline(kind, sample, cpu_budget)
+        n_el = B * (cpu_slice or T) * C
+        out["cpu_baseline"] = {"value": n_el / med, "unit": "elements/s", "cores": cores, "kind": "oracle",
+                               "sample": "%s (%d elements), median of %d run(s)" % (desc, n_el, reps)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="wall-clock budget of the oracle CPU baseline (0 skips it)")
+    ap.add_argument("--no-copy-probe", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also measure the other workloads")
+    ap.add_argument("--all-out", default=os.path.join(ROOT, "gpurun_out", "bench_all.json"))
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log("bench.py measures one GPU only: every box here has a single MI355X and this path "
+            "has no multi-GPU mode (--gpus %d requested)." % args.gpus)
+        sys.exit(2)
+
+    import torch
+
+    from linear_recurrence_rnn_amd import binding
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a ROCm GPU")
+        sys.exit(1)
+    lib = binding.load()
+    res = measure(lib, 2, "wkv4_forward", args.steps, args.warmup, args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": res["elements_per_s"],
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded: k,v~N(0,1), u~N(0,0.5), w=exp(U(-3,1)))",
+        "config": {"workload": "wkv4_forward B=8 T=1024 C=768 (169m-style width)", "B": 8, "T": 1024,
+                   "C": 768, "buffer_sets": res["rotations"]},
+        "hbm_GBps": res["roofline"]["achieved"],
+        "pct_peak_hbm": round(100 * res["roofline"]["frac"], 2),
+        "roofline": res["roofline"],
+    }
+    if "cpu_baseline" in res:
+        line["cpu_baseline"] = res["cpu_baseline"]
+    if not args.no_copy_probe:
+        line["copy_probe_GBps"] = copy_probe()
+    print(json.dumps(line), flush=True)
+
+    if args.all:
+        rows = [res]
+        for wid, kind, steps, cpu_slice in ((3, "wkv4_forward", 20, 512), (3, "wkv4_backward", 20, 256),
+                                            (4, "scan_real", 20, 512), (5, "scan_complex", 10, 16384)):
+            rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
+            log("[bench] " + json.dumps(rows[-1]))
+        os.makedirs(os.path.dirname(args.all_out), exist_ok=True)
+        with open(args.all_out, "w") as f:
+            json.dump(rows, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+/*
+ * linrec.h -- C ABI of the MI355X (gfx950) per-channel linear-recurrence library.
+ *
+ * Four operations, all over activations laid out (B, T, C) row-major with the channel
+ * index fastest (batch B, sequence length T, channels C: the layout the RWKV-LLM page
+ * "RWKV：基于RNN的LLM" uses in its section on parallel training):
+ *
+ *   wkv4_forward / wkv4_backward  the RWKV-4 time-mix operator of eq. (14) on that page
+ *   linrec_scan_real              x_t = a_t * x_{t-1} + b_t (the scan form on the
+ *                                 "Were RNNs All We Needed?" news page, minGRU section)
+ *   linrec_scan_complex           x_t = lambda * x_{t-1} + u_t (the LRU write-up on
+ *                                 "Resurrecting Recurrent Neural Networks for Long
+ *                                 Sequences", diagonal complex recurrence, eq. lr-xx)
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers (hipMalloc / torch CUDA-on-ROCm memory) unless a
+ *    comment says otherwise; the caller owns every buffer for the whole call.  Outputs
+ *    must not alias inputs or each other.
+ *  - Calls are asynchronous: they validate arguments on the host, then enqueue kernels on
+ *    `stream` (a hipStream_t; NULL means the default stream) and return.  The library never
+ *    synchronises, allocates or frees device memory; scratch memory comes from the
+ *    caller's `workspace` of at least the size the matching *_workspace_size query returns
+ *    for the same (B, T, C).  A size of 0 needs no workspace (NULL is then allowed).
+ *  - Return value: LINREC_OK or an error status.  Argument checks run before any HIP call:
+ *      B, T or C negative, or B*T*C*element size overflowing int64
+ *                                                         -> LINREC_ERR_INVALID_ARG
+ *      any of B, T, C equal to 0                          -> LINREC_OK, nothing enqueued and
+ *        no pointer read (wkv4_backward still zero-fills gw and gu when C > 0)
+ *      a required pointer NULL (for a non-empty shape)    -> LINREC_ERR_INVALID_ARG
+ *      ws_bytes below the workspace size                  -> LINREC_ERR_WORKSPACE
+ *      a pointer not aligned to its element size (4 B for float, 8 B for complex64)
+ *        or a workspace not aligned to 16 B               -> LINREC_ERR_UNSUPPORTED
+ *      a failed kernel launch                             -> LINREC_ERR_HIP
+ *    linrec_last_error() then holds a readable message (per thread).  Faults that happen
+ *    while kernels run surface on the stream, as for any HIP work.
+ *  - Input values are not inspected (that would need a device read): non-finite inputs
+ *    propagate to the outputs.
+ *  - Arithmetic is float32 (complex64 as float32 pairs); results match an fp64 evaluation
+ *    of the same definition to a relative error of about 1e-5 of the per-sequence RMS.
+ */
+#ifndef LINREC_H
+#define LINREC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LINREC_ABI_VERSION 1
+
+typedef enum {
+    LINREC_OK = 0,
+    LINREC_ERR_INVALID_ARG = 1,
+    LINREC_ERR_WORKSPACE = 2,
+    LINREC_ERR_UNSUPPORTED = 3,
+    LINREC_ERR_HIP = 4
+} linrec_status;
+
+/* Version of this ABI (LINREC_ABI_VERSION of the library that was built). */
+int linrec_abi_version(void);
+
+/* Static name of a status code ("LINREC_OK", ...); "unknown status" otherwise. */
+const char *linrec_status_string(int status);
+
+/* Detail of the last failing call on the calling thread ("" if none).  The pointer stays
+ * valid until the next library call on the same thread. */
+const char *linrec_last_error(void);
+
+/* Bytes of device workspace each operation needs for a given shape (0 when none).  Pure
+ * host functions of (B, T, C); they make no HIP call.  Negative sizes return 0. */
+size_t wkv4_forward_workspace_size(int64_t B, int64_t T, int64_t C);
+size_t wkv4_backward_workspace_size(int64_t B, int64_t T, int64_t C);
+size_t linrec_scan_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex);
+
+/*
+ * WKV-4 forward, RWKV-LLM page, section "Time-mixing block", eq. (14).  For each batch
+ * row b and channel c, with time starting at 0 and an empty past at t = 0:
+ *
+ *   y[b,t,c] = ( sum_{i<t} e^{-(t-1-i) w[c] + k[b,i,c]} v[b,i,c] + e^{u[c]+k[b,t,c]} v[b,t,c] )
+ *            / ( sum_{i<t} e^{-(t-1-i) w[c] + k[b,i,c]}          + e^{u[c]+k[b,t,c]} )
+ *
+ *   w  (C)      float32, per-channel decay, finite and >= 0 (eq. (10)'s requirement)
+ *   u  (C)      float32, per-channel bonus for the current token
+ *   k, v (B,T,C) float32 inputs;  y (B,T,C) float32 output
+ *
+ * Evaluated with a running maximum of the exponents, so no e^{k} is ever formed:
+ * k of any magnitude that keeps the sums meaningful in float32 is fine.
+ */
+int wkv4_forward(int64_t B, int64_t T, int64_t C,
+                 const float *w, const float *u, const float *k, const float *v,
+                 float *y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * WKV-4 backward: given the upstream gradient gy = dL/dy of eq. (14)'s output, writes
+ *
+ *   gw (C), gu (C)     dL/dw and dL/du, summed over batch and time (w and u are
+ *                      per-channel vectors in eq. (14)); w as it appears in eq. (14),
+ *                      not a log-parametrisation
+ *   gk, gv (B,T,C)     dL/dk and dL/dv
+ *
+ * The pages give no backward pass; these are the chain-rule derivatives of eq. (14).
+ * All four outputs are overwritten (not accumulated).  Deterministic: the batch
+ * reduction of gw and gu runs in a fixed order.
+ */
+int wkv4_backward(int64_t B, int64_t T, int64_t C,
+                  const float *w, const float *u, const float *k, const float *v,
+                  const float *gy, float *gw, float *gu, float *gk, float *gv,
+                  void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Real diagonal scan, "Were RNNs All We Needed?" page, minGRU section (v_t = a_t (.)
+ * v_{t-1} + b_t):  x[b,t,c] = a[b,t,c] * x[b,t-1,c] + b[b,t,c],  x[b,-1,c] = x0[b,c].
+ *
+ *   a, b (B,T,C) float32;  x0 (B,C) float32 or NULL for a zero initial state;
+ *   x (B,T,C) float32 output.  minGRU's h_t = (1-z_t) h_{t-1} + z_t h~_t is a = 1-z,
+ *   b = z * h~.
+ */
+int linrec_scan_real(int64_t B, int64_t T, int64_t C,
+                     const float *a, const float *b, const float *x0, float *x,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Complex diagonal scan, LRU write-up, section on the diagonal complex recurrence
+ * (eq. lr-xx):  x[b,t,c] = lambda[c] * x[b,t-1,c] + u[b,t,c],  x[b,-1,c] = x0[b,c].
+ *
+ *   lambda (C) complex64 as interleaved (re, im) float pairs, |lambda| <= 1 expected
+ *   u (B,T,C) complex64;  x0 (B,C) complex64 or NULL for zero (then x_0 = u_0, as in the
+ *   write-up's unrolled form eq. lr-e);  x (B,T,C) complex64 output.
+ *
+ * Chunk multipliers lambda^n are formed in float64 from the given complex64 lambda.
+ */
+int linrec_scan_complex(int64_t B, int64_t T, int64_t C,
+                        const float *lambda, const float *u, const float *x0, float *x,
+                        void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINREC_H */

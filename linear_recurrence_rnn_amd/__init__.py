@@ -1,0 +1,17 @@
+"""MI355X (gfx950) per-channel linear recurrences: RWKV-4 WKV forward/backward and
+real/complex diagonal scans, as hand-written HIP kernels behind a C ABI
+(``include/linrec.h``).  The Python functions here marshal torch tensors to that ABI.
+
+The binding is imported lazily so that ``linear_recurrence_rnn_amd.workloads`` (the seeded
+input generators) can be used without loading the GPU library.
+"""
+
+__all__ = ["wkv4_forward", "wkv4_backward", "scan_real", "scan_complex", "workspace_size",
+           "LinrecError"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,202 @@
+"""Thin ctypes binding of ``liblinrec.so`` (the C ABI in ``include/linrec.h``).
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  There is no fallback:
+if the library is missing or a call fails, a ``LinrecError`` is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # imported before the library so both share torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinrec.so")
+
+LINREC_OK = 0
+LINREC_ERR_INVALID_ARG = 1
+LINREC_ERR_WORKSPACE = 2
+LINREC_ERR_UNSUPPORTED = 3
+LINREC_ERR_HIP = 4
+
+_I64 = ctypes.c_int64
+_VP = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_lock = threading.Lock()
+_lib = None
+
+
+class LinrecError(RuntimeError):
+    """A library call returned an error status."""
+
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (func, status_string(status), detail))
+
+
+def load(path: str | None = None):
+    """Load the library once (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise LinrecError(-1, "load", "%s is missing; build it with "
+                              "`python -m linear_recurrence_rnn_amd.build`" % p)
+        lib = ctypes.CDLL(p)
+        lib.linrec_abi_version.restype = ctypes.c_int
+        lib.linrec_status_string.restype = ctypes.c_char_p
+        lib.linrec_status_string.argtypes = [ctypes.c_int]
+        lib.linrec_last_error.restype = ctypes.c_char_p
+        for name in ("wkv4_forward_workspace_size", "wkv4_backward_workspace_size"):
+            getattr(lib, name).restype = _SZ
+            getattr(lib, name).argtypes = [_I64, _I64, _I64]
+        lib.linrec_scan_workspace_size.restype = _SZ
+        lib.linrec_scan_workspace_size.argtypes = [_I64, _I64, _I64, ctypes.c_int]
+        lib.wkv4_forward.restype = ctypes.c_int
+        lib.wkv4_forward.argtypes = [_I64, _I64, _I64] + [_VP] * 5 + [_VP, _SZ, _VP]
+        lib.wkv4_backward.restype = ctypes.c_int
+        lib.wkv4_backward.argtypes = [_I64, _I64, _I64] + [_VP] * 9 + [_VP, _SZ, _VP]
+        lib.linrec_scan_real.restype = ctypes.c_int
+        lib.linrec_scan_real.argtypes = [_I64, _I64, _I64] + [_VP] * 4 + [_VP, _SZ, _VP]
+        lib.linrec_scan_complex.restype = ctypes.c_int
+        lib.linrec_scan_complex.argtypes = [_I64, _I64, _I64] + [_VP] * 4 + [_VP, _SZ, _VP]
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().linrec_status_string(status).decode()
+    except Exception:  # library not loadable: still describe the code
+        return str(status)
+
+
+def _check(status: int, func: str) -> None:
+    if status != LINREC_OK:
+        raise LinrecError(status, func, load().linrec_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _expect(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small: %d < %d bytes" % (
+                workspace.numel() * workspace.element_size(), nbytes))
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def workspace_size(op: str, B: int, T: int, C: int) -> int:
+    """Bytes of workspace ``op`` needs ('wkv4_forward', 'wkv4_backward', 'scan_real', 'scan_complex')."""
+    lib = load()
+    if op == "wkv4_forward":
+        return int(lib.wkv4_forward_workspace_size(B, T, C))
+    if op == "wkv4_backward":
+        return int(lib.wkv4_backward_workspace_size(B, T, C))
+    if op == "scan_real":
+        return int(lib.linrec_scan_workspace_size(B, T, C, 0))
+    if op == "scan_complex":
+        return int(lib.linrec_scan_workspace_size(B, T, C, 1))
+    raise KeyError(op)
+
+
+def wkv4_forward(w, u, k, v, out=None, workspace=None):
+    """y = WKV-4(w, u, k, v): k, v (B,T,C) float32 on a ROCm device, w, u (C,)."""
+    lib = load()
+    B, T, C = k.shape
+    dev = k.device
+    _expect(k, "k", torch.float32, (B, T, C), dev)
+    _expect(v, "v", torch.float32, (B, T, C), dev)
+    _expect(w, "w", torch.float32, (C,), dev)
+    _expect(u, "u", torch.float32, (C,), dev)
+    y = torch.empty_like(k) if out is None else out
+    _expect(y, "out", torch.float32, (B, T, C), dev)
+    ws, nws = _workspace(int(lib.wkv4_forward_workspace_size(B, T, C)), dev, workspace)
+    _check(lib.wkv4_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(ws), nws,
+                            _stream(dev)), "wkv4_forward")
+    return y
+
+
+def wkv4_backward(w, u, k, v, gy, out=None, workspace=None):
+    """(gw, gu, gk, gv) = gradients of sum(gy * WKV-4(w, u, k, v))."""
+    lib = load()
+    B, T, C = k.shape
+    dev = k.device
+    for name, t in (("k", k), ("v", v), ("gy", gy)):
+        _expect(t, name, torch.float32, (B, T, C), dev)
+    _expect(w, "w", torch.float32, (C,), dev)
+    _expect(u, "u", torch.float32, (C,), dev)
+    if out is None:
+        gw = torch.empty(C, dtype=torch.float32, device=dev)
+        gu = torch.empty(C, dtype=torch.float32, device=dev)
+        gk = torch.empty_like(k)
+        gv = torch.empty_like(k)
+    else:
+        gw, gu, gk, gv = out
+    ws, nws = _workspace(int(lib.wkv4_backward_workspace_size(B, T, C)), dev, workspace)
+    _check(lib.wkv4_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy), _ptr(gw),
+                             _ptr(gu), _ptr(gk), _ptr(gv), _ptr(ws), nws, _stream(dev)),
+           "wkv4_backward")
+    return gw, gu, gk, gv
+
+
+def scan_real(a, b, x0=None, out=None, workspace=None):
+    """x_t = a_t * x_{t-1} + b_t over (B,T,C) float32; x0 (B,C) or None for zero."""
+    lib = load()
+    B, T, C = a.shape
+    dev = a.device
+    _expect(a, "a", torch.float32, (B, T, C), dev)
+    _expect(b, "b", torch.float32, (B, T, C), dev)
+    if x0 is not None:
+        _expect(x0, "x0", torch.float32, (B, C), dev)
+    x = torch.empty_like(a) if out is None else out
+    _expect(x, "out", torch.float32, (B, T, C), dev)
+    ws, nws = _workspace(int(lib.linrec_scan_workspace_size(B, T, C, 0)), dev, workspace)
+    _check(lib.linrec_scan_real(B, T, C, _ptr(a), _ptr(b), _ptr(x0), _ptr(x), _ptr(ws), nws,
+                                _stream(dev)), "linrec_scan_real")
+    return x
+
+
+def scan_complex(lam, u, x0=None, out=None, workspace=None):
+    """x_t = lam * x_{t-1} + u_t over (B,T,C) complex64; lam (C,), x0 (B,C) or None."""
+    lib = load()
+    B, T, C = u.shape
+    dev = u.device
+    _expect(u, "u", torch.complex64, (B, T, C), dev)
+    _expect(lam, "lam", torch.complex64, (C,), dev)
+    if x0 is not None:
+        _expect(x0, "x0", torch.complex64, (B, C), dev)
+    x = torch.empty_like(u) if out is None else out
+    _expect(x, "out", torch.complex64, (B, T, C), dev)
+    ws, nws = _workspace(int(lib.linrec_scan_workspace_size(B, T, C, 1)), dev, workspace)
+    _check(lib.linrec_scan_complex(B, T, C, _ptr(lam), _ptr(u), _ptr(x0), _ptr(x), _ptr(ws), nws,
+                                   _stream(dev)), "linrec_scan_complex")
+    return x

@@ -1,0 +1,300 @@
+// scan_ops.hpp -- the three first-order recurrences as operators of the chunked scan.
+//
+// Each operator supplies, for one channel:
+//   Chan     per-channel constants,
+//   In       one time step's inputs (loaded with channel-contiguous vector loads),
+//   Agg      the state after a span of steps, and the span's effect on an incoming state,
+//   reduce   the aggregate of a chunk of n <= L steps started from the identity,
+//   combine  aggregate(s1 then s2) given the n2 steps s2 covers (s1 is earlier in time),
+//   run      the chunk's steps from an incoming state, writing one output per step.
+// Each combine is associative, which is what lets a sequence be cut into chunks whose
+// aggregates are scanned and then re-run from their carries (the two-halves split of the
+// LRU write-up, parallelisation section: x_T = lam^{T-t} x_t + local sum over (t, T]).
+#pragma once
+
+#include "chunk_scan.hpp"
+#include "device_common.hpp"
+
+namespace linrec {
+
+// ----------------------------------------------------------------------------------
+// WKV-4, RWKV-LLM page "Time-mixing block", eq. (14).
+// The past sums A_t = sum_{i<t} e^{-(t-1-i)w + k_i} v_i and B_t (same without v) are
+// kept as (a, b, p) with A = a 2^p, B = b 2^p, p the running maximum of the base-2
+// exponents, so every exponential has a non-positive argument:
+//   output  q = max(p, mu+kk_t),   y_t = (a 2^{p-q} + v_t 2^{mu+kk_t-q}) / (b 2^{p-q} + 2^{mu+kk_t-q})
+//   update  q' = max(p-om, kk_t),  a <- a 2^{p-om-q'} + v_t 2^{kk_t-q'},  b likewise,  p <- q'
+// with kk = k log2 e, om = w log2 e, mu = u log2 e.  Two spans compose as
+//   p = max(p1 - n2 om, p2),  a = a1 2^{p1-n2 om-p} + a2 2^{p2-p}  (b likewise).
+// ----------------------------------------------------------------------------------
+
+
+struct WkvOp {
+    using Args = WkvArgs;
+    struct Chan { float om, mu; };
+    struct In { float kk, v; };
+    struct Agg { float a, b, p; };
+
+    template <int L>
+    __device__ static Chan chan(const Args& A, int64_t c) {
+        return {A.w[c] * kLog2e, A.u[c] * kLog2e};
+    }
+    __device__ static Agg identity() { return {0.f, 0.f, kEmpty}; }
+    __device__ static Agg init(const Args&, int64_t, int64_t, int64_t) { return identity(); }
+
+    template <int VEC>
+    __device__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
+        const FV<VEC> k = ldg<VEC>(A.k + off);
+        const FV<VEC> v = ldg<VEC>(A.v + off);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {k.v[e] * kLog2e, v.v[e]};
+    }
+    template <int VEC>
+    __device__ static void zero(In (&in)[VEC]) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {0.f, 0.f};
+    }
+
+    // Chunk of n steps from the empty state: p = max_j m_j with m_j = kk_j - (n-1-j) om,
+    // a = sum_j 2^{m_j-p} v_j, b = sum_j 2^{m_j-p}.  A reduction, not a scan.
+    template <int L, int VEC>
+    __device__ static Agg reduce(const Chan& ch, const In (&in)[L][VEC], int e, int n) {
+        if (n <= 0) return identity();
+        float m[L];
+        float p = kEmpty;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            m[j] = (j < n) ? fmaf(-(float)(n - 1 - j), ch.om, in[j][e].kk) : kEmpty;
+            p = fmaxf(p, m[j]);
+        }
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const float f = fast_exp2(m[j] - p);  // 0 for the unused slots
+            a = fmaf(f, in[j][e].v, a);
+            b += f;
+        }
+        return {a, b, p};
+    }
+
+    __device__ static Agg combine(const Chan& ch, const Agg& s1, const Agg& s2, int64_t n2) {
+        const float p1 = fmaxf(s1.p - (float)n2 * ch.om, kEmpty);
+        const float p = fmaxf(p1, s2.p);
+        const float f1 = fast_exp2(p1 - p), f2 = fast_exp2(s2.p - p);
+        return {fmaf(s1.a, f1, s2.a * f2), fmaf(s1.b, f1, s2.b * f2), p};
+    }
+
+    template <int L, int VEC>
+    __device__ static void run(const Args& A, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], int n, int64_t off, int64_t C) {
+        float a[VEC], b[VEC], p[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) { a[e] = cin[e].a; b[e] = cin[e].b; p[e] = cin[e].p; }
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                FV<VEC> y;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float kk = in[j][e].kk, vv = in[j][e].v;
+                    const float ww = ch[e].mu + kk;
+                    const float q = fmaxf(p[e], ww);
+                    const float e1 = fast_exp2(p[e] - q), e2 = fast_exp2(ww - q);
+                    y.v[e] = __fdividef(fmaf(a[e], e1, vv * e2), fmaf(b[e], e1, e2));
+                    const float pw = p[e] - ch[e].om;
+                    const float q2 = fmaxf(pw, kk);
+                    const float f1 = fast_exp2(pw - q2), f2 = fast_exp2(kk - q2);
+                    a[e] = fmaf(a[e], f1, vv * f2);
+                    b[e] = fmaf(b[e], f1, f2);
+                    p[e] = q2;
+                }
+                stg<VEC>(A.y + off + (int64_t)j * C, y);
+            }
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------------
+// Real diagonal scan x_t = a_t x_{t-1} + b_t ("Were RNNs All We Needed?" page, minGRU
+// section).  Aggregate of a span: (m, x) = (product of its a, its output from x = 0);
+// (m1, x1) then (m2, x2) is (m1 m2, m2 x1 + x2).
+// ----------------------------------------------------------------------------------
+
+
+struct RealOp {
+    using Args = RealArgs;
+    struct Chan {};
+    struct In { float a, b; };
+    struct Agg { float m, x; };
+
+    template <int L>
+    __device__ static Chan chan(const Args&, int64_t) { return {}; }
+    __device__ static Agg identity() { return {1.f, 0.f}; }
+    __device__ static Agg init(const Args& A, int64_t b, int64_t c, int64_t C) {
+        return {1.f, A.x0 ? A.x0[b * C + c] : 0.f};
+    }
+
+    template <int VEC>
+    __device__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
+        const FV<VEC> a = ldg<VEC>(A.a + off);
+        const FV<VEC> b = ldg<VEC>(A.b + off);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {a.v[e], b.v[e]};
+    }
+    template <int VEC>
+    __device__ static void zero(In (&in)[VEC]) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {1.f, 0.f};
+    }
+
+    template <int L, int VEC>
+    __device__ static Agg reduce(const Chan&, const In (&in)[L][VEC], int e, int n) {
+        float m = 1.f, x = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                x = fmaf(in[j][e].a, x, in[j][e].b);
+                m *= in[j][e].a;
+            }
+        }
+        return {m, x};
+    }
+
+    __device__ static Agg combine(const Chan&, const Agg& s1, const Agg& s2, int64_t) {
+        return {s1.m * s2.m, fmaf(s2.m, s1.x, s2.x)};
+    }
+
+    template <int L, int VEC>
+    __device__ static void run(const Args& A, const Chan (&)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], int n, int64_t off, int64_t C) {
+        float x[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[e] = cin[e].x;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                FV<VEC> o;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    x[e] = fmaf(in[j][e].a, x[e], in[j][e].b);
+                    o.v[e] = x[e];
+                }
+                stg<VEC>(A.x + off + (int64_t)j * C, o);
+            }
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------------
+// Complex diagonal scan x_t = lam x_{t-1} + u_t (LRU write-up, eq. lr-xx), complex64.
+// Aggregate of a span of n steps: (lam^n, its output from x = 0).  lam^n for a full
+// chunk is formed in float64 by repeated squaring from the complex64 lam.
+// ----------------------------------------------------------------------------------
+
+
+__device__ __forceinline__ void cpow64(double br, double bi, int64_t n, float& rr, float& ri) {
+    double pr = 1.0, pi = 0.0;
+    while (n > 0) {
+        if (n & 1) {
+            const double t = pr * br - pi * bi;
+            pi = pr * bi + pi * br;
+            pr = t;
+        }
+        const double t = br * br - bi * bi;
+        bi = 2.0 * br * bi;
+        br = t;
+        n >>= 1;
+    }
+    rr = (float)pr;
+    ri = (float)pi;
+}
+
+struct CplxOp {
+    using Args = CplxArgs;
+    struct Chan { float lr, li, Lr, Li; };  // lam and lam^L
+    struct In { float r, i; };
+    struct Agg { float mr, mi, xr, xi; };
+
+    template <int L>
+    __device__ static Chan chan(const Args& A, int64_t c) {
+        Chan ch;
+        ch.lr = A.lam[2 * c];
+        ch.li = A.lam[2 * c + 1];
+        cpow64((double)ch.lr, (double)ch.li, L, ch.Lr, ch.Li);
+        return ch;
+    }
+    __device__ static Agg identity() { return {1.f, 0.f, 0.f, 0.f}; }
+    __device__ static Agg init(const Args& A, int64_t b, int64_t c, int64_t C) {
+        if (!A.x0) return identity();
+        return {1.f, 0.f, A.x0[2 * (b * C + c)], A.x0[2 * (b * C + c) + 1]};
+    }
+
+    template <int VEC>
+    __device__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
+        const FV<2 * VEC> t = ldg<2 * VEC>(A.u + 2 * off);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {t.v[2 * e], t.v[2 * e + 1]};
+    }
+    template <int VEC>
+    __device__ static void zero(In (&in)[VEC]) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {0.f, 0.f};
+    }
+
+    template <int L, int VEC>
+    __device__ static Agg reduce(const Chan& ch, const In (&in)[L][VEC], int e, int n) {
+        float xr = 0.f, xi = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                const float tr = fmaf(ch.lr, xr, fmaf(-ch.li, xi, in[j][e].r));
+                xi = fmaf(ch.lr, xi, fmaf(ch.li, xr, in[j][e].i));
+                xr = tr;
+            }
+        }
+        Agg r;
+        r.xr = xr;
+        r.xi = xi;
+        if (n == L) {
+            r.mr = ch.Lr;
+            r.mi = ch.Li;
+        } else {
+            cpow64((double)ch.lr, (double)ch.li, n, r.mr, r.mi);
+        }
+        return r;
+    }
+
+    __device__ static Agg combine(const Chan&, const Agg& s1, const Agg& s2, int64_t) {
+        Agg r;
+        r.mr = fmaf(s1.mr, s2.mr, -s1.mi * s2.mi);
+        r.mi = fmaf(s1.mr, s2.mi, s1.mi * s2.mr);
+        r.xr = fmaf(s2.mr, s1.xr, fmaf(-s2.mi, s1.xi, s2.xr));
+        r.xi = fmaf(s2.mr, s1.xi, fmaf(s2.mi, s1.xr, s2.xi));
+        return r;
+    }
+
+    template <int L, int VEC>
+    __device__ static void run(const Args& A, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], int n, int64_t off, int64_t C) {
+        float xr[VEC], xi[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) { xr[e] = cin[e].xr; xi[e] = cin[e].xi; }
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                FV<2 * VEC> o;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float tr = fmaf(ch[e].lr, xr[e], fmaf(-ch[e].li, xi[e], in[j][e].r));
+                    xi[e] = fmaf(ch[e].lr, xi[e], fmaf(ch[e].li, xr[e], in[j][e].i));
+                    xr[e] = tr;
+                    o.v[2 * e] = xr[e];
+                    o.v[2 * e + 1] = xi[e];
+                }
+                stg<2 * VEC>(A.x + 2 * (off + (int64_t)j * C), o);
+            }
+        }
+    }
+};
+
+}  // namespace linrec

@@ -1,0 +1,136 @@
+"""Host-only checks of the C ABI: the library loads, exports every function that
+``include/linrec.h`` declares, and rejects bad arguments before making any HIP call.
+
+No kernel is launched here: every call below returns from the host-side checks.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linrec.h")
+LIB = os.path.join(ROOT, "linear_recurrence_rnn_amd", "liblinrec.so")
+
+OK, INVALID, WORKSPACE, UNSUPPORTED, HIPERR = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("liblinrec.so is not built (run python -m linear_recurrence_rnn_amd.build)")
+    from linear_recurrence_rnn_amd import binding
+    return binding.load()
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for n in ("wkv4_forward", "wkv4_backward", "linrec_scan_real", "linrec_scan_complex",
+              "wkv4_forward_workspace_size", "wkv4_backward_workspace_size",
+              "linrec_scan_workspace_size", "linrec_abi_version", "linrec_status_string",
+              "linrec_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_the_abi_is_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert exported == set(declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    m = re.search(r"#define LINREC_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.linrec_abi_version() == int(m.group(1))
+    assert lib.linrec_status_string(OK) == b"LINREC_OK"
+    assert lib.linrec_status_string(WORKSPACE) == b"LINREC_ERR_WORKSPACE"
+    assert lib.linrec_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p(0x100000)       # aligned fake device addresses: never dereferenced
+P2 = ctypes.c_void_p(0x200000)
+ODD = ctypes.c_void_p(0x100002)     # not 4-byte aligned
+
+
+def fwd(lib, B, T, C, ptrs=None, ws=None, nws=0):
+    w, u, k, v, y = ptrs or (P, P, P, P, P2)
+    return lib.wkv4_forward(B, T, C, w, u, k, v, y, ws, nws, None)
+
+
+def test_negative_and_overflowing_sizes(lib):
+    assert fwd(lib, -1, 4, 4) == INVALID
+    assert b"negative" in lib.linrec_last_error()
+    assert fwd(lib, 4, -2, 4) == INVALID
+    assert fwd(lib, 1 << 31, 1 << 31, 1 << 10) == INVALID
+    assert b"overflow" in lib.linrec_last_error()
+    assert lib.linrec_scan_real(-1, 1, 1, P, P, None, P2, None, 0, None) == INVALID
+    assert lib.linrec_scan_complex(1, 1 << 40, 1 << 30, P, P, None, P2, None, 0, None) == INVALID
+    assert lib.wkv4_backward(1, -1, 1, P, P, P, P, P, P2, P2, P2, P2, None, 0, None) == INVALID
+
+
+def test_null_pointers(lib):
+    assert fwd(lib, 1, 4, 4, (P, None, P, P, P2)) == INVALID
+    assert b"NULL" in lib.linrec_last_error()
+    assert lib.linrec_scan_real(1, 4, 4, P, None, None, P2, None, 0, None) == INVALID
+    assert lib.linrec_scan_complex(1, 4, 4, None, P, None, P2, None, 0, None) == INVALID
+    assert lib.wkv4_backward(1, 4, 4, P, P, P, P, None, P2, P2, P2, P2, None, 0, None) == INVALID
+
+
+def test_empty_shapes_are_noops(lib):
+    # Forward and scans enqueue nothing for an empty shape.
+    assert fwd(lib, 0, 16, 16) == OK
+    assert fwd(lib, 2, 0, 16) == OK
+    assert fwd(lib, 2, 16, 0) == OK
+    assert lib.linrec_scan_real(0, 4, 4, P, P, None, P2, None, 0, None) == OK
+    assert lib.linrec_scan_complex(3, 0, 4, P, P, None, P2, None, 0, None) == OK
+    assert lib.wkv4_backward(2, 5, 0, P, P, P, P, P, P2, P2, P2, P2, None, 0, None) == OK
+
+
+def test_misaligned_pointers(lib):
+    assert fwd(lib, 1, 4, 4, (P, P, ODD, P, P2)) == UNSUPPORTED
+    assert b"aligned" in lib.linrec_last_error()
+    # complex64 needs 8-byte alignment
+    assert lib.linrec_scan_complex(1, 4, 4, P, ctypes.c_void_p(0x100004), None, P2, None, 0,
+                                   None) == UNSUPPORTED
+
+
+def test_workspace_checks(lib):
+    # A single long sequence is cut into slabs and needs workspace.
+    B, T, C = 1, 262144, 1024
+    need = lib.linrec_scan_workspace_size(B, T, C, 1)
+    assert need > 0
+    assert lib.linrec_scan_complex(B, T, C, P, P, None, P2, None, 0, None) == WORKSPACE
+    assert lib.linrec_scan_complex(B, T, C, P, P, None, P2, None, need, None) == INVALID  # NULL ws
+    assert lib.linrec_scan_complex(B, T, C, P, P, None, P2, ctypes.c_void_p(0x300008), need,
+                                   None) == UNSUPPORTED  # not 16-byte aligned
+    assert lib.wkv4_backward_workspace_size(8, 4096, 2560) > 0
+    need_b = lib.wkv4_backward_workspace_size(2, 100, 8)
+    assert lib.wkv4_backward(2, 100, 8, P, P, P, P, P, P2, P2, P2, P2, None, need_b - 1,
+                             None) == WORKSPACE
+
+
+def test_workspace_sizes(lib):
+    assert lib.wkv4_forward_workspace_size(0, 10, 10) == 0
+    assert lib.wkv4_forward_workspace_size(-1, 10, 10) == 0
+    # Enough (batch x channel-group) workgroups: one pass, no workspace.
+    assert lib.wkv4_forward_workspace_size(8, 1024, 768) == 0
+    assert lib.linrec_scan_workspace_size(64, 4096, 256, 0) == 0
+    # A long single sequence needs slab carries.
+    assert lib.wkv4_forward_workspace_size(1, 1 << 16, 64) > 0
+    assert lib.linrec_scan_workspace_size(1, 1 << 16, 64, 0) > 0
