@@ -155,7 +155,7 @@ LINREC_API int wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, con
     linrec::ScanPlan p = scan_plan(linrec::kKindWkv, B, T, C);
     if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
     p.vec = (C % 4 == 0 && aligned(k, 16) && aligned(v, 16) && aligned(y, 16)) ? 4 : 1;
-    const linrec::WkvArgs A{w, u, k, v, y};
+    const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0};
     return hip_status(linrec::run_wkv_forward(A, geom_of(p, B, T, C, workspace), p, (hipStream_t)stream),
                       "wkv4_forward launch");
 }

@@ -72,9 +72,10 @@ __global__ __launch_bounds__(CL * NR) void chunk_scan_kernel(typename Op::Args A
         }
 
         // Phase 1: chunk aggregates.
+        typename Op::Local loc[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
-            sh[r][cl * VEC + e] = Op::template reduce<L, VEC>(ch[e], in, e, active ? n : 0);
+            sh[r][cl * VEC + e] = Op::template reduce<L, VEC>(ch[e], in, e, active ? n : 0, loc[e]);
         __syncthreads();
 
         // Phase 2: inclusive scan of the NR aggregates.  end(x) = steps from the tile
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(CL * NR) void chunk_scan_kernel(typename Op::Args A
             for (int e = 0; e < VEC; ++e)
                 cin[e] = (r == 0) ? carry[e]
                                   : Op::combine(ch[e], carry[e], sh[r - 1][cl * VEC + e], end_of(r - 1));
-            Op::template run<L, VEC>(A, ch, cin, in, n, off, g.C);
+            Op::template run<L, VEC>(A, ch, cin, in, loc, n, off, g.C);
         }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) carry[e] = Op::combine(ch[e], carry[e], sh[NR - 1][cl * VEC + e], tt);

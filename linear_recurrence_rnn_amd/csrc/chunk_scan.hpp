@@ -22,6 +22,7 @@ struct WkvArgs {
     const float* k;  // (B,T,C)
     const float* v;  // (B,T,C)
     float* y;        // (B,T,C)
+    int exact_only;  // 1: always take the exact per-step path (used by tests)
 };
 struct RealArgs {
     const float* a;   // (B,T,C)

@@ -14,99 +14,160 @@
 
 #include "chunk_scan.hpp"
 #include "device_common.hpp"
+#include "wkv_math.hpp"
 
 namespace linrec {
 
 // ----------------------------------------------------------------------------------
 // WKV-4, RWKV-LLM page "Time-mixing block", eq. (14).
-// The past sums A_t = sum_{i<t} e^{-(t-1-i)w + k_i} v_i and B_t (same without v) are
-// kept as (a, b, p) with A = a 2^p, B = b 2^p, p the running maximum of the base-2
-// exponents, so every exponential has a non-positive argument:
-//   output  q = max(p, mu+kk_t),   y_t = (a 2^{p-q} + v_t 2^{mu+kk_t-q}) / (b 2^{p-q} + 2^{mu+kk_t-q})
-//   update  q' = max(p-om, kk_t),  a <- a 2^{p-om-q'} + v_t 2^{kk_t-q'},  b likewise,  p <- q'
-// with kk = k log2 e, om = w log2 e, mu = u log2 e.  Two spans compose as
-//   p = max(p1 - n2 om, p2),  a = a1 2^{p1-n2 om-p} + a2 2^{p2-p}  (b likewise).
+// The past sums A_t = sum_{i<t} e^{-(t-1-i)w + k_i} v_i and B_t (same without v) are kept
+// as (a, b, p): A = a 2^p, B = b 2^p, p an integer exponent (see wkv_math.hpp), in base 2
+// (kk = k log2 e, om = w log2 e, mu = u log2 e).
+//
+// Phase 1 (chunk of n steps from the empty state): m_j = kk_j - (n-1-j) om is the exponent
+// of step j's weight at the chunk end; p = ceil(max_j m_j), g_j = 2^{m_j - p} <= 1, and the
+// aggregate is (sum g_j v_j, sum g_j, p).  The g_j stay in registers (replacing kk_j).
+//
+// Phase 3 re-runs the chunk from its carry (a0, b0, p0).  Fast path: a frame that decays
+// with the sums, A~_j = A_{t0+j} 2^{-F_0 + j om}, turns the recurrence into plain sums,
+//   A~_{j+1} = A~_j + 2^{om-D} g_j v_j,   y_j = (A~_j + 2^{mu-D} g_j v_j) / (B~_j + 2^{mu-D} g_j),
+// with F_0 = p + (n-1) om + D and D >= max(om, mu, 0) chosen so no term exceeds 1: one
+// exponential per element, shared with phase 1.  It is taken when the largest term of the
+// first step's denominator is at least 2^-120 (so nothing that matters can underflow);
+// otherwise the chunk runs the exact per-step running maximum with integer exponents,
+//   output  q = ceil(max(M, kk_t + mu)),  y = (a 2^{p-q} + v 2^{kk+mu-q}) / (b 2^{p-q} + 2^{kk+mu-q})
+//   update  p' = ceil(max(M - om, kk_t)), a <- a 2^{p-p'-om} + v 2^{kk-p'}, b likewise,
+// where M = p + frexp_exp(b) bounds log2 B (see wkv_math.hpp),
+// re-reading k from memory (its registers now hold g).
 // ----------------------------------------------------------------------------------
-
-
 struct WkvOp {
     using Args = WkvArgs;
-    struct Chan { float om, mu; };
-    struct In { float kk, v; };
+    struct Chan { float om, mu, lift, fast_lo; };  // lift = ceil(max(om, mu, 0))
+    struct In { float kk, v; };           // kk becomes g_j after phase 1
+    struct Local { float p, m0; };        // chunk exponent p and m_0 - p
     struct Agg { float a, b, p; };
 
     template <int L>
-    __device__ static Chan chan(const Args& A, int64_t c) {
-        return {A.w[c] * kLog2e, A.u[c] * kLog2e};
+    __device__ __forceinline__ static Chan chan(const Args& A, int64_t c) {
+        Chan ch;
+        ch.om = fminf(A.w[c] * kLog2e, kMaxOm);
+        ch.mu = A.u[c] * kLog2e;
+        ch.lift = ceilf(fmaxf(fmaxf(ch.om, ch.mu), 0.f));
+        ch.fast_lo = A.exact_only ? __builtin_inff() : -120.f;
+        return ch;
     }
-    __device__ static Agg identity() { return {0.f, 0.f, kEmpty}; }
-    __device__ static Agg init(const Args&, int64_t, int64_t, int64_t) { return identity(); }
+    __device__ __forceinline__ static Agg identity() { return {0.f, 0.f, kEmpty}; }
+    __device__ __forceinline__ static Agg init(const Args&, int64_t, int64_t, int64_t) { return identity(); }
 
     template <int VEC>
-    __device__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
+    __device__ __forceinline__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
         const FV<VEC> k = ldg<VEC>(A.k + off);
         const FV<VEC> v = ldg<VEC>(A.v + off);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {k.v[e] * kLog2e, v.v[e]};
     }
     template <int VEC>
-    __device__ static void zero(In (&in)[VEC]) {
+    __device__ __forceinline__ static void zero(In (&in)[VEC]) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {0.f, 0.f};
     }
 
-    // Chunk of n steps from the empty state: p = max_j m_j with m_j = kk_j - (n-1-j) om,
-    // a = sum_j 2^{m_j-p} v_j, b = sum_j 2^{m_j-p}.  A reduction, not a scan.
     template <int L, int VEC>
-    __device__ static Agg reduce(const Chan& ch, const In (&in)[L][VEC], int e, int n) {
-        if (n <= 0) return identity();
+    __device__ __forceinline__ static Agg reduce(const Chan& ch, In (&in)[L][VEC], int e, int n, Local& loc) {
+        if (n <= 0) {
+            loc = {kEmpty, kEmpty};
+            return identity();
+        }
         float m[L];
-        float p = kEmpty;
+        float mx = kEmpty;
 #pragma unroll
         for (int j = 0; j < L; ++j) {
             m[j] = (j < n) ? fmaf(-(float)(n - 1 - j), ch.om, in[j][e].kk) : kEmpty;
-            p = fmaxf(p, m[j]);
+            mx = fmaxf(mx, m[j]);
         }
+        const float p = ceilf(mx);
         float a = 0.f, b = 0.f;
 #pragma unroll
         for (int j = 0; j < L; ++j) {
-            const float f = fast_exp2(m[j] - p);  // 0 for the unused slots
-            a = fmaf(f, in[j][e].v, a);
-            b += f;
+            const float g = fast_exp2(m[j] - p);  // 0 for the unused slots
+            in[j][e].kk = g;
+            a = fmaf(g, in[j][e].v, a);
+            b += g;
         }
+        loc = {p, m[0] - p};
         return {a, b, p};
     }
 
-    __device__ static Agg combine(const Chan& ch, const Agg& s1, const Agg& s2, int64_t n2) {
-        const float p1 = fmaxf(s1.p - (float)n2 * ch.om, kEmpty);
-        const float p = fmaxf(p1, s2.p);
-        const float f1 = fast_exp2(p1 - p), f2 = fast_exp2(s2.p - p);
+    __device__ __forceinline__ static Agg combine(const Chan& ch, const Agg& s1, const Agg& s2, int64_t n2) {
+        float p, f1, f2;
+        merge_scales(s1.p, s1.b, s2.p, s2.b, mul_split((float)n2, ch.om), p, f1, f2);
         return {fmaf(s1.a, f1, s2.a * f2), fmaf(s1.b, f1, s2.b * f2), p};
     }
 
     template <int L, int VEC>
-    __device__ static void run(const Args& A, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
-                               const In (&in)[L][VEC], int n, int64_t off, int64_t C) {
-        float a[VEC], b[VEC], p[VEC];
+    __device__ __forceinline__ static void run(const Args& A, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], const Local (&loc)[VEC], int n, int64_t off,
+                               int64_t C) {
+        float a[VEC], b[VEC], cs[VEC], us[VEC];
+        bool fast[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) { a[e] = cin[e].a; b[e] = cin[e].b; p[e] = cin[e].p; }
+        for (int e = 0; e < VEC; ++e) {
+            // Carry exponent relative to the chunk frame: p0 - p - (n-1) om.
+            const Split d = mul_split((float)(n - 1), ch[e].om);
+            const float rel = ((cin[e].p - loc[e].p) - d.hi) - d.lo;
+            const float fe = (float)__builtin_amdgcn_frexp_expf(cin[e].b);  // b0 < 2^fe
+            const float D = fmaxf(ch[e].lift, rel + fe);
+            const float carry_lo = (rel + fe - 1.f) - D;       // log2 of the carry's size, >=
+            const float cur_lo = (loc[e].m0 + ch[e].mu) - D;   // log2 of step 0's own weight
+            fast[e] = fmaxf(carry_lo, cur_lo) >= ch[e].fast_lo;
+            const float cf = fast_exp2(rel - D);
+            a[e] = cin[e].a * cf;
+            b[e] = cin[e].b * cf;
+            cs[e] = fast_exp2(ch[e].mu - D);
+            us[e] = fast_exp2(ch[e].om - D);
+        }
+        bool all_fast = true;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) all_fast = all_fast && fast[e];
+        if (all_fast) {
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                if (j < n) {
+                    FV<VEC> y;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const float g = in[j][e].kk, vv = in[j][e].v;
+                        const float cur = g * cs[e];
+                        y.v[e] = fmaf(cur, vv, a[e]) * __builtin_amdgcn_rcpf(b[e] + cur);
+                        const float up = g * us[e];
+                        a[e] = fmaf(up, vv, a[e]);
+                        b[e] += up;
+                    }
+                    stg<VEC>(A.y + off + (int64_t)j * C, y);
+                }
+            }
+            return;
+        }
+        // Exact per-step running maximum (integer exponents), all channels of the lane.
+        float pa[VEC], pb[VEC], pp[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) { pa[e] = cin[e].a; pb[e] = cin[e].b; pp[e] = cin[e].p; }
 #pragma unroll
         for (int j = 0; j < L; ++j) {
             if (j < n) {
+                const FV<VEC> kr = ldg<VEC>(A.k + off + (int64_t)j * C);
                 FV<VEC> y;
-#pragma unroll
+    #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const float kk = in[j][e].kk, vv = in[j][e].v;
-                    const float ww = ch[e].mu + kk;
-                    const float q = fmaxf(p[e], ww);
-                    const float e1 = fast_exp2(p[e] - q), e2 = fast_exp2(ww - q);
-                    y.v[e] = __fdividef(fmaf(a[e], e1, vv * e2), fmaf(b[e], e1, e2));
-                    const float pw = p[e] - ch[e].om;
-                    const float q2 = fmaxf(pw, kk);
-                    const float f1 = fast_exp2(pw - q2), f2 = fast_exp2(kk - q2);
-                    a[e] = fmaf(a[e], f1, vv * f2);
-                    b[e] = fmaf(b[e], f1, f2);
-                    p[e] = q2;
+                    const float kk = kr.v[e] * kLog2e, vv = in[j][e].v;
+                    const float q = ceilf(fmaxf(mag(pp[e], pb[e]), kk + ch[e].mu));
+                    const float e1 = fast_exp2(pp[e] - q), e2 = fast_exp2((kk - q) + ch[e].mu);
+                    y.v[e] = fmaf(pa[e], e1, vv * e2) * __builtin_amdgcn_rcpf(fmaf(pb[e], e1, e2));
+                    const float q2 = ceilf(fmaxf(mag(pp[e], pb[e]) - ch[e].om, kk));
+                    const float f1 = fast_exp2((pp[e] - q2) - ch[e].om), f2 = fast_exp2(kk - q2);
+                    pa[e] = fmaf(pa[e], f1, vv * f2);
+                    pb[e] = fmaf(pb[e], f1, f2);
+                    pp[e] = q2;
                 }
                 stg<VEC>(A.y + off + (int64_t)j * C, y);
             }
@@ -125,30 +186,31 @@ struct RealOp {
     using Args = RealArgs;
     struct Chan {};
     struct In { float a, b; };
+    struct Local {};
     struct Agg { float m, x; };
 
     template <int L>
-    __device__ static Chan chan(const Args&, int64_t) { return {}; }
-    __device__ static Agg identity() { return {1.f, 0.f}; }
-    __device__ static Agg init(const Args& A, int64_t b, int64_t c, int64_t C) {
+    __device__ __forceinline__ static Chan chan(const Args&, int64_t) { return {}; }
+    __device__ __forceinline__ static Agg identity() { return {1.f, 0.f}; }
+    __device__ __forceinline__ static Agg init(const Args& A, int64_t b, int64_t c, int64_t C) {
         return {1.f, A.x0 ? A.x0[b * C + c] : 0.f};
     }
 
     template <int VEC>
-    __device__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
+    __device__ __forceinline__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
         const FV<VEC> a = ldg<VEC>(A.a + off);
         const FV<VEC> b = ldg<VEC>(A.b + off);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {a.v[e], b.v[e]};
     }
     template <int VEC>
-    __device__ static void zero(In (&in)[VEC]) {
+    __device__ __forceinline__ static void zero(In (&in)[VEC]) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {1.f, 0.f};
     }
 
     template <int L, int VEC>
-    __device__ static Agg reduce(const Chan&, const In (&in)[L][VEC], int e, int n) {
+    __device__ __forceinline__ static Agg reduce(const Chan&, In (&in)[L][VEC], int e, int n, Local&) {
         float m = 1.f, x = 0.f;
 #pragma unroll
         for (int j = 0; j < L; ++j) {
@@ -160,13 +222,14 @@ struct RealOp {
         return {m, x};
     }
 
-    __device__ static Agg combine(const Chan&, const Agg& s1, const Agg& s2, int64_t) {
+    __device__ __forceinline__ static Agg combine(const Chan&, const Agg& s1, const Agg& s2, int64_t) {
         return {s1.m * s2.m, fmaf(s2.m, s1.x, s2.x)};
     }
 
     template <int L, int VEC>
-    __device__ static void run(const Args& A, const Chan (&)[VEC], const Agg (&cin)[VEC],
-                               const In (&in)[L][VEC], int n, int64_t off, int64_t C) {
+    __device__ __forceinline__ static void run(const Args& A, const Chan (&)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], const Local (&)[VEC], int n, int64_t off,
+                               int64_t C) {
         float x[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[e] = cin[e].x;
@@ -213,36 +276,37 @@ struct CplxOp {
     using Args = CplxArgs;
     struct Chan { float lr, li, Lr, Li; };  // lam and lam^L
     struct In { float r, i; };
+    struct Local {};
     struct Agg { float mr, mi, xr, xi; };
 
     template <int L>
-    __device__ static Chan chan(const Args& A, int64_t c) {
+    __device__ __forceinline__ static Chan chan(const Args& A, int64_t c) {
         Chan ch;
         ch.lr = A.lam[2 * c];
         ch.li = A.lam[2 * c + 1];
         cpow64((double)ch.lr, (double)ch.li, L, ch.Lr, ch.Li);
         return ch;
     }
-    __device__ static Agg identity() { return {1.f, 0.f, 0.f, 0.f}; }
-    __device__ static Agg init(const Args& A, int64_t b, int64_t c, int64_t C) {
+    __device__ __forceinline__ static Agg identity() { return {1.f, 0.f, 0.f, 0.f}; }
+    __device__ __forceinline__ static Agg init(const Args& A, int64_t b, int64_t c, int64_t C) {
         if (!A.x0) return identity();
         return {1.f, 0.f, A.x0[2 * (b * C + c)], A.x0[2 * (b * C + c) + 1]};
     }
 
     template <int VEC>
-    __device__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
+    __device__ __forceinline__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
         const FV<2 * VEC> t = ldg<2 * VEC>(A.u + 2 * off);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {t.v[2 * e], t.v[2 * e + 1]};
     }
     template <int VEC>
-    __device__ static void zero(In (&in)[VEC]) {
+    __device__ __forceinline__ static void zero(In (&in)[VEC]) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {0.f, 0.f};
     }
 
     template <int L, int VEC>
-    __device__ static Agg reduce(const Chan& ch, const In (&in)[L][VEC], int e, int n) {
+    __device__ __forceinline__ static Agg reduce(const Chan& ch, In (&in)[L][VEC], int e, int n, Local&) {
         float xr = 0.f, xi = 0.f;
 #pragma unroll
         for (int j = 0; j < L; ++j) {
@@ -264,7 +328,7 @@ struct CplxOp {
         return r;
     }
 
-    __device__ static Agg combine(const Chan&, const Agg& s1, const Agg& s2, int64_t) {
+    __device__ __forceinline__ static Agg combine(const Chan&, const Agg& s1, const Agg& s2, int64_t) {
         Agg r;
         r.mr = fmaf(s1.mr, s2.mr, -s1.mi * s2.mi);
         r.mi = fmaf(s1.mr, s2.mi, s1.mi * s2.mr);
@@ -274,8 +338,9 @@ struct CplxOp {
     }
 
     template <int L, int VEC>
-    __device__ static void run(const Args& A, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
-                               const In (&in)[L][VEC], int n, int64_t off, int64_t C) {
+    __device__ __forceinline__ static void run(const Args& A, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], const Local (&)[VEC], int n, int64_t off,
+                               int64_t C) {
         float xr[VEC], xi[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) { xr[e] = cin[e].xr; xi[e] = cin[e].xi; }
