@@ -3,6 +3,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <atomic>
+#include <random>
 #include <string>
 
 #include "linrec.h"
@@ -56,44 +58,95 @@ int check_shape(int64_t B, int64_t T, int64_t C, int64_t elem_bytes) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Launch plan of the chunked scan; a pure function of (kind, B, T, C) and the
-// environment overrides, so the workspace query and the call always agree.
-linrec::ScanPlan scan_plan(int kind, int64_t B, int64_t T, int64_t C) {
+// Launch plan of the forward scans for a given vector width; a pure function of
+// (kind, vec, B, T, C) and the environment overrides (tests use them to force shapes).
+linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
     linrec::ScanPlan p{};
-    p.vec = 1;
-    p.rows = (int)env_int("LINREC_ROWS", T >= 512 ? 64 : 16);
-    if (p.rows != 16 && p.rows != 64) p.rows = 64;
-    const int64_t tile = (int64_t)p.rows * linrec::kChunkLen;
-    const int64_t ngrp = ceil_div(C, linrec::kGroupChannels);
-    const int64_t wgs = B * ngrp;
-    const int64_t max_slabs = T > 0 ? ceil_div(T, tile) : 1;
-    int64_t nslab = 1;
-    const int64_t forced = env_int("LINREC_NSLAB", 0);
-    if (forced > 0) {
-        nslab = forced;
-    } else if (wgs > 0 && wgs < 512) {
-        nslab = ceil_div(1024, wgs);  // aim at ~1024 workgroups on 256 CUs
+    p.vec = vec;
+    // Default shapes, measured on MI355X at the workloads of the tests and the bench: WKV
+    // is arithmetic-heavy and favours occupancy (fewer registers per lane), the scans
+    // favour wider rows; long single sequences favour longer slabs (shorter look-backs).
+    if (kind == linrec::kKindWkv) {
+        p.nw = T <= 2048 ? 8 : 4;
+        p.L = 16;
+    } else if (kind == linrec::kKindReal) {
+        p.nw = 4;
+        p.L = 16;
+    } else {
+        p.nw = 8;
+        p.L = 16;
     }
-    if (nslab > max_slabs) nslab = max_slabs;
-    if (nslab < 1) nslab = 1;
-    p.slab_len = ceil_div(ceil_div(T > 0 ? T : 1, nslab), tile) * tile;
-    p.nslab = T > 0 ? ceil_div(T, p.slab_len) : 1;
+    const int nw = (int)env_int("LINREC_NW", 0), L = (int)env_int("LINREC_L", 0);
+    if (nw > 0 && L > 0 && linrec::scan_shape_supported(kind, vec, nw, L)) {
+        p.nw = nw;
+        p.L = L;
+    }
+    const int64_t cw = 64 * (int64_t)vec;
+    const int64_t nwg = B * ceil_div(C, cw) * (p.nslab = ceil_div(T, (int64_t)p.nw * p.L));
     p.ws_bytes = 0;
-    if (p.nslab > 1) p.ws_bytes = 2 * align256((size_t)(B * p.nslab * C) * linrec::agg_bytes(kind));
+    if (p.nslab > 1)
+        p.ws_bytes = align256((size_t)nwg * 8) + 2 * align256((size_t)(nwg * cw) * linrec::agg_bytes(kind));
     return p;
 }
 
-linrec::ScanGeom geom_of(const linrec::ScanPlan& p, int64_t B, int64_t T, int64_t C, void* ws) {
+int vmax_of(int kind) { return kind == linrec::kKindComplex ? 2 : 4; }
+
+// Channels per lane: the widest the alignment allows, narrowed by the default policy
+// (WKV: 1, real scan: 2) or by LINREC_VEC (tests and tuning).
+int pick_vec(int kind, int vec_aligned) {
+    int vec = vec_aligned;
+    const int64_t f = env_int("LINREC_VEC", 0);
+    if (f == 1 || f == 2 || f == 4) {
+        vec = f < vec ? (int)f : vec;
+    } else if (kind == linrec::kKindWkv) {
+        vec = 1;
+    } else if (kind == linrec::kKindReal) {
+        vec = vec < 2 ? vec : 2;
+    }
+    return vec;
+}
+
+// Workspace the caller must provide: enough for either vector width (the width depends on
+// pointer alignment, which a size query does not see).
+size_t scan_ws_bytes(int kind, int64_t B, int64_t T, int64_t C) {
+    size_t best = 0;
+    for (int vec : {vmax_of(kind), 2, 1}) {
+        const size_t x = scan_plan(kind, vec, B, T, C).ws_bytes;
+        best = x > best ? x : best;
+    }
+    return best;
+}
+
+// Per-call tag of the look-back flags: unique within the process and never 0.
+uint64_t next_tag() {
+    static std::atomic<uint64_t> counter{0};
+    static const uint64_t salt = [] {
+        std::random_device rd;
+        return ((uint64_t)rd() << 32) ^ (uint64_t)rd();
+    }();
+    uint64_t t = (salt + counter.fetch_add(1, std::memory_order_relaxed)) & ((1ull << 61) - 1);
+    return t ? t : 1;
+}
+
+linrec::ScanGeom geom_of(int kind, const linrec::ScanPlan& p, int64_t B, int64_t T, int64_t C, void* ws) {
     linrec::ScanGeom g{};
     g.B = B;
     g.T = T;
     g.C = C;
-    g.ngrp = ceil_div(C, linrec::kGroupChannels);
+    const int64_t cw = 64 * (int64_t)p.vec;
+    g.ngrp = ceil_div(C, cw);
     g.nslab = p.nslab;
-    g.slab_len = p.slab_len;
-    g.mode = linrec::kModeFull;
-    g.ws_agg = ws;
-    g.ws_carry = p.nslab > 1 ? (char*)ws + p.ws_bytes / 2 : nullptr;
+    g.tag = next_tag();
+    // Polls (each ~128 cycles) before a missing predecessor aggregate is recomputed;
+    // LINREC_SPIN overrides it (0 forces the recompute path, for tests).
+    const char* spin = std::getenv("LINREC_SPIN");
+    g.spin = (spin && *spin) ? (int)std::strtol(spin, nullptr, 10) : 4096;
+    const int64_t nwg = B * g.ngrp * g.nslab;
+    g.flags = reinterpret_cast<uint64_t*>(ws);
+    char* rec = (char*)ws + align256((size_t)nwg * 8);
+    g.rec_agg = rec;
+    g.rec_incl = rec + align256((size_t)(nwg * cw) * linrec::agg_bytes(kind));
+    if (p.nslab <= 1) g.flags = nullptr, g.rec_agg = g.rec_incl = nullptr;
     return g;
 }
 
@@ -129,12 +182,12 @@ LINREC_API const char* linrec_last_error(void) { return g_last_error.c_str(); }
 
 LINREC_API size_t wkv4_forward_workspace_size(int64_t B, int64_t T, int64_t C) {
     if (B < 0 || T < 0 || C < 0 || B == 0 || T == 0 || C == 0) return 0;
-    return scan_plan(linrec::kKindWkv, B, T, C).ws_bytes;
+    return scan_ws_bytes(linrec::kKindWkv, B, T, C);
 }
 
 LINREC_API size_t linrec_scan_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex) {
     if (B < 0 || T < 0 || C < 0 || B == 0 || T == 0 || C == 0) return 0;
-    return scan_plan(is_complex ? linrec::kKindComplex : linrec::kKindReal, B, T, C).ws_bytes;
+    return scan_ws_bytes(is_complex ? linrec::kKindComplex : linrec::kKindReal, B, T, C);
 }
 
 LINREC_API size_t wkv4_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
@@ -152,11 +205,14 @@ LINREC_API int wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, con
     const void* ptrs[] = {w, u, k, v, y};
     for (const void* p : ptrs)
         if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
-    linrec::ScanPlan p = scan_plan(linrec::kKindWkv, B, T, C);
+    const int vec = pick_vec(linrec::kKindWkv, (C % 4 == 0 && aligned(k, 16) && aligned(v, 16) && aligned(y, 16)) ? 4
+                                              : (C % 2 == 0 && aligned(k, 8) && aligned(v, 8) && aligned(y, 8)) ? 2
+                                                                                                           : 1);
+    const linrec::ScanPlan p = scan_plan(linrec::kKindWkv, vec, B, T, C);
     if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
-    p.vec = (C % 4 == 0 && aligned(k, 16) && aligned(v, 16) && aligned(y, 16)) ? 4 : 1;
     const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0};
-    return hip_status(linrec::run_wkv_forward(A, geom_of(p, B, T, C, workspace), p, (hipStream_t)stream),
+    return hip_status(linrec::run_wkv_forward(A, geom_of(linrec::kKindWkv, p, B, T, C, workspace), p,
+                                              (hipStream_t)stream),
                       "wkv4_forward launch");
 }
 
@@ -171,11 +227,14 @@ LINREC_API int linrec_scan_real(int64_t B, int64_t T, int64_t C, const float* a,
     for (const void* p : ptrs)
         if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
     if (x0 && !aligned(x0, 4)) return fail(LINREC_ERR_UNSUPPORTED, "x0 not 4-byte aligned");
-    linrec::ScanPlan p = scan_plan(linrec::kKindReal, B, T, C);
+    const int vec = pick_vec(linrec::kKindReal, (C % 4 == 0 && aligned(a, 16) && aligned(b, 16) && aligned(x, 16)) ? 4
+                                               : (C % 2 == 0 && aligned(a, 8) && aligned(b, 8) && aligned(x, 8)) ? 2
+                                                                                                            : 1);
+    const linrec::ScanPlan p = scan_plan(linrec::kKindReal, vec, B, T, C);
     if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
-    p.vec = (C % 4 == 0 && aligned(a, 16) && aligned(b, 16) && aligned(x, 16)) ? 4 : 1;
     const linrec::RealArgs A{a, b, x0, x};
-    return hip_status(linrec::run_scan_real(A, geom_of(p, B, T, C, workspace), p, (hipStream_t)stream),
+    return hip_status(linrec::run_scan_real(A, geom_of(linrec::kKindReal, p, B, T, C, workspace), p,
+                                            (hipStream_t)stream),
                       "linrec_scan_real launch");
 }
 
@@ -190,11 +249,12 @@ LINREC_API int linrec_scan_complex(int64_t B, int64_t T, int64_t C, const float*
     for (const void* p : ptrs)
         if (!aligned(p, 8)) return fail(LINREC_ERR_UNSUPPORTED, "complex64 pointer not 8-byte aligned");
     if (x0 && !aligned(x0, 8)) return fail(LINREC_ERR_UNSUPPORTED, "x0 not 8-byte aligned");
-    linrec::ScanPlan p = scan_plan(linrec::kKindComplex, B, T, C);
+    const int vec = pick_vec(linrec::kKindComplex, (C % 2 == 0 && aligned(u, 16) && aligned(x, 16)) ? 2 : 1);
+    const linrec::ScanPlan p = scan_plan(linrec::kKindComplex, vec, B, T, C);
     if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
-    p.vec = (C % 2 == 0 && aligned(u, 16) && aligned(x, 16)) ? 2 : 1;
     const linrec::CplxArgs A{lambda, u, x0, x};
-    return hip_status(linrec::run_scan_complex(A, geom_of(p, B, T, C, workspace), p, (hipStream_t)stream),
+    return hip_status(linrec::run_scan_complex(A, geom_of(linrec::kKindComplex, p, B, T, C, workspace), p,
+                                               (hipStream_t)stream),
                       "linrec_scan_complex launch");
 }
 

@@ -1,4 +1,4 @@
-// chunk_scan.hpp -- host-visible interface of the chunked-scan kernels (internal).
+// chunk_scan.hpp -- host-visible interface of the forward scan kernels (internal).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,12 +7,6 @@
 
 namespace linrec {
 
-// Steps per chunk held in registers by one workgroup row.
-constexpr int kChunkLen = 16;
-// Channels per workgroup (CL lanes x VEC channels per lane).
-constexpr int kGroupChannels = 16;
-
-enum { kModeFull = 0, kModeReduce = 1, kModeApply = 2 };
 enum { kKindWkv = 0, kKindReal = 1, kKindComplex = 2 };
 
 // Operands of each recurrence (device pointers, (B,T,C) row-major, C fastest).
@@ -37,21 +31,25 @@ struct CplxArgs {
     float* x;          // (B,T,C) complex64
 };
 
+// Launch geometry.  A workgroup of nw waves owns one time slab (nw chunks of L steps) of
+// one channel group (64 lanes x vec channels); workgroups are numbered slab-major, so a
+// slab's predecessors always have smaller block indices.
 struct ScanGeom {
     int64_t B, T, C;
-    int64_t ngrp;      // channel groups of kGroupChannels channels
-    int64_t nslab;     // time slabs per sequence (1: one workgroup walks the whole sequence)
-    int64_t slab_len;  // steps per slab, a multiple of the tile length
-    int mode;          // kMode*
-    void* ws_agg;      // (B, nslab, C) slab aggregates
-    void* ws_carry;    // (B, nslab, C) slab carries
+    int64_t ngrp;       // channel groups per batch row
+    int64_t nslab;      // slabs per sequence
+    uint64_t tag;       // per-call tag of the look-back flags (never 0)
+    int spin;           // polls of a predecessor's flag before recomputing its aggregate
+    uint64_t* flags;    // (B*ngrp*nslab) publication flags
+    void* rec_agg;      // (B*ngrp*nslab, 64*vec) slab aggregates
+    void* rec_incl;     // (B*ngrp*nslab, 64*vec) inclusive prefixes
 };
 
 struct ScanPlan {
-    int vec;       // channels per lane: 4 (2 for complex) or 1
-    int rows;      // chunks per tile: 64 or 16
-    int64_t nslab;
-    int64_t slab_len;
+    int vec;        // channels per lane (4, or 2 for complex; 1 for any C or alignment)
+    int nw;         // waves per workgroup (chunks per slab)
+    int L;          // steps per chunk
+    int64_t nslab;  // slabs per sequence
     size_t ws_bytes;
 };
 
@@ -59,5 +57,7 @@ hipError_t run_wkv_forward(const WkvArgs& A, const ScanGeom& g, const ScanPlan& 
 hipError_t run_scan_real(const RealArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
 hipError_t run_scan_complex(const CplxArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
 size_t agg_bytes(int kind);
+// Launch shapes that have kernels: (vec, nw, L) per kind.
+bool scan_shape_supported(int kind, int vec, int nw, int L);
 
 }  // namespace linrec

@@ -73,4 +73,59 @@ __device__ __forceinline__ void stg(float* __restrict__ p, const FV<N>& r) {
     }
 }
 
+// ---- buffer addressing ----------------------------------------------------------
+// Streaming tensors are addressed through a buffer resource per wave: a scalar base
+// pointer (uniform per wave), a 32-bit per-lane byte offset and a scalar per-step offset,
+// instead of one 64-bit address per load.  Accesses at or beyond num_records return 0
+// (loads) or are dropped (stores).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufNT = 2;  // cache policy: non-temporal (streamed once)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t nbytes) {
+    const int n = nbytes > 0x7fffffff ? 0x7fffffff : (nbytes < 0 ? 0 : (int)nbytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+template <int N>
+__device__ __forceinline__ FV<N> ldb(rsrc_t rs, unsigned voff, unsigned soff) {
+    FV<N> r;
+    if constexpr (N == 1) {
+        r.v[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kBufNT));
+    } else if constexpr (N == 2) {
+        const f32x2 t = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kBufNT));
+        r.v[0] = t.x; r.v[1] = t.y;
+    } else if constexpr (N == 4) {
+        const f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kBufNT));
+        r.v[0] = t.x; r.v[1] = t.y; r.v[2] = t.z; r.v[3] = t.w;
+    } else {
+        static_assert(N == 8, "unsupported vector width");
+        const f32x4 t0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kBufNT));
+        const f32x4 t1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, soff, kBufNT));
+        r.v[0] = t0.x; r.v[1] = t0.y; r.v[2] = t0.z; r.v[3] = t0.w;
+        r.v[4] = t1.x; r.v[5] = t1.y; r.v[6] = t1.z; r.v[7] = t1.w;
+    }
+    return r;
+}
+
+template <int N>
+__device__ __forceinline__ void stb(rsrc_t rs, unsigned voff, unsigned soff, const FV<N>& r) {
+    if constexpr (N == 1) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, r.v[0]), rs, voff, soff, kBufNT);
+    } else if constexpr (N == 2) {
+        const f32x2 t = {r.v[0], r.v[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, t), rs, voff, soff, kBufNT);
+    } else if constexpr (N == 4) {
+        const f32x4 t = {r.v[0], r.v[1], r.v[2], r.v[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), rs, voff, soff, kBufNT);
+    } else {
+        static_assert(N == 8, "unsupported vector width");
+        const f32x4 t0 = {r.v[0], r.v[1], r.v[2], r.v[3]};
+        const f32x4 t1 = {r.v[4], r.v[5], r.v[6], r.v[7]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t0), rs, voff, soff, kBufNT);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t1), rs, voff + 16, soff, kBufNT);
+    }
+}
+
 }  // namespace linrec

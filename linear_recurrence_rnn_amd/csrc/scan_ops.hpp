@@ -59,10 +59,15 @@ struct WkvOp {
     __device__ __forceinline__ static Agg identity() { return {0.f, 0.f, kEmpty}; }
     __device__ __forceinline__ static Agg init(const Args&, int64_t, int64_t, int64_t) { return identity(); }
 
+    static constexpr int kFloats = 1;  // floats per channel element
+    struct Res { rsrc_t k, v, y; };
+    __device__ __forceinline__ static Res res(const Args& A, int64_t base, int64_t nbytes) {
+        return {make_rsrc(A.k + base, nbytes), make_rsrc(A.v + base, nbytes), make_rsrc(A.y + base, nbytes)};
+    }
     template <int VEC>
-    __device__ __forceinline__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
-        const FV<VEC> k = ldg<VEC>(A.k + off);
-        const FV<VEC> v = ldg<VEC>(A.v + off);
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, unsigned soff, In (&in)[VEC]) {
+        const FV<VEC> k = ldb<VEC>(R.k, voff, soff);
+        const FV<VEC> v = ldb<VEC>(R.v, voff, soff);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {k.v[e] * kLog2e, v.v[e]};
     }
@@ -104,10 +109,17 @@ struct WkvOp {
         return {fmaf(s1.a, f1, s2.a * f2), fmaf(s1.b, f1, s2.b * f2), p};
     }
 
+    // The aggregate s extended by one step (the exact per-step update).
+    __device__ __forceinline__ static Agg step(const Chan& ch, const Agg& s, const In& x) {
+        const float q = ceilf(fmaxf(mag(s.p, s.b) - ch.om, x.kk));
+        const float f1 = fast_exp2((s.p - q) - ch.om), f2 = fast_exp2(x.kk - q);
+        return {fmaf(s.a, f1, x.v * f2), fmaf(s.b, f1, f2), q};
+    }
+
     template <int L, int VEC>
-    __device__ __forceinline__ static void run(const Args& A, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
-                               const In (&in)[L][VEC], const Local (&loc)[VEC], int n, int64_t off,
-                               int64_t C) {
+    __device__ __forceinline__ static void run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], const Local (&loc)[VEC], int n, unsigned voff,
+                               unsigned rowb) {
         float a[VEC], b[VEC], cs[VEC], us[VEC];
         bool fast[VEC];
 #pragma unroll
@@ -143,7 +155,7 @@ struct WkvOp {
                         a[e] = fmaf(up, vv, a[e]);
                         b[e] += up;
                     }
-                    stg<VEC>(A.y + off + (int64_t)j * C, y);
+                    stb<VEC>(R.y, voff, j * rowb, y);
                 }
             }
             return;
@@ -155,7 +167,7 @@ struct WkvOp {
 #pragma unroll
         for (int j = 0; j < L; ++j) {
             if (j < n) {
-                const FV<VEC> kr = ldg<VEC>(A.k + off + (int64_t)j * C);
+                const FV<VEC> kr = ldb<VEC>(R.k, voff, j * rowb);
                 FV<VEC> y;
     #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
@@ -169,7 +181,7 @@ struct WkvOp {
                     pb[e] = fmaf(pb[e], f1, f2);
                     pp[e] = q2;
                 }
-                stg<VEC>(A.y + off + (int64_t)j * C, y);
+                stb<VEC>(R.y, voff, j * rowb, y);
             }
         }
     }
@@ -196,10 +208,15 @@ struct RealOp {
         return {1.f, A.x0 ? A.x0[b * C + c] : 0.f};
     }
 
+    static constexpr int kFloats = 1;
+    struct Res { rsrc_t a, b, x; };
+    __device__ __forceinline__ static Res res(const Args& A, int64_t base, int64_t nbytes) {
+        return {make_rsrc(A.a + base, nbytes), make_rsrc(A.b + base, nbytes), make_rsrc(A.x + base, nbytes)};
+    }
     template <int VEC>
-    __device__ __forceinline__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
-        const FV<VEC> a = ldg<VEC>(A.a + off);
-        const FV<VEC> b = ldg<VEC>(A.b + off);
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, unsigned soff, In (&in)[VEC]) {
+        const FV<VEC> a = ldb<VEC>(R.a, voff, soff);
+        const FV<VEC> b = ldb<VEC>(R.b, voff, soff);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {a.v[e], b.v[e]};
     }
@@ -226,10 +243,14 @@ struct RealOp {
         return {s1.m * s2.m, fmaf(s2.m, s1.x, s2.x)};
     }
 
+    __device__ __forceinline__ static Agg step(const Chan&, const Agg& s, const In& x) {
+        return {s.m * x.a, fmaf(x.a, s.x, x.b)};
+    }
+
     template <int L, int VEC>
-    __device__ __forceinline__ static void run(const Args& A, const Chan (&)[VEC], const Agg (&cin)[VEC],
-                               const In (&in)[L][VEC], const Local (&)[VEC], int n, int64_t off,
-                               int64_t C) {
+    __device__ __forceinline__ static void run(const Res& R, const Chan (&)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
+                               unsigned rowb) {
         float x[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[e] = cin[e].x;
@@ -242,7 +263,7 @@ struct RealOp {
                     x[e] = fmaf(in[j][e].a, x[e], in[j][e].b);
                     o.v[e] = x[e];
                 }
-                stg<VEC>(A.x + off + (int64_t)j * C, o);
+                stb<VEC>(R.x, voff, j * rowb, o);
             }
         }
     }
@@ -293,9 +314,14 @@ struct CplxOp {
         return {1.f, 0.f, A.x0[2 * (b * C + c)], A.x0[2 * (b * C + c) + 1]};
     }
 
+    static constexpr int kFloats = 2;
+    struct Res { rsrc_t u, x; };
+    __device__ __forceinline__ static Res res(const Args& A, int64_t base, int64_t nbytes) {
+        return {make_rsrc(A.u + 2 * base, nbytes), make_rsrc(A.x + 2 * base, nbytes)};
+    }
     template <int VEC>
-    __device__ __forceinline__ static void load(const Args& A, int64_t off, In (&in)[VEC]) {
-        const FV<2 * VEC> t = ldg<2 * VEC>(A.u + 2 * off);
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, unsigned soff, In (&in)[VEC]) {
+        const FV<2 * VEC> t = ldb<2 * VEC>(R.u, voff, soff);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {t.v[2 * e], t.v[2 * e + 1]};
     }
@@ -328,6 +354,15 @@ struct CplxOp {
         return r;
     }
 
+    __device__ __forceinline__ static Agg step(const Chan& ch, const Agg& s, const In& x) {
+        Agg r;
+        r.mr = fmaf(s.mr, ch.lr, -s.mi * ch.li);
+        r.mi = fmaf(s.mr, ch.li, s.mi * ch.lr);
+        r.xr = fmaf(ch.lr, s.xr, fmaf(-ch.li, s.xi, x.r));
+        r.xi = fmaf(ch.lr, s.xi, fmaf(ch.li, s.xr, x.i));
+        return r;
+    }
+
     __device__ __forceinline__ static Agg combine(const Chan&, const Agg& s1, const Agg& s2, int64_t) {
         Agg r;
         r.mr = fmaf(s1.mr, s2.mr, -s1.mi * s2.mi);
@@ -338,9 +373,9 @@ struct CplxOp {
     }
 
     template <int L, int VEC>
-    __device__ __forceinline__ static void run(const Args& A, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
-                               const In (&in)[L][VEC], const Local (&)[VEC], int n, int64_t off,
-                               int64_t C) {
+    __device__ __forceinline__ static void run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
+                               unsigned rowb) {
         float xr[VEC], xi[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) { xr[e] = cin[e].xr; xi[e] = cin[e].xi; }
@@ -356,7 +391,7 @@ struct CplxOp {
                     o.v[2 * e] = xr[e];
                     o.v[2 * e + 1] = xi[e];
                 }
-                stg<2 * VEC>(A.x + 2 * (off + (int64_t)j * C), o);
+                stb<2 * VEC>(R.x, voff, j * rowb, o);
             }
         }
     }

@@ -128,9 +128,12 @@ def test_workspace_checks(lib):
 def test_workspace_sizes(lib):
     assert lib.wkv4_forward_workspace_size(0, 10, 10) == 0
     assert lib.wkv4_forward_workspace_size(-1, 10, 10) == 0
-    # Enough (batch x channel-group) workgroups: one pass, no workspace.
-    assert lib.wkv4_forward_workspace_size(8, 1024, 768) == 0
-    assert lib.linrec_scan_workspace_size(64, 4096, 256, 0) == 0
-    # A long single sequence needs slab carries.
-    assert lib.wkv4_forward_workspace_size(1, 1 << 16, 64) > 0
-    assert lib.linrec_scan_workspace_size(1, 1 << 16, 64, 0) > 0
+    # A sequence that fits one time slab needs no look-back records.
+    assert lib.wkv4_forward_workspace_size(1, 64, 32) == 0
+    assert lib.linrec_scan_workspace_size(3, 40, 500, 1) == 0
+    # Longer sequences need per-slab flags and records; more slabs need more.
+    w1 = lib.wkv4_forward_workspace_size(8, 1024, 768)
+    w2 = lib.wkv4_forward_workspace_size(8, 2048, 768)
+    assert 0 < w1 < w2
+    assert lib.linrec_scan_workspace_size(64, 4096, 256, 0) > 0
+    assert lib.linrec_scan_workspace_size(1, 1 << 16, 64, 1) > 0

@@ -201,26 +201,54 @@ def test_wkv_exact_path_matches_fast_path(L, monkeypatch, wid):
     assert rel_err(y_fast, y_exact.astype(np.float64)) <= 2 * TOL
 
 
-def test_wkv_forced_slabs(L, monkeypatch):
-    announce("wkv4_forward forced 7 slabs B=2 T=5000 C=48")
-    d = workloads.make_inputs(3, seed=11, shape=(2, 5000, 48))
-    ref = oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])
-    monkeypatch.setenv("LINREC_NSLAB", "7")
-    assert L.workspace_size("wkv4_forward", 2, 5000, 48) > 0
-    assert rel_err(gpu_wkv(L, d), ref) <= TOL
+SHAPES_NW_L = [("4", "16"), ("8", "8"), ("8", "16")]
 
 
-def test_wkv_rows_invariance_and_determinism(L, monkeypatch):
-    announce("wkv4_forward rows 16 vs 64, run twice B=3 T=2000 C=64")
-    d = workloads.make_inputs(2, seed=12, shape=(3, 2000, 64))
+@pytest.mark.parametrize("vec", ["4", "2", "1"])
+@pytest.mark.parametrize("nw,lc", SHAPES_NW_L, ids=["nw%s_L%s" % x for x in SHAPES_NW_L])
+def test_forward_launch_shapes(L, monkeypatch, nw, lc, vec):
+    # Every kernel shape (waves per slab x steps per chunk) against the oracle, with ragged
+    # slabs, partial channel groups and the scalar (vec 1) variant.
+    announce("forward launch shape nw=%s L=%s vec<=%s" % (nw, lc, vec))
+    monkeypatch.setenv("LINREC_NW", nw)
+    monkeypatch.setenv("LINREC_L", lc)
+    monkeypatch.setenv("LINREC_VEC", vec)
+    d = workloads.make_inputs(3, seed=11, shape=(2, 1000, 296))
+    assert rel_err(gpu_wkv(L, d), oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])) <= TOL
+    r = workloads.make_inputs(4, seed=11, shape=(3, 777, 260))
+    x0 = np.random.default_rng(3).standard_normal((3, 260)).astype(np.float32)
+    assert rel_err(host(L.scan_real(dev(r["a"]), dev(r["b"]), dev(x0))), oracle.scan_real(r["a"], r["b"], x0)) <= TOL
+    c = workloads.make_inputs(5, seed=11, shape=(2, 900, 130))
+    assert rel_err(host(L.scan_complex(dev(c["lam"]), dev(c["u"]))), oracle.scan_complex(c["lam"], c["u"])) <= TOL
+
+
+@pytest.mark.parametrize("spin", ["0", "1"])
+def test_lookback_recompute_path(L, monkeypatch, spin):
+    # With no (or one) poll of a predecessor's flag, the waiting wave recomputes the
+    # predecessor slab's aggregate from its inputs: results must not change.
+    announce("forward look-back with LINREC_SPIN=%s" % spin)
+    monkeypatch.setenv("LINREC_SPIN", spin)
+    d = workloads.make_inputs(3, seed=12, shape=(2, 1500, 512))
+    assert rel_err(gpu_wkv(L, d), oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])) <= TOL
+    r = workloads.make_inputs(4, seed=12, shape=(2, 1500, 256))
+    x0 = np.random.default_rng(4).standard_normal((2, 256)).astype(np.float32)
+    assert rel_err(host(L.scan_real(dev(r["a"]), dev(r["b"]), dev(x0))), oracle.scan_real(r["a"], r["b"], x0)) <= TOL
+    c = workloads.make_inputs(5, seed=12, shape=(1, 3000, 128))
+    xc0 = (np.ones((1, 128)) + 0.5j).astype(np.complex64)
+    assert rel_err(host(L.scan_complex(dev(c["lam"]), dev(c["u"]), dev(xc0))),
+                   oracle.scan_complex(c["lam"], c["u"], xc0)) <= TOL
+
+
+def test_forward_determinism_and_vec1(L, monkeypatch):
+    announce("wkv4_forward run twice; default width vs 4 channels per lane B=3 T=2000 C=256")
+    d = workloads.make_inputs(2, seed=12, shape=(3, 2000, 256))
     ref = oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])
-    monkeypatch.setenv("LINREC_ROWS", "16")
-    y16 = gpu_wkv(L, d)
-    monkeypatch.setenv("LINREC_ROWS", "64")
-    y64 = gpu_wkv(L, d)
-    y64b = gpu_wkv(L, d)
-    assert rel_err(y16, ref) <= TOL and rel_err(y64, ref) <= TOL
-    np.testing.assert_array_equal(y64, y64b)
+    y1 = gpu_wkv(L, d)
+    y2 = gpu_wkv(L, d)
+    np.testing.assert_array_equal(y1, y2)
+    monkeypatch.setenv("LINREC_VEC", "4")
+    y3 = gpu_wkv(L, d)
+    assert rel_err(y1, ref) <= TOL and rel_err(y3, ref) <= TOL
     g1 = gpu_wkv_bwd(L, workloads.make_inputs(3, seed=12, shape=(3, 700, 64)))
     g2 = gpu_wkv_bwd(L, workloads.make_inputs(3, seed=12, shape=(3, 700, 64)))
     for a, b in zip(g1, g2):
@@ -249,22 +277,6 @@ def test_scan_real_shapes(L, shape, with_x0):
     x0 = np.random.default_rng(1).standard_normal((shape[0], shape[2])).astype(np.float32) if with_x0 else None
     x = host(L.scan_real(dev(d["a"]), dev(d["b"]), None if x0 is None else dev(x0)))
     assert rel_err(x, oracle.scan_real(d["a"], d["b"], x0)) <= TOL
-
-
-@pytest.mark.parametrize("with_x0", [False, True])
-def test_scan_forced_slabs(L, monkeypatch, with_x0):
-    announce("scans forced 5 slabs x0=%s" % with_x0)
-    rng = np.random.default_rng(2)
-    monkeypatch.setenv("LINREC_NSLAB", "5")
-    d = workloads.make_inputs(4, seed=14, shape=(2, 3000, 20))
-    x0 = rng.standard_normal((2, 20)).astype(np.float32) if with_x0 else None
-    x = host(L.scan_real(dev(d["a"]), dev(d["b"]), None if x0 is None else dev(x0)))
-    assert rel_err(x, oracle.scan_real(d["a"], d["b"], x0)) <= TOL
-    d = workloads.make_inputs(5, seed=15, shape=(2, 3000, 20))
-    xc0 = (rng.standard_normal((2, 20)) + 1j * rng.standard_normal((2, 20))).astype(np.complex64) \
-        if with_x0 else None
-    x = host(L.scan_complex(dev(d["lam"]), dev(d["u"]), None if xc0 is None else dev(xc0)))
-    assert rel_err(x, oracle.scan_complex(d["lam"], d["u"], xc0)) <= TOL
 
 
 CPLX_SHAPES = [(1, 1, 2), (2, 777, 33), (3, 4096, 64), (1, 20000, 8)]
