@@ -70,7 +70,7 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
         p.nw = T <= 2048 ? 8 : 4;
         p.L = 16;
     } else if (kind == linrec::kKindReal) {
-        p.nw = 4;
+        p.nw = 8;
         p.L = 16;
     } else {
         p.nw = 8;
@@ -128,6 +128,20 @@ uint64_t next_tag() {
     return t ? t : 1;
 }
 
+// Backward plan for a vector width; LINREC_BWD_NW / LINREC_BWD_L override the slab shape.
+linrec::BwdPlan bwd_plan(int vec, int64_t B, int64_t T, int64_t C) {
+    return linrec::wkv_backward_plan(vec, B, T, C, (int)env_int("LINREC_BWD_NW", 0), (int)env_int("LINREC_BWD_L", 0));
+}
+
+size_t bwd_ws_bytes(int64_t B, int64_t T, int64_t C) { return bwd_plan(1, B, T, C).ws_bytes; }
+
+int spin_limit() {
+    // Polls (each ~128 cycles) before a missing predecessor aggregate is recomputed;
+    // LINREC_SPIN overrides it (0 forces the recompute path, for tests).
+    const char* spin = std::getenv("LINREC_SPIN");
+    return (spin && *spin) ? (int)std::strtol(spin, nullptr, 10) : 4096;
+}
+
 linrec::ScanGeom geom_of(int kind, const linrec::ScanPlan& p, int64_t B, int64_t T, int64_t C, void* ws) {
     linrec::ScanGeom g{};
     g.B = B;
@@ -137,10 +151,7 @@ linrec::ScanGeom geom_of(int kind, const linrec::ScanPlan& p, int64_t B, int64_t
     g.ngrp = ceil_div(C, cw);
     g.nslab = p.nslab;
     g.tag = next_tag();
-    // Polls (each ~128 cycles) before a missing predecessor aggregate is recomputed;
-    // LINREC_SPIN overrides it (0 forces the recompute path, for tests).
-    const char* spin = std::getenv("LINREC_SPIN");
-    g.spin = (spin && *spin) ? (int)std::strtol(spin, nullptr, 10) : 4096;
+    g.spin = spin_limit();
     const int64_t nwg = B * g.ngrp * g.nslab;
     g.flags = reinterpret_cast<uint64_t*>(ws);
     char* rec = (char*)ws + align256((size_t)nwg * 8);
@@ -192,7 +203,7 @@ LINREC_API size_t linrec_scan_workspace_size(int64_t B, int64_t T, int64_t C, in
 
 LINREC_API size_t wkv4_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
     if (B < 0 || T < 0 || C < 0 || B == 0 || T == 0 || C == 0) return 0;
-    return linrec::wkv_backward_plan(B, T, C).ws_bytes;
+    return bwd_ws_bytes(B, T, C);
 }
 
 LINREC_API int wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
@@ -275,13 +286,18 @@ LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, co
     const void* ptrs[] = {w, u, k, v, gy, gw, gu, gk, gv};
     for (const void* p : ptrs)
         if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
-    linrec::BwdPlan p = linrec::wkv_backward_plan(B, T, C);
+    const linrec::BwdPlan p = bwd_plan(1, B, T, C);
     if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
-    p.vec = (C % 2 == 0 && aligned(k, 8) && aligned(v, 8) && aligned(gy, 8) && aligned(gk, 8) &&
-             aligned(gv, 8))
-                ? 2
-                : 1;
+    linrec::BwdGeom g{};
+    g.B = B;
+    g.T = T;
+    g.C = C;
+    g.ngrp = ceil_div(C, 64 * (int64_t)p.vec);
+    g.nslab = p.nslab;
+    g.spin = spin_limit();
+    g.tag_f = next_tag();
+    g.tag_r = next_tag();
+    linrec::wkv_backward_layout(p, B, C, workspace, g);
     const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv};
-    return hip_status(linrec::run_wkv_backward(A, B, T, C, p, workspace, (hipStream_t)stream),
-                      "wkv4_backward launch");
+    return hip_status(linrec::run_wkv_backward(A, g, p, (hipStream_t)stream), "wkv4_backward launch");
 }

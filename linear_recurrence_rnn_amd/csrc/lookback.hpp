@@ -1,0 +1,177 @@
+// lookback.hpp -- decoupled look-back over the slabs of one sequence (device code, internal).
+//
+// A sequence is cut into slabs that the recurrence visits in a fixed order, the chain
+// (q = 0 first: time order for a forward scan, reverse time order for a backward one).  Each
+// slab publishes its aggregate (AGG), then -- once it knows its carry-in -- its inclusive
+// prefix (INCL).  A slab's carry is the nearest published INCL folded with the aggregates
+// of the slabs after it, in chain order: the association a strictly chained scan would use,
+// so the result does not depend on timing.
+//
+// Records are written and read with device-scope relaxed atomics, which the hardware keeps
+// coherent across the XCDs' L2 caches (they write through), and a publication flag is
+// stored only after all of the wave's record stores have completed (s_waitcnt).  This
+// avoids agent-scope release/acquire fences, whose L2 writeback or invalidation serialises
+// per XCD.  Records are stored field-major -- dword i of entry (e, lane) of slab q at
+// ((q * ND + i) * VEC + e) * 64 + lane -- so each of those one-dword stores covers 256
+// contiguous bytes and writes whole lines through to memory.
+//
+// Every wait is bounded: a slab whose flag has not appeared after `spin` polls is
+// recomputed from its inputs by the waiting wave.  Flags carry a per-call tag, so stale
+// flags from earlier calls read as "not published" and the workspace needs no clearing.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace linrec {
+
+constexpr uint64_t kStateAgg = 1;  // flag = tag * 4 + state
+constexpr uint64_t kStateIncl = 2;
+
+template <class Agg>
+constexpr int kDwords = (int)(sizeof(Agg) / 4);
+
+// This wave's VEC entries per lane of slab q's record (rec: dwords, field-major).
+template <int VEC, class Agg>
+__device__ __forceinline__ void store_record(uint32_t* rec, int64_t q, int lane, const Agg (&x)[VEC]) {
+    static_assert(sizeof(Agg) % 4 == 0, "record must be whole dwords");
+    constexpr int ND = kDwords<Agg>;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        uint32_t w[ND];
+        __builtin_memcpy(w, &x[e], sizeof(Agg));
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+            __hip_atomic_store(rec + ((q * ND + i) * VEC + e) * 64 + lane, w[i], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <int VEC, class Agg>
+__device__ __forceinline__ void load_record(const uint32_t* rec, int64_t q, int lane, Agg (&x)[VEC]) {
+    constexpr int ND = kDwords<Agg>;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        uint32_t w[ND];
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+            w[i] = __hip_atomic_load(rec + ((q * ND + i) * VEC + e) * 64 + lane, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_memcpy(&x[e], w, sizeof(Agg));
+    }
+}
+
+// All of this wave's memory operations have completed (compiler and hardware ordering).
+__device__ __forceinline__ void wait_memory() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wave-uniform copy of lane 0's 64-bit value (readfirstlane moves 32 bits).
+__device__ __forceinline__ uint64_t first_lane_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t poll_flag(const uint64_t* f, uint64_t tag, int spin) {
+    uint64_t v = 0;
+    for (int it = 0; it < spin; ++it) {
+        v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((v >> 2) == tag) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return v;
+}
+
+// The records of one sequence's chain: slab q owns flags[q] and the 64 * VEC entries of
+// agg and incl at slab index q (dword arrays, field-major).
+template <class Agg>
+struct Chain {
+    uint64_t* flags;
+    uint32_t* agg;
+    uint32_t* incl;
+    uint64_t tag;
+    int spin;
+};
+
+// Publish this wave's VEC records per lane for slab q as its aggregate or inclusive prefix.
+template <int VEC, class Agg>
+__device__ __forceinline__ void publish(const Chain<Agg>& ch, int64_t q, int lane, const Agg (&x)[VEC],
+                                        bool inclusive) {
+    store_record<VEC>(inclusive ? ch.incl : ch.agg, q, lane, x);
+    wait_memory();
+    if (lane == 0)
+        __hip_atomic_store(ch.flags + q, ch.tag * 4 + (inclusive ? kStateIncl : kStateAgg), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Carry into chain slab q, computed by one whole wave.  On entry `carry` holds the state
+// before chain slab 0; on return, the state before slab q:
+//   fold(carry, x, j)    carry <- carry followed by slab j whose aggregate is x;
+//   recompute(j, x)      x <- slab j's aggregate, computed from its inputs.
+// Phase A: lane i inspects slab hi-1-i, 64 predecessors per round trip, until a round finds
+// a published inclusive prefix (the nearest one, j0) or slab 0 is passed (j0 = -1); lanes
+// remember which slabs had published.  Phase B: carry = INCL_j0 (or the entry state) folded
+// with the aggregates of slabs j0+1 .. q-1, fetched KB slabs at a time (issued together,
+// then folded in order) so the fold costs one memory round trip per KB slabs.
+template <int VEC, int KB, class Agg, class Fold, class Recompute>
+__device__ __forceinline__ void look_back(const Chain<Agg>& ch, int64_t q, int lane, Agg (&carry)[VEC],
+                                          Fold&& fold, Recompute&& recompute) {
+    constexpr int kWin = 16;  // windows whose publication masks are kept
+    uint64_t pub[kWin];
+#pragma unroll
+    for (int x = 0; x < kWin; ++x) pub[x] = 0;
+    int64_t j0 = -1;
+    int nwin = 0;
+    for (int64_t hi = q; hi > 0; hi -= 64, ++nwin) {
+        const int64_t j = hi - 1 - lane;
+        const uint64_t f = (j >= 0) ? poll_flag(ch.flags + j, ch.tag, ch.spin) : 0;
+        const uint64_t incl_mask = __ballot(j >= 0 && f == ch.tag * 4 + kStateIncl);
+        const uint64_t pub_mask = __ballot(j >= 0 && (f >> 2) == ch.tag);
+#pragma unroll
+        for (int x = 0; x < kWin; ++x)
+            if (x == nwin) pub[x] = pub_mask;
+        if (incl_mask) {
+            j0 = hi - 1 - (int64_t)(__ffsll((long long)incl_mask) - 1);
+            break;
+        }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // record loads stay after the polls
+    if (j0 >= 0) load_record<VEC>(ch.incl, j0, lane, carry);
+    for (int64_t j = j0 + 1; j < q; j += KB) {
+        Agg xb[KB][VEC];
+        bool pubb[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int64_t jj = j + k;
+            pubb[k] = false;
+            if (jj < q) {
+                const int64_t back = q - 1 - jj;  // lane index of slab jj in its window
+                const int x = (int)(back >> 6);
+                if (x < kWin) {
+                    uint64_t m = 0;
+#pragma unroll
+                    for (int y = 0; y < kWin; ++y)
+                        if (y == x) m = pub[y];
+                    pubb[k] = (m >> (back & 63)) & 1;
+                } else {
+                    const uint64_t f = (lane == 0) ? poll_flag(ch.flags + jj, ch.tag, ch.spin) : 0;
+                    pubb[k] = (first_lane_u64(f) >> 2) == ch.tag;
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                }
+                if (pubb[k]) load_record<VEC>(ch.agg, jj, lane, xb[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int64_t jj = j + k;
+            if (jj < q) {
+                if (!pubb[k]) recompute(jj, xb[k]);  // not published in time
+                fold(carry, xb[k], jj);
+            }
+        }
+    }
+}
+
+}  // namespace linrec

@@ -19,16 +19,39 @@ struct WkvBwdArgs {
     float* gv;        // (B,T,C)
 };
 
+// Launch geometry of the backward.  Both streaming kernels cut each sequence into slabs of
+// nw chunks of L steps of one channel group (64 lanes x vec channels).  The state kernel
+// visits slabs in time order and publishes the forward sums at every slab end; the gradient
+// kernel visits them in reverse time order.  Workgroups are numbered chain-major.
+struct BwdGeom {
+    int64_t B, T, C;
+    int64_t ngrp;   // channel groups per batch row
+    int64_t nslab;  // slabs per sequence
+    int spin;       // polls of a predecessor's flag before recomputing its aggregate
+    uint64_t tag_f, tag_r;  // per-call tags of the two kernels' flags (never 0)
+    uint64_t* flags_f;      // (B*ngrp*nslab) forward-chain flags
+    void* agg_f;            // (B*ngrp*nslab, 64*vec) forward aggregates
+    void* incl_f;           // (B*ngrp*nslab, 64*vec) forward inclusive prefixes
+    uint64_t* flags_r;      // reverse-chain flags, records indexed by chain position
+    void* agg_r;
+    void* incl_r;
+    double* part;           // (B, C, 2) dL/dw, dL/du of each batch row
+};
+
 struct BwdPlan {
-    int vec;         // channels per lane: 2 or 1
-    int64_t ntiles;  // tiles of the time axis
-    size_t ckpt_bytes;
+    int vec;        // channels per lane (1)
+    int nw;         // waves per workgroup (chunks per slab)
+    int L;          // steps per chunk
+    int64_t nslab;  // slabs per sequence
     size_t ws_bytes;
 };
 
-BwdPlan wkv_backward_plan(int64_t B, int64_t T, int64_t C);
-hipError_t run_wkv_backward(const WkvBwdArgs& A, int64_t B, int64_t T, int64_t C, const BwdPlan& p,
-                            void* ws, hipStream_t st);
+// Plan (nw, L from the defaults or the overrides, when a kernel of that shape exists).
+BwdPlan wkv_backward_plan(int vec, int64_t B, int64_t T, int64_t C, int nw_override, int L_override);
+// Workspace layout of a plan: fills the pointers of g from ws.
+void wkv_backward_layout(const BwdPlan& p, int64_t B, int64_t C, void* ws, BwdGeom& g);
+bool bwd_shape_supported(int vec, int nw, int L);
+hipError_t run_wkv_backward(const WkvBwdArgs& A, const BwdGeom& g, const BwdPlan& p, hipStream_t st);
 // Writes zeros to gw and gu (C floats each): the sums over an empty batch or sequence.
 hipError_t run_zero_wu(float* gw, float* gu, int64_t C, hipStream_t st);
 

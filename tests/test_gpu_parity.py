@@ -239,6 +239,39 @@ def test_lookback_recompute_path(L, monkeypatch, spin):
                    oracle.scan_complex(c["lam"], c["u"], xc0)) <= TOL
 
 
+BWD_SHAPES_NW_L = [("3", "16"), ("4", "16"), ("7", "8"), ("8", "8"), ("7", "16")]
+
+
+@pytest.mark.parametrize("nw,lc", BWD_SHAPES_NW_L, ids=["nw%s_L%s" % x for x in BWD_SHAPES_NW_L])
+def test_backward_launch_shapes(L, monkeypatch, nw, lc):
+    # Every backward kernel shape against the oracle: ragged last slab, a partial channel
+    # group, and a sequence that fits one slab.
+    announce("backward launch shape nw=%s L=%s" % (nw, lc))
+    monkeypatch.setenv("LINREC_BWD_NW", nw)
+    monkeypatch.setenv("LINREC_BWD_L", lc)
+    for shape in [(2, 1001, 150), (3, 40, 70)]:
+        d = workloads.make_inputs(3, seed=13, shape=shape)
+        check_bwd(gpu_wkv_bwd(L, d), oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+
+
+@pytest.mark.parametrize("spin", ["0", "1"])
+def test_backward_lookback_recompute_path(L, monkeypatch, spin):
+    # With no (or one) poll, both the forward-state chain and the reverse chain recompute
+    # the records of slabs that have not published from their inputs.
+    announce("backward look-back with LINREC_SPIN=%s" % spin)
+    monkeypatch.setenv("LINREC_SPIN", spin)
+    d = workloads.make_inputs(3, seed=14, shape=(2, 1300, 130))
+    d["k"][1, 600, 7] = 140.0
+    check_bwd(gpu_wkv_bwd(L, d), oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+
+
+def test_backward_long_single_sequence(L):
+    # Many slabs in one chain (look-back windows of more than 64 slabs).
+    announce("wkv4_backward B=1 T=20000 C=64")
+    d = workloads.make_inputs(3, seed=15, shape=(1, 20000, 64))
+    check_bwd(gpu_wkv_bwd(L, d), oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+
+
 def test_forward_determinism_and_vec1(L, monkeypatch):
     announce("wkv4_forward run twice; default width vs 4 channels per lane B=3 T=2000 C=256")
     d = workloads.make_inputs(2, seed=12, shape=(3, 2000, 256))
