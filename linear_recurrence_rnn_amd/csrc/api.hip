@@ -297,6 +297,7 @@ LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, co
     g.spin = spin_limit();
     g.tag_f = next_tag();
     g.tag_r = next_tag();
+    g.exact_only = env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0;
     linrec::wkv_backward_layout(p, B, C, workspace, g);
     const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv};
     return hip_status(linrec::run_wkv_backward(A, g, p, (hipStream_t)stream), "wkv4_backward launch");

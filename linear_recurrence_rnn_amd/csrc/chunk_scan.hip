@@ -115,6 +115,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     const Chain<Agg> chn{g.flags + gi * g.nslab,
                          reinterpret_cast<uint32_t*>(g.rec_agg) + gi * g.nslab * (CW * kDwords<Agg>),
                          reinterpret_cast<uint32_t*>(g.rec_incl) + gi * g.nslab * (CW * kDwords<Agg>), g.tag, g.spin};
+    const uint64_t first = prefetch_window(chn, s, lane);  // overlaps the fold below
     const bool has_succ = s + 1 < g.nslab;
     // Slab aggregate; sh[x] becomes the chunks before x combined (x >= 1).
     Agg mine[VEC], carry[VEC];
@@ -149,7 +150,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
         }
     };
     constexpr int KB = VEC >= 4 ? 2 : (VEC == 2 ? 4 : 8);
-    look_back<VEC, KB>(chn, s, lane, carry, fold, recompute);
+    look_back<VEC, KB>(chn, s, lane, carry, fold, recompute, first);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) sh_carry[lane * VEC + e] = carry[e];
     __syncthreads();  // B2: the compute waves re-run while the inclusive prefix is published

@@ -110,14 +110,23 @@ __device__ __forceinline__ void publish(const Chain<Agg>& ch, int64_t q, int lan
 // before chain slab 0; on return, the state before slab q:
 //   fold(carry, x, j)    carry <- carry followed by slab j whose aggregate is x;
 //   recompute(j, x)      x <- slab j's aggregate, computed from its inputs.
+// `first` is the optional result of prefetch_window for the first round.
 // Phase A: lane i inspects slab hi-1-i, 64 predecessors per round trip, until a round finds
 // a published inclusive prefix (the nearest one, j0) or slab 0 is passed (j0 = -1); lanes
 // remember which slabs had published.  Phase B: carry = INCL_j0 (or the entry state) folded
 // with the aggregates of slabs j0+1 .. q-1, fetched KB slabs at a time (issued together,
 // then folded in order) so the fold costs one memory round trip per KB slabs.
+// One relaxed read of the flag of slab q-1-lane (the first look-back window), issued early
+// so that its round trip overlaps other work; look_back takes it as `first`.
+template <class Agg>
+__device__ __forceinline__ uint64_t prefetch_window(const Chain<Agg>& ch, int64_t q, int lane) {
+    const int64_t j = q - 1 - lane;
+    return j >= 0 ? __hip_atomic_load(ch.flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+}
+
 template <int VEC, int KB, class Agg, class Fold, class Recompute>
 __device__ __forceinline__ void look_back(const Chain<Agg>& ch, int64_t q, int lane, Agg (&carry)[VEC],
-                                          Fold&& fold, Recompute&& recompute) {
+                                          Fold&& fold, Recompute&& recompute, uint64_t first = 0) {
     constexpr int kWin = 16;  // windows whose publication masks are kept
     uint64_t pub[kWin];
 #pragma unroll
@@ -126,7 +135,9 @@ __device__ __forceinline__ void look_back(const Chain<Agg>& ch, int64_t q, int l
     int nwin = 0;
     for (int64_t hi = q; hi > 0; hi -= 64, ++nwin) {
         const int64_t j = hi - 1 - lane;
-        const uint64_t f = (j >= 0) ? poll_flag(ch.flags + j, ch.tag, ch.spin) : 0;
+        // A flag already seen published in the prefetched first window is final.
+        const bool have = nwin == 0 && (first >> 2) == ch.tag;
+        const uint64_t f = (j >= 0) ? (have ? first : poll_flag(ch.flags + j, ch.tag, ch.spin)) : 0;
         const uint64_t incl_mask = __ballot(j >= 0 && f == ch.tag * 4 + kStateIncl);
         const uint64_t pub_mask = __ballot(j >= 0 && (f >> 2) == ch.tag);
 #pragma unroll

@@ -31,6 +31,8 @@
 // unpacked float32 FMA.
 // Every sum over slabs is a fold in chain order (look-back), and dL/dw, dL/du are summed over
 // the batch in ascending row order: the results do not depend on scheduling.
+#include <atomic>
+
 #include "device_common.hpp"
 #include "lookback.hpp"
 #include "wkv_backward.hpp"
@@ -83,18 +85,81 @@ __device__ __forceinline__ Fwd fwd_chunk(float om, const float (&kk)[L][VEC], co
         m[j] = (j < n) ? fmaf(-(float)(n - 1 - j), om, kk[j][e]) : kEmpty;
         mx = fmaxf(mx, m[j]);
     }
-    Fwd s = fwd_identity();
-    s.p = ceilf(mx);
+    const float p = ceilf(mx);
+    // Sums of at most L terms in float32; the carries they feed are float64.
+    float a = 0.f, b = 0.f, ad = 0.f, bd = 0.f;
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-        const double f = fast_exp2(m[j] - s.p);  // 0 for the unused slots
-        const double fd = f * (double)max(n - 1 - j, 0);
-        s.a = fma(f, (double)vv[j][e], s.a);
-        s.b += f;
-        s.ad = fma(fd, (double)vv[j][e], s.ad);
-        s.bd += fd;
+        const float f = fast_exp2(m[j] - p);  // 0 for the unused slots
+        const float fd = f * (float)max(n - 1 - j, 0);
+        a = fmaf(f, vv[j][e], a);
+        b += f;
+        ad = fmaf(fd, vv[j][e], ad);
+        bd += fd;
     }
-    return s;
+    return {a, b, ad, bd, p};
+}
+
+// As fwd_chunk, for one channel per lane, keeping the weights: g_j = 2^{m_j - p} replaces
+// kk_j, and m0 = m_0 - p (log2 of the first weight).
+template <int L>
+__device__ __forceinline__ Fwd fwd_chunk_keep(float om, float (&kk)[L], const float (&vv)[L], int n, float& m0) {
+    m0 = kEmpty;
+    if (n <= 0) return fwd_identity();
+    float m[L];
+    float mx = kEmpty;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        m[j] = (j < n) ? fmaf(-(float)(n - 1 - j), om, kk[j]) : kEmpty;
+        mx = fmaxf(mx, m[j]);
+    }
+    const float p = ceilf(mx);
+    m0 = m[0] - p;
+    float a = 0.f, b = 0.f, ad = 0.f, bd = 0.f;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const float gj = fast_exp2(m[j] - p);  // 0 for the unused slots
+        kk[j] = gj;
+        const float fd = gj * (float)max(n - 1 - j, 0);
+        a = fmaf(gj, vv[j], a);
+        b += gj;
+        ad = fmaf(fd, vv[j], ad);
+        bd += fd;
+    }
+    return {a, b, ad, bd, p};
+}
+
+// Frame of one chunk for the gradient kernel's fast path.  With the chunk's weights
+// g_j = 2^{m_j - p} and an INTEGER frame exponent F0, the sums are carried as
+//   A~_j = A_{t0+j} 2^{j om - F0}   (B~, A'~, B'~ likewise),
+// which decay with the recurrence, so that
+//   A~_{j+1} = A~_j + us g_j v_j,  B~_{j+1} = B~_j + us g_j,  A'~_{j+1} = A'~_j + A~_j,
+//   the bonus term of step j is cur_j = cs g_j,  D~_j = B~_j + cur_j,
+// with us = 2^{p + n om - F0} and cs = 2^{mu + p + (n-1) om - F0}.  In the same frame the
+// reverse sums lose their decay too: c_t eps^{t-t0} = (g_t / D~_j) 2^{-F0}, and
+//   alpha_s G_s = g_j us (sum_{j' > j} g_{j'} / D~_{j'} + X),   X = G_end 2^{F0 - n om} (carry),
+// so the reverse takes no exponential at all.  F0 >= p0 + frexp_exp(b0) and
+// >= p + lift + (n-1) om keep every term <= ~1; the carry scale 2^{p0 - F0} is exact.
+struct ChunkFrame { float F0, cf, cs, us; bool fast; };
+
+constexpr float kBwdFastLo = -60.f;  // smallest log2 of D~ the fast path accepts
+constexpr float kBwdGradMax = 0x1p60f;  // largest |dL/dy| the fast path accepts
+
+__device__ __forceinline__ ChunkFrame chunk_frame(float om, float mu, float lift, const Fwd& cin, float p, float m0,
+                                                  int n, float gmax, bool allow) {
+    const Split d1 = mul_split((float)(n - 1), om);
+    const Split dn = mul_split((float)n, om);
+    const float fe = (float)__builtin_amdgcn_frexp_expf((float)cin.b);
+    ChunkFrame f;
+    f.F0 = fmaxf(cin.p + fe, ceilf((p + lift) + d1.hi));
+    f.cf = fast_exp2(cin.p - f.F0);
+    const float ls = ((p - f.F0) + d1.hi) + d1.lo;
+    f.cs = fast_exp2(ls + mu);
+    f.us = fast_exp2(((p - f.F0) + dn.hi) + dn.lo);
+    const float carry_lo = ((cin.p - f.F0) + fe) - 1.f;  // B~_0 >= 2^carry_lo
+    const float cur_lo = (m0 + ls) + mu;                  // log2 of cur_0
+    f.fast = allow && fmaxf(carry_lo, cur_lo) >= kBwdFastLo && gmax < kBwdGradMax;
+    return f;
 }
 
 // The forward sums advanced past one step (kj = k log2 e).
@@ -184,20 +249,13 @@ __device__ __forceinline__ void load_chan(const WkvBwdArgs& A, int64_t c0, bool 
     }
 }
 
-// The forward-state chain of sequence gi (channel group of one batch row).
-template <int VEC>
-__device__ __forceinline__ Chain<Fwd> fwd_chain(const BwdGeom& g, int64_t gi) {
-    constexpr int64_t per = 64 * VEC * kDwords<Fwd>;  // dwords per slab record
-    return {g.flags_f + gi * g.nslab, reinterpret_cast<uint32_t*>(g.agg_f) + gi * g.nslab * per,
-            reinterpret_cast<uint32_t*>(g.incl_f) + gi * g.nslab * per, g.tag_f, g.spin};
-}
-
-// Forward sums at the start of slab s: the state kernel's inclusive prefix of slab s-1.
+// Forward sums at the start of slab s: written by the state kernel at the end of slab s-1.
 template <int VEC>
 __device__ __forceinline__ void fwd_carry_in(const BwdGeom& g, int64_t gi, int64_t s, int lane, bool active,
                                              Fwd (&x)[VEC]) {
+    constexpr int64_t per = 64 * VEC * kDwords<Fwd>;  // dwords per slab record
     if (s > 0 && active) {
-        load_record<VEC>(fwd_chain<VEC>(g, gi).incl, s - 1, lane, x);
+        load_record<VEC>(reinterpret_cast<const uint32_t*>(g.incl_f) + gi * g.nslab * per, s - 1, lane, x);
     } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[e] = fwd_identity();
@@ -211,92 +269,164 @@ __device__ __forceinline__ int chunk_len(int x, int slab_n) {
 }
 
 // ------------------------------------------------------------------------------------
-// State kernel: forward sums at the end of slabs 0 .. nslab-2.  Waves 0 .. NW-1 reduce one
-// chunk each; wave NW (the coordinator) folds the chunks in order, publishes the slab's
-// aggregate, looks back over the earlier slabs and publishes the inclusive prefix.
+// State kernel: the forward sums at the end of slabs 0 .. nslab-2 (the gradient kernel's
+// slabs, "fine" slabs of SLAB = NW * L steps), for one channel per lane.  Persistent.
+//
+// An item is kStateFine consecutive fine slabs of one sequence; items form a coarse chain
+// with its own decoupled look-back.  Compute wave w streams fine slab w of the item in
+// L-step chunks (the loads of the next chunk are issued before the current one is reduced)
+// and folds it into the slab's sums; the coordinator folds the slabs into the item's
+// aggregate, publishes it, looks back over the earlier items and, from the carry, writes the
+// sums at every fine slab end and publishes the item's inclusive prefix.  The grid holds
+// only workgroups that are resident together; workgroup i takes items i, i + grid, ... in
+// chain-major order, so an item's predecessors come earlier in every workgroup's sequence.
+// LDS is double-buffered between the two roles, which meet at one barrier per item.
 // ------------------------------------------------------------------------------------
-template <int VEC, int NW, int L>
-__global__ __launch_bounds__(64 * (NW + 1)) void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
-    constexpr int CW = 64 * VEC;
+constexpr int kStateFine = 7;
+
+// As fwd_chunk, for one channel per lane (kk = k log2 e).
+template <int L>
+__device__ __forceinline__ Fwd fwd_chunk1(float om, const float (&kk)[L], const float (&vv)[L], int n) {
+    if (n <= 0) return fwd_identity();
+    float m[L];
+    float mx = kEmpty;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        m[j] = (j < n) ? fmaf(-(float)(n - 1 - j), om, kk[j]) : kEmpty;
+        mx = fmaxf(mx, m[j]);
+    }
+    const float p = ceilf(mx);
+    float a = 0.f, b = 0.f, ad = 0.f, bd = 0.f;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const float f = fast_exp2(m[j] - p);
+        const float fd = f * (float)max(n - 1 - j, 0);
+        a = fmaf(f, vv[j], a);
+        b += f;
+        ad = fmaf(fd, vv[j], ad);
+        bd += fd;
+    }
+    return {a, b, ad, bd, p};
+}
+
+template <int NW, int L>
+__global__ __launch_bounds__(64 * (kStateFine + 1)) void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
     constexpr int SLAB = NW * L;
-    __shared__ Fwd shf[NW][CW];
+    constexpr int F = kStateFine;
+    constexpr int kRec = 64 * kDwords<Fwd>;  // dwords per slab record
+    __shared__ Fwd shf[2][F][64];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int64_t G = g.B * g.ngrp;
-    const int64_t s = (int64_t)blockIdx.x / G;  // slab (time order), s < nslab - 1: always full
-    const int64_t gi = (int64_t)blockIdx.x - s * G;
-    const int64_t b = gi / g.ngrp, grp = gi - b * g.ngrp;
-    const int64_t c0 = grp * CW + (int64_t)lane * VEC;
-    const bool active = c0 < g.C;  // C is a multiple of VEC
-
-    float om[VEC], mu[VEC];
-    load_chan<VEC>(A, c0, active, om, mu);
-
+    const int64_t nfine = g.nslab - 1;             // fine slabs whose end state is needed
+    const int64_t nitem = (nfine + F - 1) / F;     // coarse chain length
+    const int64_t items = G * nitem;
     const unsigned rowb = (unsigned)(g.C * 4);
-    const unsigned voff = (unsigned)(lane * VEC * 4);
+    const unsigned voff = (unsigned)(lane * 4);
     const int64_t total = g.B * g.T * g.C;
-    if (w < NW) {
-        const int n = active ? L : 0;
-        const int64_t base = (b * g.T + s * SLAB + (int64_t)w * L) * g.C + grp * CW;
-        const rsrc_t rk = make_rsrc(A.k + base, (total - base) * 4), rv = make_rsrc(A.v + base, (total - base) * 4);
-        float kk[L][VEC], vv[L][VEC];
+    struct Item { int64_t q, gi, b, grp, c0; bool active; };
+    auto item_of = [&](int64_t u) {
+        Item it;
+        it.q = u / G;
+        it.gi = u - it.q * G;
+        it.b = it.gi / g.ngrp;
+        it.grp = it.gi - it.b * g.ngrp;
+        it.c0 = it.grp * 64 + lane;
+        it.active = it.c0 < g.C;
+        return it;
+    };
+
+    if (w < F) {
+        // This workgroup's items are u_i = blockIdx + i * grid; the wave walks the chunks of
+        // its fine slab in each, t = i * NW + c.
+        const int64_t my_items = blockIdx.x < items ? (items - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+        const int64_t nt = my_items * NW;
+        float kk[2][L], vv[2][L], wr[2];
+        auto issue = [&](int64_t t, int bs) {
+            const Item it = item_of((int64_t)blockIdx.x + (t / NW) * gridDim.x);
+            const int c = (int)(t % NW);
+            const int64_t f = it.q * F + w;
+            const bool valid = it.active && f < nfine;
+            const int64_t base = (it.b * g.T + f * SLAB + (int64_t)c * L) * g.C + it.grp * 64;
+            const rsrc_t rk = make_rsrc(A.k + base, (total - base) * 4), rv = make_rsrc(A.v + base, (total - base) * 4);
+            wr[bs] = it.active ? A.w[it.c0] : 0.f;
 #pragma unroll
-        for (int j = 0; j < L; ++j) {
-            FV<VEC> kt{}, vt{};
-            if (n > 0) {
-                kt = ldb<VEC>(rk, voff, j * rowb);
-                vt = ldb<VEC>(rv, voff, j * rowb);
+            for (int j = 0; j < L; ++j) {
+                kk[bs][j] = valid ? ldb<1>(rk, voff, j * rowb).v[0] : 0.f;
+                vv[bs][j] = valid ? ldb<1>(rv, voff, j * rowb).v[0] : 0.f;
             }
+        };
+        Fwd acc = fwd_identity();
+        int ib = 0;
+        auto step = [&](int64_t t, int bs) {
+            const Item it = item_of((int64_t)blockIdx.x + (t / NW) * gridDim.x);
+            const int c = (int)(t % NW);
+            const bool valid = it.active && it.q * F + w < nfine;
+            const float om = fminf(wr[bs] * kLog2e, kMaxOm);
+            float kl[L];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                kk[j][e] = kt.v[e] * kLog2e;
-                vv[j][e] = vt.v[e];
+            for (int j = 0; j < L; ++j) kl[j] = kk[bs][j] * kLog2e;
+            const Fwd chunk = fwd_chunk1<L>(om, kl, vv[bs], valid ? L : 0);
+            if (t + 1 < nt) issue(t + 1, bs ^ 1);
+            acc = (c == 0) ? chunk : fwd_combine(om, acc, chunk, L);
+            if (c == NW - 1) {
+                shf[ib][w][lane] = acc;
+                __syncthreads();  // the item's fine-slab sums are in shf[ib]
+                ib ^= 1;
             }
+        };
+        if (nt > 0) issue(0, 0);
+        for (int64_t t = 0; t < nt; t += 2) {
+            step(t, 0);
+            if (t + 1 < nt) step(t + 1, 1);
         }
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) shf[w][lane * VEC + e] = fwd_chunk<L, VEC>(om[e], kk, vv, e, n);
-        __syncthreads();
         return;
     }
 
-    // Coordinator.
-    __syncthreads();
-    Fwd mine[VEC], carry[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        mine[e] = shf[0][lane * VEC + e];
-        for (int x = 1; x < NW; ++x) mine[e] = fwd_combine(om[e], mine[e], shf[x][lane * VEC + e], L);
-        carry[e] = fwd_identity();
-    }
-    const Chain<Fwd> chn = fwd_chain<VEC>(g, gi);
-    publish<VEC>(chn, s, lane, mine, false);
-    auto fold = [&](Fwd (&c)[VEC], const Fwd (&x)[VEC], int64_t) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) c[e] = fwd_combine(om[e], c[e], x[e], SLAB);
-    };
-    auto recompute = [&](int64_t jj, Fwd (&x)[VEC]) {
-        const int64_t bj = (b * g.T + jj * SLAB) * g.C + grp * CW;
-        const rsrc_t rkj = make_rsrc(A.k + bj, (total - bj) * 4), rvj = make_rsrc(A.v + bj, (total - bj) * 4);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) x[e] = fwd_identity();
-        if (active) {
-            for (int t = 0; t < SLAB; ++t) {
-                const FV<VEC> kt = ldb<VEC>(rkj, voff, t * rowb), vt = ldb<VEC>(rvj, voff, t * rowb);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const float kj = kt.v[e] * kLog2e;
-                    fwd_advance(om[e], x[e], kj, (double)vt.v[e], mag(x[e].p, (float)x[e].b));
+    // ---- coordinator ----
+    int ib = 0;
+    for (int64_t u = blockIdx.x; u < items; u += gridDim.x, ib ^= 1) {
+        const Item it = item_of(u);
+        float om[1], mu[1];
+        load_chan<1>(A, it.c0, it.active, om, mu);
+        const Chain<Fwd> chn{g.flags_c + it.gi * nitem, reinterpret_cast<uint32_t*>(g.agg_c) + it.gi * nitem * kRec,
+                             reinterpret_cast<uint32_t*>(g.incl_c) + it.gi * nitem * kRec, g.tag_f, g.spin};
+        const int64_t f0 = it.q * F;
+        const int nvalid = (int)((nfine - f0) < F ? (nfine - f0) : F);
+        __syncthreads();
+        const uint64_t first = prefetch_window(chn, it.q, lane);  // overlaps the fold below
+        Fwd mine[1], carry[1];
+        mine[0] = shf[ib][0][lane];
+        for (int x = 1; x < nvalid; ++x) mine[0] = fwd_combine(om[0], mine[0], shf[ib][x][lane], SLAB);
+        carry[0] = fwd_identity();
+        const bool has_succ = it.q + 1 < nitem;
+        if (has_succ) publish<1>(chn, it.q, lane, mine, false);
+        auto fold = [&](Fwd (&c)[1], const Fwd (&x)[1], int64_t) {
+            c[0] = fwd_combine(om[0], c[0], x[0], (int64_t)F * SLAB);  // earlier items are full
+        };
+        auto recompute = [&](int64_t jj, Fwd (&x)[1]) {
+            const int64_t bj = (it.b * g.T + jj * F * SLAB) * g.C + it.grp * 64;
+            const rsrc_t rkj = make_rsrc(A.k + bj, (total - bj) * 4), rvj = make_rsrc(A.v + bj, (total - bj) * 4);
+            x[0] = fwd_identity();
+            if (it.active) {
+                for (int t = 0; t < F * SLAB; ++t) {
+                    const float kj = ldb<1>(rkj, voff, t * rowb).v[0] * kLog2e;
+                    const float vj = ldb<1>(rvj, voff, t * rowb).v[0];
+                    fwd_advance(om[0], x[0], kj, (double)vj, mag(x[0].p, (float)x[0].b));
                 }
             }
+        };
+        look_back<1, 2>(chn, it.q, lane, carry, fold, recompute, first);
+        // The sums at the end of every fine slab of the item (read by the gradient kernel).
+        uint32_t* fine = reinterpret_cast<uint32_t*>(g.incl_f) + it.gi * g.nslab * kRec;
+        for (int x = 0; x < nvalid; ++x) {
+            carry[0] = fwd_combine(om[0], carry[0], shf[ib][x][lane], SLAB);
+            store_record<1>(fine, f0 + x, lane, carry);
         }
-    };
-    look_back<VEC, 2>(chn, s, lane, carry, fold, recompute);
-    Fwd incl[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) incl[e] = fwd_combine(om[e], carry[e], mine[e], SLAB);
-    publish<VEC>(chn, s, lane, incl, true);
+        if (has_succ) publish<1>(chn, it.q, lane, carry, true);
+    }
 }
 
 // The reverse record of chain slab jj computed from its inputs (the look-back's fallback
@@ -368,77 +498,162 @@ __global__ __launch_bounds__(64 * (NW + 1)) void wkv_bwd_grad_kernel(WkvBwdArgs 
     load_chan<VEC>(A, c0, active, om, mu);
 
     if (w < NW) {
+        static_assert(VEC == 1, "the gradient kernel keeps one channel per lane");
         const int n = active ? chunk_len<L>(w, slab_n) : 0;
         const unsigned rowb = (unsigned)(g.C * 4);
-        const unsigned voff = (unsigned)(lane * VEC * 4);
+        const unsigned voff = (unsigned)(lane * 4);
         const int64_t total = g.B * g.T * g.C;
         const int64_t base = (b * g.T + t_slab + (int64_t)w * L) * g.C + grp * CW;
         const int64_t nbytes = (total - base) * 4;
-        float kk[L][VEC], vv[L][VEC], gg[L][VEC];
+        const rsrc_t rk = make_rsrc(A.k + base, nbytes), rg = make_rsrc(A.gy + base, nbytes);
+        // Per step: sa = g_j (fast path) or q_j (exact path); vv = v_j; sc = dL/dy_j, then
+        // g_j / D~_j (fast) or g_j / dm_j (exact); sy = y_j; sd = v_j - y_j.
+        float sa[L], vv[L], sc[L], sy[L], sd[L];
+        float gmax = 0.f;
         {
-            const rsrc_t rk = make_rsrc(A.k + base, nbytes), rv = make_rsrc(A.v + base, nbytes),
-                         rg = make_rsrc(A.gy + base, nbytes);
+            const rsrc_t rv = make_rsrc(A.v + base, nbytes);
 #pragma unroll
             for (int j = 0; j < L; ++j) {
-                FV<VEC> kt{}, vt{}, gt{};
+                float kt = 0.f, vt = 0.f, gt = 0.f;
                 if (j < n) {
-                    kt = ldb<VEC>(rk, voff, j * rowb);
-                    vt = ldb<VEC>(rv, voff, j * rowb);
-                    gt = ldb<VEC>(rg, voff, j * rowb);
+                    kt = ldb<1>(rk, voff, j * rowb).v[0];
+                    vt = ldb<1>(rv, voff, j * rowb).v[0];
+                    gt = ldb<1>(rg, voff, j * rowb).v[0];
                 }
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    kk[j][e] = kt.v[e] * kLog2e;
-                    vv[j][e] = vt.v[e];
-                    gg[j][e] = gt.v[e];
-                }
+                sa[j] = kt * kLog2e;
+                vv[j] = vt;
+                sc[j] = gt;
+                gmax = fmaxf(gmax, fabsf(gt));
             }
         }
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) shf[w][lane * VEC + e] = fwd_chunk<L, VEC>(om[e], kk, vv, e, n);
+        float m0;
+        shf[w][lane] = fwd_chunk_keep<L>(om[0], sa, vv, n, m0);
+        const float p_chunk = shf[w][lane].p;
         __syncthreads();  // B1
         __syncthreads();  // B2: shf[w] now holds my chunk's carry-in
 
-        // Forward re-run: per step c, q, y, v - y (the registers of g are reused for c).
-        float qs[L][VEC], ys[L][VEC], dv[L][VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            Fwd st = shf[w][lane * VEC + e];
-            double sw = 0.0, su = 0.0;
+        const float lift = ceilf(fmaxf(fmaxf(om[0], mu[0]), 0.f));
+        const Fwd cin = shf[w][lane];
+        ChunkFrame fr = chunk_frame(om[0], mu[0], lift, cin, p_chunk, m0, n, gmax, n > 0 && !g.exact_only);
+        double sw = 0.0, su = 0.0;
+        Rev ragg = rev_identity();
+        if (fr.fast) {
+            // Forward in the frame (float32: at most L terms are added to the converted
+            // carry).  Also the chunk's reverse sums seen from its start:
+            // x = sum g/D~, h = sum g y/D~, z = sum 1/D~, at exponent -F0.
+            const double cf = fr.cf;
+            float a = (float)(cin.a * cf), bb = (float)(cin.b * cf), ad = (float)(cin.ad * cf),
+                  bd = (float)(cin.bd * cf);
+            float x = 0.f, h = 0.f, z = 0.f, swf = 0.f, suf = 0.f, dmin = 1.f;
 #pragma unroll
             for (int j = 0; j < L; ++j) {
                 if (j < n) {
-                    const StepOut o = fwd_step(om[e], mu[e], st, kk[j][e], vv[j][e], gg[j][e], sw, su);
-                    gg[j][e] = o.c;
-                    qs[j][e] = o.q;
-                    ys[j][e] = o.y;
-                    dv[j][e] = o.vmy;
-                } else {
-                    gg[j][e] = 0.f;
-                    qs[j][e] = 0.f;
-                    ys[j][e] = 0.f;
-                    dv[j][e] = 0.f;
+                    const float gj = sa[j], vj = vv[j];
+                    const float cur = gj * fr.cs;
+                    const float dt = bb + cur;
+                    const float inv = __builtin_amdgcn_rcpf(dt);
+                    dmin = fminf(dmin, dt);
+                    const float y = fmaf(cur, vj, a) * inv;
+                    const float vmy = fmaf(vj, bb, -a) * inv;
+                    const float cg = sc[j] * inv;
+                    swf = fmaf(-cg, fmaf(-y, bd, ad), swf);
+                    suf = fmaf(cg * cur, vmy, suf);
+                    x += cg;
+                    h = fmaf(cg, y, h);
+                    z += inv;
+                    const float up = gj * fr.us;
+                    ad += a;
+                    bd += bb;
+                    a = fmaf(up, vj, a);
+                    bb += up;
+                    sc[j] = cg;
+                    sy[j] = y;
+                    sd[j] = vmy;
                 }
             }
-            shwu[w][lane * VEC + e][0] = sw;
-            shwu[w][lane * VEC + e][1] = su;
-            shr[w][lane * VEC + e] = rev_chunk<L, VEC>(om[e], qs, gg, ys, e, n);
+            ragg = {x, h, z, -fr.F0};
+            sw = swf;
+            su = suf;
+            // A denominator below 2^kBwdFastLo would let g / D~ leave float range: redo exactly.
+            fr.fast = dmin >= 0x1p-60f;
+            if (!fr.fast) {
+                sw = 0.0;
+                su = 0.0;
+            }
         }
+        if (!fr.fast && n > 0) {
+            // Exact per-step path (wkv_math.hpp exponents); k and dL/dy are read again.
+            Fwd st = cin;
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                if (j < n) {
+                    const float kj = ldb<1>(rk, voff, j * rowb).v[0] * kLog2e;
+                    const float gj = ldb<1>(rg, voff, j * rowb).v[0];
+                    const StepOut o = fwd_step(om[0], mu[0], st, kj, vv[j], gj, sw, su);
+                    sa[j] = o.q;
+                    sc[j] = o.c;
+                    sy[j] = o.y;
+                    sd[j] = o.vmy;
+                }
+            }
+            float qs[L][1], cg[L][1], ys[L][1];
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                qs[j][0] = sa[j];
+                cg[j][0] = sc[j];
+                ys[j][0] = sy[j];
+            }
+            ragg = rev_chunk<L, 1>(om[0], qs, cg, ys, 0, n);
+        }
+        shwu[w][lane][0] = sw;
+        shwu[w][lane][1] = su;
+        shr[w][lane] = ragg;
         __syncthreads();  // B3
         __syncthreads();  // B4: shr[w] now holds the reverse state at my chunk's end
 
-        // Reverse re-run of my chunk; the outputs replace k and v.
+        // Reverse re-run of my chunk; the outputs replace v and dL/dy's slot.
         if (n > 0) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                Rev rs = shr[w][lane * VEC + e];
+            const Rev rc = shr[w][lane];
+            if (fr.fast) {
+                // Carry in frame units, X = x_c 2^{r_c + F0 - n om}, pre-multiplied by us:
+                // alpha_s G_s = g_s (us X + us S_s) with S_s the frame sum after s in the chunk.
+                // The carry part of v X - H cancels, so it is formed in float64.
+                double Xs = 0.0, Hs = 0.0;
+                if (rc.x != 0.0 || rc.h != 0.0) {
+                    const Split dn = mul_split((float)n, om[0]);
+                    const float e = ((rc.r + fr.F0) - dn.hi) - dn.lo;
+                    const float ei = floorf(e);
+                    const double kap = ldexp((double)(fast_exp2(e - ei) * fr.us), (int)ei);
+                    Xs = rc.x * kap;
+                    Hs = rc.h * kap;
+                }
+                const float Xsf = (float)Xs;
+                float Sx = 0.f, Sh = 0.f;
 #pragma unroll
                 for (int j = L - 1; j >= 0; --j) {
                     if (j < n) {
+                        const float gj = sa[j], vj = vv[j];
+                        const float gus = gj * fr.us;
+                        const float cc = sc[j] * (gj * fr.cs);  // g beta / D
+                        const float tc = (float)fma((double)vj, Xs, -Hs);
+                        const float gv = fmaf(gus, Sx, fmaf(gj, Xsf, cc));
+                        const float gk = fmaf(cc, sd[j], fmaf(gj, tc, gus * fmaf(vj, Sx, -Sh)));
+                        Sx += sc[j];
+                        Sh = fmaf(sc[j], sy[j], Sh);
+                        sa[j] = gk;
+                        vv[j] = gv;
+                    }
+                }
+            } else {
+                Rev rs = rc;
+#pragma unroll
+                for (int j = L - 1; j >= 0; --j) {
+                    if (j < n) {
+                        const float kj = ldb<1>(rk, voff, j * rowb).v[0] * kLog2e;
                         float gk, gv;
-                        rev_step(om[e], mu[e], rs, kk[j][e], vv[j][e], gg[j][e], qs[j][e], ys[j][e], dv[j][e], gk, gv);
-                        kk[j][e] = gk;
-                        vv[j][e] = gv;
+                        rev_step(om[0], mu[0], rs, kj, vv[j], sc[j], sa[j], sy[j], sd[j], gk, gv);
+                        sa[j] = gk;
+                        vv[j] = gv;
                     }
                 }
             }
@@ -446,14 +661,11 @@ __global__ __launch_bounds__(64 * (NW + 1)) void wkv_bwd_grad_kernel(WkvBwdArgs 
 #pragma unroll
             for (int j = 0; j < L; ++j) {
                 if (j < n) {
-                    FV<VEC> ok, ov;
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        ok.v[e] = kk[j][e];
-                        ov.v[e] = vv[j][e];
-                    }
-                    stb<VEC>(rgk, voff, j * rowb, ok);
-                    stb<VEC>(rgv, voff, j * rowb, ov);
+                    FV<1> ok, ov;
+                    ok.v[0] = sa[j];
+                    ov.v[0] = vv[j];
+                    stb<1>(rgk, voff, j * rowb, ok);
+                    stb<1>(rgv, voff, j * rowb, ov);
                 }
             }
         }
@@ -461,11 +673,11 @@ __global__ __launch_bounds__(64 * (NW + 1)) void wkv_bwd_grad_kernel(WkvBwdArgs 
     }
 
     // ---- coordinator ----
+    Fwd cin[VEC];
+    fwd_carry_in<VEC>(g, gi, s, lane, active, cin);  // issued before the chunks are reduced
     __syncthreads();  // B1
     {
         // Carry-in of each chunk: the previous slab's sums (state kernel), then the chunks in order.
-        Fwd cin[VEC];
-        fwd_carry_in<VEC>(g, gi, s, lane, active, cin);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             Fwd c = cin[e];
@@ -477,7 +689,12 @@ __global__ __launch_bounds__(64 * (NW + 1)) void wkv_bwd_grad_kernel(WkvBwdArgs 
         }
     }
     __syncthreads();  // B2
+    const Chain<RevRec> chn{g.flags_r + gi * g.nslab,
+                            reinterpret_cast<uint32_t*>(g.agg_r) + gi * g.nslab * (CW * kDwords<RevRec>),
+                            reinterpret_cast<uint32_t*>(g.incl_r) + gi * g.nslab * (CW * kDwords<RevRec>), g.tag_r,
+                            g.spin};
     __syncthreads();  // B3
+    const uint64_t first = prefetch_window(chn, q, lane);  // overlaps the slab fold and publication
     RevRec mine[VEC], carry[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -492,10 +709,6 @@ __global__ __launch_bounds__(64 * (NW + 1)) void wkv_bwd_grad_kernel(WkvBwdArgs 
         mine[e] = {a, sw, su};
         carry[e] = {rev_identity(), 0.0, 0.0};
     }
-    const Chain<RevRec> chn{g.flags_r + gi * g.nslab,
-                            reinterpret_cast<uint32_t*>(g.agg_r) + gi * g.nslab * (CW * kDwords<RevRec>),
-                            reinterpret_cast<uint32_t*>(g.incl_r) + gi * g.nslab * (CW * kDwords<RevRec>), g.tag_r,
-                            g.spin};
     const bool has_succ = s > 0;
     if (has_succ) publish<VEC>(chn, q, lane, mine, false);
     // carry (the state at the end of chain slab jj) followed by slab jj, earlier in time.
@@ -512,7 +725,7 @@ __global__ __launch_bounds__(64 * (NW + 1)) void wkv_bwd_grad_kernel(WkvBwdArgs 
     auto recompute = [&](int64_t jj, RevRec (&x)[VEC]) {
         rev_record_from_inputs<VEC, SLAB>(A, g, jj, gi, b, grp, lane, active, om, mu, x);
     };
-    look_back<VEC, 2>(chn, q, lane, carry, fold, recompute);
+    look_back<VEC, 2>(chn, q, lane, carry, fold, recompute, first);
     RevRec incl[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) incl[e] = carry[e];
@@ -565,13 +778,37 @@ __global__ __launch_bounds__(256) void zero_wu_kernel(float* __restrict__ gw, fl
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workgroups of `kernel` (block of `threads`) that the current device holds at once: blocks
+// per CU from the occupancy query times the CU count, cached per device in `cache` (one
+// cache per kernel).
+constexpr int kMaxDev = 64;
+hipError_t resident_blocks(const void* kernel, int threads, std::atomic<int> (&cache)[kMaxDev], int& out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDev && (out = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+    int ncu = 0, per = 0;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0)) != hipSuccess) return e;
+    out = (per > 0 ? per : 1) * (ncu > 0 ? ncu : 1);
+    if (dev >= 0 && dev < kMaxDev) cache[dev].store(out, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
 template <int VEC, int NW, int L>
 hipError_t launch(const WkvBwdArgs& A, const BwdGeom& g, hipStream_t st) {
     const int64_t G = g.B * g.ngrp;
     if (g.nslab > 1) {
-        hipLaunchKernelGGL((wkv_bwd_state_kernel<VEC, NW, L>), dim3((unsigned)(G * (g.nslab - 1))), dim3(64 * (NW + 1)),
-                           0, st, A, g);
-        const hipError_t e = hipGetLastError();
+        // Persistent grid: no more workgroups than are resident together.
+        const auto kern = wkv_bwd_state_kernel<NW, L>;
+        static std::atomic<int> cache[kMaxDev];
+        int resident = 0;
+        hipError_t e = resident_blocks((const void*)kern, 64 * (kStateFine + 1), cache, resident);
+        if (e != hipSuccess) return e;
+        const int64_t items = G * ((g.nslab - 1 + kStateFine - 1) / kStateFine);
+        const int64_t grid = items < resident ? items : resident;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * (kStateFine + 1)), 0, st, A, g);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L>), dim3((unsigned)(G * g.nslab)), dim3(64 * (NW + 1)), 0, st,
@@ -614,8 +851,11 @@ BwdPlan wkv_backward_plan(int vec, int64_t B, int64_t T, int64_t C, int nw_overr
     const int64_t nrec = B * ((C + cw - 1) / cw) * p.nslab;
     size_t bytes = align256((size_t)(B * C) * 2 * sizeof(double));  // part
     if (p.nslab > 1) {
-        bytes += 2 * align256((size_t)nrec * 8);                           // flags
-        bytes += 2 * align256((size_t)(nrec * cw) * sizeof(Fwd));          // forward records
+        const int64_t ncoarse = B * ((C + cw - 1) / cw) * ((p.nslab - 1 + kStateFine - 1) / kStateFine);
+        bytes += align256((size_t)ncoarse * 8);                            // coarse flags
+        bytes += 2 * align256((size_t)(ncoarse * cw) * sizeof(Fwd));       // coarse records
+        bytes += align256((size_t)(nrec * cw) * sizeof(Fwd));              // sums at fine slab ends
+        bytes += align256((size_t)nrec * 8);                               // reverse flags
         bytes += 2 * align256((size_t)(nrec * cw) * sizeof(RevRec));       // reverse records
     }
     p.ws_bytes = bytes;
@@ -626,18 +866,21 @@ void wkv_backward_layout(const BwdPlan& p, int64_t B, int64_t C, void* ws, BwdGe
     char* at = (char*)ws;
     g.part = reinterpret_cast<double*>(at);
     at += align256((size_t)(B * C) * 2 * sizeof(double));
-    g.flags_f = g.flags_r = nullptr;
-    g.agg_f = g.incl_f = g.agg_r = g.incl_r = nullptr;
+    g.flags_c = g.flags_r = nullptr;
+    g.agg_c = g.incl_c = g.incl_f = g.agg_r = g.incl_r = nullptr;
     if (p.nslab <= 1) return;
     const int64_t cw = 64 * (int64_t)p.vec;
     const int64_t nrec = B * ((C + cw - 1) / cw) * p.nslab;
+    const int64_t ncoarse = B * ((C + cw - 1) / cw) * ((p.nslab - 1 + kStateFine - 1) / kStateFine);
     const size_t fl = align256((size_t)nrec * 8);
     const size_t fr = align256((size_t)(nrec * cw) * sizeof(Fwd));
     const size_t rr = align256((size_t)(nrec * cw) * sizeof(RevRec));
-    g.flags_f = reinterpret_cast<uint64_t*>(at), at += fl;
-    g.flags_r = reinterpret_cast<uint64_t*>(at), at += fl;
-    g.agg_f = at, at += fr;
+    const size_t cr = align256((size_t)(ncoarse * cw) * sizeof(Fwd));
+    g.flags_c = reinterpret_cast<uint64_t*>(at), at += align256((size_t)ncoarse * 8);
+    g.agg_c = at, at += cr;
+    g.incl_c = at, at += cr;
     g.incl_f = at, at += fr;
+    g.flags_r = reinterpret_cast<uint64_t*>(at), at += fl;
     g.agg_r = at, at += rr;
     g.incl_r = at;
 }

@@ -19,23 +19,25 @@ struct WkvBwdArgs {
     float* gv;        // (B,T,C)
 };
 
-// Launch geometry of the backward.  Both streaming kernels cut each sequence into slabs of
-// nw chunks of L steps of one channel group (64 lanes x vec channels).  The state kernel
-// visits slabs in time order and publishes the forward sums at every slab end; the gradient
-// kernel visits them in reverse time order.  Workgroups are numbered chain-major.
+// Launch geometry of the backward.  The gradient kernel cuts each sequence into slabs of nw
+// chunks of L steps of one channel group (64 lanes x vec channels) and visits them in
+// reverse time order (workgroups numbered chain-major); the state kernel writes the forward
+// sums at every slab end, looking back over items of several slabs in time order.
 struct BwdGeom {
     int64_t B, T, C;
     int64_t ngrp;   // channel groups per batch row
     int64_t nslab;  // slabs per sequence
     int spin;       // polls of a predecessor's flag before recomputing its aggregate
     uint64_t tag_f, tag_r;  // per-call tags of the two kernels' flags (never 0)
-    uint64_t* flags_f;      // (B*ngrp*nslab) forward-chain flags
-    void* agg_f;            // (B*ngrp*nslab, 64*vec) forward aggregates
-    void* incl_f;           // (B*ngrp*nslab, 64*vec) forward inclusive prefixes
+    uint64_t* flags_c;      // forward (coarse) chain of the state kernel: flags per item
+    void* agg_c;            // (B*ngrp*items, 64*vec) item aggregates
+    void* incl_c;           // (B*ngrp*items, 64*vec) item inclusive prefixes
+    void* incl_f;           // (B*ngrp*nslab, 64*vec) forward sums at the end of every slab
     uint64_t* flags_r;      // reverse-chain flags, records indexed by chain position
     void* agg_r;
     void* incl_r;
     double* part;           // (B, C, 2) dL/dw, dL/du of each batch row
+    int exact_only;         // 1: the gradient kernel never takes its frame fast path (tests)
 };
 
 struct BwdPlan {

@@ -239,6 +239,25 @@ def test_lookback_recompute_path(L, monkeypatch, spin):
                    oracle.scan_complex(c["lam"], c["u"], xc0)) <= TOL
 
 
+@pytest.mark.parametrize("wid", [2, 3])
+def test_backward_exact_path_matches_fast_path(L, monkeypatch, wid):
+    # The backward's per-chunk frame (no exponential in the reverse) and its exact per-step
+    # path must agree; both against the oracle.
+    announce("wkv4_backward exact-only path vs default, workload %d shape" % wid)
+    d = workloads.make_inputs(wid, seed=22, shape=(2, 1500, 96))
+    if "gy" not in d:
+        d["gy"] = np.random.default_rng(5).standard_normal(d["k"].shape).astype(np.float32)
+    ref = oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    fast = gpu_wkv_bwd(L, d)
+    monkeypatch.setenv("LINREC_WKV_EXACT", "1")
+    exact = gpu_wkv_bwd(L, d)
+    check_bwd(fast, ref)
+    check_bwd(exact, ref)
+    for name, a, b in zip(("gw", "gu", "gk", "gv"), fast, exact):
+        ax = None if name in ("gw", "gu") else 1
+        assert rel_err(a, b.astype(np.float64), ax) <= 2 * TOL, name
+
+
 BWD_SHAPES_NW_L = [("3", "16"), ("4", "16"), ("7", "8"), ("8", "8"), ("7", "16")]
 
 
