@@ -309,8 +309,10 @@ __device__ __forceinline__ Fwd fwd_chunk1(float om, const float (&kk)[L], const 
     return {a, b, ad, bd, p};
 }
 
+// 6 waves per SIMD (<= 80 VGPRs, no spills): three workgroups resident per CU.
 template <int NW, int L>
-__global__ __launch_bounds__(64 * (kStateFine + 1)) void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
+__global__ __launch_bounds__(64 * (kStateFine + 1)) __attribute__((amdgpu_waves_per_eu(6)))
+void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
     constexpr int SLAB = NW * L;
     constexpr int F = kStateFine;
     constexpr int kRec = 64 * kDwords<Fwd>;  // dwords per slab record
@@ -473,13 +475,23 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
 // The two roles are separate branches, so the look-back's registers do not add to those
 // of the chunk data.
 // ------------------------------------------------------------------------------------
+// Register budget: with 8-step chunks the kernel fits 80 VGPRs (6 waves per SIMD), so three
+// 8-wave workgroups share a CU; that hides one workgroup's look-back behind the others'
+// work better than the compiler's own choice (~90 VGPRs, two workgroups).
+template <int L>
+constexpr int grad_waves_per_eu() {
+    return L <= 8 ? 6 : 1;
+}
+
 template <int VEC, int NW, int L>
-__global__ __launch_bounds__(64 * (NW + 1)) void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
+__global__ __launch_bounds__(64 * (NW + 1)) __attribute__((amdgpu_waves_per_eu(grad_waves_per_eu<L>())))
+void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     constexpr int CW = 64 * VEC;
     constexpr int SLAB = NW * L;
     __shared__ Fwd shf[NW][CW];
     __shared__ Rev shr[NW][CW];
     __shared__ double shwu[NW][CW][2];
+    __shared__ RevRec sh_mine[CW];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -708,6 +720,7 @@ __global__ __launch_bounds__(64 * (NW + 1)) void wkv_bwd_grad_kernel(WkvBwdArgs 
         }
         mine[e] = {a, sw, su};
         carry[e] = {rev_identity(), 0.0, 0.0};
+        sh_mine[lane * VEC + e] = mine[e];  // kept in LDS across the look-back (registers)
     }
     const bool has_succ = s > 0;
     if (has_succ) publish<VEC>(chn, q, lane, mine, false);
@@ -725,10 +738,13 @@ __global__ __launch_bounds__(64 * (NW + 1)) void wkv_bwd_grad_kernel(WkvBwdArgs 
     auto recompute = [&](int64_t jj, RevRec (&x)[VEC]) {
         rev_record_from_inputs<VEC, SLAB>(A, g, jj, gi, b, grp, lane, active, om, mu, x);
     };
-    look_back<VEC, 2>(chn, q, lane, carry, fold, recompute, first);
+    look_back<VEC, 1>(chn, q, lane, carry, fold, recompute, first);
     RevRec incl[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) incl[e] = carry[e];
+    for (int e = 0; e < VEC; ++e) {
+        incl[e] = carry[e];
+        mine[e] = sh_mine[lane * VEC + e];
+    }
     fold(incl, mine, q);
     if (has_succ) {
         publish<VEC>(chn, q, lane, incl, true);
