@@ -40,11 +40,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
-    """Digest of the HIP sources: counter figures taken from an older build do not apply."""
+# Sources each entry point's kernels are built from (the launch plan lives in api.hip).
+_SCAN_SOURCES = ("api.hip", "chunk_scan.hip", "chunk_scan.hpp", "scan_ops.hpp", "lookback.hpp",
+                 "device_common.hpp", "wkv_math.hpp")
+KERNEL_SOURCES = {
+    "wkv4_forward": _SCAN_SOURCES,
+    "scan_real": _SCAN_SOURCES,
+    "scan_complex": _SCAN_SOURCES,
+    "wkv4_backward": ("api.hip", "wkv_backward.hip", "wkv_backward.hpp", "lookback.hpp", "device_common.hpp",
+                      "wkv_math.hpp"),
+}
+
+
+def kernel_source_digest(kind: str = "wkv4_forward") -> str:
+    """Digest of the HIP sources of one entry point: counter figures taken from an older
+    build of those kernels do not apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_recurrence_rnn_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(KERNEL_SOURCES[kind]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -59,7 +72,7 @@ def counter_traffic(workload: str, launches_per_step: int = 1):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_digest") != kernel_source_digest():
+    if rec.get("source_digest") != kernel_source_digest(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 

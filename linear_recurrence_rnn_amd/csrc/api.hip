@@ -73,8 +73,10 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
         p.nw = 8;
         p.L = 16;
     } else {
+        // Complex: one channel per lane over 32-step chunks (slabs of 256 steps) halves the
+        // look-back chains of a single long sequence; two channels per lane take 16 steps.
         p.nw = 8;
-        p.L = 16;
+        p.L = vec == 1 ? 32 : 16;
     }
     const int nw = (int)env_int("LINREC_NW", 0), L = (int)env_int("LINREC_L", 0);
     if (nw > 0 && L > 0 && linrec::scan_shape_supported(kind, vec, nw, L)) {
@@ -92,13 +94,13 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
 int vmax_of(int kind) { return kind == linrec::kKindComplex ? 2 : 4; }
 
 // Channels per lane: the widest the alignment allows, narrowed by the default policy
-// (WKV: 1, real scan: 2) or by LINREC_VEC (tests and tuning).
+// (WKV and complex: 1, real scan: 2) or by LINREC_VEC (tests and tuning).
 int pick_vec(int kind, int vec_aligned) {
     int vec = vec_aligned;
     const int64_t f = env_int("LINREC_VEC", 0);
     if (f == 1 || f == 2 || f == 4) {
         vec = f < vec ? (int)f : vec;
-    } else if (kind == linrec::kKindWkv) {
+    } else if (kind == linrec::kKindWkv || kind == linrec::kKindComplex) {
         vec = 1;
     } else if (kind == linrec::kKindReal) {
         vec = vec < 2 ? vec : 2;

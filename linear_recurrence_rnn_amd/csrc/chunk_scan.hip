@@ -169,12 +169,19 @@ hipError_t launch(const typename Op::Args& A, const ScanGeom& g, hipStream_t st)
     return hipGetLastError();
 }
 
-// Kernels that exist: vec in {VMAX, 2, 1} x (nw, L) in {(4, 16), (8, 8), (8, 16)}.
+// Kernels that exist: vec in {VMAX, 2, 1} x (nw, L) in {(4, 16), (8, 8), (8, 16)}, and for
+// the linear scans (8, 32) with one channel per lane (the registers of two channels x 16
+// steps, with slabs twice as long: shorter look-back chains).  WKV keeps chunks of at most
+// 16 steps: its per-chunk frame spans (L-1) om in exponent, which 32 steps of a fast decay
+// push to the edge of float32 range.
 template <class Op, int VEC>
 hipError_t dispatch_shape(const typename Op::Args& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st) {
     if (p.nw == 4 && p.L == 16) return launch<Op, VEC, 4, 16>(A, g, st);
     if (p.nw == 8 && p.L == 8) return launch<Op, VEC, 8, 8>(A, g, st);
     if (p.nw == 8 && p.L == 16) return launch<Op, VEC, 8, 16>(A, g, st);
+    if constexpr (VEC == 1 && !std::is_same<Op, WkvOp>::value) {
+        if (p.nw == 8 && p.L == 32) return launch<Op, VEC, 8, 32>(A, g, st);
+    }
     return hipErrorInvalidValue;
 }
 
@@ -193,7 +200,8 @@ hipError_t dispatch(const typename Op::Args& A, const ScanGeom& g, const ScanPla
 bool scan_shape_supported(int kind, int vec, int nw, int L) {
     const int vmax = kind == kKindComplex ? 2 : 4;
     const bool vec_ok = vec == vmax || vec == 2 || vec == 1;
-    return vec_ok && ((nw == 4 && L == 16) || (nw == 8 && L == 8) || (nw == 8 && L == 16));
+    return vec_ok && ((nw == 4 && L == 16) || (nw == 8 && L == 8) || (nw == 8 && L == 16) ||
+                      (kind != kKindWkv && vec == 1 && nw == 8 && L == 32));
 }
 
 hipError_t run_wkv_forward(const WkvArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st) {

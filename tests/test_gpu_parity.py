@@ -201,14 +201,15 @@ def test_wkv_exact_path_matches_fast_path(L, monkeypatch, wid):
     assert rel_err(y_fast, y_exact.astype(np.float64)) <= 2 * TOL
 
 
-SHAPES_NW_L = [("4", "16"), ("8", "8"), ("8", "16")]
+SHAPES_NW_L_VEC = [(nw, lc, vec) for (nw, lc) in [("4", "16"), ("8", "8"), ("8", "16")]
+                   for vec in ("4", "2", "1")] + [("8", "32", "1")]
 
 
-@pytest.mark.parametrize("vec", ["4", "2", "1"])
-@pytest.mark.parametrize("nw,lc", SHAPES_NW_L, ids=["nw%s_L%s" % x for x in SHAPES_NW_L])
+@pytest.mark.parametrize("nw,lc,vec", SHAPES_NW_L_VEC, ids=["nw%s_L%s_vec%s" % x for x in SHAPES_NW_L_VEC])
 def test_forward_launch_shapes(L, monkeypatch, nw, lc, vec):
     # Every kernel shape (waves per slab x steps per chunk) against the oracle, with ragged
-    # slabs, partial channel groups and the scalar (vec 1) variant.
+    # slabs, partial channel groups and the scalar (vec 1) variant.  (8, 32) exists for the
+    # linear scans only; WKV then runs its default shape.
     announce("forward launch shape nw=%s L=%s vec<=%s" % (nw, lc, vec))
     monkeypatch.setenv("LINREC_NW", nw)
     monkeypatch.setenv("LINREC_L", lc)
