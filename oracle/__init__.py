@@ -52,8 +52,12 @@ def _bind(path: str):
                                          _F32P, _F64P, _F64P, _F64P, _F64P]
     lib.oracle_scan_real.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_scan_complex.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
+    lib.oracle_scan_real_backward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F64P, _F32P,
+                                              _F64P, _F64P, _F64P]
+    lib.oracle_scan_complex_backward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F64P, _F32P,
+                                                 _F64P, _F64P, _F64P]
     for name in ("oracle_wkv4_forward", "oracle_wkv4_backward", "oracle_scan_real",
-                 "oracle_scan_complex"):
+                 "oracle_scan_complex", "oracle_scan_real_backward", "oracle_scan_complex_backward"):
         getattr(lib, name).restype = None
     return lib
 
@@ -167,3 +171,42 @@ def scan_complex(lam, u, x0=None, lib=None) -> np.ndarray:
                                 None if x0f is None else _p32(x0f),
                                 x.view(np.float64).ctypes.data_as(_F64P))
     return x
+
+
+def scan_real_backward(a, x, gx, x0=None, lib=None):
+    """(ga, gb (B,T,C), gx0 (B,C) or None) float64: the adjoint of x_t = a_t x_{t-1} + b_t
+    for upstream gradients gx, given the forward output x (float32 or float64)."""
+    a = _f32(a)
+    B, T, C = a.shape
+    gx = _f32(gx, (B, T, C))
+    xd = np.ascontiguousarray(x, dtype=np.float64)
+    if xd.shape != (B, T, C):
+        raise ValueError("x must be (B,T,C)")
+    x0a = None if x0 is None else _f32(x0, (B, C))
+    ga = np.empty((B, T, C), dtype=np.float64)
+    gb = np.empty((B, T, C), dtype=np.float64)
+    gx0 = None if x0 is None else np.empty((B, C), dtype=np.float64)
+    (lib or _load()).oracle_scan_real_backward(B, T, C, _p32(a), None if x0a is None else _p32(x0a),
+                                               _p64(xd), _p32(gx), _p64(ga), _p64(gb),
+                                               None if gx0 is None else _p64(gx0))
+    return ga, gb, gx0
+
+
+def scan_complex_backward(lam, x, gx, x0=None, lib=None):
+    """(glam (C,), gu (B,T,C), gx0 (B,C) or None) complex128: the adjoint of
+    x_t = lam x_{t-1} + u_t (gradients as dL/dRe + i dL/dIm), given the forward output x."""
+    gxc = np.ascontiguousarray(gx, dtype=np.complex64)
+    B, T, C = gxc.shape
+    lf = _c64f(lam, (C,))
+    xd = np.ascontiguousarray(x, dtype=np.complex128)
+    if xd.shape != (B, T, C):
+        raise ValueError("x must be (B,T,C)")
+    x0f = None if x0 is None else _c64f(x0, (B, C))
+    glam = np.empty(C, dtype=np.complex128)
+    gu = np.empty((B, T, C), dtype=np.complex128)
+    gx0 = None if x0 is None else np.empty((B, C), dtype=np.complex128)
+    f64 = lambda z: z.view(np.float64).ctypes.data_as(_F64P)  # noqa: E731
+    (lib or _load()).oracle_scan_complex_backward(B, T, C, _p32(lf), None if x0f is None else _p32(x0f),
+                                                  f64(xd), _p32(gxc.view(np.float32)), f64(glam), f64(gu),
+                                                  None if gx0 is None else f64(gx0))
+    return glam, gu, gx0

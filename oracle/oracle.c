@@ -217,3 +217,85 @@ void oracle_scan_complex(int64_t B, int64_t T, int64_t C,
         }
     }
 }
+
+/*
+ * Backward of the real diagonal scan x_t = a_t x_{t-1} + b_t (minGRU page, scan form;
+ * the pages give no backward).  For upstream gradients gx_t = dL/dx_t, the adjoint runs
+ * backwards in time:
+ *     gb_t = gx_t + a_{t+1} gb_{t+1}   (gb_{T-1} = gx_{T-1}),
+ *     ga_t = gb_t x_{t-1}              (x_{-1} = x0, or 0 without x0),
+ *     gx0  = a_0 gb_0                  (only with x0).
+ * x is the forward output (B,T,C) in double; a, gx are (B,T,C) float32; x0 is (B,C) or
+ * NULL.  Outputs ga, gb (B,T,C) and gx0 (B,C, may be NULL) in double.
+ */
+void oracle_scan_real_backward(int64_t B, int64_t T, int64_t C, const float *a, const float *x0,
+                               const double *x, const float *gx, double *ga, double *gb,
+                               double *gx0)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        double s = 0.0;  /* gb_{t+1} */
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int64_t o = base + t * C;
+            const double anext = (t + 1 < T) ? (double)a[o + C] : 0.0;
+            s = (double)gx[o] + anext * s;
+            gb[o] = s;
+            const double xprev = (t > 0) ? x[o - C] : (x0 ? (double)x0[b * C + c] : 0.0);
+            ga[o] = s * xprev;
+        }
+        if (gx0) gx0[b * C + c] = (T > 0 && x0) ? (double)a[base] * s : 0.0;
+    }
+}
+
+/*
+ * Backward of the complex diagonal scan x_t = lambda x_{t-1} + u_t (LRU write-up, eq.
+ * lr-xx; the pages give no backward).  Gradients of a real loss are taken as
+ * dL/dRe + i dL/dIm, so that dL = Re sum conj(g) dz.  Backwards in time:
+ *     gu_t = gx_t + conj(lambda) gu_{t+1},
+ *     glambda = sum over batch and time of gu_t conj(x_{t-1})   (x_{-1} = x0 or 0),
+ *     gx0 = conj(lambda) gu_0                                   (only with x0).
+ * lambda (C,) and gx (B,T,C) are complex64, x0 (B,C) complex64 or NULL, x (B,T,C)
+ * complex128; outputs glambda (C,), gu (B,T,C), gx0 (B,C, may be NULL) complex128.
+ * glambda adds the batch rows in ascending order.
+ */
+void oracle_scan_complex_backward(int64_t B, int64_t T, int64_t C, const float *lam, const float *x0,
+                                  const double *x, const float *gx, double *glam, double *gu,
+                                  double *gx0)
+{
+    double *part = (double *)calloc((size_t)(B * C) * 2 + 1, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        const double complex Lc = conj((double)lam[2 * c] + (double)lam[2 * c + 1] * I);
+        const double complex z0 = x0 ? (double)x0[2 * (b * C + c)] + (double)x0[2 * (b * C + c) + 1] * I : 0.0;
+        double complex s = 0.0, acc = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int64_t o = base + t * C;
+            s = ((double)gx[2 * o] + (double)gx[2 * o + 1] * I) + Lc * s;
+            gu[2 * o] = creal(s);
+            gu[2 * o + 1] = cimag(s);
+            const double complex xp = (t > 0) ? x[2 * (o - C)] + x[2 * (o - C) + 1] * I : z0;
+            acc += s * conj(xp);
+        }
+        part[2 * bc] = creal(acc);
+        part[2 * bc + 1] = cimag(acc);
+        if (gx0) {
+            const double complex g0 = (T > 0 && x0) ? Lc * s : 0.0;
+            gx0[2 * (b * C + c)] = creal(g0);
+            gx0[2 * (b * C + c) + 1] = cimag(g0);
+        }
+    }
+    for (int64_t c = 0; c < C; ++c) {
+        double re = 0.0, im = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            re += part[2 * (b * C + c)];
+            im += part[2 * (b * C + c) + 1];
+        }
+        glam[2 * c] = re;
+        glam[2 * c + 1] = im;
+    }
+    free(part);
+}

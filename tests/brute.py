@@ -138,3 +138,56 @@ def scan_complex_cumsum(lam, u):
     T = u.shape[1]
     t = np.arange(T)[None, :, None]
     return lam ** t * np.cumsum(lam ** (-t) * u, axis=1)
+
+
+def scan_real_backward_sums(a, gx, x, x0=None):
+    """Adjoint of the real scan by its unrolled sums: gb_t = sum_{s>=t} (prod_{k=t+1..s} a_k)
+    gx_s, ga_t = gb_t x_{t-1}, gx0 = a_0 gb_0 (O(T^2), float64)."""
+    a = np.asarray(a, np.float64)
+    g = np.asarray(gx, np.float64)
+    x = np.asarray(x, np.float64)
+    B, T, C = a.shape
+    gb = np.zeros((B, T, C))
+    for t in range(T):
+        prod = np.ones((B, C))
+        for s in range(t, T):
+            if s > t:
+                prod = prod * a[:, s]
+            gb[:, t] += prod * g[:, s]
+    xprev = np.concatenate([(np.zeros((B, 1, C)) if x0 is None else np.asarray(x0, np.float64)[:, None]),
+                            x[:, :-1]], axis=1)
+    ga = gb * xprev
+    gx0 = None if x0 is None else a[:, 0] * gb[:, 0]
+    return ga, gb, gx0
+
+
+def scan_complex_backward_sums(lam, gx, x, x0=None):
+    """Adjoint of the complex scan by its unrolled sums: gu_t = sum_{s>=t} conj(lam)^{s-t}
+    gx_s, glam = sum_{b,t} gu_t conj(x_{t-1}), gx0 = conj(lam) gu_0 (O(T^2), complex128)."""
+    lc = np.conj(np.asarray(lam, np.complex128))
+    g = np.asarray(gx, np.complex128)
+    x = np.asarray(x, np.complex128)
+    B, T, C = g.shape
+    gu = np.zeros((B, T, C), np.complex128)
+    for t in range(T):
+        for s in range(t, T):
+            gu[:, t] += lc ** (s - t) * g[:, s]
+    xprev = np.concatenate([(np.zeros((B, 1, C), np.complex128) if x0 is None
+                             else np.asarray(x0, np.complex128)[:, None]), x[:, :-1]], axis=1)
+    glam = (gu * np.conj(xprev)).sum(axis=(0, 1))
+    gx0 = None if x0 is None else lc * gu[:, 0]
+    return glam, gu, gx0
+
+
+def scan_torch(coef, inp, x0=None):
+    """x_t = coef_t x_{t-1} + inp_t as a plain torch loop (real or complex; coef may be (C,)
+    or (B,T,C)), differentiable by autograd."""
+    import torch
+    B, T, C = inp.shape
+    s = torch.zeros((B, C), dtype=inp.dtype) if x0 is None else x0
+    out = []
+    for t in range(T):
+        ct = coef if coef.dim() == 1 else coef[:, t]
+        s = ct * s + inp[:, t]
+        out.append(s)
+    return torch.stack(out, dim=1)

@@ -41,6 +41,16 @@ MUTANTS = [
     ("complex_conj_lambda", "s = L * s + ut;", "s = conj(L) * s + ut;"),
     ("complex_x0_transposed", "if (x0) s = (double)x0[2 * (b * C + c)] + (double)x0[2 * (b * C + c) + 1] * I;",
      "if (x0) s = (double)x0[2 * (b * C + c) + 1] + (double)x0[2 * (b * C + c)] * I;"),
+    ("real_bwd_coefficient_not_shifted", "const double anext = (t + 1 < T) ? (double)a[o + C] : 0.0;",
+     "const double anext = (t + 1 < T) ? (double)a[o] : 0.0;"),
+    ("real_bwd_ga_uses_current_x", "const double xprev = (t > 0) ? x[o - C] : (x0 ? (double)x0[b * C + c] : 0.0);",
+     "const double xprev = x[o];"),
+    ("real_bwd_gx0_without_a0", "if (gx0) gx0[b * C + c] = (T > 0 && x0) ? (double)a[base] * s : 0.0;",
+     "if (gx0) gx0[b * C + c] = (T > 0 && x0) ? s : 0.0;"),
+    ("complex_bwd_lambda_not_conjugated",
+     "const double complex Lc = conj((double)lam[2 * c] + (double)lam[2 * c + 1] * I);",
+     "const double complex Lc = (double)lam[2 * c] + (double)lam[2 * c + 1] * I;"),
+    ("complex_bwd_glam_x_not_conjugated", "acc += s * conj(xp);", "acc += s * xp;"),
 ]
 
 
@@ -70,6 +80,22 @@ def _pins_pass(lib) -> bool:
     xc0 = (rng.standard_normal((2, 3)) + 1j * rng.standard_normal((2, 3))).astype(np.complex64)
     ok &= np.allclose(oracle.scan_complex(lr["lam"], lr["u"], xc0, lib=lib),
                       brute.scan_complex_sums(lr["lam"], lr["u"], xc0), rtol=1e-11, atol=1e-12)
+
+    # Scan adjoints against torch autograd on a plain loop (forward x from the pinned sums).
+    gxr = rng.standard_normal(a.shape).astype(np.float32)
+    x = brute.scan_real_sums(a, b, x0)
+    mine = oracle.scan_real_backward(a, x, gxr, x0, lib=lib)
+    ta, tb, tx0 = (torch.tensor(z, dtype=torch.float64, requires_grad=True) for z in (a, b, x0))
+    brute.scan_torch(ta, tb, tx0).backward(torch.tensor(gxr, dtype=torch.float64))
+    for m, ref in zip(mine, (ta, tb, tx0)):
+        ok &= np.allclose(m, ref.grad.numpy(), rtol=1e-10, atol=1e-11)
+    gxc = (rng.standard_normal(lr["u"].shape) + 1j * rng.standard_normal(lr["u"].shape)).astype(np.complex64)
+    xc = brute.scan_complex_sums(lr["lam"], lr["u"], xc0)
+    mine = oracle.scan_complex_backward(lr["lam"], xc, gxc, xc0, lib=lib)
+    tl, tu, tc0 = (torch.tensor(z, dtype=torch.complex128, requires_grad=True) for z in (lr["lam"], lr["u"], xc0))
+    brute.scan_torch(tl, tu, tc0).backward(torch.tensor(gxc, dtype=torch.complex128))
+    for m, ref in zip(mine, (tl, tu, tc0)):
+        ok &= np.allclose(m, ref.grad.numpy(), rtol=1e-10, atol=1e-11)
     return bool(ok)
 
 
