@@ -11,6 +11,8 @@
  *   linrec_scan_complex           x_t = lambda * x_{t-1} + u_t (the LRU write-up on
  *                                 "Resurrecting Recurrent Neural Networks for Long
  *                                 Sequences", diagonal complex recurrence, eq. lr-xx)
+ *   linrec_scan_real_backward,    the adjoints (backward passes) of the two scans
+ *   linrec_scan_complex_backward
  *
  * Conventions shared by every entry point:
  *  - Pointers are DEVICE pointers (hipMalloc / torch CUDA-on-ROCm memory) unless a
@@ -25,7 +27,9 @@
  *      B, T or C negative, or B*T*C*element size overflowing int64
  *                                                         -> LINREC_ERR_INVALID_ARG
  *      any of B, T, C equal to 0                          -> LINREC_OK, nothing enqueued and
- *        no pointer read (wkv4_backward still zero-fills gw and gu when C > 0)
+ *        no pointer read, except that the gradient sums over an empty batch or sequence
+ *        are zero-filled: gw, gu (wkv4_backward) and glambda (linrec_scan_complex_backward)
+ *        when C > 0, and gx0 of the scan backwards when given and B, C > 0
  *      a required pointer NULL (for a non-empty shape)    -> LINREC_ERR_INVALID_ARG
  *      ws_bytes below the workspace size                  -> LINREC_ERR_WORKSPACE
  *      a pointer not aligned to its element size (4 B for float, 8 B for complex64)
@@ -73,6 +77,7 @@ const char *linrec_last_error(void);
 size_t wkv4_forward_workspace_size(int64_t B, int64_t T, int64_t C);
 size_t wkv4_backward_workspace_size(int64_t B, int64_t T, int64_t C);
 size_t linrec_scan_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex);
+size_t linrec_scan_backward_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex);
 
 /*
  * WKV-4 forward, RWKV-LLM page, section "Time-mixing block", eq. (14).  For each batch
@@ -134,6 +139,41 @@ int linrec_scan_real(int64_t B, int64_t T, int64_t C,
 int linrec_scan_complex(int64_t B, int64_t T, int64_t C,
                         const float *lambda, const float *u, const float *x0, float *x,
                         void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Adjoint of linrec_scan_real (the pages give no backward; this is the chain rule of the
+ * scan form).  Given the forward output x and the upstream gradient gx = dL/dx, runs
+ * backwards in time
+ *
+ *   gb[b,t,c] = gx[b,t,c] + a[b,t+1,c] * gb[b,t+1,c]      (gb[b,T-1,c] = gx[b,T-1,c])
+ *   ga[b,t,c] = gb[b,t,c] * x[b,t-1,c]                    (x[b,-1,c] = x0[b,c], or 0)
+ *   gx0[b,c]  = a[b,0,c] * gb[b,0,c]
+ *
+ *   a, x, gx (B,T,C) float32 inputs (x: the forward output for these a, b, x0);
+ *   x0 (B,C) float32 or NULL (zero);  ga, gb (B,T,C) float32 outputs (dL/da, dL/db);
+ *   gx0 (B,C) float32 output or NULL when the initial state's gradient is not wanted.
+ */
+int linrec_scan_real_backward(int64_t B, int64_t T, int64_t C,
+                              const float *a, const float *x0, const float *x, const float *gx,
+                              float *ga, float *gb, float *gx0,
+                              void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Adjoint of linrec_scan_complex, for a real loss L with complex gradients taken as
+ * dL/dRe + i dL/dIm (so that dL = Re sum conj(g) dz).  Backwards in time:
+ *
+ *   gu[b,t,c]  = gx[b,t,c] + conj(lambda[c]) * gu[b,t+1,c]
+ *   glambda[c] = sum over b and t of gu[b,t,c] * conj(x[b,t-1,c])   (x[b,-1,c] = x0 or 0)
+ *   gx0[b,c]   = conj(lambda[c]) * gu[b,0,c]
+ *
+ *   lambda (C), x, gx (B,T,C) complex64 inputs (x: the forward output);  x0 (B,C) or NULL;
+ *   glambda (C) complex64 output, summed over batch and time in a fixed order;
+ *   gu (B,T,C) complex64 output (dL/du);  gx0 (B,C) complex64 output or NULL.
+ */
+int linrec_scan_complex_backward(int64_t B, int64_t T, int64_t C,
+                                 const float *lambda, const float *x0, const float *x,
+                                 const float *gx, float *glambda, float *gu, float *gx0,
+                                 void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

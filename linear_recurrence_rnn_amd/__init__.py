@@ -1,13 +1,13 @@
 """MI355X (gfx950) per-channel linear recurrences: RWKV-4 WKV forward/backward and
-real/complex diagonal scans, as hand-written HIP kernels behind a C ABI
+real/complex diagonal scans with their adjoints, as hand-written HIP kernels behind a C ABI
 (``include/linrec.h``).  The Python functions here marshal torch tensors to that ABI.
 
 The binding is imported lazily so that ``linear_recurrence_rnn_amd.workloads`` (the seeded
 input generators) can be used without loading the GPU library.
 """
 
-__all__ = ["wkv4_forward", "wkv4_backward", "scan_real", "scan_complex", "workspace_size",
-           "LinrecError"]
+__all__ = ["wkv4_forward", "wkv4_backward", "scan_real", "scan_complex", "scan_real_backward",
+           "scan_complex_backward", "workspace_size", "LinrecError"]
 
 
 def __getattr__(name):

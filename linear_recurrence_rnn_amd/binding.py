@@ -65,6 +65,11 @@ def load(path: str | None = None):
         lib.linrec_scan_real.argtypes = [_I64, _I64, _I64] + [_VP] * 4 + [_VP, _SZ, _VP]
         lib.linrec_scan_complex.restype = ctypes.c_int
         lib.linrec_scan_complex.argtypes = [_I64, _I64, _I64] + [_VP] * 4 + [_VP, _SZ, _VP]
+        lib.linrec_scan_backward_workspace_size.restype = _SZ
+        lib.linrec_scan_backward_workspace_size.argtypes = [_I64, _I64, _I64, ctypes.c_int]
+        for name in ("linrec_scan_real_backward", "linrec_scan_complex_backward"):
+            getattr(lib, name).restype = ctypes.c_int
+            getattr(lib, name).argtypes = [_I64, _I64, _I64] + [_VP] * 7 + [_VP, _SZ, _VP]
         if path is None:
             _lib = lib
         return lib
@@ -115,7 +120,8 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def workspace_size(op: str, B: int, T: int, C: int) -> int:
-    """Bytes of workspace ``op`` needs ('wkv4_forward', 'wkv4_backward', 'scan_real', 'scan_complex')."""
+    """Bytes of workspace ``op`` needs ('wkv4_forward', 'wkv4_backward', 'scan_real', 'scan_complex',
+    'scan_real_backward', 'scan_complex_backward')."""
     lib = load()
     if op == "wkv4_forward":
         return int(lib.wkv4_forward_workspace_size(B, T, C))
@@ -125,6 +131,10 @@ def workspace_size(op: str, B: int, T: int, C: int) -> int:
         return int(lib.linrec_scan_workspace_size(B, T, C, 0))
     if op == "scan_complex":
         return int(lib.linrec_scan_workspace_size(B, T, C, 1))
+    if op == "scan_real_backward":
+        return int(lib.linrec_scan_backward_workspace_size(B, T, C, 0))
+    if op == "scan_complex_backward":
+        return int(lib.linrec_scan_backward_workspace_size(B, T, C, 1))
     raise KeyError(op)
 
 
@@ -200,3 +210,52 @@ def scan_complex(lam, u, x0=None, out=None, workspace=None):
     _check(lib.linrec_scan_complex(B, T, C, _ptr(lam), _ptr(u), _ptr(x0), _ptr(x), _ptr(ws), nws,
                                    _stream(dev)), "linrec_scan_complex")
     return x
+
+
+def scan_real_backward(a, x, gx, x0=None, want_gx0=None, out=None, workspace=None):
+    """(ga, gb, gx0) = adjoint of x_t = a_t x_{t-1} + b_t for dL/dx = gx, given the forward
+    output x.  gx0 is computed when ``want_gx0`` (default: when x0 is given), else None."""
+    lib = load()
+    B, T, C = a.shape
+    dev = a.device
+    for name, t in (("a", a), ("x", x), ("gx", gx)):
+        _expect(t, name, torch.float32, (B, T, C), dev)
+    if x0 is not None:
+        _expect(x0, "x0", torch.float32, (B, C), dev)
+    if want_gx0 is None:
+        want_gx0 = x0 is not None
+    if out is None:
+        ga, gb = torch.empty_like(a), torch.empty_like(a)
+        gx0 = torch.empty((B, C), dtype=torch.float32, device=dev) if want_gx0 else None
+    else:
+        ga, gb, gx0 = out
+    ws, nws = _workspace(int(lib.linrec_scan_backward_workspace_size(B, T, C, 0)), dev, workspace)
+    _check(lib.linrec_scan_real_backward(B, T, C, _ptr(a), _ptr(x0), _ptr(x), _ptr(gx), _ptr(ga), _ptr(gb),
+                                         _ptr(gx0), _ptr(ws), nws, _stream(dev)), "linrec_scan_real_backward")
+    return ga, gb, gx0
+
+
+def scan_complex_backward(lam, x, gx, x0=None, want_gx0=None, out=None, workspace=None):
+    """(glam, gu, gx0) = adjoint of x_t = lam x_{t-1} + u_t for dL/dx = gx (complex
+    gradients as dL/dRe + i dL/dIm), given the forward output x."""
+    lib = load()
+    B, T, C = x.shape
+    dev = x.device
+    for name, t in (("x", x), ("gx", gx)):
+        _expect(t, name, torch.complex64, (B, T, C), dev)
+    _expect(lam, "lam", torch.complex64, (C,), dev)
+    if x0 is not None:
+        _expect(x0, "x0", torch.complex64, (B, C), dev)
+    if want_gx0 is None:
+        want_gx0 = x0 is not None
+    if out is None:
+        glam = torch.empty(C, dtype=torch.complex64, device=dev)
+        gu = torch.empty_like(x)
+        gx0 = torch.empty((B, C), dtype=torch.complex64, device=dev) if want_gx0 else None
+    else:
+        glam, gu, gx0 = out
+    ws, nws = _workspace(int(lib.linrec_scan_backward_workspace_size(B, T, C, 1)), dev, workspace)
+    _check(lib.linrec_scan_complex_backward(B, T, C, _ptr(lam), _ptr(x0), _ptr(x), _ptr(gx), _ptr(glam),
+                                            _ptr(gu), _ptr(gx0), _ptr(ws), nws, _stream(dev)),
+           "linrec_scan_complex_backward")
+    return glam, gu, gx0

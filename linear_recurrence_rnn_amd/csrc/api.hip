@@ -72,9 +72,13 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
     } else if (kind == linrec::kKindReal) {
         p.nw = 8;
         p.L = 16;
+    } else if (kind == linrec::kKindRealBwd) {
+        p.nw = 8;
+        p.L = 16;
     } else {
-        // Complex: one channel per lane over 32-step chunks (slabs of 256 steps) halves the
-        // look-back chains of a single long sequence; two channels per lane take 16 steps.
+        // Complex (and its adjoint): one channel per lane over 32-step chunks (slabs of 256
+        // steps) halves the look-back chains of a single long sequence; two channels per lane
+        // take 16 steps.
         p.nw = 8;
         p.L = vec == 1 ? 32 : 16;
     }
@@ -88,10 +92,16 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
     p.ws_bytes = 0;
     if (p.nslab > 1)
         p.ws_bytes = align256((size_t)nwg * 8) + 2 * align256((size_t)(nwg * cw) * linrec::agg_bytes(kind));
+    if (kind == linrec::kKindComplexBwd)  // per-slab glam sums and their first-stage sums
+        p.ws_bytes += align256((size_t)(nwg * cw) * 16) +
+                      align256((size_t)(ceil_div(p.nslab, linrec::kPartBlock) * C) * 16);
     return p;
 }
 
-int vmax_of(int kind) { return kind == linrec::kKindComplex ? 2 : 4; }
+int vmax_of(int kind) {
+    if (kind == linrec::kKindRealBwd || kind == linrec::kKindComplexBwd) return 1;
+    return kind == linrec::kKindComplex ? 2 : 4;
+}
 
 // Channels per lane: the widest the alignment allows, narrowed by the default policy
 // (WKV and complex: 1, real scan: 2) or by LINREC_VEC (tests and tuning).
@@ -113,6 +123,7 @@ int pick_vec(int kind, int vec_aligned) {
 size_t scan_ws_bytes(int kind, int64_t B, int64_t T, int64_t C) {
     size_t best = 0;
     for (int vec : {vmax_of(kind), 2, 1}) {
+        if (vec > vmax_of(kind)) continue;
         const size_t x = scan_plan(kind, vec, B, T, C).ws_bytes;
         best = x > best ? x : best;
     }
@@ -159,7 +170,13 @@ linrec::ScanGeom geom_of(int kind, const linrec::ScanPlan& p, int64_t B, int64_t
     char* rec = (char*)ws + align256((size_t)nwg * 8);
     g.rec_agg = rec;
     g.rec_incl = rec + align256((size_t)(nwg * cw) * linrec::agg_bytes(kind));
-    if (p.nslab <= 1) g.flags = nullptr, g.rec_agg = g.rec_incl = nullptr;
+    char* after = (char*)g.rec_incl + align256((size_t)(nwg * cw) * linrec::agg_bytes(kind));
+    if (p.nslab <= 1) g.flags = nullptr, g.rec_agg = g.rec_incl = nullptr, after = (char*)ws;
+    g.part = g.part2 = nullptr;
+    if (kind == linrec::kKindComplexBwd) {
+        g.part = reinterpret_cast<double*>(after);
+        g.part2 = reinterpret_cast<double*>(after + align256((size_t)(nwg * cw) * 16));
+    }
     return g;
 }
 
@@ -201,6 +218,11 @@ LINREC_API size_t wkv4_forward_workspace_size(int64_t B, int64_t T, int64_t C) {
 LINREC_API size_t linrec_scan_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex) {
     if (B < 0 || T < 0 || C < 0 || B == 0 || T == 0 || C == 0) return 0;
     return scan_ws_bytes(is_complex ? linrec::kKindComplex : linrec::kKindReal, B, T, C);
+}
+
+LINREC_API size_t linrec_scan_backward_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex) {
+    if (B < 0 || T < 0 || C < 0 || B == 0 || T == 0 || C == 0) return 0;
+    return scan_ws_bytes(is_complex ? linrec::kKindComplexBwd : linrec::kKindRealBwd, B, T, C);
 }
 
 LINREC_API size_t wkv4_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
@@ -269,6 +291,60 @@ LINREC_API int linrec_scan_complex(int64_t B, int64_t T, int64_t C, const float*
     return hip_status(linrec::run_scan_complex(A, geom_of(linrec::kKindComplex, p, B, T, C, workspace), p,
                                                (hipStream_t)stream),
                       "linrec_scan_complex launch");
+}
+
+LINREC_API int linrec_scan_real_backward(int64_t B, int64_t T, int64_t C, const float* a, const float* x0,
+                                         const float* x, const float* gx, float* ga, float* gb, float* gx0,
+                                         void* workspace, size_t ws_bytes, void* stream) {
+    int st = check_shape(B, T, C, 4);
+    if (st) return st;
+    if (B == 0 || C == 0) return ok();
+    if (gx0 && !aligned(gx0, 4)) return fail(LINREC_ERR_UNSUPPORTED, "gx0 not 4-byte aligned");
+    if (T == 0) {
+        // No steps: the gradient of the initial state is zero.
+        if (!gx0) return ok();
+        return hip_status(linrec::run_fill_zero(gx0, B * C, (hipStream_t)stream), "linrec_scan_real_backward zero-fill");
+    }
+    if (!a || !x || !gx || !ga || !gb) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void* ptrs[] = {a, x, gx, ga, gb};
+    for (const void* p : ptrs)
+        if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    if (x0 && !aligned(x0, 4)) return fail(LINREC_ERR_UNSUPPORTED, "x0 not 4-byte aligned");
+    const linrec::ScanPlan p = scan_plan(linrec::kKindRealBwd, 1, B, T, C);
+    if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
+    const linrec::RealBwdArgs A{a, x0, x, gx, ga, gb, gx0};
+    return hip_status(linrec::run_scan_real_backward(A, geom_of(linrec::kKindRealBwd, p, B, T, C, workspace), p,
+                                                     (hipStream_t)stream),
+                      "linrec_scan_real_backward launch");
+}
+
+LINREC_API int linrec_scan_complex_backward(int64_t B, int64_t T, int64_t C, const float* lambda,
+                                            const float* x0, const float* x, const float* gx, float* glambda,
+                                            float* gu, float* gx0, void* workspace, size_t ws_bytes,
+                                            void* stream) {
+    int st = check_shape(B, T, C, 8);
+    if (st) return st;
+    if (C == 0) return ok();
+    if (!glambda) return fail(LINREC_ERR_INVALID_ARG, "glambda is NULL");
+    if (!aligned(glambda, 8) || (gx0 && !aligned(gx0, 8)))
+        return fail(LINREC_ERR_UNSUPPORTED, "complex64 pointer not 8-byte aligned");
+    if (B == 0 || T == 0) {
+        // Empty sums: glambda = 0, and the gradient of the initial state is zero.
+        hipError_t e = linrec::run_fill_zero(glambda, 2 * C, (hipStream_t)stream);
+        if (e == hipSuccess && gx0 && B > 0) e = linrec::run_fill_zero(gx0, 2 * B * C, (hipStream_t)stream);
+        return hip_status(e, "linrec_scan_complex_backward zero-fill");
+    }
+    if (!lambda || !x || !gx || !gu) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void* ptrs[] = {lambda, x, gx, gu};
+    for (const void* p : ptrs)
+        if (!aligned(p, 8)) return fail(LINREC_ERR_UNSUPPORTED, "complex64 pointer not 8-byte aligned");
+    if (x0 && !aligned(x0, 8)) return fail(LINREC_ERR_UNSUPPORTED, "x0 not 8-byte aligned");
+    const linrec::ScanPlan p = scan_plan(linrec::kKindComplexBwd, 1, B, T, C);
+    if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
+    const linrec::CplxBwdArgs A{lambda, x0, x, gx, gu, gx0};
+    return hip_status(linrec::run_scan_complex_backward(A, glambda, geom_of(linrec::kKindComplexBwd, p, B, T, C, workspace),
+                                                        p, (hipStream_t)stream),
+                      "linrec_scan_complex_backward launch");
 }
 
 LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,

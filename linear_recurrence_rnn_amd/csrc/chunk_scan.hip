@@ -42,7 +42,21 @@ namespace {
 // per-channel state is larger) spill at that budget and keep the compiler's choice.
 template <class Op, int VEC, int L>
 constexpr int scan_waves_per_eu() {
-    return (VEC * L <= 16 && (VEC == 1 || std::is_same<Op, RealOp>::value)) ? 7 : 1;
+    return (!Op::kReverse && VEC * L <= 16 && (VEC == 1 || std::is_same<Op, RealOp>::value)) ? 7 : 1;
+}
+
+// Addressing of a run of n consecutive logical steps starting at logical step tl of a
+// sequence of T: its lowest row (the buffer base) and the Rows of its steps.  Operators in
+// reverse time visit the sequence from its last step.
+template <bool REV>
+__device__ __forceinline__ void run_rows(int64_t T, int64_t tl, int n, unsigned rowb, int64_t& row, Rows& rows) {
+    if constexpr (REV) {
+        row = n > 0 ? T - tl - n : 0;
+        rows = {(unsigned)(n > 0 ? n - 1 : 0) * rowb, -(int)rowb, T - 1 - tl, -1};
+    } else {
+        row = tl;
+        rows = {0u, (int)rowb, tl, 1};
+    }
 }
 
 template <class Op, int VEC, int NW, int L>
@@ -54,14 +68,16 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     constexpr int CW = 64 * VEC;
     constexpr int SLAB = NW * L;
     constexpr int EF = Op::kFloats;
+    using Part = typename Op::Part;
     __shared__ Agg sh[NW][CW];    // chunk aggregates, then sh[x] = chunks 0 .. x-1 combined
     __shared__ Agg sh_carry[CW];  // the carry into the slab
+    __shared__ Part sh_part[Op::kParts ? NW : 1][Op::kParts ? CW : 1];  // chunks' shares of per-slab sums
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int64_t G = g.B * g.ngrp;
-    const int64_t s = (int64_t)blockIdx.x / G;  // slab: slowest, so predecessors come first
+    const int64_t s = (int64_t)blockIdx.x / G;  // slab in the recurrence's order: predecessors come first
     const int64_t gi = (int64_t)blockIdx.x - s * G;
     const int64_t b = gi / g.ngrp, grp = gi - b * g.ngrp;
     const int64_t c0 = grp * CW + (int64_t)lane * VEC;
@@ -76,21 +92,23 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
 
     const unsigned rowb = (unsigned)(g.C * EF * 4);           // bytes per time step
     const unsigned voff = (unsigned)(lane * VEC * EF * 4);    // this lane's bytes in the row
-    const int64_t total = g.B * g.T * g.C;
 
     if (w < NW) {
         // ---- compute wave: chunk w of the slab, held in registers ----
-        const int n = active ? chunk_len(w) : 0;
-        const int64_t base = (b * g.T + t_slab + (int64_t)w * L) * g.C + grp * CW;
-        const typename Op::Res R = Op::res(A, base, (total - base) * EF * 4);
+        const int nu = chunk_len(w);  // steps of the chunk (wave-uniform)
+        const int n = active ? nu : 0;
+        int64_t row;
+        Rows rows;
+        run_rows<Op::kReverse>(g.T, t_slab + (int64_t)w * L, nu, rowb, row, rows);
+        const typename Op::Res R = Op::res(A, g, b, row, grp * CW);
         In in[L][VEC];
         if (n == L) {
 #pragma unroll
-            for (int j = 0; j < L; ++j) Op::template load<VEC>(R, voff, j * rowb, in[j]);
+            for (int j = 0; j < L; ++j) Op::template load<VEC>(R, voff, rows, j, in[j]);
         } else {
 #pragma unroll
             for (int j = 0; j < L; ++j) {
-                if (j < n) Op::template load<VEC>(R, voff, j * rowb, in[j]);
+                if (j < n) Op::template load<VEC>(R, voff, rows, j, in[j]);
                 else Op::template zero<VEC>(in[j]);
             }
         }
@@ -99,13 +117,19 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
         for (int e = 0; e < VEC; ++e) sh[w][lane * VEC + e] = Op::template reduce<L, VEC>(ch[e], in, e, n, loc[e]);
         __syncthreads();  // B1: chunk aggregates are in sh
         __syncthreads();  // B2: the slab's carry is in sh_carry, my chunk's prefix in sh[w]
+        Part part{};
         if (n > 0) {
             Agg cin[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 cin[e] = (w == 0) ? sh_carry[lane * VEC + e]
                                   : Op::combine(ch[e], sh_carry[lane * VEC + e], sh[w][lane * VEC + e], w * L);
-            Op::template run<L, VEC>(R, ch, cin, in, loc, n, voff, rowb);
+            part = Op::template run<L, VEC>(R, ch, cin, in, loc, n, voff, rows);
+        }
+        if constexpr (Op::kParts) {
+            static_assert(VEC == 1, "per-slab sums are kept for one channel per lane");
+            sh_part[w][lane] = part;
+            __syncthreads();  // B3: the chunks' shares are in sh_part
         }
         return;
     }
@@ -127,7 +151,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
             sh[x][lane * VEC + e] = mine[e];
             mine[e] = Op::combine(ch[e], mine[e], chunk, chunk_len(x));
         }
-        carry[e] = active ? Op::init(A, b, c0 + e, g.C) : Op::identity();
+        carry[e] = active ? Op::init(A, g, b, c0 + e) : Op::identity();
     }
     if (has_succ) publish<VEC>(chn, s, lane, mine, false);
     auto fold = [&](Agg (&c)[VEC], const Agg (&x)[VEC], int64_t) {
@@ -136,14 +160,16 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     };
     // A slab whose aggregate was not published in time is recomputed from its inputs.
     auto recompute = [&](int64_t jj, Agg (&x)[VEC]) {
-        const int64_t bj = (b * g.T + jj * SLAB) * g.C + grp * CW;
-        const typename Op::Res Rj = Op::res(A, bj, (total - bj) * EF * 4);
+        int64_t rowj;
+        Rows rj;
+        run_rows<Op::kReverse>(g.T, jj * SLAB, SLAB, rowb, rowj, rj);  // predecessors are full slabs
+        const typename Op::Res Rj = Op::res(A, g, b, rowj, grp * CW);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[e] = Op::identity();
         if (active) {
             for (int t = 0; t < SLAB; ++t) {
                 In xi[VEC];
-                Op::template load<VEC>(Rj, voff, t * rowb, xi);
+                Op::template load<VEC>(Rj, voff, rj, t, xi);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) x[e] = Op::step(ch[e], x[e], xi[e]);
             }
@@ -160,6 +186,56 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
         for (int e = 0; e < VEC; ++e) incl[e] = Op::combine(ch[e], carry[e], mine[e], slab_n);
         publish<VEC>(chn, s, lane, incl, true);
     }
+    if constexpr (Op::kParts) {
+        __syncthreads();  // B3
+        // The slab's sum: chunks added in order.
+        double re = 0.0, im = 0.0;
+        for (int x = 0; x < NW; ++x) {
+            re += sh_part[x][lane].re;
+            im += sh_part[x][lane].im;
+        }
+        double* out = g.part + 2 * ((gi * g.nslab + s) * CW + lane);
+        out[0] = re;
+        out[1] = im;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.f;
+}
+
+// glam, first stage: block (group, k) adds slabs [k kPartBlock, (k+1) kPartBlock) of every
+// batch row, rows in ascending order, slabs in ascending order, for its 64 channels.
+__global__ __launch_bounds__(64) void part_sum_kernel(ScanGeom g) {
+    const int64_t grp = blockIdx.x, k = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int64_t c = grp * 64 + lane;
+    if (c >= g.C) return;
+    const int64_t s0 = k * kPartBlock, s1 = min(g.nslab, s0 + kPartBlock);
+    double re = 0.0, im = 0.0;
+    for (int64_t b = 0; b < g.B; ++b) {
+        const double* p = g.part + 2 * (((b * g.ngrp + grp) * g.nslab) * 64 + lane);
+        for (int64_t s = s0; s < s1; ++s) {
+            re += p[2 * s * 64];
+            im += p[2 * s * 64 + 1];
+        }
+    }
+    g.part2[2 * (k * g.C + c)] = re;
+    g.part2[2 * (k * g.C + c) + 1] = im;
+}
+
+// glam, second stage: the first-stage sums of a channel, in order, as complex64.
+__global__ __launch_bounds__(256) void part_final_kernel(ScanGeom g, int64_t nk, float* __restrict__ glam) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= g.C) return;
+    double re = 0.0, im = 0.0;
+    for (int64_t k = 0; k < nk; ++k) {
+        re += g.part2[2 * (k * g.C + c)];
+        im += g.part2[2 * (k * g.C + c) + 1];
+    }
+    glam[2 * c] = (float)re;
+    glam[2 * c + 1] = (float)im;
 }
 
 template <class Op, int VEC, int NW, int L>
@@ -198,8 +274,8 @@ hipError_t dispatch(const typename Op::Args& A, const ScanGeom& g, const ScanPla
 }  // namespace
 
 bool scan_shape_supported(int kind, int vec, int nw, int L) {
-    const int vmax = kind == kKindComplex ? 2 : 4;
-    const bool vec_ok = vec == vmax || vec == 2 || vec == 1;
+    const int vmax = kind == kKindComplex ? 2 : ((kind == kKindRealBwd || kind == kKindComplexBwd) ? 1 : 4);
+    const bool vec_ok = vec == vmax || (vec == 2 && vmax >= 2) || vec == 1;
     return vec_ok && ((nw == 4 && L == 16) || (nw == 8 && L == 8) || (nw == 8 && L == 16) ||
                       (kind != kKindWkv && vec == 1 && nw == 8 && L == 32));
 }
@@ -213,11 +289,35 @@ hipError_t run_scan_real(const RealArgs& A, const ScanGeom& g, const ScanPlan& p
 hipError_t run_scan_complex(const CplxArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st) {
     return dispatch<CplxOp, 2>(A, g, p, st);
 }
+// The adjoints keep one channel per lane (their steps also hold x_{t-1}).
+hipError_t run_scan_real_backward(const RealBwdArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st) {
+    if (p.vec != 1) return hipErrorInvalidValue;
+    return dispatch_shape<RealBwdOp, 1>(A, g, p, st);
+}
+hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const ScanGeom& g, const ScanPlan& p,
+                                     hipStream_t st) {
+    if (p.vec != 1) return hipErrorInvalidValue;
+    hipError_t e = dispatch_shape<CplxBwdOp, 1>(A, g, p, st);
+    if (e != hipSuccess) return e;
+    const int64_t nk = (g.nslab + kPartBlock - 1) / kPartBlock;
+    hipLaunchKernelGGL(part_sum_kernel, dim3((unsigned)g.ngrp, (unsigned)nk), dim3(64), 0, st, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(part_final_kernel, dim3((unsigned)((g.C + 255) / 256)), dim3(256), 0, st, g, nk, glam);
+    return hipGetLastError();
+}
+
+hipError_t run_fill_zero(float* p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
 
 size_t agg_bytes(int kind) {
     switch (kind) {
         case kKindWkv: return sizeof(WkvOp::Agg);
-        case kKindReal: return sizeof(RealOp::Agg);
+        case kKindReal:
+        case kKindRealBwd: return sizeof(RealOp::Agg);
         default: return sizeof(CplxOp::Agg);
     }
 }

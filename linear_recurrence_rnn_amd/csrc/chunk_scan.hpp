@@ -7,7 +7,7 @@
 
 namespace linrec {
 
-enum { kKindWkv = 0, kKindReal = 1, kKindComplex = 2 };
+enum { kKindWkv = 0, kKindReal = 1, kKindComplex = 2, kKindRealBwd = 3, kKindComplexBwd = 4 };
 
 // Operands of each recurrence (device pointers, (B,T,C) row-major, C fastest).
 struct WkvArgs {
@@ -30,6 +30,37 @@ struct CplxArgs {
     const float* x0;   // (B,C) complex64 or null
     float* x;          // (B,T,C) complex64
 };
+// Adjoints of the two linear scans (reverse time).
+struct RealBwdArgs {
+    const float* a;   // (B,T,C)
+    const float* x0;  // (B,C) or null
+    const float* x;   // (B,T,C) forward output
+    const float* gx;  // (B,T,C) dL/dx
+    float* ga;        // (B,T,C)
+    float* gb;        // (B,T,C)
+    float* gx0;       // (B,C) or null
+};
+struct CplxBwdArgs {
+    const float* lam;  // (C) complex64
+    const float* x0;   // (B,C) complex64 or null
+    const float* x;    // (B,T,C) complex64 forward output
+    const float* gx;   // (B,T,C) complex64 dL/dx
+    float* gu;         // (B,T,C) complex64
+    float* gx0;        // (B,C) complex64 or null
+};
+
+// Addressing of a run of consecutive steps (a chunk, or a slab being recomputed): logical
+// step j sits at byte offset soff(j) from the run's buffer base (its lowest row) and at
+// time t(j) of the sequence.  Scans in time order have rstep = +row bytes, tdir = +1;
+// scans in reverse time start from the run's last row.
+struct Rows {
+    unsigned s0;   // byte offset of logical step 0
+    int rstep;     // bytes from one logical step to the next (negative in reverse time)
+    int64_t t0;    // time of logical step 0
+    int tdir;      // +1 or -1
+    __device__ __forceinline__ unsigned soff(int j) const { return s0 + (unsigned)(j * rstep); }
+    __device__ __forceinline__ int64_t t(int j) const { return t0 + (int64_t)j * tdir; }
+};
 
 // Launch geometry.  A workgroup of nw waves owns one time slab (nw chunks of L steps) of
 // one channel group (64 lanes x vec channels); workgroups are numbered slab-major, so a
@@ -43,6 +74,8 @@ struct ScanGeom {
     uint64_t* flags;    // (B*ngrp*nslab) publication flags
     void* rec_agg;      // (B*ngrp*nslab, 64*vec) slab aggregates
     void* rec_incl;     // (B*ngrp*nslab, 64*vec) inclusive prefixes
+    double* part;       // (B*ngrp*nslab, 64*vec, 2) per-slab sums of operators that have them
+    double* part2;      // second-stage sums of those (see run_scan_complex_backward)
 };
 
 struct ScanPlan {
@@ -56,6 +89,13 @@ struct ScanPlan {
 hipError_t run_wkv_forward(const WkvArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
 hipError_t run_scan_real(const RealArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
 hipError_t run_scan_complex(const CplxArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
+hipError_t run_scan_real_backward(const RealBwdArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
+// Also sums g.part into glam (C complex64): g.part2 holds ceil(nslab / kPartBlock) x C pairs.
+hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const ScanGeom& g, const ScanPlan& p,
+                                     hipStream_t st);
+constexpr int kPartBlock = 64;  // slabs summed per first-stage block of the glam reduction
+// Writes n zero floats (a fill kernel, so that the call can be captured in a graph).
+hipError_t run_fill_zero(float* p, int64_t n, hipStream_t st);
 size_t agg_bytes(int kind);
 // Launch shapes that have kernels: (vec, nw, L) per kind.
 bool scan_shape_supported(int kind, int vec, int nw, int L);

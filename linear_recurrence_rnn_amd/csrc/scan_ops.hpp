@@ -5,8 +5,12 @@
 //   In       one time step's inputs (loaded with channel-contiguous vector loads),
 //   Agg      the state after a span of steps, and the span's effect on an incoming state,
 //   reduce   the aggregate of a chunk of n <= L steps started from the identity,
-//   combine  aggregate(s1 then s2) given the n2 steps s2 covers (s1 is earlier in time),
-//   run      the chunk's steps from an incoming state, writing one output per step.
+//   combine  aggregate(s1 then s2) given the n2 steps s2 covers (s1 is earlier in the
+//            recurrence's order),
+//   run      the chunk's steps from an incoming state, writing one output per step, and
+//            returning the lane's share of any per-slab sum (Part; empty for most).
+// Steps are addressed through Rows (chunk_scan.hpp): kReverse operators run backwards in
+// time, so their logical step j is time t0 - j.
 // Each combine is associative, which is what lets a sequence be cut into chunks whose
 // aggregates are scanned and then re-run from their carries (the two-halves split of the
 // LRU write-up, parallelisation section: x_T = lam^{T-t} x_t + local sum over (t, T]).
@@ -40,8 +44,13 @@ namespace linrec {
 // where M = p + frexp_exp(b) bounds log2 B (see wkv_math.hpp),
 // re-reading k from memory (its registers now hold g).
 // ----------------------------------------------------------------------------------
+struct NoPart {};
+
 struct WkvOp {
     using Args = WkvArgs;
+    static constexpr bool kReverse = false;
+    static constexpr bool kParts = false;
+    using Part = NoPart;
     struct Chan { float om, mu, lift, fast_lo; };  // lift = ceil(max(om, mu, 0))
     struct In { float kk, v; };           // kk becomes g_j after phase 1
     struct Local { float p, m0; };        // chunk exponent p and m_0 - p
@@ -57,17 +66,19 @@ struct WkvOp {
         return ch;
     }
     __device__ __forceinline__ static Agg identity() { return {0.f, 0.f, kEmpty}; }
-    __device__ __forceinline__ static Agg init(const Args&, int64_t, int64_t, int64_t) { return identity(); }
+    __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) { return identity(); }
 
     static constexpr int kFloats = 1;  // floats per channel element
     struct Res { rsrc_t k, v, y; };
-    __device__ __forceinline__ static Res res(const Args& A, int64_t base, int64_t nbytes) {
+    // Buffers of the run whose lowest row is time `row` of batch row b, from column col0.
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t base = (b * g.T + row) * g.C + col0, nbytes = (g.B * g.T * g.C - base) * 4;
         return {make_rsrc(A.k + base, nbytes), make_rsrc(A.v + base, nbytes), make_rsrc(A.y + base, nbytes)};
     }
     template <int VEC>
-    __device__ __forceinline__ static void load(const Res& R, unsigned voff, unsigned soff, In (&in)[VEC]) {
-        const FV<VEC> k = ldb<VEC>(R.k, voff, soff);
-        const FV<VEC> v = ldb<VEC>(R.v, voff, soff);
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const FV<VEC> k = ldb<VEC>(R.k, voff, rows.soff(j));
+        const FV<VEC> v = ldb<VEC>(R.v, voff, rows.soff(j));
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {k.v[e] * kLog2e, v.v[e]};
     }
@@ -117,9 +128,9 @@ struct WkvOp {
     }
 
     template <int L, int VEC>
-    __device__ __forceinline__ static void run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
                                const In (&in)[L][VEC], const Local (&loc)[VEC], int n, unsigned voff,
-                               unsigned rowb) {
+                               const Rows& rows) {
         float a[VEC], b[VEC], cs[VEC], us[VEC];
         bool fast[VEC];
 #pragma unroll
@@ -155,10 +166,10 @@ struct WkvOp {
                         a[e] = fmaf(up, vv, a[e]);
                         b[e] += up;
                     }
-                    stb<VEC>(R.y, voff, j * rowb, y);
+                    stb<VEC>(R.y, voff, rows.soff(j), y);
                 }
             }
-            return;
+            return {};
         }
         // Exact per-step running maximum (integer exponents), all channels of the lane.
         float pa[VEC], pb[VEC], pp[VEC];
@@ -167,7 +178,7 @@ struct WkvOp {
 #pragma unroll
         for (int j = 0; j < L; ++j) {
             if (j < n) {
-                const FV<VEC> kr = ldb<VEC>(R.k, voff, j * rowb);
+                const FV<VEC> kr = ldb<VEC>(R.k, voff, rows.soff(j));
                 FV<VEC> y;
     #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
@@ -181,9 +192,10 @@ struct WkvOp {
                     pb[e] = fmaf(pb[e], f1, f2);
                     pp[e] = q2;
                 }
-                stb<VEC>(R.y, voff, j * rowb, y);
+                stb<VEC>(R.y, voff, rows.soff(j), y);
             }
         }
+        return {};
     }
 };
 
@@ -196,6 +208,9 @@ struct WkvOp {
 
 struct RealOp {
     using Args = RealArgs;
+    static constexpr bool kReverse = false;
+    static constexpr bool kParts = false;
+    using Part = NoPart;
     struct Chan {};
     struct In { float a, b; };
     struct Local {};
@@ -204,19 +219,20 @@ struct RealOp {
     template <int L>
     __device__ __forceinline__ static Chan chan(const Args&, int64_t) { return {}; }
     __device__ __forceinline__ static Agg identity() { return {1.f, 0.f}; }
-    __device__ __forceinline__ static Agg init(const Args& A, int64_t b, int64_t c, int64_t C) {
-        return {1.f, A.x0 ? A.x0[b * C + c] : 0.f};
+    __device__ __forceinline__ static Agg init(const Args& A, const ScanGeom& g, int64_t b, int64_t c) {
+        return {1.f, A.x0 ? A.x0[b * g.C + c] : 0.f};
     }
 
     static constexpr int kFloats = 1;
     struct Res { rsrc_t a, b, x; };
-    __device__ __forceinline__ static Res res(const Args& A, int64_t base, int64_t nbytes) {
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t base = (b * g.T + row) * g.C + col0, nbytes = (g.B * g.T * g.C - base) * 4;
         return {make_rsrc(A.a + base, nbytes), make_rsrc(A.b + base, nbytes), make_rsrc(A.x + base, nbytes)};
     }
     template <int VEC>
-    __device__ __forceinline__ static void load(const Res& R, unsigned voff, unsigned soff, In (&in)[VEC]) {
-        const FV<VEC> a = ldb<VEC>(R.a, voff, soff);
-        const FV<VEC> b = ldb<VEC>(R.b, voff, soff);
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const FV<VEC> a = ldb<VEC>(R.a, voff, rows.soff(j));
+        const FV<VEC> b = ldb<VEC>(R.b, voff, rows.soff(j));
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {a.v[e], b.v[e]};
     }
@@ -248,9 +264,9 @@ struct RealOp {
     }
 
     template <int L, int VEC>
-    __device__ __forceinline__ static void run(const Res& R, const Chan (&)[VEC], const Agg (&cin)[VEC],
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&)[VEC], const Agg (&cin)[VEC],
                                const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
-                               unsigned rowb) {
+                               const Rows& rows) {
         float x[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[e] = cin[e].x;
@@ -263,9 +279,10 @@ struct RealOp {
                     x[e] = fmaf(in[j][e].a, x[e], in[j][e].b);
                     o.v[e] = x[e];
                 }
-                stb<VEC>(R.x, voff, j * rowb, o);
+                stb<VEC>(R.x, voff, rows.soff(j), o);
             }
         }
+        return {};
     }
 };
 
@@ -295,6 +312,9 @@ __device__ __forceinline__ void cpow64(double br, double bi, int64_t n, float& r
 
 struct CplxOp {
     using Args = CplxArgs;
+    static constexpr bool kReverse = false;
+    static constexpr bool kParts = false;
+    using Part = NoPart;
     struct Chan { float lr, li, Lr, Li; };  // lam and lam^L
     struct In { float r, i; };
     struct Local {};
@@ -309,19 +329,20 @@ struct CplxOp {
         return ch;
     }
     __device__ __forceinline__ static Agg identity() { return {1.f, 0.f, 0.f, 0.f}; }
-    __device__ __forceinline__ static Agg init(const Args& A, int64_t b, int64_t c, int64_t C) {
+    __device__ __forceinline__ static Agg init(const Args& A, const ScanGeom& g, int64_t b, int64_t c) {
         if (!A.x0) return identity();
-        return {1.f, 0.f, A.x0[2 * (b * C + c)], A.x0[2 * (b * C + c) + 1]};
+        return {1.f, 0.f, A.x0[2 * (b * g.C + c)], A.x0[2 * (b * g.C + c) + 1]};
     }
 
     static constexpr int kFloats = 2;
     struct Res { rsrc_t u, x; };
-    __device__ __forceinline__ static Res res(const Args& A, int64_t base, int64_t nbytes) {
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t base = (b * g.T + row) * g.C + col0, nbytes = (g.B * g.T * g.C - base) * 8;
         return {make_rsrc(A.u + 2 * base, nbytes), make_rsrc(A.x + 2 * base, nbytes)};
     }
     template <int VEC>
-    __device__ __forceinline__ static void load(const Res& R, unsigned voff, unsigned soff, In (&in)[VEC]) {
-        const FV<2 * VEC> t = ldb<2 * VEC>(R.u, voff, soff);
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const FV<2 * VEC> t = ldb<2 * VEC>(R.u, voff, rows.soff(j));
 #pragma unroll
         for (int e = 0; e < VEC; ++e) in[e] = {t.v[2 * e], t.v[2 * e + 1]};
     }
@@ -373,9 +394,9 @@ struct CplxOp {
     }
 
     template <int L, int VEC>
-    __device__ __forceinline__ static void run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
                                const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
-                               unsigned rowb) {
+                               const Rows& rows) {
         float xr[VEC], xi[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) { xr[e] = cin[e].xr; xi[e] = cin[e].xi; }
@@ -391,9 +412,180 @@ struct CplxOp {
                     o.v[2 * e] = xr[e];
                     o.v[2 * e + 1] = xi[e];
                 }
-                stb<2 * VEC>(R.x, voff, j * rowb, o);
+                stb<2 * VEC>(R.x, voff, rows.soff(j), o);
             }
         }
+        return {};
+    }
+};
+
+// ----------------------------------------------------------------------------------
+// Adjoint of the real scan (the pages give no backward; derived from the scan form):
+//   gb_t = gx_t + a_{t+1} gb_{t+1},  ga_t = gb_t x_{t-1} (x_{-1} = x0 or 0),  gx0 = a_0 gb_0.
+// Backwards in time it is the real scan itself with coefficients a_{t+1} (0 after the last
+// step) and inputs gx_t, so the aggregates, combine and step are RealOp's.
+// ----------------------------------------------------------------------------------
+struct RealBwdOp : RealOp {
+    using Args = RealBwdArgs;
+    static constexpr bool kReverse = true;
+    template <int L>
+    __device__ __forceinline__ static Chan chan(const Args&, int64_t) { return {}; }
+    __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) { return identity(); }
+
+    // an: a at the row above (a_{t+1}), xp: x at the row below (x_{t-1}); xshift is the
+    // row's bytes when the run starts at time 0, whose x_{t-1} is x0 instead.
+    struct Res { rsrc_t an, g, xp, ga, gb; unsigned xshift; int64_t T; const float* x0; const float* a0; float* gx0; };
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t total = g.B * g.T * g.C;
+        const int64_t base = (b * g.T + row) * g.C + col0;
+        const int64_t bn = base + g.C;                                           // row + 1
+        const int64_t bp = (b * g.T + (row > 0 ? row - 1 : 0)) * g.C + col0;     // row - 1
+        Res R;
+        R.an = make_rsrc(A.a + bn, (total - bn) * 4);
+        R.g = make_rsrc(A.gx + base, (total - base) * 4);
+        R.xp = make_rsrc(A.x + bp, (total - bp) * 4);
+        R.ga = make_rsrc(A.ga + base, (total - base) * 4);
+        R.gb = make_rsrc(A.gb + base, (total - base) * 4);
+        R.xshift = row > 0 ? 0u : (unsigned)(g.C * 4);
+        R.T = g.T;
+        R.x0 = A.x0 ? A.x0 + b * g.C + col0 : nullptr;
+        R.a0 = A.a + b * g.T * g.C + col0;
+        R.gx0 = A.gx0 ? A.gx0 + b * g.C + col0 : nullptr;
+        return R;
+    }
+    template <int VEC>
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const int64_t t = rows.t(j);
+        FV<VEC> an{};
+        if (t + 1 < R.T) an = ldb<VEC>(R.an, voff, rows.soff(j));
+        const FV<VEC> gx = ldb<VEC>(R.g, voff, rows.soff(j));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {an.v[e], gx.v[e]};
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
+                               const Rows& rows) {
+        const int lane_col = (int)(voff / 4);  // this lane's first channel in the group
+        FV<VEC> xp[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                if (rows.t(j) > 0) {
+                    xp[j] = ldb<VEC>(R.xp, voff, rows.soff(j) - R.xshift);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) xp[j].v[e] = R.x0 ? R.x0[lane_col + e] : 0.f;
+                }
+            }
+        }
+        float s[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[e] = cin[e].x;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                FV<VEC> gb, ga;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    s[e] = fmaf(in[j][e].a, s[e], in[j][e].b);
+                    gb.v[e] = s[e];
+                    ga.v[e] = s[e] * xp[j].v[e];
+                }
+                stb<VEC>(R.gb, voff, rows.soff(j), gb);
+                stb<VEC>(R.ga, voff, rows.soff(j), ga);
+                if (rows.t(j) == 0 && R.gx0) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) R.gx0[lane_col + e] = R.a0[lane_col + e] * s[e];
+                }
+            }
+        }
+        return {};
+    }
+};
+
+// ----------------------------------------------------------------------------------
+// Adjoint of the complex scan (gradients as dL/dRe + i dL/dIm; derived from eq. lr-xx):
+//   gu_t = gx_t + conj(lam) gu_{t+1},  glam = sum over batch and time of gu_t conj(x_{t-1}),
+//   gx0 = conj(lam) gu_0.
+// Backwards in time it is the complex scan with multiplier conj(lam), so the aggregates are
+// CplxOp's.  Each slab's share of glam is a Part, summed over the slab's chunks.
+// ----------------------------------------------------------------------------------
+struct CplxBwdOp : CplxOp {
+    using Args = CplxBwdArgs;
+    static constexpr bool kReverse = true;
+    static constexpr bool kParts = true;
+    struct Part { double re, im; };
+
+    template <int L>
+    __device__ __forceinline__ static Chan chan(const Args& A, int64_t c) {
+        Chan ch;
+        ch.lr = A.lam[2 * c];
+        ch.li = -A.lam[2 * c + 1];  // conj(lam)
+        cpow64((double)ch.lr, (double)ch.li, L, ch.Lr, ch.Li);
+        return ch;
+    }
+    __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) { return identity(); }
+
+    struct Res { rsrc_t g, xp, gu; unsigned xshift; const float* x0; float* gx0; };
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t total = g.B * g.T * g.C;
+        const int64_t base = (b * g.T + row) * g.C + col0;
+        const int64_t bp = (b * g.T + (row > 0 ? row - 1 : 0)) * g.C + col0;
+        Res R;
+        R.g = make_rsrc(A.gx + 2 * base, (total - base) * 8);
+        R.xp = make_rsrc(A.x + 2 * bp, (total - bp) * 8);
+        R.gu = make_rsrc(A.gu + 2 * base, (total - base) * 8);
+        R.xshift = row > 0 ? 0u : (unsigned)(g.C * 8);
+        R.x0 = A.x0 ? A.x0 + 2 * (b * g.C + col0) : nullptr;
+        R.gx0 = A.gx0 ? A.gx0 + 2 * (b * g.C + col0) : nullptr;
+        return R;
+    }
+    template <int VEC>
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const FV<2 * VEC> t = ldb<2 * VEC>(R.g, voff, rows.soff(j));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {t.v[2 * e], t.v[2 * e + 1]};
+    }
+    // Returns the lane's sum of gu_t conj(x_{t-1}) over the chunk (per channel: VEC == 1).
+    template <int L, int VEC>
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                               const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
+                               const Rows& rows) {
+        static_assert(VEC == 1, "the adjoint of the complex scan keeps one channel per lane");
+        const int lane_col = (int)(voff / 8);
+        FV<2> xp[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                if (rows.t(j) > 0) {
+                    xp[j] = ldb<2>(R.xp, voff, rows.soff(j) - R.xshift);
+                } else {
+                    xp[j].v[0] = R.x0 ? R.x0[2 * lane_col] : 0.f;
+                    xp[j].v[1] = R.x0 ? R.x0[2 * lane_col + 1] : 0.f;
+                }
+            }
+        }
+        float sr = cin[0].xr, si = cin[0].xi, ar = 0.f, ai = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                const float tr = fmaf(ch[0].lr, sr, fmaf(-ch[0].li, si, in[j][0].r));
+                si = fmaf(ch[0].lr, si, fmaf(ch[0].li, sr, in[j][0].i));
+                sr = tr;
+                FV<2> o;
+                o.v[0] = sr;
+                o.v[1] = si;
+                stb<2>(R.gu, voff, rows.soff(j), o);
+                ar = fmaf(sr, xp[j].v[0], fmaf(si, xp[j].v[1], ar));  // gu conj(x): real part
+                ai = fmaf(si, xp[j].v[0], fmaf(-sr, xp[j].v[1], ai));  // imaginary part
+                if (rows.t(j) == 0 && R.gx0) {
+                    R.gx0[2 * lane_col] = ch[0].lr * sr - ch[0].li * si;
+                    R.gx0[2 * lane_col + 1] = ch[0].lr * si + ch[0].li * sr;
+                }
+            }
+        }
+        return {(double)ar, (double)ai};
     }
 };
 

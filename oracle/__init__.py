@@ -173,9 +173,10 @@ def scan_complex(lam, u, x0=None, lib=None) -> np.ndarray:
     return x
 
 
-def scan_real_backward(a, x, gx, x0=None, lib=None):
+def scan_real_backward(a, x, gx, x0=None, want_gx0=None, lib=None):
     """(ga, gb (B,T,C), gx0 (B,C) or None) float64: the adjoint of x_t = a_t x_{t-1} + b_t
-    for upstream gradients gx, given the forward output x (float32 or float64)."""
+    for upstream gradients gx, given the forward output x (float32 or float64).  gx0 is
+    returned when ``want_gx0`` (default: when x0 is given)."""
     a = _f32(a)
     B, T, C = a.shape
     gx = _f32(gx, (B, T, C))
@@ -185,14 +186,14 @@ def scan_real_backward(a, x, gx, x0=None, lib=None):
     x0a = None if x0 is None else _f32(x0, (B, C))
     ga = np.empty((B, T, C), dtype=np.float64)
     gb = np.empty((B, T, C), dtype=np.float64)
-    gx0 = None if x0 is None else np.empty((B, C), dtype=np.float64)
+    gx0 = np.empty((B, C), dtype=np.float64) if (x0 is not None if want_gx0 is None else want_gx0) else None
     (lib or _load()).oracle_scan_real_backward(B, T, C, _p32(a), None if x0a is None else _p32(x0a),
                                                _p64(xd), _p32(gx), _p64(ga), _p64(gb),
                                                None if gx0 is None else _p64(gx0))
     return ga, gb, gx0
 
 
-def scan_complex_backward(lam, x, gx, x0=None, lib=None):
+def scan_complex_backward(lam, x, gx, x0=None, want_gx0=None, lib=None):
     """(glam (C,), gu (B,T,C), gx0 (B,C) or None) complex128: the adjoint of
     x_t = lam x_{t-1} + u_t (gradients as dL/dRe + i dL/dIm), given the forward output x."""
     gxc = np.ascontiguousarray(gx, dtype=np.complex64)
@@ -204,7 +205,7 @@ def scan_complex_backward(lam, x, gx, x0=None, lib=None):
     x0f = None if x0 is None else _c64f(x0, (B, C))
     glam = np.empty(C, dtype=np.complex128)
     gu = np.empty((B, T, C), dtype=np.complex128)
-    gx0 = None if x0 is None else np.empty((B, C), dtype=np.complex128)
+    gx0 = np.empty((B, C), dtype=np.complex128) if (x0 is not None if want_gx0 is None else want_gx0) else None
     f64 = lambda z: z.view(np.float64).ctypes.data_as(_F64P)  # noqa: E731
     (lib or _load()).oracle_scan_complex_backward(B, T, C, _p32(lf), None if x0f is None else _p32(x0f),
                                                   f64(xd), _p32(gxc.view(np.float32)), f64(glam), f64(gu),

@@ -224,7 +224,7 @@ void oracle_scan_complex(int64_t B, int64_t T, int64_t C,
  * backwards in time:
  *     gb_t = gx_t + a_{t+1} gb_{t+1}   (gb_{T-1} = gx_{T-1}),
  *     ga_t = gb_t x_{t-1}              (x_{-1} = x0, or 0 without x0),
- *     gx0  = a_0 gb_0                  (only with x0).
+ *     gx0  = a_0 gb_0                  (the initial state's gradient, also for a zero x0).
  * x is the forward output (B,T,C) in double; a, gx are (B,T,C) float32; x0 is (B,C) or
  * NULL.  Outputs ga, gb (B,T,C) and gx0 (B,C, may be NULL) in double.
  */
@@ -245,7 +245,7 @@ void oracle_scan_real_backward(int64_t B, int64_t T, int64_t C, const float *a, 
             const double xprev = (t > 0) ? x[o - C] : (x0 ? (double)x0[b * C + c] : 0.0);
             ga[o] = s * xprev;
         }
-        if (gx0) gx0[b * C + c] = (T > 0 && x0) ? (double)a[base] * s : 0.0;
+        if (gx0) gx0[b * C + c] = (T > 0) ? (double)a[base] * s : 0.0;
     }
 }
 
@@ -255,7 +255,7 @@ void oracle_scan_real_backward(int64_t B, int64_t T, int64_t C, const float *a, 
  * dL/dRe + i dL/dIm, so that dL = Re sum conj(g) dz.  Backwards in time:
  *     gu_t = gx_t + conj(lambda) gu_{t+1},
  *     glambda = sum over batch and time of gu_t conj(x_{t-1})   (x_{-1} = x0 or 0),
- *     gx0 = conj(lambda) gu_0                                   (only with x0).
+ *     gx0 = conj(lambda) gu_0                                   (also for a zero x0).
  * lambda (C,) and gx (B,T,C) are complex64, x0 (B,C) complex64 or NULL, x (B,T,C)
  * complex128; outputs glambda (C,), gu (B,T,C), gx0 (B,C, may be NULL) complex128.
  * glambda adds the batch rows in ascending order.
@@ -283,7 +283,7 @@ void oracle_scan_complex_backward(int64_t B, int64_t T, int64_t C, const float *
         part[2 * bc] = creal(acc);
         part[2 * bc + 1] = cimag(acc);
         if (gx0) {
-            const double complex g0 = (T > 0 && x0) ? Lc * s : 0.0;
+            const double complex g0 = (T > 0) ? Lc * s : 0.0;
             gx0[2 * (b * C + c)] = creal(g0);
             gx0[2 * (b * C + c) + 1] = cimag(g0);
         }

@@ -137,3 +137,25 @@ def test_workspace_sizes(lib):
     assert 0 < w1 < w2
     assert lib.linrec_scan_workspace_size(64, 4096, 256, 0) > 0
     assert lib.linrec_scan_workspace_size(1, 1 << 16, 64, 1) > 0
+
+
+def test_scan_backward_argument_checks(lib):
+    rb, cb = lib.linrec_scan_real_backward, lib.linrec_scan_complex_backward
+    # null required pointers
+    assert rb(1, 4, 4, P, None, None, P, P2, P2, None, None, 0, None) == INVALID
+    assert cb(1, 4, 4, P, None, P, P, None, P2, None, None, 0, None) == INVALID  # glambda NULL
+    assert cb(1, 4, 4, None, None, P, P, P2, P2, None, None, 0, None) == INVALID
+    # empty shapes without outputs to fill: nothing enqueued
+    assert rb(0, 4, 4, P, None, P, P, P2, P2, P2, None, 0, None) == OK
+    assert rb(2, 0, 4, P, None, P, P, P2, P2, None, None, 0, None) == OK
+    assert cb(2, 3, 0, P, None, P, P, P2, P2, None, None, 0, None) == OK
+    # alignment: complex64 needs 8 bytes
+    assert cb(1, 4, 4, P, None, ctypes.c_void_p(0x100004), P, P2, P2, None, None, 0, None) == UNSUPPORTED
+    assert rb(1, 4, 4, ODD, None, P, P, P2, P2, None, None, 0, None) == UNSUPPORTED
+    # workspace: a long single sequence needs look-back records
+    need = lib.linrec_scan_backward_workspace_size(1, 1 << 16, 64, 1)
+    assert need > 0
+    assert cb(1, 1 << 16, 64, P, None, P, P, P2, P2, None, None, need - 1, None) == WORKSPACE
+    assert lib.linrec_scan_backward_workspace_size(2, 40, 8, 0) == 0
+    # the complex adjoint always needs room for its per-slab sums of glambda
+    assert lib.linrec_scan_backward_workspace_size(2, 40, 8, 1) > 0

@@ -45,8 +45,8 @@ MUTANTS = [
      "const double anext = (t + 1 < T) ? (double)a[o] : 0.0;"),
     ("real_bwd_ga_uses_current_x", "const double xprev = (t > 0) ? x[o - C] : (x0 ? (double)x0[b * C + c] : 0.0);",
      "const double xprev = x[o];"),
-    ("real_bwd_gx0_without_a0", "if (gx0) gx0[b * C + c] = (T > 0 && x0) ? (double)a[base] * s : 0.0;",
-     "if (gx0) gx0[b * C + c] = (T > 0 && x0) ? s : 0.0;"),
+    ("real_bwd_gx0_without_a0", "if (gx0) gx0[b * C + c] = (T > 0) ? (double)a[base] * s : 0.0;",
+     "if (gx0) gx0[b * C + c] = (T > 0) ? s : 0.0;"),
     ("complex_bwd_lambda_not_conjugated",
      "const double complex Lc = conj((double)lam[2 * c] + (double)lam[2 * c + 1] * I);",
      "const double complex Lc = (double)lam[2 * c] + (double)lam[2 * c + 1] * I;"),

@@ -158,3 +158,15 @@ def test_backward_empty_and_single_step():
     e = np.zeros((2, 0, 3), np.float32)
     ga, gb, gx0 = oracle.scan_real_backward(e, e.astype(np.float64), e, x0)
     assert ga.shape == (2, 0, 3) and np.all(gx0 == 0.0)
+
+
+def test_initial_state_gradient_without_x0():
+    # The gradient of a zero initial state is still a_0 gb_0 (conj(lam) gu_0).
+    a, b, g, _ = _real_case(9)
+    x = oracle.scan_real(a, b)
+    _, gb, gx0 = oracle.scan_real_backward(a, x, g, want_gx0=True)
+    np.testing.assert_allclose(gx0, a[:, 0].astype(np.float64) * gb[:, 0], rtol=1e-15)
+    lam, u, gc, _ = _cplx_case(10)
+    xc = oracle.scan_complex(lam, u)
+    _, gu, gc0 = oracle.scan_complex_backward(lam, xc, gc, want_gx0=True)
+    np.testing.assert_allclose(gc0, np.conj(lam.astype(np.complex128)) * gu[:, 0], rtol=1e-15)
