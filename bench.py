@@ -9,8 +9,9 @@ Input/output buffer sets are rotated so that the 256 MB last-level cache (MALL) 
 serve a repeated call: R = ceil(2 * 256 MB / footprint) sets.
 
 ``--all`` also measures the other workloads (WKV-4 forward+backward at B=8 T=4096 C=2560,
-minGRU real scan at B=64 T=4096 C=256, LRU complex scan at B=1 T=262144 C=1024) and writes
-their lines to ``--all-out`` (they are parity workloads, not the headline line).
+minGRU real scan and its adjoint at B=64 T=4096 C=256, LRU complex scan and its adjoint at
+B=1 T=262144 C=1024) and writes their lines to ``--all-out`` (they are parity workloads,
+not the headline line).
 """
 
 from __future__ import annotations
@@ -33,7 +34,9 @@ METRIC = "WKV elements/s + achieved HBM GB/s (% peak), B=8 T=1024 C=768 fp32"
 PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 MALL_BYTES = 256 * 1024 * 1024  # MI355X Infinity Cache
 # Algorithmic bytes per element: inputs read once, outputs written once.
-BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "scan_complex": 16}
+BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "scan_complex": 16,
+                  "scan_real_backward": 20,      # read a, x, gx; write ga, gb
+                  "scan_complex_backward": 24}   # read x, gx; write gu (complex64)
 
 
 def log(*a):
@@ -47,6 +50,8 @@ KERNEL_SOURCES = {
     "wkv4_forward": _SCAN_SOURCES,
     "scan_real": _SCAN_SOURCES,
     "scan_complex": _SCAN_SOURCES,
+    "scan_real_backward": _SCAN_SOURCES,
+    "scan_complex_backward": _SCAN_SOURCES,
     "wkv4_backward": ("api.hip", "wkv_backward.hip", "wkv_backward.hpp", "lookback.hpp", "device_common.hpp",
                       "wkv_math.hpp"),
 }
@@ -135,6 +140,29 @@ class Row:
                 self.calls.append((lib.linrec_scan_complex, (B, T, C, lam.data_ptr(), u.data_ptr(), None,
                                    x.data_ptr(), ws.data_ptr(), nws, stream)))
             self.keep.append(lam)
+        elif kind == "scan_real_backward":
+            nws = int(lib.linrec_scan_backward_workspace_size(B, T, C, 0))
+            for _ in range(rotations):
+                a, x, gx = to(host["a"]), to(host["x"]), to(host["gx"])
+                ga, gb = torch.empty_like(a), torch.empty_like(a)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [a, x, gx, ga, gb, ws]
+                self.calls.append((lib.linrec_scan_real_backward, (B, T, C, a.data_ptr(), None, x.data_ptr(),
+                                   gx.data_ptr(), ga.data_ptr(), gb.data_ptr(), None, ws.data_ptr(), nws,
+                                   stream)))
+        elif kind == "scan_complex_backward":
+            lam = to(host["lam"])
+            nws = int(lib.linrec_scan_backward_workspace_size(B, T, C, 1))
+            glam = torch.empty(C, dtype=torch.complex64, device=dev)
+            for _ in range(rotations):
+                x, gx = to(host["x"]), to(host["gx"])
+                gu = torch.empty_like(x)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [x, gx, gu, ws]
+                self.calls.append((lib.linrec_scan_complex_backward, (B, T, C, lam.data_ptr(), None, x.data_ptr(),
+                                   gx.data_ptr(), glam.data_ptr(), gu.data_ptr(), None, ws.data_ptr(), nws,
+                                   stream)))
+            self.keep += [lam, glam]
         else:
             raise KeyError(kind)
 
@@ -183,7 +211,9 @@ def cpu_baseline(kind, host, budget_s):
           "wkv4_backward": lambda: oracle.wkv4_backward(host["w"], host["u"], host["k"], host["v"],
                                                         host["gy"]),
           "scan_real": lambda: oracle.scan_real(host["a"], host["b"]),
-          "scan_complex": lambda: oracle.scan_complex(host["lam"], host["u"])}[kind]
+          "scan_complex": lambda: oracle.scan_complex(host["lam"], host["u"]),
+          "scan_real_backward": lambda: oracle.scan_real_backward(host["a"], host["x"], host["gx"]),
+          "scan_complex_backward": lambda: oracle.scan_complex_backward(host["lam"], host["x"], host["gx"])}[kind]
     times = []
     t_start = time.perf_counter()
     while True:
@@ -223,6 +253,8 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
     wl = workloads.WORKLOADS[wid]
     B, T, C = shape or (wl.B, wl.T, wl.C)
     host = workloads.make_inputs(wid, shape=(B, T, C))
+    if kind.endswith("_backward") and kind.startswith("scan_"):
+        host.update(workloads.make_scan_adjoint_inputs(wid, host))
     elements = B * T * C
     footprint = BYTES_PER_ELEM[kind] * elements
     R = rotations_for(footprint)
@@ -246,6 +278,12 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
             Ts = cpu_slice
             sample = {k: (v[:, :Ts] if hasattr(v, "ndim") and v.ndim == 3 else v) for k, v in host.items()}
             desc = "first %d of %d time steps, all batch rows and channels" % (Ts, T)
+        if kind.endswith("_backward") and kind.startswith("scan_"):
+            # The adjoint's forward input: the oracle's own forward scan of the sample.
+            import oracle
+            sample = dict(sample)
+            sample["x"] = (oracle.scan_real(sample["a"], sample["b"]).astype("float32") if "a" in sample
+                           else oracle.scan_complex(sample["lam"], sample["u"]).astype("complex64"))
         med, reps, cores = cpu_baseline(kind, sample, cpu_budget)
         n_el = B * (cpu_slice or T) * C
         out["cpu_baseline"] = {"value": n_el / med, "unit": "elements/s", "cores": cores, "kind": "oracle",
@@ -307,7 +345,9 @@ def main():
     if args.all:
         rows = [res]
         for wid, kind, steps, cpu_slice in ((3, "wkv4_forward", 20, 512), (3, "wkv4_backward", 20, 256),
-                                            (4, "scan_real", 20, 512), (5, "scan_complex", 10, 16384)):
+                                            (4, "scan_real", 20, 512), (5, "scan_complex", 10, 16384),
+                                            (4, "scan_real_backward", 20, 512),
+                                            (5, "scan_complex_backward", 10, 16384)):
             rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
             log("[bench] " + json.dumps(rows[-1]))
         os.makedirs(os.path.dirname(args.all_out), exist_ok=True)

@@ -157,3 +157,26 @@ def make_inputs(wid: int, seed: int | None = None, shape=None):
     if wid == 5:
         return make_lru(B, T, C, seed)
     raise KeyError(wid)
+
+
+def make_scan_adjoint_inputs(wid: int, host: dict, seed: int | None = None):
+    """Extra inputs of a scan adjoint on workload ``wid`` (4: real, 5: complex) shaped like
+    ``host``: the upstream gradient gx ~ N(0,1) (complex: (N(0,1) + i N(0,1))/sqrt 2) and a
+    stand-in x of the same distribution for the forward output (for timing; parity tests
+    take x from the oracle's forward scan)."""
+    seed = (WORKLOADS[wid].seed if seed is None else seed) + 7919
+    rng = np.random.default_rng(seed)
+    if wid == 4:
+        B, T, C = host["a"].shape
+        return {"gx": _normal(rng, (B, T, C), 1.0), "x": _normal(rng, (B, T, C), 1.0)}
+    if wid == 5:
+        B, T, C = host["u"].shape
+        out = {}
+        for name in ("gx", "x"):
+            z = np.empty((B, T, C), dtype=np.complex64)
+            flat = z.reshape(-1).view(np.float32)
+            _normal_into(rng, flat[0::2], 1.0 / math.sqrt(2.0))
+            _normal_into(rng, flat[1::2], 1.0 / math.sqrt(2.0))
+            out[name] = z
+        return out
+    raise KeyError(wid)
