@@ -52,6 +52,9 @@ def _bind(path: str):
                                          _F32P, _F64P, _F64P, _F64P, _F64P]
     lib.oracle_scan_real.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_scan_complex.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
+    lib.oracle_wkv4_forward_ex.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P, _F32P, _F32P,
+                                           _F64P, _F64P]
+    lib.oracle_wkv4_forward_ex.restype = None
     lib.oracle_scan_real_backward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F64P, _F32P,
                                               _F64P, _F64P, _F64P]
     lib.oracle_scan_complex_backward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F64P, _F32P,
@@ -145,6 +148,24 @@ def wkv4_backward(w, u, k, v, gy, lib=None):
     (lib or _load()).oracle_wkv4_backward(B, T, C, _p32(w), _p32(u), _p32(k), _p32(v), _p32(gy),
                                  _p64(gw), _p64(gu), _p64(gk), _p64(gv))
     return gw, gu, gk, gv
+
+
+def wkv4_forward_ex(w, u, k, v, r=None, s_in=None, want_state=True, lib=None):
+    """(y (B,T,C), s_out (B,C,3) or None) float64: WKV-4 with the receptance gate sigma(r)
+    (eq. (15)) and a carried state (a, b, p), A = a e^p, B = b e^p (see oracle.c)."""
+    k = _f32(k)
+    B, T, C = k.shape
+    v = _f32(v, (B, T, C))
+    w = _f32(w, (C,))
+    u = _f32(u, (C,))
+    ra = None if r is None else _f32(r, (B, T, C))
+    sa = None if s_in is None else _f32(s_in, (B, C, 3))
+    y = np.empty((B, T, C), dtype=np.float64)
+    so = np.empty((B, C, 3), dtype=np.float64) if want_state else None
+    (lib or _load()).oracle_wkv4_forward_ex(B, T, C, _p32(w), _p32(u), _p32(k), _p32(v),
+                                            None if ra is None else _p32(ra), None if sa is None else _p32(sa),
+                                            _p64(y), None if so is None else _p64(so))
+    return y, so
 
 
 def scan_real(a, b, x0=None, lib=None) -> np.ndarray:

@@ -85,6 +85,54 @@ void oracle_wkv4_forward(int64_t B, int64_t T, int64_t C,
 }
 
 /*
+ * WKV-4 forward with a carried state and the receptance gate (RWKV-LLM page, "Time-mixing
+ * block": eq. (14), and eq. (15)'s sigma(r_t) (.) wkv_t).  The state before the first token
+ * of the call is (a, b, p): the past sums A = a e^p and B = b e^p of eq. (14) over every
+ * token already consumed (NULL: empty).  Then, for t = 0 .. T-1,
+ *     y_t = sigma(r_t) (A_t + e^{u+k_t} v_t) / (B_t + e^{u+k_t})     (sigma = 1 without r),
+ *     A_{t+1} = e^{-w} A_t + e^{k_t} v_t,  B_{t+1} likewise,
+ * and s_out receives (A_T, B_T) as (a, b, p) in double.  r is (B,T,C) float32 or NULL;
+ * s_in is (B,C,3) float32 or NULL; s_out is (B,C,3) double or NULL.  A state with
+ * a = b = 0 is empty whatever its p.
+ */
+void oracle_wkv4_forward_ex(int64_t B, int64_t T, int64_t C, const float *w, const float *u,
+                            const float *k, const float *v, const float *r, const float *s_in,
+                            double *y, double *s_out)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        const double a0 = s_in ? (double)s_in[3 * bc] : 0.0;
+        const double b0 = s_in ? (double)s_in[3 * bc + 1] : 0.0;
+        const double p0 = s_in ? (double)s_in[3 * bc + 2] : 0.0;
+        const int has_state = (a0 != 0.0 || b0 != 0.0);
+        /* Common rescaling: e^{-K} for every weight, K the largest exponent present. */
+        double K = T > 0 ? chan_max_k(k, T, C, base) : (has_state ? p0 : 0.0);
+        if (has_state && p0 > K) K = p0;
+        const double decay = exp(-(double)w[c]);
+        const double uu = (double)u[c];
+        double A = has_state ? a0 * exp(p0 - K) : 0.0;
+        double Bs = has_state ? b0 * exp(p0 - K) : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t o = base + t * C;
+            const double kt = (double)k[o], vt = (double)v[o];
+            const double cur = exp(uu + kt - K);
+            const double gate = r ? 1.0 / (1.0 + exp(-(double)r[o])) : 1.0;
+            y[o] = gate * (A + cur * vt) / (Bs + cur);
+            const double past = exp(kt - K);
+            A = decay * A + past * vt;
+            Bs = decay * Bs + past;
+        }
+        if (s_out) {
+            s_out[3 * bc] = A;
+            s_out[3 * bc + 1] = Bs;
+            s_out[3 * bc + 2] = K;
+        }
+    }
+}
+
+/*
  * WKV-4 backward: gradients of a scalar loss L with upstream dL/dy = gy, w.r.t. the
  * w and u of eq. (14) as printed (summed over batch and time, since both are
  * per-channel vectors in that section) and w.r.t. every k_t and v_t.  The pages give

@@ -1,0 +1,102 @@
+"""Pins of the oracle's WKV-4 forward with a carried state (a, b, p) and the receptance
+gate sigma(r) (RWKV-LLM page, "Time-mixing block", eqs. (14) and (15)).
+
+Independent of the routine under test: the brute-force sums of eq. (14) over the whole
+sequence, numpy's own sigmoid, the log-sum-exp of the final state computed in numpy, and
+the split of a sequence into calls that hand the state on.
+"""
+
+import numpy as np
+import pytest
+
+import brute
+import oracle
+from linear_recurrence_rnn_amd import workloads
+
+
+def _case(seed, B=2, T=40, C=5):
+    return workloads.make_inputs(3, seed=seed, shape=(B, T, C))
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, np.float64)))
+
+
+def test_plain_call_matches_brute_force():
+    d = _case(1)
+    y, s = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"])
+    np.testing.assert_allclose(y, brute.wkv4_sums(d["w"], d["u"], d["k"], d["v"]), rtol=1e-11, atol=1e-13)
+    np.testing.assert_array_equal(y, oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"]))
+
+
+def test_final_state_is_the_past_sums():
+    # s_out = (A_T, B_T): A_T = sum_{i<T} e^{-(T-1-i) w + k_i} v_i, checked through
+    # A/B and log B = p + log b (log-sum-exp in numpy).
+    d = _case(2)
+    _, s = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"])
+    B, T, C = d["k"].shape
+    lag = (T - 1 - np.arange(T))[None, :, None]
+    e = -lag * d["w"].astype(np.float64)[None, None, :] + d["k"].astype(np.float64)
+    m = e.max(axis=1)
+    wts = np.exp(e - m[:, None, :])
+    A = (wts * d["v"]).sum(axis=1)
+    Bs = wts.sum(axis=1)
+    np.testing.assert_allclose(s[..., 0] / s[..., 1], A / Bs, rtol=1e-12)
+    np.testing.assert_allclose(s[..., 2] + np.log(s[..., 1]), m + np.log(Bs), rtol=1e-13, atol=1e-12)
+
+
+@pytest.mark.parametrize("split", [1, 17, 39])
+def test_state_hands_the_sequence_on(split):
+    d = _case(3)
+    ref = brute.wkv4_sums(d["w"], d["u"], d["k"], d["v"])
+    y1, s1 = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"][:, :split], d["v"][:, :split])
+    y2, _ = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"][:, split:], d["v"][:, split:],
+                                   s_in=s1.astype(np.float32))
+    np.testing.assert_allclose(y1, ref[:, :split], rtol=1e-11, atol=1e-13)
+    # the state crosses the call boundary as float32 (a, b, p)
+    np.testing.assert_allclose(y2, ref[:, split:], rtol=2e-6, atol=2e-6)
+
+
+def test_decode_one_token_at_a_time():
+    d = _case(4, T=25)
+    ref = brute.wkv4_sums(d["w"], d["u"], d["k"], d["v"])
+    s = None
+    for t in range(25):
+        y, s64 = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"][:, t:t + 1], d["v"][:, t:t + 1], s_in=s)
+        s = s64.astype(np.float32)
+        np.testing.assert_allclose(y[:, 0], ref[:, t], rtol=5e-6, atol=5e-6)
+
+
+def test_state_scale_is_arbitrary():
+    d = _case(5)
+    rng = np.random.default_rng(0)
+    s = np.stack([rng.standard_normal((2, 5)), rng.uniform(0.5, 2, (2, 5)), rng.uniform(-3, 3, (2, 5))],
+                 axis=-1).astype(np.float32)
+    s2 = s.copy()
+    s2[..., 0] *= 4.0
+    s2[..., 1] *= 4.0
+    s2[..., 2] -= np.float32(np.log(4.0))
+    y1, _ = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"], s_in=s)
+    y2, _ = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"], s_in=s2)
+    np.testing.assert_allclose(y1, y2, rtol=1e-6)
+    empty = np.zeros((2, 5, 3), np.float32)
+    empty[..., 2] = 123.0
+    y3, _ = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"], s_in=empty)
+    np.testing.assert_array_equal(y3, oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"]))
+
+
+def test_receptance_gate():
+    d = _case(6)
+    r = np.random.default_rng(1).standard_normal(d["k"].shape).astype(np.float32) * 3
+    y, _ = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"], r=r)
+    np.testing.assert_allclose(y, _sigmoid(r) * brute.wkv4_sums(d["w"], d["u"], d["k"], d["v"]), rtol=1e-11,
+                               atol=1e-13)
+
+
+def test_empty_sequence_passes_the_state_through():
+    d = _case(7, T=0)
+    s = np.array([[[0.5, 2.0, 1.5]] * 5] * 2, np.float32)
+    y, so = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"], s_in=s)
+    assert y.shape == (2, 0, 5)
+    np.testing.assert_allclose(so[..., 0] / so[..., 1], 0.25)
+    np.testing.assert_allclose(so[..., 2] + np.log(so[..., 1]), 1.5 + np.log(2.0))
