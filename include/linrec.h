@@ -98,6 +98,28 @@ int wkv4_forward(int64_t B, int64_t T, int64_t C,
                  float *y, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * WKV-4 forward with a carried state and the receptance gate, for sequences processed in
+ * pieces (and token-by-token decoding, T = 1) and for the time-mix output of eq. (15) on
+ * the RWKV-LLM page ("Time-mixing block"), o_t = W_o (sigma(r_t) (.) wkv_t) before W_o:
+ *
+ *   state (a, b, p) per (batch row, channel): the past sums of eq. (14) over every token
+ *   already consumed, A = a e^p and B = b e^p, so that the call's first token sees
+ *   y_0 = sigma(r_0) (A + e^{u+k_0} v_0) / (B + e^{u+k_0});  a = b = 0 is the empty state.
+ *
+ *   r     (B,T,C) float32 or NULL (no gate: sigma = 1)
+ *   s_in  (B,C,3) float32 (a, b, p) or NULL (empty state)
+ *   y     (B,T,C) float32 output
+ *   s_out (B,C,3) float32 or NULL: the state after the last token, ready to be the next
+ *         call's s_in (its p is chosen by the library; with T = 0 it is s_in, or empty)
+ *
+ * Same workspace as wkv4_forward.  With T = 0 only s_in and s_out are used.
+ */
+int wkv4_forward_ex(int64_t B, int64_t T, int64_t C,
+                    const float *w, const float *u, const float *k, const float *v,
+                    const float *r, const float *s_in, float *y, float *s_out,
+                    void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * WKV-4 backward: given the upstream gradient gy = dL/dy of eq. (14)'s output, writes
  *
  *   gw (C), gu (C)     dL/dw and dL/du, summed over batch and time (w and u are

@@ -59,6 +59,8 @@ def load(path: str | None = None):
         lib.linrec_scan_workspace_size.argtypes = [_I64, _I64, _I64, ctypes.c_int]
         lib.wkv4_forward.restype = ctypes.c_int
         lib.wkv4_forward.argtypes = [_I64, _I64, _I64] + [_VP] * 5 + [_VP, _SZ, _VP]
+        lib.wkv4_forward_ex.restype = ctypes.c_int
+        lib.wkv4_forward_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 8 + [_VP, _SZ, _VP]
         lib.wkv4_backward.restype = ctypes.c_int
         lib.wkv4_backward.argtypes = [_I64, _I64, _I64] + [_VP] * 9 + [_VP, _SZ, _VP]
         lib.linrec_scan_real.restype = ctypes.c_int
@@ -153,6 +155,32 @@ def wkv4_forward(w, u, k, v, out=None, workspace=None):
     _check(lib.wkv4_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(ws), nws,
                             _stream(dev)), "wkv4_forward")
     return y
+
+
+def wkv4_forward_ex(w, u, k, v, r=None, state=None, want_state=True, out=None, workspace=None):
+    """(y, state_out) of WKV-4 with the receptance gate sigma(r) and a carried state
+    (a, b, p) per (batch row, channel): ``state`` (B,C,3) float32 or None (empty);
+    state_out (B,C,3) when ``want_state``."""
+    lib = load()
+    B, T, C = k.shape
+    dev = k.device
+    _expect(k, "k", torch.float32, (B, T, C), dev)
+    _expect(v, "v", torch.float32, (B, T, C), dev)
+    _expect(w, "w", torch.float32, (C,), dev)
+    _expect(u, "u", torch.float32, (C,), dev)
+    if r is not None:
+        _expect(r, "r", torch.float32, (B, T, C), dev)
+    if state is not None:
+        _expect(state, "state", torch.float32, (B, C, 3), dev)
+    if out is None:
+        y = torch.empty_like(k)
+        s_out = torch.empty((B, C, 3), dtype=torch.float32, device=dev) if want_state else None
+    else:
+        y, s_out = out
+    ws, nws = _workspace(int(lib.wkv4_forward_workspace_size(B, T, C)), dev, workspace)
+    _check(lib.wkv4_forward_ex(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(state), _ptr(y),
+                               _ptr(s_out), _ptr(ws), nws, _stream(dev)), "wkv4_forward_ex")
+    return y, s_out
 
 
 def wkv4_backward(w, u, k, v, gy, out=None, workspace=None):

@@ -230,25 +230,43 @@ LINREC_API size_t wkv4_backward_workspace_size(int64_t B, int64_t T, int64_t C) 
     return bwd_ws_bytes(B, T, C);
 }
 
-LINREC_API int wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                            const float* k, const float* v, float* y, void* workspace,
-                            size_t ws_bytes, void* stream) {
+LINREC_API int wkv4_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                               const float* k, const float* v, const float* r, const float* s_in, float* y,
+                               float* s_out, void* workspace, size_t ws_bytes, void* stream) {
     int st = check_shape(B, T, C, 4);
     if (st) return st;
-    if (B == 0 || T == 0 || C == 0) return ok();
+    if (B == 0 || C == 0) return ok();
+    if ((s_in && !aligned(s_in, 4)) || (s_out && !aligned(s_out, 4)))
+        return fail(LINREC_ERR_UNSUPPORTED, "state pointer not 4-byte aligned");
+    if (T == 0) {
+        // No tokens: the state passes through unchanged (empty without s_in).
+        if (!s_out) return ok();
+        const hipError_t e = s_in ? linrec::run_copy(s_out, s_in, 3 * B * C, (hipStream_t)stream)
+                                  : linrec::run_fill_zero(s_out, 3 * B * C, (hipStream_t)stream);
+        return hip_status(e, "wkv4_forward_ex state copy");
+    }
     if (!w || !u || !k || !v || !y) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
     const void* ptrs[] = {w, u, k, v, y};
     for (const void* p : ptrs)
         if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
-    const int vec = pick_vec(linrec::kKindWkv, (C % 4 == 0 && aligned(k, 16) && aligned(v, 16) && aligned(y, 16)) ? 4
-                                              : (C % 2 == 0 && aligned(k, 8) && aligned(v, 8) && aligned(y, 8)) ? 2
-                                                                                                           : 1);
+    if (r && !aligned(r, 4)) return fail(LINREC_ERR_UNSUPPORTED, "r not 4-byte aligned");
+    const bool wide_ok = !r || aligned(r, 16);
+    const int vec = pick_vec(linrec::kKindWkv,
+                             (C % 4 == 0 && aligned(k, 16) && aligned(v, 16) && aligned(y, 16) && wide_ok) ? 4
+                             : (C % 2 == 0 && aligned(k, 8) && aligned(v, 8) && aligned(y, 8) && (!r || aligned(r, 8))) ? 2
+                                                                                                            : 1);
     const linrec::ScanPlan p = scan_plan(linrec::kKindWkv, vec, B, T, C);
     if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
-    const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0};
+    const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0, r, s_in, s_out};
     return hip_status(linrec::run_wkv_forward(A, geom_of(linrec::kKindWkv, p, B, T, C, workspace), p,
                                               (hipStream_t)stream),
                       "wkv4_forward launch");
+}
+
+LINREC_API int wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                            const float* k, const float* v, float* y, void* workspace,
+                            size_t ws_bytes, void* stream) {
+    return wkv4_forward_ex(B, T, C, w, u, k, v, nullptr, nullptr, y, nullptr, workspace, ws_bytes, stream);
 }
 
 LINREC_API int linrec_scan_real(int64_t B, int64_t T, int64_t C, const float* a, const float* b,

@@ -185,6 +185,10 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) incl[e] = Op::combine(ch[e], carry[e], mine[e], slab_n);
         publish<VEC>(chn, s, lane, incl, true);
+    } else if (active) {
+        // The last slab: the state after the whole sequence, for operators that hand it on.
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) Op::finish(A, g, b, c0 + e, Op::combine(ch[e], carry[e], mine[e], slab_n));
     }
     if constexpr (Op::kParts) {
         __syncthreads();  // B3
@@ -255,7 +259,7 @@ hipError_t dispatch_shape(const typename Op::Args& A, const ScanGeom& g, const S
     if (p.nw == 4 && p.L == 16) return launch<Op, VEC, 4, 16>(A, g, st);
     if (p.nw == 8 && p.L == 8) return launch<Op, VEC, 8, 8>(A, g, st);
     if (p.nw == 8 && p.L == 16) return launch<Op, VEC, 8, 16>(A, g, st);
-    if constexpr (VEC == 1 && !std::is_same<Op, WkvOp>::value) {
+    if constexpr (VEC == 1 && !std::is_same<Op, WkvOp>::value && !std::is_same<Op, WkvExtOp>::value) {
         if (p.nw == 8 && p.L == 32) return launch<Op, VEC, 8, 32>(A, g, st);
     }
     return hipErrorInvalidValue;
@@ -280,7 +284,9 @@ bool scan_shape_supported(int kind, int vec, int nw, int L) {
                       (kind != kKindWkv && vec == 1 && nw == 8 && L == 32));
 }
 
+// A carried state or a gate takes the extended instance; the plain call compiles none of it.
 hipError_t run_wkv_forward(const WkvArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st) {
+    if (A.r || A.s_in || A.s_out) return dispatch<WkvExtOp, 4>(A, g, p, st);
     return dispatch<WkvOp, 4>(A, g, p, st);
 }
 hipError_t run_scan_real(const RealArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st) {
@@ -303,6 +309,18 @@ hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const Sc
     hipLaunchKernelGGL(part_sum_kernel, dim3((unsigned)g.ngrp, (unsigned)nk), dim3(64), 0, st, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(part_final_kernel, dim3((unsigned)((g.C + 255) / 256)), dim3(256), 0, st, g, nk, glam);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(float* __restrict__ d, const float* __restrict__ s, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        d[i] = s[i];
+}
+
+hipError_t run_copy(float* dst, const float* src, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st, dst, src, n);
     return hipGetLastError();
 }
 

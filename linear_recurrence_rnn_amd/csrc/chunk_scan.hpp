@@ -11,12 +11,15 @@ enum { kKindWkv = 0, kKindReal = 1, kKindComplex = 2, kKindRealBwd = 3, kKindCom
 
 // Operands of each recurrence (device pointers, (B,T,C) row-major, C fastest).
 struct WkvArgs {
-    const float* w;  // (C)
-    const float* u;  // (C)
-    const float* k;  // (B,T,C)
-    const float* v;  // (B,T,C)
-    float* y;        // (B,T,C)
-    int exact_only;  // 1: always take the exact per-step path (used by tests)
+    const float* w;     // (C)
+    const float* u;     // (C)
+    const float* k;     // (B,T,C)
+    const float* v;     // (B,T,C)
+    float* y;           // (B,T,C)
+    int exact_only;     // 1: always take the exact per-step path (used by tests)
+    const float* r;     // (B,T,C) receptance, or null: y = sigma(r) wkv
+    const float* s_in;  // (B,C,3) state (a, b, p) before the first token, or null (empty)
+    float* s_out;       // (B,C,3) state after the last token, or null
 };
 struct RealArgs {
     const float* a;   // (B,T,C)
@@ -96,6 +99,8 @@ hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const Sc
 constexpr int kPartBlock = 64;  // slabs summed per first-stage block of the glam reduction
 // Writes n zero floats (a fill kernel, so that the call can be captured in a graph).
 hipError_t run_fill_zero(float* p, int64_t n, hipStream_t st);
+// dst[i] = src[i] for n floats (a copy kernel, for the same reason).
+hipError_t run_copy(float* dst, const float* src, int64_t n, hipStream_t st);
 size_t agg_bytes(int kind);
 // Launch shapes that have kernels: (vec, nw, L) per kind.
 bool scan_shape_supported(int kind, int vec, int nw, int L);

@@ -44,9 +44,12 @@ namespace linrec {
 // where M = p + frexp_exp(b) bounds log2 B (see wkv_math.hpp),
 // re-reading k from memory (its registers now hold g).
 // ----------------------------------------------------------------------------------
+// kExt: the instance that reads a carried state, writes the final one and gates the output by
+// sigma(r).  The plain instance compiles none of that, so its registers stay as they were.
 struct NoPart {};
 
-struct WkvOp {
+template <bool kExt>
+struct WkvOpT {
     using Args = WkvArgs;
     static constexpr bool kReverse = false;
     static constexpr bool kParts = false;
@@ -66,14 +69,70 @@ struct WkvOp {
         return ch;
     }
     __device__ __forceinline__ static Agg identity() { return {0.f, 0.f, kEmpty}; }
-    __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) { return identity(); }
+
+    // A carried state (a, b, p) means A = a e^p, B = b e^p.  Natural-log exponents are
+    // converted to and from the integer base-2 ones with ln 2 split in two parts, so the
+    // exponent's own rounding does not scale the state.
+    static constexpr float kLn2Hi = 0.693145751953125f, kLn2Lo = 1.42860682030941723212e-6f;
+    __device__ __forceinline__ static Agg init(const Args& A, const ScanGeom& g, int64_t b, int64_t c) {
+        if constexpr (!kExt) return identity();
+        if (!A.s_in) return identity();
+        const float* s = A.s_in + 3 * (b * g.C + c);
+        const float sa = s[0], sb = s[1], sp = s[2];
+        if (sa == 0.f && sb == 0.f) return identity();
+        const float P = ceilf(sp * kLog2e);
+        const float rem = fmaf(-P, kLn2Lo, fmaf(-P, kLn2Hi, sp));  // sp - P ln 2, in [-ln 2, 0] about
+        const float sc = fast_exp2(rem * kLog2e);
+        return {sa * sc, sb * sc, P};
+    }
+    // After the last token: the state A = a 2^p as (a', b', p') with p' = float(p ln 2), the
+    // rounding of p' compensated in a', b'.
+    __device__ __forceinline__ static void finish(const Args& A, const ScanGeom& g, int64_t b, int64_t c,
+                                                  const Agg& s) {
+        if constexpr (!kExt) return;
+        if (!A.s_out) return;
+        float* o = A.s_out + 3 * (b * g.C + c);
+        if (s.b == 0.f) {
+            o[0] = 0.f;
+            o[1] = 0.f;
+            o[2] = 0.f;
+            return;
+        }
+        const float pn = s.p * kLn2Hi + s.p * kLn2Lo;
+        const float delta = fmaf(s.p, kLn2Lo, fmaf(s.p, kLn2Hi, -pn));  // p ln 2 - pn
+        const float sc = fast_exp2(delta * kLog2e);
+        o[0] = s.a * sc;
+        o[1] = s.b * sc;
+        o[2] = pn;
+    }
 
     static constexpr int kFloats = 1;  // floats per channel element
-    struct Res { rsrc_t k, v, y; };
+    struct Res { rsrc_t k, v, y, r; bool gated; };
     // Buffers of the run whose lowest row is time `row` of batch row b, from column col0.
     __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
         const int64_t base = (b * g.T + row) * g.C + col0, nbytes = (g.B * g.T * g.C - base) * 4;
-        return {make_rsrc(A.k + base, nbytes), make_rsrc(A.v + base, nbytes), make_rsrc(A.y + base, nbytes)};
+        return {make_rsrc(A.k + base, nbytes), make_rsrc(A.v + base, nbytes), make_rsrc(A.y + base, nbytes),
+                make_rsrc(A.r ? A.r + base : A.k + base, A.r ? nbytes : 0), A.r != nullptr};
+    }
+    // sigma(r) of the gated output (eq. (15)); 1 without a gate.
+    template <int L, int VEC>
+    __device__ __forceinline__ static void gates(const Res& R, unsigned voff, const Rows& rows, int n,
+                                                 float (&sg)[L][VEC]) {
+        if constexpr (!kExt) {
+#pragma unroll
+            for (int j = 0; j < L; ++j)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) sg[j][e] = 1.f;
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            FV<VEC> rr{};
+            if (R.gated && j < n) rr = ldb<VEC>(R.r, voff, rows.soff(j));
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                sg[j][e] = R.gated ? __builtin_amdgcn_rcpf(1.f + fast_exp2(-rr.v[e] * kLog2e)) : 1.f;
+        }
     }
     template <int VEC>
     __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
@@ -131,6 +190,8 @@ struct WkvOp {
     __device__ __forceinline__ static Part run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
                                const In (&in)[L][VEC], const Local (&loc)[VEC], int n, unsigned voff,
                                const Rows& rows) {
+        float sg[L][VEC];
+        gates<L, VEC>(R, voff, rows, n, sg);
         float a[VEC], b[VEC], cs[VEC], us[VEC];
         bool fast[VEC];
 #pragma unroll
@@ -161,7 +222,7 @@ struct WkvOp {
                     for (int e = 0; e < VEC; ++e) {
                         const float g = in[j][e].kk, vv = in[j][e].v;
                         const float cur = g * cs[e];
-                        y.v[e] = fmaf(cur, vv, a[e]) * __builtin_amdgcn_rcpf(b[e] + cur);
+                        y.v[e] = fmaf(cur, vv, a[e]) * __builtin_amdgcn_rcpf(b[e] + cur) * sg[j][e];
                         const float up = g * us[e];
                         a[e] = fmaf(up, vv, a[e]);
                         b[e] += up;
@@ -185,7 +246,7 @@ struct WkvOp {
                     const float kk = kr.v[e] * kLog2e, vv = in[j][e].v;
                     const float q = ceilf(fmaxf(mag(pp[e], pb[e]), kk + ch[e].mu));
                     const float e1 = fast_exp2(pp[e] - q), e2 = fast_exp2((kk - q) + ch[e].mu);
-                    y.v[e] = fmaf(pa[e], e1, vv * e2) * __builtin_amdgcn_rcpf(fmaf(pb[e], e1, e2));
+                    y.v[e] = fmaf(pa[e], e1, vv * e2) * __builtin_amdgcn_rcpf(fmaf(pb[e], e1, e2)) * sg[j][e];
                     const float q2 = ceilf(fmaxf(mag(pp[e], pb[e]) - ch[e].om, kk));
                     const float f1 = fast_exp2((pp[e] - q2) - ch[e].om), f2 = fast_exp2(kk - q2);
                     pa[e] = fmaf(pa[e], f1, vv * f2);
@@ -198,6 +259,8 @@ struct WkvOp {
         return {};
     }
 };
+using WkvOp = WkvOpT<false>;
+using WkvExtOp = WkvOpT<true>;
 
 // ----------------------------------------------------------------------------------
 // Real diagonal scan x_t = a_t x_{t-1} + b_t ("Were RNNs All We Needed?" page, minGRU
@@ -211,6 +274,9 @@ struct RealOp {
     static constexpr bool kReverse = false;
     static constexpr bool kParts = false;
     using Part = NoPart;
+    // The final state is the last row of x: nothing more to write.
+    template <class AnyArgs, class AnyAgg>
+    __device__ __forceinline__ static void finish(const AnyArgs&, const ScanGeom&, int64_t, int64_t, const AnyAgg&) {}
     struct Chan {};
     struct In { float a, b; };
     struct Local {};
@@ -315,6 +381,8 @@ struct CplxOp {
     static constexpr bool kReverse = false;
     static constexpr bool kParts = false;
     using Part = NoPart;
+    template <class AnyArgs, class AnyAgg>
+    __device__ __forceinline__ static void finish(const AnyArgs&, const ScanGeom&, int64_t, int64_t, const AnyAgg&) {}
     struct Chan { float lr, li, Lr, Li; };  // lam and lam^L
     struct In { float r, i; };
     struct Local {};

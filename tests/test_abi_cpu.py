@@ -159,3 +159,17 @@ def test_scan_backward_argument_checks(lib):
     assert lib.linrec_scan_backward_workspace_size(2, 40, 8, 0) == 0
     # the complex adjoint always needs room for its per-slab sums of glambda
     assert lib.linrec_scan_backward_workspace_size(2, 40, 8, 1) > 0
+
+
+def test_wkv4_forward_ex_argument_checks(lib):
+    fx = lib.wkv4_forward_ex
+    # empty batch / channels: nothing to do
+    assert fx(0, 4, 4, P, P, P, P, None, None, P2, None, None, 0, None) == OK
+    # no tokens and no state out: nothing to do
+    assert fx(2, 0, 4, P, P, P, P, None, None, P2, None, None, 0, None) == OK
+    # required pointers
+    assert fx(1, 4, 4, None, P, P, P, None, None, P2, None, None, 0, None) == INVALID
+    assert fx(1, 4, 4, P, P, P, P, None, None, None, None, None, 0, None) == INVALID
+    # misaligned optional inputs
+    assert fx(1, 4, 4, P, P, P, P, ODD, None, P2, None, None, 0, None) == UNSUPPORTED
+    assert fx(1, 4, 4, P, P, P, P, None, ODD, P2, None, None, 0, None) == UNSUPPORTED
