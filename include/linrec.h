@@ -6,6 +6,8 @@
  * "RWKV：基于RNN的LLM" uses in its section on parallel training):
  *
  *   wkv4_forward / wkv4_backward  the RWKV-4 time-mix operator of eq. (14) on that page
+ *   wkv4_forward_ex               the same with a carried state and the sigma(r) gate
+ *   wkv4_decode_step              one token of it in recurrent form (decoding)
  *   linrec_scan_real              x_t = a_t * x_{t-1} + b_t (the scan form on the
  *                                 "Were RNNs All We Needed?" news page, minGRU section)
  *   linrec_scan_complex           x_t = lambda * x_{t-1} + u_t (the LRU write-up on
@@ -17,7 +19,8 @@
  * Conventions shared by every entry point:
  *  - Pointers are DEVICE pointers (hipMalloc / torch CUDA-on-ROCm memory) unless a
  *    comment says otherwise; the caller owns every buffer for the whole call.  Outputs
- *    must not alias inputs or each other.
+ *    must not alias inputs or each other (the one exception: the state of
+ *    wkv4_decode_step, updated in place).
  *  - Calls are asynchronous: they validate arguments on the host, then enqueue kernels on
  *    `stream` (a hipStream_t; NULL means the default stream) and return.  The library never
  *    synchronises, allocates or frees device memory; scratch memory comes from the
@@ -118,6 +121,29 @@ int wkv4_forward_ex(int64_t B, int64_t T, int64_t C,
                     const float *w, const float *u, const float *k, const float *v,
                     const float *r, const float *s_in, float *y, float *s_out,
                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One token of WKV-4 in its recurrent form, for token-by-token decoding (the RNN mode of
+ * inference on the RWKV pages: the output depends only on the current input and a state of
+ * fixed size; RWKV-LLM page, "并行训练和序列解码"):
+ *
+ *   y     = sigma(r) (A + e^{u+k} v) / (B + e^{u+k})         (eqs. (14)-(15) at one step)
+ *   state <- (e^{-w} A + e^{k} v,  e^{-w} B + e^{k})
+ *
+ *   w, u  (C)     float32 as for wkv4_forward
+ *   k, v  (B,C)   float32, this token of each batch row
+ *   r     (B,C)   float32 or NULL (no gate: sigma = 1)
+ *   state (B,C,3) float32 (a, b, p), A = a e^p and B = b e^p, read and then OVERWRITTEN IN
+ *                 PLACE with the state after this token (the one buffer that is both input
+ *                 and output); a = b = 0 is the empty state.  Interchangeable with the
+ *                 s_in / s_out of wkv4_forward_ex.
+ *   y     (B,C)   float32 output
+ *
+ * No workspace.  Calling it T times gives wkv4_forward_ex's outputs and final state for the
+ * same T tokens (to rounding).
+ */
+int wkv4_decode_step(int64_t B, int64_t C, const float *w, const float *u, const float *k,
+                     const float *v, const float *r, float *state, float *y, void *stream);
 
 /*
  * WKV-4 backward: given the upstream gradient gy = dL/dy of eq. (14)'s output, writes

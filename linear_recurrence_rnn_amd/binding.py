@@ -62,6 +62,8 @@ def load(path: str | None = None):
         lib.wkv4_forward_ex.restype = ctypes.c_int
         lib.wkv4_forward_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 8 + [_VP, _SZ, _VP]
         lib.wkv4_backward.restype = ctypes.c_int
+        lib.wkv4_decode_step.restype = ctypes.c_int
+        lib.wkv4_decode_step.argtypes = [_I64, _I64] + [_VP] * 7 + [_VP]
         lib.wkv4_backward.argtypes = [_I64, _I64, _I64] + [_VP] * 9 + [_VP, _SZ, _VP]
         lib.linrec_scan_real.restype = ctypes.c_int
         lib.linrec_scan_real.argtypes = [_I64, _I64, _I64] + [_VP] * 4 + [_VP, _SZ, _VP]
@@ -177,10 +179,33 @@ def wkv4_forward_ex(w, u, k, v, r=None, state=None, want_state=True, out=None, w
         s_out = torch.empty((B, C, 3), dtype=torch.float32, device=dev) if want_state else None
     else:
         y, s_out = out
+        _expect(y, "out[0]", torch.float32, (B, T, C), dev)
+        if s_out is not None:
+            _expect(s_out, "out[1]", torch.float32, (B, C, 3), dev)
     ws, nws = _workspace(int(lib.wkv4_forward_workspace_size(B, T, C)), dev, workspace)
     _check(lib.wkv4_forward_ex(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(state), _ptr(y),
                                _ptr(s_out), _ptr(ws), nws, _stream(dev)), "wkv4_forward_ex")
     return y, s_out
+
+
+def wkv4_decode_step(w, u, k, v, state, r=None, out=None):
+    """One token of WKV-4 in recurrent form: k, v, r (B,C) float32, ``state`` (B,C,3)
+    float32 (a, b, p), updated IN PLACE.  Returns y (B,C)."""
+    lib = load()
+    B, C = k.shape
+    dev = k.device
+    _expect(k, "k", torch.float32, (B, C), dev)
+    _expect(v, "v", torch.float32, (B, C), dev)
+    _expect(w, "w", torch.float32, (C,), dev)
+    _expect(u, "u", torch.float32, (C,), dev)
+    _expect(state, "state", torch.float32, (B, C, 3), dev)
+    if r is not None:
+        _expect(r, "r", torch.float32, (B, C), dev)
+    y = torch.empty_like(k) if out is None else out
+    _expect(y, "out", torch.float32, (B, C), dev)
+    _check(lib.wkv4_decode_step(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(state), _ptr(y),
+                                _stream(dev)), "wkv4_decode_step")
+    return y
 
 
 def wkv4_backward(w, u, k, v, gy, out=None, workspace=None):

@@ -10,6 +10,7 @@
 #include "linrec.h"
 #include "chunk_scan.hpp"
 #include "wkv_backward.hpp"
+#include "wkv_decode.hpp"
 
 #define LINREC_API extern "C" __attribute__((visibility("default")))
 
@@ -267,6 +268,19 @@ LINREC_API int wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, con
                             const float* k, const float* v, float* y, void* workspace,
                             size_t ws_bytes, void* stream) {
     return wkv4_forward_ex(B, T, C, w, u, k, v, nullptr, nullptr, y, nullptr, workspace, ws_bytes, stream);
+}
+
+LINREC_API int wkv4_decode_step(int64_t B, int64_t C, const float* w, const float* u, const float* k,
+                                const float* v, const float* r, float* state, float* y, void* stream) {
+    int st = check_shape(B, 3, C, 4);
+    if (st) return st;
+    if (B == 0 || C == 0) return ok();
+    if (!w || !u || !k || !v || !state || !y) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void* ptrs[] = {w, u, k, v, r, state, y};
+    for (const void* p : ptrs)
+        if (p && !aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    const linrec::WkvStepArgs A{w, u, k, v, r, state, y};
+    return hip_status(linrec::run_wkv_decode_step(A, B, C, (hipStream_t)stream), "wkv4_decode_step launch");
 }
 
 LINREC_API int linrec_scan_real(int64_t B, int64_t T, int64_t C, const float* a, const float* b,

@@ -70,40 +70,25 @@ struct WkvOpT {
     }
     __device__ __forceinline__ static Agg identity() { return {0.f, 0.f, kEmpty}; }
 
-    // A carried state (a, b, p) means A = a e^p, B = b e^p.  Natural-log exponents are
-    // converted to and from the integer base-2 ones with ln 2 split in two parts, so the
-    // exponent's own rounding does not scale the state.
-    static constexpr float kLn2Hi = 0.693145751953125f, kLn2Lo = 1.42860682030941723212e-6f;
+    // A carried state (a, b, p) in natural log (see wkv_math.hpp), read before the first
+    // token and written after the last.
     __device__ __forceinline__ static Agg init(const Args& A, const ScanGeom& g, int64_t b, int64_t c) {
-        if constexpr (!kExt) return identity();
-        if (!A.s_in) return identity();
-        const float* s = A.s_in + 3 * (b * g.C + c);
-        const float sa = s[0], sb = s[1], sp = s[2];
-        if (sa == 0.f && sb == 0.f) return identity();
-        const float P = ceilf(sp * kLog2e);
-        const float rem = fmaf(-P, kLn2Lo, fmaf(-P, kLn2Hi, sp));  // sp - P ln 2, in [-ln 2, 0] about
-        const float sc = fast_exp2(rem * kLog2e);
-        return {sa * sc, sb * sc, P};
+        if constexpr (!kExt) {
+            return identity();
+        } else {
+            if (!A.s_in) return identity();
+            const float* s = A.s_in + 3 * (b * g.C + c);
+            const Base2State x = state_from_natural(s[0], s[1], s[2]);
+            return {x.a, x.b, x.p};
+        }
     }
-    // After the last token: the state A = a 2^p as (a', b', p') with p' = float(p ln 2), the
-    // rounding of p' compensated in a', b'.
     __device__ __forceinline__ static void finish(const Args& A, const ScanGeom& g, int64_t b, int64_t c,
                                                   const Agg& s) {
-        if constexpr (!kExt) return;
-        if (!A.s_out) return;
-        float* o = A.s_out + 3 * (b * g.C + c);
-        if (s.b == 0.f) {
-            o[0] = 0.f;
-            o[1] = 0.f;
-            o[2] = 0.f;
-            return;
+        if constexpr (kExt) {
+            if (!A.s_out) return;
+            float* o = A.s_out + 3 * (b * g.C + c);
+            state_to_natural({s.a, s.b, s.p}, o[0], o[1], o[2]);
         }
-        const float pn = s.p * kLn2Hi + s.p * kLn2Lo;
-        const float delta = fmaf(s.p, kLn2Lo, fmaf(s.p, kLn2Hi, -pn));  // p ln 2 - pn
-        const float sc = fast_exp2(delta * kLog2e);
-        o[0] = s.a * sc;
-        o[1] = s.b * sc;
-        o[2] = pn;
     }
 
     static constexpr int kFloats = 1;  // floats per channel element

@@ -45,4 +45,37 @@ __device__ __forceinline__ void merge_scales(float p1, float b1, float p2, float
     f2 = fast_exp2(p2 - p);
 }
 
+// A state handed across calls is (a, b, p) with A = a e^p, B = b e^p (natural log, so a
+// caller can read it as the past sums of eq. (14)).  Conversions to and from the integer
+// base-2 exponent use ln 2 split in two parts, so the exponent's own rounding does not
+// scale the state.  a = b = 0 is the empty state.
+constexpr float kLn2Hi = 0.693145751953125f, kLn2Lo = 1.42860682030941723212e-6f;
+
+struct Base2State { float a, b, p; };
+
+__device__ __forceinline__ Base2State state_from_natural(float sa, float sb, float sp) {
+    if (sa == 0.f && sb == 0.f) return {0.f, 0.f, kEmpty};
+    const float P = ceilf(sp * kLog2e);
+    const float rem = fmaf(-P, kLn2Lo, fmaf(-P, kLn2Hi, sp));  // sp - P ln 2, in [-ln 2, 0] about
+    const float sc = fast_exp2(rem * kLog2e);
+    return {sa * sc, sb * sc, P};
+}
+
+// The state A = a 2^p as (a', b', p') with p' = float(p ln 2), the rounding of p' compensated
+// in a' and b'.
+__device__ __forceinline__ void state_to_natural(const Base2State& s, float& oa, float& ob, float& op) {
+    if (s.b == 0.f) {
+        oa = 0.f;
+        ob = 0.f;
+        op = 0.f;
+        return;
+    }
+    const float pn = s.p * kLn2Hi + s.p * kLn2Lo;
+    const float delta = fmaf(s.p, kLn2Lo, fmaf(s.p, kLn2Hi, -pn));  // p ln 2 - pn
+    const float sc = fast_exp2(delta * kLog2e);
+    oa = s.a * sc;
+    ob = s.b * sc;
+    op = pn;
+}
+
 }  // namespace linrec

@@ -173,3 +173,23 @@ def test_wkv4_forward_ex_argument_checks(lib):
     # misaligned optional inputs
     assert fx(1, 4, 4, P, P, P, P, ODD, None, P2, None, None, 0, None) == UNSUPPORTED
     assert fx(1, 4, 4, P, P, P, P, None, ODD, P2, None, None, 0, None) == UNSUPPORTED
+
+
+def test_wkv4_decode_step_argument_checks(lib):
+    fd = lib.wkv4_decode_step
+    # empty batch / channels: nothing to do, no pointer read
+    assert fd(0, 4, None, None, None, None, None, None, None, None) == OK
+    assert fd(3, 0, None, None, None, None, None, None, None, None) == OK
+    assert fd(-1, 4, P, P, P, P, None, P2, P2, None) == INVALID
+    # B * 3 * C floats overflowing int64
+    assert fd(1 << 40, 1 << 40, P, P, P, P, None, P2, P2, None) == INVALID
+    # required pointers (r is optional)
+    for i in (0, 1, 2, 3, 5, 6):
+        args = [P, P, P, P, None, P2, P2]
+        args[i] = None
+        assert fd(2, 4, *args, None) == INVALID, i
+    # alignment of every pointer, the optional gate included
+    for i in range(7):
+        args = [P, P, P, P, P, P2, P2]
+        args[i] = ODD
+        assert fd(2, 4, *args, None) == UNSUPPORTED, i
