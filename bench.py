@@ -220,7 +220,7 @@ def cpu_baseline(kind, host, budget_s):
         t0 = time.perf_counter()
         fn()
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start >= budget_s or len(times) >= 25:
+        if time.perf_counter() - t_start >= budget_s or len(times) >= 200:
             break
     return statistics.median(times), len(times), oracle.num_threads()
 
@@ -296,7 +296,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle CPU baseline (0 skips it)")
     ap.add_argument("--no-copy-probe", action="store_true")
     ap.add_argument("--all", action="store_true", help="also measure the other workloads")
