@@ -83,6 +83,12 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
         p.nw = 8;
         p.L = vec == 1 ? 32 : 16;
     }
+    // Coordination: in wave 0 by default; in a wave of its own for the complex scans, whose
+    // chunks hold many registers and whose long chains lean on the inclusive prefixes
+    // (LINREC_COORD: 1 wave 0, 2 own wave).
+    p.sep = vec == 1 && (kind == linrec::kKindComplex || kind == linrec::kKindComplexBwd);
+    const int64_t coord = env_int("LINREC_COORD", 0);
+    if (coord == 1 || coord == 2) p.sep = vec == 1 && coord == 2;
     const int nw = (int)env_int("LINREC_NW", 0), L = (int)env_int("LINREC_L", 0);
     if (nw > 0 && L > 0 && linrec::scan_shape_supported(kind, vec, nw, L)) {
         p.nw = nw;

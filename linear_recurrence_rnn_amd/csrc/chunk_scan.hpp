@@ -83,8 +83,9 @@ struct ScanGeom {
 
 struct ScanPlan {
     int vec;        // channels per lane (4, or 2 for complex; 1 for any C or alignment)
-    int nw;         // waves per workgroup (chunks per slab)
+    int nw;         // chunks per slab (waves per workgroup, one more with sep)
     int L;          // steps per chunk
+    bool sep;       // a coordinator wave of its own (one channel per lane only)
     int64_t nslab;  // slabs per sequence
     size_t ws_bytes;
 };
