@@ -220,7 +220,7 @@ def cpu_baseline(kind, host, budget_s):
         t0 = time.perf_counter()
         fn()
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start >= budget_s or len(times) >= 200:
+        if time.perf_counter() - t_start >= budget_s or len(times) >= 5000:
             break
     return statistics.median(times), len(times), oracle.num_threads()
 

@@ -68,7 +68,7 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
     // is arithmetic-heavy and favours occupancy (fewer registers per lane), the scans
     // favour wider rows; long single sequences favour longer slabs (shorter look-backs).
     if (kind == linrec::kKindWkv) {
-        p.nw = T <= 2048 ? 8 : 4;
+        p.nw = 8;
         p.L = 16;
     } else if (kind == linrec::kKindReal) {
         p.nw = 8;
@@ -110,14 +110,19 @@ int vmax_of(int kind) {
     return kind == linrec::kKindComplex ? 2 : 4;
 }
 
-// Channels per lane: the widest the alignment allows, narrowed by the default policy
-// (WKV and complex: 1, real scan: 2) or by LINREC_VEC (tests and tuning).
-int pick_vec(int kind, int vec_aligned) {
+// Channels per lane: the widest the alignment allows, narrowed by the default policy or by
+// LINREC_VEC (tests and tuning).  Measured on MI355X: the real scan takes 2; the plain WKV
+// forward takes 2 on calls of at least 2^25 elements, which run many rounds of workgroups
+// and gain from 512-byte rows, and 1 on smaller ones, which must fit the chip in one round;
+// the WKV forward with state or gate and the complex scan take 1.
+int pick_vec(int kind, int vec_aligned, int64_t elems = 0, bool plain = false) {
     int vec = vec_aligned;
     const int64_t f = env_int("LINREC_VEC", 0);
     if (f == 1 || f == 2 || f == 4) {
         vec = f < vec ? (int)f : vec;
-    } else if (kind == linrec::kKindWkv || kind == linrec::kKindComplex) {
+    } else if (kind == linrec::kKindWkv) {
+        vec = (plain && elems >= ((int64_t)1 << 25) && vec >= 2) ? 2 : 1;
+    } else if (kind == linrec::kKindComplex) {
         vec = 1;
     } else if (kind == linrec::kKindReal) {
         vec = vec < 2 ? vec : 2;
@@ -261,7 +266,8 @@ LINREC_API int wkv4_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, 
     const int vec = pick_vec(linrec::kKindWkv,
                              (C % 4 == 0 && aligned(k, 16) && aligned(v, 16) && aligned(y, 16) && wide_ok) ? 4
                              : (C % 2 == 0 && aligned(k, 8) && aligned(v, 8) && aligned(y, 8) && (!r || aligned(r, 8))) ? 2
-                                                                                                            : 1);
+                                                                                                            : 1,
+                             B * T * C, !r && !s_in && !s_out);
     const linrec::ScanPlan p = scan_plan(linrec::kKindWkv, vec, B, T, C);
     if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
     const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0, r, s_in, s_out};
