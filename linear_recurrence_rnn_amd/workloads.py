@@ -180,3 +180,14 @@ def make_scan_adjoint_inputs(wid: int, host: dict, seed: int | None = None):
             out[name] = z
         return out
     raise KeyError(wid)
+
+
+def make_token_shift(B: int, T: int, C: int, M: int, seed: int, with_grad: bool = False):
+    """Token-shift inputs: x (B,T,C) ~ N(0,1), x_prev (B,C) ~ N(0,1), mu (M,C) ~ U(0,1), and
+    g (M,B,T,C) ~ N(0,1) if ``with_grad``; all float32, drawn in that order."""
+    rng = np.random.default_rng(seed)
+    out = {"x": _normal(rng, (B, T, C), 1.0), "x_prev": _normal(rng, (B, C), 1.0),
+           "mu": rng.uniform(0.0, 1.0, size=(M, C)).astype(np.float32)}
+    if with_grad:
+        out["g"] = _normal(rng, (M, B, T, C), 1.0)
+    return out

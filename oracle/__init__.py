@@ -59,8 +59,12 @@ def _bind(path: str):
                                               _F64P, _F64P, _F64P]
     lib.oracle_scan_complex_backward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F64P, _F32P,
                                                  _F64P, _F64P, _F64P]
+    lib.oracle_token_shift.argtypes = [_I64, _I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
+    lib.oracle_token_shift_backward.argtypes = [_I64, _I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P,
+                                                _F64P, _F64P, _F64P]
     for name in ("oracle_wkv4_forward", "oracle_wkv4_backward", "oracle_scan_real",
-                 "oracle_scan_complex", "oracle_scan_real_backward", "oracle_scan_complex_backward"):
+                 "oracle_scan_complex", "oracle_scan_real_backward", "oracle_scan_complex_backward",
+                 "oracle_token_shift", "oracle_token_shift_backward"):
         getattr(lib, name).restype = None
     return lib
 
@@ -232,3 +236,34 @@ def scan_complex_backward(lam, x, gx, x0=None, want_gx0=None, lib=None):
                                                   f64(xd), _p32(gxc.view(np.float32)), f64(glam), f64(gu),
                                                   None if gx0 is None else f64(gx0))
     return glam, gu, gx0
+
+
+def token_shift(x, mu, x_prev=None, lib=None) -> np.ndarray:
+    """(M,B,T,C) float64: mu[m] x_t + (1 - mu[m]) x_{t-1}, x_{-1} = x_prev or 0 (RWKV-LLM page,
+    eqs. (11)-(13))."""
+    x = _f32(x)
+    B, T, C = x.shape
+    mu = _f32(mu)
+    M = mu.shape[0]
+    mu = _f32(mu, (M, C))
+    xp = None if x_prev is None else _f32(x_prev, (B, C))
+    out = np.empty((M, B, T, C), dtype=np.float64)
+    (lib or _load()).oracle_token_shift(B, T, C, M, _p32(x), None if xp is None else _p32(xp), _p32(mu), _p64(out))
+    return out
+
+
+def token_shift_backward(x, mu, g, x_prev=None, want_gx_prev=True, lib=None):
+    """(gx (B,T,C), gmu (M,C), gx_prev (B,C) or None) float64 of token_shift given g = dL/dout."""
+    x = _f32(x)
+    B, T, C = x.shape
+    mu = _f32(mu)
+    M = mu.shape[0]
+    mu = _f32(mu, (M, C))
+    g = _f32(g, (M, B, T, C))
+    xp = None if x_prev is None else _f32(x_prev, (B, C))
+    gx = np.empty((B, T, C), dtype=np.float64)
+    gmu = np.empty((M, C), dtype=np.float64)
+    gxp = np.empty((B, C), dtype=np.float64) if want_gx_prev else None
+    (lib or _load()).oracle_token_shift_backward(B, T, C, M, _p32(x), None if xp is None else _p32(xp), _p32(mu),
+                                                 _p32(g), _p64(gx), _p64(gmu), None if gxp is None else _p64(gxp))
+    return gx, gmu, gxp

@@ -347,3 +347,81 @@ void oracle_scan_complex_backward(int64_t B, int64_t T, int64_t C, const float *
     }
     free(part);
 }
+
+/*
+ * Token shift of the RWKV time-mix block.  RWKV-LLM page, section "Time-mixing block",
+ * eqs. (11)-(13): each projection input is a per-channel linear interpolation between
+ * the current token and the previous one (the page calls the recurrent form a linear
+ * interpolation of the current and previous inputs),
+ *
+ *   xm[m,b,t,c] = mu[m,c] x[b,t,c] + (1 - mu[m,c]) x[b,t-1,c],   m = 0 .. M-1,
+ *
+ * with x[b,-1,c] = x_prev[b,c] (the last token of an earlier call) or 0.  x (B,T,C),
+ * x_prev (B,C) or NULL, mu (M,C) float32; out (M,B,T,C) float64.
+ */
+void oracle_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, const float *x, const float *x_prev,
+                        const float *mu, double *out)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        for (int64_t m = 0; m < M; ++m) {
+            const double mm = (double)mu[m * C + c];
+            double prev = x_prev ? (double)x_prev[b * C + c] : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const double cur = (double)x[base + t * C];
+                out[m * B * T * C + base + t * C] = mm * cur + (1.0 - mm) * prev;
+                prev = cur;
+            }
+        }
+    }
+}
+
+/*
+ * Backward of oracle_token_shift (the pages give none; chain rule of eqs. (11)-(13)).
+ * With g = dL/dxm (M,B,T,C):
+ *   gx[b,t,c]     = sum_m ( mu[m,c] g[m,b,t,c] + (1 - mu[m,c]) g[m,b,t+1,c] )   (no t+1 term at T-1)
+ *   gx_prev[b,c]  = sum_m (1 - mu[m,c]) g[m,b,0,c]
+ *   gmu[m,c]      = sum over b and t of g[m,b,t,c] (x[b,t,c] - x[b,t-1,c])
+ * gmu adds each row's time sum, then the batch rows in ascending order.  gx (B,T,C),
+ * gmu (M,C) and gx_prev (B,C, may be NULL) are float64.
+ */
+void oracle_token_shift_backward(int64_t B, int64_t T, int64_t C, int64_t M, const float *x,
+                                 const float *x_prev, const float *mu, const float *g, double *gx,
+                                 double *gmu, double *gx_prev)
+{
+    double *part = (double *)calloc((size_t)(M * B * C) + 1, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        for (int64_t t = 0; t < T; ++t) gx[base + t * C] = 0.0;
+        double gp = 0.0;
+        for (int64_t m = 0; m < M; ++m) {
+            const double mm = (double)mu[m * C + c];
+            const float *gm = g + m * B * T * C;
+            double acc = 0.0;
+            double prev = x_prev ? (double)x_prev[b * C + c] : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t o = base + t * C;
+                const double gt = (double)gm[o];
+                const double gnext = (t + 1 < T) ? (double)gm[o + C] : 0.0;
+                gx[o] += mm * gt + (1.0 - mm) * gnext;
+                const double cur = (double)x[o];
+                acc += gt * (cur - prev);
+                prev = cur;
+            }
+            part[m * B * C + bc] = acc;
+            if (T > 0) gp += (1.0 - mm) * (double)gm[base];
+        }
+        if (gx_prev) gx_prev[b * C + c] = gp;
+    }
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < C; ++c) {
+            double s = 0.0;
+            for (int64_t b = 0; b < B; ++b) s += part[m * B * C + b * C + c];
+            gmu[m * C + c] = s;
+        }
+    free(part);
+}

@@ -62,6 +62,13 @@ MUTANTS = [
     ("gate_without_sigmoid", "const double gate = r ? 1.0 / (1.0 + exp(-(double)r[o])) : 1.0;",
      "const double gate = r ? (double)r[o] : 1.0;"),
     ("state_out_scale_dropped", "            s_out[3 * bc + 2] = K;", "            s_out[3 * bc + 2] = 0.0;"),
+    ("shift_mu_swapped", "out[m * B * T * C + base + t * C] = mm * cur + (1.0 - mm) * prev;",
+     "out[m * B * T * C + base + t * C] = (1.0 - mm) * cur + mm * prev;"),
+    ("shift_prev_ignored", "            double prev = x_prev ? (double)x_prev[b * C + c] : 0.0;\n            for (int64_t t = 0; t < T; ++t) {\n                const double cur = (double)x[base + t * C];\n                out",
+     "            double prev = 0.0;\n            for (int64_t t = 0; t < T; ++t) {\n                const double cur = (double)x[base + t * C];\n                out"),
+    ("shift_bwd_next_term_dropped", "gx[o] += mm * gt + (1.0 - mm) * gnext;", "gx[o] += mm * gt;"),
+    ("shift_bwd_gmu_sign", "acc += gt * (cur - prev);", "acc += gt * (prev - cur);"),
+    ("shift_bwd_gx_prev_weight", "if (T > 0) gp += (1.0 - mm) * (double)gm[base];", "if (T > 0) gp += mm * (double)gm[base];"),
 ]
 
 
@@ -118,6 +125,25 @@ def _pins_pass(lib) -> bool:
     r = rng.standard_normal(d["k"].shape).astype(np.float32)
     yg, _ = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"], r=r, lib=lib)
     ok &= np.allclose(yg, ref / (1.0 + np.exp(-r.astype(np.float64))), rtol=1e-10, atol=1e-12)
+
+    # Token shift: the end points mu = 1 (current token) and mu = 0 (previous token, x_prev
+    # first), and the exact adjoint identity of the linear map in x, x_prev and mu.
+    ts = workloads.make_token_shift(2, 9, 4, 2, 5, with_grad=True)
+    C4 = ts["x"].shape[2]
+    one = np.ones((1, C4), np.float32)
+    ok &= np.array_equal(oracle.token_shift(ts["x"], one, ts["x_prev"], lib=lib)[0], ts["x"].astype(np.float64))
+    o0 = oracle.token_shift(ts["x"], 0 * one, ts["x_prev"], lib=lib)[0]
+    ok &= np.array_equal(o0[:, 0], ts["x_prev"].astype(np.float64))
+    ok &= np.array_equal(o0[:, 1:], ts["x"][:, :-1].astype(np.float64))
+    gx, gmu, gxp = oracle.token_shift_backward(ts["x"], ts["mu"], ts["g"], ts["x_prev"], lib=lib)
+    vx = rng.standard_normal(ts["x"].shape).astype(np.float32)
+    vp = rng.standard_normal(ts["x_prev"].shape).astype(np.float32)
+    lhs = float(np.sum(ts["g"] * oracle.token_shift(vx, ts["mu"], vp, lib=lib)))
+    ok &= abs(lhs - float(np.sum(gx * vx) + np.sum(gxp * vp))) <= 1e-9 * max(1.0, abs(lhs))
+    mu2 = ts["mu"].copy()
+    mu2[1, 2] += np.float32(0.25)
+    diff = oracle.token_shift(ts["x"], mu2, ts["x_prev"], lib=lib) - oracle.token_shift(ts["x"], ts["mu"], ts["x_prev"], lib=lib)
+    ok &= abs(float(np.sum(ts["g"] * diff)) - gmu[1, 2] * (float(mu2[1, 2]) - float(ts["mu"][1, 2]))) <= 1e-9
     return bool(ok)
 
 
