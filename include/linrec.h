@@ -8,6 +8,7 @@
  *   wkv4_forward / wkv4_backward  the RWKV-4 time-mix operator of eq. (14) on that page
  *   wkv4_forward_ex               the same with a carried state and the sigma(r) gate
  *   wkv4_decode_step              one token of it in recurrent form (decoding)
+ *   rwkv_token_shift (+ backward) the time-mix token shift of eqs. (11)-(13) feeding it
  *   linrec_scan_real              x_t = a_t * x_{t-1} + b_t (the scan form on the
  *                                 "Were RNNs All We Needed?" news page, minGRU section)
  *   linrec_scan_complex           x_t = lambda * x_{t-1} + u_t (the LRU write-up on
@@ -121,6 +122,47 @@ int wkv4_forward_ex(int64_t B, int64_t T, int64_t C,
                     const float *w, const float *u, const float *k, const float *v,
                     const float *r, const float *s_in, float *y, float *s_out,
                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Token shift of the RWKV time-mix block (RWKV-LLM page, section "Time-mixing block", eqs.
+ * (11)-(13)): the inputs of the r, k and v projections interpolate per channel between the
+ * current token and the previous one,
+ *
+ *   out[m,b,t,c] = mu[m,c] * x[b,t,c] + (1 - mu[m,c]) * x[b,t-1,c],    m = 0 .. M-1,
+ *
+ * with x[b,-1,c] = x_prev[b,c], or 0 when x_prev is NULL.  One call reads x once and writes
+ * all M mixes (M = 3 for the time mix's r, k, v; 2 for the channel mix's r, k).
+ *
+ *   x      (B,T,C) float32;  x_prev (B,C) float32 or NULL (the last token of an earlier
+ *          call, for sequences processed in pieces)
+ *   mu     (M,C) float32, 1 <= M <= 4
+ *   out    (M,B,T,C) float32 output, mix m at out + m*B*T*C
+ *
+ * No workspace.  M outside 1..4 -> LINREC_ERR_INVALID_ARG.
+ */
+int rwkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, const float *x, const float *x_prev,
+                     const float *mu, float *out, void *stream);
+
+/*
+ * Backward of rwkv_token_shift (chain rule; the pages give none).  Given g = dL/dout
+ * (M,B,T,C):
+ *
+ *   gx[b,t,c]    = sum_m mu[m,c] g[m,b,t,c] + (1 - mu[m,c]) g[m,b,t+1,c]   (no t+1 term at T-1)
+ *   gmu[m,c]     = sum over b and t of g[m,b,t,c] (x[b,t,c] - x[b,t-1,c])
+ *   gx_prev[b,c] = sum_m (1 - mu[m,c]) g[m,b,0,c]
+ *
+ *   x, x_prev, mu as for the forward;  gx (B,T,C), gmu (M,C) float32 outputs;
+ *   gx_prev (B,C) float32 output or NULL.
+ *
+ * gmu is summed in float64 in a fixed order (results do not depend on scheduling) and
+ * needs rwkv_token_shift_backward_workspace_size(B, T, C, M) bytes of workspace.  With B or
+ * T = 0, gmu (and gx_prev when B > 0) are zero-filled.
+ */
+size_t rwkv_token_shift_backward_workspace_size(int64_t B, int64_t T, int64_t C, int64_t M);
+int rwkv_token_shift_backward(int64_t B, int64_t T, int64_t C, int64_t M, const float *x,
+                              const float *x_prev, const float *mu, const float *g, float *gx,
+                              float *gmu, float *gx_prev, void *workspace, size_t ws_bytes,
+                              void *stream);
 
 /*
  * One token of WKV-4 in its recurrent form, for token-by-token decoding (the RNN mode of

@@ -62,6 +62,12 @@ def load(path: str | None = None):
         lib.wkv4_forward_ex.restype = ctypes.c_int
         lib.wkv4_forward_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 8 + [_VP, _SZ, _VP]
         lib.wkv4_backward.restype = ctypes.c_int
+        lib.rwkv_token_shift.restype = ctypes.c_int
+        lib.rwkv_token_shift.argtypes = [_I64, _I64, _I64, _I64] + [_VP] * 4 + [_VP]
+        lib.rwkv_token_shift_backward_workspace_size.restype = _SZ
+        lib.rwkv_token_shift_backward_workspace_size.argtypes = [_I64, _I64, _I64, _I64]
+        lib.rwkv_token_shift_backward.restype = ctypes.c_int
+        lib.rwkv_token_shift_backward.argtypes = [_I64, _I64, _I64, _I64] + [_VP] * 7 + [_VP, _SZ, _VP]
         lib.wkv4_decode_step.restype = ctypes.c_int
         lib.wkv4_decode_step.argtypes = [_I64, _I64] + [_VP] * 7 + [_VP]
         lib.wkv4_backward.argtypes = [_I64, _I64, _I64] + [_VP] * 9 + [_VP, _SZ, _VP]
@@ -206,6 +212,50 @@ def wkv4_decode_step(w, u, k, v, state, r=None, out=None):
     _check(lib.wkv4_decode_step(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(state), _ptr(y),
                                 _stream(dev)), "wkv4_decode_step")
     return y
+
+
+def token_shift(x, mu, x_prev=None, out=None):
+    """(M,B,T,C) mixes mu[m] x_t + (1 - mu[m]) x_{t-1} of x (B,T,C) float32, mu (M,C);
+    x_{-1} = x_prev (B,C) or 0."""
+    lib = load()
+    B, T, C = x.shape
+    dev = x.device
+    M = mu.shape[0] if mu.dim() == 2 else -1
+    _expect(x, "x", torch.float32, (B, T, C), dev)
+    _expect(mu, "mu", torch.float32, (M, C), dev)
+    if x_prev is not None:
+        _expect(x_prev, "x_prev", torch.float32, (B, C), dev)
+    o = torch.empty((M, B, T, C), dtype=torch.float32, device=dev) if out is None else out
+    _expect(o, "out", torch.float32, (M, B, T, C), dev)
+    _check(lib.rwkv_token_shift(B, T, C, M, _ptr(x), _ptr(x_prev), _ptr(mu), _ptr(o), _stream(dev)),
+           "rwkv_token_shift")
+    return o
+
+
+def token_shift_backward(x, mu, g, x_prev=None, want_gx_prev=None, out=None, workspace=None):
+    """(gx (B,T,C), gmu (M,C), gx_prev (B,C) or None) of token_shift given g = dL/dout (M,B,T,C).
+    gx_prev is returned when ``want_gx_prev`` (default: when x_prev is given)."""
+    lib = load()
+    B, T, C = x.shape
+    dev = x.device
+    M = mu.shape[0] if mu.dim() == 2 else -1
+    _expect(x, "x", torch.float32, (B, T, C), dev)
+    _expect(mu, "mu", torch.float32, (M, C), dev)
+    _expect(g, "g", torch.float32, (M, B, T, C), dev)
+    if x_prev is not None:
+        _expect(x_prev, "x_prev", torch.float32, (B, C), dev)
+    if want_gx_prev is None:
+        want_gx_prev = x_prev is not None
+    if out is None:
+        gx = torch.empty_like(x)
+        gmu = torch.empty((M, C), dtype=torch.float32, device=dev)
+        gxp = torch.empty((B, C), dtype=torch.float32, device=dev) if want_gx_prev else None
+    else:
+        gx, gmu, gxp = out
+    ws, nws = _workspace(int(lib.rwkv_token_shift_backward_workspace_size(B, T, C, M)), dev, workspace)
+    _check(lib.rwkv_token_shift_backward(B, T, C, M, _ptr(x), _ptr(x_prev), _ptr(mu), _ptr(g), _ptr(gx), _ptr(gmu),
+                                         _ptr(gxp), _ptr(ws), nws, _stream(dev)), "rwkv_token_shift_backward")
+    return gx, gmu, gxp
 
 
 def wkv4_backward(w, u, k, v, gy, out=None, workspace=None):

@@ -11,6 +11,7 @@
 #include "chunk_scan.hpp"
 #include "wkv_backward.hpp"
 #include "wkv_decode.hpp"
+#include "token_shift.hpp"
 
 #define LINREC_API extern "C" __attribute__((visibility("default")))
 
@@ -280,6 +281,62 @@ LINREC_API int wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, con
                             const float* k, const float* v, float* y, void* workspace,
                             size_t ws_bytes, void* stream) {
     return wkv4_forward_ex(B, T, C, w, u, k, v, nullptr, nullptr, y, nullptr, workspace, ws_bytes, stream);
+}
+
+LINREC_API int rwkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t M, const float* x, const float* x_prev,
+                                const float* mu, float* out, void* stream) {
+    int st = check_shape(B, T, C, 4);
+    if (st) return st;
+    if (M < 1 || M > linrec::kShiftMaxM) return fail(LINREC_ERR_INVALID_ARG, "M must be 1..%d", linrec::kShiftMaxM);
+    if ((st = check_shape(M, B * T, C, 4))) return st;
+    if (B == 0 || T == 0 || C == 0) return ok();
+    if (!x || !mu || !out) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void* ptrs[] = {x, x_prev, mu, out};
+    for (const void* p : ptrs)
+        if (p && !aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    const bool a16 = aligned(x, 16) && aligned(out, 16) && (!x_prev || aligned(x_prev, 16));
+    const bool a8 = aligned(x, 8) && aligned(out, 8) && (!x_prev || aligned(x_prev, 8));
+    int vec = (C % 4 == 0 && a16) ? 4 : ((C % 2 == 0 && a8) ? 2 : 1);
+    const int64_t f = env_int("LINREC_VEC", 0);
+    if ((f == 1 || f == 2) && f < vec) vec = (int)f;
+    const linrec::TokenShiftArgs A{x, x_prev, mu, out};
+    return hip_status(linrec::run_token_shift(A, B, T, C, (int)M, vec, (hipStream_t)stream), "rwkv_token_shift launch");
+}
+
+LINREC_API size_t rwkv_token_shift_backward_workspace_size(int64_t B, int64_t T, int64_t C, int64_t M) {
+    if (check_shape(B, T, C, 4) || M < 1 || M > linrec::kShiftMaxM || B == 0 || T == 0 || C == 0) return 0;
+    return align256(linrec::token_shift_backward_ws_bytes(B, T, C, (int)M));
+}
+
+LINREC_API int rwkv_token_shift_backward(int64_t B, int64_t T, int64_t C, int64_t M, const float* x,
+                                         const float* x_prev, const float* mu, const float* g, float* gx,
+                                         float* gmu, float* gx_prev, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+    int st = check_shape(B, T, C, 4);
+    if (st) return st;
+    if (M < 1 || M > linrec::kShiftMaxM) return fail(LINREC_ERR_INVALID_ARG, "M must be 1..%d", linrec::kShiftMaxM);
+    if ((st = check_shape(M, B * T, C, 4))) return st;
+    if (C == 0) return ok();
+    if (B == 0 || T == 0) {
+        // Sums over an empty batch or sequence: zero.
+        if (!gmu) return fail(LINREC_ERR_INVALID_ARG, "gmu is NULL");
+        if (!aligned(gmu, 4) || (gx_prev && !aligned(gx_prev, 4)))
+            return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+        hipError_t e = linrec::run_fill_zero(gmu, M * C, (hipStream_t)stream);
+        if (e == hipSuccess && gx_prev && B > 0) e = linrec::run_fill_zero(gx_prev, B * C, (hipStream_t)stream);
+        return hip_status(e, "rwkv_token_shift_backward zero fill");
+    }
+    if (!x || !mu || !g || !gx || !gmu) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void* ptrs[] = {x, x_prev, mu, g, gx, gmu, gx_prev};
+    for (const void* p : ptrs)
+        if (p && !aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    if ((st = check_ws(workspace, ws_bytes, rwkv_token_shift_backward_workspace_size(B, T, C, M)))) return st;
+    const bool a8 = aligned(x, 8) && aligned(g, 8) && aligned(gx, 8) && (!x_prev || aligned(x_prev, 8));
+    int vec = (C % 2 == 0 && a8) ? 2 : 1;
+    if (env_int("LINREC_VEC", 0) == 1) vec = 1;
+    const linrec::TokenShiftBwdArgs A{x, x_prev, mu, g, gx, gmu, gx_prev, reinterpret_cast<double*>(workspace)};
+    return hip_status(linrec::run_token_shift_backward(A, B, T, C, (int)M, vec, (hipStream_t)stream),
+                      "rwkv_token_shift_backward launch");
 }
 
 LINREC_API int wkv4_decode_step(int64_t B, int64_t C, const float* w, const float* u, const float* k,

@@ -1,0 +1,210 @@
+// token_shift.hip -- the token shift of the RWKV time-mix block on gfx950.
+//
+// RWKV-LLM page, section "Time-mixing block", eqs. (11)-(13): the inputs of the r, k and v
+// projections interpolate per channel between the current token and the previous one,
+//   out[m,b,t,c] = mu[m,c] x[b,t,c] + (1 - mu[m,c]) x[b,t-1,c] = p + mu (x - p),  p = x[b,t-1,c],
+// with x[b,-1,c] = x_prev[b,c] (the last token of an earlier call) or 0.  One pass reads x
+// once and writes all M mixes (the r, k, v inputs of the time mix, or the r, k inputs of the
+// channel mix), instead of one pass per mix.
+//
+// Backward (chain rule; the pages give none), with g = dL/dout:
+//   gx[b,t,c]    = sum_m mu[m,c] g[m,b,t,c] + (1 - mu[m,c]) g[m,b,t+1,c]
+//   gx_prev[b,c] = sum_m (1 - mu[m,c]) g[m,b,0,c]
+//   gmu[m,c]     = sum_{b,t} g[m,b,t,c] (x[b,t,c] - x[b,t-1,c])
+//
+// Layout of work: a wave owns VEC channels per lane (64 * VEC contiguous channels, so every
+// wave-wide access is one contiguous row segment) over TS consecutive time steps, and holds
+// the rows it needs in registers: the TS rows of its span and the row before it (read
+// again by the neighbouring span, 1/TS extra), plus, in the backward, the row after it.
+// Both passes are HBM-bound streams (forward 4 + 4M bytes per element, backward 8 + 4M).
+// gmu is summed in float64: per wave over its span, over the 4 waves of a block in order,
+// then over blocks in a fixed order by a second kernel, so it does not depend on scheduling.
+#include "device_common.hpp"
+#include "token_shift.hpp"
+
+namespace linrec {
+
+namespace {
+
+constexpr int kShiftTS = 16;       // time steps per wave
+constexpr int kShiftWaves = 4;     // waves per block
+
+template <int VEC>
+__device__ __forceinline__ FV<VEC> load_or_zero(const float* p, bool ok) {
+    FV<VEC> r{};
+    if (ok) r = ldg<VEC>(p);
+    return r;
+}
+
+// Forward: wave item (b, tc, grp), grp fastest, so neighbouring waves stream neighbouring
+// channel groups of the same rows.
+template <int VEC>
+__global__ __launch_bounds__(64 * kShiftWaves) void token_shift_kernel(TokenShiftArgs A, int64_t B, int64_t T,
+                                                                       int64_t C, int M) {
+    constexpr int TS = kShiftTS;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ngrp = (C + 64 * VEC - 1) / (64 * VEC), ntc = (T + TS - 1) / TS;
+    const int64_t item = (int64_t)blockIdx.x * kShiftWaves + wv;
+    if (item >= B * ntc * ngrp) return;  // wave-uniform
+    const int64_t grp = item % ngrp, tc = (item / ngrp) % ntc, b = item / (ngrp * ntc);
+    const int64_t c = grp * 64 * VEC + (int64_t)lane * VEC;
+    const bool active = c < C;  // C is a multiple of VEC
+    const int64_t t0 = tc * TS;
+    const int n = (int)((T - t0) < TS ? (T - t0) : TS);
+    const float* xr = A.x + (b * T + t0) * C + c;
+
+    FV<VEC> prev = load_or_zero<VEC>(t0 > 0 ? xr - C : (A.x_prev ? A.x_prev + b * C + c : nullptr),
+                                     active && (t0 > 0 || A.x_prev));
+    FV<VEC> xs[TS];
+#pragma unroll
+    for (int j = 0; j < TS; ++j) xs[j] = load_or_zero<VEC>(xr + (int64_t)j * C, active && j < n);
+    if (!active) return;
+    for (int m = 0; m < M; ++m) {
+        float mu[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) mu[e] = A.mu[m * C + c + e];
+        float* o = A.out + (int64_t)m * B * T * C + (b * T + t0) * C + c;
+        FV<VEC> p = prev;
+#pragma unroll
+        for (int j = 0; j < TS; ++j) {
+            if (j < n) {
+                FV<VEC> y;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) y.v[e] = fmaf(mu[e], xs[j].v[e] - p.v[e], p.v[e]);
+                stg<VEC>(o + (int64_t)j * C, y);
+            }
+            p = xs[j];
+        }
+    }
+}
+
+// Backward: block (b, tcb, grp); wave w takes steps [tcb*4*TS + w*TS, +TS).
+template <int VEC>
+__global__ __launch_bounds__(64 * kShiftWaves) void token_shift_bwd_kernel(TokenShiftBwdArgs A, int64_t B, int64_t T,
+                                                                           int64_t C, int M) {
+    constexpr int TS = kShiftTS;
+    constexpr int CW = 64 * VEC;
+    __shared__ double sh[kShiftWaves][kShiftMaxM][CW];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ngrp = (C + CW - 1) / CW, ntcb = (T + kShiftWaves * TS - 1) / (kShiftWaves * TS);
+    const int64_t blk = blockIdx.x;
+    const int64_t grp = blk % ngrp, tcb = (blk / ngrp) % ntcb, b = blk / (ngrp * ntcb);
+    const int64_t c = grp * CW + (int64_t)lane * VEC;
+    const bool active = c < C;
+    const int64_t t0 = (tcb * kShiftWaves + wv) * TS;
+    const int n = t0 >= T ? 0 : (int)((T - t0) < TS ? (T - t0) : TS);
+    const float* xr = A.x + (b * T + t0) * C + c;
+
+    // x rows t0-1 .. t0+n-1 (row t0-1 is x_prev, or 0, at the start of the sequence).
+    FV<VEC> xs[TS + 1];
+    xs[0] = load_or_zero<VEC>(t0 > 0 ? xr - C : (A.x_prev ? A.x_prev + b * C + c : nullptr),
+                              active && n > 0 && (t0 > 0 || A.x_prev));
+#pragma unroll
+    for (int j = 0; j < TS; ++j) xs[j + 1] = load_or_zero<VEC>(xr + (int64_t)j * C, active && j < n);
+    FV<VEC> gx[TS];
+#pragma unroll
+    for (int j = 0; j < TS; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) gx[j].v[e] = 0.f;
+    float gxp[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) gxp[e] = 0.f;
+
+    for (int m = 0; m < M; ++m) {
+        const float* gr = A.g + (int64_t)m * B * T * C + (b * T + t0) * C + c;
+        // g rows t0 .. t0+n (row t0+n belongs to the next span; 0 past the end).
+        FV<VEC> gs[TS + 1];
+#pragma unroll
+        for (int j = 0; j <= TS; ++j) gs[j] = load_or_zero<VEC>(gr + (int64_t)j * C, active && j <= n && t0 + j < T);
+        float mu[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) mu[e] = active ? A.mu[m * C + c + e] : 0.f;
+        double part[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) part[e] = 0.0;
+#pragma unroll
+        for (int j = 0; j < TS; ++j) {
+            if (j < n) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    gx[j].v[e] = fmaf(mu[e], gs[j].v[e], fmaf(1.f - mu[e], gs[j + 1].v[e], gx[j].v[e]));
+                    part[e] = fma((double)gs[j].v[e], (double)xs[j + 1].v[e] - (double)xs[j].v[e], part[e]);
+                }
+            }
+        }
+        if (t0 == 0) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) gxp[e] = fmaf(1.f - mu[e], gs[0].v[e], gxp[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sh[wv][m][lane * VEC + e] = part[e];
+    }
+    if (active) {
+        float* go = A.gx + (b * T + t0) * C + c;
+#pragma unroll
+        for (int j = 0; j < TS; ++j)
+            if (j < n) stg<VEC>(go + (int64_t)j * C, gx[j]);
+        if (t0 == 0 && A.gx_prev) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) A.gx_prev[b * C + c + e] = gxp[e];
+        }
+    }
+    __syncthreads();
+    if (wv == 0 && active) {
+        for (int m = 0; m < M; ++m) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                double s = 0.0;
+                for (int w = 0; w < kShiftWaves; ++w) s += sh[w][m][lane * VEC + e];
+                A.part[((b * ntcb + tcb) * M + m) * C + c + e] = s;
+            }
+        }
+    }
+}
+
+// gmu[m,c] = sum over (b, tcb) of the block sums, b outer, tcb inner.
+__global__ __launch_bounds__(256) void token_shift_mu_kernel(TokenShiftBwdArgs A, int64_t nblk, int64_t C, int M) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)M * C) return;
+    const int64_t m = i / C, c = i - m * C;
+    double s = 0.0;
+    for (int64_t k = 0; k < nblk; ++k) s += A.part[(k * M + m) * C + c];
+    A.gmu[i] = (float)s;
+}
+
+}  // namespace
+
+hipError_t run_token_shift(const TokenShiftArgs& A, int64_t B, int64_t T, int64_t C, int M, int vec,
+                           hipStream_t st) {
+    const int64_t cw = 64 * vec;
+    const int64_t items = B * ((T + kShiftTS - 1) / kShiftTS) * ((C + cw - 1) / cw);
+    const dim3 grid((unsigned)((items + kShiftWaves - 1) / kShiftWaves)), block(64 * kShiftWaves);
+    if (vec == 4) hipLaunchKernelGGL(token_shift_kernel<4>, grid, block, 0, st, A, B, T, C, M);
+    else if (vec == 2) hipLaunchKernelGGL(token_shift_kernel<2>, grid, block, 0, st, A, B, T, C, M);
+    else hipLaunchKernelGGL(token_shift_kernel<1>, grid, block, 0, st, A, B, T, C, M);
+    return hipGetLastError();
+}
+
+size_t token_shift_backward_ws_bytes(int64_t B, int64_t T, int64_t C, int M) {
+    const int64_t ntcb = (T + kShiftWaves * kShiftTS - 1) / (kShiftWaves * kShiftTS);
+    return (size_t)(B * ntcb * M * C) * sizeof(double);
+}
+
+hipError_t run_token_shift_backward(const TokenShiftBwdArgs& A, int64_t B, int64_t T, int64_t C, int M, int vec,
+                                    hipStream_t st) {
+    const int64_t cw = 64 * vec;
+    const int64_t ntcb = (T + kShiftWaves * kShiftTS - 1) / (kShiftWaves * kShiftTS);
+    const int64_t nblk = B * ntcb;
+    const dim3 grid((unsigned)(nblk * ((C + cw - 1) / cw))), block(64 * kShiftWaves);
+    if (vec == 2) hipLaunchKernelGGL(token_shift_bwd_kernel<2>, grid, block, 0, st, A, B, T, C, M);
+    else hipLaunchKernelGGL(token_shift_bwd_kernel<1>, grid, block, 0, st, A, B, T, C, M);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t mc = (int64_t)M * C;
+    hipLaunchKernelGGL(token_shift_mu_kernel, dim3((unsigned)((mc + 255) / 256)), dim3(256), 0, st, A, nblk, C, M);
+    return hipGetLastError();
+}
+
+}  // namespace linrec

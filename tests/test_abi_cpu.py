@@ -193,3 +193,31 @@ def test_wkv4_decode_step_argument_checks(lib):
         args = [P, P, P, P, P, P2, P2]
         args[i] = ODD
         assert fd(2, 4, *args, None) == UNSUPPORTED, i
+
+
+def test_token_shift_argument_checks(lib):
+    f, fb, wsz = lib.rwkv_token_shift, lib.rwkv_token_shift_backward, lib.rwkv_token_shift_backward_workspace_size
+    # empty shapes: nothing to do, no pointer read
+    assert f(0, 4, 4, 3, None, None, None, None, None) == OK
+    assert f(2, 0, 4, 3, None, None, None, None, None) == OK
+    # M outside 1..4, negative sizes, overflow
+    assert f(1, 4, 4, 0, P, None, P, P2, None) == INVALID
+    assert f(1, 4, 4, 5, P, None, P, P2, None) == INVALID
+    assert f(-1, 4, 4, 3, P, None, P, P2, None) == INVALID
+    assert f(1 << 40, 1 << 20, 4, 3, P, None, P, P2, None) == INVALID
+    # required pointers, alignment (x_prev optional)
+    assert f(1, 4, 4, 3, None, None, P, P2, None) == INVALID
+    assert f(1, 4, 4, 3, P, None, P, None, None) == INVALID
+    assert f(1, 4, 4, 3, P, ODD, P, P2, None) == UNSUPPORTED
+    assert f(1, 4, 4, 3, P, None, ODD, P2, None) == UNSUPPORTED
+    # backward: workspace size and checks
+    need = wsz(2, 100, 8, 3)
+    assert need > 0 and wsz(2, 0, 8, 3) == 0 and wsz(2, 100, 8, 7) == 0
+    assert fb(2, 100, 8, 3, P, None, P, P, P2, P2, None, None, need, None) == INVALID   # NULL workspace
+    assert fb(2, 100, 8, 3, P, None, P, P, P2, P2, None, P, need - 1, None) == WORKSPACE
+    assert fb(2, 100, 8, 3, P, None, P, None, P2, P2, None, P, need, None) == INVALID
+    assert fb(2, 100, 8, 3, P, None, P, P, P2, ODD, None, P, need, None) == UNSUPPORTED
+    assert fb(2, 100, 8, 9, P, None, P, P, P2, P2, None, P, need, None) == INVALID
+    assert fb(2, 100, 0, 3, None, None, None, None, None, None, None, None, 0, None) == OK
+    # empty batch or sequence needs gmu to zero-fill
+    assert fb(2, 0, 8, 3, None, None, None, None, None, None, None, None, 0, None) == INVALID
