@@ -10,8 +10,8 @@ serve a repeated call: R = ceil(2 * 256 MB / footprint) sets.
 
 ``--all`` also measures the other workloads (WKV-4 forward+backward at B=8 T=4096 C=2560,
 minGRU real scan and its adjoint at B=64 T=4096 C=256, LRU complex scan and its adjoint at
-B=1 T=262144 C=1024) and writes their lines to ``--all-out`` (they are parity workloads,
-not the headline line).
+B=1 T=262144 C=1024, the RWKV token shift and its backward at B=8 T=1024 C=768 with 3 mixes)
+and writes their lines to ``--all-out`` (they are parity workloads, not the headline line).
 """
 
 from __future__ import annotations
@@ -36,7 +36,10 @@ MALL_BYTES = 256 * 1024 * 1024  # MI355X Infinity Cache
 # Algorithmic bytes per element: inputs read once, outputs written once.
 BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "scan_complex": 16,
                   "scan_real_backward": 20,      # read a, x, gx; write ga, gb
-                  "scan_complex_backward": 24}   # read x, gx; write gu (complex64)
+                  "scan_complex_backward": 24,   # read x, gx; write gu (complex64)
+                  "token_shift": 16,             # read x; write 3 mixes
+                  "token_shift_backward": 20}    # read x, 3 gradients; write gx
+SHIFT_M = 3  # token-shift mixes timed: the r, k, v inputs of the time mix
 
 
 def log(*a):
@@ -52,6 +55,8 @@ KERNEL_SOURCES = {
     "scan_complex": _SCAN_SOURCES,
     "scan_real_backward": _SCAN_SOURCES,
     "scan_complex_backward": _SCAN_SOURCES,
+    "token_shift": ("api.hip", "token_shift.hip", "token_shift.hpp", "device_common.hpp"),
+    "token_shift_backward": ("api.hip", "token_shift.hip", "token_shift.hpp", "device_common.hpp"),
     "wkv4_backward": ("api.hip", "wkv_backward.hip", "wkv_backward.hpp", "lookback.hpp", "device_common.hpp",
                       "wkv_math.hpp"),
 }
@@ -163,6 +168,30 @@ class Row:
                                    gx.data_ptr(), glam.data_ptr(), gu.data_ptr(), None, ws.data_ptr(), nws,
                                    stream)))
             self.keep += [lam, glam]
+        elif kind == "token_shift":
+            M = host["mu"].shape[0]
+            mu = to(host["mu"])
+            for _ in range(rotations):
+                x = to(host["x"])
+                out = torch.empty((M, B, T, C), dtype=torch.float32, device=dev)
+                self.keep += [x, out]
+                self.calls.append((lib.rwkv_token_shift, (B, T, C, M, x.data_ptr(), None, mu.data_ptr(),
+                                   out.data_ptr(), stream)))
+            self.keep.append(mu)
+        elif kind == "token_shift_backward":
+            M = host["mu"].shape[0]
+            mu = to(host["mu"])
+            nws = int(lib.rwkv_token_shift_backward_workspace_size(B, T, C, M))
+            gmu = torch.empty((M, C), dtype=torch.float32, device=dev)
+            for _ in range(rotations):
+                x, g = to(host["x"]), to(host["g"])
+                gx = torch.empty_like(x)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [x, g, gx, ws]
+                self.calls.append((lib.rwkv_token_shift_backward, (B, T, C, M, x.data_ptr(), None, mu.data_ptr(),
+                                   g.data_ptr(), gx.data_ptr(), gmu.data_ptr(), None, ws.data_ptr(), nws,
+                                   stream)))
+            self.keep += [mu, gmu]
         else:
             raise KeyError(kind)
 
@@ -213,7 +242,10 @@ def cpu_baseline(kind, host, budget_s):
           "scan_real": lambda: oracle.scan_real(host["a"], host["b"]),
           "scan_complex": lambda: oracle.scan_complex(host["lam"], host["u"]),
           "scan_real_backward": lambda: oracle.scan_real_backward(host["a"], host["x"], host["gx"]),
-          "scan_complex_backward": lambda: oracle.scan_complex_backward(host["lam"], host["x"], host["gx"])}[kind]
+          "scan_complex_backward": lambda: oracle.scan_complex_backward(host["lam"], host["x"], host["gx"]),
+          "token_shift": lambda: oracle.token_shift(host["x"], host["mu"]),
+          "token_shift_backward": lambda: oracle.token_shift_backward(host["x"], host["mu"], host["g"],
+                                                                      want_gx_prev=False)}[kind]
     times = []
     t_start = time.perf_counter()
     while True:
@@ -252,20 +284,27 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
 
     wl = workloads.WORKLOADS[wid]
     B, T, C = shape or (wl.B, wl.T, wl.C)
-    host = workloads.make_inputs(wid, shape=(B, T, C))
+    if kind.startswith("token_shift"):
+        host = workloads.make_token_shift(B, T, C, SHIFT_M, wl.seed, with_grad=kind.endswith("_backward"))
+    else:
+        host = workloads.make_inputs(wid, shape=(B, T, C))
     if kind.endswith("_backward") and kind.startswith("scan_"):
         host.update(workloads.make_scan_adjoint_inputs(wid, host))
     elements = B * T * C
+    label = wl.label
+    if kind.startswith("token_shift"):
+        label = "RWKV token shift%s, %d mixes, fp32 B=%d T=%d C=%d" % (
+            " backward" if kind.endswith("_backward") else "", SHIFT_M, B, T, C)
     footprint = BYTES_PER_ELEM[kind] * elements
     R = rotations_for(footprint)
     log("[bench] %s %s: B=%d T=%d C=%d, %d buffer set(s) of %.1f MB" % (
-        kind, wl.label, B, T, C, R, footprint / 1e6))
+        kind, label, B, T, C, R, footprint / 1e6))
     row = Row(lib, kind, B, T, C, host, R)
     wall, ev_s = row.run(steps, warmup)
     per_step = wall / steps
     per_launch = ev_s / steps
     out = {
-        "kind": kind, "workload": wl.label, "B": B, "T": T, "C": C, "rotations": R,
+        "kind": kind, "workload": label, "B": B, "T": T, "C": C, "rotations": R,
         "ms_per_step": round(per_step * 1e3, 5), "event_ms_per_step": round(per_launch * 1e3, 5),
         "elements_per_s": elements / per_step,
         "roofline": roofline(kind, elements, per_launch, counter_traffic(kind)),
@@ -276,7 +315,8 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
         desc = "full workload"
         if cpu_slice is not None:
             Ts = cpu_slice
-            sample = {k: (v[:, :Ts] if hasattr(v, "ndim") and v.ndim == 3 else v) for k, v in host.items()}
+            sample = {k: (v[:, :Ts] if hasattr(v, "ndim") and v.ndim == 3 else
+                          (v[:, :, :Ts] if hasattr(v, "ndim") and v.ndim == 4 else v)) for k, v in host.items()}
             desc = "first %d of %d time steps, all batch rows and channels" % (Ts, T)
         if kind.endswith("_backward") and kind.startswith("scan_"):
             # The adjoint's forward input: the oracle's own forward scan of the sample.
@@ -347,7 +387,8 @@ def main():
         for wid, kind, steps, cpu_slice in ((3, "wkv4_forward", 20, 512), (3, "wkv4_backward", 20, 256),
                                             (4, "scan_real", 20, 512), (5, "scan_complex", 10, 16384),
                                             (4, "scan_real_backward", 20, 512),
-                                            (5, "scan_complex_backward", 10, 16384)):
+                                            (5, "scan_complex_backward", 10, 16384),
+                                            (2, "token_shift", 50, None), (2, "token_shift_backward", 50, None)):
             rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
             log("[bench] " + json.dumps(rows[-1]))
         os.makedirs(os.path.dirname(args.all_out), exist_ok=True)

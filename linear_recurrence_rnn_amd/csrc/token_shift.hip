@@ -79,13 +79,14 @@ __global__ __launch_bounds__(64 * kShiftWaves) void token_shift_kernel(TokenShif
     }
 }
 
-// Backward: block (b, tcb, grp); wave w takes steps [tcb*4*TS + w*TS, +TS).
-template <int VEC>
+// Backward: block (b, tcb, grp); wave w takes steps [(tcb*4 + w)*TS, +TS).  Every row the
+// wave needs (x and all M gradients) is loaded before any is used, so the whole span is in
+// flight at once.
+template <int VEC, int TS, int M>
 __global__ __launch_bounds__(64 * kShiftWaves) void token_shift_bwd_kernel(TokenShiftBwdArgs A, int64_t B, int64_t T,
-                                                                           int64_t C, int M) {
-    constexpr int TS = kShiftTS;
+                                                                           int64_t C) {
     constexpr int CW = 64 * VEC;
-    __shared__ double sh[kShiftWaves][kShiftMaxM][CW];
+    __shared__ double sh[kShiftWaves][M][CW];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t ngrp = (C + CW - 1) / CW, ntcb = (T + kShiftWaves * TS - 1) / (kShiftWaves * TS);
@@ -97,62 +98,68 @@ __global__ __launch_bounds__(64 * kShiftWaves) void token_shift_bwd_kernel(Token
     const int n = t0 >= T ? 0 : (int)((T - t0) < TS ? (T - t0) : TS);
     const float* xr = A.x + (b * T + t0) * C + c;
 
-    // x rows t0-1 .. t0+n-1 (row t0-1 is x_prev, or 0, at the start of the sequence).
+    // x rows t0-1 .. t0+n-1 (row t0-1 is x_prev, or 0, at the start of the sequence) and
+    // g rows t0 .. t0+n (row t0+n belongs to the next span; 0 past the end).
     FV<VEC> xs[TS + 1];
     xs[0] = load_or_zero<VEC>(t0 > 0 ? xr - C : (A.x_prev ? A.x_prev + b * C + c : nullptr),
                               active && n > 0 && (t0 > 0 || A.x_prev));
 #pragma unroll
     for (int j = 0; j < TS; ++j) xs[j + 1] = load_or_zero<VEC>(xr + (int64_t)j * C, active && j < n);
-    FV<VEC> gx[TS];
+    FV<VEC> gs[M][TS + 1];
 #pragma unroll
-    for (int j = 0; j < TS; ++j)
+    for (int m = 0; m < M; ++m) {
+        const float* gr = A.g + (int64_t)m * B * T * C + (b * T + t0) * C + c;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) gx[j].v[e] = 0.f;
+        for (int j = 0; j <= TS; ++j)
+            gs[m][j] = load_or_zero<VEC>(gr + (int64_t)j * C, active && j <= n && t0 + j < T);
+    }
+    float mu[M][VEC];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) mu[m][e] = active ? A.mu[m * C + c + e] : 0.f;
+
     float gxp[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) gxp[e] = 0.f;
-
+#pragma unroll
     for (int m = 0; m < M; ++m) {
-        const float* gr = A.g + (int64_t)m * B * T * C + (b * T + t0) * C + c;
-        // g rows t0 .. t0+n (row t0+n belongs to the next span; 0 past the end).
-        FV<VEC> gs[TS + 1];
-#pragma unroll
-        for (int j = 0; j <= TS; ++j) gs[j] = load_or_zero<VEC>(gr + (int64_t)j * C, active && j <= n && t0 + j < T);
-        float mu[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) mu[e] = active ? A.mu[m * C + c + e] : 0.f;
         double part[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) part[e] = 0.0;
+        for (int e = 0; e < VEC; ++e) {
+            part[e] = 0.0;
 #pragma unroll
-        for (int j = 0; j < TS; ++j) {
-            if (j < n) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    gx[j].v[e] = fmaf(mu[e], gs[j].v[e], fmaf(1.f - mu[e], gs[j + 1].v[e], gx[j].v[e]));
-                    part[e] = fma((double)gs[j].v[e], (double)xs[j + 1].v[e] - (double)xs[j].v[e], part[e]);
-                }
-            }
+            for (int j = 0; j < TS; ++j)
+                if (j < n) part[e] = fma((double)gs[m][j].v[e], (double)xs[j + 1].v[e] - (double)xs[j].v[e], part[e]);
+            gxp[e] = fmaf(1.f - mu[m][e], gs[m][0].v[e], gxp[e]);
+            sh[wv][m][lane * VEC + e] = part[e];
         }
-        if (t0 == 0) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) gxp[e] = fmaf(1.f - mu[e], gs[0].v[e], gxp[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) sh[wv][m][lane * VEC + e] = part[e];
     }
     if (active) {
         float* go = A.gx + (b * T + t0) * C + c;
 #pragma unroll
-        for (int j = 0; j < TS; ++j)
-            if (j < n) stg<VEC>(go + (int64_t)j * C, gx[j]);
-        if (t0 == 0 && A.gx_prev) {
+        for (int j = 0; j < TS; ++j) {
+            if (j < n) {
+                FV<VEC> gx;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        acc = fmaf(mu[m][e], gs[m][j].v[e], fmaf(1.f - mu[m][e], gs[m][j + 1].v[e], acc));
+                    gx.v[e] = acc;
+                }
+                stg<VEC>(go + (int64_t)j * C, gx);
+            }
+        }
+        if (t0 == 0 && n > 0 && A.gx_prev) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) A.gx_prev[b * C + c + e] = gxp[e];
         }
     }
     __syncthreads();
     if (wv == 0 && active) {
+#pragma unroll
         for (int m = 0; m < M; ++m) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -164,14 +171,42 @@ __global__ __launch_bounds__(64 * kShiftWaves) void token_shift_bwd_kernel(Token
     }
 }
 
-// gmu[m,c] = sum over (b, tcb) of the block sums, b outer, tcb inner.
-__global__ __launch_bounds__(256) void token_shift_mu_kernel(TokenShiftBwdArgs A, int64_t nblk, int64_t C, int M) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)M * C) return;
-    const int64_t m = i / C, c = i - m * C;
+// gmu[m,c] = sum over the nblk block sums (b outer, tcb inner), in a fixed association:
+// block (m, 64 channels) of 16 waves; wave w adds the w-th sixteenth of the block sums
+// round-robin into 8 accumulators (8 loads in flight at a time), which are then added in
+// order, and the 16 parts are added in order.
+constexpr int kMuWaves = 16;
+
+__global__ __launch_bounds__(64 * kMuWaves) void token_shift_mu_kernel(TokenShiftBwdArgs A, int64_t nblk, int64_t C,
+                                                                        int M) {
+    __shared__ double sh[kMuWaves][64];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int64_t ncg = (C + 63) / 64;
+    const int64_t m = blockIdx.x / ncg, c = (blockIdx.x - m * ncg) * 64 + lane;
+    const int64_t q = (nblk + kMuWaves - 1) / kMuWaves;
+    const int64_t k0 = wv * q < nblk ? wv * q : nblk, k1 = (k0 + q) < nblk ? (k0 + q) : nblk;
+    double acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+    if (c < C) {
+        int64_t k = k0;
+        for (; k + 8 <= k1; k += 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += A.part[((k + i) * M + m) * C + c];
+        }
+        for (int i = 0; k < k1; ++k, ++i) acc[i] += A.part[(k * M + m) * C + c];
+    }
     double s = 0.0;
-    for (int64_t k = 0; k < nblk; ++k) s += A.part[(k * M + m) * C + c];
-    A.gmu[i] = (float)s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += acc[i];
+    sh[wv][lane] = s;
+    __syncthreads();
+    if (wv == 0 && c < C) {
+        double t = 0.0;
+        for (int w = 0; w < kMuWaves; ++w) t += sh[w][lane];
+        A.gmu[m * C + c] = (float)t;
+    }
 }
 
 }  // namespace
@@ -187,23 +222,40 @@ hipError_t run_token_shift(const TokenShiftArgs& A, int64_t B, int64_t T, int64_
     return hipGetLastError();
 }
 
-size_t token_shift_backward_ws_bytes(int64_t B, int64_t T, int64_t C, int M) {
-    const int64_t ntcb = (T + kShiftWaves * kShiftTS - 1) / (kShiftWaves * kShiftTS);
+// Backward spans: 16 steps for one channel per lane, 8 for two (the gradient rows of every
+// mix stay in registers).
+constexpr int shift_bwd_ts(int vec) { return vec == 2 ? 8 : kShiftTS; }
+
+size_t token_shift_backward_ws_bytes(int64_t B, int64_t T, int64_t C, int M, int vec) {
+    const int ts = shift_bwd_ts(vec);
+    const int64_t ntcb = (T + kShiftWaves * ts - 1) / (kShiftWaves * ts);
     return (size_t)(B * ntcb * M * C) * sizeof(double);
 }
+
+namespace {
+template <int VEC, int TS>
+void launch_bwd(const TokenShiftBwdArgs& A, dim3 grid, int64_t B, int64_t T, int64_t C, int M, hipStream_t st) {
+    const dim3 block(64 * kShiftWaves);
+    if (M == 1) hipLaunchKernelGGL((token_shift_bwd_kernel<VEC, TS, 1>), grid, block, 0, st, A, B, T, C);
+    else if (M == 2) hipLaunchKernelGGL((token_shift_bwd_kernel<VEC, TS, 2>), grid, block, 0, st, A, B, T, C);
+    else if (M == 3) hipLaunchKernelGGL((token_shift_bwd_kernel<VEC, TS, 3>), grid, block, 0, st, A, B, T, C);
+    else hipLaunchKernelGGL((token_shift_bwd_kernel<VEC, TS, 4>), grid, block, 0, st, A, B, T, C);
+}
+}  // namespace
 
 hipError_t run_token_shift_backward(const TokenShiftBwdArgs& A, int64_t B, int64_t T, int64_t C, int M, int vec,
                                     hipStream_t st) {
     const int64_t cw = 64 * vec;
-    const int64_t ntcb = (T + kShiftWaves * kShiftTS - 1) / (kShiftWaves * kShiftTS);
+    const int ts = shift_bwd_ts(vec);
+    const int64_t ntcb = (T + kShiftWaves * ts - 1) / (kShiftWaves * ts);
     const int64_t nblk = B * ntcb;
-    const dim3 grid((unsigned)(nblk * ((C + cw - 1) / cw))), block(64 * kShiftWaves);
-    if (vec == 2) hipLaunchKernelGGL(token_shift_bwd_kernel<2>, grid, block, 0, st, A, B, T, C, M);
-    else hipLaunchKernelGGL(token_shift_bwd_kernel<1>, grid, block, 0, st, A, B, T, C, M);
+    const dim3 grid((unsigned)(nblk * ((C + cw - 1) / cw)));
+    if (vec == 2) launch_bwd<2, shift_bwd_ts(2)>(A, grid, B, T, C, M, st);
+    else launch_bwd<1, shift_bwd_ts(1)>(A, grid, B, T, C, M, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t mc = (int64_t)M * C;
-    hipLaunchKernelGGL(token_shift_mu_kernel, dim3((unsigned)((mc + 255) / 256)), dim3(256), 0, st, A, nblk, C, M);
+    hipLaunchKernelGGL(token_shift_mu_kernel, dim3((unsigned)(M * ((C + 63) / 64))), dim3(64 * kMuWaves), 0, st, A,
+                       nblk, C, M);
     return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ constexpr int kShiftMaxM = 4;  // mixes per call
 // vec: channels per lane (1, 2 or 4; 4 and 2 need C and the pointers to allow them).
 hipError_t run_token_shift(const TokenShiftArgs& A, int64_t B, int64_t T, int64_t C, int M, int vec,
                            hipStream_t st);
-size_t token_shift_backward_ws_bytes(int64_t B, int64_t T, int64_t C, int M);
+size_t token_shift_backward_ws_bytes(int64_t B, int64_t T, int64_t C, int M, int vec);
 hipError_t run_token_shift_backward(const TokenShiftBwdArgs& A, int64_t B, int64_t T, int64_t C, int M, int vec,
                                     hipStream_t st);
 
