@@ -62,6 +62,13 @@ def _bind(path: str):
     lib.oracle_token_shift.argtypes = [_I64, _I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_token_shift_backward.argtypes = [_I64, _I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P,
                                                 _F64P, _F64P, _F64P]
+    lib.oracle_scan_mingru.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
+    lib.oracle_scan_minlstm.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P, _F64P]
+    lib.oracle_scan_real_decay.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
+    lib.oracle_scan_complex_normalized.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
+    for name in ("oracle_scan_mingru", "oracle_scan_minlstm", "oracle_scan_real_decay",
+                 "oracle_scan_complex_normalized"):
+        getattr(lib, name).restype = None
     for name in ("oracle_wkv4_forward", "oracle_wkv4_backward", "oracle_scan_real",
                  "oracle_scan_complex", "oracle_scan_real_backward", "oracle_scan_complex_backward",
                  "oracle_token_shift", "oracle_token_shift_backward"):
@@ -267,3 +274,51 @@ def token_shift_backward(x, mu, g, x_prev=None, want_gx_prev=True, lib=None):
     (lib or _load()).oracle_token_shift_backward(B, T, C, M, _p32(x), None if xp is None else _p32(xp), _p32(mu),
                                                  _p32(g), _p64(gx), _p64(gmu), None if gxp is None else _p64(gxp))
     return gx, gmu, gxp
+
+
+def scan_mingru(kz, h, x0=None, lib=None) -> np.ndarray:
+    """x (B,T,C) float64 of minGRU: z = sigmoid(kz), x_t = (1 - z_t) x_{t-1} + z_t h_t."""
+    kz = _f32(kz)
+    B, T, C = kz.shape
+    h = _f32(h, (B, T, C))
+    x0a = None if x0 is None else _f32(x0, (B, C))
+    x = np.empty((B, T, C), dtype=np.float64)
+    (lib or _load()).oracle_scan_mingru(B, T, C, _p32(kz), _p32(h), None if x0a is None else _p32(x0a), _p64(x))
+    return x
+
+
+def scan_minlstm(kf, ki, h, x0=None, lib=None) -> np.ndarray:
+    """x (B,T,C) float64 of minLSTM: f, i = sigmoid(kf), sigmoid(ki), normalised to sum to 1."""
+    kf = _f32(kf)
+    B, T, C = kf.shape
+    ki = _f32(ki, (B, T, C))
+    h = _f32(h, (B, T, C))
+    x0a = None if x0 is None else _f32(x0, (B, C))
+    x = np.empty((B, T, C), dtype=np.float64)
+    (lib or _load()).oracle_scan_minlstm(B, T, C, _p32(kf), _p32(ki), _p32(h),
+                                         None if x0a is None else _p32(x0a), _p64(x))
+    return x
+
+
+def scan_real_decay(lam, u, x0=None, lib=None) -> np.ndarray:
+    """x (B,T,C) float64 of x_t = lam_c x_{t-1} + u_t (lam (C,))."""
+    u = _f32(u)
+    B, T, C = u.shape
+    lam = _f32(lam, (C,))
+    x0a = None if x0 is None else _f32(x0, (B, C))
+    x = np.empty((B, T, C), dtype=np.float64)
+    (lib or _load()).oracle_scan_real_decay(B, T, C, _p32(lam), _p32(u), None if x0a is None else _p32(x0a), _p64(x))
+    return x
+
+
+def scan_complex_normalized(lam, u, x0=None, lib=None) -> np.ndarray:
+    """x (B,T,C) complex128 of x_t = lam x_{t-1} + sqrt(1 - |lam|^2) u_t."""
+    u = np.ascontiguousarray(u, dtype=np.complex64)
+    B, T, C = u.shape
+    lamf = _c64f(lam, (C,))
+    uf = u.view(np.float32)
+    x0f = None if x0 is None else _c64f(x0, (B, C))
+    x = np.empty((B, T, C), dtype=np.complex128)
+    (lib or _load()).oracle_scan_complex_normalized(B, T, C, _p32(lamf), _p32(uf), None if x0f is None else _p32(x0f),
+                                                    x.view(np.float64).ctypes.data_as(_F64P))
+    return x

@@ -425,3 +425,101 @@ void oracle_token_shift_backward(int64_t B, int64_t T, int64_t C, int64_t M, con
         }
     free(part);
 }
+
+/*
+ * minGRU in scan form (minGRU page: the GRU reduced to v_t = a_t (.) v_{t-1} + b_t once the
+ * hidden-state dependence and the tanh are dropped; the page's equations are images, and
+ * the reading is h_t = (1 - z_t) h_{t-1} + z_t h~_t with z_t = sigmoid of the gate's
+ * pre-activation).  kz (B,T,C) pre-activations, h (B,T,C) candidates h~, x0 (B,C) or NULL
+ * (zero); x (B,T,C) double.
+ */
+void oracle_scan_mingru(int64_t B, int64_t T, int64_t C, const float *kz, const float *h, const float *x0,
+                        double *x)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        double s = x0 ? (double)x0[b * C + c] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t o = base + t * C;
+            const double z = 1.0 / (1.0 + exp(-(double)kz[o]));
+            s = (1.0 - z) * s + z * (double)h[o];
+            x[o] = s;
+        }
+    }
+}
+
+/*
+ * minLSTM in scan form (minGRU page, minLSTM section: the output gate and the cell are
+ * dropped and the two remaining gates are normalised to share the hidden state's input):
+ * f_t = sigmoid(kf_t), i_t = sigmoid(ki_t), f'_t = f_t / (f_t + i_t), i'_t = i_t / (f_t + i_t),
+ * h_t = f'_t h_{t-1} + i'_t h~_t.  Valid while sigmoid(kf) + sigmoid(ki) does not
+ * underflow double (logits above about -700).
+ */
+void oracle_scan_minlstm(int64_t B, int64_t T, int64_t C, const float *kf, const float *ki, const float *h,
+                         const float *x0, double *x)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        double s = x0 ? (double)x0[b * C + c] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t o = base + t * C;
+            const double f = 1.0 / (1.0 + exp(-(double)kf[o]));
+            const double i = 1.0 / (1.0 + exp(-(double)ki[o]));
+            s = (f / (f + i)) * s + (i / (f + i)) * (double)h[o];
+            x[o] = s;
+        }
+    }
+}
+
+/*
+ * Real scan with one decay per channel (an SLRU, the LRU write-up's section on RWKV: each of
+ * RWKV's two sums is such a recurrence): x_t = lambda_c x_{t-1} + u_t.  lambda (C), u
+ * (B,T,C), x0 (B,C) or NULL; x (B,T,C) double.
+ */
+void oracle_scan_real_decay(int64_t B, int64_t T, int64_t C, const float *lam, const float *u, const float *x0,
+                            double *x)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        const double L = (double)lam[c];
+        double s = x0 ? (double)x0[b * C + c] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t o = base + t * C;
+            s = L * s + (double)u[o];
+            x[o] = s;
+        }
+    }
+}
+
+/*
+ * The LRU's normalised input (LRU write-up, initialisation section: with |lambda| < 1 a
+ * stationary input of variance s feeds a state of variance s / (1 - |lambda|^2), so the
+ * input is scaled by gamma = sqrt(1 - |lambda|^2) to keep the state's scale):
+ * x_t = lambda x_{t-1} + gamma u_t, gamma per channel.  Arguments as oracle_scan_complex.
+ */
+void oracle_scan_complex_normalized(int64_t B, int64_t T, int64_t C, const float *lam, const float *u,
+                                    const float *x0, double *x)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        const double complex L = (double)lam[2 * c] + (double)lam[2 * c + 1] * I;
+        const double gamma = sqrt(1.0 - creal(L * conj(L)));
+        double complex s = 0.0;
+        if (x0) s = (double)x0[2 * (b * C + c)] + (double)x0[2 * (b * C + c) + 1] * I;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t o = base + t * C;
+            const double complex ut = (double)u[2 * o] + (double)u[2 * o + 1] * I;
+            s = L * s + gamma * ut;
+            x[2 * o] = creal(s);
+            x[2 * o + 1] = cimag(s);
+        }
+    }
+}

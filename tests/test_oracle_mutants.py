@@ -42,10 +42,11 @@ MUTANTS = [
     ("H_without_y", "H = q * Y[s] + eps * H;", "H = q + eps * H;"),
     ("real_scan_order", "s = (double)a[o] * s + (double)bb[o];",
      "s = (double)a[o] * (s + (double)bb[o]);"),
-    ("real_scan_x0_ignored", "double s = x0 ? (double)x0[b * C + c] : 0.0;", "double s = 0.0;"),
+    ("real_scan_x0_ignored", "double s = x0 ? (double)x0[b * C + c] : 0.0;\n        for (int64_t t = 0; t < T; ++t) {\n            const int64_t o = base + t * C;\n            s = (double)a[o] * s",
+     "double s = 0.0;\n        for (int64_t t = 0; t < T; ++t) {\n            const int64_t o = base + t * C;\n            s = (double)a[o] * s"),
     ("complex_conj_lambda", "s = L * s + ut;", "s = conj(L) * s + ut;"),
-    ("complex_x0_transposed", "if (x0) s = (double)x0[2 * (b * C + c)] + (double)x0[2 * (b * C + c) + 1] * I;",
-     "if (x0) s = (double)x0[2 * (b * C + c) + 1] + (double)x0[2 * (b * C + c)] * I;"),
+    ("complex_x0_transposed", "double complex s = 0.0;\n        if (x0) s = (double)x0[2 * (b * C + c)] + (double)x0[2 * (b * C + c) + 1] * I;\n        for (int64_t t = 0; t < T; ++t) {\n            const int64_t o = base + t * C;\n            const double complex ut = (double)u[2 * o] + (double)u[2 * o + 1] * I;\n            s = L * s + ut;",
+     "double complex s = 0.0;\n        if (x0) s = (double)x0[2 * (b * C + c) + 1] + (double)x0[2 * (b * C + c)] * I;\n        for (int64_t t = 0; t < T; ++t) {\n            const int64_t o = base + t * C;\n            const double complex ut = (double)u[2 * o] + (double)u[2 * o + 1] * I;\n            s = L * s + ut;"),
     ("real_bwd_coefficient_not_shifted", "const double anext = (t + 1 < T) ? (double)a[o + C] : 0.0;",
      "const double anext = (t + 1 < T) ? (double)a[o] : 0.0;"),
     ("real_bwd_ga_uses_current_x", "const double xprev = (t > 0) ? x[o - C] : (x0 ? (double)x0[b * C + c] : 0.0);",
@@ -68,6 +69,12 @@ MUTANTS = [
      "            double prev = 0.0;\n            for (int64_t t = 0; t < T; ++t) {\n                const double cur = (double)x[base + t * C];\n                out"),
     ("shift_bwd_next_term_dropped", "gx[o] += mm * gt + (1.0 - mm) * gnext;", "gx[o] += mm * gt;"),
     ("shift_bwd_gmu_sign", "acc += gt * (cur - prev);", "acc += gt * (prev - cur);"),
+    ("mingru_gate_swapped", "s = (1.0 - z) * s + z * (double)h[o];", "s = z * s + (1.0 - z) * (double)h[o];"),
+    ("minlstm_not_normalised", "s = (f / (f + i)) * s + (i / (f + i)) * (double)h[o];",
+     "s = f * s + i * (double)h[o];"),
+    ("decay_of_channel_zero", "const double L = (double)lam[c];", "const double L = (double)lam[0];"),
+    ("lru_gamma_without_sqrt", "const double gamma = sqrt(1.0 - creal(L * conj(L)));",
+     "const double gamma = 1.0 - creal(L * conj(L));"),
     ("shift_bwd_gx_prev_weight", "if (T > 0) gp += (1.0 - mm) * (double)gm[base];", "if (T > 0) gp += mm * (double)gm[base];"),
 ]
 
@@ -144,6 +151,25 @@ def _pins_pass(lib) -> bool:
     mu2[1, 2] += np.float32(0.25)
     diff = oracle.token_shift(ts["x"], mu2, ts["x_prev"], lib=lib) - oracle.token_shift(ts["x"], ts["mu"], ts["x_prev"], lib=lib)
     ok &= abs(float(np.sum(ts["g"] * diff)) - gmu[1, 2] * (float(mu2[1, 2]) - float(ts["mu"][1, 2]))) <= 1e-9
+
+    # Fused scan variants: gate limits and unrolled sums, minLSTM's equal-gate average, the
+    # per-channel decay's unrolled sums and the LRU normalisation's unrolled sums.
+    hv, xv0 = rng.standard_normal((2, 12, 3)).astype(np.float32), rng.standard_normal((2, 3)).astype(np.float32)
+    kz = (rng.standard_normal((2, 12, 3)) * 1.5).astype(np.float32)
+    z = 1.0 / (1.0 + np.exp(-kz.astype(np.float64)))
+    ok &= np.allclose(oracle.scan_mingru(kz, hv, xv0, lib=lib),
+                      brute.scan_real_sums(1.0 - z, z * hv, xv0), rtol=1e-12, atol=1e-13)
+    ok &= np.allclose(oracle.scan_minlstm(kz, kz, hv, xv0, lib=lib),
+                      brute.scan_real_sums(np.full(hv.shape, 0.5), 0.5 * hv.astype(np.float64), xv0),
+                      rtol=1e-12, atol=1e-13)
+    lam_r = rng.uniform(-1, 1, 3).astype(np.float32)
+    ok &= np.allclose(oracle.scan_real_decay(lam_r, hv, xv0, lib=lib),
+                      brute.scan_real_sums(np.broadcast_to(lam_r.astype(np.float64), hv.shape), hv, xv0),
+                      rtol=1e-12, atol=1e-13)
+    gam = np.sqrt(1.0 - np.abs(lr["lam"].astype(np.complex128)) ** 2)
+    ok &= np.allclose(oracle.scan_complex_normalized(lr["lam"], lr["u"], xc0, lib=lib),
+                      brute.scan_complex_sums(lr["lam"], gam * lr["u"].astype(np.complex128), xc0),
+                      rtol=1e-11, atol=1e-12)
     return bool(ok)
 
 
