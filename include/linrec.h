@@ -16,6 +16,9 @@
  *                                 Sequences", diagonal complex recurrence, eq. lr-xx)
  *   linrec_scan_real_backward,    the adjoints (backward passes) of the two scans
  *   linrec_scan_complex_backward
+ *   linrec_scan_mingru, _minlstm, gated variants of the real scan (minGRU, minLSTM, one decay
+ *   _real_decay                   per channel) and the LRU with normalised input
+ *   linrec_scan_complex_normalized
  *
  * Conventions shared by every entry point:
  *  - Pointers are DEVICE pointers (hipMalloc / torch CUDA-on-ROCm memory) unless a
@@ -80,6 +83,8 @@ const char *linrec_last_error(void);
  * host functions of (B, T, C); they make no HIP call.  Negative sizes return 0. */
 size_t wkv4_forward_workspace_size(int64_t B, int64_t T, int64_t C);
 size_t wkv4_backward_workspace_size(int64_t B, int64_t T, int64_t C);
+/* is_complex: 0 for linrec_scan_real and its gated variants, 1 for linrec_scan_complex and
+ * linrec_scan_complex_normalized. */
 size_t linrec_scan_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex);
 size_t linrec_scan_backward_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex);
 
@@ -229,6 +234,44 @@ int linrec_scan_real(int64_t B, int64_t T, int64_t C,
 int linrec_scan_complex(int64_t B, int64_t T, int64_t C,
                         const float *lambda, const float *u, const float *x0, float *x,
                         void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Gated variants of linrec_scan_real: the coefficients are formed from the gates inside the
+ * kernel, so a and b never travel through memory.  All take x0 (B,C) float32 or NULL (zero),
+ * write x (B,T,C) float32, and need linrec_scan_workspace_size(B, T, C, 0) bytes of
+ * workspace.  Inputs are float32 (B,T,C) unless marked (C).
+ *
+ * linrec_scan_mingru (minGRU page, minGRU section; its equations are images, read as)
+ *     z_t = sigmoid(kz_t),   x_t = (1 - z_t) x_{t-1} + z_t h_t      (h: the candidate h~)
+ * linrec_scan_minlstm (minGRU page, minLSTM section: the two gates are normalised)
+ *     f_t = sigmoid(kf_t), i_t = sigmoid(ki_t),
+ *     x_t = f_t / (f_t + i_t) x_{t-1} + i_t / (f_t + i_t) h_t
+ *     (evaluated through log-gate differences: finite for any finite kf, ki)
+ * linrec_scan_real_decay (one decay per channel: an SLRU, LRU write-up, section on RWKV)
+ *     x_t = lambda[c] x_{t-1} + u_t,   lambda (C)
+ */
+int linrec_scan_mingru(int64_t B, int64_t T, int64_t C, const float *kz, const float *h,
+                       const float *x0, float *x, void *workspace, size_t ws_bytes, void *stream);
+int linrec_scan_minlstm(int64_t B, int64_t T, int64_t C, const float *kf, const float *ki,
+                        const float *h, const float *x0, float *x, void *workspace,
+                        size_t ws_bytes, void *stream);
+int linrec_scan_real_decay(int64_t B, int64_t T, int64_t C, const float *lambda, const float *u,
+                           const float *x0, float *x, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/*
+ * The LRU with normalised input (LRU write-up, initialisation section: a stationary input
+ * of variance s feeds a state of variance s / (1 - |lambda|^2), so the input is scaled to
+ * keep the state's scale):
+ *
+ *   x_t = lambda x_{t-1} + gamma u_t,   gamma[c] = sqrt(1 - |lambda[c]|^2)
+ *
+ * Arguments, layout and workspace as linrec_scan_complex (|lambda| <= 1; gamma is taken
+ * as 0 where |lambda| rounds above 1).
+ */
+int linrec_scan_complex_normalized(int64_t B, int64_t T, int64_t C, const float *lambda,
+                                   const float *u, const float *x0, float *x, void *workspace,
+                                   size_t ws_bytes, void *stream);
 
 /*
  * Adjoint of linrec_scan_real (the pages give no backward; this is the chain rule of the

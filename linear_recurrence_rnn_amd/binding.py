@@ -62,6 +62,10 @@ def load(path: str | None = None):
         lib.wkv4_forward_ex.restype = ctypes.c_int
         lib.wkv4_forward_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 8 + [_VP, _SZ, _VP]
         lib.wkv4_backward.restype = ctypes.c_int
+        for name, n in (("linrec_scan_mingru", 4), ("linrec_scan_minlstm", 5), ("linrec_scan_real_decay", 4),
+                        ("linrec_scan_complex_normalized", 4)):
+            getattr(lib, name).restype = ctypes.c_int
+            getattr(lib, name).argtypes = [_I64, _I64, _I64] + [_VP] * n + [_VP, _SZ, _VP]
         lib.rwkv_token_shift.restype = ctypes.c_int
         lib.rwkv_token_shift.argtypes = [_I64, _I64, _I64, _I64] + [_VP] * 4 + [_VP]
         lib.rwkv_token_shift_backward_workspace_size.restype = _SZ
@@ -312,6 +316,57 @@ def scan_complex(lam, u, x0=None, out=None, workspace=None):
     ws, nws = _workspace(int(lib.linrec_scan_workspace_size(B, T, C, 1)), dev, workspace)
     _check(lib.linrec_scan_complex(B, T, C, _ptr(lam), _ptr(u), _ptr(x0), _ptr(x), _ptr(ws), nws,
                                    _stream(dev)), "linrec_scan_complex")
+    return x
+
+
+def _gated_real(name, tensors, chan, x0, out, workspace):
+    lib = load()
+    first = tensors[0][1]
+    B, T, C = first.shape
+    dev = first.device
+    for nm, t in tensors:
+        _expect(t, nm, torch.float32, (B, T, C), dev)
+    if chan is not None:
+        _expect(chan, "lam", torch.float32, (C,), dev)
+    if x0 is not None:
+        _expect(x0, "x0", torch.float32, (B, C), dev)
+    x = torch.empty_like(first) if out is None else out
+    _expect(x, "out", torch.float32, (B, T, C), dev)
+    ws, nws = _workspace(int(lib.linrec_scan_workspace_size(B, T, C, 0)), dev, workspace)
+    ptrs = ([_ptr(chan)] if chan is not None else []) + [_ptr(t) for _, t in tensors]
+    _check(getattr(lib, name)(B, T, C, *ptrs, _ptr(x0), _ptr(x), _ptr(ws), nws, _stream(dev)), name)
+    return x
+
+
+def scan_mingru(kz, h, x0=None, out=None, workspace=None):
+    """minGRU: z = sigmoid(kz), x_t = (1 - z_t) x_{t-1} + z_t h_t; (B,T,C) float32."""
+    return _gated_real("linrec_scan_mingru", [("kz", kz), ("h", h)], None, x0, out, workspace)
+
+
+def scan_minlstm(kf, ki, h, x0=None, out=None, workspace=None):
+    """minLSTM: f, i = sigmoid(kf), sigmoid(ki); x_t = (f x_{t-1} + i h_t) / (f + i)."""
+    return _gated_real("linrec_scan_minlstm", [("kf", kf), ("ki", ki), ("h", h)], None, x0, out, workspace)
+
+
+def scan_real_decay(lam, u, x0=None, out=None, workspace=None):
+    """x_t = lam_c x_{t-1} + u_t with one decay per channel, lam (C,) float32."""
+    return _gated_real("linrec_scan_real_decay", [("u", u)], lam, x0, out, workspace)
+
+
+def scan_complex_normalized(lam, u, x0=None, out=None, workspace=None):
+    """x_t = lam x_{t-1} + sqrt(1 - |lam|^2) u_t over (B,T,C) complex64; lam (C,)."""
+    lib = load()
+    B, T, C = u.shape
+    dev = u.device
+    _expect(u, "u", torch.complex64, (B, T, C), dev)
+    _expect(lam, "lam", torch.complex64, (C,), dev)
+    if x0 is not None:
+        _expect(x0, "x0", torch.complex64, (B, C), dev)
+    x = torch.empty_like(u) if out is None else out
+    _expect(x, "out", torch.complex64, (B, T, C), dev)
+    ws, nws = _workspace(int(lib.linrec_scan_workspace_size(B, T, C, 1)), dev, workspace)
+    _check(lib.linrec_scan_complex_normalized(B, T, C, _ptr(lam), _ptr(u), _ptr(x0), _ptr(x), _ptr(ws), nws,
+                                              _stream(dev)), "linrec_scan_complex_normalized")
     return x
 
 

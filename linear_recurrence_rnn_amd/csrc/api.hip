@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <atomic>
+#include <initializer_list>
 #include <random>
 #include <string>
 
@@ -71,7 +72,8 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
     if (kind == linrec::kKindWkv) {
         p.nw = 8;
         p.L = 16;
-    } else if (kind == linrec::kKindReal) {
+    } else if (kind == linrec::kKindReal || kind == linrec::kKindMinGru || kind == linrec::kKindMinLstm ||
+               kind == linrec::kKindRealDecay) {
         p.nw = 8;
         p.L = 16;
     } else if (kind == linrec::kKindRealBwd) {
@@ -87,7 +89,8 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
     // Coordination: in wave 0 by default; in a wave of its own for the complex scans, whose
     // chunks hold many registers and whose long chains lean on the inclusive prefixes
     // (LINREC_COORD: 1 wave 0, 2 own wave).
-    p.sep = vec == 1 && (kind == linrec::kKindComplex || kind == linrec::kKindComplexBwd);
+    p.sep = vec == 1 && (kind == linrec::kKindComplex || kind == linrec::kKindComplexBwd ||
+                         kind == linrec::kKindComplexNorm);
     const int64_t coord = env_int("LINREC_COORD", 0);
     if (coord == 1 || coord == 2) p.sep = vec == 1 && coord == 2;
     const int nw = (int)env_int("LINREC_NW", 0), L = (int)env_int("LINREC_L", 0);
@@ -108,7 +111,7 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
 
 int vmax_of(int kind) {
     if (kind == linrec::kKindRealBwd || kind == linrec::kKindComplexBwd) return 1;
-    return kind == linrec::kKindComplex ? 2 : 4;
+    return (kind == linrec::kKindWkv || kind == linrec::kKindReal) ? 4 : 2;
 }
 
 // Channels per lane: the widest the alignment allows, narrowed by the default policy or by
@@ -123,10 +126,10 @@ int pick_vec(int kind, int vec_aligned, int64_t elems = 0, bool plain = false) {
         vec = f < vec ? (int)f : vec;
     } else if (kind == linrec::kKindWkv) {
         vec = (plain && elems >= ((int64_t)1 << 25) && vec >= 2) ? 2 : 1;
-    } else if (kind == linrec::kKindComplex) {
+    } else if (kind == linrec::kKindComplex || kind == linrec::kKindComplexNorm) {
         vec = 1;
-    } else if (kind == linrec::kKindReal) {
-        vec = vec < 2 ? vec : 2;
+    } else {
+        vec = vec < 2 ? vec : 2;  // the real scan and its gated variants
     }
     return vec;
 }
@@ -398,6 +401,80 @@ LINREC_API int linrec_scan_complex(int64_t B, int64_t T, int64_t C, const float*
     return hip_status(linrec::run_scan_complex(A, geom_of(linrec::kKindComplex, p, B, T, C, workspace), p,
                                                (hipStream_t)stream),
                       "linrec_scan_complex launch");
+}
+
+namespace {
+
+// Shared checks and launch of the gated real-scan variants: `tensors` are the (B,T,C)
+// inputs, `chan` an optional (C) input; vec from the alignment of all of them and of x.
+template <class Args, class Run>
+int gated_real_scan(const char* name, int kind, int64_t B, int64_t T, int64_t C, std::initializer_list<const float*> tensors,
+                    const float* chan, const float* x0, float* x, void* workspace, size_t ws_bytes, void* stream,
+                    const Args& A, Run&& run) {
+    int st = check_shape(B, T, C, 4);
+    if (st) return st;
+    if (B == 0 || T == 0 || C == 0) return ok();
+    bool a16 = aligned(x, 16), a8 = aligned(x, 8);
+    if (!x) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    for (const float* p : tensors) {
+        if (!p) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+        a16 = a16 && aligned(p, 16);
+        a8 = a8 && aligned(p, 8);
+    }
+    const void* ptrs[] = {chan, x0, x};
+    for (const void* p : ptrs)
+        if (p && !aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    for (const float* p : tensors)
+        if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    const int vec = pick_vec(kind, (C % 4 == 0 && a16) ? 4 : ((C % 2 == 0 && a8) ? 2 : 1));
+    const linrec::ScanPlan p = scan_plan(kind, vec, B, T, C);
+    if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
+    return hip_status(run(A, geom_of(kind, p, B, T, C, workspace), p, (hipStream_t)stream), name);
+}
+
+}  // namespace
+
+LINREC_API int linrec_scan_mingru(int64_t B, int64_t T, int64_t C, const float* kz, const float* h,
+                                  const float* x0, float* x, void* workspace, size_t ws_bytes, void* stream) {
+    const linrec::MinGruArgs A{kz, h, x0, x};
+    return gated_real_scan("linrec_scan_mingru launch", linrec::kKindMinGru, B, T, C, {kz, h}, nullptr, x0, x,
+                           workspace, ws_bytes, stream, A, linrec::run_scan_mingru);
+}
+
+LINREC_API int linrec_scan_minlstm(int64_t B, int64_t T, int64_t C, const float* kf, const float* ki,
+                                   const float* h, const float* x0, float* x, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+    const linrec::MinLstmArgs A{kf, ki, h, x0, x};
+    return gated_real_scan("linrec_scan_minlstm launch", linrec::kKindMinLstm, B, T, C, {kf, ki, h}, nullptr, x0, x,
+                           workspace, ws_bytes, stream, A, linrec::run_scan_minlstm);
+}
+
+LINREC_API int linrec_scan_real_decay(int64_t B, int64_t T, int64_t C, const float* lambda, const float* u,
+                                      const float* x0, float* x, void* workspace, size_t ws_bytes, void* stream) {
+    if (B > 0 && T > 0 && C > 0 && !lambda) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const linrec::RealDecayArgs A{lambda, u, x0, x};
+    return gated_real_scan("linrec_scan_real_decay launch", linrec::kKindRealDecay, B, T, C, {u}, lambda, x0, x,
+                           workspace, ws_bytes, stream, A, linrec::run_scan_real_decay);
+}
+
+LINREC_API int linrec_scan_complex_normalized(int64_t B, int64_t T, int64_t C, const float* lambda,
+                                              const float* u, const float* x0, float* x, void* workspace,
+                                              size_t ws_bytes, void* stream) {
+    int st = check_shape(B, T, C, 8);
+    if (st) return st;
+    if (B == 0 || T == 0 || C == 0) return ok();
+    if (!lambda || !u || !x) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void* ptrs[] = {lambda, u, x};
+    for (const void* p : ptrs)
+        if (!aligned(p, 8)) return fail(LINREC_ERR_UNSUPPORTED, "complex64 pointer not 8-byte aligned");
+    if (x0 && !aligned(x0, 8)) return fail(LINREC_ERR_UNSUPPORTED, "x0 not 8-byte aligned");
+    const int vec = pick_vec(linrec::kKindComplexNorm, (C % 2 == 0 && aligned(u, 16) && aligned(x, 16)) ? 2 : 1);
+    const linrec::ScanPlan p = scan_plan(linrec::kKindComplexNorm, vec, B, T, C);
+    if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
+    const linrec::CplxArgs A{lambda, u, x0, x};
+    return hip_status(linrec::run_scan_complex_normalized(A, geom_of(linrec::kKindComplexNorm, p, B, T, C, workspace),
+                                                          p, (hipStream_t)stream),
+                      "linrec_scan_complex_normalized launch");
 }
 
 LINREC_API int linrec_scan_real_backward(int64_t B, int64_t T, int64_t C, const float* a, const float* x0,

@@ -1,261 +1,14 @@
-// chunk_scan.hip -- single-pass, time-parallel evaluation of a first-order recurrence on gfx950.
-//
-// Layout.  A channel group is 64 lanes x VEC channels (1 KB of float32 per time step for
-// VEC = 4), so every wave-wide load or store touches one contiguous row segment.  A
-// workgroup owns one slab of NW*L time steps of one group: wave w (of NW) holds chunk w,
-// steps [w*L, (w+1)*L) of the slab, in registers.
-// Every input element is read from HBM once and every output written once.
-//
-//   compute   each wave reduces its chunk to an aggregate (from the identity state);
-//   carry     wave 0, its chunk parked in LDS, coordinates: it folds the chunk aggregates
-//             into the slab aggregate, publishes it, looks back over the earlier slabs of
-//             the same group (decoupled look-back, 64 slabs per round trip, one per lane) for
-//             the nearest published inclusive prefix and folds the aggregates after it in
-//             time order (the association a chained scan would use: results do not depend on
-//             timing), and publishes the slab's own inclusive prefix;
-//   re-run    each wave combines the slab's carry with the chunks before its own (prepared
-//             by the coordinator) and re-runs its chunk straight from registers.
-// The waves meet at two barriers only.  Parking wave 0's chunk keeps the look-back's
-// registers from adding to the chunk's, and having no wave without a chunk lets 3
-// workgroups of 8 waves share a CU (the CU holds about 24 of these waves).  The combine of
-// two spans is associative, which is what lets a sequence be cut into chunks and slabs (the
-// two-halves split of the LRU write-up, parallelisation section).
-//
-// Progress: workgroups are numbered slab-major, so a slab's predecessors have smaller block
-// indices and are dispatched first.  A wait is bounded all the same: if a predecessor has
-// not published after g.spin polls, the waiting wave recomputes that slab's aggregate from
-// its inputs.  No wait depends on dispatch order or on the workspace contents; flags carry
-// a per-call tag, so stale flags from earlier calls read as "not published".
-#include <type_traits>
-
-#include "chunk_scan.hpp"
-#include "lookback.hpp"
-#include "scan_ops.hpp"
+// chunk_scan.hip -- the scan kernel (scan_kernel.hpp) instantiated for the WKV-4 forward,
+// the real and complex scans and their adjoints, and the small helper kernels of those
+// entry points (fills, copies, the two-stage glambda sum of the complex adjoint).
+#include "scan_kernel.hpp"
 
 namespace linrec {
 
 namespace {
 
-// Waves per SIMD the register budget is set for.  When a compute wave holds at most 32
-// floats of chunk data, 7 waves (<= 72 VGPRs) fit without spilling and let three 9-wave
-// workgroups share a CU, so one workgroup's look-back hides behind the others' streaming.
-// Other shapes (wider chunks, or several channels per lane of WKV or complex pairs, whose
-// per-channel state is larger) spill at that budget and keep the compiler's choice.
-template <class Op, int VEC, int L>
-constexpr int scan_waves_per_eu() {
-    return (!Op::kReverse && VEC * L <= 16 && (VEC == 1 || std::is_same<Op, RealOp>::value)) ? 7 : 1;
-}
-
-// Addressing of a run of n consecutive logical steps starting at logical step tl of a
-// sequence of T: its lowest row (the buffer base) and the Rows of its steps.  Operators in
-// reverse time visit the sequence from its last step.
-template <bool REV>
-__device__ __forceinline__ void run_rows(int64_t T, int64_t tl, int n, unsigned rowb, int64_t& row, Rows& rows) {
-    if constexpr (REV) {
-        row = n > 0 ? T - tl - n : 0;
-        rows = {(unsigned)(n > 0 ? n - 1 : 0) * rowb, -(int)rowb, T - 1 - tl, -1};
-    } else {
-        row = tl;
-        rows = {0u, (int)rowb, tl, 1};
-    }
-}
-
-// SEP selects where the coordination runs: false, in wave 0, whose chunk is parked in LDS
-// meanwhile (NW waves per workgroup); true, in a wave of its own (NW + 1 waves), which
-// publishes the inclusive prefix while the chunks re-run.  The first packs more chunks onto
-// a CU (it holds about 24 such waves); the second keeps the publication off the chunks'
-// path, which pays for long look-back chains of register-heavy operators.
-template <class Op, int VEC, int NW, int L, bool SEP>
-__global__ __launch_bounds__(64 * (NW + SEP)) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<Op, VEC, L>())))
-void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
-    using Agg = typename Op::Agg;
-    using In = typename Op::In;
-    using Chan = typename Op::Chan;
-    using Local = typename Op::Local;
-    constexpr int CW = 64 * VEC;
-    constexpr int SLAB = NW * L;
-    constexpr int EF = Op::kFloats;
-    constexpr int PL = SEP ? 1 : L;  // parked steps
-    using Part = typename Op::Part;
-    __shared__ Agg sh[NW][CW];    // chunk aggregates, then sh[x] = chunks 0 .. x-1 combined
-    __shared__ Agg sh_carry[CW];  // the carry into the slab
-    __shared__ In sh_park[PL][CW];  // wave 0's chunk while it coordinates
-    __shared__ Local sh_park_loc[CW];
-    __shared__ Part sh_part[Op::kParts ? NW : 1][Op::kParts ? CW : 1];  // chunks' shares of per-slab sums
-
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int64_t G = g.B * g.ngrp;
-    const int64_t s = (int64_t)blockIdx.x / G;  // slab in the recurrence's order: predecessors come first
-    const int64_t gi = (int64_t)blockIdx.x - s * G;
-    const int64_t b = gi / g.ngrp, grp = gi - b * g.ngrp;
-    const int64_t c0 = grp * CW + (int64_t)lane * VEC;
-    const bool active = c0 < g.C;  // C is a multiple of VEC
-    const int64_t t_slab = s * SLAB;
-    const int slab_n = (int)((g.T - t_slab) < SLAB ? (g.T - t_slab) : SLAB);
-    auto chunk_len = [&](int x) { return max(0, min(L, slab_n - x * L)); };
-
-    Chan ch[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) ch[e] = active ? Op::template chan<L>(A, c0 + e) : Chan{};
-
-    const unsigned rowb = (unsigned)(g.C * EF * 4);           // bytes per time step
-    const unsigned voff = (unsigned)(lane * VEC * EF * 4);    // this lane's bytes in the row
-    const Chain<Agg> chn{g.flags + gi * g.nslab,
-                         reinterpret_cast<uint32_t*>(g.rec_agg) + gi * g.nslab * (CW * kDwords<Agg>),
-                         reinterpret_cast<uint32_t*>(g.rec_incl) + gi * g.nslab * (CW * kDwords<Agg>), g.tag, g.spin};
-    const bool has_succ = s + 1 < g.nslab;
-
-    // Coordination, by one whole wave after B1: the slab aggregate (published), the carry
-    // into the slab (look-back; into sh_carry), sh[x] = the chunks before x combined (x >= 1).
-    // Returns the inclusive prefix, carry followed by the slab.
-    auto coordinate = [&](uint64_t first, Agg (&incl)[VEC]) {
-        Agg mine[VEC], carry[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            mine[e] = sh[0][lane * VEC + e];
-            for (int x = 1; x < NW; ++x) {
-                const Agg chunk = sh[x][lane * VEC + e];
-                sh[x][lane * VEC + e] = mine[e];
-                mine[e] = Op::combine(ch[e], mine[e], chunk, chunk_len(x));
-            }
-            carry[e] = active ? Op::init(A, g, b, c0 + e) : Op::identity();
-        }
-        if (has_succ) publish<VEC>(chn, s, lane, mine, false);
-        auto fold = [&](Agg (&c)[VEC], const Agg (&x)[VEC], int64_t) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) c[e] = Op::combine(ch[e], c[e], x[e], SLAB);
-        };
-        // A slab whose aggregate was not published in time is recomputed from its inputs.
-        auto recompute = [&](int64_t jj, Agg (&x)[VEC]) {
-            int64_t rowj;
-            Rows rj;
-            run_rows<Op::kReverse>(g.T, jj * SLAB, SLAB, rowb, rowj, rj);  // predecessors are full slabs
-            const typename Op::Res Rj = Op::res(A, g, b, rowj, grp * CW);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) x[e] = Op::identity();
-            if (active) {
-                for (int t = 0; t < SLAB; ++t) {
-                    In xi[VEC];
-                    Op::template load<VEC>(Rj, voff, rj, t, xi);
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) x[e] = Op::step(ch[e], x[e], xi[e]);
-                }
-            }
-        };
-        constexpr int KB = VEC >= 4 ? 2 : (VEC == 2 ? 4 : 8);
-        look_back<VEC, KB>(chn, s, lane, carry, fold, recompute, first);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            sh_carry[lane * VEC + e] = carry[e];
-            incl[e] = Op::combine(ch[e], carry[e], mine[e], slab_n);
-        }
-    };
-    // Hands the inclusive prefix on: published for the next slab, or, in the last slab, the
-    // state after the whole sequence for operators that return it.
-    auto hand_on = [&](const Agg (&incl)[VEC]) {
-        if (has_succ) {
-            publish<VEC>(chn, s, lane, incl, true);
-        } else if (active) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) Op::finish(A, g, b, c0 + e, incl[e]);
-        }
-    };
-    // The slab's per-slab sum (operators that keep one): the chunks' shares added in order.
-    auto slab_sum = [&]() {
-        if constexpr (Op::kParts) {
-            double re = 0.0, im = 0.0;
-            for (int x = 0; x < NW; ++x) {
-                re += sh_part[x][lane].re;
-                im += sh_part[x][lane].im;
-            }
-            double* out = g.part + 2 * ((gi * g.nslab + s) * CW + lane);
-            out[0] = re;
-            out[1] = im;
-        }
-    };
-
-    if constexpr (SEP) {
-        if (w == NW) {
-            // ---- the coordinator wave ----
-            __syncthreads();  // B1: chunk aggregates are in sh
-            Agg incl[VEC];
-            coordinate(prefetch_window(chn, s, lane), incl);
-            __syncthreads();  // B2: the chunks re-run while the inclusive prefix is published
-            hand_on(incl);
-            if constexpr (Op::kParts) {
-                __syncthreads();  // B3: the chunks' shares are in sh_part
-                slab_sum();
-            }
-            return;
-        }
-    }
-
-    // ---- compute waves: chunk w of the slab, loaded into registers and reduced ----
-    const int nu = chunk_len(w);  // steps of the chunk (wave-uniform)
-    const int n = active ? nu : 0;
-    int64_t row;
-    Rows rows;
-    run_rows<Op::kReverse>(g.T, t_slab + (int64_t)w * L, nu, rowb, row, rows);
-    const typename Op::Res R = Op::res(A, g, b, row, grp * CW);
-    In in[L][VEC];
-    if (n == L) {
-#pragma unroll
-        for (int j = 0; j < L; ++j) Op::template load<VEC>(R, voff, rows, j, in[j]);
-    } else {
-#pragma unroll
-        for (int j = 0; j < L; ++j) {
-            if (j < n) Op::template load<VEC>(R, voff, rows, j, in[j]);
-            else Op::template zero<VEC>(in[j]);
-        }
-    }
-    Local loc[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) sh[w][lane * VEC + e] = Op::template reduce<L, VEC>(ch[e], in, e, n, loc[e]);
-    if (SEP || w != 0) {
-        __syncthreads();  // B1: chunk aggregates are in sh
-        __syncthreads();  // B2: the slab's carry is in sh_carry, every chunk's prefix in sh[w]
-    } else {
-        // Wave 0 coordinates.  Its chunk waits in LDS meanwhile, and the whole role sits in
-        // this one branch, so that the look-back's registers do not add to the chunk's.
-#pragma unroll
-        for (int j = 0; j < PL; ++j)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) sh_park[j][lane * VEC + e] = in[j][e];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) sh_park_loc[lane * VEC + e] = loc[e];
-        const uint64_t first = prefetch_window(chn, s, lane);  // overlaps the wait at B1
-        __syncthreads();  // B1
-        Agg incl[VEC];
-        coordinate(first, incl);
-        hand_on(incl);
-        __syncthreads();  // B2
-#pragma unroll
-        for (int j = 0; j < PL; ++j)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) in[j][e] = sh_park[j][lane * VEC + e];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) loc[e] = sh_park_loc[lane * VEC + e];
-    }
-
-    // ---- re-run the chunk from its carry ----
-    Part part{};
-    if (n > 0) {
-        Agg cin[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            cin[e] = (w == 0) ? sh_carry[lane * VEC + e]
-                              : Op::combine(ch[e], sh_carry[lane * VEC + e], sh[w][lane * VEC + e], w * L);
-        part = Op::template run<L, VEC>(R, ch, cin, in, loc, n, voff, rows);
-    }
-    if constexpr (Op::kParts) {
-        static_assert(VEC == 1, "per-slab sums are kept for one channel per lane");
-        sh_part[w][lane] = part;
-        __syncthreads();  // B3: the chunks' shares are in sh_part
-        if (!SEP && w == 0) slab_sum();
-    }
-}
+using scan_kernel::dispatch;
+using scan_kernel::dispatch_shape;
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
@@ -295,51 +48,10 @@ __global__ __launch_bounds__(256) void part_final_kernel(ScanGeom g, int64_t nk,
     glam[2 * c + 1] = (float)im;
 }
 
-template <class Op, int VEC, int NW, int L>
-hipError_t launch(const typename Op::Args& A, const ScanGeom& g, bool sep, hipStream_t st) {
-    const int64_t nb = g.B * g.ngrp * g.nslab;
-    if constexpr (VEC == 1) {
-        if (sep) {
-            hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, true>), dim3((unsigned)nb), dim3(64 * (NW + 1)),
-                               0, st, A, g);
-            return hipGetLastError();
-        }
-    }
-    hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, false>), dim3((unsigned)nb), dim3(64 * NW), 0, st, A, g);
-    return hipGetLastError();
-}
-
-// Kernels that exist: vec in {VMAX, 2, 1} x (nw, L) in {(4, 16), (8, 8), (8, 16)}, and for
-// the linear scans (8, 32) with one channel per lane (the registers of two channels x 16
-// steps, with slabs twice as long: shorter look-back chains); each with the coordination in
-// wave 0, and for one channel per lane also with a coordinator wave.  WKV keeps chunks of at
-// most 16 steps: its per-chunk frame spans (L-1) om in exponent, which 32 steps of a fast
-// decay push to the edge of float32 range.
-template <class Op, int VEC>
-hipError_t dispatch_shape(const typename Op::Args& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st) {
-    if (p.nw == 4 && p.L == 16) return launch<Op, VEC, 4, 16>(A, g, p.sep, st);
-    if (p.nw == 8 && p.L == 8) return launch<Op, VEC, 8, 8>(A, g, p.sep, st);
-    if (p.nw == 8 && p.L == 16) return launch<Op, VEC, 8, 16>(A, g, p.sep, st);
-    if constexpr (VEC == 1 && !std::is_same<Op, WkvOp>::value && !std::is_same<Op, WkvExtOp>::value) {
-        if (p.nw == 8 && p.L == 32) return launch<Op, VEC, 8, 32>(A, g, p.sep, st);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <class Op, int VMAX>
-hipError_t dispatch(const typename Op::Args& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st) {
-    if (p.vec == VMAX) return dispatch_shape<Op, VMAX>(A, g, p, st);
-    if constexpr (VMAX > 2) {
-        if (p.vec == 2) return dispatch_shape<Op, 2>(A, g, p, st);
-    }
-    if (p.vec == 1) return dispatch_shape<Op, 1>(A, g, p, st);
-    return hipErrorInvalidValue;
-}
-
 }  // namespace
 
 bool scan_shape_supported(int kind, int vec, int nw, int L) {
-    const int vmax = kind == kKindComplex ? 2 : ((kind == kKindRealBwd || kind == kKindComplexBwd) ? 1 : 4);
+    const int vmax = (kind == kKindRealBwd || kind == kKindComplexBwd) ? 1 : ((kind == kKindWkv || kind == kKindReal) ? 4 : 2);
     const bool vec_ok = vec == vmax || (vec == 2 && vmax >= 2) || vec == 1;
     return vec_ok && ((nw == 4 && L == 16) || (nw == 8 && L == 8) || (nw == 8 && L == 16) ||
                       (kind != kKindWkv && vec == 1 && nw == 8 && L == 32));
@@ -396,7 +108,10 @@ size_t agg_bytes(int kind) {
     switch (kind) {
         case kKindWkv: return sizeof(WkvOp::Agg);
         case kKindReal:
-        case kKindRealBwd: return sizeof(RealOp::Agg);
+        case kKindRealBwd:
+        case kKindMinGru:
+        case kKindMinLstm: return sizeof(RealOp::Agg);
+        case kKindRealDecay: return sizeof(RealDecayOp::Agg);
         default: return sizeof(CplxOp::Agg);
     }
 }

@@ -7,7 +7,8 @@
 
 namespace linrec {
 
-enum { kKindWkv = 0, kKindReal = 1, kKindComplex = 2, kKindRealBwd = 3, kKindComplexBwd = 4 };
+enum { kKindWkv = 0, kKindReal = 1, kKindComplex = 2, kKindRealBwd = 3, kKindComplexBwd = 4,
+       kKindMinGru = 5, kKindMinLstm = 6, kKindRealDecay = 7, kKindComplexNorm = 8 };
 
 // Operands of each recurrence (device pointers, (B,T,C) row-major, C fastest).
 struct WkvArgs {
@@ -32,6 +33,26 @@ struct CplxArgs {
     const float* u;    // (B,T,C) complex64
     const float* x0;   // (B,C) complex64 or null
     float* x;          // (B,T,C) complex64
+};
+// Gated variants of the real scan (coefficients formed from the gates in the kernel).
+struct MinGruArgs {
+    const float* kz;  // (B,T,C) gate pre-activation: z = sigmoid(kz)
+    const float* h;   // (B,T,C) candidate h~
+    const float* x0;  // (B,C) or null
+    float* x;         // (B,T,C)
+};
+struct MinLstmArgs {
+    const float* kf;  // (B,T,C) forget-gate pre-activation
+    const float* ki;  // (B,T,C) input-gate pre-activation
+    const float* h;   // (B,T,C) candidate h~
+    const float* x0;  // (B,C) or null
+    float* x;         // (B,T,C)
+};
+struct RealDecayArgs {
+    const float* lam;  // (C) decay per channel
+    const float* u;    // (B,T,C)
+    const float* x0;   // (B,C) or null
+    float* x;          // (B,T,C)
 };
 // Adjoints of the two linear scans (reverse time).
 struct RealBwdArgs {
@@ -93,6 +114,10 @@ struct ScanPlan {
 hipError_t run_wkv_forward(const WkvArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
 hipError_t run_scan_real(const RealArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
 hipError_t run_scan_complex(const CplxArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
+hipError_t run_scan_mingru(const MinGruArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
+hipError_t run_scan_minlstm(const MinLstmArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
+hipError_t run_scan_real_decay(const RealDecayArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
+hipError_t run_scan_complex_normalized(const CplxArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
 hipError_t run_scan_real_backward(const RealBwdArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
 // Also sums g.part into glam (C complex64): g.part2 holds ceil(nslab / kPartBlock) x C pairs.
 hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const ScanGeom& g, const ScanPlan& p,

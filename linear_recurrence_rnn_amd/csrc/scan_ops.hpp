@@ -314,8 +314,9 @@ struct RealOp {
         return {s.m * x.a, fmaf(x.a, s.x, x.b)};
     }
 
-    template <int L, int VEC>
-    __device__ __forceinline__ static Part run(const Res& R, const Chan (&)[VEC], const Agg (&cin)[VEC],
+    // RS: any buffer set with the output x (the gated variants below bring their own).
+    template <int L, int VEC, class RS>
+    __device__ __forceinline__ static Part run(const RS& R, const Chan (&)[VEC], const Agg (&cin)[VEC],
                                const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
                                const Rows& rows) {
         float x[VEC];
@@ -639,6 +640,182 @@ struct CplxBwdOp : CplxOp {
             }
         }
         return {(double)ar, (double)ai};
+    }
+};
+
+// ----------------------------------------------------------------------------------
+// Gated variants of the real scan: the coefficients a_t, b_t are formed from the gates as
+// each step is loaded, so they never travel through memory (minGRU page, minGRU and minLSTM
+// sections; LRU write-up, section on RWKV, for the per-channel decay).
+// ----------------------------------------------------------------------------------
+__device__ __forceinline__ float sigmoidf(float k) { return __builtin_amdgcn_rcpf(1.f + fast_exp2(-k * kLog2e)); }
+// log(1 + e^y) without overflow: max(y, 0) + log(1 + e^{-|y|}).
+__device__ __forceinline__ float softplusf(float y) {
+    constexpr float kLn2 = 0.6931471805599453f;
+    return fmaxf(y, 0.f) + __builtin_amdgcn_logf(1.f + fast_exp2(-fabsf(y) * kLog2e)) * kLn2;
+}
+
+// minGRU: z = sigmoid(kz), h_t = (1 - z) h_{t-1} + z h~_t.  1 - z is taken as sigmoid(-kz),
+// which keeps its relative precision when z is close to 1.
+struct MinGruOp : RealOp {
+    using Args = MinGruArgs;
+    template <int L>
+    __device__ __forceinline__ static Chan chan(const Args&, int64_t) { return {}; }
+    __device__ __forceinline__ static Agg init(const Args& A, const ScanGeom& g, int64_t b, int64_t c) {
+        return {1.f, A.x0 ? A.x0[b * g.C + c] : 0.f};
+    }
+    struct Res { rsrc_t kz, h, x; };
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t base = (b * g.T + row) * g.C + col0, nbytes = (g.B * g.T * g.C - base) * 4;
+        return {make_rsrc(A.kz + base, nbytes), make_rsrc(A.h + base, nbytes), make_rsrc(A.x + base, nbytes)};
+    }
+    template <int VEC>
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const FV<VEC> k = ldb<VEC>(R.kz, voff, rows.soff(j));
+        const FV<VEC> h = ldb<VEC>(R.h, voff, rows.soff(j));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {sigmoidf(-k.v[e]), sigmoidf(k.v[e]) * h.v[e]};
+    }
+};
+
+// minLSTM: f = sigmoid(kf), i = sigmoid(ki), h_t = f/(f+i) h_{t-1} + i/(f+i) h~_t.  The
+// normalised gates are sigmoid(+-d) with d = log f - log i = softplus(-ki) - softplus(-kf),
+// which stay finite however small f and i are.
+struct MinLstmOp : RealOp {
+    using Args = MinLstmArgs;
+    template <int L>
+    __device__ __forceinline__ static Chan chan(const Args&, int64_t) { return {}; }
+    __device__ __forceinline__ static Agg init(const Args& A, const ScanGeom& g, int64_t b, int64_t c) {
+        return {1.f, A.x0 ? A.x0[b * g.C + c] : 0.f};
+    }
+    struct Res { rsrc_t kf, ki, h, x; };
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t base = (b * g.T + row) * g.C + col0, nbytes = (g.B * g.T * g.C - base) * 4;
+        return {make_rsrc(A.kf + base, nbytes), make_rsrc(A.ki + base, nbytes), make_rsrc(A.h + base, nbytes),
+                make_rsrc(A.x + base, nbytes)};
+    }
+    template <int VEC>
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const FV<VEC> kf = ldb<VEC>(R.kf, voff, rows.soff(j));
+        const FV<VEC> ki = ldb<VEC>(R.ki, voff, rows.soff(j));
+        const FV<VEC> h = ldb<VEC>(R.h, voff, rows.soff(j));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float d = softplusf(-ki.v[e]) - softplusf(-kf.v[e]);
+            in[e] = {sigmoidf(d), sigmoidf(-d) * h.v[e]};
+        }
+    }
+};
+
+// One decay per channel: x_t = lam_c x_{t-1} + u_t (an SLRU).  The decay lives in the
+// channel constants, so only u is streamed.
+struct RealDecayOp {
+    using Args = RealDecayArgs;
+    static constexpr bool kReverse = false;
+    static constexpr bool kParts = false;
+    using Part = NoPart;
+    template <class AnyArgs, class AnyAgg>
+    __device__ __forceinline__ static void finish(const AnyArgs&, const ScanGeom&, int64_t, int64_t, const AnyAgg&) {}
+    struct Chan { float lam; };
+    struct In { float u; };
+    struct Local {};
+    struct Agg { float m, x; };
+
+    template <int L>
+    __device__ __forceinline__ static Chan chan(const Args& A, int64_t c) { return {A.lam[c]}; }
+    __device__ __forceinline__ static Agg identity() { return {1.f, 0.f}; }
+    __device__ __forceinline__ static Agg init(const Args& A, const ScanGeom& g, int64_t b, int64_t c) {
+        return {1.f, A.x0 ? A.x0[b * g.C + c] : 0.f};
+    }
+    static constexpr int kFloats = 1;
+    struct Res { rsrc_t u, x; };
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t base = (b * g.T + row) * g.C + col0, nbytes = (g.B * g.T * g.C - base) * 4;
+        return {make_rsrc(A.u + base, nbytes), make_rsrc(A.x + base, nbytes)};
+    }
+    template <int VEC>
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const FV<VEC> u = ldb<VEC>(R.u, voff, rows.soff(j));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {u.v[e]};
+    }
+    template <int VEC>
+    __device__ __forceinline__ static void zero(In (&in)[VEC]) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {0.f};
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Agg reduce(const Chan& ch, In (&in)[L][VEC], int e, int n, Local&) {
+        float m = 1.f, x = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                x = fmaf(ch.lam, x, in[j][e].u);
+                m *= ch.lam;
+            }
+        }
+        return {m, x};
+    }
+    __device__ __forceinline__ static Agg combine(const Chan&, const Agg& s1, const Agg& s2, int64_t) {
+        return {s1.m * s2.m, fmaf(s2.m, s1.x, s2.x)};
+    }
+    __device__ __forceinline__ static Agg step(const Chan& ch, const Agg& s, const In& x) {
+        return {s.m * ch.lam, fmaf(ch.lam, s.x, x.u)};
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                                               const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
+                                               const Rows& rows) {
+        float x[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[e] = cin[e].x;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                FV<VEC> o;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    x[e] = fmaf(ch[e].lam, x[e], in[j][e].u);
+                    o.v[e] = x[e];
+                }
+                stb<VEC>(R.x, voff, rows.soff(j), o);
+            }
+        }
+        return {};
+    }
+};
+
+// The LRU with normalised input (LRU write-up, initialisation section):
+// x_t = lam x_{t-1} + gamma u_t, gamma = sqrt(1 - |lam|^2) per channel.  The loaded inputs
+// are scaled once, when the chunk is reduced (the re-run then uses them as they are), and
+// in the look-back's per-step recompute.
+struct CplxNormOp : CplxOp {
+    struct Chan : CplxOp::Chan { float gamma; };
+    template <int L>
+    __device__ __forceinline__ static Chan chan(const Args& A, int64_t c) {
+        Chan ch;
+        static_cast<CplxOp::Chan&>(ch) = CplxOp::template chan<L>(A, c);
+        const double lr = ch.lr, li = ch.li;
+        ch.gamma = (float)sqrt(fmax(0.0, 1.0 - (lr * lr + li * li)));
+        return ch;
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Agg reduce(const Chan& ch, In (&in)[L][VEC], int e, int n, Local& loc) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) in[j][e] = {ch.gamma * in[j][e].r, ch.gamma * in[j][e].i};
+        return CplxOp::template reduce<L, VEC>(ch, in, e, n, loc);
+    }
+    __device__ __forceinline__ static Agg step(const Chan& ch, const Agg& s, const In& x) {
+        return CplxOp::step(ch, s, In{ch.gamma * x.r, ch.gamma * x.i});
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                                               const In (&in)[L][VEC], const Local (&loc)[VEC], int n, unsigned voff,
+                                               const Rows& rows) {
+        CplxOp::Chan cb[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) cb[e] = ch[e];
+        return CplxOp::template run<L, VEC>(R, cb, cin, in, loc, n, voff, rows);
     }
 };
 

@@ -191,3 +191,15 @@ def make_token_shift(B: int, T: int, C: int, M: int, seed: int, with_grad: bool 
     if with_grad:
         out["g"] = _normal(rng, (M, B, T, C), 1.0)
     return out
+
+
+def make_gated(B: int, T: int, C: int, seed: int, logit_std: float = 1.0):
+    """Inputs of the gated scan variants: gate pre-activations kz, kf, ki ~ N(0, logit_std),
+    candidates h ~ N(0,1), x0 ~ N(0,1) (B,C), a per-channel decay lam ~ U(-1, 1) (C,); all
+    float32, drawn in that order."""
+    rng = np.random.default_rng(seed)
+    out = {n: _normal(rng, (B, T, C), logit_std) for n in ("kz", "kf", "ki")}
+    out["h"] = _normal(rng, (B, T, C), 1.0)
+    out["x0"] = _normal(rng, (B, C), 1.0)
+    out["lam"] = rng.uniform(-1.0, 1.0, size=C).astype(np.float32)
+    return out

@@ -221,3 +221,27 @@ def test_token_shift_argument_checks(lib):
     assert fb(2, 100, 0, 3, None, None, None, None, None, None, None, None, 0, None) == OK
     # empty batch or sequence needs gmu to zero-fill
     assert fb(2, 0, 8, 3, None, None, None, None, None, None, None, None, 0, None) == INVALID
+
+
+def test_gated_scan_argument_checks(lib):
+    need = lib.linrec_scan_workspace_size(2, 1 << 12, 64, 0)
+    needc = lib.linrec_scan_workspace_size(2, 1 << 12, 64, 1)
+    for name, nin in (("linrec_scan_mingru", 2), ("linrec_scan_minlstm", 3), ("linrec_scan_real_decay", 2)):
+        f = getattr(lib, name)
+        ins = [P] * nin
+        assert f(0, 4, 4, *[None] * nin, None, None, None, 0, None) == OK, name
+        assert f(-1, 4, 4, *ins, None, P2, None, 0, None) == INVALID, name
+        for i in range(nin):
+            bad = list(ins)
+            bad[i] = None
+            assert f(2, 1 << 12, 64, *bad, None, P2, P, need, None) == INVALID, (name, i)
+            bad[i] = ODD
+            assert f(2, 1 << 12, 64, *bad, None, P2, P, need, None) == UNSUPPORTED, (name, i)
+        assert f(2, 1 << 12, 64, *ins, None, None, P, need, None) == INVALID, name
+        assert f(2, 1 << 12, 64, *ins, ODD, P2, P, need, None) == UNSUPPORTED, name
+        assert f(2, 1 << 12, 64, *ins, None, P2, P, 16, None) == WORKSPACE, name
+    fc = lib.linrec_scan_complex_normalized
+    assert fc(0, 4, 4, None, None, None, None, None, 0, None) == OK
+    assert fc(2, 1 << 12, 64, P, None, None, P2, P, needc, None) == INVALID
+    assert fc(2, 1 << 12, 64, P, ctypes.c_void_p(0x100004), None, P2, P, needc, None) == UNSUPPORTED
+    assert fc(2, 1 << 12, 64, P, P, None, P2, P, 16, None) == WORKSPACE
