@@ -26,6 +26,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -37,6 +39,10 @@ MALL_BYTES = 256 * 1024 * 1024  # MI355X Infinity Cache
 BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "scan_complex": 16,
                   "scan_real_backward": 20,      # read a, x, gx; write ga, gb
                   "scan_complex_backward": 24,   # read x, gx; write gu (complex64)
+                  "scan_mingru": 12,             # read kz, h; write x
+                  "scan_minlstm": 16,            # read kf, ki, h; write x
+                  "scan_real_decay": 8,          # read u; write x
+                  "scan_complex_normalized": 16, # read u; write x (complex64)
                   "token_shift": 16,             # read x; write 3 mixes
                   "token_shift_backward": 20}    # read x, 3 gradients; write gx
 SHIFT_M = 3  # token-shift mixes timed: the r, k, v inputs of the time mix
@@ -47,7 +53,7 @@ def log(*a):
 
 
 # Sources each entry point's kernels are built from (the launch plan lives in api.hip).
-_SCAN_SOURCES = ("api.hip", "chunk_scan.hip", "chunk_scan.hpp", "scan_ops.hpp", "lookback.hpp",
+_SCAN_SOURCES = ("api.hip", "chunk_scan.hip", "chunk_scan.hpp", "scan_kernel.hpp", "scan_ops.hpp", "lookback.hpp",
                  "device_common.hpp", "wkv_math.hpp")
 KERNEL_SOURCES = {
     "wkv4_forward": _SCAN_SOURCES,
@@ -55,6 +61,10 @@ KERNEL_SOURCES = {
     "scan_complex": _SCAN_SOURCES,
     "scan_real_backward": _SCAN_SOURCES,
     "scan_complex_backward": _SCAN_SOURCES,
+    "scan_mingru": _SCAN_SOURCES + ("scan_kernel.hpp", "scan_variants.hip"),
+    "scan_minlstm": _SCAN_SOURCES + ("scan_kernel.hpp", "scan_variants.hip"),
+    "scan_real_decay": _SCAN_SOURCES + ("scan_kernel.hpp", "scan_variants.hip"),
+    "scan_complex_normalized": _SCAN_SOURCES + ("scan_kernel.hpp", "scan_variants.hip"),
     "token_shift": ("api.hip", "token_shift.hip", "token_shift.hpp", "device_common.hpp"),
     "token_shift_backward": ("api.hip", "token_shift.hip", "token_shift.hpp", "device_common.hpp"),
     "wkv4_backward": ("api.hip", "wkv_backward.hip", "wkv_backward.hpp", "lookback.hpp", "device_common.hpp",
@@ -168,6 +178,31 @@ class Row:
                                    gx.data_ptr(), glam.data_ptr(), gu.data_ptr(), None, ws.data_ptr(), nws,
                                    stream)))
             self.keep += [lam, glam]
+        elif kind in ("scan_mingru", "scan_minlstm", "scan_real_decay"):
+            names = {"scan_mingru": ("kz", "h"), "scan_minlstm": ("kf", "ki", "h"), "scan_real_decay": ("h",)}[kind]
+            fn = getattr(lib, "linrec_" + kind)
+            nws = int(lib.linrec_scan_workspace_size(B, T, C, 0))
+            lam = to(host["lam"]) if kind == "scan_real_decay" else None
+            for _ in range(rotations):
+                ins = [to(host[n]) for n in names]
+                x = torch.empty_like(ins[0])
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += ins + [x, ws]
+                ptrs = ([lam.data_ptr()] if lam is not None else []) + [t.data_ptr() for t in ins]
+                self.calls.append((fn, (B, T, C, *ptrs, None, x.data_ptr(), ws.data_ptr(), nws, stream)))
+            if lam is not None:
+                self.keep.append(lam)
+        elif kind == "scan_complex_normalized":
+            lam = to(host["lam"])
+            nws = int(lib.linrec_scan_workspace_size(B, T, C, 1))
+            for _ in range(rotations):
+                u = to(host["u"])
+                x = torch.empty_like(u)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [u, x, ws]
+                self.calls.append((lib.linrec_scan_complex_normalized, (B, T, C, lam.data_ptr(), u.data_ptr(), None,
+                                   x.data_ptr(), ws.data_ptr(), nws, stream)))
+            self.keep.append(lam)
         elif kind == "token_shift":
             M = host["mu"].shape[0]
             mu = to(host["mu"])
@@ -243,6 +278,10 @@ def cpu_baseline(kind, host, budget_s):
           "scan_complex": lambda: oracle.scan_complex(host["lam"], host["u"]),
           "scan_real_backward": lambda: oracle.scan_real_backward(host["a"], host["x"], host["gx"]),
           "scan_complex_backward": lambda: oracle.scan_complex_backward(host["lam"], host["x"], host["gx"]),
+          "scan_mingru": lambda: oracle.scan_mingru(host["kz"], host["h"]),
+          "scan_minlstm": lambda: oracle.scan_minlstm(host["kf"], host["ki"], host["h"]),
+          "scan_real_decay": lambda: oracle.scan_real_decay(host["lam"], host["h"]),
+          "scan_complex_normalized": lambda: oracle.scan_complex_normalized(host["lam"], host["u"]),
           "token_shift": lambda: oracle.token_shift(host["x"], host["mu"]),
           "token_shift_backward": lambda: oracle.token_shift_backward(host["x"], host["mu"], host["g"],
                                                                       want_gx_prev=False)}[kind]
@@ -286,12 +325,19 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
     B, T, C = shape or (wl.B, wl.T, wl.C)
     if kind.startswith("token_shift"):
         host = workloads.make_token_shift(B, T, C, SHIFT_M, wl.seed, with_grad=kind.endswith("_backward"))
+    elif kind in ("scan_mingru", "scan_minlstm", "scan_real_decay"):
+        host = workloads.make_gated(B, T, C, wl.seed)
+        host["lam"] = (0.5 + 0.5 * np.abs(host["lam"])).astype(np.float32)
     else:
         host = workloads.make_inputs(wid, shape=(B, T, C))
     if kind.endswith("_backward") and kind.startswith("scan_"):
         host.update(workloads.make_scan_adjoint_inputs(wid, host))
     elements = B * T * C
     label = wl.label
+    if kind in ("scan_mingru", "scan_minlstm", "scan_real_decay", "scan_complex_normalized"):
+        label = {"scan_mingru": "minGRU from gate logits", "scan_minlstm": "minLSTM from gate logits",
+                 "scan_real_decay": "real scan with one decay per channel",
+                 "scan_complex_normalized": "LRU with normalised input"}[kind] + " fp32 B=%d T=%d C=%d" % (B, T, C)
     if kind.startswith("token_shift"):
         label = "RWKV token shift%s, %d mixes, fp32 B=%d T=%d C=%d" % (
             " backward" if kind.endswith("_backward") else "", SHIFT_M, B, T, C)
@@ -388,6 +434,8 @@ def main():
                                             (4, "scan_real", 20, 512), (5, "scan_complex", 10, 16384),
                                             (4, "scan_real_backward", 20, 512),
                                             (5, "scan_complex_backward", 10, 16384),
+                                            (4, "scan_mingru", 20, 512), (4, "scan_minlstm", 20, 512),
+                                            (4, "scan_real_decay", 20, 512), (5, "scan_complex_normalized", 10, 16384),
                                             (2, "token_shift", 50, None), (2, "token_shift_backward", 50, None)):
             rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
             log("[bench] " + json.dumps(rows[-1]))
