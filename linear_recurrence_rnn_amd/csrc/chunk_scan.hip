@@ -16,7 +16,9 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 }
 
 // glam, first stage: block (group, k) adds slabs [k kPartBlock, (k+1) kPartBlock) of every
-// batch row, rows in ascending order, slabs in ascending order, for its 64 channels.
+// batch row for its 64 channels.  The association is fixed: within a row, slab s goes to
+// accumulator s mod 8 (so 8 loads are in flight at a time, not one), the 8 accumulators are
+// added in order, and the rows in ascending order.
 __global__ __launch_bounds__(64) void part_sum_kernel(ScanGeom g) {
     const int64_t grp = blockIdx.x, k = blockIdx.y;
     const int lane = threadIdx.x;
@@ -26,9 +28,25 @@ __global__ __launch_bounds__(64) void part_sum_kernel(ScanGeom g) {
     double re = 0.0, im = 0.0;
     for (int64_t b = 0; b < g.B; ++b) {
         const double* p = g.part + 2 * (((b * g.ngrp + grp) * g.nslab) * 64 + lane);
-        for (int64_t s = s0; s < s1; ++s) {
-            re += p[2 * s * 64];
-            im += p[2 * s * 64 + 1];
+        double ar[8], ai[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ar[i] = ai[i] = 0.0;
+        int64_t s = s0;
+        for (; s + 8 <= s1; s += 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                ar[i] += p[2 * (s + i) * 64];
+                ai[i] += p[2 * (s + i) * 64 + 1];
+            }
+        }
+        for (int i = 0; s < s1; ++s, ++i) {
+            ar[i] += p[2 * s * 64];
+            ai[i] += p[2 * s * 64 + 1];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            re += ar[i];
+            im += ai[i];
         }
     }
     g.part2[2 * (k * g.C + c)] = re;
