@@ -62,6 +62,9 @@ def _bind(path: str):
     lib.oracle_token_shift.argtypes = [_I64, _I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_token_shift_backward.argtypes = [_I64, _I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P,
                                                 _F64P, _F64P, _F64P]
+    lib.oracle_wkv4_backward_gated.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P, _F32P, _F32P,
+                                               _F64P, _F64P, _F64P, _F64P, _F64P]
+    lib.oracle_wkv4_backward_gated.restype = None
     lib.oracle_scan_mingru.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_scan_minlstm.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_scan_real_decay.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
@@ -322,3 +325,16 @@ def scan_complex_normalized(lam, u, x0=None, lib=None) -> np.ndarray:
     (lib or _load()).oracle_scan_complex_normalized(B, T, C, _p32(lamf), _p32(uf), None if x0f is None else _p32(x0f),
                                                     x.view(np.float64).ctypes.data_as(_F64P))
     return x
+
+
+def wkv4_backward_gated(w, u, k, v, r, gy, lib=None):
+    """(gw, gu, gk, gv, gr) float64 of the gated output sigma(r) wkv (eq. (15)) given gy."""
+    k = _f32(k)
+    B, T, C = k.shape
+    v, r, gy = _f32(v, (B, T, C)), _f32(r, (B, T, C)), _f32(gy, (B, T, C))
+    w, u = _f32(w, (C,)), _f32(u, (C,))
+    gw, gu = np.empty(C), np.empty(C)
+    gk, gv, gr = (np.empty((B, T, C)) for _ in range(3))
+    (lib or _load()).oracle_wkv4_backward_gated(B, T, C, _p32(w), _p32(u), _p32(k), _p32(v), _p32(r), _p32(gy),
+                                                _p64(gw), _p64(gu), _p64(gk), _p64(gv), _p64(gr))
+    return gw, gu, gk, gv, gr

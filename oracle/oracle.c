@@ -152,10 +152,14 @@ void oracle_wkv4_forward_ex(int64_t B, int64_t T, int64_t C, const float *w, con
  * G_{s-1} = gy_s / D_s + eps G_s from G_{T-1} = 0.
  * gw and gu are (C,); gk and gv are (B,T,C).
  */
-void oracle_wkv4_backward(int64_t B, int64_t T, int64_t C,
-                          const float *w, const float *u,
-                          const float *k, const float *v, const float *gy,
-                          double *gw, double *gu, double *gk, double *gv)
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* r NULL: the plain operator.  Otherwise the output is sigma(r_t) y_t (eq. (15)); the sums
+ * above then run with g_t = gy_t sigma(r_t), and gr_t = gy_t y_t sigma(r_t) (1 - sigma(r_t)). */
+static void wkv4_backward_impl(int64_t B, int64_t T, int64_t C,
+                               const float *w, const float *u,
+                               const float *k, const float *v, const float *r, const float *gy,
+                               double *gw, double *gu, double *gk, double *gv, double *gr)
 {
     double *gw_bc = (double *)calloc((size_t)(B * C), sizeof(double));
     double *gu_bc = (double *)calloc((size_t)(B * C), sizeof(double));
@@ -173,13 +177,18 @@ void oracle_wkv4_backward(int64_t B, int64_t T, int64_t C,
             double A = 0.0, Bs = 0.0, Ad = 0.0, Bd = 0.0, sgw = 0.0, sgu = 0.0;
             for (int64_t t = 0; t < T; ++t) {
                 const int64_t o = base + t * C;
-                const double kt = (double)k[o], vt = (double)v[o], g = (double)gy[o];
+                const double kt = (double)k[o], vt = (double)v[o];
+                const double g = r ? (double)gy[o] * sigmoid((double)r[o]) : (double)gy[o];
                 const double beta = exp(uu + kt - K);
                 const double alpha = exp(kt - K);
                 const double Dt = Bs + beta;
                 const double yt = (A + beta * vt) / Dt;
                 D[t] = Dt;
                 Y[t] = yt;
+                if (gr) {
+                    const double sg = sigmoid((double)r[o]);
+                    gr[o] = (double)gy[o] * yt * sg * (1.0 - sg);
+                }
                 sgu += g * beta * (vt - yt) / Dt;
                 sgw -= g * (Ad - yt * Bd) / Dt;
                 Ad = eps * (Ad + A);
@@ -192,7 +201,8 @@ void oracle_wkv4_backward(int64_t B, int64_t T, int64_t C,
             double G = 0.0, H = 0.0; /* G_{T-1} = H_{T-1} = 0 */
             for (int64_t s = T - 1; s >= 0; --s) {
                 const int64_t o = base + s * C;
-                const double ks = (double)k[o], vs = (double)v[o], g = (double)gy[o];
+                const double ks = (double)k[o], vs = (double)v[o];
+                const double g = r ? (double)gy[o] * sigmoid((double)r[o]) : (double)gy[o];
                 const double beta = exp(uu + ks - K);
                 const double alpha = exp(ks - K);
                 const double q = g / D[s];
@@ -216,6 +226,27 @@ void oracle_wkv4_backward(int64_t B, int64_t T, int64_t C,
     }
     free(gw_bc);
     free(gu_bc);
+}
+
+void oracle_wkv4_backward(int64_t B, int64_t T, int64_t C,
+                          const float *w, const float *u,
+                          const float *k, const float *v, const float *gy,
+                          double *gw, double *gu, double *gk, double *gv)
+{
+    wkv4_backward_impl(B, T, C, w, u, k, v, NULL, gy, gw, gu, gk, gv, NULL);
+}
+
+/*
+ * Backward of the gated output o_t = sigma(r_t) wkv_t (RWKV-LLM page, eq. (15), before W_o)
+ * given gy = dL/do: the WKV gradients with dL/dwkv_t = gy_t sigma(r_t), and
+ * gr_t = dL/dr_t = gy_t wkv_t sigma(r_t) (1 - sigma(r_t)).  gr is (B,T,C) double.
+ */
+void oracle_wkv4_backward_gated(int64_t B, int64_t T, int64_t C,
+                                const float *w, const float *u, const float *k, const float *v,
+                                const float *r, const float *gy,
+                                double *gw, double *gu, double *gk, double *gv, double *gr)
+{
+    wkv4_backward_impl(B, T, C, w, u, k, v, r, gy, gw, gu, gk, gv, gr);
 }
 
 /*

@@ -75,6 +75,9 @@ MUTANTS = [
     ("decay_of_channel_zero", "const double L = (double)lam[c];", "const double L = (double)lam[0];"),
     ("lru_gamma_without_sqrt", "const double gamma = sqrt(1.0 - creal(L * conj(L)));",
      "const double gamma = 1.0 - creal(L * conj(L));"),
+    ("gated_bwd_gr_without_sigmoid_slope", "gr[o] = (double)gy[o] * yt * sg * (1.0 - sg);", "gr[o] = (double)gy[o] * yt * sg;"),
+    ("gated_bwd_ungated_k_grad", "                const double ks = (double)k[o], vs = (double)v[o];\n                const double g = r ? (double)gy[o] * sigmoid((double)r[o]) : (double)gy[o];",
+     "                const double ks = (double)k[o], vs = (double)v[o];\n                const double g = (double)gy[o];"),
     ("shift_bwd_gx_prev_weight", "if (T > 0) gp += (1.0 - mm) * (double)gm[base];", "if (T > 0) gp += mm * (double)gm[base];"),
 ]
 
@@ -132,6 +135,16 @@ def _pins_pass(lib) -> bool:
     r = rng.standard_normal(d["k"].shape).astype(np.float32)
     yg, _ = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"], r=r, lib=lib)
     ok &= np.allclose(yg, ref / (1.0 + np.exp(-r.astype(np.float64))), rtol=1e-10, atol=1e-12)
+    # Gated backward against torch autograd of sigmoid(r) times the dense evaluation.
+    dg = workloads.make_inputs(1, seed=95, shape=(2, 10, 3))
+    rg = rng.standard_normal(dg["k"].shape).astype(np.float32)
+    gyg = rng.standard_normal(dg["k"].shape).astype(np.float32)
+    mine = oracle.wkv4_backward_gated(dg["w"], dg["u"], dg["k"], dg["v"], rg, gyg, lib=lib)
+    tws = [torch.tensor(dg[n], dtype=torch.float64, requires_grad=True) for n in ("w", "u", "k", "v")]
+    trg = torch.tensor(rg, dtype=torch.float64, requires_grad=True)
+    (brute.wkv4_torch(*tws) * torch.sigmoid(trg) * torch.tensor(gyg, dtype=torch.float64)).sum().backward()
+    for m, t in zip(mine, tws + [trg]):
+        ok &= np.allclose(m, t.grad.numpy(), rtol=1e-9, atol=1e-10)
 
     # Token shift: the end points mu = 1 (current token) and mu = 0 (previous token, x_prev
     # first), and the exact adjoint identity of the linear map in x, x_prev and mu.

@@ -100,3 +100,29 @@ def test_empty_sequence_passes_the_state_through():
     assert y.shape == (2, 0, 5)
     np.testing.assert_allclose(so[..., 0] / so[..., 1], 0.25)
     np.testing.assert_allclose(so[..., 2] + np.log(so[..., 1]), 1.5 + np.log(2.0))
+
+
+def test_gated_backward_matches_torch_autograd():
+    """Backward of o = sigma(r) wkv (eq. (15)) against torch fp64 autograd of the dense
+    evaluation of eq. (14) times sigmoid(r)."""
+    torch = pytest.importorskip("torch")
+    d = workloads.make_inputs(1, seed=91, shape=(2, 18, 5))
+    rng = np.random.default_rng(92)
+    r = (rng.standard_normal(d["k"].shape) * 2).astype(np.float32)
+    gy = rng.standard_normal(d["k"].shape).astype(np.float32)
+    mine = oracle.wkv4_backward_gated(d["w"], d["u"], d["k"], d["v"], r, gy)
+    tw, tu, tk, tv, tr = (torch.tensor(x, dtype=torch.float64, requires_grad=True)
+                          for x in (d["w"], d["u"], d["k"], d["v"], r))
+    (brute.wkv4_torch(tw, tu, tk, tv) * torch.sigmoid(tr) * torch.tensor(gy, dtype=torch.float64)).sum().backward()
+    for m, t in zip(mine, (tw, tu, tk, tv, tr)):
+        np.testing.assert_allclose(m, t.grad.numpy(), rtol=1e-9, atol=1e-10)
+
+
+def test_gated_backward_open_gate_is_the_plain_backward():
+    d = workloads.make_inputs(1, seed=93, shape=(2, 12, 4))
+    gy = np.random.default_rng(94).standard_normal(d["k"].shape).astype(np.float32)
+    r = np.full(d["k"].shape, 60.0, np.float32)  # sigmoid = 1 to double precision, sigmoid' ~ 1e-26
+    gw, gu, gk, gv, gr = oracle.wkv4_backward_gated(d["w"], d["u"], d["k"], d["v"], r, gy)
+    for m, ref in zip((gw, gu, gk, gv), oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], gy)):
+        np.testing.assert_allclose(m, ref, rtol=1e-14, atol=1e-15)
+    assert np.max(np.abs(gr)) < 1e-20
