@@ -7,6 +7,7 @@
  *
  *   wkv4_forward / wkv4_backward  the RWKV-4 time-mix operator of eq. (14) on that page
  *   wkv4_forward_ex               the same with a carried state and the sigma(r) gate
+ *   wkv4_backward_ex              the backward through the sigma(r) gate
  *   wkv4_decode_step              one token of it in recurrent form (decoding)
  *   rwkv_token_shift (+ backward) the time-mix token shift of eqs. (11)-(13) feeding it
  *   linrec_scan_real              x_t = a_t * x_{t-1} + b_t (the scan form on the
@@ -208,6 +209,21 @@ int wkv4_backward(int64_t B, int64_t T, int64_t C,
                   const float *w, const float *u, const float *k, const float *v,
                   const float *gy, float *gw, float *gu, float *gk, float *gv,
                   void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of the gated time-mix output o_t = sigma(r_t) wkv_t (RWKV-LLM page, eq. (15),
+ * before W_o; the forward is wkv4_forward_ex with r).  Given gy = dL/do it writes the
+ * gradients of wkv4_backward for dL/dwkv_t = gy_t sigma(r_t), and
+ *
+ *   gr (B,T,C) float32 output:  dL/dr_t = gy_t wkv_t sigma(r_t) (1 - sigma(r_t))
+ *
+ * r (B,T,C) float32.  r and gr are given together (both NULL is wkv4_backward); otherwise
+ * LINREC_ERR_INVALID_ARG.  Same workspace as wkv4_backward.
+ */
+int wkv4_backward_ex(int64_t B, int64_t T, int64_t C,
+                     const float *w, const float *u, const float *k, const float *v,
+                     const float *r, const float *gy, float *gw, float *gu, float *gk, float *gv,
+                     float *gr, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Real diagonal scan, "Were RNNs All We Needed?" page, minGRU section (v_t = a_t (.)

@@ -72,6 +72,8 @@ def load(path: str | None = None):
         lib.rwkv_token_shift_backward_workspace_size.argtypes = [_I64, _I64, _I64, _I64]
         lib.rwkv_token_shift_backward.restype = ctypes.c_int
         lib.rwkv_token_shift_backward.argtypes = [_I64, _I64, _I64, _I64] + [_VP] * 7 + [_VP, _SZ, _VP]
+        lib.wkv4_backward_ex.restype = ctypes.c_int
+        lib.wkv4_backward_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 11 + [_VP, _SZ, _VP]
         lib.wkv4_decode_step.restype = ctypes.c_int
         lib.wkv4_decode_step.argtypes = [_I64, _I64] + [_VP] * 7 + [_VP]
         lib.wkv4_backward.argtypes = [_I64, _I64, _I64] + [_VP] * 9 + [_VP, _SZ, _VP]
@@ -260,6 +262,26 @@ def token_shift_backward(x, mu, g, x_prev=None, want_gx_prev=None, out=None, wor
     _check(lib.rwkv_token_shift_backward(B, T, C, M, _ptr(x), _ptr(x_prev), _ptr(mu), _ptr(g), _ptr(gx), _ptr(gmu),
                                          _ptr(gxp), _ptr(ws), nws, _stream(dev)), "rwkv_token_shift_backward")
     return gx, gmu, gxp
+
+
+def wkv4_backward_gated(w, u, k, v, r, gy, out=None, workspace=None):
+    """(gw, gu, gk, gv, gr) of the gated output sigma(r) wkv given gy = dL/d(output)."""
+    lib = load()
+    B, T, C = k.shape
+    dev = k.device
+    for name, t in (("k", k), ("v", v), ("r", r), ("gy", gy)):
+        _expect(t, name, torch.float32, (B, T, C), dev)
+    _expect(w, "w", torch.float32, (C,), dev)
+    _expect(u, "u", torch.float32, (C,), dev)
+    if out is None:
+        gw, gu = torch.empty_like(w), torch.empty_like(u)
+        gk, gv, gr = torch.empty_like(k), torch.empty_like(k), torch.empty_like(k)
+    else:
+        gw, gu, gk, gv, gr = out
+    ws, nws = _workspace(int(lib.wkv4_backward_workspace_size(B, T, C)), dev, workspace)
+    _check(lib.wkv4_backward_ex(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(gy), _ptr(gw), _ptr(gu),
+                                _ptr(gk), _ptr(gv), _ptr(gr), _ptr(ws), nws, _stream(dev)), "wkv4_backward_ex")
+    return gw, gu, gk, gv, gr
 
 
 def wkv4_backward(w, u, k, v, gy, out=None, workspace=None):

@@ -531,12 +531,14 @@ LINREC_API int linrec_scan_complex_backward(int64_t B, int64_t T, int64_t C, con
                       "linrec_scan_complex_backward launch");
 }
 
-LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                             const float* k, const float* v, const float* gy, float* gw, float* gu,
-                             float* gk, float* gv, void* workspace, size_t ws_bytes, void* stream) {
+LINREC_API int wkv4_backward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                                const float* k, const float* v, const float* r, const float* gy, float* gw,
+                                float* gu, float* gk, float* gv, float* gr, void* workspace, size_t ws_bytes,
+                                void* stream) {
     int st = check_shape(B, T, C, 4);
     if (st) return st;
     if (C > 0 && (!gw || !gu)) return fail(LINREC_ERR_INVALID_ARG, "gw or gu is NULL");
+    if ((r == nullptr) != (gr == nullptr)) return fail(LINREC_ERR_INVALID_ARG, "r and gr must be given together");
     if (B == 0 || T == 0 || C == 0) {
         // Empty batch or sequence: the per-channel sums dL/dw, dL/du are zero.
         if (C == 0) return ok();
@@ -545,9 +547,9 @@ LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, co
     }
     if (!w || !u || !k || !v || !gy || !gk || !gv)
         return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
-    const void* ptrs[] = {w, u, k, v, gy, gw, gu, gk, gv};
+    const void* ptrs[] = {w, u, k, v, r, gy, gw, gu, gk, gv, gr};
     for (const void* p : ptrs)
-        if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+        if (p && !aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
     const linrec::BwdPlan p = bwd_plan(1, B, T, C);
     if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
     linrec::BwdGeom g{};
@@ -561,6 +563,12 @@ LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, co
     g.tag_r = next_tag();
     g.exact_only = env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0;
     linrec::wkv_backward_layout(p, B, C, workspace, g);
-    const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv};
+    const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv, r, gr};
     return hip_status(linrec::run_wkv_backward(A, g, p, (hipStream_t)stream), "wkv4_backward launch");
+}
+
+LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                             const float* k, const float* v, const float* gy, float* gw, float* gu,
+                             float* gk, float* gv, void* workspace, size_t ws_bytes, void* stream) {
+    return wkv4_backward_ex(B, T, C, w, u, k, v, nullptr, gy, gw, gu, gk, gv, nullptr, workspace, ws_bytes, stream);
 }

@@ -43,6 +43,8 @@ namespace linrec {
 
 namespace {
 
+__device__ __forceinline__ float gate_sigmoid(float r) { return __builtin_amdgcn_rcpf(1.f + fast_exp2(-r * kLog2e)); }
+
 // Forward sums over a span: A = a 2^p, B = b 2^p, A' = ad 2^p, B' = bd 2^p.
 struct Fwd { double a, b, ad, bd; float p; };
 // Reverse sums: G-like = x 2^r, H-like = h 2^r; z 2^r is the sum of the (positive) weights,
@@ -449,14 +451,20 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
     const unsigned voff = (unsigned)(lane * VEC * 4);
     const rsrc_t rkj = make_rsrc(A.k + bj, (total - bj) * 4), rvj = make_rsrc(A.v + bj, (total - bj) * 4),
                  rgj = make_rsrc(A.gy + bj, (total - bj) * 4);
+    const rsrc_t rrj = make_rsrc(A.r ? A.r + bj : A.gy + bj, A.r ? (total - bj) * 4 : 0);
     Fwd fs[VEC];
     fwd_carry_in<VEC>(g, gi, sj, lane, active, fs);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) x[e] = {rev_identity(), 0.0, 0.0};
     if (!active) return;
     for (int t = 0; t < nj; ++t) {
-        const FV<VEC> kt = ldb<VEC>(rkj, voff, t * rowb), vt = ldb<VEC>(rvj, voff, t * rowb),
-                      gt = ldb<VEC>(rgj, voff, t * rowb);
+        const FV<VEC> kt = ldb<VEC>(rkj, voff, t * rowb), vt = ldb<VEC>(rvj, voff, t * rowb);
+        FV<VEC> gt = ldb<VEC>(rgj, voff, t * rowb);
+        if (A.r) {
+            const FV<VEC> rt = ldb<VEC>(rrj, voff, t * rowb);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) gt.v[e] *= gate_sigmoid(rt.v[e]);
+        }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const StepOut o = fwd_step(om[e], mu[e], fs[e], kt.v[e] * kLog2e, vt.v[e], gt.v[e], x[e].sw, x[e].su);
@@ -479,13 +487,16 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
 // Register budget: with 8-step chunks the kernel fits 80 VGPRs (6 waves per SIMD), so three
 // 8-wave workgroups share a CU; that hides one workgroup's look-back behind the others'
 // work better than the compiler's own choice (~90 VGPRs, two workgroups).
-template <int L>
+template <int L, bool GATE>
 constexpr int grad_waves_per_eu() {
-    return L <= 8 ? 6 : 1;
+    return L <= 8 ? (GATE ? 5 : 6) : 1;  // the gate's r_j take 8 more registers (5: no spills)
 }
 
-template <int VEC, int NW, int L>
-__global__ __launch_bounds__(64 * (NW + 1)) __attribute__((amdgpu_waves_per_eu(grad_waves_per_eu<L>())))
+// GATE: the output is sigma(r) wkv (eq. (15)); dL/dwkv = gy sigma(r) drives every sum, and
+// dL/dr = dL/dwkv wkv sigma(-r) is written where wkv is formed.  A separate instance, so the
+// plain kernel's registers are unchanged.
+template <int VEC, int NW, int L, bool GATE>
+__global__ __launch_bounds__(64 * (NW + 1)) __attribute__((amdgpu_waves_per_eu(grad_waves_per_eu<L, GATE>())))
 void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     constexpr int CW = 64 * VEC;
     constexpr int SLAB = NW * L;
@@ -522,9 +533,12 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         // Per step: sa = g_j (fast path) or q_j (exact path); vv = v_j; sc = dL/dy_j, then
         // g_j / D~_j (fast) or g_j / dm_j (exact); sy = y_j; sd = v_j - y_j.
         float sa[L], vv[L], sc[L], sy[L], sd[L];
+        float rr[GATE ? L : 1];  // r_j
+        const rsrc_t rgr = make_rsrc(GATE ? A.gr + base : A.gk + base, GATE ? nbytes : 0);
         float gmax = 0.f;
         {
             const rsrc_t rv = make_rsrc(A.v + base, nbytes);
+            const rsrc_t rrs = make_rsrc(GATE ? A.r + base : A.k + base, GATE ? nbytes : 0);
 #pragma unroll
             for (int j = 0; j < L; ++j) {
                 float kt = 0.f, vt = 0.f, gt = 0.f;
@@ -532,6 +546,10 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
                     kt = ldb<1>(rk, voff, j * rowb).v[0];
                     vt = ldb<1>(rv, voff, j * rowb).v[0];
                     gt = ldb<1>(rg, voff, j * rowb).v[0];
+                }
+                if constexpr (GATE) {
+                    rr[j] = j < n ? ldb<1>(rrs, voff, j * rowb).v[0] : 0.f;
+                    gt *= gate_sigmoid(rr[j]);
                 }
                 sa[j] = kt * kLog2e;
                 vv[j] = vt;
@@ -568,6 +586,11 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
                     dmin = fminf(dmin, dt);
                     const float y = fmaf(cur, vj, a) * inv;
                     const float vmy = fmaf(vj, bb, -a) * inv;
+                    if constexpr (GATE) {
+                        FV<1> o;
+                        o.v[0] = sc[j] * y * gate_sigmoid(-rr[j]);
+                        stb<1>(rgr, voff, j * rowb, o);
+                    }
                     const float cg = sc[j] * inv;
                     swf = fmaf(-cg, fmaf(-y, bd, ad), swf);
                     suf = fmaf(cg * cur, vmy, suf);
@@ -601,8 +624,15 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
             for (int j = 0; j < L; ++j) {
                 if (j < n) {
                     const float kj = ldb<1>(rk, voff, j * rowb).v[0] * kLog2e;
-                    const float gj = ldb<1>(rg, voff, j * rowb).v[0];
+                    float gj = ldb<1>(rg, voff, j * rowb).v[0];
+                    if constexpr (GATE) gj *= gate_sigmoid(rr[j]);
                     const StepOut o = fwd_step(om[0], mu[0], st, kj, vv[j], gj, sw, su);
+                    if constexpr (GATE) {
+                        // Overwrites the fast path's value when that path was abandoned.
+                        FV<1> og;
+                        og.v[0] = gj * o.y * gate_sigmoid(-rr[j]);
+                        stb<1>(rgr, voff, j * rowb, og);
+                    }
                     sa[j] = o.q;
                     sc[j] = o.c;
                     sy[j] = o.y;
@@ -828,8 +858,13 @@ hipError_t launch(const WkvBwdArgs& A, const BwdGeom& g, hipStream_t st) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L>), dim3((unsigned)(G * g.nslab)), dim3(64 * (NW + 1)), 0, st,
-                       A, g);
+    if (A.r) {
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true>), dim3((unsigned)(G * g.nslab)), dim3(64 * (NW + 1)),
+                           0, st, A, g);
+    } else {
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false>), dim3((unsigned)(G * g.nslab)),
+                           dim3(64 * (NW + 1)), 0, st, A, g);
+    }
     return hipGetLastError();
 }
 

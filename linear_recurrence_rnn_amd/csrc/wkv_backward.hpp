@@ -17,6 +17,8 @@ struct WkvBwdArgs {
     float* gu;        // (C)
     float* gk;        // (B,T,C)
     float* gv;        // (B,T,C)
+    const float* r;   // (B,T,C) receptance of the gated output sigma(r) wkv, or null
+    float* gr;        // (B,T,C) dL/dr when r is given
 };
 
 // Launch geometry of the backward.  The gradient kernel cuts each sequence into slabs of nw

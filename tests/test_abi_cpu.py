@@ -245,3 +245,17 @@ def test_gated_scan_argument_checks(lib):
     assert fc(2, 1 << 12, 64, P, None, None, P2, P, needc, None) == INVALID
     assert fc(2, 1 << 12, 64, P, ctypes.c_void_p(0x100004), None, P2, P, needc, None) == UNSUPPORTED
     assert fc(2, 1 << 12, 64, P, P, None, P2, P, 16, None) == WORKSPACE
+
+
+def test_wkv4_backward_ex_argument_checks(lib):
+    f = lib.wkv4_backward_ex
+    need = lib.wkv4_backward_workspace_size(2, 1000, 64)
+    # r and gr must come together
+    assert f(2, 1000, 64, P, P, P, P, P, P, P2, P2, P2, P2, None, P, need, None) == INVALID
+    assert f(2, 1000, 64, P, P, P, P, None, P, P2, P2, P2, P2, P2, P, need, None) == INVALID
+    # alignment of the gate pointers
+    assert f(2, 1000, 64, P, P, P, P, ODD, P, P2, P2, P2, P2, P2, P, need, None) == UNSUPPORTED
+    assert f(2, 1000, 64, P, P, P, P, P, P, P2, P2, P2, P2, ODD, P, need, None) == UNSUPPORTED
+    # workspace, required pointers
+    assert f(2, 1000, 64, P, P, P, P, P, P, P2, P2, P2, P2, P2, P, 16, None) == WORKSPACE
+    assert f(2, 1000, 64, P, P, P, P, P, None, P2, P2, P2, P2, P2, P, need, None) == INVALID
