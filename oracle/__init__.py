@@ -65,6 +65,8 @@ def _bind(path: str):
     lib.oracle_wkv4_backward_gated.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P, _F32P, _F32P,
                                                _F64P, _F64P, _F64P, _F64P, _F64P]
     lib.oracle_wkv4_backward_gated.restype = None
+    lib.oracle_wkv4_backward_ex.argtypes = [_I64, _I64, _I64] + [_F32P] * 9 + [_F64P] * 6
+    lib.oracle_wkv4_backward_ex.restype = None
     lib.oracle_scan_mingru.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_scan_minlstm.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_scan_real_decay.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
@@ -338,3 +340,26 @@ def wkv4_backward_gated(w, u, k, v, r, gy, lib=None):
     (lib or _load()).oracle_wkv4_backward_gated(B, T, C, _p32(w), _p32(u), _p32(k), _p32(v), _p32(r), _p32(gy),
                                                 _p64(gw), _p64(gu), _p64(gk), _p64(gv), _p64(gr))
     return gw, gu, gk, gv, gr
+
+
+def wkv4_backward_ex(w, u, k, v, gy, r=None, s_in=None, s_out=None, gs_out=None, want_gs_in=True, lib=None):
+    """(gw, gu, gk, gv, gr or None, gs_in (B,C,2) or None) float64 of WKV-4 with the optional
+    gate sigma(r) and carried state: s_in (a, b, p); gs_out = dL/d(a', b') of s_out = (a', b', p')
+    (p' fixed); gs_in = dL/d(a, b) of s_in (its p fixed)."""
+    k = _f32(k)
+    B, T, C = k.shape
+    v, gy = _f32(v, (B, T, C)), _f32(gy, (B, T, C))
+    w, u = _f32(w, (C,)), _f32(u, (C,))
+    ra = None if r is None else _f32(r, (B, T, C))
+    si = None if s_in is None else _f32(s_in, (B, C, 3))
+    so = None if s_out is None else _f32(s_out, (B, C, 3))
+    go = None if gs_out is None else _f32(gs_out, (B, C, 2))
+    gw, gu = np.empty(C), np.empty(C)
+    gk, gv = np.empty((B, T, C)), np.empty((B, T, C))
+    gr = None if ra is None else np.empty((B, T, C))
+    gsi = np.empty((B, C, 2)) if want_gs_in else None
+    opt = lambda a, f: None if a is None else f(a)  # noqa: E731
+    (lib or _load()).oracle_wkv4_backward_ex(B, T, C, _p32(w), _p32(u), _p32(k), _p32(v), opt(ra, _p32), opt(si, _p32),
+                                             opt(so, _p32), _p32(gy), opt(go, _p32), _p64(gw), _p64(gu), _p64(gk),
+                                             _p64(gv), opt(gr, _p64), opt(gsi, _p64))
+    return gw, gu, gk, gv, gr, gsi

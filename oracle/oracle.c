@@ -155,11 +155,20 @@ void oracle_wkv4_forward_ex(int64_t B, int64_t T, int64_t C, const float *w, con
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 /* r NULL: the plain operator.  Otherwise the output is sigma(r_t) y_t (eq. (15)); the sums
- * above then run with g_t = gy_t sigma(r_t), and gr_t = gy_t y_t sigma(r_t) (1 - sigma(r_t)). */
+ * above then run with g_t = gy_t sigma(r_t), and gr_t = gy_t y_t sigma(r_t) (1 - sigma(r_t)).
+ *
+ * s_in (B,C,3) (a, b, p) or NULL: a carried state, A_0 = a e^p and B_0 = b e^p, decayed with
+ * the sums (A_t = eps^t A_0 + ..., so A'_t gains t eps^t A_0 and dL/dw its share).
+ * gs_out (B,C,2) or NULL: dL/d(a', b') of the state after the last token, s_out = (a', b', p')
+ * with p' = s_out[.,.,2] held fixed, so dL/dA_T = a'-gradient e^{-p'}: it enters the reverse
+ * sums as G_{T-1} = dL/dA_T, H_{T-1} = -dL/dB_T, and dL/dw gains -(dL/dA_T A'_T + dL/dB_T B'_T).
+ * gs_in (B,C,2) or NULL: dL/d(a, b) of s_in with its p held fixed (p = 0 without s_in):
+ * G_{-1} e^p and -H_{-1} e^p. */
 static void wkv4_backward_impl(int64_t B, int64_t T, int64_t C,
                                const float *w, const float *u,
                                const float *k, const float *v, const float *r, const float *gy,
-                               double *gw, double *gu, double *gk, double *gv, double *gr)
+                               double *gw, double *gu, double *gk, double *gv, double *gr,
+                               const float *s_in, const float *s_out, const float *gs_out, double *gs_in)
 {
     double *gw_bc = (double *)calloc((size_t)(B * C), sizeof(double));
     double *gu_bc = (double *)calloc((size_t)(B * C), sizeof(double));
@@ -171,10 +180,24 @@ static void wkv4_backward_impl(int64_t B, int64_t T, int64_t C,
         for (int64_t bc = 0; bc < B * C; ++bc) {
             const int64_t b = bc / C, c = bc % C;
             const int64_t base = b * T * C + c;
-            const double K = chan_max_k(k, T, C, base);
+            const double p0 = s_in ? (double)s_in[3 * bc + 2] : 0.0;
+            if (T == 0) {
+                /* No tokens: the state passes through, s_out = s_in. */
+                gw_bc[bc] = gu_bc[bc] = 0.0;
+                if (gs_in) {
+                    const double f = gs_out ? exp(p0 - (double)s_out[3 * bc + 2]) : 0.0;
+                    gs_in[2 * bc] = gs_out ? (double)gs_out[2 * bc] * f : 0.0;
+                    gs_in[2 * bc + 1] = gs_out ? (double)gs_out[2 * bc + 1] * f : 0.0;
+                }
+                continue;
+            }
+            double K = chan_max_k(k, T, C, base);
+            if (s_in && (s_in[3 * bc] != 0.0f || s_in[3 * bc + 1] != 0.0f) && p0 > K) K = p0;
             const double eps = exp(-(double)w[c]);
             const double uu = (double)u[c];
-            double A = 0.0, Bs = 0.0, Ad = 0.0, Bd = 0.0, sgw = 0.0, sgu = 0.0;
+            double A = s_in ? (double)s_in[3 * bc] * exp(p0 - K) : 0.0;
+            double Bs = s_in ? (double)s_in[3 * bc + 1] * exp(p0 - K) : 0.0;
+            double Ad = 0.0, Bd = 0.0, sgw = 0.0, sgu = 0.0;
             for (int64_t t = 0; t < T; ++t) {
                 const int64_t o = base + t * C;
                 const double kt = (double)k[o], vt = (double)v[o];
@@ -196,9 +219,14 @@ static void wkv4_backward_impl(int64_t B, int64_t T, int64_t C,
                 A = eps * A + alpha * vt;
                 Bs = eps * Bs + alpha;
             }
+            /* The state after the last token: its gradient seeds the reverse sums. */
+            const double so = gs_out ? exp(K - (double)s_out[3 * bc + 2]) : 0.0;
+            const double gA = gs_out ? (double)gs_out[2 * bc] * so : 0.0;   /* dL/dA_T e^K */
+            const double gB = gs_out ? (double)gs_out[2 * bc + 1] * so : 0.0;
+            sgw -= gA * Ad + gB * Bd;
             gw_bc[bc] = sgw;
             gu_bc[bc] = sgu;
-            double G = 0.0, H = 0.0; /* G_{T-1} = H_{T-1} = 0 */
+            double G = gA, H = -gB; /* G_{T-1}, H_{T-1} */
             for (int64_t s = T - 1; s >= 0; --s) {
                 const int64_t o = base + s * C;
                 const double ks = (double)k[o], vs = (double)v[o];
@@ -210,6 +238,10 @@ static void wkv4_backward_impl(int64_t B, int64_t T, int64_t C,
                 gk[o] = q * beta * (vs - Y[s]) + alpha * (vs * G - H);
                 G = q + eps * G;      /* becomes G_{s-1} */
                 H = q * Y[s] + eps * H;
+            }
+            if (gs_in) {
+                gs_in[2 * bc] = G * exp(p0 - K);
+                gs_in[2 * bc + 1] = -H * exp(p0 - K);
             }
         }
         free(D);
@@ -233,7 +265,7 @@ void oracle_wkv4_backward(int64_t B, int64_t T, int64_t C,
                           const float *k, const float *v, const float *gy,
                           double *gw, double *gu, double *gk, double *gv)
 {
-    wkv4_backward_impl(B, T, C, w, u, k, v, NULL, gy, gw, gu, gk, gv, NULL);
+    wkv4_backward_impl(B, T, C, w, u, k, v, NULL, gy, gw, gu, gk, gv, NULL, NULL, NULL, NULL, NULL);
 }
 
 /*
@@ -246,7 +278,20 @@ void oracle_wkv4_backward_gated(int64_t B, int64_t T, int64_t C,
                                 const float *r, const float *gy,
                                 double *gw, double *gu, double *gk, double *gv, double *gr)
 {
-    wkv4_backward_impl(B, T, C, w, u, k, v, r, gy, gw, gu, gk, gv, gr);
+    wkv4_backward_impl(B, T, C, w, u, k, v, r, gy, gw, gu, gk, gv, gr, NULL, NULL, NULL, NULL);
+}
+
+/*
+ * Backward with a carried state (the forward is oracle_wkv4_forward_ex): r and gr as in
+ * oracle_wkv4_backward_gated (NULL for the plain output); s_in, s_out, gs_out, gs_in as
+ * described at wkv4_backward_impl.  Any of them may be NULL.
+ */
+void oracle_wkv4_backward_ex(int64_t B, int64_t T, int64_t C, const float *w, const float *u, const float *k,
+                             const float *v, const float *r, const float *s_in, const float *s_out,
+                             const float *gy, const float *gs_out, double *gw, double *gu, double *gk, double *gv,
+                             double *gr, double *gs_in)
+{
+    wkv4_backward_impl(B, T, C, w, u, k, v, r, gy, gw, gu, gk, gv, gr, s_in, s_out, gs_out, gs_in);
 }
 
 /*

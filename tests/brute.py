@@ -191,3 +191,26 @@ def scan_torch(coef, inp, x0=None):
         s = ct * s + inp[:, t]
         out.append(s)
     return torch.stack(out, dim=1)
+
+
+def wkv4_state_torch(w, u, k, v, a0, b0, p0, p_out):
+    """Dense torch form of eq. (14) with a carried state A_0 = a0 e^p0, B_0 = b0 e^p0:
+    y_t = (eps^t A_0 + sum_{i<t} ...) / (eps^t B_0 + sum_{i<t} ... + e^{u+k_t}), and the state
+    after the last token in units of e^{p_out}."""
+    import torch
+    B, T, C = k.shape
+    t = torch.arange(T, dtype=torch.float64)
+    dist = (t[:, None] - 1.0 - t[None, :])
+    mask = (t[None, :] < t[:, None])
+    kk, vv = k.permute(0, 2, 1), v.permute(0, 2, 1)
+    expo = -dist[None, None] * w[None, :, None, None] + kk[:, :, None, :]
+    E = torch.exp(torch.where(mask[None, None], expo, torch.full_like(expo, -torch.inf)))
+    cur = torch.exp(u[None, :, None] + kk)
+    decay = torch.exp(-t[None, None, :] * w[None, :, None])  # eps^t
+    A0 = (a0 * torch.exp(p0)).unsqueeze(-1)
+    B0 = (b0 * torch.exp(p0)).unsqueeze(-1)
+    y = ((E * vv[:, :, None, :]).sum(-1) + decay * A0 + cur * vv) / (E.sum(-1) + decay * B0 + cur)
+    wT = torch.exp(-(T - 1.0 - t)[None, None, :] * w[None, :, None] + kk)  # eps^{T-1-i} e^{k_i}
+    AT = (wT * vv).sum(-1) + torch.exp(-T * w)[None, :] * A0[..., 0]
+    BT = wT.sum(-1) + torch.exp(-T * w)[None, :] * B0[..., 0]
+    return y.permute(0, 2, 1), AT * torch.exp(-p_out), BT * torch.exp(-p_out)

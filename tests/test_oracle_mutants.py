@@ -78,6 +78,9 @@ MUTANTS = [
     ("gated_bwd_gr_without_sigmoid_slope", "gr[o] = (double)gy[o] * yt * sg * (1.0 - sg);", "gr[o] = (double)gy[o] * yt * sg;"),
     ("gated_bwd_ungated_k_grad", "                const double ks = (double)k[o], vs = (double)v[o];\n                const double g = r ? (double)gy[o] * sigmoid((double)r[o]) : (double)gy[o];",
      "                const double ks = (double)k[o], vs = (double)v[o];\n                const double g = (double)gy[o];"),
+    ("state_bwd_w_term_dropped", "            sgw -= gA * Ad + gB * Bd;\n", "\n"),
+    ("state_bwd_H_seed_sign", "double G = gA, H = -gB;", "double G = gA, H = gB;"),
+    ("state_bwd_gs_in_b_sign", "gs_in[2 * bc + 1] = -H * exp(p0 - K);", "gs_in[2 * bc + 1] = H * exp(p0 - K);"),
     ("shift_bwd_gx_prev_weight", "if (T > 0) gp += (1.0 - mm) * (double)gm[base];", "if (T > 0) gp += mm * (double)gm[base];"),
 ]
 
@@ -144,6 +147,25 @@ def _pins_pass(lib) -> bool:
     trg = torch.tensor(rg, dtype=torch.float64, requires_grad=True)
     (brute.wkv4_torch(*tws) * torch.sigmoid(trg) * torch.tensor(gyg, dtype=torch.float64)).sum().backward()
     for m, t in zip(mine, tws + [trg]):
+        ok &= np.allclose(m, t.grad.numpy(), rtol=1e-9, atol=1e-10)
+
+    # Backward with a carried state and the gradient of the state after the last token,
+    # against torch autograd of the dense form that carries the state.
+    ds = workloads.make_inputs(1, seed=96, shape=(2, 9, 3))
+    si = np.stack([rng.standard_normal((2, 3)), rng.uniform(0.2, 2, (2, 3)), rng.uniform(-2, 3, (2, 3))],
+                  axis=-1).astype(np.float32)
+    so = np.stack([np.zeros((2, 3)), np.ones((2, 3)), rng.uniform(0, 4, (2, 3))], axis=-1).astype(np.float32)
+    gso = rng.standard_normal((2, 3, 2)).astype(np.float32)
+    gys = rng.standard_normal(ds["k"].shape).astype(np.float32)
+    mine = oracle.wkv4_backward_ex(ds["w"], ds["u"], ds["k"], ds["v"], gys, s_in=si, s_out=so, gs_out=gso, lib=lib)
+    tws = [torch.tensor(ds[n], dtype=torch.float64, requires_grad=True) for n in ("w", "u", "k", "v")]
+    ta = torch.tensor(si[..., 0], dtype=torch.float64, requires_grad=True)
+    tb = torch.tensor(si[..., 1], dtype=torch.float64, requires_grad=True)
+    yy, aT, bT = brute.wkv4_state_torch(*tws, ta, tb, torch.tensor(si[..., 2], dtype=torch.float64),
+                                        torch.tensor(so[..., 2], dtype=torch.float64))
+    ((yy * torch.tensor(gys, dtype=torch.float64)).sum() + (aT * torch.tensor(gso[..., 0], dtype=torch.float64)).sum()
+     + (bT * torch.tensor(gso[..., 1], dtype=torch.float64)).sum()).backward()
+    for m, t in zip(list(mine[:4]) + [mine[5][..., 0], mine[5][..., 1]], tws + [ta, tb]):
         ok &= np.allclose(m, t.grad.numpy(), rtol=1e-9, atol=1e-10)
 
     # Token shift: the end points mu = 1 (current token) and mu = 0 (previous token, x_prev

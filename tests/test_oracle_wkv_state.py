@@ -126,3 +126,63 @@ def test_gated_backward_open_gate_is_the_plain_backward():
     for m, ref in zip((gw, gu, gk, gv), oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], gy)):
         np.testing.assert_allclose(m, ref, rtol=1e-14, atol=1e-15)
     assert np.max(np.abs(gr)) < 1e-20
+
+
+def _state_backward_case(seed, B=2, T=24, C=5):
+    d = workloads.make_inputs(1, seed=seed, shape=(B, T, C))
+    rng = np.random.default_rng(seed + 1)
+    gy = rng.standard_normal(d["k"].shape).astype(np.float32)
+    return d, gy, rng
+
+
+@pytest.mark.parametrize("split", [1, 9, 23])
+def test_state_backward_chains_calls(split):
+    """A sequence cut in two, forward chained through the state and backward chained through
+    its gradient, gives the gradients of one call over the whole sequence."""
+    d, gy, _ = _state_backward_case(101)
+    w, u, k, v = d["w"], d["u"], d["k"], d["v"]
+    whole = oracle.wkv4_backward(w, u, k, v, gy)
+    _, s1 = oracle.wkv4_forward_ex(w, u, k[:, :split], v[:, :split])
+    s1 = s1.astype(np.float32)
+    g2 = oracle.wkv4_backward_ex(w, u, k[:, split:], v[:, split:], gy[:, split:], s_in=s1)
+    g1 = oracle.wkv4_backward_ex(w, u, k[:, :split], v[:, :split], gy[:, :split], s_out=s1,
+                                 gs_out=g2[5].astype(np.float32), want_gs_in=False)
+    # the state is rounded to float32 once at the cut: agreement to float32 precision
+    np.testing.assert_allclose(g1[0] + g2[0], whole[0], rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(g1[1] + g2[1], whole[1], rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(np.concatenate([g1[2], g2[2]], axis=1), whole[2], rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(np.concatenate([g1[3], g2[3]], axis=1), whole[3], rtol=1e-5, atol=1e-6)
+
+
+def test_state_backward_matches_torch_autograd():
+    torch = pytest.importorskip("torch")
+    d, gy, rng = _state_backward_case(103, T=20)
+    B, T, C = d["k"].shape
+    s_in = np.stack([rng.standard_normal((B, C)), rng.uniform(0.2, 2.0, (B, C)), rng.uniform(-2, 3, (B, C))],
+                    axis=-1).astype(np.float32)
+    s_out = np.stack([np.zeros((B, C)), np.ones((B, C)), rng.uniform(0, 4, (B, C))], axis=-1).astype(np.float32)
+    gs_out = rng.standard_normal((B, C, 2)).astype(np.float32)
+    mine = oracle.wkv4_backward_ex(d["w"], d["u"], d["k"], d["v"], gy, s_in=s_in, s_out=s_out, gs_out=gs_out)
+    tw, tu, tk, tv = (torch.tensor(d[n], dtype=torch.float64, requires_grad=True) for n in ("w", "u", "k", "v"))
+    ta = torch.tensor(s_in[..., 0], dtype=torch.float64, requires_grad=True)
+    tb = torch.tensor(s_in[..., 1], dtype=torch.float64, requires_grad=True)
+    y, aT, bT = brute.wkv4_state_torch(tw, tu, tk, tv, ta, tb, torch.tensor(s_in[..., 2], dtype=torch.float64),
+                                 torch.tensor(s_out[..., 2], dtype=torch.float64))
+    loss = (y * torch.tensor(gy, dtype=torch.float64)).sum() + (aT * torch.tensor(gs_out[..., 0], dtype=torch.float64)).sum() \
+        + (bT * torch.tensor(gs_out[..., 1], dtype=torch.float64)).sum()
+    loss.backward()
+    for m, t in zip(mine[:4], (tw, tu, tk, tv)):
+        np.testing.assert_allclose(m, t.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(mine[5][..., 0], ta.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(mine[5][..., 1], tb.grad.numpy(), rtol=1e-9, atol=1e-10)
+
+
+def test_state_backward_no_tokens_passes_gradient_through():
+    d, gy, rng = _state_backward_case(105, T=0)
+    B, _, C = d["k"].shape
+    s = np.stack([rng.standard_normal((B, C)), rng.uniform(0.2, 2.0, (B, C)), rng.uniform(-2, 3, (B, C))],
+                 axis=-1).astype(np.float32)
+    gs = rng.standard_normal((B, C, 2)).astype(np.float32)
+    gw, gu, _, _, _, gsi = oracle.wkv4_backward_ex(d["w"], d["u"], d["k"], d["v"], gy, s_in=s, s_out=s, gs_out=gs)
+    np.testing.assert_array_equal(gsi, gs.astype(np.float64))
+    assert np.all(gw == 0) and np.all(gu == 0)
