@@ -7,7 +7,7 @@
  *
  *   wkv4_forward / wkv4_backward  the RWKV-4 time-mix operator of eq. (14) on that page
  *   wkv4_forward_ex               the same with a carried state and the sigma(r) gate
- *   wkv4_backward_ex              the backward through the sigma(r) gate
+ *   wkv4_backward_ex              its backward (gate and carried state)
  *   wkv4_decode_step              one token of it in recurrent form (decoding)
  *   rwkv_token_shift (+ backward) the time-mix token shift of eqs. (11)-(13) feeding it
  *   linrec_scan_real              x_t = a_t * x_{t-1} + b_t (the scan form on the
@@ -211,19 +211,35 @@ int wkv4_backward(int64_t B, int64_t T, int64_t C,
                   void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * Backward of the gated time-mix output o_t = sigma(r_t) wkv_t (RWKV-LLM page, eq. (15),
- * before W_o; the forward is wkv4_forward_ex with r).  Given gy = dL/do it writes the
- * gradients of wkv4_backward for dL/dwkv_t = gy_t sigma(r_t), and
+ * Backward of wkv4_forward_ex: the gated time-mix output o_t = sigma(r_t) wkv_t (RWKV-LLM
+ * page, eq. (15), before W_o) over a sequence that may start from a carried state and
+ * whose final state may feed a later call.  Given gy = dL/do it writes the gradients of
+ * wkv4_backward for dL/dwkv_t = gy_t sigma(r_t), and
  *
- *   gr (B,T,C) float32 output:  dL/dr_t = gy_t wkv_t sigma(r_t) (1 - sigma(r_t))
+ *   gr    (B,T,C) float32 output:  dL/dr_t = gy_t wkv_t sigma(r_t) (1 - sigma(r_t))
+ *   gs_in (B,C,2) float32 output:  dL/da, dL/db of s_in = (a, b, p), its p held fixed
  *
- * r (B,T,C) float32.  r and gr are given together (both NULL is wkv4_backward); otherwise
- * LINREC_ERR_INVALID_ARG.  Same workspace as wkv4_backward.
+ *   r      (B,T,C) float32, as given to the forward; r and gr are given together (both NULL:
+ *                  no gate, sigma = 1), otherwise LINREC_ERR_INVALID_ARG
+ *   s_in   (B,C,3) float32 (a, b, p) as given to the forward, or NULL (empty state)
+ *   s_out  (B,C,3) float32, the forward's s_out; only its p is read, and only with gs_out
+ *   gs_out (B,C,2) float32 dL/d(a', b') of s_out = (a', b', p') with p' held fixed, or NULL
+ *                  (the final state not used); given without s_out: LINREC_ERR_INVALID_ARG
+ *   gs_in  may be NULL (not wanted)
+ *
+ * With p fixed, A = a e^p gives dL/dA = (dL/da) e^{-p}: the final state's gradient enters the
+ * reverse sums as dL/dA_T, dL/dB_T, and dL/dw gains their share.  Calls chained through the
+ * state (s_out of one as s_in of the next) chain their gradients the same way: the gs_in of
+ * the later call is the gs_out of the earlier one.  The pages give no backward; this is the
+ * chain rule of eq. (14) with the state as its sums before the first token.  T = 0: the
+ * state passes through, gs_in = gs_out e^{p_in - p_out} (zero without gs_out), gw = gu = 0.
+ * Same workspace as wkv4_backward.
  */
 int wkv4_backward_ex(int64_t B, int64_t T, int64_t C,
                      const float *w, const float *u, const float *k, const float *v,
-                     const float *r, const float *gy, float *gw, float *gu, float *gk, float *gv,
-                     float *gr, void *workspace, size_t ws_bytes, void *stream);
+                     const float *r, const float *s_in, const float *s_out, const float *gy,
+                     const float *gs_out, float *gw, float *gu, float *gk, float *gv, float *gr,
+                     float *gs_in, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Real diagonal scan, "Were RNNs All We Needed?" page, minGRU section (v_t = a_t (.)

@@ -73,7 +73,7 @@ def load(path: str | None = None):
         lib.rwkv_token_shift_backward.restype = ctypes.c_int
         lib.rwkv_token_shift_backward.argtypes = [_I64, _I64, _I64, _I64] + [_VP] * 7 + [_VP, _SZ, _VP]
         lib.wkv4_backward_ex.restype = ctypes.c_int
-        lib.wkv4_backward_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 11 + [_VP, _SZ, _VP]
+        lib.wkv4_backward_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 15 + [_VP, _SZ, _VP]
         lib.wkv4_decode_step.restype = ctypes.c_int
         lib.wkv4_decode_step.argtypes = [_I64, _I64] + [_VP] * 7 + [_VP]
         lib.wkv4_backward.argtypes = [_I64, _I64, _I64] + [_VP] * 9 + [_VP, _SZ, _VP]
@@ -264,24 +264,45 @@ def token_shift_backward(x, mu, g, x_prev=None, want_gx_prev=None, out=None, wor
     return gx, gmu, gxp
 
 
-def wkv4_backward_gated(w, u, k, v, r, gy, out=None, workspace=None):
-    """(gw, gu, gk, gv, gr) of the gated output sigma(r) wkv given gy = dL/d(output)."""
+def wkv4_backward_ex(w, u, k, v, gy, r=None, s_in=None, s_out=None, gs_out=None, want_gs_in=True, out=None,
+                     workspace=None):
+    """(gw, gu, gk, gv, gr, gs_in) of wkv4_forward_ex: gy = dL/d(output); r the gate (gr None
+    without it); s_in the carried state (a, b, p) given to the forward or None; s_out the
+    forward's final state, read (its p) only with gs_out = dL/d(a', b') (B,C,2); gs_in =
+    dL/d(a, b) of s_in (B,C,2) when ``want_gs_in``, else None."""
     lib = load()
     B, T, C = k.shape
     dev = k.device
-    for name, t in (("k", k), ("v", v), ("r", r), ("gy", gy)):
+    for name, t in (("k", k), ("v", v), ("gy", gy)):
         _expect(t, name, torch.float32, (B, T, C), dev)
     _expect(w, "w", torch.float32, (C,), dev)
     _expect(u, "u", torch.float32, (C,), dev)
+    if r is not None:
+        _expect(r, "r", torch.float32, (B, T, C), dev)
+    for name, t, n in (("s_in", s_in, 3), ("s_out", s_out, 3), ("gs_out", gs_out, 2)):
+        if t is not None:
+            _expect(t, name, torch.float32, (B, C, n), dev)
+    if gs_out is not None and s_out is None:
+        raise ValueError("gs_out needs s_out (the forward's final state)")
     if out is None:
         gw, gu = torch.empty_like(w), torch.empty_like(u)
-        gk, gv, gr = torch.empty_like(k), torch.empty_like(k), torch.empty_like(k)
+        gk, gv = torch.empty_like(k), torch.empty_like(k)
+        gr = None if r is None else torch.empty_like(k)
+        gs_in = torch.empty((B, C, 2), dtype=torch.float32, device=dev) if want_gs_in else None
     else:
-        gw, gu, gk, gv, gr = out
+        gw, gu, gk, gv, gr, gs_in = out
     ws, nws = _workspace(int(lib.wkv4_backward_workspace_size(B, T, C)), dev, workspace)
-    _check(lib.wkv4_backward_ex(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(gy), _ptr(gw), _ptr(gu),
-                                _ptr(gk), _ptr(gv), _ptr(gr), _ptr(ws), nws, _stream(dev)), "wkv4_backward_ex")
-    return gw, gu, gk, gv, gr
+    _check(lib.wkv4_backward_ex(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(s_in), _ptr(s_out),
+                                _ptr(gy), _ptr(gs_out), _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(gr),
+                                _ptr(gs_in), _ptr(ws), nws, _stream(dev)), "wkv4_backward_ex")
+    return gw, gu, gk, gv, gr, gs_in
+
+
+def wkv4_backward_gated(w, u, k, v, r, gy, out=None, workspace=None):
+    """(gw, gu, gk, gv, gr) of the gated output sigma(r) wkv given gy = dL/d(output)."""
+    _expect(r, "r", torch.float32, tuple(k.shape), k.device)
+    return wkv4_backward_ex(w, u, k, v, gy, r=r, want_gs_in=False,
+                            out=None if out is None else tuple(out) + (None,), workspace=workspace)[:5]
 
 
 def wkv4_backward(w, u, k, v, gy, out=None, workspace=None):

@@ -532,18 +532,27 @@ LINREC_API int linrec_scan_complex_backward(int64_t B, int64_t T, int64_t C, con
 }
 
 LINREC_API int wkv4_backward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                                const float* k, const float* v, const float* r, const float* gy, float* gw,
-                                float* gu, float* gk, float* gv, float* gr, void* workspace, size_t ws_bytes,
+                                const float* k, const float* v, const float* r, const float* s_in,
+                                const float* s_out, const float* gy, const float* gs_out, float* gw, float* gu,
+                                float* gk, float* gv, float* gr, float* gs_in, void* workspace, size_t ws_bytes,
                                 void* stream) {
     int st = check_shape(B, T, C, 4);
     if (st) return st;
     if (C > 0 && (!gw || !gu)) return fail(LINREC_ERR_INVALID_ARG, "gw or gu is NULL");
     if ((r == nullptr) != (gr == nullptr)) return fail(LINREC_ERR_INVALID_ARG, "r and gr must be given together");
+    if (gs_out && !s_out) return fail(LINREC_ERR_INVALID_ARG, "gs_out needs s_out (its exponents)");
+    const void* sptrs[] = {s_in, s_out, gs_out, gs_in};
+    for (const void* p : sptrs)
+        if (p && !aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "state pointer not 4-byte aligned");
+    const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv, r, gr, s_in, s_out, gs_out, gs_in};
     if (B == 0 || T == 0 || C == 0) {
-        // Empty batch or sequence: the per-channel sums dL/dw, dL/du are zero.
+        // Empty batch or sequence: the per-channel sums dL/dw, dL/du are zero, and without
+        // tokens the state passes through (dL/ds_in from dL/ds_out alone).
         if (C == 0) return ok();
         if (!aligned(gw, 4) || !aligned(gu, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
-        return hip_status(linrec::run_zero_wu(gw, gu, C, (hipStream_t)stream), "wkv4_backward zero-fill");
+        hipError_t e = linrec::run_zero_wu(gw, gu, C, (hipStream_t)stream);
+        if (e == hipSuccess && gs_in) e = linrec::run_state_grad_passthrough(A, B, C, (hipStream_t)stream);
+        return hip_status(e, "wkv4_backward zero-fill");
     }
     if (!w || !u || !k || !v || !gy || !gk || !gv)
         return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -563,12 +572,12 @@ LINREC_API int wkv4_backward_ex(int64_t B, int64_t T, int64_t C, const float* w,
     g.tag_r = next_tag();
     g.exact_only = env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0;
     linrec::wkv_backward_layout(p, B, C, workspace, g);
-    const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv, r, gr};
     return hip_status(linrec::run_wkv_backward(A, g, p, (hipStream_t)stream), "wkv4_backward launch");
 }
 
 LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
                              const float* k, const float* v, const float* gy, float* gw, float* gu,
                              float* gk, float* gv, void* workspace, size_t ws_bytes, void* stream) {
-    return wkv4_backward_ex(B, T, C, w, u, k, v, nullptr, gy, gw, gu, gk, gv, nullptr, workspace, ws_bytes, stream);
+    return wkv4_backward_ex(B, T, C, w, u, k, v, nullptr, nullptr, nullptr, gy, nullptr, gw, gu, gk, gv, nullptr,
+                            nullptr, workspace, ws_bytes, stream);
 }

@@ -252,16 +252,68 @@ __device__ __forceinline__ void load_chan(const WkvBwdArgs& A, int64_t c0, bool 
     }
 }
 
-// Forward sums at the start of slab s: written by the state kernel at the end of slab s-1.
-template <int VEC>
-__device__ __forceinline__ void fwd_carry_in(const BwdGeom& g, int64_t gi, int64_t s, int lane, bool active,
-                                             Fwd (&x)[VEC]) {
+// ---- a carried state (chain rule of eq. (14) over a sequence cut in pieces) ----
+// The state (a, b, p) means A = a e^p, B = b e^p; its gradients are taken w.r.t. (a, b) with
+// p held fixed, so that calls chained through the state chain their gradients too.
+// 2^r e^x for an integer-valued r: e^x = 2^P e^{x - P ln 2} with ln 2 split in two parts (as
+// for the state's exponent), so a large |x| costs no accuracy; 0 for an empty exponent.
+__device__ __forceinline__ double pow2_exp(float r, float x) {
+    if (r == kEmpty) return 0.0;
+    const float P = ceilf(x * kLog2e);
+    const float rem = fmaf(-P, kLn2Lo, fmaf(-P, kLn2Hi, x));
+    return ldexp((double)fast_exp2(rem * kLog2e), (int)(r + P));
+}
+
+// The forward sums before the first token: s_in in base-2 form (empty without it).
+__device__ __forceinline__ Fwd fwd_state_in(const WkvBwdArgs& A, const BwdGeom& g, int64_t b, int64_t c) {
+    if (!A.s_in) return fwd_identity();
+    const float* s = A.s_in + 3 * (b * g.C + c);
+    const Base2State x = state_from_natural(s[0], s[1], s[2]);
+    if (x.b == 0.f && x.a == 0.f) return fwd_identity();
+    return {(double)x.a, (double)x.b, 0.0, 0.0, x.p};
+}
+
+// The reverse sums after the last token: G_{T-1} = dL/dA_T = ga' e^{-p'}, H_{T-1} = -dL/dB_T.
+__device__ __forceinline__ Rev rev_state_out(const WkvBwdArgs& A, const BwdGeom& g, int64_t b, int64_t c) {
+    if (!A.gs_out) return rev_identity();
+    const float ga = A.gs_out[2 * (b * g.C + c)], gb = A.gs_out[2 * (b * g.C + c) + 1];
+    if (ga == 0.f && gb == 0.f) return rev_identity();
+    // e^{-p'} = 2^P 2^{rem log2 e}, P integer, rem = -p' - P ln 2 with ln 2 split in two parts.
+    const float np = -A.s_out[3 * (b * g.C + c) + 2];
+    const float P = ceilf(np * kLog2e);
+    const float rem = fmaf(-P, kLn2Lo, fmaf(-P, kLn2Hi, np));
+    const double sc = (double)fast_exp2(rem * kLog2e);
+    return {ga * sc, -(double)gb * sc, (fabs((double)ga) + fabs((double)gb)) * sc, P};
+}
+
+// dL/dw's share of the state after the last token: -(dL/dA_T A'_T + dL/dB_T B'_T), with the
+// forward sums at the end of the sequence.
+__device__ __forceinline__ double sw_state_out(const WkvBwdArgs& A, const BwdGeom& g, int64_t b, int64_t c,
+                                               const Fwd& end) {
+    if (!A.gs_out) return 0.0;
+    const double ga = A.gs_out[2 * (b * g.C + c)], gb = A.gs_out[2 * (b * g.C + c) + 1];
+    return -(ga * end.ad + gb * end.bd) * pow2_exp(end.p, -A.s_out[3 * (b * g.C + c) + 2]);
+}
+
+// dL/d(a, b) of s_in from the reverse sums before the first token (G_{-1}, H_{-1}).
+__device__ __forceinline__ void write_state_grad(const WkvBwdArgs& A, const BwdGeom& g, int64_t b, int64_t c,
+                                                 const Rev& st) {
+    const double f = pow2_exp(st.r, A.s_in ? A.s_in[3 * (b * g.C + c) + 2] : 0.f);
+    A.gs_in[2 * (b * g.C + c)] = (float)(st.x * f);
+    A.gs_in[2 * (b * g.C + c) + 1] = (float)(-st.h * f);
+}
+
+// Forward sums at the start of slab s: written by the state kernel at the end of slab s-1;
+// before the first slab, the carried state (STATE) or the empty one.
+template <int VEC, bool STATE>
+__device__ __forceinline__ void fwd_carry_in(const WkvBwdArgs& A, const BwdGeom& g, int64_t gi, int64_t b,
+                                             int64_t c0, int64_t s, int lane, bool active, Fwd (&x)[VEC]) {
     constexpr int64_t per = 64 * VEC * kDwords<Fwd>;  // dwords per slab record
     if (s > 0 && active) {
         load_record<VEC>(reinterpret_cast<const uint32_t*>(g.incl_f) + gi * g.nslab * per, s - 1, lane, x);
     } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) x[e] = fwd_identity();
+        for (int e = 0; e < VEC; ++e) x[e] = (STATE && active) ? fwd_state_in(A, g, b, c0 + e) : fwd_identity();
     }
 }
 
@@ -405,7 +457,7 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
         Fwd mine[1], carry[1];
         mine[0] = shf[ib][0][lane];
         for (int x = 1; x < nvalid; ++x) mine[0] = fwd_combine(om[0], mine[0], shf[ib][x][lane], SLAB);
-        carry[0] = fwd_identity();
+        carry[0] = it.active ? fwd_state_in(A, g, it.b, it.c0) : fwd_identity();
         const bool has_succ = it.q + 1 < nitem;
         if (has_succ) publish<1>(chn, it.q, lane, mine, false);
         auto fold = [&](Fwd (&c)[1], const Fwd (&x)[1], int64_t) {
@@ -437,7 +489,7 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
 // The reverse record of chain slab jj computed from its inputs (the look-back's fallback
 // when the slab has not published in time): the slab's forward re-run from the state
 // kernel's sums, one step at a time, accumulating its reverse sums in time order.
-template <int VEC, int SLAB>
+template <int VEC, int SLAB, bool STATE>
 __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, const BwdGeom& g, int64_t jj,
                                                        int64_t gi, int64_t b, int64_t grp, int lane, bool active,
                                                        const float (&om)[VEC], const float (&mu)[VEC],
@@ -453,7 +505,8 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
                  rgj = make_rsrc(A.gy + bj, (total - bj) * 4);
     const rsrc_t rrj = make_rsrc(A.r ? A.r + bj : A.gy + bj, A.r ? (total - bj) * 4 : 0);
     Fwd fs[VEC];
-    fwd_carry_in<VEC>(g, gi, sj, lane, active, fs);
+    const int64_t c0 = grp * CW + (int64_t)lane * VEC;
+    fwd_carry_in<VEC, STATE>(A, g, gi, b, c0, sj, lane, active, fs);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) x[e] = {rev_identity(), 0.0, 0.0};
     if (!active) return;
@@ -472,6 +525,15 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
             x[e].st = rev_combine(om[e], one, x[e].st, t);
         }
     }
+    if (STATE && jj == 0) {
+        // The last slab of the sequence: its record also holds the final state's gradient
+        // (the reverse sums behind the slab and dL/dw's share).
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            x[e].st = rev_combine(om[e], rev_state_out(A, g, b, c0 + e), x[e].st, nj);
+            x[e].sw += sw_state_out(A, g, b, c0 + e, fs[e]);
+        }
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -487,16 +549,20 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
 // Register budget: with 8-step chunks the kernel fits 80 VGPRs (6 waves per SIMD), so three
 // 8-wave workgroups share a CU; that hides one workgroup's look-back behind the others'
 // work better than the compiler's own choice (~90 VGPRs, two workgroups).
-template <int L, bool GATE>
+template <int L, bool GATE, bool STATE>
 constexpr int grad_waves_per_eu() {
-    return L <= 8 ? (GATE ? 5 : 6) : 1;  // the gate's r_j take 8 more registers (5: no spills)
+    // The gate's r_j take 8 more registers, the state's terms a few: 5 waves (96 VGPRs), 4
+    // with both (no spills).
+    return L <= 8 ? ((GATE && STATE) ? 4 : (GATE || STATE) ? 5 : 6) : 1;
 }
 
 // GATE: the output is sigma(r) wkv (eq. (15)); dL/dwkv = gy sigma(r) drives every sum, and
-// dL/dr = dL/dwkv wkv sigma(-r) is written where wkv is formed.  A separate instance, so the
-// plain kernel's registers are unchanged.
-template <int VEC, int NW, int L, bool GATE>
-__global__ __launch_bounds__(64 * (NW + 1)) __attribute__((amdgpu_waves_per_eu(grad_waves_per_eu<L, GATE>())))
+// dL/dr = dL/dwkv wkv sigma(-r) is written where wkv is formed.  STATE: a carried state
+// s_in starts the forward sums, the final state's gradient gs_out starts the reverse ones and
+// gs_in is written.  Separate instances, so the plain kernel's registers are unchanged.
+template <int VEC, int NW, int L, bool GATE, bool STATE>
+__global__ __launch_bounds__(64 * (NW + 1))
+__attribute__((amdgpu_waves_per_eu(grad_waves_per_eu<L, GATE, STATE>())))
 void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     constexpr int CW = 64 * VEC;
     constexpr int SLAB = NW * L;
@@ -717,7 +783,7 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
 
     // ---- coordinator ----
     Fwd cin[VEC];
-    fwd_carry_in<VEC>(g, gi, s, lane, active, cin);  // issued before the chunks are reduced
+    fwd_carry_in<VEC, STATE>(A, g, gi, b, c0, s, lane, active, cin);  // issued before the chunks are reduced
     __syncthreads();  // B1
     {
         // Carry-in of each chunk: the previous slab's sums (state kernel), then the chunks in order.
@@ -729,6 +795,8 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
                 shf[x][lane * VEC + e] = c;
                 c = fwd_combine(om[e], c, chunk, chunk_len<L>(x, slab_n));
             }
+            // The last slab: dL/dw's share of the final state, parked in LDS until the record.
+            if constexpr (STATE) sh_mine[lane * VEC + e].sw = (q == 0 && active) ? sw_state_out(A, g, b, c0 + e, c) : 0.0;
         }
     }
     __syncthreads();  // B2
@@ -744,11 +812,15 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         // Reverse sums of the slab from its start: chunks folded from the last to the first.
         Rev a = rev_identity();
         double sw = 0.0, su = 0.0;
+        // The last slab's record also holds the final state's gradient, so that every chain
+        // starts from the empty carry.
+        if (STATE && q == 0 && active) a = rev_state_out(A, g, b, c0 + e);
         for (int x = NW - 1; x >= 0; --x) a = rev_combine(om[e], a, shr[x][lane * VEC + e], chunk_len<L>(x, slab_n));
         for (int x = 0; x < NW; ++x) {
             sw += shwu[x][lane * VEC + e][0];
             su += shwu[x][lane * VEC + e][1];
         }
+        if constexpr (STATE) sw += sh_mine[lane * VEC + e].sw;
         mine[e] = {a, sw, su};
         carry[e] = {rev_identity(), 0.0, 0.0};
         sh_mine[lane * VEC + e] = mine[e];  // kept in LDS across the look-back (registers)
@@ -767,7 +839,7 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         }
     };
     auto recompute = [&](int64_t jj, RevRec (&x)[VEC]) {
-        rev_record_from_inputs<VEC, SLAB>(A, g, jj, gi, b, grp, lane, active, om, mu, x);
+        rev_record_from_inputs<VEC, SLAB, STATE>(A, g, jj, gi, b, grp, lane, active, om, mu, x);
     };
     look_back<VEC, 1>(chn, q, lane, carry, fold, recompute, first);
     RevRec incl[VEC];
@@ -784,12 +856,13 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         for (int e = 0; e < VEC; ++e) {
             g.part[2 * (b * g.C + c0 + e)] = incl[e].sw;
             g.part[2 * (b * g.C + c0 + e) + 1] = incl[e].su;
+            if (STATE && A.gs_in) write_state_grad(A, g, b, c0 + e, incl[e].st);  // the sequence's first slab
         }
     }
     // Reverse state at the end of each chunk: from the slab's end, backwards.
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        Rev r = carry[e].st;
+        Rev r = (STATE && q == 0 && active) ? rev_state_out(A, g, b, c0 + e) : carry[e].st;
         for (int x = NW - 1; x >= 0; --x) {
             const Rev chunk = shr[x][lane * VEC + e];
             shr[x][lane * VEC + e] = r;
@@ -858,12 +931,16 @@ hipError_t launch(const WkvBwdArgs& A, const BwdGeom& g, hipStream_t st) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (A.r) {
-        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true>), dim3((unsigned)(G * g.nslab)), dim3(64 * (NW + 1)),
-                           0, st, A, g);
+    const bool state = A.s_in || A.gs_out || A.gs_in;
+    const dim3 grid((unsigned)(G * g.nslab)), block(64 * (NW + 1));
+    if (A.r && state) {
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true, true>), grid, block, 0, st, A, g);
+    } else if (A.r) {
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true, false>), grid, block, 0, st, A, g);
+    } else if (state) {
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false, true>), grid, block, 0, st, A, g);
     } else {
-        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false>), dim3((unsigned)(G * g.nslab)),
-                           dim3(64 * (NW + 1)), 0, st, A, g);
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false, false>), grid, block, 0, st, A, g);
     }
     return hipGetLastError();
 }
@@ -942,6 +1019,27 @@ hipError_t run_wkv_backward(const WkvBwdArgs& A, const BwdGeom& g, const BwdPlan
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(wkv_bwd_wu_kernel, dim3((unsigned)((g.C + 255) / 256)), dim3(256), 0, st, g.part, g.B, g.C,
                        A.gw, A.gu);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void state_grad_passthrough_kernel(WkvBwdArgs A, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    double f = 0.0, ga = 0.0, gb = 0.0;
+    if (A.gs_out) {
+        const double p_in = A.s_in ? (double)A.s_in[3 * i + 2] : 0.0;
+        f = exp(p_in - (double)A.s_out[3 * i + 2]);
+        ga = A.gs_out[2 * i];
+        gb = A.gs_out[2 * i + 1];
+    }
+    A.gs_in[2 * i] = (float)(ga * f);
+    A.gs_in[2 * i + 1] = (float)(gb * f);
+}
+
+hipError_t run_state_grad_passthrough(const WkvBwdArgs& A, int64_t B, int64_t C, hipStream_t st) {
+    const int64_t n = B * C;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(state_grad_passthrough_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A, n);
     return hipGetLastError();
 }
 

@@ -19,6 +19,10 @@ struct WkvBwdArgs {
     float* gv;        // (B,T,C)
     const float* r;   // (B,T,C) receptance of the gated output sigma(r) wkv, or null
     float* gr;        // (B,T,C) dL/dr when r is given
+    const float* s_in;    // (B,C,3) carried state (a, b, p) before the first token, or null
+    const float* s_out;   // (B,C,3) the forward's state after the last token (its p), or null
+    const float* gs_out;  // (B,C,2) dL/d(a', b') of s_out (p' fixed), or null
+    float* gs_in;         // (B,C,2) dL/d(a, b) of s_in (its p fixed), or null
 };
 
 // Launch geometry of the backward.  The gradient kernel cuts each sequence into slabs of nw
@@ -58,5 +62,7 @@ bool bwd_shape_supported(int vec, int nw, int L);
 hipError_t run_wkv_backward(const WkvBwdArgs& A, const BwdGeom& g, const BwdPlan& p, hipStream_t st);
 // Writes zeros to gw and gu (C floats each): the sums over an empty batch or sequence.
 hipError_t run_zero_wu(float* gw, float* gu, int64_t C, hipStream_t st);
+// No tokens: the state passes through, so gs_in = gs_out e^{p_in - p_out} (zero without gs_out).
+hipError_t run_state_grad_passthrough(const WkvBwdArgs& A, int64_t B, int64_t C, hipStream_t st);
 
 }  // namespace linrec

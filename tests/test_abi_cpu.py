@@ -250,12 +250,23 @@ def test_gated_scan_argument_checks(lib):
 def test_wkv4_backward_ex_argument_checks(lib):
     f = lib.wkv4_backward_ex
     need = lib.wkv4_backward_workspace_size(2, 1000, 64)
+
+    def call(r=P, s_in=None, s_out=None, gy=P, gs_out=None, gr=P2, gs_in=None, ws=need, T=1000):
+        # (B, T, C, w, u, k, v, r, s_in, s_out, gy, gs_out, gw, gu, gk, gv, gr, gs_in, ws, bytes, stream)
+        return f(2, T, 64, P, P, P, P, r, s_in, s_out, gy, gs_out, P2, P2, P2, P2, gr, gs_in, P, ws, None)
+
     # r and gr must come together
-    assert f(2, 1000, 64, P, P, P, P, P, P, P2, P2, P2, P2, None, P, need, None) == INVALID
-    assert f(2, 1000, 64, P, P, P, P, None, P, P2, P2, P2, P2, P2, P, need, None) == INVALID
-    # alignment of the gate pointers
-    assert f(2, 1000, 64, P, P, P, P, ODD, P, P2, P2, P2, P2, P2, P, need, None) == UNSUPPORTED
-    assert f(2, 1000, 64, P, P, P, P, P, P, P2, P2, P2, P2, ODD, P, need, None) == UNSUPPORTED
+    assert call(gr=None) == INVALID
+    assert call(r=None) == INVALID
+    # alignment of the gate and state pointers
+    assert call(r=ODD) == UNSUPPORTED
+    assert call(gr=ODD) == UNSUPPORTED
+    assert call(s_in=ODD) == UNSUPPORTED
+    assert call(gs_in=ODD) == UNSUPPORTED
+    assert call(s_out=P, gs_out=ODD) == UNSUPPORTED
+    # the final state's gradient needs its exponents
+    assert call(gs_out=P2) == INVALID
+    assert call(gs_out=P2, T=0) == INVALID
     # workspace, required pointers
-    assert f(2, 1000, 64, P, P, P, P, P, P, P2, P2, P2, P2, P2, P, 16, None) == WORKSPACE
-    assert f(2, 1000, 64, P, P, P, P, P, None, P2, P2, P2, P2, P2, P, need, None) == INVALID
+    assert call(ws=16) == WORKSPACE
+    assert call(gy=None) == INVALID
