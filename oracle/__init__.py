@@ -71,8 +71,17 @@ def _bind(path: str):
     lib.oracle_scan_minlstm.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_scan_real_decay.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_scan_complex_normalized.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
+    lib.oracle_scan_mingru_backward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P, _F32P,
+                                                _F64P, _F64P, _F64P]
+    lib.oracle_scan_minlstm_backward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P, _F64P, _F32P,
+                                                 _F64P, _F64P, _F64P, _F64P]
+    lib.oracle_scan_real_decay_backward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F64P, _F32P,
+                                                    _F64P, _F64P, _F64P]
+    lib.oracle_scan_complex_normalized_backward.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P, _F32P,
+                                                            _F64P, _F64P, _F64P]
     for name in ("oracle_scan_mingru", "oracle_scan_minlstm", "oracle_scan_real_decay",
-                 "oracle_scan_complex_normalized"):
+                 "oracle_scan_complex_normalized", "oracle_scan_mingru_backward", "oracle_scan_minlstm_backward",
+                 "oracle_scan_real_decay_backward", "oracle_scan_complex_normalized_backward"):
         getattr(lib, name).restype = None
     for name in ("oracle_wkv4_forward", "oracle_wkv4_backward", "oracle_scan_real",
                  "oracle_scan_complex", "oracle_scan_real_backward", "oracle_scan_complex_backward",
@@ -327,6 +336,87 @@ def scan_complex_normalized(lam, u, x0=None, lib=None) -> np.ndarray:
     (lib or _load()).oracle_scan_complex_normalized(B, T, C, _p32(lamf), _p32(uf), None if x0f is None else _p32(x0f),
                                                     x.view(np.float64).ctypes.data_as(_F64P))
     return x
+
+
+def _want(x0, want_gx0):
+    return x0 is not None if want_gx0 is None else want_gx0
+
+
+def _x64(x, shape):
+    xd = np.ascontiguousarray(x, dtype=np.float64)
+    if xd.shape != shape:
+        raise ValueError("x must be %s" % (shape,))
+    return xd
+
+
+def scan_mingru_backward(kz, h, x, gx, x0=None, want_gx0=None, lib=None):
+    """(gkz, gh (B,T,C), gx0 (B,C) or None) float64: the backward of minGRU given its forward
+    output x and the upstream gradient gx."""
+    kz = _f32(kz)
+    B, T, C = kz.shape
+    h, gx = _f32(h, (B, T, C)), _f32(gx, (B, T, C))
+    xd = _x64(x, (B, T, C))
+    x0a = None if x0 is None else _f32(x0, (B, C))
+    gkz, gh = np.empty((B, T, C)), np.empty((B, T, C))
+    gx0 = np.empty((B, C)) if _want(x0, want_gx0) else None
+    (lib or _load()).oracle_scan_mingru_backward(B, T, C, _p32(kz), _p32(h), None if x0a is None else _p32(x0a),
+                                                 _p64(xd), _p32(gx), _p64(gkz), _p64(gh),
+                                                 None if gx0 is None else _p64(gx0))
+    return gkz, gh, gx0
+
+
+def scan_minlstm_backward(kf, ki, h, x, gx, x0=None, want_gx0=None, lib=None):
+    """(gkf, gki, gh (B,T,C), gx0 (B,C) or None) float64: the backward of minLSTM."""
+    kf = _f32(kf)
+    B, T, C = kf.shape
+    ki, h, gx = _f32(ki, (B, T, C)), _f32(h, (B, T, C)), _f32(gx, (B, T, C))
+    xd = _x64(x, (B, T, C))
+    x0a = None if x0 is None else _f32(x0, (B, C))
+    gkf, gki, gh = np.empty((B, T, C)), np.empty((B, T, C)), np.empty((B, T, C))
+    gx0 = np.empty((B, C)) if _want(x0, want_gx0) else None
+    (lib or _load()).oracle_scan_minlstm_backward(B, T, C, _p32(kf), _p32(ki), _p32(h),
+                                                  None if x0a is None else _p32(x0a), _p64(xd), _p32(gx),
+                                                  _p64(gkf), _p64(gki), _p64(gh), None if gx0 is None else _p64(gx0))
+    return gkf, gki, gh, gx0
+
+
+def scan_real_decay_backward(lam, x, gx, x0=None, want_gx0=None, lib=None):
+    """(glam (C,), gu (B,T,C), gx0 (B,C) or None) float64: the backward of
+    x_t = lam_c x_{t-1} + u_t."""
+    gx = _f32(gx)
+    B, T, C = gx.shape
+    lam = _f32(lam, (C,))
+    xd = _x64(x, (B, T, C))
+    x0a = None if x0 is None else _f32(x0, (B, C))
+    glam, gu = np.empty(C), np.empty((B, T, C))
+    gx0 = np.empty((B, C)) if _want(x0, want_gx0) else None
+    (lib or _load()).oracle_scan_real_decay_backward(B, T, C, _p32(lam), None if x0a is None else _p32(x0a),
+                                                     _p64(xd), _p32(gx), _p64(glam), _p64(gu),
+                                                     None if gx0 is None else _p64(gx0))
+    return glam, gu, gx0
+
+
+def scan_complex_normalized_backward(lam, u, x, gx, x0=None, want_gx0=None, lib=None):
+    """(glam (C,), gu (B,T,C), gx0 (B,C) or None) complex128: the backward of
+    x_t = lam x_{t-1} + sqrt(1 - |lam|^2) u_t (gradients as dL/dRe + i dL/dIm)."""
+    gxc = np.ascontiguousarray(gx, dtype=np.complex64)
+    B, T, C = gxc.shape
+    lf = _c64f(lam, (C,))
+    uc = np.ascontiguousarray(u, dtype=np.complex64)
+    if uc.shape != (B, T, C):
+        raise ValueError("u must be (B,T,C)")
+    xd = np.ascontiguousarray(x, dtype=np.complex128)
+    if xd.shape != (B, T, C):
+        raise ValueError("x must be (B,T,C)")
+    x0f = None if x0 is None else _c64f(x0, (B, C))
+    glam = np.empty(C, dtype=np.complex128)
+    gu = np.empty((B, T, C), dtype=np.complex128)
+    gx0 = np.empty((B, C), dtype=np.complex128) if _want(x0, want_gx0) else None
+    f64 = lambda z: z.view(np.float64).ctypes.data_as(_F64P)  # noqa: E731
+    (lib or _load()).oracle_scan_complex_normalized_backward(
+        B, T, C, _p32(lf), _p32(uc.view(np.float32)), None if x0f is None else _p32(x0f), f64(xd),
+        _p32(gxc.view(np.float32)), f64(glam), f64(gu), None if gx0 is None else f64(gx0))
+    return glam, gu, gx0
 
 
 def wkv4_backward_gated(w, u, k, v, r, gy, lib=None):

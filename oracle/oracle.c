@@ -599,3 +599,159 @@ void oracle_scan_complex_normalized(int64_t B, int64_t T, int64_t C, const float
         }
     }
 }
+
+/*
+ * Backward of minGRU (the pages give none; chain rule of the minGRU reading above).  With
+ * z_t = sigmoid(kz_t) and d_t = dL/dh_t, the total gradient of the hidden state,
+ *     d_t = gx_t + (1 - z_{t+1}) d_{t+1}          (d_T = 0)
+ *     dL/dz_t  = d_t (h~_t - h_{t-1}),   dL/dkz_t = dL/dz_t z_t (1 - z_t)
+ *     dL/dh~_t = d_t z_t,                dL/dx0   = (1 - z_0) d_0
+ * x is the forward output (double), h_{-1} = x0 or 0.  gx0 may be NULL.
+ */
+void oracle_scan_mingru_backward(int64_t B, int64_t T, int64_t C, const float *kz, const float *h,
+                                 const float *x0, const double *x, const float *gx, double *gkz,
+                                 double *gh, double *gx0)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        const double h0 = x0 ? (double)x0[b * C + c] : 0.0;
+        double d = 0.0, znext = 0.0;  /* d_{t+1} and z_{t+1}; the step after the last adds nothing */
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int64_t o = base + t * C;
+            const double z = 1.0 / (1.0 + exp(-(double)kz[o]));
+            d = (double)gx[o] + (t + 1 < T ? (1.0 - znext) * d : 0.0);
+            const double hprev = t > 0 ? x[o - C] : h0;
+            gkz[o] = d * ((double)h[o] - hprev) * z * (1.0 - z);
+            gh[o] = d * z;
+            znext = z;
+        }
+        if (gx0) gx0[b * C + c] = T > 0 ? (1.0 - znext) * d : 0.0;
+    }
+}
+
+/*
+ * Backward of minLSTM (chain rule of the minLSTM reading above).  With f = sigmoid(kf),
+ * i = sigmoid(ki), a = f / (f + i) (the weight of h_{t-1}; i / (f + i) = 1 - a weighs h~):
+ *     d_t = gx_t + a_{t+1} d_{t+1},   dL/da_t = d_t (h_{t-1} - h~_t),   dL/dh~_t = d_t (1 - a_t)
+ *     da/df = i / (f + i)^2,  da/di = -f / (f + i)^2,  df/dkf = f (1 - f),  di/dki = i (1 - i)
+ *     dL/dx0 = a_0 d_0
+ */
+void oracle_scan_minlstm_backward(int64_t B, int64_t T, int64_t C, const float *kf, const float *ki,
+                                  const float *h, const float *x0, const double *x, const float *gx,
+                                  double *gkf, double *gki, double *gh, double *gx0)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        const double h0 = x0 ? (double)x0[b * C + c] : 0.0;
+        double d = 0.0, anext = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int64_t o = base + t * C;
+            const double f = 1.0 / (1.0 + exp(-(double)kf[o]));
+            const double i = 1.0 / (1.0 + exp(-(double)ki[o]));
+            const double a = f / (f + i);
+            d = (double)gx[o] + (t + 1 < T ? anext * d : 0.0);
+            const double hprev = t > 0 ? x[o - C] : h0;
+            const double ga = d * (hprev - (double)h[o]);
+            gkf[o] = ga * i / ((f + i) * (f + i)) * f * (1.0 - f);
+            gki[o] = -ga * f / ((f + i) * (f + i)) * i * (1.0 - i);
+            gh[o] = d * (1.0 - a);
+            anext = a;
+        }
+        if (gx0) gx0[b * C + c] = T > 0 ? anext * d : 0.0;
+    }
+}
+
+/*
+ * Backward of the real scan with one decay per channel, x_t = lam_c x_{t-1} + u_t:
+ *     gu_t = gx_t + lam_c gu_{t+1},   glam_c = sum over batch and time of gu_t x_{t-1},
+ *     gx0 = lam_c gu_0.   glam adds the batch rows in ascending order.
+ */
+void oracle_scan_real_decay_backward(int64_t B, int64_t T, int64_t C, const float *lam, const float *x0,
+                                     const double *x, const float *gx, double *glam, double *gu, double *gx0)
+{
+    double *part = (double *)calloc((size_t)(B * C) + 1, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        const double L = (double)lam[c];
+        const double h0 = x0 ? (double)x0[b * C + c] : 0.0;
+        double s = 0.0, acc = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int64_t o = base + t * C;
+            s = (double)gx[o] + L * s;
+            gu[o] = s;
+            acc += s * (t > 0 ? x[o - C] : h0);
+        }
+        part[bc] = acc;
+        if (gx0) gx0[b * C + c] = T > 0 ? L * s : 0.0;
+    }
+    for (int64_t c = 0; c < C; ++c) {
+        double sum = 0.0;
+        for (int64_t b = 0; b < B; ++b) sum += part[b * C + c];
+        glam[c] = sum;
+    }
+    free(part);
+}
+
+/*
+ * Backward of the LRU with normalised input, x_t = lambda x_{t-1} + gamma u_t with
+ * gamma = sqrt(1 - |lambda|^2) (gradients as dL/dRe + i dL/dIm, as for the complex scan):
+ *     s_t = gx_t + conj(lambda) s_{t+1},   dL/du_t = gamma s_t,   dL/dx0 = conj(lambda) s_0,
+ *     dL/dgamma = sum over batch and time of Re(conj(s_t) u_t),
+ *     glambda = sum of s_t conj(x_{t-1}) + dL/dgamma (dgamma/dRe + i dgamma/dIm)
+ *             = sum of s_t conj(x_{t-1}) - (dL/dgamma / gamma) lambda,
+ * the last term taken as 0 where gamma = 0 (|lambda| = 1, where gamma has no derivative).
+ */
+void oracle_scan_complex_normalized_backward(int64_t B, int64_t T, int64_t C, const float *lam, const float *u,
+                                             const float *x0, const double *x, const float *gx, double *glam,
+                                             double *gu, double *gx0)
+{
+    double *part = (double *)calloc((size_t)(B * C) * 3 + 1, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bc = 0; bc < B * C; ++bc) {
+        const int64_t b = bc / C, c = bc % C;
+        const int64_t base = b * T * C + c;
+        const double complex L = (double)lam[2 * c] + (double)lam[2 * c + 1] * I;
+        const double gamma = sqrt(1.0 - creal(L * conj(L)));
+        const double complex z0 = x0 ? (double)x0[2 * (b * C + c)] + (double)x0[2 * (b * C + c) + 1] * I : 0.0;
+        double complex s = 0.0, acc = 0.0;
+        double dgam = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int64_t o = base + t * C;
+            s = ((double)gx[2 * o] + (double)gx[2 * o + 1] * I) + conj(L) * s;
+            gu[2 * o] = gamma * creal(s);
+            gu[2 * o + 1] = gamma * cimag(s);
+            const double complex xp = t > 0 ? x[2 * (o - C)] + x[2 * (o - C) + 1] * I : z0;
+            acc += s * conj(xp);
+            const double complex ut = (double)u[2 * o] + (double)u[2 * o + 1] * I;
+            dgam += creal(conj(s) * ut);
+        }
+        part[3 * bc] = creal(acc);
+        part[3 * bc + 1] = cimag(acc);
+        part[3 * bc + 2] = dgam;
+        if (gx0) {
+            const double complex g0 = T > 0 ? conj(L) * s : 0.0;
+            gx0[2 * (b * C + c)] = creal(g0);
+            gx0[2 * (b * C + c) + 1] = cimag(g0);
+        }
+    }
+    for (int64_t c = 0; c < C; ++c) {
+        const double complex L = (double)lam[2 * c] + (double)lam[2 * c + 1] * I;
+        const double gamma = sqrt(1.0 - creal(L * conj(L)));
+        double re = 0.0, im = 0.0, dg = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            re += part[3 * (b * C + c)];
+            im += part[3 * (b * C + c) + 1];
+            dg += part[3 * (b * C + c) + 2];
+        }
+        const double k = gamma > 0.0 ? dg / gamma : 0.0;
+        glam[2 * c] = re - k * creal(L);
+        glam[2 * c + 1] = im - k * cimag(L);
+    }
+    free(part);
+}

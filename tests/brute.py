@@ -214,3 +214,25 @@ def wkv4_state_torch(w, u, k, v, a0, b0, p0, p_out):
     AT = (wT * vv).sum(-1) + torch.exp(-T * w)[None, :] * A0[..., 0]
     BT = wT.sum(-1) + torch.exp(-T * w)[None, :] * B0[..., 0]
     return y.permute(0, 2, 1), AT * torch.exp(-p_out), BT * torch.exp(-p_out)
+
+
+def mingru_torch(kz, h, x0=None):
+    """minGRU as a plain torch loop: z = sigmoid(kz), x_t = (1 - z_t) x_{t-1} + z_t h_t."""
+    import torch
+    z = torch.sigmoid(kz)
+    return scan_torch(1.0 - z, z * h, x0)
+
+
+def minlstm_torch(kf, ki, h, x0=None):
+    """minLSTM as a plain torch loop: f, i = sigmoid(kf), sigmoid(ki),
+    x_t = f/(f+i) x_{t-1} + i/(f+i) h_t."""
+    import torch
+    f, i = torch.sigmoid(kf), torch.sigmoid(ki)
+    return scan_torch(f / (f + i), i / (f + i) * h, x0)
+
+
+def lru_normalized_torch(lam, u, x0=None):
+    """x_t = lam x_{t-1} + sqrt(1 - |lam|^2) u_t as a plain torch loop (complex)."""
+    import torch
+    gamma = torch.sqrt(1.0 - lam.abs() ** 2)
+    return scan_torch(lam, gamma * u, x0)

@@ -56,7 +56,8 @@ MUTANTS = [
     ("complex_bwd_lambda_not_conjugated",
      "const double complex Lc = conj((double)lam[2 * c] + (double)lam[2 * c + 1] * I);",
      "const double complex Lc = (double)lam[2 * c] + (double)lam[2 * c + 1] * I;"),
-    ("complex_bwd_glam_x_not_conjugated", "acc += s * conj(xp);", "acc += s * xp;"),
+    ("complex_bwd_glam_x_not_conjugated", "x[2 * (o - C) + 1] * I : z0;\n            acc += s * conj(xp);\n        }\n        part[2 * bc]",
+     "x[2 * (o - C) + 1] * I : z0;\n            acc += s * xp;\n        }\n        part[2 * bc]"),
     ("state_in_scale_inverted", "double A = has_state ? a0 * exp(p0 - K) : 0.0;",
      "double A = has_state ? a0 * exp(K - p0) : 0.0;"),
     ("state_denominator_not_carried", "double Bs = has_state ? b0 * exp(p0 - K) : 0.0;", "double Bs = 0.0;"),
@@ -72,15 +73,26 @@ MUTANTS = [
     ("mingru_gate_swapped", "s = (1.0 - z) * s + z * (double)h[o];", "s = z * s + (1.0 - z) * (double)h[o];"),
     ("minlstm_not_normalised", "s = (f / (f + i)) * s + (i / (f + i)) * (double)h[o];",
      "s = f * s + i * (double)h[o];"),
-    ("decay_of_channel_zero", "const double L = (double)lam[c];", "const double L = (double)lam[0];"),
-    ("lru_gamma_without_sqrt", "const double gamma = sqrt(1.0 - creal(L * conj(L)));",
-     "const double gamma = 1.0 - creal(L * conj(L));"),
+    ("decay_of_channel_zero", "const double L = (double)lam[c];\n        double s = x0",
+     "const double L = (double)lam[0];\n        double s = x0"),
+    ("lru_gamma_without_sqrt", "const double gamma = sqrt(1.0 - creal(L * conj(L)));\n        double complex s = 0.0;",
+     "const double gamma = 1.0 - creal(L * conj(L));\n        double complex s = 0.0;"),
     ("gated_bwd_gr_without_sigmoid_slope", "gr[o] = (double)gy[o] * yt * sg * (1.0 - sg);", "gr[o] = (double)gy[o] * yt * sg;"),
     ("gated_bwd_ungated_k_grad", "                const double ks = (double)k[o], vs = (double)v[o];\n                const double g = r ? (double)gy[o] * sigmoid((double)r[o]) : (double)gy[o];",
      "                const double ks = (double)k[o], vs = (double)v[o];\n                const double g = (double)gy[o];"),
     ("state_bwd_w_term_dropped", "            sgw -= gA * Ad + gB * Bd;\n", "\n"),
     ("state_bwd_H_seed_sign", "double G = gA, H = -gB;", "double G = gA, H = gB;"),
     ("state_bwd_gs_in_b_sign", "gs_in[2 * bc + 1] = -H * exp(p0 - K);", "gs_in[2 * bc + 1] = H * exp(p0 - K);"),
+    ("mingru_bwd_gate_slope_dropped", "gkz[o] = d * ((double)h[o] - hprev) * z * (1.0 - z);",
+     "gkz[o] = d * ((double)h[o] - hprev);"),
+    ("mingru_bwd_carry_with_own_gate", "d = (double)gx[o] + (t + 1 < T ? (1.0 - znext) * d : 0.0);",
+     "d = (double)gx[o] + (t + 1 < T ? (1.0 - z) * d : 0.0);"),
+    ("minlstm_bwd_gki_sign", "gki[o] = -ga * f / ((f + i) * (f + i)) * i * (1.0 - i);",
+     "gki[o] = ga * f / ((f + i) * (f + i)) * i * (1.0 - i);"),
+    ("minlstm_bwd_candidate_weight", "gh[o] = d * (1.0 - a);", "gh[o] = d * a;"),
+    ("decay_bwd_x0_ignored", "acc += s * (t > 0 ? x[o - C] : h0);", "acc += s * (t > 0 ? x[o - C] : 0.0);"),
+    ("lru_norm_bwd_gamma_term_sign", "glam[2 * c] = re - k * creal(L);", "glam[2 * c] = re + k * creal(L);"),
+    ("lru_norm_bwd_gu_unscaled", "gu[2 * o] = gamma * creal(s);", "gu[2 * o] = creal(s);"),
     ("shift_bwd_gx_prev_weight", "if (T > 0) gp += (1.0 - mm) * (double)gm[base];", "if (T > 0) gp += mm * (double)gm[base];"),
 ]
 
@@ -205,6 +217,36 @@ def _pins_pass(lib) -> bool:
     ok &= np.allclose(oracle.scan_complex_normalized(lr["lam"], lr["u"], xc0, lib=lib),
                       brute.scan_complex_sums(lr["lam"], gam * lr["u"].astype(np.complex128), xc0),
                       rtol=1e-11, atol=1e-12)
+
+    # Backward of the fused variants against torch autograd of plain torch forwards.
+    gv3 = rng.standard_normal(hv.shape).astype(np.float32)
+    tg = torch.tensor(gv3, dtype=torch.float64)
+    xm = oracle.scan_mingru(kz, hv, xv0, lib=lib)
+    mine = oracle.scan_mingru_backward(kz, hv, xm, gv3, xv0, lib=lib)
+    tk, th, tx = (torch.tensor(z, dtype=torch.float64, requires_grad=True) for z in (kz, hv, xv0))
+    brute.mingru_torch(tk, th, tx).backward(tg)
+    for m, t in zip(mine, (tk, th, tx)):
+        ok &= np.allclose(m, t.grad.numpy(), rtol=1e-10, atol=1e-11)
+    ki = (rng.standard_normal(hv.shape) * 1.5).astype(np.float32)
+    xl = oracle.scan_minlstm(kz, ki, hv, xv0, lib=lib)
+    mine = oracle.scan_minlstm_backward(kz, ki, hv, xl, gv3, xv0, lib=lib)
+    tf, ti, th, tx = (torch.tensor(z, dtype=torch.float64, requires_grad=True) for z in (kz, ki, hv, xv0))
+    brute.minlstm_torch(tf, ti, th, tx).backward(tg)
+    for m, t in zip(mine, (tf, ti, th, tx)):
+        ok &= np.allclose(m, t.grad.numpy(), rtol=1e-10, atol=1e-11)
+    xd = oracle.scan_real_decay(lam_r, hv, xv0, lib=lib)
+    mine = oracle.scan_real_decay_backward(lam_r, xd, gv3, xv0, lib=lib)
+    tl, tu, tx = (torch.tensor(z, dtype=torch.float64, requires_grad=True) for z in (lam_r, hv, xv0))
+    brute.scan_torch(tl, tu, tx).backward(tg)
+    for m, t in zip(mine, (tl, tu, tx)):
+        ok &= np.allclose(m, t.grad.numpy(), rtol=1e-10, atol=1e-11)
+    lr2 = workloads.make_lru(2, 15, 3, 6, 0.5, 0.99, 2 * math.pi)
+    xn = oracle.scan_complex_normalized(lr2["lam"], lr2["u"], xc0, lib=lib)
+    mine = oracle.scan_complex_normalized_backward(lr2["lam"], lr2["u"], xn, gxc, xc0, lib=lib)
+    tl, tu, tc0 = (torch.tensor(z, dtype=torch.complex128, requires_grad=True) for z in (lr2["lam"], lr2["u"], xc0))
+    brute.lru_normalized_torch(tl, tu, tc0).backward(torch.tensor(gxc, dtype=torch.complex128))
+    for m, t in zip(mine, (tl, tu, tc0)):
+        ok &= np.allclose(m, t.grad.numpy(), rtol=1e-10, atol=1e-11)
     return bool(ok)
 
 
