@@ -18,8 +18,8 @@
  *   linrec_scan_real_backward,    the adjoints (backward passes) of the two scans
  *   linrec_scan_complex_backward
  *   linrec_scan_mingru, _minlstm, gated variants of the real scan (minGRU, minLSTM, one decay
- *   _real_decay                   per channel) and the LRU with normalised input
- *   linrec_scan_complex_normalized
+ *   _real_decay                   per channel) and the LRU with normalised input, and their
+ *   linrec_scan_complex_normalized adjoints (*_backward)
  *
  * Conventions shared by every entry point:
  *  - Pointers are DEVICE pointers (hipMalloc / torch CUDA-on-ROCm memory) unless a
@@ -36,8 +36,9 @@
  *                                                         -> LINREC_ERR_INVALID_ARG
  *      any of B, T, C equal to 0                          -> LINREC_OK, nothing enqueued and
  *        no pointer read, except that the gradient sums over an empty batch or sequence
- *        are zero-filled: gw, gu (wkv4_backward) and glambda (linrec_scan_complex_backward)
- *        when C > 0, and gx0 of the scan backwards when given and B, C > 0
+ *        are zero-filled: gw, gu (wkv4_backward, and gs_in passed through by
+ *        wkv4_backward_ex) and glambda (the complex, real-decay and normalised-LRU
+ *        backwards) when C > 0, and gx0 of the scan backwards when given and B, C > 0
  *      a required pointer NULL (for a non-empty shape)    -> LINREC_ERR_INVALID_ARG
  *      ws_bytes below the workspace size                  -> LINREC_ERR_WORKSPACE
  *      a pointer not aligned to its element size (4 B for float, 8 B for complex64)
@@ -85,7 +86,8 @@ const char *linrec_last_error(void);
 size_t wkv4_forward_workspace_size(int64_t B, int64_t T, int64_t C);
 size_t wkv4_backward_workspace_size(int64_t B, int64_t T, int64_t C);
 /* is_complex: 0 for linrec_scan_real and its gated variants, 1 for linrec_scan_complex and
- * linrec_scan_complex_normalized. */
+ * linrec_scan_complex_normalized; the backward query likewise covers every adjoint of the
+ * family (the plain scan's and its variants'). */
 size_t linrec_scan_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex);
 size_t linrec_scan_backward_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex);
 
@@ -339,6 +341,54 @@ int linrec_scan_complex_backward(int64_t B, int64_t T, int64_t C,
                                  const float *lambda, const float *x0, const float *x,
                                  const float *gx, float *glambda, float *gu, float *gx0,
                                  void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Adjoints of the gated variants (chain rule of their forward forms; the pages give no
+ * backward).  Each runs backwards in time like linrec_scan_real_backward, with the
+ * multiplier a_{t+1} formed from the gates, and d_t = dL/dx_t (all paths):
+ *
+ *   d_t = gx_t + a_{t+1} d_{t+1}                                  (no carry at T-1)
+ *
+ * minGRU (a = 1 - z, z = sigmoid(kz)):
+ *   gkz_t = d_t z_t (1 - z_t) (h~_t - x_{t-1}),  gh_t = d_t z_t,  gx0 = (1 - z_0) d_0
+ * minLSTM (a = f/(f+i), f = sigmoid(kf), i = sigmoid(ki); ga_t = d_t (x_{t-1} - h~_t)):
+ *   gkf_t = ga_t a (1 - a) (1 - f),  gki_t = -ga_t a (1 - a) (1 - i),  gh_t = d_t (1 - a_t),
+ *   gx0 = a_0 d_0
+ * per-channel decay (a = lambda[c]):
+ *   gu_t = d_t,  glambda[c] = sum over b and t of d_t x_{t-1},  gx0 = lambda d_0
+ *
+ * x_{-1} = x0 or 0.  Inputs as for the forward call plus x (B,T,C), the forward's output for
+ * the same inputs, and gx (B,T,C) = dL/dx; outputs (B,T,C) float32 gkz, gh / gkf, gki, gh /
+ * gu; glambda (C) float32 (summed in float64 in a fixed order); gx0 (B,C) or NULL.
+ * Workspace: linrec_scan_backward_workspace_size(B, T, C, 0).  With B or T = 0, glambda and
+ * gx0 are zero-filled.
+ */
+int linrec_scan_mingru_backward(int64_t B, int64_t T, int64_t C, const float *kz, const float *h,
+                                const float *x0, const float *x, const float *gx, float *gkz, float *gh,
+                                float *gx0, void *workspace, size_t ws_bytes, void *stream);
+int linrec_scan_minlstm_backward(int64_t B, int64_t T, int64_t C, const float *kf, const float *ki,
+                                 const float *h, const float *x0, const float *x, const float *gx, float *gkf,
+                                 float *gki, float *gh, float *gx0, void *workspace, size_t ws_bytes,
+                                 void *stream);
+int linrec_scan_real_decay_backward(int64_t B, int64_t T, int64_t C, const float *lambda, const float *x0,
+                                    const float *x, const float *gx, float *glambda, float *gu, float *gx0,
+                                    void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Adjoint of linrec_scan_complex_normalized (complex gradients as dL/dRe + i dL/dIm), with
+ * s_t the adjoint of linrec_scan_complex_backward (s_t = gx_t + conj(lambda) s_{t+1}):
+ *
+ *   gu_t    = gamma s_t,   gx0 = conj(lambda) s_0,
+ *   glambda = sum of s_t conj(x_{t-1}) - (sum of Re(conj(s_t) u_t) / gamma) lambda
+ *
+ * (gamma = sqrt(1 - |lambda|^2); the second term is dL/dgamma times gamma's gradient, taken
+ * as 0 where gamma = 0).  u (B,T,C) complex64 is the forward's input; the rest as
+ * linrec_scan_complex_backward.  Workspace: linrec_scan_backward_workspace_size(B, T, C, 1).
+ */
+int linrec_scan_complex_normalized_backward(int64_t B, int64_t T, int64_t C, const float *lambda,
+                                            const float *u, const float *x0, const float *x,
+                                            const float *gx, float *glambda, float *gu, float *gx0,
+                                            void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

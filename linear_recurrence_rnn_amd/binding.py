@@ -83,9 +83,11 @@ def load(path: str | None = None):
         lib.linrec_scan_complex.argtypes = [_I64, _I64, _I64] + [_VP] * 4 + [_VP, _SZ, _VP]
         lib.linrec_scan_backward_workspace_size.restype = _SZ
         lib.linrec_scan_backward_workspace_size.argtypes = [_I64, _I64, _I64, ctypes.c_int]
-        for name in ("linrec_scan_real_backward", "linrec_scan_complex_backward"):
+        for name, n in (("linrec_scan_real_backward", 7), ("linrec_scan_complex_backward", 7),
+                        ("linrec_scan_mingru_backward", 8), ("linrec_scan_minlstm_backward", 10),
+                        ("linrec_scan_real_decay_backward", 7), ("linrec_scan_complex_normalized_backward", 8)):
             getattr(lib, name).restype = ctypes.c_int
-            getattr(lib, name).argtypes = [_I64, _I64, _I64] + [_VP] * 7 + [_VP, _SZ, _VP]
+            getattr(lib, name).argtypes = [_I64, _I64, _I64] + [_VP] * n + [_VP, _SZ, _VP]
         if path is None:
             _lib = lib
         return lib
@@ -459,4 +461,72 @@ def scan_complex_backward(lam, x, gx, x0=None, want_gx0=None, out=None, workspac
     _check(lib.linrec_scan_complex_backward(B, T, C, _ptr(lam), _ptr(x0), _ptr(x), _ptr(gx), _ptr(glam),
                                             _ptr(gu), _ptr(gx0), _ptr(ws), nws, _stream(dev)),
            "linrec_scan_complex_backward")
+    return glam, gu, gx0
+
+
+def _gated_real_backward(name, ins, n_out, chan, x, gx, x0, want_gx0, workspace):
+    """Marshals a real variant's adjoint: ``ins`` the (B,T,C) gate/candidate inputs, then x,
+    gx; returns the ``n_out`` (B,T,C) gradients, glam (when ``chan`` is given) and gx0."""
+    lib = load()
+    B, T, C = x.shape
+    dev = x.device
+    for nm, t in list(ins) + [("x", x), ("gx", gx)]:
+        _expect(t, nm, torch.float32, (B, T, C), dev)
+    if chan is not None:
+        _expect(chan, "lam", torch.float32, (C,), dev)
+    if x0 is not None:
+        _expect(x0, "x0", torch.float32, (B, C), dev)
+    if want_gx0 is None:
+        want_gx0 = x0 is not None
+    outs = [torch.empty_like(x) for _ in range(n_out)]
+    glam = torch.empty(C, dtype=torch.float32, device=dev) if chan is not None else None
+    gx0 = torch.empty((B, C), dtype=torch.float32, device=dev) if want_gx0 else None
+    ws, nws = _workspace(int(lib.linrec_scan_backward_workspace_size(B, T, C, 0)), dev, workspace)
+    if chan is not None:
+        ptrs = [_ptr(chan), _ptr(x0), _ptr(x), _ptr(gx), _ptr(glam)] + [_ptr(o) for o in outs]
+    else:
+        ptrs = [_ptr(t) for _, t in ins] + [_ptr(x0), _ptr(x), _ptr(gx)] + [_ptr(o) for o in outs]
+    _check(getattr(lib, name)(B, T, C, *ptrs, _ptr(gx0), _ptr(ws), nws, _stream(dev)), name)
+    return tuple(outs) + ((glam,) if chan is not None else ()) + (gx0,)
+
+
+def scan_mingru_backward(kz, h, x, gx, x0=None, want_gx0=None, workspace=None):
+    """(gkz, gh, gx0) of minGRU for dL/dx = gx, given its forward output x."""
+    return _gated_real_backward("linrec_scan_mingru_backward", [("kz", kz), ("h", h)], 2, None, x, gx, x0, want_gx0,
+                                workspace)
+
+
+def scan_minlstm_backward(kf, ki, h, x, gx, x0=None, want_gx0=None, workspace=None):
+    """(gkf, gki, gh, gx0) of minLSTM for dL/dx = gx, given its forward output x."""
+    return _gated_real_backward("linrec_scan_minlstm_backward", [("kf", kf), ("ki", ki), ("h", h)], 3, None, x, gx,
+                                x0, want_gx0, workspace)
+
+
+def scan_real_decay_backward(lam, x, gx, x0=None, want_gx0=None, workspace=None):
+    """(glam (C,), gu, gx0) of x_t = lam_c x_{t-1} + u_t for dL/dx = gx, given x."""
+    gu, glam, gx0 = _gated_real_backward("linrec_scan_real_decay_backward", [], 1, lam, x, gx, x0, want_gx0,
+                                         workspace)
+    return glam, gu, gx0
+
+
+def scan_complex_normalized_backward(lam, u, x, gx, x0=None, want_gx0=None, workspace=None):
+    """(glam, gu, gx0) of x_t = lam x_{t-1} + sqrt(1 - |lam|^2) u_t for dL/dx = gx (complex
+    gradients as dL/dRe + i dL/dIm), given the input u and the forward output x."""
+    lib = load()
+    B, T, C = x.shape
+    dev = x.device
+    for name, t in (("u", u), ("x", x), ("gx", gx)):
+        _expect(t, name, torch.complex64, (B, T, C), dev)
+    _expect(lam, "lam", torch.complex64, (C,), dev)
+    if x0 is not None:
+        _expect(x0, "x0", torch.complex64, (B, C), dev)
+    if want_gx0 is None:
+        want_gx0 = x0 is not None
+    glam = torch.empty(C, dtype=torch.complex64, device=dev)
+    gu = torch.empty_like(x)
+    gx0 = torch.empty((B, C), dtype=torch.complex64, device=dev) if want_gx0 else None
+    ws, nws = _workspace(int(lib.linrec_scan_backward_workspace_size(B, T, C, 1)), dev, workspace)
+    _check(lib.linrec_scan_complex_normalized_backward(B, T, C, _ptr(lam), _ptr(u), _ptr(x0), _ptr(x), _ptr(gx),
+                                                       _ptr(glam), _ptr(gu), _ptr(gx0), _ptr(ws), nws, _stream(dev)),
+           "linrec_scan_complex_normalized_backward")
     return glam, gu, gx0

@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <atomic>
 #include <initializer_list>
 #include <random>
@@ -76,7 +77,9 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
                kind == linrec::kKindRealDecay) {
         p.nw = 8;
         p.L = 16;
-    } else if (kind == linrec::kKindRealBwd) {
+    } else if (kind == linrec::kKindRealBwd || kind == linrec::kKindMinGruBwd || kind == linrec::kKindMinLstmBwd ||
+               kind == linrec::kKindRealDecayBwd || kind == linrec::kKindComplexNormBwd) {
+        // The normalised LRU's adjoint also holds u per step: 32-step chunks would spill.
         p.nw = 8;
         p.L = 16;
     } else {
@@ -90,7 +93,7 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
     // chunks hold many registers and whose long chains lean on the inclusive prefixes
     // (LINREC_COORD: 1 wave 0, 2 own wave).
     p.sep = vec == 1 && (kind == linrec::kKindComplex || kind == linrec::kKindComplexBwd ||
-                         kind == linrec::kKindComplexNorm);
+                         kind == linrec::kKindComplexNorm || kind == linrec::kKindComplexNormBwd);
     const int64_t coord = env_int("LINREC_COORD", 0);
     if (coord == 1 || coord == 2) p.sep = vec == 1 && coord == 2;
     const int nw = (int)env_int("LINREC_NW", 0), L = (int)env_int("LINREC_L", 0);
@@ -103,14 +106,14 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
     p.ws_bytes = 0;
     if (p.nslab > 1)
         p.ws_bytes = align256((size_t)nwg * 8) + 2 * align256((size_t)(nwg * cw) * linrec::agg_bytes(kind));
-    if (kind == linrec::kKindComplexBwd)  // per-slab glam sums and their first-stage sums
+    if (linrec::has_parts(kind))  // per-slab glam sums and their first-stage sums
         p.ws_bytes += align256((size_t)(nwg * cw) * 16) +
                       align256((size_t)(ceil_div(p.nslab, linrec::kPartBlock) * C) * 16);
     return p;
 }
 
 int vmax_of(int kind) {
-    if (kind == linrec::kKindRealBwd || kind == linrec::kKindComplexBwd) return 1;
+    if (linrec::is_bwd_kind(kind)) return 1;
     return (kind == linrec::kKindWkv || kind == linrec::kKindReal) ? 4 : 2;
 }
 
@@ -189,7 +192,7 @@ linrec::ScanGeom geom_of(int kind, const linrec::ScanPlan& p, int64_t B, int64_t
     char* after = (char*)g.rec_incl + align256((size_t)(nwg * cw) * linrec::agg_bytes(kind));
     if (p.nslab <= 1) g.flags = nullptr, g.rec_agg = g.rec_incl = nullptr, after = (char*)ws;
     g.part = g.part2 = nullptr;
-    if (kind == linrec::kKindComplexBwd) {
+    if (linrec::has_parts(kind)) {
         g.part = reinterpret_cast<double*>(after);
         g.part2 = reinterpret_cast<double*>(after + align256((size_t)(nwg * cw) * 16));
     }
@@ -238,7 +241,17 @@ LINREC_API size_t linrec_scan_workspace_size(int64_t B, int64_t T, int64_t C, in
 
 LINREC_API size_t linrec_scan_backward_workspace_size(int64_t B, int64_t T, int64_t C, int is_complex) {
     if (B < 0 || T < 0 || C < 0 || B == 0 || T == 0 || C == 0) return 0;
-    return scan_ws_bytes(is_complex ? linrec::kKindComplexBwd : linrec::kKindRealBwd, B, T, C);
+    // Enough for every adjoint of the family (the plain scan's and its variants').
+    size_t best = 0;
+    const int real_kinds[] = {linrec::kKindRealBwd, linrec::kKindMinGruBwd, linrec::kKindMinLstmBwd,
+                              linrec::kKindRealDecayBwd};
+    const int cplx_kinds[] = {linrec::kKindComplexBwd, linrec::kKindComplexNormBwd};
+    if (is_complex) {
+        for (int k : cplx_kinds) best = std::max(best, scan_ws_bytes(k, B, T, C));
+    } else {
+        for (int k : real_kinds) best = std::max(best, scan_ws_bytes(k, B, T, C));
+    }
+    return best;
 }
 
 LINREC_API size_t wkv4_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
@@ -529,6 +542,103 @@ LINREC_API int linrec_scan_complex_backward(int64_t B, int64_t T, int64_t C, con
     return hip_status(linrec::run_scan_complex_backward(A, glambda, geom_of(linrec::kKindComplexBwd, p, B, T, C, workspace),
                                                         p, (hipStream_t)stream),
                       "linrec_scan_complex_backward launch");
+}
+
+namespace {
+
+// Shared checks and launch of the real variants' adjoints: `ins` are the (B,T,C) inputs,
+// `outs` the (B,T,C) outputs; gx0 (B,C) optional.  With T = 0 only gx0 (zero) and glam
+// (zero, real decay) are written.
+template <class Args, class Run>
+int gated_real_backward(const char* name, int kind, int64_t B, int64_t T, int64_t C,
+                        std::initializer_list<const float*> ins, std::initializer_list<float*> outs,
+                        const float* x0, float* gx0, float* glam, void* workspace, size_t ws_bytes, void* stream,
+                        const Args& A, Run run) {
+    int st = check_shape(B, T, C, 4);
+    if (st) return st;
+    if (C == 0) return ok();
+    if (kind == linrec::kKindRealDecayBwd && !glam) return fail(LINREC_ERR_INVALID_ARG, "glambda is NULL");
+    if ((gx0 && !aligned(gx0, 4)) || (glam && !aligned(glam, 4)))
+        return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    if (B == 0 || T == 0) {
+        // Empty sums: glambda = 0, and the gradient of the initial state is zero.
+        hipError_t e = hipSuccess;
+        if (glam) e = linrec::run_fill_zero(glam, C, (hipStream_t)stream);
+        if (e == hipSuccess && gx0 && B > 0) e = linrec::run_fill_zero(gx0, B * C, (hipStream_t)stream);
+        return hip_status(e, name);
+    }
+    for (const float* p : ins)
+        if (!p) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    for (const float* p : outs)
+        if (!p) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    for (const float* p : ins)
+        if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    for (const float* p : outs)
+        if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    if (x0 && !aligned(x0, 4)) return fail(LINREC_ERR_UNSUPPORTED, "x0 not 4-byte aligned");
+    const linrec::ScanPlan p = scan_plan(kind, 1, B, T, C);
+    if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
+    return hip_status(run(A, geom_of(kind, p, B, T, C, workspace), p, (hipStream_t)stream), name);
+}
+
+}  // namespace
+
+LINREC_API int linrec_scan_mingru_backward(int64_t B, int64_t T, int64_t C, const float* kz, const float* h,
+                                           const float* x0, const float* x, const float* gx, float* gkz, float* gh,
+                                           float* gx0, void* workspace, size_t ws_bytes, void* stream) {
+    const linrec::MinGruBwdArgs A{kz, h, x0, x, gx, gkz, gh, gx0};
+    return gated_real_backward("linrec_scan_mingru_backward launch", linrec::kKindMinGruBwd, B, T, C, {kz, h, x, gx},
+                               {gkz, gh}, x0, gx0, nullptr, workspace, ws_bytes, stream, A,
+                               linrec::run_scan_mingru_backward);
+}
+
+LINREC_API int linrec_scan_minlstm_backward(int64_t B, int64_t T, int64_t C, const float* kf, const float* ki,
+                                            const float* h, const float* x0, const float* x, const float* gx,
+                                            float* gkf, float* gki, float* gh, float* gx0, void* workspace,
+                                            size_t ws_bytes, void* stream) {
+    const linrec::MinLstmBwdArgs A{kf, ki, h, x0, x, gx, gkf, gki, gh, gx0};
+    return gated_real_backward("linrec_scan_minlstm_backward launch", linrec::kKindMinLstmBwd, B, T, C,
+                               {kf, ki, h, x, gx}, {gkf, gki, gh}, x0, gx0, nullptr, workspace, ws_bytes, stream, A,
+                               linrec::run_scan_minlstm_backward);
+}
+
+LINREC_API int linrec_scan_real_decay_backward(int64_t B, int64_t T, int64_t C, const float* lambda, const float* x0,
+                                               const float* x, const float* gx, float* glambda, float* gu, float* gx0,
+                                               void* workspace, size_t ws_bytes, void* stream) {
+    const linrec::RealDecayBwdArgs A{lambda, x0, x, gx, gu, gx0};
+    auto run = [glambda](const linrec::RealDecayBwdArgs& a, const linrec::ScanGeom& g, const linrec::ScanPlan& p,
+                         hipStream_t st) { return linrec::run_scan_real_decay_backward(a, glambda, g, p, st); };
+    return gated_real_backward("linrec_scan_real_decay_backward launch", linrec::kKindRealDecayBwd, B, T, C,
+                               {lambda, x, gx}, {gu}, x0, gx0, glambda, workspace, ws_bytes, stream, A, run);
+}
+
+LINREC_API int linrec_scan_complex_normalized_backward(int64_t B, int64_t T, int64_t C, const float* lambda,
+                                                       const float* u, const float* x0, const float* x,
+                                                       const float* gx, float* glambda, float* gu, float* gx0,
+                                                       void* workspace, size_t ws_bytes, void* stream) {
+    int st = check_shape(B, T, C, 8);
+    if (st) return st;
+    if (C == 0) return ok();
+    if (!glambda) return fail(LINREC_ERR_INVALID_ARG, "glambda is NULL");
+    if (!aligned(glambda, 8) || (gx0 && !aligned(gx0, 8)))
+        return fail(LINREC_ERR_UNSUPPORTED, "complex64 pointer not 8-byte aligned");
+    if (B == 0 || T == 0) {
+        hipError_t e = linrec::run_fill_zero(glambda, 2 * C, (hipStream_t)stream);
+        if (e == hipSuccess && gx0 && B > 0) e = linrec::run_fill_zero(gx0, 2 * B * C, (hipStream_t)stream);
+        return hip_status(e, "linrec_scan_complex_normalized_backward zero-fill");
+    }
+    if (!lambda || !u || !x || !gx || !gu) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void* ptrs[] = {lambda, u, x, gx, gu};
+    for (const void* p : ptrs)
+        if (!aligned(p, 8)) return fail(LINREC_ERR_UNSUPPORTED, "complex64 pointer not 8-byte aligned");
+    if (x0 && !aligned(x0, 8)) return fail(LINREC_ERR_UNSUPPORTED, "x0 not 8-byte aligned");
+    const linrec::ScanPlan p = scan_plan(linrec::kKindComplexNormBwd, 1, B, T, C);
+    if ((st = check_ws(workspace, ws_bytes, p.ws_bytes))) return st;
+    const linrec::CplxBwdArgs A{lambda, x0, x, gx, gu, gx0, u};
+    return hip_status(linrec::run_scan_complex_normalized_backward(
+                          A, glambda, geom_of(linrec::kKindComplexNormBwd, p, B, T, C, workspace), p,
+                          (hipStream_t)stream),
+                      "linrec_scan_complex_normalized_backward launch");
 }
 
 LINREC_API int wkv4_backward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float* u,

@@ -53,8 +53,10 @@ __global__ __launch_bounds__(64) void part_sum_kernel(ScanGeom g) {
     g.part2[2 * (k * g.C + c) + 1] = im;
 }
 
-// glam, second stage: the first-stage sums of a channel, in order, as complex64.
-__global__ __launch_bounds__(256) void part_final_kernel(ScanGeom g, int64_t nk, float* __restrict__ glam) {
+// glam, second stage: the first-stage sums of a channel, in order, as complex64 (or the
+// real part alone as float32).
+__global__ __launch_bounds__(256) void part_final_kernel(ScanGeom g, int64_t nk, float* __restrict__ glam,
+                                                         bool complex_out) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= g.C) return;
     double re = 0.0, im = 0.0;
@@ -62,14 +64,18 @@ __global__ __launch_bounds__(256) void part_final_kernel(ScanGeom g, int64_t nk,
         re += g.part2[2 * (k * g.C + c)];
         im += g.part2[2 * (k * g.C + c) + 1];
     }
-    glam[2 * c] = (float)re;
-    glam[2 * c + 1] = (float)im;
+    if (complex_out) {
+        glam[2 * c] = (float)re;
+        glam[2 * c + 1] = (float)im;
+    } else {
+        glam[c] = (float)re;
+    }
 }
 
 }  // namespace
 
 bool scan_shape_supported(int kind, int vec, int nw, int L) {
-    const int vmax = (kind == kKindRealBwd || kind == kKindComplexBwd) ? 1 : ((kind == kKindWkv || kind == kKindReal) ? 4 : 2);
+    const int vmax = is_bwd_kind(kind) ? 1 : ((kind == kKindWkv || kind == kKindReal) ? 4 : 2);
     const bool vec_ok = vec == vmax || (vec == 2 && vmax >= 2) || vec == 1;
     return vec_ok && ((nw == 4 && L == 16) || (nw == 8 && L == 8) || (nw == 8 && L == 16) ||
                       (kind != kKindWkv && vec == 1 && nw == 8 && L == 32));
@@ -94,12 +100,17 @@ hipError_t run_scan_real_backward(const RealBwdArgs& A, const ScanGeom& g, const
 hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const ScanGeom& g, const ScanPlan& p,
                                      hipStream_t st) {
     if (p.vec != 1) return hipErrorInvalidValue;
-    hipError_t e = dispatch_shape<CplxBwdOp, 1>(A, g, p, st);
-    if (e != hipSuccess) return e;
+    const hipError_t e = dispatch_shape<CplxBwdOp, 1>(A, g, p, st);
+    return e != hipSuccess ? e : run_part_sums(g, glam, true, st);
+}
+
+hipError_t run_part_sums(const ScanGeom& g, float* glam, bool complex_out, hipStream_t st) {
     const int64_t nk = (g.nslab + kPartBlock - 1) / kPartBlock;
     hipLaunchKernelGGL(part_sum_kernel, dim3((unsigned)g.ngrp, (unsigned)nk), dim3(64), 0, st, g);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(part_final_kernel, dim3((unsigned)((g.C + 255) / 256)), dim3(256), 0, st, g, nk, glam);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(part_final_kernel, dim3((unsigned)((g.C + 255) / 256)), dim3(256), 0, st, g, nk, glam,
+                       complex_out);
     return hipGetLastError();
 }
 
@@ -128,8 +139,11 @@ size_t agg_bytes(int kind) {
         case kKindReal:
         case kKindRealBwd:
         case kKindMinGru:
-        case kKindMinLstm: return sizeof(RealOp::Agg);
-        case kKindRealDecay: return sizeof(RealDecayOp::Agg);
+        case kKindMinLstm:
+        case kKindMinGruBwd:
+        case kKindMinLstmBwd: return sizeof(RealOp::Agg);
+        case kKindRealDecay:
+        case kKindRealDecayBwd: return sizeof(RealDecayOp::Agg);
         default: return sizeof(CplxOp::Agg);
     }
 }

@@ -8,7 +8,17 @@
 namespace linrec {
 
 enum { kKindWkv = 0, kKindReal = 1, kKindComplex = 2, kKindRealBwd = 3, kKindComplexBwd = 4,
-       kKindMinGru = 5, kKindMinLstm = 6, kKindRealDecay = 7, kKindComplexNorm = 8 };
+       kKindMinGru = 5, kKindMinLstm = 6, kKindRealDecay = 7, kKindComplexNorm = 8,
+       kKindMinGruBwd = 9, kKindMinLstmBwd = 10, kKindRealDecayBwd = 11, kKindComplexNormBwd = 12 };
+
+// Kinds of the reverse-time adjoints (one channel per lane).
+inline bool is_bwd_kind(int kind) {
+    return kind == kKindRealBwd || kind == kKindComplexBwd || kind >= kKindMinGruBwd;
+}
+// Kinds whose adjoint sums a per-channel gradient over batch and time (glambda).
+inline bool has_parts(int kind) {
+    return kind == kKindComplexBwd || kind == kKindRealDecayBwd || kind == kKindComplexNormBwd;
+}
 
 // Operands of each recurrence (device pointers, (B,T,C) row-major, C fastest).
 struct WkvArgs {
@@ -71,6 +81,38 @@ struct CplxBwdArgs {
     const float* gx;   // (B,T,C) complex64 dL/dx
     float* gu;         // (B,T,C) complex64
     float* gx0;        // (B,C) complex64 or null
+    const float* u;    // (B,T,C) complex64 input (normalised LRU only: dL/dgamma), else null
+};
+// Adjoints of the gated variants.
+struct MinGruBwdArgs {
+    const float* kz;  // (B,T,C)
+    const float* h;   // (B,T,C)
+    const float* x0;  // (B,C) or null
+    const float* x;   // (B,T,C) forward output
+    const float* gx;  // (B,T,C) dL/dx
+    float* gkz;       // (B,T,C)
+    float* gh;        // (B,T,C)
+    float* gx0;       // (B,C) or null
+};
+struct MinLstmBwdArgs {
+    const float* kf;  // (B,T,C)
+    const float* ki;  // (B,T,C)
+    const float* h;   // (B,T,C)
+    const float* x0;  // (B,C) or null
+    const float* x;   // (B,T,C) forward output
+    const float* gx;  // (B,T,C) dL/dx
+    float* gkf;       // (B,T,C)
+    float* gki;       // (B,T,C)
+    float* gh;        // (B,T,C)
+    float* gx0;       // (B,C) or null
+};
+struct RealDecayBwdArgs {
+    const float* lam;  // (C)
+    const float* x0;   // (B,C) or null
+    const float* x;    // (B,T,C) forward output
+    const float* gx;   // (B,T,C) dL/dx
+    float* gu;         // (B,T,C)
+    float* gx0;        // (B,C) or null
 };
 
 // Addressing of a run of consecutive steps (a chunk, or a slab being recomputed): logical
@@ -119,6 +161,17 @@ hipError_t run_scan_minlstm(const MinLstmArgs& A, const ScanGeom& g, const ScanP
 hipError_t run_scan_real_decay(const RealDecayArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
 hipError_t run_scan_complex_normalized(const CplxArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
 hipError_t run_scan_real_backward(const RealBwdArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
+hipError_t run_scan_mingru_backward(const MinGruBwdArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
+hipError_t run_scan_minlstm_backward(const MinLstmBwdArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st);
+// Also sums the per-slab shares of dL/dlam into glam (C float32).
+hipError_t run_scan_real_decay_backward(const RealDecayBwdArgs& A, float* glam, const ScanGeom& g, const ScanPlan& p,
+                                        hipStream_t st);
+// As run_scan_complex_backward, with A.u the input scaled by gamma.
+hipError_t run_scan_complex_normalized_backward(const CplxBwdArgs& A, float* glam, const ScanGeom& g,
+                                                const ScanPlan& p, hipStream_t st);
+// Sums g.part (per-slab shares, pairs) over slabs and batch rows into glam: C complex64
+// (`complex_out`) or C float32 (the first of each pair).
+hipError_t run_part_sums(const ScanGeom& g, float* glam, bool complex_out, hipStream_t st);
 // Also sums g.part into glam (C complex64): g.part2 holds ceil(nslab / kPartBlock) x C pairs.
 hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const ScanGeom& g, const ScanPlan& p,
                                      hipStream_t st);

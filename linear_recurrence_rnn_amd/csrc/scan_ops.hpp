@@ -819,4 +819,306 @@ struct CplxNormOp : CplxOp {
     }
 };
 
+// ----------------------------------------------------------------------------------
+// Adjoints of the gated variants (chain rule of the forward readings; the pages give no
+// backward).  Backwards in time each is the real (or complex) scan's adjoint whose
+// multiplier is formed from the gates as the step is loaded; the step's own gate
+// derivatives are taken where the adjoint state d_t is formed, with h_{t-1} read from the
+// forward output (x0 at t = 0).
+// ----------------------------------------------------------------------------------
+
+// Buffers shared by the real adjoints: the row above (t+1) of the multiplier's inputs, the
+// row itself, the row below of x.  xshift as in RealBwdOp.
+struct BwdRows {
+    __device__ __forceinline__ static int64_t above(const ScanGeom& g, int64_t base) { return base + g.C; }
+    __device__ __forceinline__ static int64_t below(const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        return (b * g.T + (row > 0 ? row - 1 : 0)) * g.C + col0;
+    }
+};
+
+// minGRU: d_t = gx_t + sigmoid(-kz_{t+1}) d_{t+1};  dL/dkz_t = d_t z_t (1 - z_t) (h~_t - h_{t-1}),
+// dL/dh~_t = d_t z_t, dL/dx0 = (1 - z_0) d_0.
+struct MinGruBwdOp : RealOp {
+    using Args = MinGruBwdArgs;
+    static constexpr bool kReverse = true;
+    template <int L>
+    __device__ __forceinline__ static Chan chan(const Args&, int64_t) { return {}; }
+    __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) { return identity(); }
+
+    struct Res { rsrc_t kn, g, k, h, xp, gk, gh; unsigned xshift; int64_t T; const float* x0; float* gx0; };
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t total = g.B * g.T * g.C;
+        const int64_t base = (b * g.T + row) * g.C + col0;
+        const int64_t bn = BwdRows::above(g, base), bp = BwdRows::below(g, b, row, col0);
+        Res R;
+        R.kn = make_rsrc(A.kz + bn, (total - bn) * 4);
+        R.g = make_rsrc(A.gx + base, (total - base) * 4);
+        R.k = make_rsrc(A.kz + base, (total - base) * 4);
+        R.h = make_rsrc(A.h + base, (total - base) * 4);
+        R.xp = make_rsrc(A.x + bp, (total - bp) * 4);
+        R.gk = make_rsrc(A.gkz + base, (total - base) * 4);
+        R.gh = make_rsrc(A.gh + base, (total - base) * 4);
+        R.xshift = row > 0 ? 0u : (unsigned)(g.C * 4);
+        R.T = g.T;
+        R.x0 = A.x0 ? A.x0 + b * g.C + col0 : nullptr;
+        R.gx0 = A.gx0 ? A.gx0 + b * g.C + col0 : nullptr;
+        return R;
+    }
+    template <int VEC>
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const bool last = rows.t(j) + 1 >= R.T;
+        FV<VEC> kn{};
+        if (!last) kn = ldb<VEC>(R.kn, voff, rows.soff(j));
+        const FV<VEC> gx = ldb<VEC>(R.g, voff, rows.soff(j));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {last ? 0.f : sigmoidf(-kn.v[e]), gx.v[e]};
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&)[VEC], const Agg (&cin)[VEC],
+                                               const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
+                                               const Rows& rows) {
+        static_assert(VEC == 1, "the adjoints keep one channel per lane");
+        const int lane_col = (int)(voff / 4);
+        float xp[L], kz[L], hh[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                xp[j] = rows.t(j) > 0 ? ldb<1>(R.xp, voff, rows.soff(j) - R.xshift).v[0]
+                                      : (R.x0 ? R.x0[lane_col] : 0.f);
+                kz[j] = ldb<1>(R.k, voff, rows.soff(j)).v[0];
+                hh[j] = ldb<1>(R.h, voff, rows.soff(j)).v[0];
+            }
+        }
+        float d = cin[0].x;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                d = fmaf(in[j][0].a, d, in[j][0].b);
+                const float z = sigmoidf(kz[j]), zc = sigmoidf(-kz[j]);
+                FV<1> gk, gh;
+                gk.v[0] = d * (z * zc) * (hh[j] - xp[j]);
+                gh.v[0] = d * z;
+                stb<1>(R.gk, voff, rows.soff(j), gk);
+                stb<1>(R.gh, voff, rows.soff(j), gh);
+                if (rows.t(j) == 0 && R.gx0) R.gx0[lane_col] = zc * d;
+            }
+        }
+        return {};
+    }
+};
+
+// minLSTM: with a = sigmoid(dd), dd = softplus(-ki) - softplus(-kf) (the weight f/(f+i) of
+// h_{t-1}), d_t = gx_t + a_{t+1} d_{t+1};  g_dd = a (1 - a) d_t (h_{t-1} - h~_t),
+// dL/dkf = g_dd sigmoid(-kf), dL/dki = -g_dd sigmoid(-ki), dL/dh~_t = d_t (1 - a_t),
+// dL/dx0 = a_0 d_0.
+struct MinLstmBwdOp : RealOp {
+    using Args = MinLstmBwdArgs;
+    static constexpr bool kReverse = true;
+    template <int L>
+    __device__ __forceinline__ static Chan chan(const Args&, int64_t) { return {}; }
+    __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) { return identity(); }
+
+    struct Res { rsrc_t fn, in_, g, f, i, h, xp, gf, gi, gh; unsigned xshift; int64_t T; const float* x0; float* gx0; };
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t total = g.B * g.T * g.C;
+        const int64_t base = (b * g.T + row) * g.C + col0;
+        const int64_t bn = BwdRows::above(g, base), bp = BwdRows::below(g, b, row, col0);
+        Res R;
+        R.fn = make_rsrc(A.kf + bn, (total - bn) * 4);
+        R.in_ = make_rsrc(A.ki + bn, (total - bn) * 4);
+        R.g = make_rsrc(A.gx + base, (total - base) * 4);
+        R.f = make_rsrc(A.kf + base, (total - base) * 4);
+        R.i = make_rsrc(A.ki + base, (total - base) * 4);
+        R.h = make_rsrc(A.h + base, (total - base) * 4);
+        R.xp = make_rsrc(A.x + bp, (total - bp) * 4);
+        R.gf = make_rsrc(A.gkf + base, (total - base) * 4);
+        R.gi = make_rsrc(A.gki + base, (total - base) * 4);
+        R.gh = make_rsrc(A.gh + base, (total - base) * 4);
+        R.xshift = row > 0 ? 0u : (unsigned)(g.C * 4);
+        R.T = g.T;
+        R.x0 = A.x0 ? A.x0 + b * g.C + col0 : nullptr;
+        R.gx0 = A.gx0 ? A.gx0 + b * g.C + col0 : nullptr;
+        return R;
+    }
+    __device__ __forceinline__ static float logit(float kf, float ki) { return softplusf(-ki) - softplusf(-kf); }
+    template <int VEC>
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const bool last = rows.t(j) + 1 >= R.T;
+        FV<VEC> fn{}, inn{};
+        if (!last) {
+            fn = ldb<VEC>(R.fn, voff, rows.soff(j));
+            inn = ldb<VEC>(R.in_, voff, rows.soff(j));
+        }
+        const FV<VEC> gx = ldb<VEC>(R.g, voff, rows.soff(j));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {last ? 0.f : sigmoidf(logit(fn.v[e], inn.v[e])), gx.v[e]};
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&)[VEC], const Agg (&cin)[VEC],
+                                               const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
+                                               const Rows& rows) {
+        static_assert(VEC == 1, "the adjoints keep one channel per lane");
+        const int lane_col = (int)(voff / 4);
+        float xp[L], kf[L], ki[L], hh[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                xp[j] = rows.t(j) > 0 ? ldb<1>(R.xp, voff, rows.soff(j) - R.xshift).v[0]
+                                      : (R.x0 ? R.x0[lane_col] : 0.f);
+                kf[j] = ldb<1>(R.f, voff, rows.soff(j)).v[0];
+                ki[j] = ldb<1>(R.i, voff, rows.soff(j)).v[0];
+                hh[j] = ldb<1>(R.h, voff, rows.soff(j)).v[0];
+            }
+        }
+        float d = cin[0].x;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                d = fmaf(in[j][0].a, d, in[j][0].b);
+                const float dd = logit(kf[j], ki[j]);
+                const float a = sigmoidf(dd), ac = sigmoidf(-dd);
+                const float gdd = (a * ac) * d * (xp[j] - hh[j]);
+                FV<1> gf, gi, gh;
+                gf.v[0] = gdd * sigmoidf(-kf[j]);
+                gi.v[0] = -gdd * sigmoidf(-ki[j]);
+                gh.v[0] = d * ac;
+                stb<1>(R.gf, voff, rows.soff(j), gf);
+                stb<1>(R.gi, voff, rows.soff(j), gi);
+                stb<1>(R.gh, voff, rows.soff(j), gh);
+                if (rows.t(j) == 0 && R.gx0) R.gx0[lane_col] = a * d;
+            }
+        }
+        return {};
+    }
+};
+
+// The per-channel decay: d_t = gx_t + lam d_{t+1};  dL/du_t = d_t, dL/dlam = sum over batch
+// and time of d_t x_{t-1} (a per-slab share, summed like the complex adjoint's),
+// dL/dx0 = lam d_0.
+struct RealDecayBwdOp : RealDecayOp {
+    using Args = RealDecayBwdArgs;
+    static constexpr bool kReverse = true;
+    static constexpr bool kParts = true;
+    struct Part { double re, im; };
+    template <int L>
+    __device__ __forceinline__ static Chan chan(const Args& A, int64_t c) { return {A.lam[c]}; }
+    __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) { return identity(); }
+
+    struct Res { rsrc_t g, xp, gu; unsigned xshift; const float* x0; float* gx0; };
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        const int64_t total = g.B * g.T * g.C;
+        const int64_t base = (b * g.T + row) * g.C + col0, bp = BwdRows::below(g, b, row, col0);
+        Res R;
+        R.g = make_rsrc(A.gx + base, (total - base) * 4);
+        R.xp = make_rsrc(A.x + bp, (total - bp) * 4);
+        R.gu = make_rsrc(A.gu + base, (total - base) * 4);
+        R.xshift = row > 0 ? 0u : (unsigned)(g.C * 4);
+        R.x0 = A.x0 ? A.x0 + b * g.C + col0 : nullptr;
+        R.gx0 = A.gx0 ? A.gx0 + b * g.C + col0 : nullptr;
+        return R;
+    }
+    template <int VEC>
+    __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
+        const FV<VEC> gx = ldb<VEC>(R.g, voff, rows.soff(j));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {gx.v[e]};
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                                               const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
+                                               const Rows& rows) {
+        static_assert(VEC == 1, "the adjoints keep one channel per lane");
+        const int lane_col = (int)(voff / 4);
+        float xp[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                xp[j] = rows.t(j) > 0 ? ldb<1>(R.xp, voff, rows.soff(j) - R.xshift).v[0]
+                                      : (R.x0 ? R.x0[lane_col] : 0.f);
+            }
+        }
+        float d = cin[0].x, acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                d = fmaf(ch[0].lam, d, in[j][0].u);
+                FV<1> o;
+                o.v[0] = d;
+                stb<1>(R.gu, voff, rows.soff(j), o);
+                acc = fmaf(d, xp[j], acc);
+                if (rows.t(j) == 0 && R.gx0) R.gx0[lane_col] = ch[0].lam * d;
+            }
+        }
+        return {(double)acc, 0.0};
+    }
+};
+
+// The normalised LRU: s_t = gx_t + conj(lam) s_{t+1};  dL/du_t = gamma s_t,
+// dL/dx0 = conj(lam) s_0, and dL/dlam = sum of s_t conj(x_{t-1}) + kg Re(conj(s_t) u_t) with
+// kg = -lam / gamma (dgamma/dRe + i dgamma/dIm, times 1/dL/dgamma's own sum), 0 where gamma = 0.
+struct CplxNormBwdOp : CplxBwdOp {
+    struct Chan : CplxBwdOp::Chan { float gamma, kgr, kgi; };
+    template <int L>
+    __device__ __forceinline__ static Chan chan(const Args& A, int64_t c) {
+        Chan ch;
+        static_cast<CplxBwdOp::Chan&>(ch) = CplxBwdOp::template chan<L>(A, c);
+        const double lr = A.lam[2 * c], li = A.lam[2 * c + 1];
+        const double gam = sqrt(fmax(0.0, 1.0 - (lr * lr + li * li)));
+        ch.gamma = (float)gam;
+        ch.kgr = gam > 0.0 ? (float)(-lr / gam) : 0.f;
+        ch.kgi = gam > 0.0 ? (float)(-li / gam) : 0.f;
+        return ch;
+    }
+    struct Res : CplxBwdOp::Res { rsrc_t u; };
+    __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
+        Res R;
+        static_cast<CplxBwdOp::Res&>(R) = CplxBwdOp::res(A, g, b, row, col0);
+        const int64_t total = g.B * g.T * g.C;
+        const int64_t base = (b * g.T + row) * g.C + col0;
+        R.u = make_rsrc(A.u + 2 * base, (total - base) * 8);
+        return R;
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Part run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
+                                               const In (&in)[L][VEC], const Local (&)[VEC], int n, unsigned voff,
+                                               const Rows& rows) {
+        static_assert(VEC == 1, "the adjoint of the complex scan keeps one channel per lane");
+        const int lane_col = (int)(voff / 8);
+        FV<2> xp[L], uu[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                if (rows.t(j) > 0) {
+                    xp[j] = ldb<2>(R.xp, voff, rows.soff(j) - R.xshift);
+                } else {
+                    xp[j].v[0] = R.x0 ? R.x0[2 * lane_col] : 0.f;
+                    xp[j].v[1] = R.x0 ? R.x0[2 * lane_col + 1] : 0.f;
+                }
+                uu[j] = ldb<2>(R.u, voff, rows.soff(j));
+            }
+        }
+        float sr = cin[0].xr, si = cin[0].xi, ar = 0.f, ai = 0.f, dg = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                const float tr = fmaf(ch[0].lr, sr, fmaf(-ch[0].li, si, in[j][0].r));
+                si = fmaf(ch[0].lr, si, fmaf(ch[0].li, sr, in[j][0].i));
+                sr = tr;
+                FV<2> o;
+                o.v[0] = ch[0].gamma * sr;
+                o.v[1] = ch[0].gamma * si;
+                stb<2>(R.gu, voff, rows.soff(j), o);
+                ar = fmaf(sr, xp[j].v[0], fmaf(si, xp[j].v[1], ar));  // s conj(x): real part
+                ai = fmaf(si, xp[j].v[0], fmaf(-sr, xp[j].v[1], ai));  // imaginary part
+                dg = fmaf(sr, uu[j].v[0], fmaf(si, uu[j].v[1], dg));   // Re(conj(s) u)
+                if (rows.t(j) == 0 && R.gx0) {
+                    R.gx0[2 * lane_col] = ch[0].lr * sr - ch[0].li * si;
+                    R.gx0[2 * lane_col + 1] = ch[0].lr * si + ch[0].li * sr;
+                }
+            }
+        }
+        return {(double)fmaf(ch[0].kgr, dg, ar), (double)fmaf(ch[0].kgi, dg, ai)};
+    }
+};
+
 }  // namespace linrec

@@ -19,4 +19,26 @@ hipError_t run_scan_complex_normalized(const CplxArgs& A, const ScanGeom& g, con
     return scan_kernel::dispatch<CplxNormOp, 2>(A, g, p, st);
 }
 
+// The adjoints keep one channel per lane (their steps also hold x_{t-1} and the gates).
+hipError_t run_scan_mingru_backward(const MinGruBwdArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st) {
+    if (p.vec != 1) return hipErrorInvalidValue;
+    return scan_kernel::dispatch_shape<MinGruBwdOp, 1>(A, g, p, st);
+}
+hipError_t run_scan_minlstm_backward(const MinLstmBwdArgs& A, const ScanGeom& g, const ScanPlan& p, hipStream_t st) {
+    if (p.vec != 1) return hipErrorInvalidValue;
+    return scan_kernel::dispatch_shape<MinLstmBwdOp, 1>(A, g, p, st);
+}
+hipError_t run_scan_real_decay_backward(const RealDecayBwdArgs& A, float* glam, const ScanGeom& g, const ScanPlan& p,
+                                        hipStream_t st) {
+    if (p.vec != 1) return hipErrorInvalidValue;
+    const hipError_t e = scan_kernel::dispatch_shape<RealDecayBwdOp, 1>(A, g, p, st);
+    return e != hipSuccess ? e : run_part_sums(g, glam, false, st);
+}
+hipError_t run_scan_complex_normalized_backward(const CplxBwdArgs& A, float* glam, const ScanGeom& g,
+                                                const ScanPlan& p, hipStream_t st) {
+    if (p.vec != 1 || !A.u) return hipErrorInvalidValue;
+    const hipError_t e = scan_kernel::dispatch_shape<CplxNormBwdOp, 1>(A, g, p, st);
+    return e != hipSuccess ? e : run_part_sums(g, glam, true, st);
+}
+
 }  // namespace linrec

@@ -129,8 +129,10 @@ def make_mingru(B: int, T: int, C: int, seed: int):
 
 
 def make_lru(B: int, T: int, C: int, seed: int, r_lo: float = 0.9, r_hi: float = 0.999,
-             theta_hi: float = math.pi / 10):
-    """LRU scan inputs: lam (C,) complex64 with |lam| = r, arg lam = theta; u (B,T,C) complex64."""
+             theta_hi: float = math.pi / 10, with_x0: bool = False):
+    """LRU scan inputs: lam (C,) complex64 with |lam| = r, arg lam = theta; u (B,T,C) complex64;
+    with ``with_x0`` an initial state x0 (B,C) complex64 of the same distribution as u, drawn
+    after u (else None)."""
     rng = np.random.default_rng(seed)
     r = rng.uniform(r_lo, r_hi, size=C)
     theta = rng.uniform(0.0, theta_hi, size=C)
@@ -140,7 +142,13 @@ def make_lru(B: int, T: int, C: int, seed: int, r_lo: float = 0.9, r_hi: float =
     s2 = 1.0 / math.sqrt(2.0)
     _normal_into(rng, flat[0::2], s2)
     _normal_into(rng, flat[1::2], s2)
-    return {"lam": lam, "u": u, "x0": None}
+    x0 = None
+    if with_x0:
+        x0 = np.empty((B, C), dtype=np.complex64)
+        f0 = x0.reshape(-1).view(np.float32)
+        _normal_into(rng, f0[0::2], s2)
+        _normal_into(rng, f0[1::2], s2)
+    return {"lam": lam, "u": u, "x0": x0}
 
 
 def make_inputs(wid: int, seed: int | None = None, shape=None):
@@ -193,13 +201,16 @@ def make_token_shift(B: int, T: int, C: int, M: int, seed: int, with_grad: bool 
     return out
 
 
-def make_gated(B: int, T: int, C: int, seed: int, logit_std: float = 1.0):
+def make_gated(B: int, T: int, C: int, seed: int, logit_std: float = 1.0, with_grad: bool = False):
     """Inputs of the gated scan variants: gate pre-activations kz, kf, ki ~ N(0, logit_std),
-    candidates h ~ N(0,1), x0 ~ N(0,1) (B,C), a per-channel decay lam ~ U(-1, 1) (C,); all
-    float32, drawn in that order."""
+    candidates h ~ N(0,1), x0 ~ N(0,1) (B,C), a per-channel decay lam ~ U(-1, 1) (C,), and
+    with ``with_grad`` an upstream gradient gx ~ N(0,1) (B,T,C); all float32, drawn in that
+    order."""
     rng = np.random.default_rng(seed)
     out = {n: _normal(rng, (B, T, C), logit_std) for n in ("kz", "kf", "ki")}
     out["h"] = _normal(rng, (B, T, C), 1.0)
     out["x0"] = _normal(rng, (B, C), 1.0)
     out["lam"] = rng.uniform(-1.0, 1.0, size=C).astype(np.float32)
+    if with_grad:
+        out["gx"] = _normal(rng, (B, T, C), 1.0)
     return out

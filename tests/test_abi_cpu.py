@@ -155,10 +155,34 @@ def test_scan_backward_argument_checks(lib):
     # workspace: a long single sequence needs look-back records
     need = lib.linrec_scan_backward_workspace_size(1, 1 << 16, 64, 1)
     assert need > 0
-    assert cb(1, 1 << 16, 64, P, None, P, P, P2, P2, None, None, need - 1, None) == WORKSPACE
-    assert lib.linrec_scan_backward_workspace_size(2, 40, 8, 0) == 0
-    # the complex adjoint always needs room for its per-slab sums of glambda
+    assert cb(1, 1 << 16, 64, P, None, P, P, P2, P2, None, P, 16, None) == WORKSPACE
+    # the complex adjoints always need room for their per-slab sums of glambda; so does the
+    # real family's query, which covers the per-channel decay's adjoint
     assert lib.linrec_scan_backward_workspace_size(2, 40, 8, 1) > 0
+    assert lib.linrec_scan_backward_workspace_size(2, 40, 8, 0) > 0
+
+
+def test_variant_backward_argument_checks(lib):
+    mg, ml = lib.linrec_scan_mingru_backward, lib.linrec_scan_minlstm_backward
+    rd, cn = lib.linrec_scan_real_decay_backward, lib.linrec_scan_complex_normalized_backward
+    # (B, T, C, ins..., x0, x, gx, outs..., gx0, ws, bytes, stream)
+    assert mg(2, 8, 4, P, None, None, P, P, P2, P2, None, P, 1 << 20, None) == INVALID       # h NULL
+    assert ml(2, 8, 4, P, P, P, None, P, P, P2, None, P2, None, P, 1 << 20, None) == INVALID  # gki NULL
+    assert mg(2, 8, 4, P, P, None, P, ODD, P2, P2, None, P, 1 << 20, None) == UNSUPPORTED
+    assert mg(2, 8, 4, P, P, ODD, P, P, P2, P2, None, P, 1 << 20, None) == UNSUPPORTED     # x0
+    # empty shapes: nothing to do without outputs to fill
+    assert mg(0, 8, 4, P, P, None, P, P, P2, P2, None, None, 0, None) == OK
+    assert ml(2, 8, 0, P, P, P, None, P, P, P2, P2, P2, None, None, 0, None) == OK
+    # the decay's adjoint needs glambda; complex64 pointers need 8 bytes
+    assert rd(2, 8, 4, P, None, P, P, None, P2, None, P, 1 << 20, None) == INVALID
+    assert rd(2, 8, 4, P, None, P, P, ODD, P2, None, P, 1 << 20, None) == UNSUPPORTED
+    assert cn(2, 8, 4, P, None, None, P, P, P2, P2, None, P, 1 << 20, None) == INVALID      # u NULL
+    assert cn(2, 8, 4, P, P, None, P, P, ctypes.c_void_p(0x200004), P2, None, P, 1 << 20, None) == UNSUPPORTED
+    # workspace
+    need = lib.linrec_scan_backward_workspace_size(1, 1 << 14, 64, 0)
+    assert need > 0
+    assert rd(1, 1 << 14, 64, P, None, P, P, P2, P2, None, P, 16, None) == WORKSPACE
+    assert cn(1, 1 << 14, 64, P, P, None, P, P, P2, P2, None, P, 16, None) == WORKSPACE
 
 
 def test_wkv4_forward_ex_argument_checks(lib):
