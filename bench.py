@@ -44,7 +44,12 @@ BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "sca
                   "scan_real_decay": 8,          # read u; write x
                   "scan_complex_normalized": 16, # read u; write x (complex64)
                   "token_shift": 16,             # read x; write 3 mixes
-                  "token_shift_backward": 20}    # read x, 3 gradients; write gx
+                  "token_shift_backward": 20,    # read x, 3 gradients; write gx
+                  "wkv4_backward_gated": 28,     # read k, v, r, gy; write gk, gv, gr
+                  "scan_mingru_backward": 24,    # read kz, h, x, gx; write gkz, gh
+                  "scan_minlstm_backward": 32,   # read kf, ki, h, x, gx; write gkf, gki, gh
+                  "scan_real_decay_backward": 12,  # read x, gx; write gu
+                  "scan_complex_normalized_backward": 32}  # read u, x, gx; write gu (complex64)
 SHIFT_M = 3  # token-shift mixes timed: the r, k, v inputs of the time mix
 
 
@@ -69,7 +74,13 @@ KERNEL_SOURCES = {
     "token_shift_backward": ("api.hip", "token_shift.hip", "token_shift.hpp", "device_common.hpp"),
     "wkv4_backward": ("api.hip", "wkv_backward.hip", "wkv_backward.hpp", "lookback.hpp", "device_common.hpp",
                       "wkv_math.hpp"),
+    "wkv4_backward_gated": ("api.hip", "wkv_backward.hip", "wkv_backward.hpp", "lookback.hpp",
+                            "device_common.hpp", "wkv_math.hpp"),
 }
+for _k in ("scan_mingru_backward", "scan_minlstm_backward", "scan_real_decay_backward",
+           "scan_complex_normalized_backward"):
+    KERNEL_SOURCES[_k] = _SCAN_SOURCES + ("scan_variants.hip",)
+VARIANT_BWD = ("scan_mingru_backward", "scan_minlstm_backward", "scan_real_decay_backward")
 
 
 def kernel_source_digest(kind: str = "wkv4_forward") -> str:
@@ -135,6 +146,54 @@ class Row:
                                    v.data_ptr(), gy.data_ptr(), gw.data_ptr(), gu.data_ptr(),
                                    gk.data_ptr(), gv.data_ptr(), ws.data_ptr(), nws, stream)))
             self.keep += [w, u]
+        elif kind == "wkv4_backward_gated":
+            w, u = to(host["w"]), to(host["u"])
+            nws = int(lib.wkv4_backward_workspace_size(B, T, C))
+            gw = torch.empty(C, dtype=torch.float32, device=dev)
+            gu = torch.empty(C, dtype=torch.float32, device=dev)
+            for _ in range(rotations):
+                k, v, r, gy = to(host["k"]), to(host["v"]), to(host["r"]), to(host["gy"])
+                gk, gv, gr = torch.empty_like(k), torch.empty_like(k), torch.empty_like(k)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [k, v, r, gy, gk, gv, gr, ws]
+                self.calls.append((lib.wkv4_backward_ex, (B, T, C, w.data_ptr(), u.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), r.data_ptr(), None, None, gy.data_ptr(), None, gw.data_ptr(),
+                                   gu.data_ptr(), gk.data_ptr(), gv.data_ptr(), gr.data_ptr(), None,
+                                   ws.data_ptr(), nws, stream)))
+            self.keep += [w, u, gw, gu]
+        elif kind in VARIANT_BWD:
+            names = {"scan_mingru_backward": ("kz", "h"), "scan_minlstm_backward": ("kf", "ki", "h"),
+                     "scan_real_decay_backward": ()}[kind]
+            n_out = {"scan_mingru_backward": 2, "scan_minlstm_backward": 3, "scan_real_decay_backward": 1}[kind]
+            fn = getattr(lib, "linrec_" + kind)
+            nws = int(lib.linrec_scan_backward_workspace_size(B, T, C, 0))
+            lam = to(host["lam"]) if kind == "scan_real_decay_backward" else None
+            glam = torch.empty(C, dtype=torch.float32, device=dev)
+            for _ in range(rotations):
+                ins = [to(host[n]) for n in names]
+                x, gx = to(host["x"]), to(host["gx"])
+                outs = [torch.empty_like(x) for _ in range(n_out)]
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += ins + [x, gx, ws] + outs
+                if lam is not None:
+                    ptrs = [lam.data_ptr(), None, x.data_ptr(), gx.data_ptr(), glam.data_ptr(), outs[0].data_ptr()]
+                else:
+                    ptrs = [t.data_ptr() for t in ins] + [None, x.data_ptr(), gx.data_ptr()] + [o.data_ptr() for o in outs]
+                self.calls.append((fn, (B, T, C, *ptrs, None, ws.data_ptr(), nws, stream)))
+            self.keep += [glam] + ([lam] if lam is not None else [])
+        elif kind == "scan_complex_normalized_backward":
+            lam = to(host["lam"])
+            nws = int(lib.linrec_scan_backward_workspace_size(B, T, C, 1))
+            glam = torch.empty(C, dtype=torch.complex64, device=dev)
+            for _ in range(rotations):
+                u, x, gx = to(host["u"]), to(host["x"]), to(host["gx"])
+                gu = torch.empty_like(x)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [u, x, gx, gu, ws]
+                self.calls.append((lib.linrec_scan_complex_normalized_backward,
+                                   (B, T, C, lam.data_ptr(), u.data_ptr(), None, x.data_ptr(), gx.data_ptr(),
+                                    glam.data_ptr(), gu.data_ptr(), None, ws.data_ptr(), nws, stream)))
+            self.keep += [lam, glam]
         elif kind == "scan_real":
             nws = int(lib.linrec_scan_workspace_size(B, T, C, 0))
             for _ in range(rotations):
@@ -284,7 +343,15 @@ def cpu_baseline(kind, host, budget_s):
           "scan_complex_normalized": lambda: oracle.scan_complex_normalized(host["lam"], host["u"]),
           "token_shift": lambda: oracle.token_shift(host["x"], host["mu"]),
           "token_shift_backward": lambda: oracle.token_shift_backward(host["x"], host["mu"], host["g"],
-                                                                      want_gx_prev=False)}[kind]
+                                                                      want_gx_prev=False),
+          "wkv4_backward_gated": lambda: oracle.wkv4_backward_gated(host["w"], host["u"], host["k"], host["v"],
+                                                                    host["r"], host["gy"]),
+          "scan_mingru_backward": lambda: oracle.scan_mingru_backward(host["kz"], host["h"], host["x"], host["gx"]),
+          "scan_minlstm_backward": lambda: oracle.scan_minlstm_backward(host["kf"], host["ki"], host["h"], host["x"],
+                                                                        host["gx"]),
+          "scan_real_decay_backward": lambda: oracle.scan_real_decay_backward(host["lam"], host["x"], host["gx"]),
+          "scan_complex_normalized_backward": lambda: oracle.scan_complex_normalized_backward(
+              host["lam"], host["u"], host["x"], host["gx"])}[kind]
     times = []
     t_start = time.perf_counter()
     while True:
@@ -325,19 +392,28 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
     B, T, C = shape or (wl.B, wl.T, wl.C)
     if kind.startswith("token_shift"):
         host = workloads.make_token_shift(B, T, C, SHIFT_M, wl.seed, with_grad=kind.endswith("_backward"))
-    elif kind in ("scan_mingru", "scan_minlstm", "scan_real_decay"):
-        host = workloads.make_gated(B, T, C, wl.seed)
+    elif kind in ("scan_mingru", "scan_minlstm", "scan_real_decay") or kind in VARIANT_BWD:
+        host = workloads.make_gated(B, T, C, wl.seed, with_grad=kind in VARIANT_BWD)
         host["lam"] = (0.5 + 0.5 * np.abs(host["lam"])).astype(np.float32)
+        if kind in VARIANT_BWD:
+            host["x"] = host["h"]  # stand-in of the forward output's distribution (timing only)
     else:
         host = workloads.make_inputs(wid, shape=(B, T, C))
-    if kind.endswith("_backward") and kind.startswith("scan_"):
+    if kind == "wkv4_backward_gated":
+        host["r"] = host["v"]  # stand-in receptance ~ N(0,1) (timing only)
+    if kind.endswith("_backward") and kind.startswith("scan_") and kind not in VARIANT_BWD:
         host.update(workloads.make_scan_adjoint_inputs(wid, host))
     elements = B * T * C
     label = wl.label
-    if kind in ("scan_mingru", "scan_minlstm", "scan_real_decay", "scan_complex_normalized"):
-        label = {"scan_mingru": "minGRU from gate logits", "scan_minlstm": "minLSTM from gate logits",
-                 "scan_real_decay": "real scan with one decay per channel",
-                 "scan_complex_normalized": "LRU with normalised input"}[kind] + " fp32 B=%d T=%d C=%d" % (B, T, C)
+    variant_labels = {"scan_mingru": "minGRU from gate logits", "scan_minlstm": "minLSTM from gate logits",
+                      "scan_real_decay": "real scan with one decay per channel",
+                      "scan_complex_normalized": "LRU with normalised input"}
+    base_kind = kind[:-len("_backward")] if kind.endswith("_backward") else kind
+    if base_kind in variant_labels:
+        label = variant_labels[base_kind] + (", backward" if kind.endswith("_backward") else "") + \
+            " fp32 B=%d T=%d C=%d" % (B, T, C)
+    if kind == "wkv4_backward_gated":
+        label = "WKV-4 backward through the sigma(r) gate fp32 B=%d T=%d C=%d" % (B, T, C)
     if kind.startswith("token_shift"):
         label = "RWKV token shift%s, %d mixes, fp32 B=%d T=%d C=%d" % (
             " backward" if kind.endswith("_backward") else "", SHIFT_M, B, T, C)
@@ -364,7 +440,7 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
             sample = {k: (v[:, :Ts] if hasattr(v, "ndim") and v.ndim == 3 else
                           (v[:, :, :Ts] if hasattr(v, "ndim") and v.ndim == 4 else v)) for k, v in host.items()}
             desc = "first %d of %d time steps, all batch rows and channels" % (Ts, T)
-        if kind.endswith("_backward") and kind.startswith("scan_"):
+        if kind in ("scan_real_backward", "scan_complex_backward"):
             # The adjoint's forward input: the oracle's own forward scan of the sample.
             import oracle
             sample = dict(sample)
@@ -436,7 +512,11 @@ def main():
                                             (5, "scan_complex_backward", 10, 16384),
                                             (4, "scan_mingru", 20, 512), (4, "scan_minlstm", 20, 512),
                                             (4, "scan_real_decay", 20, 512), (5, "scan_complex_normalized", 10, 16384),
-                                            (2, "token_shift", 50, None), (2, "token_shift_backward", 50, None)):
+                                            (2, "token_shift", 50, None), (2, "token_shift_backward", 50, None),
+                                            (3, "wkv4_backward_gated", 20, 256),
+                                            (4, "scan_mingru_backward", 20, 512), (4, "scan_minlstm_backward", 20, 512),
+                                            (4, "scan_real_decay_backward", 20, 512),
+                                            (5, "scan_complex_normalized_backward", 10, 16384)):
             rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
             log("[bench] " + json.dumps(rows[-1]))
         os.makedirs(os.path.dirname(args.all_out), exist_ok=True)

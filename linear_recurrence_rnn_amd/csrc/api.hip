@@ -108,7 +108,7 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
         p.ws_bytes = align256((size_t)nwg * 8) + 2 * align256((size_t)(nwg * cw) * linrec::agg_bytes(kind));
     if (linrec::has_parts(kind))  // per-slab glam sums and their first-stage sums
         p.ws_bytes += align256((size_t)(nwg * cw) * 16) +
-                      align256((size_t)(ceil_div(p.nslab, linrec::kPartBlock) * C) * 16);
+                      align256((size_t)(B * ceil_div(p.nslab, linrec::kPartBlock) * C) * 16);
     return p;
 }
 

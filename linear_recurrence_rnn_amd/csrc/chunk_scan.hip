@@ -15,18 +15,18 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
         p[i] = 0.f;
 }
 
-// glam, first stage: block (group, k) adds slabs [k kPartBlock, (k+1) kPartBlock) of every
-// batch row for its 64 channels.  The association is fixed: within a row, slab s goes to
-// accumulator s mod 8 (so 8 loads are in flight at a time, not one), the 8 accumulators are
-// added in order, and the rows in ascending order.
+// glam, first stage: block (group, k, b) adds slabs [k kPartBlock, (k+1) kPartBlock) of batch
+// row b for its 64 channels, so that many rows of short sequences still fill the chip.  The
+// association is fixed: slab s goes to accumulator s mod 8 (8 loads in flight at a time, not
+// one) and the 8 accumulators are added in order.
 __global__ __launch_bounds__(64) void part_sum_kernel(ScanGeom g) {
     const int64_t grp = blockIdx.x, k = blockIdx.y;
     const int lane = threadIdx.x;
     const int64_t c = grp * 64 + lane;
     if (c >= g.C) return;
+    const int64_t nk = gridDim.y;
     const int64_t s0 = k * kPartBlock, s1 = min(g.nslab, s0 + kPartBlock);
-    double re = 0.0, im = 0.0;
-    for (int64_t b = 0; b < g.B; ++b) {
+    for (int64_t b = blockIdx.z; b < g.B; b += gridDim.z) {
         const double* p = g.part + 2 * (((b * g.ngrp + grp) * g.nslab) * 64 + lane);
         double ar[8], ai[8];
 #pragma unroll
@@ -43,26 +43,45 @@ __global__ __launch_bounds__(64) void part_sum_kernel(ScanGeom g) {
             ar[i] += p[2 * s * 64];
             ai[i] += p[2 * s * 64 + 1];
         }
+        double re = 0.0, im = 0.0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             re += ar[i];
             im += ai[i];
         }
+        g.part2[2 * ((b * nk + k) * g.C + c)] = re;
+        g.part2[2 * ((b * nk + k) * g.C + c) + 1] = im;
     }
-    g.part2[2 * (k * g.C + c)] = re;
-    g.part2[2 * (k * g.C + c) + 1] = im;
 }
 
-// glam, second stage: the first-stage sums of a channel, in order, as complex64 (or the
-// real part alone as float32).
+// glam, second stage: the first-stage sums of a channel (batch rows in ascending order,
+// slab blocks within a row in order; entry e to accumulator e mod 8, added in order), as
+// complex64 (or the real part alone as float32).
 __global__ __launch_bounds__(256) void part_final_kernel(ScanGeom g, int64_t nk, float* __restrict__ glam,
                                                          bool complex_out) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= g.C) return;
+    const int64_t n = g.B * nk;
+    double ar[8], ai[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ar[i] = ai[i] = 0.0;
+    int64_t e = 0;
+    for (; e + 8 <= n; e += 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ar[i] += g.part2[2 * ((e + i) * g.C + c)];
+            ai[i] += g.part2[2 * ((e + i) * g.C + c) + 1];
+        }
+    }
+    for (int i = 0; e < n; ++e, ++i) {
+        ar[i] += g.part2[2 * (e * g.C + c)];
+        ai[i] += g.part2[2 * (e * g.C + c) + 1];
+    }
     double re = 0.0, im = 0.0;
-    for (int64_t k = 0; k < nk; ++k) {
-        re += g.part2[2 * (k * g.C + c)];
-        im += g.part2[2 * (k * g.C + c) + 1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        re += ar[i];
+        im += ai[i];
     }
     if (complex_out) {
         glam[2 * c] = (float)re;
@@ -106,7 +125,8 @@ hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const Sc
 
 hipError_t run_part_sums(const ScanGeom& g, float* glam, bool complex_out, hipStream_t st) {
     const int64_t nk = (g.nslab + kPartBlock - 1) / kPartBlock;
-    hipLaunchKernelGGL(part_sum_kernel, dim3((unsigned)g.ngrp, (unsigned)nk), dim3(64), 0, st, g);
+    const unsigned nb = (unsigned)(g.B < 65535 ? g.B : 65535);
+    hipLaunchKernelGGL(part_sum_kernel, dim3((unsigned)g.ngrp, (unsigned)nk, nb), dim3(64), 0, st, g);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(part_final_kernel, dim3((unsigned)((g.C + 255) / 256)), dim3(256), 0, st, g, nk, glam,

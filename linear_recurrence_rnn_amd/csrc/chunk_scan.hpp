@@ -172,7 +172,7 @@ hipError_t run_scan_complex_normalized_backward(const CplxBwdArgs& A, float* gla
 // Sums g.part (per-slab shares, pairs) over slabs and batch rows into glam: C complex64
 // (`complex_out`) or C float32 (the first of each pair).
 hipError_t run_part_sums(const ScanGeom& g, float* glam, bool complex_out, hipStream_t st);
-// Also sums g.part into glam (C complex64): g.part2 holds ceil(nslab / kPartBlock) x C pairs.
+// Also sums g.part into glam (C complex64): g.part2 holds B x ceil(nslab / kPartBlock) x C pairs.
 hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const ScanGeom& g, const ScanPlan& p,
                                      hipStream_t st);
 constexpr int kPartBlock = 64;  // slabs summed per first-stage block of the glam reduction

@@ -836,11 +836,32 @@ struct BwdRows {
     }
 };
 
+// sigma(k) and sigma(-k) from one exponential: with e = e^{-|k|}, sigma(|k|) = 1/(1+e) and
+// sigma(-|k|) = e/(1+e), both without cancellation.
+__device__ __forceinline__ void sigmoid_pair(float k, float& s, float& sc) {
+    const float e = fast_exp2(-fabsf(k) * kLog2e);
+    const float r = __builtin_amdgcn_rcpf(1.f + e);
+    const float q = e * r;
+    s = k >= 0.f ? r : q;
+    sc = k >= 0.f ? q : r;
+}
+__device__ __forceinline__ float sigmoid_neg(float k) {
+    float s, sc;
+    sigmoid_pair(k, s, sc);
+    return sc;
+}
+
+// The gated adjoints keep the RAW gate logits of row t+1 in their chunk registers (not the
+// multiplier formed from them): step j's multiplier needs row t+1 and its own derivatives
+// need row t, which is step j+1's row t+1, so each gate row is read from memory once (one
+// extra row per chunk).  Past the last row the logit is +inf, whose multiplier is 0.
+
 // minGRU: d_t = gx_t + sigmoid(-kz_{t+1}) d_{t+1};  dL/dkz_t = d_t z_t (1 - z_t) (h~_t - h_{t-1}),
 // dL/dh~_t = d_t z_t, dL/dx0 = (1 - z_0) d_0.
 struct MinGruBwdOp : RealOp {
     using Args = MinGruBwdArgs;
     static constexpr bool kReverse = true;
+    struct In { float k, g; };  // kz_{t+1} (+inf past the end), gx_t
     template <int L>
     __device__ __forceinline__ static Chan chan(const Args&, int64_t) { return {}; }
     __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) { return identity(); }
@@ -871,7 +892,29 @@ struct MinGruBwdOp : RealOp {
         if (!last) kn = ldb<VEC>(R.kn, voff, rows.soff(j));
         const FV<VEC> gx = ldb<VEC>(R.g, voff, rows.soff(j));
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) in[e] = {last ? 0.f : sigmoidf(-kn.v[e]), gx.v[e]};
+        for (int e = 0; e < VEC; ++e) in[e] = {last ? __builtin_inff() : kn.v[e], gx.v[e]};
+    }
+    template <int VEC>
+    __device__ __forceinline__ static void zero(In (&in)[VEC]) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {__builtin_inff(), 0.f};
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Agg reduce(const Chan&, In (&in)[L][VEC], int e, int n, Local&) {
+        float m = 1.f, x = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                const float a = sigmoid_neg(in[j][e].k);
+                x = fmaf(a, x, in[j][e].g);
+                m *= a;
+            }
+        }
+        return {m, x};
+    }
+    __device__ __forceinline__ static Agg step(const Chan&, const Agg& s, const In& x) {
+        const float a = sigmoid_neg(x.k);
+        return {s.m * a, fmaf(a, s.x, x.g)};
     }
     template <int L, int VEC>
     __device__ __forceinline__ static Part run(const Res& R, const Chan (&)[VEC], const Agg (&cin)[VEC],
@@ -879,28 +922,32 @@ struct MinGruBwdOp : RealOp {
                                                const Rows& rows) {
         static_assert(VEC == 1, "the adjoints keep one channel per lane");
         const int lane_col = (int)(voff / 4);
-        float xp[L], kz[L], hh[L];
+        float xp[L], hh[L];
 #pragma unroll
         for (int j = 0; j < L; ++j) {
             if (j < n) {
                 xp[j] = rows.t(j) > 0 ? ldb<1>(R.xp, voff, rows.soff(j) - R.xshift).v[0]
                                       : (R.x0 ? R.x0[lane_col] : 0.f);
-                kz[j] = ldb<1>(R.k, voff, rows.soff(j)).v[0];
                 hh[j] = ldb<1>(R.h, voff, rows.soff(j)).v[0];
             }
         }
-        float d = cin[0].x;
+        // The gate row of the chunk's earliest step (the only one not among the k_{t+1}).
+        const float k_low = n > 0 ? ldb<1>(R.k, voff, rows.soff(n - 1)).v[0] : 0.f;
+        float d = cin[0].x, a = sigmoid_neg(in[0][0].k);
 #pragma unroll
         for (int j = 0; j < L; ++j) {
             if (j < n) {
-                d = fmaf(in[j][0].a, d, in[j][0].b);
-                const float z = sigmoidf(kz[j]), zc = sigmoidf(-kz[j]);
+                d = fmaf(a, d, in[j][0].g);
+                const float kz = (j + 1 < L && j + 1 < n) ? in[j + 1 < L ? j + 1 : j][0].k : k_low;
+                float z, zc;
+                sigmoid_pair(kz, z, zc);
                 FV<1> gk, gh;
                 gk.v[0] = d * (z * zc) * (hh[j] - xp[j]);
                 gh.v[0] = d * z;
                 stb<1>(R.gk, voff, rows.soff(j), gk);
                 stb<1>(R.gh, voff, rows.soff(j), gh);
                 if (rows.t(j) == 0 && R.gx0) R.gx0[lane_col] = zc * d;
+                a = zc;  // the multiplier of the next step (one time step earlier)
             }
         }
         return {};
@@ -914,6 +961,7 @@ struct MinGruBwdOp : RealOp {
 struct MinLstmBwdOp : RealOp {
     using Args = MinLstmBwdArgs;
     static constexpr bool kReverse = true;
+    struct In { float f, i, g; };  // kf_{t+1} (+inf past the end), ki_{t+1}, gx_t
     template <int L>
     __device__ __forceinline__ static Chan chan(const Args&, int64_t) { return {}; }
     __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) { return identity(); }
@@ -951,7 +999,35 @@ struct MinLstmBwdOp : RealOp {
         }
         const FV<VEC> gx = ldb<VEC>(R.g, voff, rows.soff(j));
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) in[e] = {last ? 0.f : sigmoidf(logit(fn.v[e], inn.v[e])), gx.v[e]};
+        for (int e = 0; e < VEC; ++e) in[e] = {last ? __builtin_inff() : fn.v[e], inn.v[e], gx.v[e]};
+    }
+    template <int VEC>
+    __device__ __forceinline__ static void zero(In (&in)[VEC]) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) in[e] = {__builtin_inff(), 0.f, 0.f};
+    }
+    // The multiplier a = f/(f+i) of the step whose gate logits are (kf, ki); 0 for kf = +inf.
+    __device__ __forceinline__ static float mult(float kf, float ki) {
+        float a, ac;
+        sigmoid_pair(logit(kf, ki), a, ac);
+        return a;
+    }
+    template <int L, int VEC>
+    __device__ __forceinline__ static Agg reduce(const Chan&, In (&in)[L][VEC], int e, int n, Local&) {
+        float m = 1.f, x = 0.f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < n) {
+                const float a = mult(in[j][e].f, in[j][e].i);
+                x = fmaf(a, x, in[j][e].g);
+                m *= a;
+            }
+        }
+        return {m, x};
+    }
+    __device__ __forceinline__ static Agg step(const Chan&, const Agg& s, const In& x) {
+        const float a = mult(x.f, x.i);
+        return {s.m * a, fmaf(a, s.x, x.g)};
     }
     template <int L, int VEC>
     __device__ __forceinline__ static Part run(const Res& R, const Chan (&)[VEC], const Agg (&cin)[VEC],
@@ -959,33 +1035,39 @@ struct MinLstmBwdOp : RealOp {
                                                const Rows& rows) {
         static_assert(VEC == 1, "the adjoints keep one channel per lane");
         const int lane_col = (int)(voff / 4);
-        float xp[L], kf[L], ki[L], hh[L];
+        float xp[L], hh[L];
 #pragma unroll
         for (int j = 0; j < L; ++j) {
             if (j < n) {
                 xp[j] = rows.t(j) > 0 ? ldb<1>(R.xp, voff, rows.soff(j) - R.xshift).v[0]
                                       : (R.x0 ? R.x0[lane_col] : 0.f);
-                kf[j] = ldb<1>(R.f, voff, rows.soff(j)).v[0];
-                ki[j] = ldb<1>(R.i, voff, rows.soff(j)).v[0];
                 hh[j] = ldb<1>(R.h, voff, rows.soff(j)).v[0];
             }
         }
-        float d = cin[0].x;
+        const float f_low = n > 0 ? ldb<1>(R.f, voff, rows.soff(n - 1)).v[0] : 0.f;
+        const float i_low = n > 0 ? ldb<1>(R.i, voff, rows.soff(n - 1)).v[0] : 0.f;
+        float d = cin[0].x, a = mult(in[0][0].f, in[0][0].i);
 #pragma unroll
         for (int j = 0; j < L; ++j) {
             if (j < n) {
-                d = fmaf(in[j][0].a, d, in[j][0].b);
-                const float dd = logit(kf[j], ki[j]);
-                const float a = sigmoidf(dd), ac = sigmoidf(-dd);
-                const float gdd = (a * ac) * d * (xp[j] - hh[j]);
+                d = fmaf(a, d, in[j][0].g);
+                const bool inner = j + 1 < L && j + 1 < n;
+                const int jn = j + 1 < L ? j + 1 : j;
+                const float kf = inner ? in[jn][0].f : f_low, ki = inner ? in[jn][0].i : i_low;
+                float at, ac, sf, sfc, si, sic;
+                sigmoid_pair(softplusf(-ki) - softplusf(-kf), at, ac);
+                sigmoid_pair(kf, sf, sfc);
+                sigmoid_pair(ki, si, sic);
+                const float gdd = (at * ac) * d * (xp[j] - hh[j]);
                 FV<1> gf, gi, gh;
-                gf.v[0] = gdd * sigmoidf(-kf[j]);
-                gi.v[0] = -gdd * sigmoidf(-ki[j]);
+                gf.v[0] = gdd * sfc;
+                gi.v[0] = -gdd * sic;
                 gh.v[0] = d * ac;
                 stb<1>(R.gf, voff, rows.soff(j), gf);
                 stb<1>(R.gi, voff, rows.soff(j), gi);
                 stb<1>(R.gh, voff, rows.soff(j), gh);
-                if (rows.t(j) == 0 && R.gx0) R.gx0[lane_col] = a * d;
+                if (rows.t(j) == 0 && R.gx0) R.gx0[lane_col] = at * d;
+                a = at;
             }
         }
         return {};
