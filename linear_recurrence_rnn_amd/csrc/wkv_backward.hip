@@ -718,6 +718,28 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         shwu[w][lane][1] = su;
         shr[w][lane] = ragg;
         __syncthreads();  // B3
+        if (fr.fast && n > 0) {
+            // The chunk's own part of the reverse re-run, while the coordinator looks back
+            // for the carry: with S_s the frame sums after step s in the chunk,
+            //   dL/dv_s = (g beta / D)_s + g_s us S^x_s + [g_s X],
+            //   dL/dk_s = (g beta / D)_s (v - y)_s + g_s us (v_s S^x_s - S^h_s) + [g_s (v_s X - H)],
+            // the bracketed carry terms are added after B4.  sy and sd take the partial sums.
+            float Sx = 0.f, Sh = 0.f;
+#pragma unroll
+            for (int j = L - 1; j >= 0; --j) {
+                if (j < n) {
+                    const float gj = sa[j], vj = vv[j];
+                    const float gus = gj * fr.us;
+                    const float cc = sc[j] * (gj * fr.cs);  // g beta / D
+                    const float gvl = fmaf(gus, Sx, cc);
+                    const float gkl = fmaf(cc, sd[j], gus * fmaf(vj, Sx, -Sh));
+                    Sx += sc[j];
+                    Sh = fmaf(sc[j], sy[j], Sh);
+                    sy[j] = gvl;
+                    sd[j] = gkl;
+                }
+            }
+        }
         __syncthreads();  // B4: shr[w] now holds the reverse state at my chunk's end
 
         // Reverse re-run of my chunk; the outputs replace v and dL/dy's slot.
@@ -737,20 +759,13 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
                     Hs = rc.h * kap;
                 }
                 const float Xsf = (float)Xs;
-                float Sx = 0.f, Sh = 0.f;
 #pragma unroll
                 for (int j = L - 1; j >= 0; --j) {
                     if (j < n) {
                         const float gj = sa[j], vj = vv[j];
-                        const float gus = gj * fr.us;
-                        const float cc = sc[j] * (gj * fr.cs);  // g beta / D
                         const float tc = (float)fma((double)vj, Xs, -Hs);
-                        const float gv = fmaf(gus, Sx, fmaf(gj, Xsf, cc));
-                        const float gk = fmaf(cc, sd[j], fmaf(gj, tc, gus * fmaf(vj, Sx, -Sh)));
-                        Sx += sc[j];
-                        Sh = fmaf(sc[j], sy[j], Sh);
-                        sa[j] = gk;
-                        vv[j] = gv;
+                        sa[j] = fmaf(gj, tc, sd[j]);
+                        vv[j] = fmaf(gj, Xsf, sy[j]);
                     }
                 }
             } else {
