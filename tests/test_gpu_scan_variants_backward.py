@@ -157,3 +157,36 @@ def test_empty_sequence_zero_fills(L):
     assert host(glam).tolist() == [0.0] * 8 and np.all(host(gx0) == 0)
     gkz, gh, gx0 = L.scan_mingru_backward(z, z, z, z, x0)
     assert np.all(host(gx0) == 0)
+
+
+def test_unit_circle_decays(L):
+    """|lambda| = 1 exactly (lambda = 1, -1, i, -i): gamma = 0, so the normalised LRU keeps
+    x0 rotating, dL/du = 0 and dL/dlambda has no gamma term."""
+    announce("normalised LRU adjoint on the unit circle")
+    B, T, C = 2, 700, 8
+    d = workloads.make_lru(B, T, C, 81, 0.9, 0.999, math.pi / 10, with_x0=True)
+    d.update(workloads.make_scan_adjoint_inputs(5, d, seed=82))
+    lam = d["lam"].copy()
+    lam[:4] = np.array([1, -1, 1j, -1j], dtype=np.complex64)
+    x = oracle.scan_complex_normalized(lam, d["u"], d["x0"])
+    xc = x.astype(np.complex64)
+    got = L.scan_complex_normalized_backward(dev(lam), dev(d["u"]), dev(xc), dev(d["gx"]), dev(d["x0"]))
+    ref = oracle.scan_complex_normalized_backward(lam, d["u"], xc, d["gx"], d["x0"])
+    check(got, ref, (None, 1, None))
+    assert np.all(host(got[1])[:, :, :4] == 0)
+
+
+def test_lambda_sums_are_deterministic(L):
+    """dL/dlambda is summed in a fixed order: two calls give the same bits."""
+    announce("glambda determinism (decay and normalised LRU adjoints)")
+    d = workloads.make_gated(8, 3000, 96, seed=83, with_grad=True)
+    x = dev(f32(oracle.scan_real_decay(d["lam"], d["h"], d["x0"])))
+    a = host(L.scan_real_decay_backward(dev(d["lam"]), x, dev(d["gx"]), dev(d["x0"]))[0])
+    b = host(L.scan_real_decay_backward(dev(d["lam"]), x, dev(d["gx"]), dev(d["x0"]))[0])
+    assert np.array_equal(a, b)
+    c = workloads.make_lru(4, 5000, 64, 84, 0.9, 0.999, math.pi / 10)
+    c.update(workloads.make_scan_adjoint_inputs(5, c, seed=85))
+    xc = dev(oracle.scan_complex_normalized(c["lam"], c["u"]).astype(np.complex64))
+    a = host(L.scan_complex_normalized_backward(dev(c["lam"]), dev(c["u"]), xc, dev(c["gx"]))[0])
+    b = host(L.scan_complex_normalized_backward(dev(c["lam"]), dev(c["u"]), xc, dev(c["gx"]))[0])
+    assert np.array_equal(a, b)
