@@ -8,10 +8,12 @@ already resident in HBM.  Prints ONE JSON line on stdout; diagnostics go to stde
 Input/output buffer sets are rotated so that the 256 MB last-level cache (MALL) cannot
 serve a repeated call: R = ceil(2 * 256 MB / footprint) sets.
 
-``--all`` also measures the other workloads (WKV-4 forward+backward at B=8 T=4096 C=2560,
-minGRU real scan and its adjoint at B=64 T=4096 C=256, LRU complex scan and its adjoint at
-B=1 T=262144 C=1024, the RWKV token shift and its backward at B=8 T=1024 C=768 with 3 mixes)
-and writes their lines to ``--all-out`` (they are parity workloads, not the headline line).
+``--all`` also measures the other rows (WKV-4 forward, backward and gated backward at B=8
+T=4096 C=2560; the real scan, minGRU, minLSTM, the per-channel decay and their adjoints at
+B=64 T=4096 C=256; the LRU complex scan, the normalised LRU and their adjoints at B=1
+T=262144 C=1024; the RWKV token shift and its backward at B=8 T=1024 C=768 with 3 mixes),
+logs each on stderr and, with ``--all-out PATH``, writes them to PATH (they are parity
+workloads, not the headline line).
 """
 
 from __future__ import annotations
@@ -462,7 +464,7 @@ def main():
                     help="wall-clock budget of the oracle CPU baseline (0 skips it)")
     ap.add_argument("--no-copy-probe", action="store_true")
     ap.add_argument("--all", action="store_true", help="also measure the other workloads")
-    ap.add_argument("--all-out", default=os.path.join(ROOT, "gpurun_out", "bench_all.json"))
+    ap.add_argument("--all-out", default=None, help="write the --all rows to this JSON file")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -519,9 +521,10 @@ def main():
                                             (5, "scan_complex_normalized_backward", 10, 16384)):
             rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
             log("[bench] " + json.dumps(rows[-1]))
-        os.makedirs(os.path.dirname(args.all_out), exist_ok=True)
-        with open(args.all_out, "w") as f:
-            json.dump(rows, f, indent=1)
+        if args.all_out:
+            os.makedirs(os.path.dirname(os.path.abspath(args.all_out)), exist_ok=True)
+            with open(args.all_out, "w") as f:
+                json.dump(rows, f, indent=1)
 
 
 if __name__ == "__main__":
