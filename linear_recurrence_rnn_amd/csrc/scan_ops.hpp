@@ -854,7 +854,8 @@ __device__ __forceinline__ float sigmoid_neg(float k) {
 // The gated adjoints keep the RAW gate logits of row t+1 in their chunk registers (not the
 // multiplier formed from them): step j's multiplier needs row t+1 and its own derivatives
 // need row t, which is step j+1's row t+1, so each gate row is read from memory once (one
-// extra row per chunk).  Past the last row the logit is +inf, whose multiplier is 0.
+// extra row per chunk).  Past the last row the logits take values whose multiplier is 0
+// (minGRU: k_z = +inf; minLSTM: k_f = -inf, a closed forget gate).
 
 // minGRU: d_t = gx_t + sigmoid(-kz_{t+1}) d_{t+1};  dL/dkz_t = d_t z_t (1 - z_t) (h~_t - h_{t-1}),
 // dL/dh~_t = d_t z_t, dL/dx0 = (1 - z_0) d_0.
@@ -961,7 +962,7 @@ struct MinGruBwdOp : RealOp {
 struct MinLstmBwdOp : RealOp {
     using Args = MinLstmBwdArgs;
     static constexpr bool kReverse = true;
-    struct In { float f, i, g; };  // kf_{t+1} (+inf past the end), ki_{t+1}, gx_t
+    struct In { float f, i, g; };  // kf_{t+1} (-inf past the end), ki_{t+1}, gx_t
     template <int L>
     __device__ __forceinline__ static Chan chan(const Args&, int64_t) { return {}; }
     __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) { return identity(); }
@@ -999,14 +1000,14 @@ struct MinLstmBwdOp : RealOp {
         }
         const FV<VEC> gx = ldb<VEC>(R.g, voff, rows.soff(j));
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) in[e] = {last ? __builtin_inff() : fn.v[e], inn.v[e], gx.v[e]};
+        for (int e = 0; e < VEC; ++e) in[e] = {last ? -__builtin_inff() : fn.v[e], inn.v[e], gx.v[e]};
     }
     template <int VEC>
     __device__ __forceinline__ static void zero(In (&in)[VEC]) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) in[e] = {__builtin_inff(), 0.f, 0.f};
+        for (int e = 0; e < VEC; ++e) in[e] = {-__builtin_inff(), 0.f, 0.f};
     }
-    // The multiplier a = f/(f+i) of the step whose gate logits are (kf, ki); 0 for kf = +inf.
+    // The multiplier a = f/(f+i) of the step whose gate logits are (kf, ki); 0 for kf = -inf.
     __device__ __forceinline__ static float mult(float kf, float ki) {
         float a, ac;
         sigmoid_pair(logit(kf, ki), a, ac);
