@@ -48,6 +48,7 @@ BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "sca
                   "token_shift": 16,             # read x; write 3 mixes
                   "token_shift_backward": 20,    # read x, 3 gradients; write gx
                   "wkv4_backward_gated": 28,     # read k, v, r, gy; write gk, gv, gr
+                  "wkv4_forward_gated": 16,      # read k, v, r; write sigma(r) wkv
                   "scan_mingru_backward": 24,    # read kz, h, x, gx; write gkz, gh
                   "scan_minlstm_backward": 32,   # read kf, ki, h, x, gx; write gkf, gki, gh
                   "scan_real_decay_backward": 12,  # read x, gx; write gu
@@ -64,6 +65,7 @@ _SCAN_SOURCES = ("api.hip", "chunk_scan.hip", "chunk_scan.hpp", "scan_kernel.hpp
                  "device_common.hpp", "wkv_math.hpp")
 KERNEL_SOURCES = {
     "wkv4_forward": _SCAN_SOURCES,
+    "wkv4_forward_gated": _SCAN_SOURCES,
     "scan_real": _SCAN_SOURCES,
     "scan_complex": _SCAN_SOURCES,
     "scan_real_backward": _SCAN_SOURCES,
@@ -147,6 +149,18 @@ class Row:
                 self.calls.append((lib.wkv4_backward, (B, T, C, w.data_ptr(), u.data_ptr(), k.data_ptr(),
                                    v.data_ptr(), gy.data_ptr(), gw.data_ptr(), gu.data_ptr(),
                                    gk.data_ptr(), gv.data_ptr(), ws.data_ptr(), nws, stream)))
+            self.keep += [w, u]
+        elif kind == "wkv4_forward_gated":
+            w, u = to(host["w"]), to(host["u"])
+            nws = int(lib.wkv4_forward_workspace_size(B, T, C))
+            for _ in range(rotations):
+                k, v, r = to(host["k"]), to(host["v"]), to(host["r"])
+                y = torch.empty_like(k)
+                ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+                self.keep += [k, v, r, y, ws]
+                self.calls.append((lib.wkv4_forward_ex, (B, T, C, w.data_ptr(), u.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), r.data_ptr(), None, y.data_ptr(), None, ws.data_ptr(), nws,
+                                   stream)))
             self.keep += [w, u]
         elif kind == "wkv4_backward_gated":
             w, u = to(host["w"]), to(host["u"])
@@ -346,6 +360,8 @@ def cpu_baseline(kind, host, budget_s):
           "token_shift": lambda: oracle.token_shift(host["x"], host["mu"]),
           "token_shift_backward": lambda: oracle.token_shift_backward(host["x"], host["mu"], host["g"],
                                                                       want_gx_prev=False),
+          "wkv4_forward_gated": lambda: oracle.wkv4_forward_ex(host["w"], host["u"], host["k"], host["v"],
+                                                               r=host["r"]),
           "wkv4_backward_gated": lambda: oracle.wkv4_backward_gated(host["w"], host["u"], host["k"], host["v"],
                                                                     host["r"], host["gy"]),
           "scan_mingru_backward": lambda: oracle.scan_mingru_backward(host["kz"], host["h"], host["x"], host["gx"]),
@@ -401,7 +417,7 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
             host["x"] = host["h"]  # stand-in of the forward output's distribution (timing only)
     else:
         host = workloads.make_inputs(wid, shape=(B, T, C))
-    if kind == "wkv4_backward_gated":
+    if kind in ("wkv4_backward_gated", "wkv4_forward_gated"):
         host["r"] = host["v"]  # stand-in receptance ~ N(0,1) (timing only)
     if kind.endswith("_backward") and kind.startswith("scan_") and kind not in VARIANT_BWD:
         host.update(workloads.make_scan_adjoint_inputs(wid, host))
@@ -416,6 +432,8 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
             " fp32 B=%d T=%d C=%d" % (B, T, C)
     if kind == "wkv4_backward_gated":
         label = "WKV-4 backward through the sigma(r) gate fp32 B=%d T=%d C=%d" % (B, T, C)
+    if kind == "wkv4_forward_gated":
+        label = "WKV-4 forward with the sigma(r) gate fp32 B=%d T=%d C=%d" % (B, T, C)
     if kind.startswith("token_shift"):
         label = "RWKV token shift%s, %d mixes, fp32 B=%d T=%d C=%d" % (
             " backward" if kind.endswith("_backward") else "", SHIFT_M, B, T, C)
@@ -515,7 +533,7 @@ def main():
                                             (4, "scan_mingru", 20, 512), (4, "scan_minlstm", 20, 512),
                                             (4, "scan_real_decay", 20, 512), (5, "scan_complex_normalized", 10, 16384),
                                             (2, "token_shift", 50, None), (2, "token_shift_backward", 50, None),
-                                            (3, "wkv4_backward_gated", 20, 256),
+                                            (3, "wkv4_forward_gated", 20, 512), (3, "wkv4_backward_gated", 20, 256),
                                             (4, "scan_mingru_backward", 20, 512), (4, "scan_minlstm_backward", 20, 512),
                                             (4, "scan_real_decay_backward", 20, 512),
                                             (5, "scan_complex_normalized_backward", 10, 16384)):

@@ -42,8 +42,11 @@ namespace scan_kernel {
 // workgroups share a CU, so one workgroup's look-back hides behind the others' streaming.
 // Other shapes (wider chunks, or several channels per lane of WKV or complex pairs, whose
 // per-channel state is larger) spill at that budget and keep the compiler's choice.
+// The gated WKV instance also holds r per step (80 VGPRs, 6 waves per SIMD): its 8-wave
+// workgroups still fit 3 to a CU, as the SGPRs allow no more anyway.
 template <class Op, int VEC, int L>
 constexpr int scan_waves_per_eu() {
+    if (std::is_same<Op, WkvExtOp>::value && VEC * L <= 16) return 6;
     return (!Op::kReverse && VEC * L <= 16 && (VEC == 1 || std::is_same<Op, RealOp>::value)) ? 7 : 1;
 }
 

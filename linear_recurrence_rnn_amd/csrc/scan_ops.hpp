@@ -16,6 +16,8 @@
 // LRU write-up, parallelisation section: x_T = lam^{T-t} x_t + local sum over (t, T]).
 #pragma once
 
+#include <type_traits>
+
 #include "chunk_scan.hpp"
 #include "device_common.hpp"
 #include "wkv_math.hpp"
@@ -55,7 +57,11 @@ struct WkvOpT {
     static constexpr bool kParts = false;
     using Part = NoPart;
     struct Chan { float om, mu, lift, fast_lo; };  // lift = ceil(max(om, mu, 0))
-    struct In { float kk, v; };           // kk becomes g_j after phase 1
+    // kk becomes g_j after phase 1.  The gated instance also loads r with the chunk, so that
+    // its loads are in flight with k and v instead of after the look-back.
+    struct InPlain { float kk, v; };
+    struct InGated { float kk, v, r; };
+    using In = typename std::conditional<kExt, InGated, InPlain>::type;
     struct Local { float p, m0; };        // chunk exponent p and m_0 - p
     struct Agg { float a, b, p; };
 
@@ -101,35 +107,36 @@ struct WkvOpT {
     }
     // sigma(r) of the gated output (eq. (15)); 1 without a gate.
     template <int L, int VEC>
-    __device__ __forceinline__ static void gates(const Res& R, unsigned voff, const Rows& rows, int n,
-                                                 float (&sg)[L][VEC]) {
-        if constexpr (!kExt) {
+    __device__ __forceinline__ static void gates(const Res& R, const In (&in)[L][VEC], float (&sg)[L][VEC]) {
 #pragma unroll
-            for (int j = 0; j < L; ++j)
+        for (int j = 0; j < L; ++j)
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) sg[j][e] = 1.f;
-            return;
-        }
-#pragma unroll
-        for (int j = 0; j < L; ++j) {
-            FV<VEC> rr{};
-            if (R.gated && j < n) rr = ldb<VEC>(R.r, voff, rows.soff(j));
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                sg[j][e] = R.gated ? __builtin_amdgcn_rcpf(1.f + fast_exp2(-rr.v[e] * kLog2e)) : 1.f;
-        }
+            for (int e = 0; e < VEC; ++e) {
+                if constexpr (kExt) {
+                    sg[j][e] = R.gated ? __builtin_amdgcn_rcpf(1.f + fast_exp2(-in[j][e].r * kLog2e)) : 1.f;
+                } else {
+                    sg[j][e] = 1.f;
+                }
+            }
     }
     template <int VEC>
     __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
         const FV<VEC> k = ldb<VEC>(R.k, voff, rows.soff(j));
         const FV<VEC> v = ldb<VEC>(R.v, voff, rows.soff(j));
+        if constexpr (kExt) {
+            FV<VEC> r{};
+            if (R.gated) r = ldb<VEC>(R.r, voff, rows.soff(j));
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) in[e] = {k.v[e] * kLog2e, v.v[e]};
+            for (int e = 0; e < VEC; ++e) in[e] = {k.v[e] * kLog2e, v.v[e], r.v[e]};
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) in[e] = {k.v[e] * kLog2e, v.v[e]};
+        }
     }
     template <int VEC>
     __device__ __forceinline__ static void zero(In (&in)[VEC]) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) in[e] = {0.f, 0.f};
+        for (int e = 0; e < VEC; ++e) in[e] = In{};
     }
 
     template <int L, int VEC>
@@ -176,7 +183,7 @@ struct WkvOpT {
                                const In (&in)[L][VEC], const Local (&loc)[VEC], int n, unsigned voff,
                                const Rows& rows) {
         float sg[L][VEC];
-        gates<L, VEC>(R, voff, rows, n, sg);
+        gates<L, VEC>(R, in, sg);
         float a[VEC], b[VEC], cs[VEC], us[VEC];
         bool fast[VEC];
 #pragma unroll
