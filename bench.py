@@ -403,7 +403,8 @@ def copy_probe():
     return round(2 * 4 * n / s / 1e9, 1)
 
 
-def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=None):
+def make_host(wid, kind, shape=None):
+    """The seeded host inputs of one row: workload ``wid``'s generator at ``shape``."""
     from linear_recurrence_rnn_amd import workloads
 
     wl = workloads.WORKLOADS[wid]
@@ -421,6 +422,15 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
         host["r"] = host["v"]  # stand-in receptance ~ N(0,1) (timing only)
     if kind.endswith("_backward") and kind.startswith("scan_") and kind not in VARIANT_BWD:
         host.update(workloads.make_scan_adjoint_inputs(wid, host))
+    return host
+
+
+def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=None):
+    from linear_recurrence_rnn_amd import workloads
+
+    wl = workloads.WORKLOADS[wid]
+    B, T, C = shape or (wl.B, wl.T, wl.C)
+    host = make_host(wid, kind, (B, T, C))
     elements = B * T * C
     label = wl.label
     variant_labels = {"scan_mingru": "minGRU from gate logits", "scan_minlstm": "minLSTM from gate logits",
