@@ -293,6 +293,14 @@ def wkv4_backward_ex(w, u, k, v, gy, r=None, s_in=None, s_out=None, gs_out=None,
         gs_in = torch.empty((B, C, 2), dtype=torch.float32, device=dev) if want_gs_in else None
     else:
         gw, gu, gk, gv, gr, gs_in = out
+        for name, t, shape in (("gw", gw, (C,)), ("gu", gu, (C,)), ("gk", gk, (B, T, C)), ("gv", gv, (B, T, C))):
+            _expect(t, "out " + name, torch.float32, shape, dev)
+        if (gr is None) != (r is None):
+            raise ValueError("out gr must be given exactly when r is")
+        if gr is not None:
+            _expect(gr, "out gr", torch.float32, (B, T, C), dev)
+        if gs_in is not None:
+            _expect(gs_in, "out gs_in", torch.float32, (B, C, 2), dev)
     ws, nws = _workspace(int(lib.wkv4_backward_workspace_size(B, T, C)), dev, workspace)
     _check(lib.wkv4_backward_ex(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(s_in), _ptr(s_out),
                                 _ptr(gy), _ptr(gs_out), _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(gr),
