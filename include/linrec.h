@@ -31,6 +31,11 @@
  *    synchronises, allocates or frees device memory; scratch memory comes from the
  *    caller's `workspace` of at least the size the matching *_workspace_size query returns
  *    for the same (B, T, C).  A size of 0 needs no workspace (NULL is then allowed).
+ *  - Each call stamps its workspace's look-back flags with a tag drawn on the host at call
+ *    time, so stale flags of earlier calls read as unpublished and the workspace needs no
+ *    clearing.  A call recorded into a HIP graph keeps its tag on every replay: replaying
+ *    it is not supported (issue the call again instead).  Two calls in flight at the same
+ *    time must not share a workspace.
  *  - Return value: LINREC_OK or an error status.  Argument checks run before any HIP call:
  *      B, T or C negative, or B*T*C*element size overflowing int64
  *                                                         -> LINREC_ERR_INVALID_ARG

@@ -176,7 +176,7 @@ hipError_t run_part_sums(const ScanGeom& g, float* glam, bool complex_out, hipSt
 hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const ScanGeom& g, const ScanPlan& p,
                                      hipStream_t st);
 constexpr int kPartBlock = 64;  // slabs summed per first-stage block of the glam reduction
-// Writes n zero floats (a fill kernel, so that the call can be captured in a graph).
+// Writes n zero floats (a fill kernel: the library records no memset).
 hipError_t run_fill_zero(float* p, int64_t n, hipStream_t st);
 // dst[i] = src[i] for n floats (a copy kernel, for the same reason).
 hipError_t run_copy(float* dst, const float* src, int64_t n, hipStream_t st);
