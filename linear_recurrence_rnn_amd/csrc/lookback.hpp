@@ -185,4 +185,47 @@ __device__ __forceinline__ void look_back(const Chain<Agg>& ch, int64_t q, int l
     }
 }
 
+// A non-blocking attempt at look_back's result, for a coordinator that would otherwise sit
+// idle while its workgroup's other waves work: polls the flags of the 64 nearest
+// predecessors until they hold a published inclusive prefix with every aggregate after it
+// published (or, for q <= 64, every predecessor's aggregate), then folds exactly as
+// look_back does -- same records, same association, so the same bits -- and returns true.
+// Returns false, with `carry` untouched, as soon as give_up() holds; the caller then
+// publishes its aggregate and calls look_back.  Chains longer than 64 slabs without an
+// inclusive prefix in that window always end in give_up().
+template <int VEC, class Agg, class Fold, class GiveUp>
+__device__ __forceinline__ bool try_look_back(const Chain<Agg>& ch, int64_t q, int lane, Agg (&carry)[VEC],
+                                              Fold&& fold, GiveUp&& give_up) {
+    if (q == 0) return true;
+    const int64_t j = q - 1 - lane;  // lane i watches slab q-1-i
+    for (;;) {
+        const uint64_t f = j >= 0 ? __hip_atomic_load(ch.flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        const uint64_t incl_mask = __ballot(j >= 0 && f == ch.tag * 4 + kStateIncl);
+        const uint64_t pub_mask = __ballot(j >= 0 && (f >> 2) == ch.tag);
+        bool ready = false;
+        int64_t j0 = -1;
+        if (incl_mask) {
+            const int i0 = __ffsll((long long)incl_mask) - 1;  // the nearest inclusive prefix
+            const uint64_t need = i0 == 0 ? 0ull : ((1ull << i0) - 1);
+            ready = (pub_mask & need) == need;
+            j0 = q - 1 - i0;
+        } else if (q <= 64) {
+            const uint64_t need = q == 64 ? ~0ull : ((1ull << q) - 1);
+            ready = (pub_mask & need) == need;
+        }
+        if (ready) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);  // record loads stay after the polls
+            if (j0 >= 0) load_record<VEC>(ch.incl, j0, lane, carry);
+            for (int64_t jj = j0 + 1; jj < q; ++jj) {
+                Agg x[VEC];
+                load_record<VEC>(ch.agg, jj, lane, x);
+                fold(carry, x, jj);
+            }
+            return true;
+        }
+        if (give_up()) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 }  // namespace linrec

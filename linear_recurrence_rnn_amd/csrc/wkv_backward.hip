@@ -570,6 +570,8 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     __shared__ Rev shr[NW][CW];
     __shared__ double shwu[NW][CW][2];
     __shared__ RevRec sh_mine[CW];
+    __shared__ int sh_done;  // compute waves past their forward re-run (the coordinator's cue)
+    __shared__ RevRec sh_carry[CW];  // the reverse carry, when found before B3
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -717,6 +719,7 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         shwu[w][lane][0] = sw;
         shwu[w][lane][1] = su;
         shr[w][lane] = ragg;
+        if (lane == 0) __hip_atomic_fetch_add(&sh_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         __syncthreads();  // B3
         if (fr.fast && n > 0) {
             // The chunk's own part of the reverse re-run, while the coordinator looks back
@@ -797,6 +800,7 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     }
 
     // ---- coordinator ----
+    if (lane == 0) sh_done = 0;
     Fwd cin[VEC];
     fwd_carry_in<VEC, STATE>(A, g, gi, b, c0, s, lane, active, cin);  // issued before the chunks are reduced
     __syncthreads();  // B1
@@ -819,9 +823,33 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
                             reinterpret_cast<uint32_t*>(g.agg_r) + gi * g.nslab * (CW * kDwords<RevRec>),
                             reinterpret_cast<uint32_t*>(g.incl_r) + gi * g.nslab * (CW * kDwords<RevRec>), g.tag_r,
                             g.spin};
+    // carry (the state at the end of chain slab jj) followed by slab jj, earlier in time.
+    auto fold = [&](RevRec (&cr)[VEC], const RevRec (&x)[VEC], int64_t jj) {
+        const int64_t sj = g.nslab - 1 - jj;
+        const int64_t len = (g.T - sj * SLAB) < SLAB ? (g.T - sj * SLAB) : SLAB;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            cr[e].st = rev_combine(om[e], cr[e].st, x[e].st, len);
+            cr[e].sw += x[e].sw;
+            cr[e].su += x[e].su;
+        }
+    };
+    // While the chunks re-run the forward, look back for the reverse carry: the later slabs
+    // have usually published by then, and the carry is then ready when the chunks' sums are.
+    bool early;
+    {
+        RevRec c[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) c[e] = {rev_identity(), 0.0, 0.0};
+        early = try_look_back<VEC>(chn, q, lane, c, fold, [&]() {
+            return __hip_atomic_load(&sh_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= NW;
+        });
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sh_carry[lane * VEC + e] = c[e];  // parked across B3 (registers)
+    }
     __syncthreads();  // B3
-    const uint64_t first = prefetch_window(chn, q, lane);  // overlaps the slab fold and publication
     RevRec mine[VEC], carry[VEC];
+    const uint64_t first = early ? 0 : prefetch_window(chn, q, lane);  // overlaps the slab fold
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
         // Reverse sums of the slab from its start: chunks folded from the last to the first.
@@ -837,26 +865,18 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         }
         if constexpr (STATE) sw += sh_mine[lane * VEC + e].sw;
         mine[e] = {a, sw, su};
-        carry[e] = {rev_identity(), 0.0, 0.0};
         sh_mine[lane * VEC + e] = mine[e];  // kept in LDS across the look-back (registers)
     }
     const bool has_succ = s > 0;
     if (has_succ) publish<VEC>(chn, q, lane, mine, false);
-    // carry (the state at the end of chain slab jj) followed by slab jj, earlier in time.
-    auto fold = [&](RevRec (&cr)[VEC], const RevRec (&x)[VEC], int64_t jj) {
-        const int64_t sj = g.nslab - 1 - jj;
-        const int64_t len = (g.T - sj * SLAB) < SLAB ? (g.T - sj * SLAB) : SLAB;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            cr[e].st = rev_combine(om[e], cr[e].st, x[e].st, len);
-            cr[e].sw += x[e].sw;
-            cr[e].su += x[e].su;
-        }
-    };
-    auto recompute = [&](int64_t jj, RevRec (&x)[VEC]) {
-        rev_record_from_inputs<VEC, SLAB, STATE>(A, g, jj, gi, b, grp, lane, active, om, mu, x);
-    };
-    look_back<VEC, 1>(chn, q, lane, carry, fold, recompute, first);
+    for (int e = 0; e < VEC; ++e) carry[e] = sh_carry[lane * VEC + e];  // the carry, or the empty one
+    if (!early) {
+        auto recompute = [&](int64_t jj, RevRec (&x)[VEC]) {
+            rev_record_from_inputs<VEC, SLAB, STATE>(A, g, jj, gi, b, grp, lane, active, om, mu, x);
+        };
+        look_back<VEC, 1>(chn, q, lane, carry, fold, recompute, first);
+    }
     RevRec incl[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
