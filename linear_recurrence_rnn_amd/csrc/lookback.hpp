@@ -190,15 +190,15 @@ __device__ __forceinline__ void look_back(const Chain<Agg>& ch, int64_t q, int l
 // predecessors until they hold a published inclusive prefix with every aggregate after it
 // published (or, for q <= 64, every predecessor's aggregate), then folds exactly as
 // look_back does -- same records, same association, so the same bits -- and returns true.
-// Returns false, with `carry` untouched, as soon as give_up() holds; the caller then
-// publishes its aggregate and calls look_back.  Chains longer than 64 slabs without an
-// inclusive prefix in that window always end in give_up().
+// Returns false, with `carry` untouched, as soon as give_up() holds or after ch.spin polls;
+// the caller then publishes its aggregate and calls look_back.  Chains longer than 64 slabs
+// without an inclusive prefix in that window always end that way.
 template <int VEC, class Agg, class Fold, class GiveUp>
 __device__ __forceinline__ bool try_look_back(const Chain<Agg>& ch, int64_t q, int lane, Agg (&carry)[VEC],
                                               Fold&& fold, GiveUp&& give_up) {
     if (q == 0) return true;
     const int64_t j = q - 1 - lane;  // lane i watches slab q-1-i
-    for (;;) {
+    for (int it = 0;; ++it) {
         const uint64_t f = j >= 0 ? __hip_atomic_load(ch.flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
         const uint64_t incl_mask = __ballot(j >= 0 && f == ch.tag * 4 + kStateIncl);
         const uint64_t pub_mask = __ballot(j >= 0 && (f >> 2) == ch.tag);
@@ -223,7 +223,7 @@ __device__ __forceinline__ bool try_look_back(const Chain<Agg>& ch, int64_t q, i
             }
             return true;
         }
-        if (give_up()) return false;
+        if (give_up() || it >= ch.spin) return false;
         __builtin_amdgcn_s_sleep(2);
     }
 }
