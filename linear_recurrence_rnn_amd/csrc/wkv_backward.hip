@@ -539,10 +539,12 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
 // ------------------------------------------------------------------------------------
 // Gradient kernel: slabs in reverse time order (chain position q = nslab-1-s).  Waves
 // 0 .. NW-1 own one chunk each and hold its inputs and per-step values in registers; wave
-// NW (the coordinator) turns the chunk sums into carries between the compute phases:
-//   B1  chunks' forward sums in shf      -> coordinator: carry-in of each chunk, in shf
+// NW (the coordinator) handles the slab's records:
+//   B1  chunks' forward sums in shf,     -> each chunk folds its own carry-in from them; the
+//       the slab's start in sh_cin          coordinator tries the reverse look-back meanwhile
 //   B3  chunks' reverse sums in shr, and -> coordinator: slab record, look-back over the
-//       their dL/dw, dL/du in shwu           later slabs, reverse state at each chunk end, in shr
+//       their dL/dw, dL/du in shwu           later slabs (unless found already), reverse
+//                                           state at each chunk end, in shr
 // The two roles are separate branches, so the look-back's registers do not add to those
 // of the chunk data.
 // ------------------------------------------------------------------------------------
@@ -572,6 +574,7 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     __shared__ RevRec sh_mine[CW];
     __shared__ int sh_done;  // compute waves past their forward re-run (the coordinator's cue)
     __shared__ RevRec sh_carry[CW];  // the reverse carry, when found before B3
+    __shared__ Fwd sh_cin[CW];       // the forward sums at the slab's start
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -628,11 +631,13 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         float m0;
         shf[w][lane] = fwd_chunk_keep<L>(om[0], sa, vv, n, m0);
         const float p_chunk = shf[w][lane].p;
-        __syncthreads();  // B1
-        __syncthreads();  // B2: shf[w] now holds my chunk's carry-in
+        __syncthreads();  // B1: every chunk's sums are in shf, the slab's start in sh_cin
+        // My chunk's carry-in: the slab's start followed by the chunks before mine, folded by
+        // this wave itself (the waves' folds run side by side, none waits for another).
+        Fwd cin = sh_cin[lane];
+        for (int x = 0; x < w; ++x) cin = fwd_combine(om[0], cin, shf[x][lane], chunk_len<L>(x, slab_n));
 
         const float lift = ceilf(fmaxf(fmaxf(om[0], mu[0]), 0.f));
-        const Fwd cin = shf[w][lane];
         ChunkFrame fr = chunk_frame(om[0], mu[0], lift, cin, p_chunk, m0, n, gmax, n > 0 && !g.exact_only);
         double sw = 0.0, su = 0.0;
         Rev ragg = rev_identity();
@@ -801,24 +806,28 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
 
     // ---- coordinator ----
     if (lane == 0) sh_done = 0;
-    Fwd cin[VEC];
-    fwd_carry_in<VEC, STATE>(A, g, gi, b, c0, s, lane, active, cin);  // issued before the chunks are reduced
-    __syncthreads();  // B1
     {
-        // Carry-in of each chunk: the previous slab's sums (state kernel), then the chunks in order.
+        // The slab's start: the previous slab's sums (state kernel), or the carried state.
+        Fwd cin[VEC];
+        fwd_carry_in<VEC, STATE>(A, g, gi, b, c0, s, lane, active, cin);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sh_cin[lane * VEC + e] = cin[e];
+    }
+    __syncthreads();  // B1
+    if constexpr (STATE) {
+        // The last slab: dL/dw's share of the final state, from the sums at the slab's end,
+        // parked in LDS until the record.
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            Fwd c = cin[e];
-            for (int x = 0; x < NW; ++x) {
-                const Fwd chunk = shf[x][lane * VEC + e];
-                shf[x][lane * VEC + e] = c;
-                c = fwd_combine(om[e], c, chunk, chunk_len<L>(x, slab_n));
+            double v = 0.0;
+            if (q == 0 && active) {
+                Fwd c = sh_cin[lane * VEC + e];
+                for (int x = 0; x < NW; ++x) c = fwd_combine(om[e], c, shf[x][lane * VEC + e], chunk_len<L>(x, slab_n));
+                v = sw_state_out(A, g, b, c0 + e, c);
             }
-            // The last slab: dL/dw's share of the final state, parked in LDS until the record.
-            if constexpr (STATE) sh_mine[lane * VEC + e].sw = (q == 0 && active) ? sw_state_out(A, g, b, c0 + e, c) : 0.0;
+            sh_mine[lane * VEC + e].sw = v;
         }
     }
-    __syncthreads();  // B2
     const Chain<RevRec> chn{g.flags_r + gi * g.nslab,
                             reinterpret_cast<uint32_t*>(g.agg_r) + gi * g.nslab * (CW * kDwords<RevRec>),
                             reinterpret_cast<uint32_t*>(g.incl_r) + gi * g.nslab * (CW * kDwords<RevRec>), g.tag_r,
