@@ -543,8 +543,9 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
 //   B1  chunks' forward sums in shf,     -> each chunk folds its own carry-in from them; the
 //       the slab's start in sh_cin          coordinator tries the reverse look-back meanwhile
 //   B3  chunks' reverse sums in shr, and -> coordinator: slab record, look-back over the
-//       their dL/dw, dL/du in shwu           later slabs (unless found already), reverse
-//                                           state at each chunk end, in shr
+//       their dL/dw, dL/du in shwu           later slabs (unless found already), the
+//                                           reverse sums at the slab's end in sh_rend
+//   B4                                   -> each chunk folds the reverse sums at its own end
 // The two roles are separate branches, so the look-back's registers do not add to those
 // of the chunk data.
 // ------------------------------------------------------------------------------------
@@ -575,6 +576,7 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     __shared__ int sh_done;  // compute waves past their forward re-run (the coordinator's cue)
     __shared__ RevRec sh_carry[CW];  // the reverse carry, when found before B3
     __shared__ Fwd sh_cin[CW];       // the forward sums at the slab's start
+    __shared__ Rev sh_rend[CW];      // the reverse sums at the slab's end
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -748,11 +750,14 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
                 }
             }
         }
-        __syncthreads();  // B4: shr[w] now holds the reverse state at my chunk's end
+        __syncthreads();  // B4: the reverse sums at the slab's end are in sh_rend
 
         // Reverse re-run of my chunk; the outputs replace v and dL/dy's slot.
         if (n > 0) {
-            const Rev rc = shr[w][lane];
+            // The reverse sums at my chunk's end: the slab's end followed (backwards) by the
+            // chunks after mine, folded by this wave itself.
+            Rev rc = sh_rend[lane];
+            for (int x = NW - 1; x > w; --x) rc = rev_combine(om[0], rc, shr[x][lane], chunk_len<L>(x, slab_n));
             if (fr.fast) {
                 // Carry in frame units, X = x_c 2^{r_c + F0 - n om}, pre-multiplied by us:
                 // alpha_s G_s = g_s (us X + us S_s) with S_s the frame sum after s in the chunk.
@@ -903,16 +908,10 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
             if (STATE && A.gs_in) write_state_grad(A, g, b, c0 + e, incl[e].st);  // the sequence's first slab
         }
     }
-    // Reverse state at the end of each chunk: from the slab's end, backwards.
+    // The reverse sums at the slab's end; each chunk folds its own from them.
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        Rev r = (STATE && q == 0 && active) ? rev_state_out(A, g, b, c0 + e) : carry[e].st;
-        for (int x = NW - 1; x >= 0; --x) {
-            const Rev chunk = shr[x][lane * VEC + e];
-            shr[x][lane * VEC + e] = r;
-            r = rev_combine(om[e], r, chunk, chunk_len<L>(x, slab_n));
-        }
-    }
+    for (int e = 0; e < VEC; ++e)
+        sh_rend[lane * VEC + e] = (STATE && q == 0 && active) ? rev_state_out(A, g, b, c0 + e) : carry[e].st;
     __syncthreads();  // B4
 }
 
