@@ -542,9 +542,12 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
 // NW (the coordinator) handles the slab's records:
 //   B1  chunks' forward sums in shf,     -> each chunk folds its own carry-in from them; the
 //       the slab's start in sh_cin          coordinator tries the reverse look-back meanwhile
-//   B3  chunks' reverse sums in shr, and -> coordinator: slab record, look-back over the
-//       their dL/dw, dL/du in shwu           later slabs (unless found already), the
-//                                           reverse sums at the slab's end in sh_rend
+//   B3  chunks' reverse sums in shr, and -> coordinator: the reverse sums at the slab's end
+//       their dL/dw, dL/du in shwu           in sh_rend -- at once when the early look-back
+//                                           found the carry, the slab's records being formed
+//                                           and published after B4 while the chunks run;
+//                                           otherwise after publishing the aggregate and the
+//                                           look-back
 //   B4                                   -> each chunk folds the reverse sums at its own end
 // The two roles are separate branches, so the look-back's registers do not add to those
 // of the chunk data.
@@ -862,7 +865,21 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         for (int e = 0; e < VEC; ++e) sh_carry[lane * VEC + e] = c[e];  // parked across B3 (registers)
     }
     __syncthreads();  // B3
+    // The reverse sums at the slab's end: the carry (the last slab: the final state's
+    // gradient, which its record holds as well).
+    auto slab_end = [&](const RevRec (&cr)[VEC]) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            sh_rend[lane * VEC + e] = (STATE && q == 0 && active) ? rev_state_out(A, g, b, c0 + e) : cr[e].st;
+    };
     RevRec mine[VEC], carry[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) carry[e] = sh_carry[lane * VEC + e];  // the carry, or the empty one
+    if (early) {
+        // The chunks need only the carry: let them run, then form and publish the records.
+        slab_end(carry);
+        __syncthreads();  // B4
+    }
     const uint64_t first = early ? 0 : prefetch_window(chn, q, lane);  // overlaps the slab fold
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -883,8 +900,6 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     }
     const bool has_succ = s > 0;
     if (has_succ) publish<VEC>(chn, q, lane, mine, false);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) carry[e] = sh_carry[lane * VEC + e];  // the carry, or the empty one
     if (!early) {
         auto recompute = [&](int64_t jj, RevRec (&x)[VEC]) {
             rev_record_from_inputs<VEC, SLAB, STATE>(A, g, jj, gi, b, grp, lane, active, om, mu, x);
@@ -908,11 +923,10 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
             if (STATE && A.gs_in) write_state_grad(A, g, b, c0 + e, incl[e].st);  // the sequence's first slab
         }
     }
-    // The reverse sums at the slab's end; each chunk folds its own from them.
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-        sh_rend[lane * VEC + e] = (STATE && q == 0 && active) ? rev_state_out(A, g, b, c0 + e) : carry[e].st;
-    __syncthreads();  // B4
+    if (!early) {
+        slab_end(carry);
+        __syncthreads();  // B4
+    }
 }
 
 // gw[c] = sum_b part[b, c].w, gu likewise, in ascending b.
