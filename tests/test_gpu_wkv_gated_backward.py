@@ -101,3 +101,19 @@ def test_open_gate_equals_plain_backward(L):
     for a, b in zip(got[:4], plain):
         assert np.array_equal(a, b)
     assert np.max(np.abs(got[4])) < 1e-20
+
+
+def test_backward_bits_do_not_depend_on_timing(L):
+    """Three runs of a many-slab backward (2340 slabs per call): the slabs' carries come from
+    the early or the blocking look-back as timing decides, and fold the same records in the
+    same order either way, so every output is bit-identical."""
+    announce("wkv4_backward / gated: 3 runs, B=8 T=4096 C=256, bitwise")
+    d = workloads.make_inputs(3, seed=89, shape=(8, 4096, 256))
+    r = np.random.default_rng(90).standard_normal(d["k"].shape).astype(np.float32)
+    args = [dev(d[n]) for n in ("w", "u", "k", "v")]
+    runs = [[host(t) for t in L.wkv4_backward(*args, dev(d["gy"]))] for _ in range(3)]
+    runs_g = [[host(t) for t in L.wkv4_backward_gated(*args, dev(r), dev(d["gy"]))] for _ in range(3)]
+    for rr in (runs, runs_g):
+        for other in rr[1:]:
+            for a, b in zip(rr[0], other):
+                np.testing.assert_array_equal(a, b)
