@@ -52,7 +52,9 @@ BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "sca
                   "scan_mingru_backward": 24,    # read kz, h, x, gx; write gkz, gh
                   "scan_minlstm_backward": 32,   # read kf, ki, h, x, gx; write gkf, gki, gh
                   "scan_real_decay_backward": 12,  # read x, gx; write gu
-                  "scan_complex_normalized_backward": 32}  # read u, x, gx; write gu (complex64)
+                  "scan_complex_normalized_backward": 32,  # read u, x, gx; write gu (complex64)
+                  "wkv4_train_step": 32,         # forward (12) then backward (20), separate passes
+                  "wkv4_train_step_ckpt": 32}    # the same step, the backward from the forward's sums
 SHIFT_M = 3  # token-shift mixes timed: the r, k, v inputs of the time mix
 
 
@@ -77,10 +79,13 @@ KERNEL_SOURCES = {
     "token_shift": ("api.hip", "token_shift.hip", "token_shift.hpp", "device_common.hpp"),
     "token_shift_backward": ("api.hip", "token_shift.hip", "token_shift.hpp", "device_common.hpp"),
     "wkv4_backward": ("api.hip", "wkv_backward.hip", "wkv_backward.hpp", "lookback.hpp", "device_common.hpp",
-                      "wkv_math.hpp"),
+                      "wkv_math.hpp", "wkv_sums.hpp"),
     "wkv4_backward_gated": ("api.hip", "wkv_backward.hip", "wkv_backward.hpp", "lookback.hpp",
-                            "device_common.hpp", "wkv_math.hpp"),
+                            "device_common.hpp", "wkv_math.hpp", "wkv_sums.hpp"),
 }
+KERNEL_SOURCES["wkv4_train_step"] = tuple(sorted(set(_SCAN_SOURCES + KERNEL_SOURCES["wkv4_backward"])))
+KERNEL_SOURCES["wkv4_train_step_ckpt"] = tuple(sorted(set(
+    _SCAN_SOURCES + KERNEL_SOURCES["wkv4_backward"] + ("wkv_ckpt.hip", "wkv_sums.hpp"))))
 for _k in ("scan_mingru_backward", "scan_minlstm_backward", "scan_real_decay_backward",
            "scan_complex_normalized_backward"):
     KERNEL_SOURCES[_k] = _SCAN_SOURCES + ("scan_variants.hip",)
@@ -150,6 +155,39 @@ class Row:
                                    v.data_ptr(), gy.data_ptr(), gw.data_ptr(), gu.data_ptr(),
                                    gk.data_ptr(), gv.data_ptr(), ws.data_ptr(), nws, stream)))
             self.keep += [w, u]
+        elif kind in ("wkv4_train_step", "wkv4_train_step_ckpt"):
+            # One training step of the WKV layer: the forward, then the backward of its output.
+            w, u = to(host["w"]), to(host["u"])
+            ck = kind.endswith("_ckpt")
+            nfw = int(lib.wkv4_forward_ckpt_workspace_size(B, T, C) if ck else lib.wkv4_forward_workspace_size(B, T, C))
+            nbw = int(lib.wkv4_backward_ckpt_workspace_size(B, T, C) if ck else
+                      lib.wkv4_backward_workspace_size(B, T, C))
+            nck = int(lib.wkv4_checkpoint_size(B, T, C)) if ck else 0
+            fws = torch.empty(max(nfw, 1), dtype=torch.uint8, device=dev)
+            bws = torch.empty(max(nbw, 1), dtype=torch.uint8, device=dev)
+            gw = torch.empty(C, dtype=torch.float32, device=dev)
+            gu = torch.empty(C, dtype=torch.float32, device=dev)
+            self.keep += [w, u, fws, bws, gw, gu]
+            for _ in range(rotations):
+                k, v, gy = to(host["k"]), to(host["v"]), to(host["gy"])
+                y, gk, gv = torch.empty_like(k), torch.empty_like(k), torch.empty_like(k)
+                cbuf = torch.empty(max(nck, 1), dtype=torch.uint8, device=dev)
+                self.keep += [k, v, gy, y, gk, gv, cbuf]
+                p = lambda t: t.data_ptr()  # noqa: E731
+                if ck:
+                    fa = (lib.wkv4_forward_ckpt, (B, T, C, p(w), p(u), p(k), p(v), p(y), p(cbuf), nck, p(fws), nfw,
+                                                  stream))
+                    ba = (lib.wkv4_backward_ckpt, (B, T, C, p(w), p(u), p(k), p(v), p(gy), p(cbuf), nck, p(gw),
+                                                   p(gu), p(gk), p(gv), p(bws), nbw, stream))
+                else:
+                    fa = (lib.wkv4_forward, (B, T, C, p(w), p(u), p(k), p(v), p(y), p(fws), nfw, stream))
+                    ba = (lib.wkv4_backward, (B, T, C, p(w), p(u), p(k), p(v), p(gy), p(gw), p(gu), p(gk), p(gv),
+                                              p(bws), nbw, stream))
+
+                def both(fa=fa, ba=ba):
+                    st = fa[0](*fa[1])
+                    return st if st else ba[0](*ba[1])
+                self.calls.append((both, ()))
         elif kind == "wkv4_forward_gated":
             w, u = to(host["w"]), to(host["u"])
             nws = int(lib.wkv4_forward_workspace_size(B, T, C))
@@ -349,6 +387,11 @@ def cpu_baseline(kind, host, budget_s):
     fn = {"wkv4_forward": lambda: oracle.wkv4_forward(host["w"], host["u"], host["k"], host["v"]),
           "wkv4_backward": lambda: oracle.wkv4_backward(host["w"], host["u"], host["k"], host["v"],
                                                         host["gy"]),
+          "wkv4_train_step": lambda: (oracle.wkv4_forward(host["w"], host["u"], host["k"], host["v"]),
+                                      oracle.wkv4_backward(host["w"], host["u"], host["k"], host["v"], host["gy"])),
+          "wkv4_train_step_ckpt": lambda: (oracle.wkv4_forward(host["w"], host["u"], host["k"], host["v"]),
+                                           oracle.wkv4_backward(host["w"], host["u"], host["k"], host["v"],
+                                                                host["gy"])),
           "scan_real": lambda: oracle.scan_real(host["a"], host["b"]),
           "scan_complex": lambda: oracle.scan_complex(host["lam"], host["u"]),
           "scan_real_backward": lambda: oracle.scan_real_backward(host["a"], host["x"], host["gx"]),
@@ -444,6 +487,9 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
         label = "WKV-4 backward through the sigma(r) gate fp32 B=%d T=%d C=%d" % (B, T, C)
     if kind == "wkv4_forward_gated":
         label = "WKV-4 forward with the sigma(r) gate fp32 B=%d T=%d C=%d" % (B, T, C)
+    if kind.startswith("wkv4_train_step"):
+        label = "WKV-4 training step (forward, then backward%s) fp32 B=%d T=%d C=%d" % (
+            " from the forward's kept sums" if kind.endswith("_ckpt") else "", B, T, C)
     if kind.startswith("token_shift"):
         label = "RWKV token shift%s, %d mixes, fp32 B=%d T=%d C=%d" % (
             " backward" if kind.endswith("_backward") else "", SHIFT_M, B, T, C)
@@ -546,7 +592,8 @@ def main():
                                             (3, "wkv4_forward_gated", 20, 512), (3, "wkv4_backward_gated", 20, 256),
                                             (4, "scan_mingru_backward", 20, 512), (4, "scan_minlstm_backward", 20, 512),
                                             (4, "scan_real_decay_backward", 20, 512),
-                                            (5, "scan_complex_normalized_backward", 10, 16384)):
+                                            (5, "scan_complex_normalized_backward", 10, 16384),
+                                            (3, "wkv4_train_step", 10, 256), (3, "wkv4_train_step_ckpt", 10, 256)):
             rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
             log("[bench] " + json.dumps(rows[-1]))
         if args.all_out:

@@ -249,6 +249,46 @@ int wkv4_backward_ex(int64_t B, int64_t T, int64_t C,
                      float *gs_in, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Checkpointed training step of WKV-4 (eq. (14); the pages give no backward, whose chain
+ * rule needs the forward sums A, B and their derivatives A', B' in w at every step).
+ * wkv4_backward recomputes, in a pass of its own over k and v, those sums at the start of
+ * every slab of its gradient kernel.  A forward that is
+ * followed by a backward can keep those sums instead:
+ *
+ *   wkv4_forward_ckpt   writes y exactly as wkv4_forward (to rounding), and the sums at the
+ *                       end of every slab into ckpt;
+ *   wkv4_backward_ckpt  writes gw, gu, gk, gv exactly as wkv4_backward (to rounding) from
+ *                       the same w, u, k, v, gy and that ckpt, without the extra pass.
+ *
+ *   ckpt  device buffer of at least wkv4_checkpoint_size(B, T, C) bytes, 16-byte aligned,
+ *         owned by the caller.  Its contents are opaque (float64 sums with an integer
+ *         exponent per channel and slab); they are valid only for the B, T, C, w and k, v of
+ *         the forward that wrote them, and only after that forward has completed in stream
+ *         order.  The backward only reads it.
+ *   other arguments as for wkv4_forward / wkv4_backward.  No carried state and no gate:
+ *   those calls stay with wkv4_forward_ex / wkv4_backward_ex.
+ *
+ * Workspaces: wkv4_forward_ckpt_workspace_size and wkv4_backward_ckpt_workspace_size (the
+ * latter smaller than wkv4_backward's: no state pass).  Errors as for the other calls, and
+ * a ckpt smaller than wkv4_checkpoint_size -> LINREC_ERR_WORKSPACE, NULL -> INVALID_ARG,
+ * misaligned -> UNSUPPORTED.  B, T or C = 0: the forward does nothing; the backward
+ * zero-fills gw and gu (when C > 0).  The slab length of the checkpoints is fixed by the
+ * library (56 steps) and does not follow the tuning overrides of the plain calls.
+ */
+size_t wkv4_checkpoint_size(int64_t B, int64_t T, int64_t C);
+size_t wkv4_forward_ckpt_workspace_size(int64_t B, int64_t T, int64_t C);
+size_t wkv4_backward_ckpt_workspace_size(int64_t B, int64_t T, int64_t C);
+int wkv4_forward_ckpt(int64_t B, int64_t T, int64_t C,
+                      const float *w, const float *u, const float *k, const float *v,
+                      float *y, void *ckpt, size_t ckpt_bytes,
+                      void *workspace, size_t ws_bytes, void *stream);
+int wkv4_backward_ckpt(int64_t B, int64_t T, int64_t C,
+                       const float *w, const float *u, const float *k, const float *v,
+                       const float *gy, const void *ckpt, size_t ckpt_bytes,
+                       float *gw, float *gu, float *gk, float *gv,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Real diagonal scan, "Were RNNs All We Needed?" page, minGRU section (v_t = a_t (.)
  * v_{t-1} + b_t):  x[b,t,c] = a[b,t,c] * x[b,t-1,c] + b[b,t,c],  x[b,-1,c] = x0[b,c].
  *

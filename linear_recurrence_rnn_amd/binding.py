@@ -52,7 +52,8 @@ def load(path: str | None = None):
         lib.linrec_status_string.restype = ctypes.c_char_p
         lib.linrec_status_string.argtypes = [ctypes.c_int]
         lib.linrec_last_error.restype = ctypes.c_char_p
-        for name in ("wkv4_forward_workspace_size", "wkv4_backward_workspace_size"):
+        for name in ("wkv4_forward_workspace_size", "wkv4_backward_workspace_size", "wkv4_checkpoint_size",
+                     "wkv4_forward_ckpt_workspace_size", "wkv4_backward_ckpt_workspace_size"):
             getattr(lib, name).restype = _SZ
             getattr(lib, name).argtypes = [_I64, _I64, _I64]
         lib.linrec_scan_workspace_size.restype = _SZ
@@ -74,6 +75,10 @@ def load(path: str | None = None):
         lib.rwkv_token_shift_backward.argtypes = [_I64, _I64, _I64, _I64] + [_VP] * 7 + [_VP, _SZ, _VP]
         lib.wkv4_backward_ex.restype = ctypes.c_int
         lib.wkv4_backward_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 15 + [_VP, _SZ, _VP]
+        lib.wkv4_forward_ckpt.restype = ctypes.c_int
+        lib.wkv4_forward_ckpt.argtypes = [_I64, _I64, _I64] + [_VP] * 6 + [_SZ, _VP, _SZ, _VP]
+        lib.wkv4_backward_ckpt.restype = ctypes.c_int
+        lib.wkv4_backward_ckpt.argtypes = [_I64, _I64, _I64] + [_VP] * 6 + [_SZ] + [_VP] * 4 + [_VP, _SZ, _VP]
         lib.wkv4_decode_step.restype = ctypes.c_int
         lib.wkv4_decode_step.argtypes = [_I64, _I64] + [_VP] * 7 + [_VP]
         lib.wkv4_backward.argtypes = [_I64, _I64, _I64] + [_VP] * 9 + [_VP, _SZ, _VP]
@@ -335,6 +340,65 @@ def wkv4_backward(w, u, k, v, gy, out=None, workspace=None):
     _check(lib.wkv4_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy), _ptr(gw),
                              _ptr(gu), _ptr(gk), _ptr(gv), _ptr(ws), nws, _stream(dev)),
            "wkv4_backward")
+    return gw, gu, gk, gv
+
+
+def wkv4_checkpoint_size(B: int, T: int, C: int) -> int:
+    """Bytes of the checkpoint buffer of wkv4_forward_ckpt / wkv4_backward_ckpt."""
+    return int(load().wkv4_checkpoint_size(B, T, C))
+
+
+def wkv4_forward_ckpt(w, u, k, v, out=None, workspace=None):
+    """(y, ckpt): y as wkv4_forward, and ckpt (uint8 device buffer) holding the forward sums
+    that wkv4_backward_ckpt starts its slabs from.  ``out`` = (y, ckpt) to reuse buffers."""
+    lib = load()
+    B, T, C = k.shape
+    dev = k.device
+    _expect(k, "k", torch.float32, (B, T, C), dev)
+    _expect(v, "v", torch.float32, (B, T, C), dev)
+    _expect(w, "w", torch.float32, (C,), dev)
+    _expect(u, "u", torch.float32, (C,), dev)
+    nck = int(lib.wkv4_checkpoint_size(B, T, C))
+    if out is None:
+        y = torch.empty_like(k)
+        ckpt = torch.empty(nck, dtype=torch.uint8, device=dev)
+    else:
+        y, ckpt = out
+        _expect(y, "out[0]", torch.float32, (B, T, C), dev)
+        _expect(ckpt, "out[1]", torch.uint8, (nck,), dev)
+    ws, nws = _workspace(int(lib.wkv4_forward_ckpt_workspace_size(B, T, C)), dev, workspace)
+    _check(lib.wkv4_forward_ckpt(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(ckpt), nck,
+                                 _ptr(ws), nws, _stream(dev)), "wkv4_forward_ckpt")
+    return y, ckpt
+
+
+def wkv4_backward_ckpt(w, u, k, v, gy, ckpt, out=None, workspace=None):
+    """(gw, gu, gk, gv) as wkv4_backward, from the ckpt that wkv4_forward_ckpt wrote for the
+    same w, u, k, v."""
+    lib = load()
+    B, T, C = k.shape
+    dev = k.device
+    for name, t in (("k", k), ("v", v), ("gy", gy)):
+        _expect(t, name, torch.float32, (B, T, C), dev)
+    _expect(w, "w", torch.float32, (C,), dev)
+    _expect(u, "u", torch.float32, (C,), dev)
+    nck = int(lib.wkv4_checkpoint_size(B, T, C))
+    _expect(ckpt, "ckpt", torch.uint8, (nck,), dev)
+    if out is None:
+        gw = torch.empty(C, dtype=torch.float32, device=dev)
+        gu = torch.empty(C, dtype=torch.float32, device=dev)
+        gk = torch.empty_like(k)
+        gv = torch.empty_like(k)
+    else:
+        gw, gu, gk, gv = out
+        _expect(gw, "out[0]", torch.float32, (C,), dev)
+        _expect(gu, "out[1]", torch.float32, (C,), dev)
+        _expect(gk, "out[2]", torch.float32, (B, T, C), dev)
+        _expect(gv, "out[3]", torch.float32, (B, T, C), dev)
+    ws, nws = _workspace(int(lib.wkv4_backward_ckpt_workspace_size(B, T, C)), dev, workspace)
+    _check(lib.wkv4_backward_ckpt(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy), _ptr(ckpt), nck,
+                                  _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(ws), nws, _stream(dev)),
+           "wkv4_backward_ckpt")
     return gw, gu, gk, gv
 
 

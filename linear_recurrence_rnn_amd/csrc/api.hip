@@ -685,6 +685,86 @@ LINREC_API int wkv4_backward_ex(int64_t B, int64_t T, int64_t C, const float* w,
     return hip_status(linrec::run_wkv_backward(A, g, p, (hipStream_t)stream), "wkv4_backward launch");
 }
 
+LINREC_API size_t wkv4_checkpoint_size(int64_t B, int64_t T, int64_t C) {
+    if (B < 0 || T < 0 || C < 0 || B == 0 || T == 0 || C == 0) return 0;
+    return linrec::wkv_ckpt_bytes(B, T, C);
+}
+
+LINREC_API size_t wkv4_forward_ckpt_workspace_size(int64_t B, int64_t T, int64_t C) {
+    if (B < 0 || T < 0 || C < 0 || B == 0 || T == 0 || C == 0) return 0;
+    return linrec::wkv_ckpt_forward_ws_bytes(B, T, C);
+}
+
+LINREC_API size_t wkv4_backward_ckpt_workspace_size(int64_t B, int64_t T, int64_t C) {
+    if (B < 0 || T < 0 || C < 0 || B == 0 || T == 0 || C == 0) return 0;
+    return linrec::wkv_backward_ckpt_ws_bytes(B, T, C);
+}
+
+namespace {
+int check_ckpt(const void* ckpt, size_t ckpt_bytes, size_t need) {
+    if (ckpt_bytes < need)
+        return fail(LINREC_ERR_WORKSPACE, "checkpoint buffer of %zu bytes, need %zu", ckpt_bytes, need);
+    if (ckpt == nullptr) return fail(LINREC_ERR_INVALID_ARG, "checkpoint buffer is NULL");
+    if (!aligned(ckpt, 16)) return fail(LINREC_ERR_UNSUPPORTED, "checkpoint buffer not 16-byte aligned");
+    return LINREC_OK;
+}
+}  // namespace
+
+LINREC_API int wkv4_forward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                                 const float* k, const float* v, float* y, void* ckpt, size_t ckpt_bytes,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+    int st = check_shape(B, T, C, 4);
+    if (st) return st;
+    if (B == 0 || T == 0 || C == 0) return ok();
+    if (!w || !u || !k || !v || !y) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void* ptrs[] = {w, u, k, v, y};
+    for (const void* p : ptrs)
+        if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    if ((st = check_ckpt(ckpt, ckpt_bytes, linrec::wkv_ckpt_bytes(B, T, C)))) return st;
+    if ((st = check_ws(workspace, ws_bytes, linrec::wkv_ckpt_forward_ws_bytes(B, T, C)))) return st;
+    const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0, nullptr, nullptr, nullptr};
+    // Coordination in a wave of its own by default; LINREC_COORD=1 puts it in wave 0.
+    const bool sep = env_int("LINREC_COORD", 0) != 1;
+    return hip_status(linrec::run_wkv_forward_ckpt(A, B, T, C, ckpt, workspace, next_tag(), spin_limit(), sep,
+                                                   (hipStream_t)stream),
+                      "wkv4_forward_ckpt launch");
+}
+
+LINREC_API int wkv4_backward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                                  const float* k, const float* v, const float* gy, const void* ckpt,
+                                  size_t ckpt_bytes, float* gw, float* gu, float* gk, float* gv, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+    int st = check_shape(B, T, C, 4);
+    if (st) return st;
+    if (C > 0 && (!gw || !gu)) return fail(LINREC_ERR_INVALID_ARG, "gw or gu is NULL");
+    if (B == 0 || T == 0 || C == 0) {
+        if (C == 0) return ok();
+        if (!aligned(gw, 4) || !aligned(gu, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+        return hip_status(linrec::run_zero_wu(gw, gu, C, (hipStream_t)stream), "wkv4_backward_ckpt zero-fill");
+    }
+    if (!w || !u || !k || !v || !gy || !gk || !gv)
+        return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void* ptrs[] = {w, u, k, v, gy, gw, gu, gk, gv};
+    for (const void* p : ptrs)
+        if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    if ((st = check_ckpt(ckpt, ckpt_bytes, linrec::wkv_ckpt_bytes(B, T, C)))) return st;
+    const linrec::BwdPlan p = linrec::wkv_backward_plan(1, B, T, C, 0, 0);  // the checkpoints' slabs
+    if ((st = check_ws(workspace, ws_bytes, linrec::wkv_backward_ckpt_ws_bytes(B, T, C)))) return st;
+    const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    linrec::BwdGeom g{};
+    g.B = B;
+    g.T = T;
+    g.C = C;
+    g.ngrp = ceil_div(C, 64);
+    g.nslab = p.nslab;
+    g.spin = spin_limit();
+    g.tag_f = next_tag();
+    g.tag_r = next_tag();
+    g.exact_only = env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0;
+    linrec::wkv_backward_layout_ckpt(p, B, C, workspace, ckpt, g);
+    return hip_status(linrec::run_wkv_backward(A, g, p, (hipStream_t)stream), "wkv4_backward_ckpt launch");
+}
+
 LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
                              const float* k, const float* v, const float* gy, float* gw, float* gu,
                              float* gk, float* gv, void* workspace, size_t ws_bytes, void* stream) {

@@ -148,7 +148,8 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
                 }
             }
         };
-        constexpr int KB = VEC >= 4 ? 2 : (VEC == 2 ? 4 : 8);
+        // Records in flight per lane: fewer for the wide (float64) aggregates.
+        constexpr int KB = (VEC >= 4 || kDwords<Agg> > 4) ? 2 : (VEC == 2 ? 4 : 8);
         look_back<VEC, KB>(chn, s, lane, carry, fold, recompute, first);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {

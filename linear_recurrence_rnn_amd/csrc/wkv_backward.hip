@@ -38,6 +38,7 @@
 #include "lookback.hpp"
 #include "wkv_backward.hpp"
 #include "wkv_math.hpp"
+#include "wkv_sums.hpp"
 
 namespace linrec {
 
@@ -45,26 +46,13 @@ namespace {
 
 __device__ __forceinline__ float gate_sigmoid(float r) { return __builtin_amdgcn_rcpf(1.f + fast_exp2(-r * kLog2e)); }
 
-// Forward sums over a span: A = a 2^p, B = b 2^p, A' = ad 2^p, B' = bd 2^p.
-struct Fwd { double a, b, ad, bd; float p; };
 // Reverse sums: G-like = x 2^r, H-like = h 2^r; z 2^r is the sum of the (positive) weights,
 // which x and h can cancel below, and sets the exponent.
 struct Rev { double x, h, z; float r; };
 // Reverse look-back record: the reverse sums of a run of slabs and their dL/dw, dL/du sums.
 struct RevRec { Rev st; double sw, su; };
 
-__device__ __forceinline__ Fwd fwd_identity() { return {0.0, 0.0, 0.0, 0.0, kEmpty}; }
 __device__ __forceinline__ Rev rev_identity() { return {0.0, 0.0, 0.0, kEmpty}; }
-
-// State s1, then a span s2 of n2 steps:
-//   A = eps^n2 A1 + A2,   A' = eps^n2 (A'1 + n2 A1) + A'2   (B, B' likewise).
-__device__ __forceinline__ Fwd fwd_combine(float om, const Fwd& s1, const Fwd& s2, int64_t n2) {
-    float p, f1, f2;
-    merge_scales(s1.p, (float)s1.b, s2.p, (float)s2.b, mul_split((float)n2, om), p, f1, f2);
-    const double g1 = f1, g2 = f2, fn = (double)n2;
-    return {fma(s1.a, g1, s2.a * g2), fma(s1.b, g1, s2.b * g2), fma(fma(fn, s1.a, s1.ad), g1, s2.ad * g2),
-            fma(fma(fn, s1.b, s1.bd), g1, s2.bd * g2), p};
-}
 
 // Reverse sums: s1 is the state at the end of an earlier span s2 of n2 steps; the result is
 // the state at the start of s2:  X = s2 + eps^n2 s1.
@@ -163,17 +151,6 @@ __device__ __forceinline__ ChunkFrame chunk_frame(float om, float mu, float lift
     const float cur_lo = (m0 + ls) + mu;                  // log2 of cur_0
     f.fast = allow && fmaxf(carry_lo, cur_lo) >= kBwdFastLo && gmax < kBwdGradMax;
     return f;
-}
-
-// The forward sums advanced past one step (kj = k log2 e).
-__device__ __forceinline__ void fwd_advance(float om, Fwd& s, float kj, double vj, float M) {
-    const float q2 = ceilf(fmaxf(M - om, kj));
-    const double f1 = fast_exp2((s.p - q2) - om), f2 = fast_exp2(kj - q2);
-    s.ad = (s.ad + s.a) * f1;  // A'_{t+1} = eps (A'_t + A_t)
-    s.bd = (s.bd + s.b) * f1;
-    s.a = fma(s.a, f1, vj * f2);
-    s.b = fma(s.b, f1, f2);
-    s.p = q2;
 }
 
 // One forward step from the sums over i < t: the step's values that the reverse needs
@@ -975,7 +952,7 @@ hipError_t resident_blocks(const void* kernel, int threads, std::atomic<int> (&c
 template <int VEC, int NW, int L>
 hipError_t launch(const WkvBwdArgs& A, const BwdGeom& g, hipStream_t st) {
     const int64_t G = g.B * g.ngrp;
-    if (g.nslab > 1) {
+    if (g.nslab > 1 && !g.from_ckpt) {
         // Persistent grid: no more workgroups than are resident together.
         const auto kern = wkv_bwd_state_kernel<NW, L>;
         static std::atomic<int> cache[kMaxDev];
@@ -1067,6 +1044,33 @@ void wkv_backward_layout(const BwdPlan& p, int64_t B, int64_t C, void* ws, BwdGe
     g.incl_c = at, at += cr;
     g.incl_f = at, at += fr;
     g.flags_r = reinterpret_cast<uint64_t*>(at), at += fl;
+    g.agg_r = at, at += rr;
+    g.incl_r = at;
+}
+
+size_t wkv_backward_ckpt_ws_bytes(int64_t B, int64_t T, int64_t C) {
+    const BwdPlan p = wkv_backward_plan(1, B, T, C, 0, 0);
+    size_t bytes = align256((size_t)(B * C) * 2 * sizeof(double));  // part
+    if (p.nslab > 1) {
+        const int64_t nrec = B * ((C + 63) / 64) * p.nslab;
+        bytes += align256((size_t)nrec * 8);                          // reverse flags
+        bytes += 2 * align256((size_t)(nrec * 64) * sizeof(RevRec));  // reverse records
+    }
+    return bytes;
+}
+
+void wkv_backward_layout_ckpt(const BwdPlan& p, int64_t B, int64_t C, void* ws, const void* ckpt, BwdGeom& g) {
+    char* at = (char*)ws;
+    g.part = reinterpret_cast<double*>(at);
+    at += align256((size_t)(B * C) * 2 * sizeof(double));
+    g.flags_c = g.flags_r = nullptr;
+    g.agg_c = g.incl_c = g.incl_f = g.agg_r = g.incl_r = nullptr;
+    g.from_ckpt = 1;
+    if (p.nslab <= 1) return;
+    const int64_t nrec = B * ((C + 63) / 64) * p.nslab;
+    const size_t rr = align256((size_t)(nrec * 64) * sizeof(RevRec));
+    g.incl_f = const_cast<void*>(ckpt);  // read only
+    g.flags_r = reinterpret_cast<uint64_t*>(at), at += align256((size_t)nrec * 8);
     g.agg_r = at, at += rr;
     g.incl_r = at;
 }

@@ -44,6 +44,7 @@ struct BwdGeom {
     void* incl_r;
     double* part;           // (B, C, 2) dL/dw, dL/du of each batch row
     int exact_only;         // 1: the gradient kernel never takes its frame fast path (tests)
+    int from_ckpt;          // 1: incl_f holds a checkpointing forward's sums; no state kernel
 };
 
 struct BwdPlan {
@@ -64,5 +65,18 @@ hipError_t run_wkv_backward(const WkvBwdArgs& A, const BwdGeom& g, const BwdPlan
 hipError_t run_zero_wu(float* gw, float* gu, int64_t C, hipStream_t st);
 // No tokens: the state passes through, so gs_in = gs_out e^{p_in - p_out} (zero without gs_out).
 hipError_t run_state_grad_passthrough(const WkvBwdArgs& A, int64_t B, int64_t C, hipStream_t st);
+
+// The checkpointing forward (wkv_ckpt.hip): y as wkv4_forward, and the forward sums at the end
+// of every slab of the default backward plan written to ckpt (the layout of incl_f).
+// Checkpoint bytes, forward workspace bytes, and the launch (ws holds flags and aggregates).
+size_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C);
+size_t wkv_ckpt_forward_ws_bytes(int64_t B, int64_t T, int64_t C);
+struct WkvArgs;
+// The backward from such checkpoints: workspace bytes (dL/dw, dL/du rows and the reverse
+// look-back only) and the layout, with incl_f = ckpt and the state kernel skipped.
+size_t wkv_backward_ckpt_ws_bytes(int64_t B, int64_t T, int64_t C);
+void wkv_backward_layout_ckpt(const BwdPlan& p, int64_t B, int64_t C, void* ws, const void* ckpt, BwdGeom& g);
+hipError_t run_wkv_forward_ckpt(const WkvArgs& A, int64_t B, int64_t T, int64_t C, void* ckpt, void* ws,
+                                uint64_t tag, int spin, bool sep, hipStream_t st);
 
 }  // namespace linrec

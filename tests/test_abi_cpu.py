@@ -294,3 +294,38 @@ def test_wkv4_backward_ex_argument_checks(lib):
     # workspace, required pointers
     assert call(ws=16) == WORKSPACE
     assert call(gy=None) == INVALID
+
+def test_wkv4_checkpoint_argument_checks(lib):
+    B, T, C = 2, 1000, 64
+    nck = lib.wkv4_checkpoint_size(B, T, C)
+    nfw = lib.wkv4_forward_ckpt_workspace_size(B, T, C)
+    nbw = lib.wkv4_backward_ckpt_workspace_size(B, T, C)
+    # one record (4 float64 sums and an exponent, padded to 40 bytes) per slab of 56 steps,
+    # channel and batch row; the backward's workspace drops the state pass
+    assert nck == B * C * ((T + 55) // 56) * 40
+    assert 0 < nbw < lib.wkv4_backward_workspace_size(B, T, C)
+    assert nfw > 0
+    assert lib.wkv4_checkpoint_size(0, T, C) == 0 and lib.wkv4_checkpoint_size(-1, T, C) == 0
+
+    def fw(ck=P2, nc=nck, ws=P, nws=nfw, y=P2, k=P):
+        return lib.wkv4_forward_ckpt(B, T, C, P, P, k, P, y, ck, nc, ws, nws, None)
+
+    def bw(ck=P2, nc=nck, ws=P, nws=nbw, gy=P, gw=P2):
+        return lib.wkv4_backward_ckpt(B, T, C, P, P, P, P, gy, ck, nc, gw, P2, P2, P2, ws, nws, None)
+
+    for f in (fw, bw):
+        assert f(nc=nck - 1) == WORKSPACE
+        assert b"checkpoint" in lib.linrec_last_error()
+        assert f(ck=None) == INVALID
+        assert f(ck=ctypes.c_void_p(0x200008)) == UNSUPPORTED
+        assert f(nws=16) == WORKSPACE
+        assert f(ws=None) == INVALID
+    assert fw(y=None) == INVALID
+    assert fw(k=ODD) == UNSUPPORTED
+    assert bw(gy=None) == INVALID
+    assert bw(gw=None) == INVALID
+    assert lib.wkv4_forward_ckpt(-1, T, C, P, P, P, P, P2, P2, nck, P, nfw, None) == INVALID
+    # empty shapes return before any launch: nothing to do (B = 0), nothing read
+    assert lib.wkv4_forward_ckpt(0, T, C, None, None, None, None, None, None, 0, None, 0, None) == OK
+    assert lib.wkv4_backward_ckpt(B, T, 0, None, None, None, None, None, None, 0, None, None, None, None,
+                                  None, 0, None) == OK

@@ -71,10 +71,12 @@ def check_bwd(got, ref, tol=TOL):
     T = gk.shape[1]
     errs = {"gk": rel_err(gk, rk), "gv": rel_err(gv, rv)}
     if T == 1:
-        # One step: y_0 = v_0 exactly, so dL/dw = dL/du = 0; the oracle's values are its
-        # own rounding noise (~1e-17), so compare absolutely.
+        # One step: y_0 = v_0 exactly, so dL/dw = dL/du = 0 and dL/dk_0 = 0 (no later step
+        # feeds G or H); the oracle's values are its own rounding noise (~1e-16), so
+        # compare absolutely, dL/dk against a bound far below any real value.
         errs["gw"] = float(np.max(np.abs(gw - rw)))
         errs["gu"] = float(np.max(np.abs(gu - ru)))
+        errs["gk"] = float(np.max(np.abs(gk - rk))) * (TOL / 1e-6)
     else:
         errs["gw"] = rel_err(gw, rw, None)
         errs["gu"] = rel_err(gu, ru, None)

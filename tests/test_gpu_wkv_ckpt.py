@@ -1,0 +1,157 @@
+"""GPU parity of the checkpointed WKV-4 training step (wkv4_forward_ckpt, then
+wkv4_backward_ckpt from the sums the forward kept) against the fp64 oracle.
+
+The forward's y and the backward's gradients are held to the same bounds as the plain
+calls (RMS-floored relative error 1e-4, ``oracle.compare``); the gradients are also
+compared with those of wkv4_backward, which finds the same sums in a pass of its own.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.compare import rel_err
+from linear_recurrence_rnn_amd import workloads
+
+from test_gpu_parity import TOL, announce, check_bwd, dev, host, gpu_wkv_bwd
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    import torch  # noqa: F401
+    from linear_recurrence_rnn_amd import binding
+    binding.load()
+    return binding
+
+
+def ckpt_step(L, d):
+    """(y, (gw, gu, gk, gv), ckpt bytes) of the checkpointed step, on the host."""
+    w, u, k, v = dev(d["w"]), dev(d["u"]), dev(d["k"]), dev(d["v"])
+    y, ck = L.wkv4_forward_ckpt(w, u, k, v)
+    grads = L.wkv4_backward_ckpt(w, u, k, v, dev(d["gy"]), ck)
+    return host(y), [host(t) for t in grads], host(ck)
+
+
+def check_step(L, d, compare_plain=True):
+    ref_y = oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])
+    ref_g = oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    y, g, _ = ckpt_step(L, d)
+    assert rel_err(y, ref_y) <= TOL, rel_err(y, ref_y)
+    check_bwd(g, ref_g)
+    if compare_plain and d["k"].shape[1] > 1:
+        plain = gpu_wkv_bwd(L, d)
+        for name, a, b in zip(("gw", "gu", "gk", "gv"), g, plain):
+            ax = None if name in ("gw", "gu") else 1
+            assert rel_err(a, b.astype(np.float64), ax) <= 2 * TOL, name
+
+
+SHAPES = [(1, 1, 4), (3, 1000, 40), (2, 333, 37), (1, 17, 1), (4, 2049, 20), (2, 64, 16), (2, 56, 64),
+          (2, 57, 65), (3, 112, 130)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+def test_ckpt_step_shapes(L, shape):
+    # Ragged last slabs, partial channel groups, one-slab sequences (T <= 56: no sums kept),
+    # and exact multiples of the slab.
+    announce("wkv4 checkpointed step shape %s" % (shape,))
+    check_step(L, workloads.make_inputs(3, seed=31, shape=shape))
+
+
+def test_ckpt_step_workload3(L):
+    announce("wkv4 checkpointed step B=8 T=4096 C=2560")
+    check_step(L, workloads.make_inputs(3), compare_plain=False)
+
+
+def test_ckpt_step_spikes(L):
+    announce("wkv4 checkpointed step, k spikes +-150, w in {0, 1e4}")
+    d = workloads.make_inputs(3, seed=32, shape=(2, 700, 32))
+    d["k"][0, 100, :] = 150.0
+    d["k"][1, 350, 3] = -150.0
+    d["k"][1, 20:40, 5] = 120.0
+    d["w"][0] = 0.0
+    d["w"][1] = 1e4
+    check_step(L, d)
+
+
+def test_ckpt_step_exact_path(L, monkeypatch):
+    # Both kernels without their frame fast paths (the exact per-step running maximum).
+    announce("wkv4 checkpointed step, exact-only paths")
+    monkeypatch.setenv("LINREC_WKV_EXACT", "1")
+    check_step(L, workloads.make_inputs(3, seed=33, shape=(2, 1500, 96)))
+
+
+@pytest.mark.parametrize("spin", ["0", "1"])
+def test_ckpt_step_lookback_recompute(L, monkeypatch, spin):
+    # With no (or one) poll, slabs that have not published are recomputed from their
+    # inputs step by step (the float64 sums advanced one step at a time).
+    announce("wkv4 checkpointed step with LINREC_SPIN=%s" % spin)
+    monkeypatch.setenv("LINREC_SPIN", spin)
+    d = workloads.make_inputs(3, seed=34, shape=(2, 1300, 130))
+    d["k"][1, 600, 7] = 140.0
+    check_step(L, d)
+
+
+def test_ckpt_forward_coordinator_in_wave0(L, monkeypatch):
+    announce("wkv4_forward_ckpt with the coordination in wave 0")
+    monkeypatch.setenv("LINREC_COORD", "1")
+    check_step(L, workloads.make_inputs(3, seed=35, shape=(2, 1001, 150)))
+
+
+def test_ckpt_ignores_backward_shape_overrides(L, monkeypatch):
+    # The checkpoints' slabs are fixed (56 steps): tuning overrides of the plain backward's
+    # slab shape must not change them.
+    announce("wkv4 checkpointed step with LINREC_BWD_NW/L overrides set")
+    monkeypatch.setenv("LINREC_BWD_NW", "8")
+    monkeypatch.setenv("LINREC_BWD_L", "8")
+    check_step(L, workloads.make_inputs(3, seed=36, shape=(2, 1001, 70)))
+
+
+def test_ckpt_long_single_sequence(L):
+    # More than 64 slabs in one chain (several look-back windows).
+    announce("wkv4 checkpointed step B=1 T=20000 C=64")
+    check_step(L, workloads.make_inputs(3, seed=37, shape=(1, 20000, 64)))
+
+
+def test_ckpt_step_is_deterministic_and_buffers_reusable(L):
+    # Bit-identical outputs and checkpoints on a repeat; a checkpoint buffer (and the
+    # workspaces) reused by a forward on other inputs serves that forward's backward.
+    announce("wkv4 checkpointed step: repeat, then reuse of the buffers")
+    import torch
+    d1 = workloads.make_inputs(3, seed=38, shape=(2, 900, 128))
+    d2 = workloads.make_inputs(3, seed=39, shape=(2, 900, 128))
+    y1, g1, c1 = ckpt_step(L, d1)
+    y1b, g1b, c1b = ckpt_step(L, d1)
+
+    def sums(c):
+        # records of 10 dwords per lane (four float64 sums, the exponent, one padding dword)
+        # per slab and channel group of 64; the last slab's record is never written
+        r = c.view(np.uint32).reshape(2 * 2, 17, 10, 64)
+        return r[:, :16, :9, :]
+
+    assert np.array_equal(y1, y1b) and np.array_equal(sums(c1), sums(c1b))
+    for a, b in zip(g1, g1b):
+        assert np.array_equal(a, b)
+    w, u, k, v = dev(d2["w"]), dev(d2["u"]), dev(d2["k"]), dev(d2["v"])
+    nck = L.wkv4_checkpoint_size(2, 900, 128)
+    ck = torch.from_numpy(c1.copy()).cuda()  # the first input's sums, to be overwritten
+    assert ck.numel() == nck
+    fws = torch.empty(L.load().wkv4_forward_ckpt_workspace_size(2, 900, 128), dtype=torch.uint8, device="cuda")
+    y2, _ = L.wkv4_forward_ckpt(w, u, k, v, out=(torch.empty_like(k), ck), workspace=fws)
+    g2 = L.wkv4_backward_ckpt(w, u, k, v, dev(d2["gy"]), ck)
+    assert rel_err(host(y2), oracle.wkv4_forward(d2["w"], d2["u"], d2["k"], d2["v"])) <= TOL
+    check_bwd([host(t) for t in g2], oracle.wkv4_backward(d2["w"], d2["u"], d2["k"], d2["v"], d2["gy"]))
+
+
+def test_ckpt_backward_empty_sequence(L):
+    import torch
+    announce("wkv4_backward_ckpt T=0")
+    C = 40
+    z = torch.empty((2, 0, C), dtype=torch.float32, device="cuda")
+    w = torch.ones(C, dtype=torch.float32, device="cuda")
+    ck = torch.empty(0, dtype=torch.uint8, device="cuda")
+    gw = torch.full((C,), 7.0, device="cuda")
+    gu = torch.full((C,), 7.0, device="cuda")
+    L.wkv4_backward_ckpt(w, w, z, z, z, ck, out=(gw, gu, torch.empty_like(z), torch.empty_like(z)))
+    assert np.all(host(gw) == 0) and np.all(host(gu) == 0)
