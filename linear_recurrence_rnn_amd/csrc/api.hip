@@ -723,8 +723,9 @@ LINREC_API int wkv4_forward_ckpt(int64_t B, int64_t T, int64_t C, const float* w
     if ((st = check_ckpt(ckpt, ckpt_bytes, linrec::wkv_ckpt_bytes(B, T, C)))) return st;
     if ((st = check_ws(workspace, ws_bytes, linrec::wkv_ckpt_forward_ws_bytes(B, T, C)))) return st;
     const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0, nullptr, nullptr, nullptr};
-    // Coordination in a wave of its own by default; LINREC_COORD=1 puts it in wave 0.
-    const bool sep = env_int("LINREC_COORD", 0) != 1;
+    // Coordination in wave 0 by default (measured faster); LINREC_COORD=2 gives it a wave of
+    // its own.
+    const bool sep = env_int("LINREC_COORD", 0) == 2;
     return hip_status(linrec::run_wkv_forward_ckpt(A, B, T, C, ckpt, workspace, next_tag(), spin_limit(), sep,
                                                    (hipStream_t)stream),
                       "wkv4_forward_ckpt launch");

@@ -1,16 +1,16 @@
 // wkv_ckpt.hip -- the checkpointing WKV-4 forward on gfx950: y of eq. (14) (RWKV-LLM page,
 // "Time-mixing block"), and on the way the forward sums (A, B, A', B') at the end of every
-// slab of the backward's gradient kernel, so that a training step's backward can skip its
-// own forward pass over k and v (the state kernel).
+// slab of the backward's gradient kernel (every 56 steps), so that a training step's backward
+// can skip its own forward pass over k and v (the state kernel).
 //
-// It is the chunked look-back scan of the plain forward with a wider aggregate: the chunk
-// reduction also forms A' and B' (each weight times its distance to the chunk end), slabs
-// combine with the float64 fold of wkv_sums.hpp, and the slabs are the gradient kernel's
-// (7 chunks of 8 steps).  The look-back's inclusive prefix of slab s is exactly the sums at
-// the end of slab s, which the gradient kernel reads at the start of slab s + 1: the
-// caller's checkpoint buffer serves as the look-back's inclusive-record array, so keeping the
-// sums costs no traffic beyond the records the scan writes anyway.  The re-run of each chunk
-// is the plain forward's (A and B rounded to float32 at the chunk's carry-in).
+// It is the chunked look-back scan of the plain forward (one channel per lane, slabs of 8
+// chunks of 16 steps) with a wider aggregate: the chunk reduction also forms A' and B' (each
+// weight times its distance to the chunk end), and slabs combine with the float64 fold of
+// wkv_sums.hpp.  Each chunk starts its re-run from its carry-in, the sums before its first
+// step.  A chunk that contains a multiple of 56 (at most one: 16 < 56) forms the sums there
+// -- the carry-in followed by the steps before it, reduced exactly from k and v -- and writes
+// them in the record layout the gradient kernel reads.  The re-run itself is the plain
+// forward's (A and B rounded to float32 at the carry-in).
 #include "scan_kernel.hpp"
 #include "wkv_backward.hpp"
 #include "wkv_sums.hpp"
@@ -21,8 +21,15 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kCkptSlab = 56;  // steps between kept sums: the gradient kernel's slab (7 x 8)
+
+struct WkvCkptArgs : WkvArgs {
+    uint32_t* ckpt;  // (B*ngrp, nck, 10 dwords, 64 lanes) kept sums
+    int64_t nck;     // records per channel group: ceil(T / 56)
+};
+
 struct WkvCkptOp {
-    using Args = WkvArgs;
+    using Args = WkvCkptArgs;
     using Base = WkvOp;
     static constexpr bool kReverse = false;
     static constexpr bool kParts = false;
@@ -32,7 +39,14 @@ struct WkvCkptOp {
     using Local = Base::Local;
     using Agg = Fwd;
     static constexpr int kFloats = 1;
-    using Res = Base::Res;
+    // The plain buffers, and where the run starting at `row` keeps sums: at step js of the
+    // run (the first multiple of 56 at or after row, if before T), into record m.
+    struct Res {
+        Base::Res base;
+        uint32_t* rec;
+        int64_t m;
+        int js;
+    };
 
     template <int L>
     __device__ __forceinline__ static Chan chan(const Args& A, int64_t c) { return Base::template chan<L>(A, c); }
@@ -44,11 +58,17 @@ struct WkvCkptOp {
     }
     __device__ __forceinline__ static void finish(const Args&, const ScanGeom&, int64_t, int64_t, const Agg&) {}
     __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
-        return Base::res(A, g, b, row, col0);
+        Res R;
+        R.base = Base::res(A, g, b, row, col0);
+        const int64_t mb = row > 0 ? ((row + kCkptSlab - 1) / kCkptSlab) * kCkptSlab : kCkptSlab;
+        R.js = (mb < g.T) ? (int)(mb - row) : -1;
+        R.m = mb / kCkptSlab - 1;
+        R.rec = A.ckpt + (b * g.ngrp + col0 / 64) * A.nck * (64 * kDwords<Fwd>);
+        return R;
     }
     template <int VEC>
     __device__ __forceinline__ static void load(const Res& R, unsigned voff, const Rows& rows, int j, In (&in)[VEC]) {
-        Base::template load<VEC>(R, voff, rows, j, in);
+        Base::template load<VEC>(R.base, voff, rows, j, in);
     }
     template <int VEC>
     __device__ __forceinline__ static void zero(In (&in)[VEC]) {
@@ -99,46 +119,71 @@ struct WkvCkptOp {
     __device__ __forceinline__ static Part run(const Res& R, const Chan (&ch)[VEC], const Agg (&cin)[VEC],
                                                const In (&in)[L][VEC], const Local (&loc)[VEC], int n, unsigned voff,
                                                const Rows& rows) {
+        static_assert(VEC == 1, "the kept sums are laid out for one channel per lane");
+        if (R.js >= 0 && R.js < n) {  // a multiple of 56 falls in this chunk (same for the wave)
+            // The sums before step js: the carry-in advanced exactly over steps 0 .. js-1 (k is
+            // read again: in[] holds weights relative to the chunk's end, which can underflow
+            // where later steps dominate).
+            Fwd st = cin[0];
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                if (j < R.js) {
+                    const float kk = ldb<1>(R.base.k, voff, rows.soff(j)).v[0] * kLog2e;
+                    fwd_advance(ch[0].om, st, kk, (double)in[j][0].v, mag(st.p, (float)st.b));
+                }
+            }
+            Fwd x[1] = {st};
+            store_record<1>(R.rec, R.m, (int)(voff >> 2), x);
+        }
         Base::Agg c[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) c[e] = {(float)cin[e].a, (float)cin[e].b, cin[e].p};
-        return Base::template run<L, VEC>(R, ch, c, in, loc, n, voff, rows);
+        return Base::template run<L, VEC>(R.base, ch, c, in, loc, n, voff, rows);
     }
 };
 
 }  // namespace
 
+// Slabs of the forward: 8 chunks of 16 steps.
+constexpr int kCkptNW = 8, kCkptL = 16;
+
 size_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C) {
-    const BwdPlan p = wkv_backward_plan(1, B, T, C, 0, 0);
-    return (size_t)(B * ((C + 63) / 64) * p.nslab * 64) * sizeof(Fwd);
+    const int64_t nck = (T + kCkptSlab - 1) / kCkptSlab;
+    return (size_t)(B * ((C + 63) / 64) * nck * 64) * sizeof(Fwd);
 }
 
 size_t wkv_ckpt_forward_ws_bytes(int64_t B, int64_t T, int64_t C) {
-    const BwdPlan p = wkv_backward_plan(1, B, T, C, 0, 0);
-    if (p.nslab <= 1) return 0;
-    const int64_t nwg = B * ((C + 63) / 64) * p.nslab;
-    return align256((size_t)nwg * 8) + align256((size_t)(nwg * 64) * sizeof(Fwd));
+    const int64_t nslab = (T + kCkptNW * kCkptL - 1) / (kCkptNW * kCkptL);
+    if (nslab <= 1) return 0;
+    const int64_t nwg = B * ((C + 63) / 64) * nslab;
+    return align256((size_t)nwg * 8) + 2 * align256((size_t)(nwg * 64) * sizeof(Fwd));
 }
 
 hipError_t run_wkv_forward_ckpt(const WkvArgs& A, int64_t B, int64_t T, int64_t C, void* ckpt, void* ws,
                                 uint64_t tag, int spin, bool sep, hipStream_t st) {
-    const BwdPlan p = wkv_backward_plan(1, B, T, C, 0, 0);
-    if (p.nw != 7 || p.L != 8) return hipErrorInvalidValue;
+    // The kept sums are the gradient kernel's slab starts: its default plan must match.
+    const BwdPlan bp = wkv_backward_plan(1, B, T, C, 0, 0);
+    if (bp.nw * bp.L != kCkptSlab) return hipErrorInvalidValue;
+    WkvCkptArgs X;
+    static_cast<WkvArgs&>(X) = A;
+    X.ckpt = reinterpret_cast<uint32_t*>(ckpt);
+    X.nck = (T + kCkptSlab - 1) / kCkptSlab;
     ScanGeom g{};
     g.B = B;
     g.T = T;
     g.C = C;
     g.ngrp = (C + 63) / 64;
-    g.nslab = p.nslab;
+    g.nslab = (T + kCkptNW * kCkptL - 1) / (kCkptNW * kCkptL);
     g.tag = tag;
     g.spin = spin;
-    if (p.nslab > 1) {
+    if (g.nslab > 1) {
         const int64_t nwg = B * g.ngrp * g.nslab;
+        const size_t rec = align256((size_t)(nwg * 64) * sizeof(Fwd));
         g.flags = reinterpret_cast<uint64_t*>(ws);
         g.rec_agg = (char*)ws + align256((size_t)nwg * 8);
-        g.rec_incl = ckpt;  // the inclusive prefixes are the checkpoints
+        g.rec_incl = (char*)g.rec_agg + rec;
     }
-    return scan_kernel::launch<WkvCkptOp, 1, 7, 8>(A, g, sep, st);
+    return scan_kernel::launch<WkvCkptOp, 1, kCkptNW, kCkptL>(X, g, sep, st);
 }
 
 }  // namespace linrec

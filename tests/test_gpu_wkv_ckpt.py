@@ -48,13 +48,14 @@ def check_step(L, d, compare_plain=True):
 
 
 SHAPES = [(1, 1, 4), (3, 1000, 40), (2, 333, 37), (1, 17, 1), (4, 2049, 20), (2, 64, 16), (2, 56, 64),
-          (2, 57, 65), (3, 112, 130)]
+          (2, 57, 65), (3, 112, 130), (2, 128, 64), (2, 129, 64), (1, 448, 64), (2, 449, 70)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
 def test_ckpt_step_shapes(L, shape):
     # Ragged last slabs, partial channel groups, one-slab sequences (T <= 56: no sums kept),
-    # and exact multiples of the slab.
+    # exact multiples of the kept sums' spacing (56) and of the forward's slab (128), and
+    # their common multiple (448), where a kept sum falls on a slab start.
     announce("wkv4 checkpointed step shape %s" % (shape,))
     check_step(L, workloads.make_inputs(3, seed=31, shape=shape))
 
@@ -93,9 +94,9 @@ def test_ckpt_step_lookback_recompute(L, monkeypatch, spin):
     check_step(L, d)
 
 
-def test_ckpt_forward_coordinator_in_wave0(L, monkeypatch):
-    announce("wkv4_forward_ckpt with the coordination in wave 0")
-    monkeypatch.setenv("LINREC_COORD", "1")
+def test_ckpt_forward_coordinator_wave(L, monkeypatch):
+    announce("wkv4_forward_ckpt with a coordinator wave of its own")
+    monkeypatch.setenv("LINREC_COORD", "2")
     check_step(L, workloads.make_inputs(3, seed=35, shape=(2, 1001, 150)))
 
 
