@@ -54,7 +54,9 @@ BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "sca
                   "scan_real_decay_backward": 12,  # read x, gx; write gu
                   "scan_complex_normalized_backward": 32,  # read u, x, gx; write gu (complex64)
                   "wkv4_train_step": 32,         # forward (12) then backward (20), separate passes
-                  "wkv4_train_step_ckpt": 32}    # the same step, the backward from the forward's sums
+                  "wkv4_train_step_ckpt": 32,    # the same step, the backward from the forward's sums
+                  "wkv4_train_step_gated": 44,   # gated forward (16) then gated backward (28)
+                  "wkv4_train_step_gated_ckpt": 44}
 SHIFT_M = 3  # token-shift mixes timed: the r, k, v inputs of the time mix
 
 
@@ -84,6 +86,9 @@ KERNEL_SOURCES = {
                             "device_common.hpp", "wkv_math.hpp", "wkv_sums.hpp"),
 }
 KERNEL_SOURCES["wkv4_train_step"] = tuple(sorted(set(_SCAN_SOURCES + KERNEL_SOURCES["wkv4_backward"])))
+KERNEL_SOURCES["wkv4_train_step_gated"] = KERNEL_SOURCES["wkv4_train_step"]
+KERNEL_SOURCES["wkv4_train_step_gated_ckpt"] = tuple(sorted(set(
+    _SCAN_SOURCES + KERNEL_SOURCES["wkv4_backward"] + ("wkv_ckpt.hip", "wkv_sums.hpp"))))
 KERNEL_SOURCES["wkv4_train_step_ckpt"] = tuple(sorted(set(
     _SCAN_SOURCES + KERNEL_SOURCES["wkv4_backward"] + ("wkv_ckpt.hip", "wkv_sums.hpp"))))
 for _k in ("scan_mingru_backward", "scan_minlstm_backward", "scan_real_decay_backward",
@@ -155,10 +160,12 @@ class Row:
                                    v.data_ptr(), gy.data_ptr(), gw.data_ptr(), gu.data_ptr(),
                                    gk.data_ptr(), gv.data_ptr(), ws.data_ptr(), nws, stream)))
             self.keep += [w, u]
-        elif kind in ("wkv4_train_step", "wkv4_train_step_ckpt"):
-            # One training step of the WKV layer: the forward, then the backward of its output.
+        elif kind.startswith("wkv4_train_step"):
+            # One training step of the WKV layer: the forward, then the backward of its output
+            # (with the sigma(r) gate of the time mix for the gated rows).
             w, u = to(host["w"]), to(host["u"])
             ck = kind.endswith("_ckpt")
+            gated = "_gated" in kind
             nfw = int(lib.wkv4_forward_ckpt_workspace_size(B, T, C) if ck else lib.wkv4_forward_workspace_size(B, T, C))
             nbw = int(lib.wkv4_backward_ckpt_workspace_size(B, T, C) if ck else
                       lib.wkv4_backward_workspace_size(B, T, C))
@@ -173,12 +180,20 @@ class Row:
                 y, gk, gv = torch.empty_like(k), torch.empty_like(k), torch.empty_like(k)
                 cbuf = torch.empty(max(nck, 1), dtype=torch.uint8, device=dev)
                 self.keep += [k, v, gy, y, gk, gv, cbuf]
-                p = lambda t: t.data_ptr()  # noqa: E731
+                p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+                r = to(host["r"]) if gated else None
+                gr = torch.empty_like(k) if gated else None
+                self.keep += [r, gr]
                 if ck:
-                    fa = (lib.wkv4_forward_ckpt, (B, T, C, p(w), p(u), p(k), p(v), p(y), p(cbuf), nck, p(fws), nfw,
-                                                  stream))
-                    ba = (lib.wkv4_backward_ckpt, (B, T, C, p(w), p(u), p(k), p(v), p(gy), p(cbuf), nck, p(gw),
-                                                   p(gu), p(gk), p(gv), p(bws), nbw, stream))
+                    fa = (lib.wkv4_forward_ckpt, (B, T, C, p(w), p(u), p(k), p(v), p(r), p(y), p(cbuf), nck, p(fws),
+                                                  nfw, stream))
+                    ba = (lib.wkv4_backward_ckpt, (B, T, C, p(w), p(u), p(k), p(v), p(r), p(gy), p(cbuf), nck, p(gw),
+                                                   p(gu), p(gk), p(gv), p(gr), p(bws), nbw, stream))
+                elif gated:
+                    fa = (lib.wkv4_forward_ex, (B, T, C, p(w), p(u), p(k), p(v), p(r), None, p(y), None, p(fws), nfw,
+                                                stream))
+                    ba = (lib.wkv4_backward_ex, (B, T, C, p(w), p(u), p(k), p(v), p(r), None, None, p(gy), None, p(gw),
+                                                 p(gu), p(gk), p(gv), p(gr), None, p(bws), nbw, stream))
                 else:
                     fa = (lib.wkv4_forward, (B, T, C, p(w), p(u), p(k), p(v), p(y), p(fws), nfw, stream))
                     ba = (lib.wkv4_backward, (B, T, C, p(w), p(u), p(k), p(v), p(gy), p(gw), p(gu), p(gk), p(gv),
@@ -392,6 +407,12 @@ def cpu_baseline(kind, host, budget_s):
           "wkv4_train_step_ckpt": lambda: (oracle.wkv4_forward(host["w"], host["u"], host["k"], host["v"]),
                                            oracle.wkv4_backward(host["w"], host["u"], host["k"], host["v"],
                                                                 host["gy"])),
+          "wkv4_train_step_gated": lambda: (
+              oracle.wkv4_forward_ex(host["w"], host["u"], host["k"], host["v"], r=host["r"]),
+              oracle.wkv4_backward_gated(host["w"], host["u"], host["k"], host["v"], host["r"], host["gy"])),
+          "wkv4_train_step_gated_ckpt": lambda: (
+              oracle.wkv4_forward_ex(host["w"], host["u"], host["k"], host["v"], r=host["r"]),
+              oracle.wkv4_backward_gated(host["w"], host["u"], host["k"], host["v"], host["r"], host["gy"])),
           "scan_real": lambda: oracle.scan_real(host["a"], host["b"]),
           "scan_complex": lambda: oracle.scan_complex(host["lam"], host["u"]),
           "scan_real_backward": lambda: oracle.scan_real_backward(host["a"], host["x"], host["gx"]),
@@ -461,7 +482,7 @@ def make_host(wid, kind, shape=None):
             host["x"] = host["h"]  # stand-in of the forward output's distribution (timing only)
     else:
         host = workloads.make_inputs(wid, shape=(B, T, C))
-    if kind in ("wkv4_backward_gated", "wkv4_forward_gated"):
+    if kind in ("wkv4_backward_gated", "wkv4_forward_gated") or kind.startswith("wkv4_train_step_gated"):
         host["r"] = host["v"]  # stand-in receptance ~ N(0,1) (timing only)
     if kind.endswith("_backward") and kind.startswith("scan_") and kind not in VARIANT_BWD:
         host.update(workloads.make_scan_adjoint_inputs(wid, host))
@@ -488,7 +509,8 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
     if kind == "wkv4_forward_gated":
         label = "WKV-4 forward with the sigma(r) gate fp32 B=%d T=%d C=%d" % (B, T, C)
     if kind.startswith("wkv4_train_step"):
-        label = "WKV-4 training step (forward, then backward%s) fp32 B=%d T=%d C=%d" % (
+        label = "WKV-4 training step (%sforward, then backward%s) fp32 B=%d T=%d C=%d" % (
+            "sigma(r)-gated " if "_gated" in kind else "",
             " from the forward's kept sums" if kind.endswith("_ckpt") else "", B, T, C)
     if kind.startswith("token_shift"):
         label = "RWKV token shift%s, %d mixes, fp32 B=%d T=%d C=%d" % (
@@ -593,7 +615,9 @@ def main():
                                             (4, "scan_mingru_backward", 20, 512), (4, "scan_minlstm_backward", 20, 512),
                                             (4, "scan_real_decay_backward", 20, 512),
                                             (5, "scan_complex_normalized_backward", 10, 16384),
-                                            (3, "wkv4_train_step", 10, 256), (3, "wkv4_train_step_ckpt", 10, 256)):
+                                            (3, "wkv4_train_step", 10, 256), (3, "wkv4_train_step_ckpt", 10, 256),
+                                            (3, "wkv4_train_step_gated", 10, 256),
+                                            (3, "wkv4_train_step_gated_ckpt", 10, 256)):
             rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
             log("[bench] " + json.dumps(rows[-1]))
         if args.all_out:

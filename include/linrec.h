@@ -259,14 +259,18 @@ int wkv4_backward_ex(int64_t B, int64_t T, int64_t C,
  *                       end of every slab into ckpt;
  *   wkv4_backward_ckpt  writes gw, gu, gk, gv exactly as wkv4_backward (to rounding) from
  *                       the same w, u, k, v, gy and that ckpt, without the extra pass.
+ *   (The sums do not depend on r: one ckpt serves the gated and the plain backward.)
  *
  *   ckpt  device buffer of at least wkv4_checkpoint_size(B, T, C) bytes, 16-byte aligned,
  *         owned by the caller.  Its contents are opaque (float64 sums with an integer
  *         exponent per channel and slab); they are valid only for the B, T, C, w and k, v of
  *         the forward that wrote them, and only after that forward has completed in stream
  *         order.  The backward only reads it.
- *   other arguments as for wkv4_forward / wkv4_backward.  No carried state and no gate:
- *   those calls stay with wkv4_forward_ex / wkv4_backward_ex.
+ *   r     (B,T,C) float32 receptance, or NULL: with r the output is the gated sigma(r) wkv
+ *         (eq. (15)), as wkv4_forward_ex / wkv4_backward_ex with r, and the backward writes
+ *   gr    (B,T,C) dL/dr; r and gr are given together to the backward (else INVALID_ARG)
+ *   other arguments as for wkv4_forward / wkv4_backward.  No carried state: such calls stay
+ *   with wkv4_forward_ex / wkv4_backward_ex.
  *
  * Workspaces: wkv4_forward_ckpt_workspace_size and wkv4_backward_ckpt_workspace_size (the
  * latter smaller than wkv4_backward's: no state pass).  Errors as for the other calls, and
@@ -280,12 +284,12 @@ size_t wkv4_forward_ckpt_workspace_size(int64_t B, int64_t T, int64_t C);
 size_t wkv4_backward_ckpt_workspace_size(int64_t B, int64_t T, int64_t C);
 int wkv4_forward_ckpt(int64_t B, int64_t T, int64_t C,
                       const float *w, const float *u, const float *k, const float *v,
-                      float *y, void *ckpt, size_t ckpt_bytes,
+                      const float *r, float *y, void *ckpt, size_t ckpt_bytes,
                       void *workspace, size_t ws_bytes, void *stream);
 int wkv4_backward_ckpt(int64_t B, int64_t T, int64_t C,
                        const float *w, const float *u, const float *k, const float *v,
-                       const float *gy, const void *ckpt, size_t ckpt_bytes,
-                       float *gw, float *gu, float *gk, float *gv,
+                       const float *r, const float *gy, const void *ckpt, size_t ckpt_bytes,
+                       float *gw, float *gu, float *gk, float *gv, float *gr,
                        void *workspace, size_t ws_bytes, void *stream);
 
 /*

@@ -76,9 +76,9 @@ def load(path: str | None = None):
         lib.wkv4_backward_ex.restype = ctypes.c_int
         lib.wkv4_backward_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 15 + [_VP, _SZ, _VP]
         lib.wkv4_forward_ckpt.restype = ctypes.c_int
-        lib.wkv4_forward_ckpt.argtypes = [_I64, _I64, _I64] + [_VP] * 6 + [_SZ, _VP, _SZ, _VP]
+        lib.wkv4_forward_ckpt.argtypes = [_I64, _I64, _I64] + [_VP] * 7 + [_SZ, _VP, _SZ, _VP]
         lib.wkv4_backward_ckpt.restype = ctypes.c_int
-        lib.wkv4_backward_ckpt.argtypes = [_I64, _I64, _I64] + [_VP] * 6 + [_SZ] + [_VP] * 4 + [_VP, _SZ, _VP]
+        lib.wkv4_backward_ckpt.argtypes = [_I64, _I64, _I64] + [_VP] * 7 + [_SZ] + [_VP] * 5 + [_VP, _SZ, _VP]
         lib.wkv4_decode_step.restype = ctypes.c_int
         lib.wkv4_decode_step.argtypes = [_I64, _I64] + [_VP] * 7 + [_VP]
         lib.wkv4_backward.argtypes = [_I64, _I64, _I64] + [_VP] * 9 + [_VP, _SZ, _VP]
@@ -348,14 +348,17 @@ def wkv4_checkpoint_size(B: int, T: int, C: int) -> int:
     return int(load().wkv4_checkpoint_size(B, T, C))
 
 
-def wkv4_forward_ckpt(w, u, k, v, out=None, workspace=None):
-    """(y, ckpt): y as wkv4_forward, and ckpt (uint8 device buffer) holding the forward sums
-    that wkv4_backward_ckpt starts its slabs from.  ``out`` = (y, ckpt) to reuse buffers."""
+def wkv4_forward_ckpt(w, u, k, v, r=None, out=None, workspace=None):
+    """(y, ckpt): y as wkv4_forward (gated by sigma(r) when ``r`` is given), and ckpt (uint8
+    device buffer) holding the forward sums that wkv4_backward_ckpt starts its slabs from.
+    ``out`` = (y, ckpt) to reuse buffers."""
     lib = load()
     B, T, C = k.shape
     dev = k.device
     _expect(k, "k", torch.float32, (B, T, C), dev)
     _expect(v, "v", torch.float32, (B, T, C), dev)
+    if r is not None:
+        _expect(r, "r", torch.float32, (B, T, C), dev)
     _expect(w, "w", torch.float32, (C,), dev)
     _expect(u, "u", torch.float32, (C,), dev)
     nck = int(lib.wkv4_checkpoint_size(B, T, C))
@@ -367,19 +370,22 @@ def wkv4_forward_ckpt(w, u, k, v, out=None, workspace=None):
         _expect(y, "out[0]", torch.float32, (B, T, C), dev)
         _expect(ckpt, "out[1]", torch.uint8, (nck,), dev)
     ws, nws = _workspace(int(lib.wkv4_forward_ckpt_workspace_size(B, T, C)), dev, workspace)
-    _check(lib.wkv4_forward_ckpt(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(ckpt), nck,
+    _check(lib.wkv4_forward_ckpt(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(y), _ptr(ckpt), nck,
                                  _ptr(ws), nws, _stream(dev)), "wkv4_forward_ckpt")
     return y, ckpt
 
 
-def wkv4_backward_ckpt(w, u, k, v, gy, ckpt, out=None, workspace=None):
+def wkv4_backward_ckpt(w, u, k, v, gy, ckpt, r=None, out=None, workspace=None):
     """(gw, gu, gk, gv) as wkv4_backward, from the ckpt that wkv4_forward_ckpt wrote for the
-    same w, u, k, v."""
+    same w, u, k, v; with ``r``, the gradients of the gated output sigma(r) wkv and
+    (gw, gu, gk, gv, gr)."""
     lib = load()
     B, T, C = k.shape
     dev = k.device
     for name, t in (("k", k), ("v", v), ("gy", gy)):
         _expect(t, name, torch.float32, (B, T, C), dev)
+    if r is not None:
+        _expect(r, "r", torch.float32, (B, T, C), dev)
     _expect(w, "w", torch.float32, (C,), dev)
     _expect(u, "u", torch.float32, (C,), dev)
     nck = int(lib.wkv4_checkpoint_size(B, T, C))
@@ -389,17 +395,21 @@ def wkv4_backward_ckpt(w, u, k, v, gy, ckpt, out=None, workspace=None):
         gu = torch.empty(C, dtype=torch.float32, device=dev)
         gk = torch.empty_like(k)
         gv = torch.empty_like(k)
+        gr = torch.empty_like(k) if r is not None else None
     else:
-        gw, gu, gk, gv = out
+        gw, gu, gk, gv = out[:4]
+        gr = out[4] if r is not None else None
         _expect(gw, "out[0]", torch.float32, (C,), dev)
         _expect(gu, "out[1]", torch.float32, (C,), dev)
         _expect(gk, "out[2]", torch.float32, (B, T, C), dev)
         _expect(gv, "out[3]", torch.float32, (B, T, C), dev)
+        if gr is not None:
+            _expect(gr, "out[4]", torch.float32, (B, T, C), dev)
     ws, nws = _workspace(int(lib.wkv4_backward_ckpt_workspace_size(B, T, C)), dev, workspace)
-    _check(lib.wkv4_backward_ckpt(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy), _ptr(ckpt), nck,
-                                  _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(ws), nws, _stream(dev)),
+    _check(lib.wkv4_backward_ckpt(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(gy), _ptr(ckpt), nck,
+                                  _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(gr), _ptr(ws), nws, _stream(dev)),
            "wkv4_backward_ckpt")
-    return gw, gu, gk, gv
+    return (gw, gu, gk, gv) if r is None else (gw, gu, gk, gv, gr)
 
 
 def scan_real(a, b, x0=None, out=None, workspace=None):

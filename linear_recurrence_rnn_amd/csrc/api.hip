@@ -711,18 +711,18 @@ int check_ckpt(const void* ckpt, size_t ckpt_bytes, size_t need) {
 }  // namespace
 
 LINREC_API int wkv4_forward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                                 const float* k, const float* v, float* y, void* ckpt, size_t ckpt_bytes,
-                                 void* workspace, size_t ws_bytes, void* stream) {
+                                 const float* k, const float* v, const float* r, float* y, void* ckpt,
+                                 size_t ckpt_bytes, void* workspace, size_t ws_bytes, void* stream) {
     int st = check_shape(B, T, C, 4);
     if (st) return st;
     if (B == 0 || T == 0 || C == 0) return ok();
     if (!w || !u || !k || !v || !y) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
-    const void* ptrs[] = {w, u, k, v, y};
+    const void* ptrs[] = {w, u, k, v, y, r};
     for (const void* p : ptrs)
-        if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+        if (p && !aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
     if ((st = check_ckpt(ckpt, ckpt_bytes, linrec::wkv_ckpt_bytes(B, T, C)))) return st;
     if ((st = check_ws(workspace, ws_bytes, linrec::wkv_ckpt_forward_ws_bytes(B, T, C)))) return st;
-    const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0, nullptr, nullptr, nullptr};
+    const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0, r, nullptr, nullptr};
     // Coordination in wave 0 by default (measured faster); LINREC_COORD=2 gives it a wave of
     // its own.
     const bool sep = env_int("LINREC_COORD", 0) == 2;
@@ -732,11 +732,12 @@ LINREC_API int wkv4_forward_ckpt(int64_t B, int64_t T, int64_t C, const float* w
 }
 
 LINREC_API int wkv4_backward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                                  const float* k, const float* v, const float* gy, const void* ckpt,
-                                  size_t ckpt_bytes, float* gw, float* gu, float* gk, float* gv, void* workspace,
-                                  size_t ws_bytes, void* stream) {
+                                  const float* k, const float* v, const float* r, const float* gy,
+                                  const void* ckpt, size_t ckpt_bytes, float* gw, float* gu, float* gk,
+                                  float* gv, float* gr, void* workspace, size_t ws_bytes, void* stream) {
     int st = check_shape(B, T, C, 4);
     if (st) return st;
+    if (!r != !gr) return fail(LINREC_ERR_INVALID_ARG, "r and gr must be given together");
     if (C > 0 && (!gw || !gu)) return fail(LINREC_ERR_INVALID_ARG, "gw or gu is NULL");
     if (B == 0 || T == 0 || C == 0) {
         if (C == 0) return ok();
@@ -745,13 +746,13 @@ LINREC_API int wkv4_backward_ckpt(int64_t B, int64_t T, int64_t C, const float* 
     }
     if (!w || !u || !k || !v || !gy || !gk || !gv)
         return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
-    const void* ptrs[] = {w, u, k, v, gy, gw, gu, gk, gv};
+    const void* ptrs[] = {w, u, k, v, gy, gw, gu, gk, gv, r, gr};
     for (const void* p : ptrs)
-        if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+        if (p && !aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
     if ((st = check_ckpt(ckpt, ckpt_bytes, linrec::wkv_ckpt_bytes(B, T, C)))) return st;
     const linrec::BwdPlan p = linrec::wkv_backward_plan(1, B, T, C, 0, 0);  // the checkpoints' slabs
     if ((st = check_ws(workspace, ws_bytes, linrec::wkv_backward_ckpt_ws_bytes(B, T, C)))) return st;
-    const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv, r, gr, nullptr, nullptr, nullptr, nullptr};
     linrec::BwdGeom g{};
     g.B = B;
     g.T = T;

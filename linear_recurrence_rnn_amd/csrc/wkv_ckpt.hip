@@ -10,7 +10,7 @@
 // step.  A chunk that contains a multiple of 56 (at most one: 16 < 56) forms the sums there
 // -- the carry-in followed by the steps before it, reduced exactly from k and v -- and writes
 // them in the record layout the gradient kernel reads.  The re-run itself is the plain
-// forward's (A and B rounded to float32 at the carry-in).
+// forward's (A and B rounded to float32 at the carry-in), gated by sigma(r) when r is given.
 #include "scan_kernel.hpp"
 #include "wkv_backward.hpp"
 #include "wkv_sums.hpp"
@@ -28,21 +28,23 @@ struct WkvCkptArgs : WkvArgs {
     int64_t nck;     // records per channel group: ceil(T / 56)
 };
 
-struct WkvCkptOp {
+// GATED: the output is sigma(r) wkv (eq. (15)); the plain instance compiles none of it.
+template <bool GATED>
+struct WkvCkptOpT {
     using Args = WkvCkptArgs;
-    using Base = WkvOp;
+    using Base = typename std::conditional<GATED, WkvExtOp, WkvOp>::type;
     static constexpr bool kReverse = false;
     static constexpr bool kParts = false;
     using Part = NoPart;
-    using Chan = Base::Chan;
-    using In = Base::In;
-    using Local = Base::Local;
+    using Chan = typename Base::Chan;
+    using In = typename Base::In;
+    using Local = typename Base::Local;
     using Agg = Fwd;
     static constexpr int kFloats = 1;
     // The plain buffers, and where the run starting at `row` keeps sums: at step js of the
     // run (the first multiple of 56 at or after row, if before T), into record m.
     struct Res {
-        Base::Res base;
+        typename Base::Res base;
         uint32_t* rec;
         int64_t m;
         int js;
@@ -135,7 +137,7 @@ struct WkvCkptOp {
             Fwd x[1] = {st};
             store_record<1>(R.rec, R.m, (int)(voff >> 2), x);
         }
-        Base::Agg c[VEC];
+        typename Base::Agg c[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) c[e] = {(float)cin[e].a, (float)cin[e].b, cin[e].p};
         return Base::template run<L, VEC>(R.base, ch, c, in, loc, n, voff, rows);
@@ -143,6 +145,15 @@ struct WkvCkptOp {
 };
 
 }  // namespace
+
+// The gated instance also holds r per step: at 6 waves per SIMD (80 VGPRs) it spills around
+// the kept sums; 5 (96 VGPRs) does not, and measured faster (gated step 984 -> 948 us).
+namespace scan_kernel {
+template <>
+constexpr int scan_waves_per_eu<WkvCkptOpT<true>, 1, 16>() {
+    return 5;
+}
+}  // namespace scan_kernel
 
 // Slabs of the forward: 8 chunks of 16 steps.
 constexpr int kCkptNW = 8, kCkptL = 16;
@@ -183,7 +194,8 @@ hipError_t run_wkv_forward_ckpt(const WkvArgs& A, int64_t B, int64_t T, int64_t 
         g.rec_agg = (char*)ws + align256((size_t)nwg * 8);
         g.rec_incl = (char*)g.rec_agg + rec;
     }
-    return scan_kernel::launch<WkvCkptOp, 1, kCkptNW, kCkptL>(X, g, sep, st);
+    if (A.r) return scan_kernel::launch<WkvCkptOpT<true>, 1, kCkptNW, kCkptL>(X, g, sep, st);
+    return scan_kernel::launch<WkvCkptOpT<false>, 1, kCkptNW, kCkptL>(X, g, sep, st);
 }
 
 }  // namespace linrec

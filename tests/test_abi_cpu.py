@@ -307,11 +307,11 @@ def test_wkv4_checkpoint_argument_checks(lib):
     assert nfw > 0
     assert lib.wkv4_checkpoint_size(0, T, C) == 0 and lib.wkv4_checkpoint_size(-1, T, C) == 0
 
-    def fw(ck=P2, nc=nck, ws=P, nws=nfw, y=P2, k=P):
-        return lib.wkv4_forward_ckpt(B, T, C, P, P, k, P, y, ck, nc, ws, nws, None)
+    def fw(ck=P2, nc=nck, ws=P, nws=nfw, y=P2, k=P, r=None):
+        return lib.wkv4_forward_ckpt(B, T, C, P, P, k, P, r, y, ck, nc, ws, nws, None)
 
-    def bw(ck=P2, nc=nck, ws=P, nws=nbw, gy=P, gw=P2):
-        return lib.wkv4_backward_ckpt(B, T, C, P, P, P, P, gy, ck, nc, gw, P2, P2, P2, ws, nws, None)
+    def bw(ck=P2, nc=nck, ws=P, nws=nbw, gy=P, gw=P2, r=None, gr=None):
+        return lib.wkv4_backward_ckpt(B, T, C, P, P, P, P, r, gy, ck, nc, gw, P2, P2, P2, gr, ws, nws, None)
 
     for f in (fw, bw):
         assert f(nc=nck - 1) == WORKSPACE
@@ -322,10 +322,15 @@ def test_wkv4_checkpoint_argument_checks(lib):
         assert f(ws=None) == INVALID
     assert fw(y=None) == INVALID
     assert fw(k=ODD) == UNSUPPORTED
+    assert fw(r=ODD) == UNSUPPORTED
     assert bw(gy=None) == INVALID
     assert bw(gw=None) == INVALID
-    assert lib.wkv4_forward_ckpt(-1, T, C, P, P, P, P, P2, P2, nck, P, nfw, None) == INVALID
+    # the gate and its gradient come together
+    assert bw(r=P) == INVALID
+    assert bw(gr=P) == INVALID
+    assert bw(r=ODD, gr=P) == UNSUPPORTED
+    assert lib.wkv4_forward_ckpt(-1, T, C, P, P, P, P, None, P2, P2, nck, P, nfw, None) == INVALID
     # empty shapes return before any launch: nothing to do (B = 0), nothing read
-    assert lib.wkv4_forward_ckpt(0, T, C, None, None, None, None, None, None, 0, None, 0, None) == OK
-    assert lib.wkv4_backward_ckpt(B, T, 0, None, None, None, None, None, None, 0, None, None, None, None,
-                                  None, 0, None) == OK
+    assert lib.wkv4_forward_ckpt(0, T, C, None, None, None, None, None, None, None, 0, None, 0, None) == OK
+    assert lib.wkv4_backward_ckpt(B, T, 0, None, None, None, None, None, None, None, 0, None, None, None, None,
+                                  None, None, 0, None) == OK

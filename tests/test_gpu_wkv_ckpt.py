@@ -156,3 +156,45 @@ def test_ckpt_backward_empty_sequence(L):
     gu = torch.full((C,), 7.0, device="cuda")
     L.wkv4_backward_ckpt(w, w, z, z, z, ck, out=(gw, gu, torch.empty_like(z), torch.empty_like(z)))
     assert np.all(host(gw) == 0) and np.all(host(gu) == 0)
+
+
+# ---------------------------------------------------------------- the gated time-mix output
+def check_gated_step(L, d, r):
+    """The checkpointed step of o = sigma(r) wkv (eq. (15)) against the oracle."""
+    ref_y, _ = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"], r=r, want_state=False)
+    ref = oracle.wkv4_backward_gated(d["w"], d["u"], d["k"], d["v"], r, d["gy"])
+    w, u, k, v, rr = dev(d["w"]), dev(d["u"]), dev(d["k"]), dev(d["v"]), dev(r)
+    y, ck = L.wkv4_forward_ckpt(w, u, k, v, r=rr)
+    got = [host(t) for t in L.wkv4_backward_ckpt(w, u, k, v, dev(d["gy"]), ck, r=rr)]
+    assert rel_err(host(y), ref_y) <= TOL, rel_err(host(y), ref_y)
+    check_bwd(got[:4], ref[:4])
+    assert rel_err(got[4], ref[4]) <= TOL, rel_err(got[4], ref[4])
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 64), (2, 333, 37), (3, 1000, 40), (2, 449, 70), (1, 4000, 64)], ids=str)
+def test_ckpt_step_gated(L, shape):
+    announce("wkv4 checkpointed gated step %s" % (shape,))
+    d = workloads.make_inputs(3, seed=41, shape=shape)
+    r = (np.random.default_rng(42).standard_normal(shape) * 2).astype(np.float32)
+    check_gated_step(L, d, r)
+
+
+def test_ckpt_step_gated_saturated_and_exact(L, monkeypatch):
+    # |r| up to ~40 (sigma 0 or 1), then both kernels on their exact per-step paths.
+    announce("wkv4 checkpointed gated step, saturated gates; exact paths")
+    d = workloads.make_inputs(3, seed=43, shape=(2, 700, 96))
+    r = (np.random.default_rng(44).standard_normal(d["k"].shape) * 15).astype(np.float32)
+    check_gated_step(L, d, r)
+    monkeypatch.setenv("LINREC_WKV_EXACT", "1")
+    check_gated_step(L, d, r)
+
+
+def test_ckpt_serves_gated_and_plain_backward(L):
+    # The kept sums do not depend on r: one checkpoint serves both backward calls.
+    announce("wkv4 checkpoint from the gated forward, used by the plain backward")
+    d = workloads.make_inputs(3, seed=45, shape=(2, 500, 64))
+    r = np.random.default_rng(46).standard_normal(d["k"].shape).astype(np.float32)
+    w, u, k, v = dev(d["w"]), dev(d["u"]), dev(d["k"]), dev(d["v"])
+    _, ck = L.wkv4_forward_ckpt(w, u, k, v, r=dev(r))
+    got = [host(t) for t in L.wkv4_backward_ckpt(w, u, k, v, dev(d["gy"]), ck)]
+    check_bwd(got, oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
