@@ -8,8 +8,9 @@
 // weight times its distance to the chunk end), and slabs combine with the float64 fold of
 // wkv_sums.hpp.  Each chunk starts its re-run from its carry-in, the sums before its first
 // step.  A chunk that contains a multiple of 56 (at most one: 16 < 56) forms the sums there
-// -- the carry-in followed by the steps before it, reduced exactly from k and v -- and writes
-// them in the record layout the gradient kernel reads.  The re-run itself is the plain
+// -- the carry-in followed by the steps before it, from the chunk's own weights (or, behind a
+// spike that may have flushed them, from k and v step by step) -- and writes them in the
+// record layout the gradient kernel reads.  The re-run itself is the plain
 // forward's (A and B rounded to float32 at the carry-in), gated by sigma(r) when r is given.
 #include "scan_kernel.hpp"
 #include "wkv_backward.hpp"
@@ -27,6 +28,21 @@ struct WkvCkptArgs : WkvArgs {
     uint32_t* ckpt;  // (B*ngrp, nck, 10 dwords, 64 lanes) kept sums
     int64_t nck;     // records per channel group: ceil(T / 56)
 };
+
+// The sums s1, then a span of n2 steps whose sums (a, b, ad, bd) carry the exponent p2 + ne om
+// (not an integer): as fwd_combine, with that exponent kept split (p2 and the resulting
+// exponent are integers, ne om = hi + lo exactly), so the scale factors lose nothing to its
+// rounding.
+__device__ __forceinline__ Fwd fwd_combine_shifted(float om, const Fwd& s1, float a, float b, float ad, float bd,
+                                                   float p2, int ne, int n2) {
+    const Split d = mul_split((float)n2, om), e = mul_split((float)ne, om);
+    const float P = ceilf(fmaxf(mag(s1.p, (float)s1.b) - d.hi, mag(p2 + e.hi, b)));
+    const double f1 = fast_exp2(((s1.p - P) - d.hi) - d.lo);
+    const double f2 = fast_exp2(((p2 - P) + e.hi) + e.lo);
+    const double fn = (double)n2;
+    return {fma(s1.a, f1, a * f2), fma(s1.b, f1, b * f2), fma(fma(fn, s1.a, s1.ad), f1, ad * f2),
+            fma(fma(fn, s1.b, s1.bd), f1, bd * f2), P};
+}
 
 // GATED: the output is sigma(r) wkv (eq. (15)); the plain instance compiles none of it.
 template <bool GATED>
@@ -123,15 +139,35 @@ struct WkvCkptOpT {
                                                const Rows& rows) {
         static_assert(VEC == 1, "the kept sums are laid out for one channel per lane");
         if (R.js >= 0 && R.js < n) {  // a multiple of 56 falls in this chunk (same for the wave)
-            // The sums before step js: the carry-in advanced exactly over steps 0 .. js-1 (k is
-            // read again: in[] holds weights relative to the chunk's end, which can underflow
-            // where later steps dominate).
+            // The sums before step js: the carry-in followed by steps 0 .. js-1.  Their weights
+            // at js are the chunk's g_j (relative to its end, exponent p) times 2^{(n-js) om}.
+            // If a later step of the chunk dominates so much that these g_j may have lost
+            // terms to underflow, the steps are re-read and advanced exactly instead.
             Fwd st = cin[0];
+            const int js = R.js;
+            if (js > 0) {
+                float a = 0.f, b = 0.f, ad = 0.f, bd = 0.f, gmax = 0.f;
 #pragma unroll
-            for (int j = 0; j < L; ++j) {
-                if (j < R.js) {
-                    const float kk = ldb<1>(R.base.k, voff, rows.soff(j)).v[0] * kLog2e;
-                    fwd_advance(ch[0].om, st, kk, (double)in[j][0].v, mag(st.p, (float)st.b));
+                for (int j = 0; j < L; ++j) {
+                    if (j < js) {
+                        const float gj = in[j][0].kk, fd = gj * (float)(js - 1 - j);
+                        a = fmaf(gj, in[j][0].v, a);
+                        b += gj;
+                        ad = fmaf(fd, in[j][0].v, ad);
+                        bd += fd;
+                        gmax = fmaxf(gmax, gj);
+                    }
+                }
+                if (gmax >= 0x1p-60f) {
+                    st = fwd_combine_shifted(ch[0].om, st, a, b, ad, bd, loc[0].p, n - js, js);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < L; ++j) {
+                        if (j < js) {
+                            const float kk = ldb<1>(R.base.k, voff, rows.soff(j)).v[0] * kLog2e;
+                            fwd_advance(ch[0].om, st, kk, (double)in[j][0].v, mag(st.p, (float)st.b));
+                        }
+                    }
                 }
             }
             Fwd x[1] = {st};

@@ -76,6 +76,18 @@ def test_ckpt_step_spikes(L):
     check_step(L, d)
 
 
+def test_ckpt_step_spike_after_kept_sum(L):
+    # A kept sum inside a chunk (56 in [48, 64), 168 in [160, 176)) with a spike later in the
+    # same chunk: the chunk's weights of the earlier steps underflow (k = +150, +60), which
+    # sends the kept sum down the step-by-step path, or merely shrink (+30, -40).
+    announce("wkv4 checkpointed step, spikes after a kept sum in the same chunk")
+    d = workloads.make_inputs(3, seed=47, shape=(2, 400, 64))
+    for c, kv in enumerate((150.0, 60.0, 30.0, -40.0)):
+        d["k"][0, 60, 8 * c:8 * c + 8] = kv
+        d["k"][1, 170, 8 * c + 3] = kv
+    check_step(L, d)
+
+
 def test_ckpt_step_exact_path(L, monkeypatch):
     # Both kernels without their frame fast paths (the exact per-step running maximum).
     announce("wkv4 checkpointed step, exact-only paths")
