@@ -210,3 +210,20 @@ def test_ckpt_serves_gated_and_plain_backward(L):
     _, ck = L.wkv4_forward_ckpt(w, u, k, v, r=dev(r))
     got = [host(t) for t in L.wkv4_backward_ckpt(w, u, k, v, dev(d["gy"]), ck)]
     check_bwd(got, oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+
+
+def test_ckpt_step_gated_lookback_recompute(L, monkeypatch):
+    # The gated instance's look-back recompute path (no poll of a predecessor's flag).
+    announce("wkv4 checkpointed gated step with LINREC_SPIN=0")
+    monkeypatch.setenv("LINREC_SPIN", "0")
+    d = workloads.make_inputs(3, seed=48, shape=(2, 1300, 130))
+    r = np.random.default_rng(49).standard_normal(d["k"].shape).astype(np.float32)
+    check_gated_step(L, d, r)
+
+
+def test_ckpt_step_gated_workload3(L):
+    # The gated training step at the size the bench times it (r ~ N(0,1)).
+    announce("wkv4 checkpointed gated step B=8 T=4096 C=2560")
+    d = workloads.make_inputs(3)
+    r = np.random.default_rng(50).standard_normal(d["k"].shape).astype(np.float32)
+    check_gated_step(L, d, r)
