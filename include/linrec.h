@@ -347,10 +347,13 @@ int linrec_scan_real_decay(int64_t B, int64_t T, int64_t C, const float *lambda,
  * of variance s feeds a state of variance s / (1 - |lambda|^2), so the input is scaled to
  * keep the state's scale):
  *
- *   x_t = lambda x_{t-1} + gamma u_t,   gamma[c] = sqrt(1 - |lambda[c]|^2)
+ *   x_t = lambda x_{t-1} + gamma u_t,   gamma[c] = sqrt(max(0, 1 - |lambda[c]|^2))
  *
- * Arguments, layout and workspace as linrec_scan_complex (|lambda| <= 1; gamma is taken
- * as 0 where |lambda| rounds above 1).
+ * Arguments, layout and workspace as linrec_scan_complex.  The method's domain is
+ * |lambda| <= 1 (the write-up's r in [0, 1]); |lambda|^2 is formed in double from the
+ * complex64 components, and where it exceeds 1 (a unit-modulus lambda rounded to
+ * complex64 often does) gamma is 0, its value at r = 1.  Values are not checked: a lambda
+ * well outside the unit disc is also scanned with gamma = 0.
  */
 int linrec_scan_complex_normalized(int64_t B, int64_t T, int64_t C, const float *lambda,
                                    const float *u, const float *x0, float *x, void *workspace,
@@ -430,8 +433,9 @@ int linrec_scan_real_decay_backward(int64_t B, int64_t T, int64_t C, const float
  *   gu_t    = gamma s_t,   gx0 = conj(lambda) s_0,
  *   glambda = sum of s_t conj(x_{t-1}) - (sum of Re(conj(s_t) u_t) / gamma) lambda
  *
- * (gamma = sqrt(1 - |lambda|^2); the second term is dL/dgamma times gamma's gradient, taken
- * as 0 where gamma = 0).  u (B,T,C) complex64 is the forward's input; the rest as
+ * (gamma = sqrt(max(0, 1 - |lambda|^2)) as in the forward; the second term is dL/dgamma
+ * times gamma's gradient, taken as 0 where gamma = 0, where gamma has no derivative).
+ * u (B,T,C) complex64 is the forward's input; the rest as
  * linrec_scan_complex_backward.  Workspace: linrec_scan_backward_workspace_size(B, T, C, 1).
  */
 int linrec_scan_complex_normalized_backward(int64_t B, int64_t T, int64_t C, const float *lambda,

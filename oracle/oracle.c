@@ -574,10 +574,22 @@ void oracle_scan_real_decay(int64_t B, int64_t T, int64_t C, const float *lam, c
 }
 
 /*
+ * gamma = sqrt(1 - |lambda|^2), the normalised LRU's input scale, for a lambda of modulus
+ * r in [0, 1] (LRU write-up: the polar form with r in [0, 1]; the initialisation section's
+ * state variance 1 / (1 - r^2)).  A unit-modulus lambda stored as complex64 often has
+ * |lambda|^2 a rounding above 1; it takes the value at r = 1, gamma = 0.
+ */
+static double lru_gamma(double complex L)
+{
+    return sqrt(fmax(0.0, 1.0 - creal(L * conj(L))));
+}
+
+/*
  * The LRU's normalised input (LRU write-up, initialisation section: with |lambda| < 1 a
  * stationary input of variance s feeds a state of variance s / (1 - |lambda|^2), so the
  * input is scaled by gamma = sqrt(1 - |lambda|^2) to keep the state's scale):
- * x_t = lambda x_{t-1} + gamma u_t, gamma per channel.  Arguments as oracle_scan_complex.
+ * x_t = lambda x_{t-1} + gamma u_t, gamma per channel (lru_gamma).  Arguments as
+ * oracle_scan_complex.
  */
 void oracle_scan_complex_normalized(int64_t B, int64_t T, int64_t C, const float *lam, const float *u,
                                     const float *x0, double *x)
@@ -587,7 +599,7 @@ void oracle_scan_complex_normalized(int64_t B, int64_t T, int64_t C, const float
         const int64_t b = bc / C, c = bc % C;
         const int64_t base = b * T * C + c;
         const double complex L = (double)lam[2 * c] + (double)lam[2 * c + 1] * I;
-        const double gamma = sqrt(1.0 - creal(L * conj(L)));
+        const double gamma = lru_gamma(L);
         double complex s = 0.0;
         if (x0) s = (double)x0[2 * (b * C + c)] + (double)x0[2 * (b * C + c) + 1] * I;
         for (int64_t t = 0; t < T; ++t) {
@@ -717,7 +729,7 @@ void oracle_scan_complex_normalized_backward(int64_t B, int64_t T, int64_t C, co
         const int64_t b = bc / C, c = bc % C;
         const int64_t base = b * T * C + c;
         const double complex L = (double)lam[2 * c] + (double)lam[2 * c + 1] * I;
-        const double gamma = sqrt(1.0 - creal(L * conj(L)));
+        const double gamma = lru_gamma(L);
         const double complex z0 = x0 ? (double)x0[2 * (b * C + c)] + (double)x0[2 * (b * C + c) + 1] * I : 0.0;
         double complex s = 0.0, acc = 0.0;
         double dgam = 0.0;
@@ -742,7 +754,7 @@ void oracle_scan_complex_normalized_backward(int64_t B, int64_t T, int64_t C, co
     }
     for (int64_t c = 0; c < C; ++c) {
         const double complex L = (double)lam[2 * c] + (double)lam[2 * c + 1] * I;
-        const double gamma = sqrt(1.0 - creal(L * conj(L)));
+        const double gamma = lru_gamma(L);
         double re = 0.0, im = 0.0, dg = 0.0;
         for (int64_t b = 0; b < B; ++b) {
             re += part[3 * (b * C + c)];

@@ -106,6 +106,28 @@ def test_complex_normalized(L, shape, tol):
     assert rel_err(got, oracle.scan_complex_normalized(lr["lam"], lr["u"], x0)) <= tol
 
 
+@pytest.mark.parametrize("shape", [(2, 700, 200), (1, 3000, 64), (3, 1, 40)], ids=str)
+def test_complex_normalized_unit_circle(L, shape):
+    """r = 1, the end of the LRU write-up's range r in [0, 1]: lambda = e^{i theta} stored
+    as complex64.  Many such lambdas have |lambda|^2 a rounding above 1 (gamma = 0: the state
+    rotates x0) and the rest a rounding below (gamma ~ 1e-4); both sides take gamma =
+    sqrt(max(0, 1 - |lambda|^2)) from the same complex64 lambda."""
+    B, T, C = shape
+    announce("linrec_scan_complex_normalized unit circle %s" % (shape,))
+    lr = workloads.make_lru(B, T, C, 86, 1.0, 1.0, 2 * math.pi, with_x0=True)
+    lam = lr["lam"].copy()
+    lam[:4] = np.array([1, -1, 1j, -1j], dtype=np.complex64)
+    m2 = lam.real.astype(np.float64) ** 2 + lam.imag.astype(np.float64) ** 2  # exact squares, one rounding
+    assert (m2 > 1.0).sum() >= C // 8 and (m2 < 1.0).sum() >= C // 8
+    ref = oracle.scan_complex_normalized(lam, lr["u"], lr["x0"])
+    assert np.all(np.isfinite(ref))
+    got = host(L.scan_complex_normalized(dev(lam), dev(lr["u"]), dev(lr["x0"])))
+    assert np.all(np.isfinite(got))
+    assert rel_err(got, ref) <= TOL
+    ref0 = oracle.scan_complex_normalized(lam, lr["u"])
+    assert rel_err(host(L.scan_complex_normalized(dev(lam), dev(lr["u"]))), ref0) <= TOL
+
+
 @pytest.mark.parametrize("vec", ["1", "2"])
 def test_lane_widths(L, vec, monkeypatch):
     monkeypatch.setenv("LINREC_VEC", vec)

@@ -118,6 +118,35 @@ def test_complex_normalized_backward(L, shape, with_x0):
     check(got, ref, (None, 1, None))
 
 
+@pytest.mark.parametrize("shape", [(2, 700, 200), (1, 3000, 64), (3, 1, 40)], ids=str)
+def test_complex_normalized_backward_unit_circle(L, shape):
+    """The adjoint at r = 1: complex64 e^{i theta}, many with |lambda|^2 a rounding above 1
+    (gamma = 0: dL/du = 0 and dL/dlambda has no gamma term) and the rest a rounding below
+    (gamma ~ 1e-4, a large gamma term).  dL/dlambda is compared on each group with its own
+    RMS floor, so the large terms below 1 do not loosen the check of those at the edge."""
+    B, T, C = shape
+    announce("linrec_scan_complex_normalized_backward unit circle %s" % (shape,))
+    d = workloads.make_lru(B, T, C, 87, 1.0, 1.0, 2 * math.pi, with_x0=True)
+    d.update(workloads.make_scan_adjoint_inputs(5, d, seed=88))
+    lam = d["lam"].copy()
+    lam[:4] = np.array([1, -1, 1j, -1j], dtype=np.complex64)
+    m2 = lam.real.astype(np.float64) ** 2 + lam.imag.astype(np.float64) ** 2  # exact squares, one rounding
+    edge = m2 >= 1.0
+    assert (m2 > 1.0).sum() >= C // 8 and (~edge).sum() >= C // 8
+    xc = oracle.scan_complex_normalized(lam, d["u"], d["x0"]).astype(np.complex64)
+    got = L.scan_complex_normalized_backward(dev(lam), dev(d["u"]), dev(xc), dev(d["gx"]), dev(d["x0"]),
+                                             want_gx0=True)
+    ref = oracle.scan_complex_normalized_backward(lam, d["u"], xc, d["gx"], d["x0"], want_gx0=True)
+    assert all(np.all(np.isfinite(r)) for r in ref)
+    glam, gu, gx0 = (host(g) for g in got)
+    assert np.all(np.isfinite(glam)) and np.all(np.isfinite(gu)) and np.all(np.isfinite(gx0))
+    assert np.all(gu[..., edge] == 0)
+    errs = {"glam_edge": rel_err(glam[edge], ref[0][edge], None),
+            "glam_inner": rel_err(glam[~edge], ref[0][~edge], None),
+            "gu": rel_err(gu, ref[1]), "gx0": rel_err(gx0, ref[2], None)}
+    assert all(v <= TOL for v in errs.values()), errs
+
+
 def test_gates_with_extreme_logits_backward(L):
     """Logits ~ N(0, 30): the saturated gates' derivatives underflow to 0 and every gradient
     stays finite."""

@@ -75,8 +75,12 @@ MUTANTS = [
      "s = f * s + i * (double)h[o];"),
     ("decay_of_channel_zero", "const double L = (double)lam[c];\n        double s = x0",
      "const double L = (double)lam[0];\n        double s = x0"),
-    ("lru_gamma_without_sqrt", "const double gamma = sqrt(1.0 - creal(L * conj(L)));\n        double complex s = 0.0;",
-     "const double gamma = 1.0 - creal(L * conj(L));\n        double complex s = 0.0;"),
+    ("lru_gamma_without_sqrt", "return sqrt(fmax(0.0, 1.0 - creal(L * conj(L))));",
+     "return fmax(0.0, 1.0 - creal(L * conj(L)));"),
+    ("lru_gamma_unclamped", "return sqrt(fmax(0.0, 1.0 - creal(L * conj(L))));",
+     "return sqrt(1.0 - creal(L * conj(L)));"),
+    ("lru_norm_bwd_gamma_term_at_edge", "const double k = gamma > 0.0 ? dg / gamma : 0.0;",
+     "const double k = dg / gamma;"),
     ("gated_bwd_gr_without_sigmoid_slope", "gr[o] = (double)gy[o] * yt * sg * (1.0 - sg);", "gr[o] = (double)gy[o] * yt * sg;"),
     ("gated_bwd_ungated_k_grad", "                const double ks = (double)k[o], vs = (double)v[o];\n                const double g = r ? (double)gy[o] * sigmoid((double)r[o]) : (double)gy[o];",
      "                const double ks = (double)k[o], vs = (double)v[o];\n                const double g = (double)gy[o];"),
@@ -247,6 +251,21 @@ def _pins_pass(lib) -> bool:
     brute.lru_normalized_torch(tl, tu, tc0).backward(torch.tensor(gxc, dtype=torch.complex128))
     for m, t in zip(mine, (tl, tu, tc0)):
         ok &= np.allclose(m, t.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+    # The normalised LRU at r = 1 (gamma = 0; complex64 lambdas on the unit circle, several
+    # with |lam|^2 rounding above 1): the state rotates x0, nothing reaches u, and the
+    # adjoint's dL/dlambda, dL/dx0 are the plain scan's unrolled adjoint sums.
+    lu = workloads.make_lru(2, 12, 24, 27, 1.0, 1.0, 2 * math.pi, with_x0=True)
+    edge = lu["lam"].real.astype(np.float64) ** 2 + lu["lam"].imag.astype(np.float64) ** 2 >= 1.0
+    xu = oracle.scan_complex_normalized(lu["lam"], lu["u"], lu["x0"], lib=lib)
+    rot = brute.scan_complex_sums(lu["lam"], np.zeros(lu["u"].shape, np.complex128), lu["x0"])
+    ok &= bool(edge.sum() >= 4) and np.allclose(xu[..., edge], rot[..., edge], rtol=1e-12, atol=1e-13)
+    gu_ = (rng.standard_normal(lu["u"].shape) + 1j * rng.standard_normal(lu["u"].shape)).astype(np.complex64)
+    gl, gq, g0 = oracle.scan_complex_normalized_backward(lu["lam"], lu["u"], rot, gu_, lu["x0"], want_gx0=True,
+                                                         lib=lib)
+    rl, _, r0 = brute.scan_complex_backward_sums(lu["lam"][edge], gu_[..., edge], rot[..., edge], lu["x0"][:, edge])
+    ok &= np.allclose(gl[edge], rl, rtol=1e-10, atol=1e-10) and np.allclose(g0[:, edge], r0, rtol=1e-11, atol=1e-11)
+    ok &= bool(np.all(gq[..., edge] == 0))
     return bool(ok)
 
 

@@ -109,6 +109,27 @@ def test_complex_normalized_unrolled_sums():
     np.testing.assert_allclose(oracle.scan_complex_normalized(lr["lam"], lr["u"], x0), ref, rtol=1e-11, atol=1e-12)
 
 
+def test_complex_normalized_on_the_unit_circle():
+    """r = 1, the end of the LRU write-up's range r in [0, 1]: gamma = 0, so the state only
+    rotates x0, x_t = lam^{t+1} x0.  A unit-modulus lambda stored as complex64 has |lam|^2
+    a rounding above or below 1; above (and at 1 exactly) the state is that rotation and
+    finite, below it gamma is the small sqrt(1 - |lam|^2) of the unrolled sums."""
+    lr = workloads.make_lru(2, 40, 64, 27, 1.0, 1.0, 2 * math.pi, with_x0=True)
+    lam = lr["lam"].copy()
+    lam[:4] = np.array([1, -1, 1j, -1j], dtype=np.complex64)
+    m2 = lam.real.astype(np.float64) ** 2 + lam.imag.astype(np.float64) ** 2  # exact squares, one rounding
+    edge = m2 >= 1.0
+    assert edge.sum() >= 16 and (m2 > 1.0).sum() >= 8 and (~edge).sum() >= 8
+    x = oracle.scan_complex_normalized(lam, lr["u"], lr["x0"])
+    assert np.all(np.isfinite(x))
+    rot = brute.scan_complex_sums(lam, np.zeros(lr["u"].shape, np.complex128), lr["x0"])
+    np.testing.assert_allclose(x[..., edge], rot[..., edge], rtol=1e-12, atol=1e-13)
+    gamma = np.sqrt(1.0 - m2[~edge])
+    inner = brute.scan_complex_sums(lam[~edge], gamma * lr["u"][..., ~edge].astype(np.complex128),
+                                    lr["x0"][:, ~edge])
+    np.testing.assert_allclose(x[..., ~edge], inner, rtol=1e-9, atol=1e-10)
+
+
 def test_complex_normalized_keeps_unit_variance():
     """White input of unit variance: the normalised state has unit variance once the start
     is forgotten (the raw one has 1 / (1 - |lam|^2)); 64 x 32 sequences, 5% tolerance."""

@@ -108,6 +108,35 @@ def test_lru_normalized_backward_matches_autograd(with_x0):
     close(gx0, tx0.grad.numpy())
 
 
+def test_lru_normalized_backward_on_the_unit_circle():
+    """r = 1 (gamma = 0, including complex64 lambdas whose |lam|^2 rounds above 1): nothing
+    reaches u, and dL/dlambda and dL/dx0 are the plain complex scan's unrolled adjoint sums
+    (gamma has no derivative there and its term is taken as 0); below 1 the gradients are
+    torch autograd's of the plain torch forward."""
+    B, T, C = 2, 30, 48
+    lr = workloads.make_lru(B, T, C, 31, 1.0, 1.0, 2 * math.pi, with_x0=True)
+    lam = lr["lam"].copy()
+    lam[:4] = np.array([1, -1, 1j, -1j], dtype=np.complex64)
+    m2 = lam.real.astype(np.float64) ** 2 + lam.imag.astype(np.float64) ** 2  # exact squares, one rounding
+    edge = m2 >= 1.0
+    assert (m2 > 1.0).sum() >= 8 and (~edge).sum() >= 8
+    g = (rnd((B, T, C), 32) + 1j * rnd((B, T, C), 33)).astype(np.complex64)
+    x = oracle.scan_complex_normalized(lam, lr["u"], lr["x0"])
+    glam, gu, gx0 = oracle.scan_complex_normalized_backward(lam, lr["u"], x, g, lr["x0"], want_gx0=True)
+    assert np.all(np.isfinite(glam)) and np.all(np.isfinite(gu)) and np.all(np.isfinite(gx0))
+    assert np.all(gu[..., edge] == 0)
+    rl, _, r0 = brute.scan_complex_backward_sums(lam[edge], g[..., edge], x[..., edge], lr["x0"][:, edge])
+    close(glam[edge], rl, rtol=1e-10, atol=1e-10)
+    close(gx0[:, edge], r0, rtol=1e-11, atol=1e-11)
+    tl, tu, tx0 = t64(lam[~edge]), t64(lr["u"][..., ~edge]), t64(lr["x0"][:, ~edge])
+    brute.lru_normalized_torch(tl, tu, tx0).backward(torch.tensor(g[..., ~edge], dtype=torch.complex128))
+    # Just below 1, 1 - |lam|^2 cancels to ~1e-8, so torch's |lam| (a square root, then
+    # squared) and the oracle's exact |lam|^2 give gamma's -lam/gamma term to ~1e-8 only.
+    close(glam[~edge], tl.grad.numpy(), rtol=1e-7, atol=1e-9)
+    close(gu[..., ~edge], tu.grad.numpy(), rtol=1e-7, atol=1e-12)
+    close(gx0[:, ~edge], tx0.grad.numpy())
+
+
 # ---- finite differences of the plain forward ---------------------------------------
 
 def test_minlstm_backward_finite_differences():
