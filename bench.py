@@ -8,6 +8,12 @@ already resident in HBM.  Prints ONE JSON line on stdout; diagnostics go to stde
 Input/output buffer sets are rotated so that the 256 MB last-level cache (MALL) cannot
 serve a repeated call: R = ceil(2 * 256 MB / footprint) sets.
 
+The line also carries ``stream_ceiling`` (the same bytes moved by a plain elementwise
+kernel, y = k + v, over the same rotated buffers), ``copy_probe_GBps`` (a 1 GiB device copy)
+and ``workloads``: the WKV forward, backward and checkpointed training step at B=8 T=4096
+C=2560, the real scan and fused minGRU at B=64 T=4096 C=256 and the LRU complex scan at B=1
+T=262144 C=1024, a few launches each (``--no-workloads`` skips them).
+
 ``--all`` also measures the other rows (WKV-4 forward, backward and gated backward at B=8
 T=4096 C=2560; the real scan, minGRU, minLSTM, the per-channel decay and their adjoints at
 B=64 T=4096 C=256; the LRU complex scan, the normalised LRU and their adjoints at B=1
@@ -467,6 +473,70 @@ def copy_probe():
     return round(2 * 4 * n / s / 1e9, 1)
 
 
+def host_info():
+    """The host the CPU baseline ran on: logical CPUs, the threads the process may use, the
+    OpenMP setting and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"os_cpu_count": os.cpu_count(), "usable_cpus": usable,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "cpu_model": model}
+
+
+def stream_ceiling(B, T, C, rotations, steps, warmup):
+    """The same bytes as one wkv4_forward call moved by a plain elementwise kernel:
+    y = k + v (torch.add) over the same rotated buffer sets, 8 B read and 4 B written per
+    element, timed with HIP events on the launch stream like the forward.  It is the
+    attainable streaming rate for this footprint and access pattern on the box."""
+    import torch
+
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    sets = []
+    for _ in range(rotations):
+        k = torch.randn((B, T, C), device=dev, generator=g)
+        v = torch.randn((B, T, C), device=dev, generator=g)
+        sets.append((k, v, torch.empty_like(k)))
+    for i in range(warmup):
+        k, v, y = sets[i % rotations]
+        torch.add(k, v, out=y)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(steps):
+        k, v, y = sets[(warmup + i) % rotations]
+        torch.add(k, v, out=y)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    s = ev0.elapsed_time(ev1) / 1e3 / steps
+    del sets
+    torch.cuda.empty_cache()
+    gbps = 12 * B * T * C / s / 1e9
+    return {"what": "torch.add(k, v, out=y), fp32 (B=%d, T=%d, C=%d), %d rotated buffer sets" % (B, T, C, rotations),
+            "us_per_launch": round(s * 1e6, 3), "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
+def summary(res):
+    """The figures of one measured row for the headline line's per-workload block."""
+    rf = res["roofline"]
+    return {"kind": res["kind"], "workload": res["workload"], "B": res["B"], "T": res["T"], "C": res["C"],
+            "steps": res["steps"], "us_per_launch": round(res["event_ms_per_step"] * 1e3, 2),
+            "elements_per_s": res["elements_per_s"], "GBps": rf["achieved"], "frac": rf["frac"],
+            "traffic": rf["traffic"], "algorithmic_bytes": rf["algorithmic_bytes"]}
+
+
 def make_host(wid, kind, shape=None):
     """The seeded host inputs of one row: workload ``wid``'s generator at ``shape``."""
     from linear_recurrence_rnn_amd import workloads
@@ -489,12 +559,13 @@ def make_host(wid, kind, shape=None):
     return host
 
 
-def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=None):
+def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=None, host=None):
     from linear_recurrence_rnn_amd import workloads
 
     wl = workloads.WORKLOADS[wid]
     B, T, C = shape or (wl.B, wl.T, wl.C)
-    host = make_host(wid, kind, (B, T, C))
+    if host is None:
+        host = make_host(wid, kind, (B, T, C))
     elements = B * T * C
     label = wl.label
     variant_labels = {"scan_mingru": "minGRU from gate logits", "scan_minlstm": "minLSTM from gate logits",
@@ -524,12 +595,14 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
     per_step = wall / steps
     per_launch = ev_s / steps
     out = {
-        "kind": kind, "workload": label, "B": B, "T": T, "C": C, "rotations": R,
+        "kind": kind, "workload": label, "B": B, "T": T, "C": C, "rotations": R, "steps": steps,
         "ms_per_step": round(per_step * 1e3, 5), "event_ms_per_step": round(per_launch * 1e3, 5),
         "elements_per_s": elements / per_step,
         "roofline": roofline(kind, elements, per_launch, counter_traffic(kind)),
     }
     del row
+    import torch
+    torch.cuda.empty_cache()
     if cpu_budget > 0:
         sample = host
         desc = "full workload"
@@ -547,7 +620,8 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
         med, reps, cores = cpu_baseline(kind, sample, cpu_budget)
         n_el = B * (cpu_slice or T) * C
         out["cpu_baseline"] = {"value": n_el / med, "unit": "elements/s", "cores": cores, "kind": "oracle",
-                               "sample": "%s (%d elements), median of %d run(s)" % (desc, n_el, reps)}
+                               "sample": "%s (%d elements), median of %d run(s)" % (desc, n_el, reps),
+                               "host": host_info()}
     return out
 
 
@@ -559,8 +633,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle CPU baseline (0 skips it)")
     ap.add_argument("--no-copy-probe", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads' figures in the headline line")
     ap.add_argument("--all", action="store_true", help="also measure the other workloads")
     ap.add_argument("--all-out", default=None, help="write the --all rows to this JSON file")
+    ap.add_argument("--only", default=None,
+                    help="KIND@WORKLOAD[,...]: time only these rows (e.g. wkv4_backward@3), one JSON "
+                         "line each, no headline line (for profiler runs)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -576,6 +655,14 @@ def main():
         log("bench.py needs a ROCm GPU")
         sys.exit(1)
     lib = binding.load()
+    if args.only:
+        for item in args.only.split(","):
+            kind, wid = item.split("@")
+            if kind not in BYTES_PER_ELEM:
+                log("unknown row %r; rows: %s" % (kind, ", ".join(sorted(BYTES_PER_ELEM))))
+                sys.exit(2)
+            print(json.dumps(measure(lib, int(wid), kind, args.steps, args.warmup, 0)), flush=True)
+        return
     res = measure(lib, 2, "wkv4_forward", args.steps, args.warmup, args.cpu_seconds)
     line = {
         "metric": METRIC,
@@ -599,7 +686,23 @@ def main():
     if "cpu_baseline" in res:
         line["cpu_baseline"] = res["cpu_baseline"]
     if not args.no_copy_probe:
+        line["stream_ceiling"] = stream_ceiling(8, 1024, 768, res["rotations"], args.steps, args.warmup)
         line["copy_probe_GBps"] = copy_probe()
+    if not args.no_workloads:
+        # The other workloads, measured in the same run with a few launches each: the WKV
+        # forward, backward and checkpointed training step at B=8 T=4096 C=2560, the real
+        # scan and fused minGRU at B=64 T=4096 C=256 (the minGRU page's batch 64 x seq 4096)
+        # and the LRU complex scan at B=1 T=262144 C=1024.
+        extras = []
+        h3 = make_host(3, "wkv4_backward")
+        for kind in ("wkv4_forward", "wkv4_backward", "wkv4_train_step_ckpt"):
+            extras.append(summary(measure(lib, 3, kind, 20, 3, 0, host=h3)))
+            log("[bench] " + json.dumps(extras[-1]))
+        del h3
+        for wid, kind, steps in ((4, "scan_real", 20), (4, "scan_mingru", 20), (5, "scan_complex", 10)):
+            extras.append(summary(measure(lib, wid, kind, steps, 3, 0)))
+            log("[bench] " + json.dumps(extras[-1]))
+        line["workloads"] = extras
     print(json.dumps(line), flush=True)
 
     if args.all:
