@@ -443,6 +443,30 @@ int linrec_scan_complex_normalized_backward(int64_t B, int64_t T, int64_t C, con
                                             const float *gx, float *glambda, float *gu, float *gx0,
                                             void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * wkv4_forward without a workspace argument, for callers that cannot allocate device memory
+ * or pass a workspace: code being captured into a HIP graph, tight serving loops, harnesses
+ * that forbid allocation.  It computes exactly what wkv4_forward computes (the same kernels);
+ * the look-back flags and records those kernels need live in a static device array of
+ * LINREC_NOALLOC_SCRATCH_BYTES that the library keeps on every GPU it runs on until the
+ * process ends.  The call allocates and frees nothing.
+ *
+ *   arguments as wkv4_forward, without workspace / ws_bytes;
+ *   a call whose launch needs more scratch than the array holds (e.g. B=8 T=1024 C=768 needs
+ *   about 1.2 MB, B=8 T=4096 C=2560 about 15.8 MB) returns LINREC_ERR_UNSUPPORTED before any
+ *   HIP call; use wkv4_forward with a workspace for those;
+ *   calls on one GPU share its array: two calls that may run at the same time on one GPU
+ *   (different streams, or different host threads on different streams) race and must be
+ *   ordered by the caller.  Calls in sequence on one stream are safe: the flags carry a
+ *   per-call tag, so an earlier call's records never read as this call's.
+ *   The first call on each device looks up the array's address there (hipGetSymbolAddress,
+ *   with that device current); a failure is LINREC_ERR_HIP.
+ */
+#define LINREC_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+int wkv4_forward_noalloc(int64_t B, int64_t T, int64_t C,
+                         const float *w, const float *u, const float *k, const float *v,
+                         float *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

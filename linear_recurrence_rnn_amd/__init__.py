@@ -6,7 +6,7 @@ The binding is imported lazily so that ``linear_recurrence_rnn_amd.workloads`` (
 input generators) can be used without loading the GPU library.
 """
 
-__all__ = ["wkv4_forward", "wkv4_forward_ex", "wkv4_decode_step", "token_shift", "token_shift_backward", "wkv4_backward", "wkv4_backward_gated", "wkv4_backward_ex",
+__all__ = ["wkv4_forward", "wkv4_forward_noalloc", "wkv4_forward_ex", "wkv4_decode_step", "token_shift", "token_shift_backward", "wkv4_backward", "wkv4_backward_gated", "wkv4_backward_ex",
            "wkv4_forward_ckpt", "wkv4_backward_ckpt", "wkv4_checkpoint_size", "scan_real", "scan_complex", "scan_real_backward",
            "scan_complex_backward", "scan_mingru", "scan_minlstm", "scan_real_decay",
            "scan_complex_normalized", "scan_mingru_backward", "scan_minlstm_backward",

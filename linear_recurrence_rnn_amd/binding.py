@@ -61,6 +61,8 @@ def load(path: str | None = None):
         lib.wkv4_forward.restype = ctypes.c_int
         lib.wkv4_forward.argtypes = [_I64, _I64, _I64] + [_VP] * 5 + [_VP, _SZ, _VP]
         lib.wkv4_forward_ex.restype = ctypes.c_int
+        lib.wkv4_forward_noalloc.restype = ctypes.c_int
+        lib.wkv4_forward_noalloc.argtypes = [_I64, _I64, _I64] + [_VP] * 5 + [_VP]
         lib.wkv4_forward_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 8 + [_VP, _SZ, _VP]
         lib.wkv4_backward.restype = ctypes.c_int
         for name, n in (("linrec_scan_mingru", 4), ("linrec_scan_minlstm", 5), ("linrec_scan_real_decay", 4),
@@ -175,6 +177,24 @@ def wkv4_forward(w, u, k, v, out=None, workspace=None):
     ws, nws = _workspace(int(lib.wkv4_forward_workspace_size(B, T, C)), dev, workspace)
     _check(lib.wkv4_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(ws), nws,
                             _stream(dev)), "wkv4_forward")
+    return y
+
+
+def wkv4_forward_noalloc(w, u, k, v, out=None):
+    """y as wkv4_forward, through the entry point that takes no workspace (its scratch is a
+    static device array of the library; see include/linrec.h for the size limit and the rule
+    that calls overlapping on one GPU race)."""
+    lib = load()
+    B, T, C = k.shape
+    dev = k.device
+    _expect(k, "k", torch.float32, (B, T, C), dev)
+    _expect(w, "w", torch.float32, (C,), dev)
+    _expect(u, "u", torch.float32, (C,), dev)
+    _expect(v, "v", torch.float32, (B, T, C), dev)
+    y = out if out is not None else torch.empty_like(k)
+    _expect(y, "out", torch.float32, (B, T, C), dev)
+    _check(lib.wkv4_forward_noalloc(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _stream(dev)),
+           "wkv4_forward_noalloc")
     return y
 
 

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <initializer_list>
+#include <mutex>
 #include <random>
 #include <string>
 
@@ -772,4 +773,70 @@ LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, co
                              float* gk, float* gv, void* workspace, size_t ws_bytes, void* stream) {
     return wkv4_backward_ex(B, T, C, w, u, k, v, nullptr, nullptr, nullptr, gy, nullptr, gw, gu, gk, gv, nullptr,
                             nullptr, workspace, ws_bytes, stream);
+}
+
+// ---- the forward for callers that cannot allocate ----
+// wkv4_forward_noalloc runs wkv4_forward's kernels with their look-back flags and records in
+// `scratch`, a file-scope device array, instead of a caller workspace.  The runtime gives
+// each GPU its own copy of the array, at its own address: the host-side name is only a
+// stand-in, so kernels are handed the address hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept.
+namespace {
+
+static_assert(LINREC_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch is whole 256-byte blocks");
+__device__ __align__(256) unsigned char scratch[LINREC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` per device (null: not looked up)
+
+// The device address of `scratch` on the current device; the first call on a device looks
+// it up (with that device current) and keeps it.
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(LINREC_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(LINREC_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return LINREC_OK;
+}
+
+}  // namespace
+
+LINREC_API int wkv4_forward_noalloc(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                                    const float* k, const float* v, float* y, void* stream) {
+    int st = check_shape(B, T, C, 4);
+    if (st) return st;
+    if (B == 0 || T == 0 || C == 0) return ok();
+    if (!w || !u || !k || !v || !y) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
+    const void* ptrs[] = {w, u, k, v, y};
+    for (const void* p : ptrs)
+        if (!aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
+    const int vec = pick_vec(linrec::kKindWkv,
+                             (C % 4 == 0 && aligned(k, 16) && aligned(v, 16) && aligned(y, 16))  ? 4
+                             : (C % 2 == 0 && aligned(k, 8) && aligned(v, 8) && aligned(y, 8)) ? 2
+                                                                                                  : 1,
+                             B * T * C, true);
+    const linrec::ScanPlan p = scan_plan(linrec::kKindWkv, vec, B, T, C);
+    if (p.ws_bytes > (size_t)LINREC_NOALLOC_SCRATCH_BYTES)
+        return fail(LINREC_ERR_UNSUPPORTED,
+                    "B=%lld T=%lld C=%lld needs %zu bytes of scratch; the static array holds %zu (use wkv4_forward "
+                    "with a workspace)",
+                    (long long)B, (long long)T, (long long)C, p.ws_bytes, (size_t)LINREC_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws))) return st;
+    // The flags carry a per-call tag and the array starts zeroed (static storage), so neither
+    // an earlier call's records nor the initial contents read as published: nothing needs
+    // clearing.
+    const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0, nullptr, nullptr, nullptr};
+    return hip_status(linrec::run_wkv_forward(A, geom_of(linrec::kKindWkv, p, B, T, C, ws), p, (hipStream_t)stream),
+                      "wkv4_forward_noalloc launch");
 }

@@ -334,3 +334,21 @@ def test_wkv4_checkpoint_argument_checks(lib):
     assert lib.wkv4_forward_ckpt(0, T, C, None, None, None, None, None, None, None, 0, None, 0, None) == OK
     assert lib.wkv4_backward_ckpt(B, T, 0, None, None, None, None, None, None, None, 0, None, None, None, None,
                                   None, None, 0, None) == OK
+
+
+def test_noalloc_forward_host_checks(lib):
+    """wkv4_forward_noalloc: the same argument checks as wkv4_forward, and a launch that would
+    need more scratch than the library's static array holds is refused before any HIP call."""
+    m = re.search(r"#define LINREC_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", open(HEADER).read())
+    limit = int(m.group(1)) << 20
+    na = lib.wkv4_forward_noalloc
+    assert na(-1, 4, 4, P, P, P, P, P2, None) == INVALID
+    assert na(1, 4, 4, P, None, P, P, P2, None) == INVALID
+    assert na(1, 4, 4, P, P, ODD, P, P2, None) == UNSUPPORTED
+    assert na(0, 16, 16, P, P, P, P, P2, None) == OK
+    assert na(2, 0, 16, None, None, None, None, None, None) == OK
+    # The bench and long-context shapes fit; a much larger one does not.
+    assert lib.wkv4_forward_workspace_size(8, 1024, 768) < limit
+    assert lib.wkv4_forward_workspace_size(64, 65536, 1024) > limit
+    assert na(64, 65536, 1024, P, P, P, P, P2, None) == UNSUPPORTED
+    assert b"scratch" in lib.linrec_last_error()
