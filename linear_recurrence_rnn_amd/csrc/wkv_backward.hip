@@ -360,15 +360,40 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
     const unsigned rowb = (unsigned)(g.C * 4);
     const unsigned voff = (unsigned)(lane * 4);
     const int64_t total = g.B * g.T * g.C;
+    // Item u = q G + b ngrp + grp.  This workgroup's items u_i = blockIdx + i grid are
+    // decomposed once and then advanced by the decomposed grid step, so the walk divides
+    // nothing (a 64-bit division is a long scalar sequence, and it ran twice per chunk).
     struct Item { int64_t q, gi, b, grp, c0; bool active; };
-    auto item_of = [&](int64_t u) {
-        Item it;
-        it.q = u / G;
-        it.gi = u - it.q * G;
-        it.b = it.gi / g.ngrp;
-        it.grp = it.gi - it.b * g.ngrp;
+    const int64_t ugrid = gridDim.x;
+    const int64_t dq = ugrid / G, dgi = ugrid - dq * G;
+    const int64_t db = dgi / g.ngrp, dgrp = dgi - db * g.ngrp;
+    auto settle = [&](Item& it) {
+        it.gi = it.b * g.ngrp + it.grp;
         it.c0 = it.grp * 64 + lane;
         it.active = it.c0 < g.C;
+    };
+    auto first_item = [&]() {
+        Item it;
+        it.q = (int64_t)blockIdx.x / G;
+        const int64_t gi = (int64_t)blockIdx.x - it.q * G;
+        it.b = gi / g.ngrp;
+        it.grp = gi - it.b * g.ngrp;
+        settle(it);
+        return it;
+    };
+    auto next_item = [&](Item it) {  // u -> u + grid
+        it.grp += dgrp;
+        it.b += db;
+        if (it.grp >= g.ngrp) {
+            it.grp -= g.ngrp;
+            ++it.b;
+        }
+        it.q += dq;
+        if (it.b >= g.B) {
+            it.b -= g.B;
+            ++it.q;
+        }
+        settle(it);
         return it;
     };
 
@@ -378,9 +403,15 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
         const int64_t my_items = blockIdx.x < items ? (items - 1 - blockIdx.x) / gridDim.x + 1 : 0;
         const int64_t nt = my_items * NW;
         float kk[2][L], vv[2][L], wr[2];
-        auto issue = [&](int64_t t, int bs) {
-            const Item it = item_of((int64_t)blockIdx.x + (t / NW) * gridDim.x);
-            const int c = (int)(t % NW);
+        Item iss = first_item();  // chunk c_iss of item iss is the next to be issued
+        int c_iss = 0;
+        auto issue = [&](int bs) {
+            const Item it = iss;
+            const int c = c_iss;
+            if (++c_iss == NW) {
+                c_iss = 0;
+                iss = next_item(iss);
+            }
             const int64_t f = it.q * F + w;
             const bool valid = it.active && f < nfine;
             const int64_t base = (it.b * g.T + f * SLAB + (int64_t)c * L) * g.C + it.grp * 64;
@@ -394,16 +425,22 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
         };
         Fwd acc = fwd_identity();
         int ib = 0;
+        Item cur = first_item();  // chunk c_cur of item cur is the next to be reduced
+        int c_cur = 0;
         auto step = [&](int64_t t, int bs) {
-            const Item it = item_of((int64_t)blockIdx.x + (t / NW) * gridDim.x);
-            const int c = (int)(t % NW);
+            const Item it = cur;
+            const int c = c_cur;
+            if (++c_cur == NW) {
+                c_cur = 0;
+                cur = next_item(cur);
+            }
             const bool valid = it.active && it.q * F + w < nfine;
             const float om = fminf(wr[bs] * kLog2e, kMaxOm);
             float kl[L];
 #pragma unroll
             for (int j = 0; j < L; ++j) kl[j] = kk[bs][j] * kLog2e;
             const Fwd chunk = fwd_chunk1<L>(om, kl, vv[bs], valid ? L : 0);
-            if (t + 1 < nt) issue(t + 1, bs ^ 1);
+            if (t + 1 < nt) issue(bs ^ 1);
             acc = (c == 0) ? chunk : fwd_combine(om, acc, chunk, L);
             if (c == NW - 1) {
                 shf[ib][w][lane] = acc;
@@ -411,7 +448,7 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
                 ib ^= 1;
             }
         };
-        if (nt > 0) issue(0, 0);
+        if (nt > 0) issue(0);
         for (int64_t t = 0; t < nt; t += 2) {
             step(t, 0);
             if (t + 1 < nt) step(t + 1, 1);
@@ -421,8 +458,8 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
 
     // ---- coordinator ----
     int ib = 0;
-    for (int64_t u = blockIdx.x; u < items; u += gridDim.x, ib ^= 1) {
-        const Item it = item_of(u);
+    Item it = first_item();
+    for (int64_t u = blockIdx.x; u < items; u += gridDim.x, ib ^= 1, it = next_item(it)) {
         float om[1], mu[1];
         load_chan<1>(A, it.c0, it.active, om, mu);
         const Chain<Fwd> chn{g.flags_c + it.gi * nitem, reinterpret_cast<uint32_t*>(g.agg_c) + it.gi * nitem * kRec,
