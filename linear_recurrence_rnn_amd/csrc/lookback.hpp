@@ -3,7 +3,8 @@
 // A sequence is cut into slabs that the recurrence visits in a fixed order, the chain
 // (q = 0 first: time order for a forward scan, reverse time order for a backward one).  Each
 // slab publishes its aggregate (AGG), then -- once it knows its carry-in -- its inclusive
-// prefix (INCL).  A slab's carry is the nearest published INCL folded with the aggregates
+// prefix (INCL); a slab that knows its carry before its aggregate is formed may publish
+// INCL alone (its flag never reads AGG, so no reader looks for the missing record).  A slab's carry is the nearest published INCL folded with the aggregates
 // of the slabs after it, in chain order: the association a strictly chained scan would use,
 // so the result does not depend on timing.
 //
@@ -152,11 +153,11 @@ __device__ __forceinline__ void look_back(const Chain<Agg>& ch, int64_t q, int l
     if (j0 >= 0) load_record<VEC>(ch.incl, j0, lane, carry);
     for (int64_t j = j0 + 1; j < q; j += KB) {
         Agg xb[KB][VEC];
-        bool pubb[KB];
+        bool pubb[KB], inclb[KB];
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             const int64_t jj = j + k;
-            pubb[k] = false;
+            pubb[k] = inclb[k] = false;
             if (jj < q) {
                 const int64_t back = q - 1 - jj;  // lane index of slab jj in its window
                 const int x = (int)(back >> 6);
@@ -167,19 +168,29 @@ __device__ __forceinline__ void look_back(const Chain<Agg>& ch, int64_t q, int l
                         if (y == x) m = pub[y];
                     pubb[k] = (m >> (back & 63)) & 1;
                 } else {
-                    const uint64_t f = (lane == 0) ? poll_flag(ch.flags + jj, ch.tag, ch.spin) : 0;
-                    pubb[k] = (first_lane_u64(f) >> 2) == ch.tag;
+                    // Beyond the remembered windows the flag is read again.  A slab may
+                    // publish its inclusive prefix without an aggregate (a writer that knew
+                    // its carry early); one seen now replaces the carry folded so far, which
+                    // it extends in the same association.
+                    const uint64_t f = first_lane_u64((lane == 0) ? poll_flag(ch.flags + jj, ch.tag, ch.spin) : 0);
+                    pubb[k] = (f >> 2) == ch.tag;
+                    inclb[k] = f == ch.tag * 4 + kStateIncl;
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 }
-                if (pubb[k]) load_record<VEC>(ch.agg, jj, lane, xb[k]);
+                if (pubb[k]) load_record<VEC>(inclb[k] ? ch.incl : ch.agg, jj, lane, xb[k]);
             }
         }
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             const int64_t jj = j + k;
             if (jj < q) {
-                if (!pubb[k]) recompute(jj, xb[k]);  // not published in time
-                fold(carry, xb[k], jj);
+                if (inclb[k]) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) carry[e] = xb[k][e];
+                } else {
+                    if (!pubb[k]) recompute(jj, xb[k]);  // not published in time
+                    fold(carry, xb[k], jj);
+                }
             }
         }
     }

@@ -913,7 +913,9 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         sh_mine[lane * VEC + e] = mine[e];  // kept in LDS across the look-back (registers)
     }
     const bool has_succ = s > 0;
-    if (has_succ) publish<VEC>(chn, q, lane, mine, false);
+    // With the carry already known the inclusive record follows at once: the aggregate would
+    // only cost the workgroup one more write round trip before its slot is released.
+    if (has_succ && !early) publish<VEC>(chn, q, lane, mine, false);
     if (!early) {
         auto recompute = [&](int64_t jj, RevRec (&x)[VEC]) {
             rev_record_from_inputs<VEC, SLAB, STATE>(A, g, jj, gi, b, grp, lane, active, om, mu, x);
