@@ -38,8 +38,9 @@ namespace linrec {
 namespace scan_kernel {
 
 // Waves per SIMD the register budget is set for.  When a compute wave holds at most 32
-// floats of chunk data, 7 waves (<= 72 VGPRs) fit without spilling and let three 9-wave
-// workgroups share a CU, so one workgroup's look-back hides behind the others' streaming.
+// floats of chunk data, 7 waves (<= 72 VGPRs) fit without spilling, and a CU holds three of
+// the 8-wave workgroups (coordination in wave 0; the SGPR budget allows about 28 waves per
+// CU), so one workgroup's look-back hides behind the others' streaming.
 // Other shapes (wider chunks, or several channels per lane of WKV or complex pairs, whose
 // per-channel state is larger) spill at that budget and keep the compiler's choice.
 // The gated WKV instance also holds r per step (80 VGPRs, 6 waves per SIMD): its 8-wave
