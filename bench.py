@@ -62,7 +62,9 @@ BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "sca
                   "wkv4_train_step": 32,         # forward (12) then backward (20), separate passes
                   "wkv4_train_step_ckpt": 32,    # the same step, the backward from the forward's sums
                   "wkv4_train_step_gated": 44,   # gated forward (16) then gated backward (28)
-                  "wkv4_train_step_gated_ckpt": 44}
+                  "wkv4_train_step_gated_ckpt": 44,
+                  "wkv4_train_step_state": 32,   # forward then backward of a piece with a carried state
+                  "wkv4_train_step_state_ckpt": 32}
 SHIFT_M = 3  # token-shift mixes timed: the r, k, v inputs of the time mix
 
 
@@ -95,6 +97,8 @@ KERNEL_SOURCES["wkv4_train_step"] = tuple(sorted(set(_SCAN_SOURCES + KERNEL_SOUR
 KERNEL_SOURCES["wkv4_train_step_gated"] = KERNEL_SOURCES["wkv4_train_step"]
 KERNEL_SOURCES["wkv4_train_step_gated_ckpt"] = tuple(sorted(set(
     _SCAN_SOURCES + KERNEL_SOURCES["wkv4_backward"] + ("wkv_ckpt.hip", "wkv_sums.hpp"))))
+KERNEL_SOURCES["wkv4_train_step_state"] = KERNEL_SOURCES["wkv4_train_step"]
+KERNEL_SOURCES["wkv4_train_step_state_ckpt"] = KERNEL_SOURCES["wkv4_train_step_gated_ckpt"]
 KERNEL_SOURCES["wkv4_train_step_ckpt"] = tuple(sorted(set(
     _SCAN_SOURCES + KERNEL_SOURCES["wkv4_backward"] + ("wkv_ckpt.hip", "wkv_sums.hpp"))))
 for _k in ("scan_mingru_backward", "scan_minlstm_backward", "scan_real_decay_backward",
@@ -166,7 +170,7 @@ class Row:
                                    v.data_ptr(), gy.data_ptr(), gw.data_ptr(), gu.data_ptr(),
                                    gk.data_ptr(), gv.data_ptr(), ws.data_ptr(), nws, stream)))
             self.keep += [w, u]
-        elif kind.startswith("wkv4_train_step"):
+        elif kind.startswith("wkv4_train_step") and "_state" not in kind:
             # One training step of the WKV layer: the forward, then the backward of its output
             # (with the sigma(r) gate of the time mix for the gated rows).
             w, u = to(host["w"]), to(host["u"])
@@ -204,6 +208,48 @@ class Row:
                     fa = (lib.wkv4_forward, (B, T, C, p(w), p(u), p(k), p(v), p(y), p(fws), nfw, stream))
                     ba = (lib.wkv4_backward, (B, T, C, p(w), p(u), p(k), p(v), p(gy), p(gw), p(gu), p(gk), p(gv),
                                               p(bws), nbw, stream))
+
+                def both(fa=fa, ba=ba):
+                    st = fa[0](*fa[1])
+                    return st if st else ba[0](*ba[1])
+                self.calls.append((both, ()))
+        elif kind.startswith("wkv4_train_step_state"):
+            # One training step of a piece of a longer sequence: the forward from a carried
+            # state (writing the state after the piece), then the backward with the gradient
+            # of that final state (plain: wkv4_forward_ex / wkv4_backward_ex; checkpointed:
+            # wkv4_forward_ckpt_ex / wkv4_backward_ckpt_ex).
+            w, u = to(host["w"]), to(host["u"])
+            ck = kind.endswith("_ckpt")
+            nfw = int(lib.wkv4_forward_ckpt_workspace_size(B, T, C) if ck else lib.wkv4_forward_workspace_size(B, T, C))
+            nbw = int(lib.wkv4_backward_ckpt_workspace_size(B, T, C) if ck else
+                      lib.wkv4_backward_workspace_size(B, T, C))
+            nck = int(lib.wkv4_checkpoint_size(B, T, C)) if ck else 0
+            fws = torch.empty(max(nfw, 1), dtype=torch.uint8, device=dev)
+            bws = torch.empty(max(nbw, 1), dtype=torch.uint8, device=dev)
+            gw = torch.empty(C, dtype=torch.float32, device=dev)
+            gu = torch.empty(C, dtype=torch.float32, device=dev)
+            s_in, gs_out = to(host["s_in"]), to(host["gs_out"])
+            s_out = torch.empty_like(s_in)
+            gs_in = torch.empty_like(gs_out)
+            self.keep += [w, u, fws, bws, gw, gu, s_in, gs_out, s_out, gs_in]
+            p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+            for _ in range(rotations):
+                k, v, gy = to(host["k"]), to(host["v"]), to(host["gy"])
+                y, gk, gv = torch.empty_like(k), torch.empty_like(k), torch.empty_like(k)
+                cbuf = torch.empty(max(nck, 1), dtype=torch.uint8, device=dev)
+                self.keep += [k, v, gy, y, gk, gv, cbuf]
+                if ck:
+                    fa = (lib.wkv4_forward_ckpt_ex, (B, T, C, p(w), p(u), p(k), p(v), None, p(s_in), p(y), p(s_out),
+                                                     p(cbuf), nck, p(fws), nfw, stream))
+                    ba = (lib.wkv4_backward_ckpt_ex, (B, T, C, p(w), p(u), p(k), p(v), None, p(s_in), p(s_out), p(gy),
+                                                      p(gs_out), p(cbuf), nck, p(gw), p(gu), p(gk), p(gv), None,
+                                                      p(gs_in), p(bws), nbw, stream))
+                else:
+                    fa = (lib.wkv4_forward_ex, (B, T, C, p(w), p(u), p(k), p(v), None, p(s_in), p(y), p(s_out),
+                                                p(fws), nfw, stream))
+                    ba = (lib.wkv4_backward_ex, (B, T, C, p(w), p(u), p(k), p(v), None, p(s_in), p(s_out), p(gy),
+                                                 p(gs_out), p(gw), p(gu), p(gk), p(gv), None, p(gs_in), p(bws), nbw,
+                                                 stream))
 
                 def both(fa=fa, ba=ba):
                     st = fa[0](*fa[1])
@@ -401,6 +447,15 @@ def roofline(kind, elements, launch_s, traffic):
             "algorithmic_bytes": algo}
 
 
+def _state_step(host):
+    """The oracle's training step of a piece with a carried state."""
+    import oracle
+
+    _, s_out = oracle.wkv4_forward_ex(host["w"], host["u"], host["k"], host["v"], s_in=host["s_in"])
+    return oracle.wkv4_backward_ex(host["w"], host["u"], host["k"], host["v"], host["gy"], s_in=host["s_in"],
+                                   s_out=s_out.astype("float32"), gs_out=host["gs_out"])
+
+
 def cpu_baseline(kind, host, budget_s):
     """The fp64 oracle, as it stands, on the host cores: median seconds per call."""
     import oracle
@@ -419,6 +474,8 @@ def cpu_baseline(kind, host, budget_s):
           "wkv4_train_step_gated_ckpt": lambda: (
               oracle.wkv4_forward_ex(host["w"], host["u"], host["k"], host["v"], r=host["r"]),
               oracle.wkv4_backward_gated(host["w"], host["u"], host["k"], host["v"], host["r"], host["gy"])),
+          "wkv4_train_step_state": lambda: _state_step(host),
+          "wkv4_train_step_state_ckpt": lambda: _state_step(host),
           "scan_real": lambda: oracle.scan_real(host["a"], host["b"]),
           "scan_complex": lambda: oracle.scan_complex(host["lam"], host["u"]),
           "scan_real_backward": lambda: oracle.scan_real_backward(host["a"], host["x"], host["gx"]),
@@ -554,6 +611,12 @@ def make_host(wid, kind, shape=None):
         host = workloads.make_inputs(wid, shape=(B, T, C))
     if kind in ("wkv4_backward_gated", "wkv4_forward_gated") or kind.startswith("wkv4_train_step_gated"):
         host["r"] = host["v"]  # stand-in receptance ~ N(0,1) (timing only)
+    if kind.startswith("wkv4_train_step_state"):
+        # A carried state (a, b, p) and the gradient of the final state, seeded (timing only).
+        rng = np.random.default_rng(wl.seed + 17)
+        host["s_in"] = np.stack([rng.standard_normal((B, C)), rng.uniform(0.2, 3.0, (B, C)),
+                                 rng.uniform(-5.0, 20.0, (B, C))], axis=-1).astype(np.float32)
+        host["gs_out"] = rng.standard_normal((B, C, 2)).astype(np.float32)
     if kind.endswith("_backward") and kind.startswith("scan_") and kind not in VARIANT_BWD:
         host.update(workloads.make_scan_adjoint_inputs(wid, host))
     return host
@@ -580,9 +643,10 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
     if kind == "wkv4_forward_gated":
         label = "WKV-4 forward with the sigma(r) gate fp32 B=%d T=%d C=%d" % (B, T, C)
     if kind.startswith("wkv4_train_step"):
-        label = "WKV-4 training step (%sforward, then backward%s) fp32 B=%d T=%d C=%d" % (
+        label = "WKV-4 training step (%sforward, then backward%s%s) fp32 B=%d T=%d C=%d" % (
             "sigma(r)-gated " if "_gated" in kind else "",
-            " from the forward's kept sums" if kind.endswith("_ckpt") else "", B, T, C)
+            " from the forward's kept sums" if kind.endswith("_ckpt") else "",
+            ", a piece with a carried state" if "_state" in kind else "", B, T, C)
     if kind.startswith("token_shift"):
         label = "RWKV token shift%s, %d mixes, fp32 B=%d T=%d C=%d" % (
             " backward" if kind.endswith("_backward") else "", SHIFT_M, B, T, C)
@@ -608,8 +672,9 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
         desc = "full workload"
         if cpu_slice is not None:
             Ts = cpu_slice
-            sample = {k: (v[:, :Ts] if hasattr(v, "ndim") and v.ndim == 3 else
-                          (v[:, :, :Ts] if hasattr(v, "ndim") and v.ndim == 4 else v)) for k, v in host.items()}
+            per_step = lambda k, v: hasattr(v, "ndim") and k not in ("s_in", "gs_out")  # noqa: E731
+            sample = {k: (v[:, :Ts] if per_step(k, v) and v.ndim == 3 else
+                          (v[:, :, :Ts] if per_step(k, v) and v.ndim == 4 else v)) for k, v in host.items()}
             desc = "first %d of %d time steps, all batch rows and channels" % (Ts, T)
         if kind in ("scan_real_backward", "scan_complex_backward"):
             # The adjoint's forward input: the oracle's own forward scan of the sample.
@@ -720,7 +785,9 @@ def main():
                                             (5, "scan_complex_normalized_backward", 10, 16384),
                                             (3, "wkv4_train_step", 10, 256), (3, "wkv4_train_step_ckpt", 10, 256),
                                             (3, "wkv4_train_step_gated", 10, 256),
-                                            (3, "wkv4_train_step_gated_ckpt", 10, 256)):
+                                            (3, "wkv4_train_step_gated_ckpt", 10, 256),
+                                            (3, "wkv4_train_step_state", 10, 256),
+                                            (3, "wkv4_train_step_state_ckpt", 10, 256)):
             rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
             log("[bench] " + json.dumps(rows[-1]))
         if args.all_out:

@@ -269,8 +269,8 @@ int wkv4_backward_ex(int64_t B, int64_t T, int64_t C,
  *   r     (B,T,C) float32 receptance, or NULL: with r the output is the gated sigma(r) wkv
  *         (eq. (15)), as wkv4_forward_ex / wkv4_backward_ex with r, and the backward writes
  *   gr    (B,T,C) dL/dr; r and gr are given together to the backward (else INVALID_ARG)
- *   other arguments as for wkv4_forward / wkv4_backward.  No carried state: such calls stay
- *   with wkv4_forward_ex / wkv4_backward_ex.
+ *   other arguments as for wkv4_forward / wkv4_backward.  For a carried state see
+ *   wkv4_forward_ckpt_ex / wkv4_backward_ckpt_ex below.
  *
  * Workspaces: wkv4_forward_ckpt_workspace_size and wkv4_backward_ckpt_workspace_size (the
  * latter smaller than wkv4_backward's: no state pass).  Errors as for the other calls, and
@@ -291,6 +291,39 @@ int wkv4_backward_ckpt(int64_t B, int64_t T, int64_t C,
                        const float *r, const float *gy, const void *ckpt, size_t ckpt_bytes,
                        float *gw, float *gu, float *gk, float *gv, float *gr,
                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The checkpointed training step for a sequence processed in pieces (RWKV-LLM page, section
+ * "并行训练和序列解码": the recurrence carries a state from one piece to the next): as
+ * wkv4_forward_ckpt / wkv4_backward_ckpt, with the carried state of wkv4_forward_ex /
+ * wkv4_backward_ex.
+ *
+ *   wkv4_forward_ckpt_ex   starts from s_in (B,C,3) (a, b, p) or NULL (empty state), writes
+ *                          y, the kept sums (which then include the state) and, when s_out
+ *                          is not NULL, the state after the last token (B,C,3);
+ *   wkv4_backward_ckpt_ex  takes the same s_in, the forward's s_out (only its p is read, and
+ *                          only with gs_out), gs_out = dL/d(a', b') of s_out (B,C,2) or NULL,
+ *                          and writes gs_in = dL/d(a, b) of s_in (B,C,2) when not NULL; the
+ *                          gradients are those of wkv4_backward_ex (to rounding), from the
+ *                          ckpt its forward wrote for the same w, k, v and s_in.
+ *
+ * Calls chained through the state chain their gradients as wkv4_backward_ex's do (the gs_in
+ * of a later piece is the gs_out of the earlier one).  T = 0: the forward passes the state
+ * through (s_out = s_in, or empty) and writes no checkpoint; the backward writes gw = gu = 0
+ * and gs_in = gs_out e^{p_in - p_out}.  Sizes, workspaces and errors as for the calls above,
+ * plus: gs_out without s_out -> LINREC_ERR_INVALID_ARG; a state pointer not 4-byte aligned
+ * -> LINREC_ERR_UNSUPPORTED.
+ */
+int wkv4_forward_ckpt_ex(int64_t B, int64_t T, int64_t C,
+                         const float *w, const float *u, const float *k, const float *v,
+                         const float *r, const float *s_in, float *y, float *s_out,
+                         void *ckpt, size_t ckpt_bytes, void *workspace, size_t ws_bytes, void *stream);
+int wkv4_backward_ckpt_ex(int64_t B, int64_t T, int64_t C,
+                          const float *w, const float *u, const float *k, const float *v,
+                          const float *r, const float *s_in, const float *s_out, const float *gy,
+                          const float *gs_out, const void *ckpt, size_t ckpt_bytes,
+                          float *gw, float *gu, float *gk, float *gv, float *gr, float *gs_in,
+                          void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Real diagonal scan, "Were RNNs All We Needed?" page, minGRU section (v_t = a_t (.)

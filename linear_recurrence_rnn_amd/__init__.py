@@ -7,7 +7,7 @@ input generators) can be used without loading the GPU library.
 """
 
 __all__ = ["wkv4_forward", "wkv4_forward_noalloc", "wkv4_forward_ex", "wkv4_decode_step", "token_shift", "token_shift_backward", "wkv4_backward", "wkv4_backward_gated", "wkv4_backward_ex",
-           "wkv4_forward_ckpt", "wkv4_backward_ckpt", "wkv4_checkpoint_size", "scan_real", "scan_complex", "scan_real_backward",
+           "wkv4_forward_ckpt", "wkv4_backward_ckpt", "wkv4_forward_ckpt_ex", "wkv4_backward_ckpt_ex", "wkv4_checkpoint_size", "scan_real", "scan_complex", "scan_real_backward",
            "scan_complex_backward", "scan_mingru", "scan_minlstm", "scan_real_decay",
            "scan_complex_normalized", "scan_mingru_backward", "scan_minlstm_backward",
            "scan_real_decay_backward", "scan_complex_normalized_backward", "workspace_size", "LinrecError"]

@@ -80,6 +80,11 @@ def load(path: str | None = None):
         lib.wkv4_forward_ckpt.restype = ctypes.c_int
         lib.wkv4_forward_ckpt.argtypes = [_I64, _I64, _I64] + [_VP] * 7 + [_SZ, _VP, _SZ, _VP]
         lib.wkv4_backward_ckpt.restype = ctypes.c_int
+        lib.wkv4_forward_ckpt_ex.restype = ctypes.c_int
+        lib.wkv4_forward_ckpt_ex.argtypes = [_I64, _I64, _I64] + [_VP] * 9 + [_SZ, _VP, _SZ, _VP]
+        lib.wkv4_backward_ckpt_ex.restype = ctypes.c_int
+        lib.wkv4_backward_ckpt_ex.argtypes = ([_I64, _I64, _I64] + [_VP] * 9 + [_VP, _SZ] + [_VP] * 6 +
+                                              [_VP, _SZ, _VP])
         lib.wkv4_backward_ckpt.argtypes = [_I64, _I64, _I64] + [_VP] * 7 + [_SZ] + [_VP] * 5 + [_VP, _SZ, _VP]
         lib.wkv4_decode_step.restype = ctypes.c_int
         lib.wkv4_decode_step.argtypes = [_I64, _I64] + [_VP] * 7 + [_VP]
@@ -430,6 +435,64 @@ def wkv4_backward_ckpt(w, u, k, v, gy, ckpt, r=None, out=None, workspace=None):
                                   _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(gr), _ptr(ws), nws, _stream(dev)),
            "wkv4_backward_ckpt")
     return (gw, gu, gk, gv) if r is None else (gw, gu, gk, gv, gr)
+
+
+def wkv4_forward_ckpt_ex(w, u, k, v, r=None, state=None, want_state=True, workspace=None):
+    """(y, ckpt, state_out): wkv4_forward_ckpt starting from the carried state ``state``
+    (B,C,3) (a, b, p) or None (empty), with the state after the last token (B,C,3) when
+    ``want_state``."""
+    lib = load()
+    B, T, C = k.shape
+    dev = k.device
+    for name, t in (("k", k), ("v", v)):
+        _expect(t, name, torch.float32, (B, T, C), dev)
+    if r is not None:
+        _expect(r, "r", torch.float32, (B, T, C), dev)
+    if state is not None:
+        _expect(state, "state", torch.float32, (B, C, 3), dev)
+    _expect(w, "w", torch.float32, (C,), dev)
+    _expect(u, "u", torch.float32, (C,), dev)
+    nck = int(lib.wkv4_checkpoint_size(B, T, C))
+    y = torch.empty_like(k)
+    ckpt = torch.empty(max(nck, 1), dtype=torch.uint8, device=dev)
+    s_out = torch.empty((B, C, 3), dtype=torch.float32, device=dev) if want_state else None
+    ws, nws = _workspace(int(lib.wkv4_forward_ckpt_workspace_size(B, T, C)), dev, workspace)
+    _check(lib.wkv4_forward_ckpt_ex(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(state), _ptr(y),
+                                    _ptr(s_out), _ptr(ckpt), nck, _ptr(ws), nws, _stream(dev)),
+           "wkv4_forward_ckpt_ex")
+    return y, ckpt, s_out
+
+
+def wkv4_backward_ckpt_ex(w, u, k, v, gy, ckpt, r=None, s_in=None, s_out=None, gs_out=None, want_gs_in=True,
+                          workspace=None):
+    """(gw, gu, gk, gv, gr, gs_in) as wkv4_backward_ex, from the ckpt that
+    wkv4_forward_ckpt_ex wrote for the same w, u, k, v and s_in (gr None without r, gs_in
+    None unless ``want_gs_in``)."""
+    lib = load()
+    B, T, C = k.shape
+    dev = k.device
+    for name, t in (("k", k), ("v", v), ("gy", gy)):
+        _expect(t, name, torch.float32, (B, T, C), dev)
+    if r is not None:
+        _expect(r, "r", torch.float32, (B, T, C), dev)
+    for name, t, n in (("s_in", s_in, 3), ("s_out", s_out, 3), ("gs_out", gs_out, 2)):
+        if t is not None:
+            _expect(t, name, torch.float32, (B, C, n), dev)
+    if gs_out is not None and s_out is None:
+        raise ValueError("gs_out needs s_out (the forward's final state)")
+    _expect(w, "w", torch.float32, (C,), dev)
+    _expect(u, "u", torch.float32, (C,), dev)
+    nck = int(lib.wkv4_checkpoint_size(B, T, C))
+    gw, gu = torch.empty_like(w), torch.empty_like(u)
+    gk, gv = torch.empty_like(k), torch.empty_like(k)
+    gr = None if r is None else torch.empty_like(k)
+    gs_in = torch.empty((B, C, 2), dtype=torch.float32, device=dev) if want_gs_in else None
+    ws, nws = _workspace(int(lib.wkv4_backward_ckpt_workspace_size(B, T, C)), dev, workspace)
+    _check(lib.wkv4_backward_ckpt_ex(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(s_in), _ptr(s_out),
+                                     _ptr(gy), _ptr(gs_out), _ptr(ckpt), nck, _ptr(gw), _ptr(gu), _ptr(gk),
+                                     _ptr(gv), _ptr(gr), _ptr(gs_in), _ptr(ws), nws, _stream(dev)),
+           "wkv4_backward_ckpt_ex")
+    return gw, gu, gk, gv, gr, gs_in
 
 
 def scan_real(a, b, x0=None, out=None, workspace=None):

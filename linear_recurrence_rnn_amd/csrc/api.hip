@@ -711,19 +711,29 @@ int check_ckpt(const void* ckpt, size_t ckpt_bytes, size_t need) {
 }
 }  // namespace
 
-LINREC_API int wkv4_forward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                                 const float* k, const float* v, const float* r, float* y, void* ckpt,
-                                 size_t ckpt_bytes, void* workspace, size_t ws_bytes, void* stream) {
+LINREC_API int wkv4_forward_ckpt_ex(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                                    const float* k, const float* v, const float* r, const float* s_in, float* y,
+                                    float* s_out, void* ckpt, size_t ckpt_bytes, void* workspace, size_t ws_bytes,
+                                    void* stream) {
     int st = check_shape(B, T, C, 4);
     if (st) return st;
-    if (B == 0 || T == 0 || C == 0) return ok();
+    if (B == 0 || C == 0) return ok();
+    if ((s_in && !aligned(s_in, 4)) || (s_out && !aligned(s_out, 4)))
+        return fail(LINREC_ERR_UNSUPPORTED, "state pointer not 4-byte aligned");
+    if (T == 0) {
+        // No tokens: nothing to keep; the state passes through unchanged (empty without s_in).
+        if (!s_out) return ok();
+        const hipError_t e = s_in ? linrec::run_copy(s_out, s_in, 3 * B * C, (hipStream_t)stream)
+                                  : linrec::run_fill_zero(s_out, 3 * B * C, (hipStream_t)stream);
+        return hip_status(e, "wkv4_forward_ckpt_ex state copy");
+    }
     if (!w || !u || !k || !v || !y) return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
     const void* ptrs[] = {w, u, k, v, y, r};
     for (const void* p : ptrs)
         if (p && !aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
     if ((st = check_ckpt(ckpt, ckpt_bytes, linrec::wkv_ckpt_bytes(B, T, C)))) return st;
     if ((st = check_ws(workspace, ws_bytes, linrec::wkv_ckpt_forward_ws_bytes(B, T, C)))) return st;
-    const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0, r, nullptr, nullptr};
+    const linrec::WkvArgs A{w, u, k, v, y, env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0, r, s_in, s_out};
     // Coordination in wave 0 by default (measured faster); LINREC_COORD=2 gives it a wave of
     // its own.
     const bool sep = env_int("LINREC_COORD", 0) == 2;
@@ -732,18 +742,34 @@ LINREC_API int wkv4_forward_ckpt(int64_t B, int64_t T, int64_t C, const float* w
                       "wkv4_forward_ckpt launch");
 }
 
-LINREC_API int wkv4_backward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                                  const float* k, const float* v, const float* r, const float* gy,
-                                  const void* ckpt, size_t ckpt_bytes, float* gw, float* gu, float* gk,
-                                  float* gv, float* gr, void* workspace, size_t ws_bytes, void* stream) {
+LINREC_API int wkv4_forward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                                 const float* k, const float* v, const float* r, float* y, void* ckpt,
+                                 size_t ckpt_bytes, void* workspace, size_t ws_bytes, void* stream) {
+    return wkv4_forward_ckpt_ex(B, T, C, w, u, k, v, r, nullptr, y, nullptr, ckpt, ckpt_bytes, workspace, ws_bytes,
+                                stream);
+}
+
+LINREC_API int wkv4_backward_ckpt_ex(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                                     const float* k, const float* v, const float* r, const float* s_in,
+                                     const float* s_out, const float* gy, const float* gs_out, const void* ckpt,
+                                     size_t ckpt_bytes, float* gw, float* gu, float* gk, float* gv, float* gr,
+                                     float* gs_in, void* workspace, size_t ws_bytes, void* stream) {
     int st = check_shape(B, T, C, 4);
     if (st) return st;
     if (!r != !gr) return fail(LINREC_ERR_INVALID_ARG, "r and gr must be given together");
     if (C > 0 && (!gw || !gu)) return fail(LINREC_ERR_INVALID_ARG, "gw or gu is NULL");
+    if (gs_out && !s_out) return fail(LINREC_ERR_INVALID_ARG, "gs_out needs s_out (its exponents)");
+    const void* sptrs[] = {s_in, s_out, gs_out, gs_in};
+    for (const void* p : sptrs)
+        if (p && !aligned(p, 4)) return fail(LINREC_ERR_UNSUPPORTED, "state pointer not 4-byte aligned");
+    const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv, r, gr, s_in, s_out, gs_out, gs_in};
     if (B == 0 || T == 0 || C == 0) {
+        // As wkv4_backward_ex: zero sums, and without tokens the state's gradient passes through.
         if (C == 0) return ok();
         if (!aligned(gw, 4) || !aligned(gu, 4)) return fail(LINREC_ERR_UNSUPPORTED, "pointer not 4-byte aligned");
-        return hip_status(linrec::run_zero_wu(gw, gu, C, (hipStream_t)stream), "wkv4_backward_ckpt zero-fill");
+        hipError_t e = linrec::run_zero_wu(gw, gu, C, (hipStream_t)stream);
+        if (e == hipSuccess && gs_in && B > 0) e = linrec::run_state_grad_passthrough(A, B, C, (hipStream_t)stream);
+        return hip_status(e, "wkv4_backward_ckpt zero-fill");
     }
     if (!w || !u || !k || !v || !gy || !gk || !gv)
         return fail(LINREC_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -753,7 +779,6 @@ LINREC_API int wkv4_backward_ckpt(int64_t B, int64_t T, int64_t C, const float* 
     if ((st = check_ckpt(ckpt, ckpt_bytes, linrec::wkv_ckpt_bytes(B, T, C)))) return st;
     const linrec::BwdPlan p = linrec::wkv_backward_plan(1, B, T, C, 0, 0);  // the checkpoints' slabs
     if ((st = check_ws(workspace, ws_bytes, linrec::wkv_backward_ckpt_ws_bytes(B, T, C)))) return st;
-    const linrec::WkvBwdArgs A{w, u, k, v, gy, gw, gu, gk, gv, r, gr, nullptr, nullptr, nullptr, nullptr};
     linrec::BwdGeom g{};
     g.B = B;
     g.T = T;
@@ -766,6 +791,14 @@ LINREC_API int wkv4_backward_ckpt(int64_t B, int64_t T, int64_t C, const float* 
     g.exact_only = env_int("LINREC_WKV_EXACT", 0) > 0 ? 1 : 0;
     linrec::wkv_backward_layout_ckpt(p, B, C, workspace, ckpt, g);
     return hip_status(linrec::run_wkv_backward(A, g, p, (hipStream_t)stream), "wkv4_backward_ckpt launch");
+}
+
+LINREC_API int wkv4_backward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                                  const float* k, const float* v, const float* r, const float* gy,
+                                  const void* ckpt, size_t ckpt_bytes, float* gw, float* gu, float* gk,
+                                  float* gv, float* gr, void* workspace, size_t ws_bytes, void* stream) {
+    return wkv4_backward_ckpt_ex(B, T, C, w, u, k, v, r, nullptr, nullptr, gy, nullptr, ckpt, ckpt_bytes, gw, gu, gk,
+                                 gv, gr, nullptr, workspace, ws_bytes, stream);
 }
 
 LINREC_API int wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,

@@ -12,6 +12,7 @@
 // spike that may have flushed them, from k and v step by step) -- and writes them in the
 // record layout the gradient kernel reads.  The re-run itself is the plain
 // forward's (A and B rounded to float32 at the carry-in), gated by sigma(r) when r is given.
+// A carried state seeds the chain (the slab-0 carry) and the last slab writes the final state.
 #include "scan_kernel.hpp"
 #include "wkv_backward.hpp"
 #include "wkv_sums.hpp"
@@ -44,11 +45,15 @@ __device__ __forceinline__ Fwd fwd_combine_shifted(float om, const Fwd& s1, floa
             fma(fma(fn, s1.b, s1.bd), f1, bd * f2), P};
 }
 
-// GATED: the output is sigma(r) wkv (eq. (15)); the plain instance compiles none of it.
-template <bool GATED>
+// GATED: the output is sigma(r) wkv (eq. (15)).  STATE: the sequence starts from a carried
+// state s_in (the past sums (a, b, p) of every earlier token, as wkv4_forward_ex takes it),
+// whose own derivatives in w are zero (the state is an input: its gradient is dL/d(a, b)),
+// and the state after the last token is written to s_out.  The plain instance compiles none
+// of either.
+template <bool GATED, bool STATE>
 struct WkvCkptOpT {
     using Args = WkvCkptArgs;
-    using Base = typename std::conditional<GATED, WkvExtOp, WkvOp>::type;
+    using Base = typename std::conditional<GATED || STATE, WkvExtOp, WkvOp>::type;
     static constexpr bool kReverse = false;
     static constexpr bool kParts = false;
     using Part = NoPart;
@@ -69,12 +74,26 @@ struct WkvCkptOpT {
     template <int L>
     __device__ __forceinline__ static Chan chan(const Args& A, int64_t c) { return Base::template chan<L>(A, c); }
     __device__ __forceinline__ static Agg identity() { return fwd_identity(); }
-    // No carried state: the sequence starts from the empty sums, and the final state is
-    // not written.
-    __device__ __forceinline__ static Agg init(const Args&, const ScanGeom&, int64_t, int64_t) {
+    // The sums before the first token: empty, or the carried state in base-2 form (A' = B' = 0).
+    __device__ __forceinline__ static Agg init(const Args& A, const ScanGeom& g, int64_t b, int64_t c) {
+        if constexpr (STATE) {
+            if (A.s_in) {
+                const float* s = A.s_in + 3 * (b * g.C + c);
+                const Base2State x = state_from_natural(s[0], s[1], s[2]);
+                if (x.a != 0.f || x.b != 0.f) return {(double)x.a, (double)x.b, 0.0, 0.0, x.p};
+            }
+        }
         return fwd_identity();
     }
-    __device__ __forceinline__ static void finish(const Args&, const ScanGeom&, int64_t, int64_t, const Agg&) {}
+    // The state after the last token, as wkv4_forward_ex writes it.
+    __device__ __forceinline__ static void finish(const Args& A, const ScanGeom& g, int64_t b, int64_t c,
+                                                  const Agg& s) {
+        if constexpr (STATE) {
+            if (!A.s_out) return;
+            float* o = A.s_out + 3 * (b * g.C + c);
+            state_to_natural({(float)s.a, (float)s.b, s.p}, o[0], o[1], o[2]);
+        }
+    }
     __device__ __forceinline__ static Res res(const Args& A, const ScanGeom& g, int64_t b, int64_t row, int64_t col0) {
         Res R;
         R.base = Base::res(A, g, b, row, col0);
@@ -183,10 +202,19 @@ struct WkvCkptOpT {
 }  // namespace
 
 // The gated instance also holds r per step: at 6 waves per SIMD (80 VGPRs) it spills around
-// the kept sums; 5 (96 VGPRs) does not, and measured faster (gated step 984 -> 948 us).
+// the kept sums; 5 (96 VGPRs) does not, and measured faster (gated step 984 -> 948 us).  The
+// carried-state instances share the gated one's per-step inputs (r is loaded when given).
 namespace scan_kernel {
 template <>
-constexpr int scan_waves_per_eu<WkvCkptOpT<true>, 1, 16>() {
+constexpr int scan_waves_per_eu<WkvCkptOpT<true, false>, 1, 16>() {
+    return 5;
+}
+template <>
+constexpr int scan_waves_per_eu<WkvCkptOpT<false, true>, 1, 16>() {
+    return 5;
+}
+template <>
+constexpr int scan_waves_per_eu<WkvCkptOpT<true, true>, 1, 16>() {
     return 5;
 }
 }  // namespace scan_kernel
@@ -230,8 +258,11 @@ hipError_t run_wkv_forward_ckpt(const WkvArgs& A, int64_t B, int64_t T, int64_t 
         g.rec_agg = (char*)ws + align256((size_t)nwg * 8);
         g.rec_incl = (char*)g.rec_agg + rec;
     }
-    if (A.r) return scan_kernel::launch<WkvCkptOpT<true>, 1, kCkptNW, kCkptL>(X, g, sep, st);
-    return scan_kernel::launch<WkvCkptOpT<false>, 1, kCkptNW, kCkptL>(X, g, sep, st);
+    const bool state = A.s_in || A.s_out;
+    if (A.r && state) return scan_kernel::launch<WkvCkptOpT<true, true>, 1, kCkptNW, kCkptL>(X, g, sep, st);
+    if (A.r) return scan_kernel::launch<WkvCkptOpT<true, false>, 1, kCkptNW, kCkptL>(X, g, sep, st);
+    if (state) return scan_kernel::launch<WkvCkptOpT<false, true>, 1, kCkptNW, kCkptL>(X, g, sep, st);
+    return scan_kernel::launch<WkvCkptOpT<false, false>, 1, kCkptNW, kCkptL>(X, g, sep, st);
 }
 
 }  // namespace linrec
