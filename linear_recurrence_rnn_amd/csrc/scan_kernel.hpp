@@ -45,6 +45,18 @@ namespace scan_kernel {
 // per-channel state is larger) spill at that budget and keep the compiler's choice.
 // The gated WKV instance also holds r per step (80 VGPRs, 6 waves per SIMD): its 8-wave
 // workgroups still fit 3 to a CU, as the SGPRs allow no more anyway.
+// Operators whose lane offset is used for buffer accesses alone declare kUniformSteps.  For
+// them every lane of a wave runs the same step count, and a lane past the last channel gets
+// a buffer offset of 2^31, beyond any buffer's range (at most 2^31 - 1 bytes, and row
+// offsets stay below 2^31), so its loads return 0 and its stores are dropped by the
+// hardware.  The steps' loops then branch on a wave-uniform count instead of a per-lane one
+// (B8 T1024 C768 forward: 18.3 -> 17.6 us).
+template <class Op, class = void>
+struct uniform_steps : std::false_type {};
+template <class Op>
+struct uniform_steps<Op, std::void_t<decltype(Op::kUniformSteps)>> : std::bool_constant<Op::kUniformSteps> {};
+constexpr unsigned kOutOfRange = 0x80000000u;
+
 template <class Op, int VEC, int L>
 constexpr int scan_waves_per_eu() {
     if (std::is_same<Op, WkvExtOp>::value && VEC * L <= 16) return 6;
@@ -106,7 +118,9 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     for (int e = 0; e < VEC; ++e) ch[e] = active ? Op::template chan<L>(A, c0 + e) : Chan{};
 
     const unsigned rowb = (unsigned)(g.C * EF * 4);           // bytes per time step
-    const unsigned voff = (unsigned)(lane * VEC * EF * 4);    // this lane's bytes in the row
+    constexpr bool UN = uniform_steps<Op>::value;
+    // this lane's bytes in the row (out of range for an inactive lane of a uniform-step operator)
+    const unsigned voff = (UN && !active) ? kOutOfRange : (unsigned)(lane * VEC * EF * 4);
     const Chain<Agg> chn{g.flags + gi * g.nslab,
                          reinterpret_cast<uint32_t*>(g.rec_agg) + gi * g.nslab * (CW * kDwords<Agg>),
                          reinterpret_cast<uint32_t*>(g.rec_incl) + gi * g.nslab * (CW * kDwords<Agg>), g.tag, g.spin};
@@ -200,7 +214,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
 
     // ---- compute waves: chunk w of the slab, loaded into registers and reduced ----
     const int nu = chunk_len(w);  // steps of the chunk (wave-uniform)
-    const int n = active ? nu : 0;
+    const int n = (UN || active) ? nu : 0;
     int64_t row;
     Rows rows;
     run_rows<Op::kReverse>(g.T, t_slab + (int64_t)w * L, nu, rowb, row, rows);

@@ -55,6 +55,10 @@ struct WkvOpT {
     using Args = WkvArgs;
     static constexpr bool kReverse = false;
     static constexpr bool kParts = false;
+    // Uses its lane offset only for buffer accesses: the kernel may run every lane of a wave
+    // over the same step count and drop an inactive lane's accesses by an out-of-range offset
+    // (see scan_kernel.hpp).
+    static constexpr bool kUniformSteps = true;
     using Part = NoPart;
     struct Chan { float om, mu, lift, fast_lo; };  // lift = ceil(max(om, mu, 0))
     // kk becomes g_j after phase 1.  The gated instance also loads r with the chunk, so that
