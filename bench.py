@@ -67,6 +67,26 @@ BYTES_PER_ELEM = {"wkv4_forward": 12, "wkv4_backward": 20, "scan_real": 12, "sca
                   "wkv4_train_step_state_ckpt": 32}
 SHIFT_M = 3  # token-shift mixes timed: the r, k, v inputs of the time mix
 
+# The rows of --all after the headline, in order: (workload id, row, timed steps, time steps of
+# the oracle baseline's sample).
+ALL_ROWS = (
+    (3, "wkv4_forward", 20, 512), (3, "wkv4_backward", 20, 256),
+    (4, "scan_real", 20, 512), (5, "scan_complex", 10, 16384),
+    (4, "scan_real_backward", 20, 512),
+    (5, "scan_complex_backward", 10, 16384),
+    (4, "scan_mingru", 20, 512), (4, "scan_minlstm", 20, 512),
+    (4, "scan_real_decay", 20, 512), (5, "scan_complex_normalized", 10, 16384),
+    (2, "token_shift", 50, None), (2, "token_shift_backward", 50, None),
+    (3, "wkv4_forward_gated", 20, 512), (3, "wkv4_backward_gated", 20, 256),
+    (4, "scan_mingru_backward", 20, 512), (4, "scan_minlstm_backward", 20, 512),
+    (4, "scan_real_decay_backward", 20, 512),
+    (5, "scan_complex_normalized_backward", 10, 16384),
+    (3, "wkv4_train_step", 10, 256), (3, "wkv4_train_step_ckpt", 10, 256),
+    (3, "wkv4_train_step_gated", 10, 256),
+    (3, "wkv4_train_step_gated_ckpt", 10, 256),
+    (3, "wkv4_train_step_state", 10, 256),
+    (3, "wkv4_train_step_state_ckpt", 10, 256))
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -118,18 +138,19 @@ def kernel_source_digest(kind: str = "wkv4_forward") -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload: str, launches_per_step: int = 1):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches
-    the current kernel sources; None otherwise."""
-    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+def counter_traffic(kind: str, B: int, T: int, C: int):
+    """HBM bytes per step of row `kind` at (B, T, C) from the committed rocprofv3 counter
+    record (profiles/counters.json), if it was taken on the current kernel sources; None
+    otherwise."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
     try:
         with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            rec = json.load(f)["rows"].get("%s@%dx%dx%d" % (kind, B, T, C))
+    except (OSError, ValueError, KeyError, AttributeError):
         return None
-    if rec.get("source_digest") != kernel_source_digest(workload):
+    if not rec or rec.get("source_digest") != kernel_source_digest(kind):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_step")
 
 
 class Row:
@@ -662,7 +683,7 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
         "kind": kind, "workload": label, "B": B, "T": T, "C": C, "rotations": R, "steps": steps,
         "ms_per_step": round(per_step * 1e3, 5), "event_ms_per_step": round(per_launch * 1e3, 5),
         "elements_per_s": elements / per_step,
-        "roofline": roofline(kind, elements, per_launch, counter_traffic(kind)),
+        "roofline": roofline(kind, elements, per_launch, counter_traffic(kind, B, T, C)),
     }
     del row
     import torch
@@ -772,22 +793,7 @@ def main():
 
     if args.all:
         rows = [res]
-        for wid, kind, steps, cpu_slice in ((3, "wkv4_forward", 20, 512), (3, "wkv4_backward", 20, 256),
-                                            (4, "scan_real", 20, 512), (5, "scan_complex", 10, 16384),
-                                            (4, "scan_real_backward", 20, 512),
-                                            (5, "scan_complex_backward", 10, 16384),
-                                            (4, "scan_mingru", 20, 512), (4, "scan_minlstm", 20, 512),
-                                            (4, "scan_real_decay", 20, 512), (5, "scan_complex_normalized", 10, 16384),
-                                            (2, "token_shift", 50, None), (2, "token_shift_backward", 50, None),
-                                            (3, "wkv4_forward_gated", 20, 512), (3, "wkv4_backward_gated", 20, 256),
-                                            (4, "scan_mingru_backward", 20, 512), (4, "scan_minlstm_backward", 20, 512),
-                                            (4, "scan_real_decay_backward", 20, 512),
-                                            (5, "scan_complex_normalized_backward", 10, 16384),
-                                            (3, "wkv4_train_step", 10, 256), (3, "wkv4_train_step_ckpt", 10, 256),
-                                            (3, "wkv4_train_step_gated", 10, 256),
-                                            (3, "wkv4_train_step_gated_ckpt", 10, 256),
-                                            (3, "wkv4_train_step_state", 10, 256),
-                                            (3, "wkv4_train_step_state_ckpt", 10, 256)):
+        for wid, kind, steps, cpu_slice in ALL_ROWS:
             rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
             log("[bench] " + json.dumps(rows[-1]))
         if args.all_out:
