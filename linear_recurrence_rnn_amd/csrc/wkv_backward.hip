@@ -192,11 +192,14 @@ __device__ __forceinline__ Rev rev_chunk(float om, const float (&qs)[L][VEC], co
     s.r = ceilf(mx);
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-        const float wgt = fast_exp2(m[j] - s.r);  // 0 for the unused slots
-        const double f = wgt * cg[j][e];
-        s.x += f;
-        s.h = fma(f, (double)ys[j][e], s.h);
-        s.z += wgt;
+        // Slots past n are skipped, not weighted by 0: their values are not defined.
+        if (j < n) {
+            const float wgt = fast_exp2(m[j] - s.r);
+            const double f = wgt * cg[j][e];
+            s.x += f;
+            s.h = fma(f, (double)ys[j][e], s.h);
+            s.z += wgt;
+        }
     }
     return s;
 }
