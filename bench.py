@@ -94,6 +94,7 @@ def log(*a):
 
 # Sources each entry point's kernels are built from (the launch plan lives in api.hip).
 _SCAN_SOURCES = ("api.hip", "chunk_scan.hip", "chunk_scan.hpp", "scan_kernel.hpp", "scan_ops.hpp", "lookback.hpp",
+                 "part_reduce.hpp",
                  "device_common.hpp", "wkv_math.hpp")
 KERNEL_SOURCES = {
     "wkv4_forward": _SCAN_SOURCES,

@@ -107,9 +107,10 @@ linrec::ScanPlan scan_plan(int kind, int vec, int64_t B, int64_t T, int64_t C) {
     p.ws_bytes = 0;
     if (p.nslab > 1)
         p.ws_bytes = align256((size_t)nwg * 8) + 2 * align256((size_t)(nwg * cw) * linrec::agg_bytes(kind));
-    if (linrec::has_parts(kind))  // per-slab glam sums and their first-stage sums
-        p.ws_bytes += align256((size_t)(nwg * cw) * 16) +
-                      align256((size_t)(B * ceil_div(p.nslab, linrec::kPartBlock) * C) * 16);
+    if (linrec::has_parts(kind)) {  // per-slab glam sums and their first-stage sums
+        const int64_t nk = ceil_div(p.nslab, linrec::kPartBlock);
+        p.ws_bytes += align256((size_t)(nwg * cw) * 16) + align256((size_t)(B * nk * C) * 16);
+    }
     return p;
 }
 
@@ -193,6 +194,7 @@ linrec::ScanGeom geom_of(int kind, const linrec::ScanPlan& p, int64_t B, int64_t
     char* after = (char*)g.rec_incl + align256((size_t)(nwg * cw) * linrec::agg_bytes(kind));
     if (p.nslab <= 1) g.flags = nullptr, g.rec_agg = g.rec_incl = nullptr, after = (char*)ws;
     g.part = g.part2 = nullptr;
+    g.nk = ceil_div(g.nslab, linrec::kPartBlock);
     if (linrec::has_parts(kind)) {
         g.part = reinterpret_cast<double*>(after);
         g.part2 = reinterpret_cast<double*>(after + align256((size_t)(nwg * cw) * 16));

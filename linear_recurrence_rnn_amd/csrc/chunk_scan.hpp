@@ -141,7 +141,8 @@ struct ScanGeom {
     void* rec_agg;      // (B*ngrp*nslab, 64*vec) slab aggregates
     void* rec_incl;     // (B*ngrp*nslab, 64*vec) inclusive prefixes
     double* part;       // (B*ngrp*nslab, 64*vec, 2) per-slab sums of operators that have them
-    double* part2;      // second-stage sums of those (see run_scan_complex_backward)
+    double* part2;      // (B*nk, C, 2) their first-stage sums (see run_scan_complex_backward)
+    int64_t nk;         // ceil(nslab / kPartBlock): first-stage blocks per row
 };
 
 struct ScanPlan {

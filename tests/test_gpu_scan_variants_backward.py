@@ -219,3 +219,39 @@ def test_lambda_sums_are_deterministic(L):
     a = host(L.scan_complex_normalized_backward(dev(c["lam"]), dev(c["u"]), xc, dev(c["gx"]))[0])
     b = host(L.scan_complex_normalized_backward(dev(c["lam"]), dev(c["u"]), xc, dev(c["gx"]))[0])
     assert np.array_equal(a, b)
+
+
+def test_lambda_sums_independent_of_workspace_bytes(L):
+    """dL/dlambda has the same bits whatever bytes the workspace held before the call (stale
+    look-back flags and per-slab sums are never read as this call's), and stays within the
+    oracle's tolerance.  Shapes span several first-stage blocks of 64 slabs per row, several
+    rows, and a channel group with idle lanes."""
+    import torch
+    announce("glambda with workspaces filled with 0x00, 0xff, 0x5a")
+
+    def fills(run, nbytes):
+        outs = []
+        for fill in (0x00, 0xFF, 0x5A):
+            ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+            outs.append(run(ws))
+        for o in outs[1:]:
+            assert np.array_equal(outs[0], o)
+        return outs[0]
+
+    for shape in [(3, 40000, 96), (8, 3000, 64)]:
+        d = workloads.make_gated(*shape, seed=86, with_grad=True)
+        x = oracle.scan_real_decay(d["lam"], d["h"], d["x0"])
+        args = (dev(d["lam"]), dev(f32(x)), dev(d["gx"]), dev(d["x0"]))
+        nb = L.workspace_size("scan_real_backward", *shape)
+        a = fills(lambda ws: host(L.scan_real_decay_backward(*args, workspace=ws)[0]), nb)
+        ref = oracle.scan_real_decay_backward(d["lam"], f32(x), d["gx"], d["x0"])[0]
+        assert rel_err(a, ref, None) <= TOL, shape
+    for shape in [(2, 70000, 72), (1, 300, 64)]:
+        c = workloads.make_lru(*shape, 87, 0.9, 0.999, math.pi / 10, with_x0=True)
+        c.update(workloads.make_scan_adjoint_inputs(5, c, seed=88))
+        xc = oracle.scan_complex_normalized(c["lam"], c["u"], c["x0"]).astype(np.complex64)
+        args = (dev(c["lam"]), dev(c["u"]), dev(xc), dev(c["gx"]), dev(c["x0"]))
+        nb = L.workspace_size("scan_complex_backward", *shape)
+        a = fills(lambda ws: host(L.scan_complex_normalized_backward(*args, workspace=ws)[0]), nb)
+        ref = oracle.scan_complex_normalized_backward(c["lam"], c["u"], xc, c["gx"], c["x0"])[0]
+        assert rel_err(a, ref, None) <= TOL, shape
