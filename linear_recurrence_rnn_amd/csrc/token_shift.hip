@@ -15,10 +15,12 @@
 // Layout of work: a wave owns VEC channels per lane (64 * VEC contiguous channels, so every
 // wave-wide access is one contiguous row segment) over TS consecutive time steps, and holds
 // the rows it needs in registers: the TS rows of its span and the row before it (read
-// again by the neighbouring span, 1/TS extra), plus, in the backward, the row after it.
+// again by the neighbouring span, 1/TS extra), plus, in the backward, the row after it
+// (there handed over between the waves of a block, so 1/(8 TS) extra).
 // Both passes are HBM-bound streams (forward 4 + 4M bytes per element, backward 8 + 4M).
-// gmu is summed in float64: per wave over its span, over the 4 waves of a block in order,
-// then over blocks in a fixed order by a second kernel, so it does not depend on scheduling.
+// gmu is summed in float64: per wave over its span, over the 8 waves of a backward block in
+// order, then over blocks in a fixed order by a second kernel, so it does not depend on
+// scheduling.
 #include "device_common.hpp"
 #include "token_shift.hpp"
 
@@ -79,30 +81,38 @@ __global__ __launch_bounds__(64 * kShiftWaves) void token_shift_kernel(TokenShif
     }
 }
 
-// Backward: block (b, tcb, grp); wave w takes steps [(tcb*4 + w)*TS, +TS).  Every row the
-// wave needs (x and all M gradients) is loaded before any is used, so the whole span is in
-// flight at once.
+// Backward: block (b, tcb, grp) of kShiftBwdWaves waves; wave w takes steps
+// [(tcb*NWV + w)*TS, +TS).  Every row the wave needs (x and all M gradients) is loaded before
+// any is used, so the whole span is in flight.  The rows a span needs beyond its own -- x
+// at t0-1 and the gradients at t0+TS -- are the neighbouring waves' last and first rows,
+// handed over through LDS; only the block's outer waves read them from memory.
+constexpr int kShiftBwdWaves = 8;
+
 template <int VEC, int TS, int M>
-__global__ __launch_bounds__(64 * kShiftWaves) void token_shift_bwd_kernel(TokenShiftBwdArgs A, int64_t B, int64_t T,
-                                                                           int64_t C) {
+__global__ __launch_bounds__(64 * kShiftBwdWaves) void token_shift_bwd_kernel(TokenShiftBwdArgs A, int64_t B,
+                                                                              int64_t T, int64_t C) {
     constexpr int CW = 64 * VEC;
-    __shared__ double sh[kShiftWaves][M][CW];
+    constexpr int NWV = kShiftBwdWaves;
+    __shared__ double sh[NWV][M][CW];    // the waves' dL/dmu sums
+    __shared__ float sh_xl[NWV][CW];     // each span's last x row
+    __shared__ float sh_gf[NWV][M][CW];  // each span's first gradient rows
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t ngrp = (C + CW - 1) / CW, ntcb = (T + kShiftWaves * TS - 1) / (kShiftWaves * TS);
+    const int64_t ngrp = (C + CW - 1) / CW, ntcb = (T + NWV * TS - 1) / (NWV * TS);
     const int64_t blk = blockIdx.x;
     const int64_t grp = blk % ngrp, tcb = (blk / ngrp) % ntcb, b = blk / (ngrp * ntcb);
     const int64_t c = grp * CW + (int64_t)lane * VEC;
     const bool active = c < C;
-    const int64_t t0 = (tcb * kShiftWaves + wv) * TS;
+    const int64_t t0 = (tcb * NWV + wv) * TS;
     const int n = t0 >= T ? 0 : (int)((T - t0) < TS ? (T - t0) : TS);
     const float* xr = A.x + (b * T + t0) * C + c;
 
-    // x rows t0-1 .. t0+n-1 (row t0-1 is x_prev, or 0, at the start of the sequence) and
-    // g rows t0 .. t0+n (row t0+n belongs to the next span; 0 past the end).
+    // x rows t0-1 .. t0+n-1 and g rows t0 .. t0+n (0 past the end of the sequence).  Row
+    // t0-1 is x_prev, or 0, at the start of the sequence.
     FV<VEC> xs[TS + 1];
-    xs[0] = load_or_zero<VEC>(t0 > 0 ? xr - C : (A.x_prev ? A.x_prev + b * C + c : nullptr),
-                              active && n > 0 && (t0 > 0 || A.x_prev));
+    if (wv == 0)
+        xs[0] = load_or_zero<VEC>(t0 > 0 ? xr - C : (A.x_prev ? A.x_prev + b * C + c : nullptr),
+                                  active && n > 0 && (t0 > 0 || A.x_prev));
 #pragma unroll
     for (int j = 0; j < TS; ++j) xs[j + 1] = load_or_zero<VEC>(xr + (int64_t)j * C, active && j < n);
     FV<VEC> gs[M][TS + 1];
@@ -110,8 +120,24 @@ __global__ __launch_bounds__(64 * kShiftWaves) void token_shift_bwd_kernel(Token
     for (int m = 0; m < M; ++m) {
         const float* gr = A.g + (int64_t)m * B * T * C + (b * T + t0) * C + c;
 #pragma unroll
-        for (int j = 0; j <= TS; ++j)
-            gs[m][j] = load_or_zero<VEC>(gr + (int64_t)j * C, active && j <= n && t0 + j < T);
+        for (int j = 0; j < TS; ++j) gs[m][j] = load_or_zero<VEC>(gr + (int64_t)j * C, active && j < n);
+        if (wv == NWV - 1) gs[m][TS] = load_or_zero<VEC>(gr + (int64_t)TS * C, active && n == TS && t0 + TS < T);
+    }
+    // Hand the neighbours their rows: a span's last x row (row t0+TS-1 when the span is
+    // full; the next span is empty otherwise) and its first gradient rows (0 when n = 0).
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        sh_xl[wv][lane * VEC + e] = xs[TS].v[e];
+#pragma unroll
+        for (int m = 0; m < M; ++m) sh_gf[wv][m][lane * VEC + e] = gs[m][0].v[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        if (wv > 0) xs[0].v[e] = sh_xl[wv - 1][lane * VEC + e];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            if (wv < NWV - 1) gs[m][TS].v[e] = n == TS ? sh_gf[wv + 1][m][lane * VEC + e] : 0.f;
     }
     float mu[M][VEC];
 #pragma unroll
@@ -164,7 +190,7 @@ __global__ __launch_bounds__(64 * kShiftWaves) void token_shift_bwd_kernel(Token
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 double s = 0.0;
-                for (int w = 0; w < kShiftWaves; ++w) s += sh[w][m][lane * VEC + e];
+                for (int w = 0; w < NWV; ++w) s += sh[w][m][lane * VEC + e];
                 A.part[((b * ntcb + tcb) * M + m) * C + c + e] = s;
             }
         }
@@ -228,14 +254,14 @@ constexpr int shift_bwd_ts(int vec) { return vec == 2 ? 8 : kShiftTS; }
 
 size_t token_shift_backward_ws_bytes(int64_t B, int64_t T, int64_t C, int M, int vec) {
     const int ts = shift_bwd_ts(vec);
-    const int64_t ntcb = (T + kShiftWaves * ts - 1) / (kShiftWaves * ts);
+    const int64_t ntcb = (T + kShiftBwdWaves * ts - 1) / (kShiftBwdWaves * ts);
     return (size_t)(B * ntcb * M * C) * sizeof(double);
 }
 
 namespace {
 template <int VEC, int TS>
 void launch_bwd(const TokenShiftBwdArgs& A, dim3 grid, int64_t B, int64_t T, int64_t C, int M, hipStream_t st) {
-    const dim3 block(64 * kShiftWaves);
+    const dim3 block(64 * kShiftBwdWaves);
     if (M == 1) hipLaunchKernelGGL((token_shift_bwd_kernel<VEC, TS, 1>), grid, block, 0, st, A, B, T, C);
     else if (M == 2) hipLaunchKernelGGL((token_shift_bwd_kernel<VEC, TS, 2>), grid, block, 0, st, A, B, T, C);
     else if (M == 3) hipLaunchKernelGGL((token_shift_bwd_kernel<VEC, TS, 3>), grid, block, 0, st, A, B, T, C);
@@ -247,7 +273,7 @@ hipError_t run_token_shift_backward(const TokenShiftBwdArgs& A, int64_t B, int64
                                     hipStream_t st) {
     const int64_t cw = 64 * vec;
     const int ts = shift_bwd_ts(vec);
-    const int64_t ntcb = (T + kShiftWaves * ts - 1) / (kShiftWaves * ts);
+    const int64_t ntcb = (T + kShiftBwdWaves * ts - 1) / (kShiftBwdWaves * ts);
     const int64_t nblk = B * ntcb;
     const dim3 grid((unsigned)(nblk * ((C + cw - 1) / cw)));
     if (vec == 2) launch_bwd<2, shift_bwd_ts(2)>(A, grid, B, T, C, M, st);
