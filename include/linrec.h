@@ -33,9 +33,11 @@
  *    for the same (B, T, C).  A size of 0 needs no workspace (NULL is then allowed).
  *  - Each call stamps its workspace's look-back flags with a tag drawn on the host at call
  *    time, so stale flags of earlier calls read as unpublished and the workspace needs no
- *    clearing.  A call recorded into a HIP graph keeps its tag on every replay: replaying
- *    it is not supported (issue the call again instead).  Two calls in flight at the same
- *    time must not share a workspace.
+ *    clearing.  A call made while `stream` is capturing into a HIP graph keeps its tag on
+ *    every replay, so it also records a fill kernel that clears its flags before its own
+ *    kernels: each replay of the graph computes afresh (replays see the workspace and
+ *    buffers captured with the call).  Two calls in flight at the same time must not share
+ *    a workspace.
  *  - Return value: LINREC_OK or an error status.  Argument checks run before any HIP call:
  *      B, T or C negative, or B*T*C*element size overflowing int64
  *                                                         -> LINREC_ERR_INVALID_ARG

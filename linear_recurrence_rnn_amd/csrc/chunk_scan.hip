@@ -69,6 +69,15 @@ hipError_t run_copy(float* dst, const float* src, int64_t n, hipStream_t st) {
     return hipGetLastError();
 }
 
+hipError_t clear_flags_if_capturing(uint64_t* flags, int64_t n, hipStream_t st) {
+    if (!flags || n <= 0) return hipSuccess;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess) return e;
+    if (cs != hipStreamCaptureStatusActive) return hipSuccess;
+    return run_fill_zero(reinterpret_cast<float*>(flags), 2 * n, st);
+}
+
 hipError_t run_fill_zero(float* p, int64_t n, hipStream_t st) {
     if (n <= 0) return hipSuccess;
     const int64_t blocks = (n + 255) / 256;

@@ -179,6 +179,10 @@ hipError_t run_scan_complex_backward(const CplxBwdArgs& A, float* glam, const Sc
 constexpr int kPartBlock = 64;  // slabs summed per first-stage block of the glam reduction
 // Writes n zero floats (a fill kernel: the library records no memset).
 hipError_t run_fill_zero(float* p, int64_t n, hipStream_t st);
+// A call recorded into a HIP graph keeps its host-drawn tag on every replay, so the flags a
+// replay publishes would meet the previous replay's.  While `st` is capturing, this records
+// a fill kernel that zeroes the n flags first ("not published"); otherwise it does nothing.
+hipError_t clear_flags_if_capturing(uint64_t* flags, int64_t n, hipStream_t st);
 // dst[i] = src[i] for n floats (a copy kernel, for the same reason).
 hipError_t run_copy(float* dst, const float* src, int64_t n, hipStream_t st);
 size_t agg_bytes(int kind);

@@ -280,6 +280,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
 template <class Op, int VEC, int NW, int L>
 hipError_t launch(const typename Op::Args& A, const ScanGeom& g, bool sep, hipStream_t st) {
     const int64_t nb = g.B * g.ngrp * g.nslab;
+    if (const hipError_t e = clear_flags_if_capturing(g.flags, nb, st)) return e;
     if constexpr (VEC == 1) {
         if (sep) {
             hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, true>), dim3((unsigned)nb), dim3(64 * (NW + 1)),

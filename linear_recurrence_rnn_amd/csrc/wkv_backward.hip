@@ -34,6 +34,7 @@
 // the batch in ascending row order: the results do not depend on scheduling.
 #include <atomic>
 
+#include "chunk_scan.hpp"
 #include "device_common.hpp"
 #include "lookback.hpp"
 #include "wkv_backward.hpp"
@@ -994,6 +995,12 @@ hipError_t resident_blocks(const void* kernel, int threads, std::atomic<int> (&c
 template <int VEC, int NW, int L>
 hipError_t launch(const WkvBwdArgs& A, const BwdGeom& g, hipStream_t st) {
     const int64_t G = g.B * g.ngrp;
+    if (g.nslab > 1) {
+        hipError_t e = clear_flags_if_capturing(g.flags_r, G * g.nslab, st);
+        if (e == hipSuccess && !g.from_ckpt)
+            e = clear_flags_if_capturing(g.flags_c, G * ((g.nslab - 1 + kStateFine - 1) / kStateFine), st);
+        if (e != hipSuccess) return e;
+    }
     if (g.nslab > 1 && !g.from_ckpt) {
         // Persistent grid: no more workgroups than are resident together.
         const auto kern = wkv_bwd_state_kernel<NW, L>;
