@@ -189,8 +189,14 @@ struct WkvCkptOpT {
                     }
                 }
             }
-            Fwd x[1] = {st};
-            store_record<1>(R.rec, R.m, (int)(voff >> 2), x);
+            // This lane's entry of the kept sums.  A lane past the last channel runs the
+            // chunk too (its buffer offset out of range: loads 0, stores dropped) but keeps
+            // nothing: its offset names no entry.
+            const unsigned slot = voff >> 2;
+            if (slot < 64) {
+                Fwd x[1] = {st};
+                store_record<1>(R.rec, R.m, (int)slot, x);
+            }
         }
         typename Base::Agg c[VEC];
 #pragma unroll

@@ -227,3 +227,35 @@ def test_ckpt_step_gated_workload3(L):
     d = workloads.make_inputs(3)
     r = np.random.default_rng(50).standard_normal(d["k"].shape).astype(np.float32)
     check_gated_step(L, d, r)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_ckpt_forward_writes_only_its_buffer(L, gated):
+    """Lanes past the last channel (C = 70: the second group uses 6 of its 64 lanes) run
+    their chunks with out-of-range buffer offsets, which drop their loads and stores; the
+    kept sums are stored for real lanes only.  A canary of 2 GiB + 1 MiB right after the
+    checkpoint buffer (where an offset-derived lane index of 2^29 would land) keeps its
+    bytes, and the step stays within the oracle's tolerance."""
+    import torch
+    announce("wkv4 checkpointing forward leaves a 2 GiB canary intact, gated=%s" % gated)
+    B, T, C = 2, 1001, 70
+    d = workloads.make_inputs(3, seed=51, shape=(B, T, C))
+    r = (np.random.default_rng(52).standard_normal((B, T, C)) * 2).astype(np.float32) if gated else None
+    nck = int(L.wkv4_checkpoint_size(B, T, C))
+    big = torch.full((nck + (2 << 30) + (1 << 20),), 0x5A, dtype=torch.uint8, device="cuda")
+    ck = big[:nck]
+    w, u, k, v = dev(d["w"]), dev(d["u"]), dev(d["k"]), dev(d["v"])
+    rd = dev(r) if gated else None
+    y = torch.empty_like(k)
+    L.wkv4_forward_ckpt(w, u, k, v, r=rd, out=(y, ck))
+    torch.cuda.synchronize()
+    assert not bool((big[nck:] != 0x5A).any())
+    ref_y = oracle.wkv4_forward_ex(d["w"], d["u"], d["k"], d["v"], r=r)[0] if gated else \
+        oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])
+    assert rel_err(host(y), ref_y) <= TOL
+    grads = L.wkv4_backward_ckpt(w, u, k, v, dev(d["gy"]), ck, r=rd)
+    ref_g = oracle.wkv4_backward_ex(d["w"], d["u"], d["k"], d["v"], d["gy"], r=r, want_gs_in=False)
+    for name, a, b in zip(("gw", "gu", "gk", "gv", "gr"), [host(t) for t in grads], ref_g):
+        assert rel_err(a, b, None if name in ("gw", "gu") else 1) <= TOL, name
+    del big
+    torch.cuda.empty_cache()
