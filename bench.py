@@ -780,14 +780,15 @@ def main():
         # forward, backward and checkpointed training step at B=8 T=4096 C=2560, the real
         # scan and fused minGRU at B=64 T=4096 C=256 (the minGRU page's batch 64 x seq 4096)
         # and the LRU complex scan at B=1 T=262144 C=1024.
+        # 10 warm-up launches each: the first launches on freshly allocated buffers run slower.
         extras = []
         h3 = make_host(3, "wkv4_backward")
         for kind in ("wkv4_forward", "wkv4_backward", "wkv4_train_step_ckpt"):
-            extras.append(summary(measure(lib, 3, kind, 20, 3, 0, host=h3)))
+            extras.append(summary(measure(lib, 3, kind, 20, 10, 0, host=h3)))
             log("[bench] " + json.dumps(extras[-1]))
         del h3
         for wid, kind, steps in ((4, "scan_real", 20), (4, "scan_mingru", 20), (5, "scan_complex", 10)):
-            extras.append(summary(measure(lib, wid, kind, steps, 3, 0)))
+            extras.append(summary(measure(lib, wid, kind, steps, 10, 0)))
             log("[bench] " + json.dumps(extras[-1]))
         line["workloads"] = extras
     print(json.dumps(line), flush=True)
@@ -795,7 +796,7 @@ def main():
     if args.all:
         rows = [res]
         for wid, kind, steps, cpu_slice in ALL_ROWS:
-            rows.append(measure(lib, wid, kind, steps, 3, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
+            rows.append(measure(lib, wid, kind, steps, 10, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
             log("[bench] " + json.dumps(rows[-1]))
         if args.all_out:
             os.makedirs(os.path.dirname(os.path.abspath(args.all_out)), exist_ok=True)
