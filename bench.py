@@ -438,11 +438,25 @@ class Row:
         if st != 0:
             raise RuntimeError("%s returned status %d" % (self.kind, st))
 
-    def run(self, steps, warmup):
+    def run(self, steps, warmup, min_warm_s=0.0):
+        """Times `steps` launches after `warmup` untimed ones; with ``min_warm_s``, the warm-up
+        goes on (in batches of `warmup`) until that much wall time has passed, so that the GPU
+        has left its idle clocks (a backward at B8 T4096 C2560 runs ~10% slower for its first
+        ~50 launches after an idle second).  Returns (wall seconds, event seconds)."""
         import torch
 
-        for i in range(warmup):
-            self.launch(i)
+        t_w = time.perf_counter()
+        i = 0
+        while True:
+            for _ in range(warmup):
+                self.launch(i)
+                i += 1
+            if warmup <= 0 or min_warm_s <= 0.0:
+                break
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_w >= min_warm_s:
+                break
+        warmup = i
         stream = torch.cuda.current_stream()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
@@ -644,7 +658,7 @@ def make_host(wid, kind, shape=None):
     return host
 
 
-def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=None, host=None):
+def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=None, host=None, min_warm_s=0.0):
     from linear_recurrence_rnn_amd import workloads
 
     wl = workloads.WORKLOADS[wid]
@@ -677,7 +691,7 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
     log("[bench] %s %s: B=%d T=%d C=%d, %d buffer set(s) of %.1f MB" % (
         kind, label, B, T, C, R, footprint / 1e6))
     row = Row(lib, kind, B, T, C, host, R)
-    wall, ev_s = row.run(steps, warmup)
+    wall, ev_s = row.run(steps, warmup, min_warm_s)
     per_step = wall / steps
     per_launch = ev_s / steps
     out = {
@@ -716,7 +730,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle CPU baseline (0 skips it)")
     ap.add_argument("--no-copy-probe", action="store_true")
@@ -780,15 +794,15 @@ def main():
         # forward, backward and checkpointed training step at B=8 T=4096 C=2560, the real
         # scan and fused minGRU at B=64 T=4096 C=256 (the minGRU page's batch 64 x seq 4096)
         # and the LRU complex scan at B=1 T=262144 C=1024.
-        # 10 warm-up launches each: the first launches on freshly allocated buffers run slower.
+        # At least 10 warm-up launches and 0.1 s each (the GPU ramps its clocks after idling).
         extras = []
         h3 = make_host(3, "wkv4_backward")
         for kind in ("wkv4_forward", "wkv4_backward", "wkv4_train_step_ckpt"):
-            extras.append(summary(measure(lib, 3, kind, 20, 10, 0, host=h3)))
+            extras.append(summary(measure(lib, 3, kind, 20, 10, 0, host=h3, min_warm_s=0.1)))
             log("[bench] " + json.dumps(extras[-1]))
         del h3
         for wid, kind, steps in ((4, "scan_real", 20), (4, "scan_mingru", 20), (5, "scan_complex", 10)):
-            extras.append(summary(measure(lib, wid, kind, steps, 10, 0)))
+            extras.append(summary(measure(lib, wid, kind, steps, 10, 0, min_warm_s=0.1)))
             log("[bench] " + json.dumps(extras[-1]))
         line["workloads"] = extras
     print(json.dumps(line), flush=True)
@@ -796,7 +810,8 @@ def main():
     if args.all:
         rows = [res]
         for wid, kind, steps, cpu_slice in ALL_ROWS:
-            rows.append(measure(lib, wid, kind, steps, 10, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice))
+            rows.append(measure(lib, wid, kind, steps, 10, min(args.cpu_seconds, 3.0), cpu_slice=cpu_slice,
+                                min_warm_s=0.1))
             log("[bench] " + json.dumps(rows[-1]))
         if args.all_out:
             os.makedirs(os.path.dirname(os.path.abspath(args.all_out)), exist_ok=True)
