@@ -289,9 +289,12 @@ __device__ __forceinline__ void write_state_grad(const WkvBwdArgs& A, const BwdG
 template <int VEC, bool STATE>
 __device__ __forceinline__ void fwd_carry_in(const WkvBwdArgs& A, const BwdGeom& g, int64_t gi, int64_t b,
                                              int64_t c0, int64_t s, int lane, bool active, Fwd (&x)[VEC]) {
-    constexpr int64_t per = 64 * VEC * kDwords<Fwd>;  // dwords per slab record
+    constexpr int64_t per = 64 * VEC * kDwords<FwdRec>;  // dwords per slab record
     if (s > 0 && active) {
-        load_record<VEC>(reinterpret_cast<const uint32_t*>(g.incl_f) + gi * g.nslab * per, s - 1, lane, x);
+        FwdRec r[VEC];
+        load_record<VEC>(reinterpret_cast<const uint32_t*>(g.incl_f) + gi * g.nslab * per, s - 1, lane, r);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[e] = fwd_from_rec(r[e]);
     } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[e] = (STATE && active) ? fwd_state_in(A, g, b, c0 + e) : fwd_identity();
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(64 * (kStateFine + 1)) __attribute__((amdgpu_waves_
 void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
     constexpr int SLAB = NW * L;
     constexpr int F = kStateFine;
-    constexpr int kRec = 64 * kDwords<Fwd>;  // dwords per slab record
+    constexpr int kRec = 64 * kDwords<Fwd>;  // dwords per coarse-chain record
     __shared__ Fwd shf[2][F][64];
 
     const int tid = threadIdx.x;
@@ -495,10 +498,11 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
         };
         look_back<1, 2>(chn, it.q, lane, carry, fold, recompute, first);
         // The sums at the end of every fine slab of the item (read by the gradient kernel).
-        uint32_t* fine = reinterpret_cast<uint32_t*>(g.incl_f) + it.gi * g.nslab * kRec;
+        uint32_t* fine = reinterpret_cast<uint32_t*>(g.incl_f) + it.gi * g.nslab * (64 * kDwords<FwdRec>);
         for (int x = 0; x < nvalid; ++x) {
             carry[0] = fwd_combine(om[0], carry[0], shf[ib][x][lane], SLAB);
-            store_record<1>(fine, f0 + x, lane, carry);
+            const FwdRec r[1] = {fwd_to_rec(carry[0])};
+            store_record<1>(fine, f0 + x, lane, r);
         }
         if (has_succ) publish<1>(chn, it.q, lane, carry, true);
     }
@@ -1066,7 +1070,7 @@ BwdPlan wkv_backward_plan(int vec, int64_t B, int64_t T, int64_t C, int nw_overr
         const int64_t ncoarse = B * ((C + cw - 1) / cw) * ((p.nslab - 1 + kStateFine - 1) / kStateFine);
         bytes += align256((size_t)ncoarse * 8);                            // coarse flags
         bytes += 2 * align256((size_t)(ncoarse * cw) * sizeof(Fwd));       // coarse records
-        bytes += align256((size_t)(nrec * cw) * sizeof(Fwd));              // sums at fine slab ends
+        bytes += align256((size_t)(nrec * cw) * sizeof(FwdRec));           // sums at fine slab ends
         bytes += align256((size_t)nrec * 8);                               // reverse flags
         bytes += 2 * align256((size_t)(nrec * cw) * sizeof(RevRec));       // reverse records
     }
@@ -1085,7 +1089,7 @@ void wkv_backward_layout(const BwdPlan& p, int64_t B, int64_t C, void* ws, BwdGe
     const int64_t nrec = B * ((C + cw - 1) / cw) * p.nslab;
     const int64_t ncoarse = B * ((C + cw - 1) / cw) * ((p.nslab - 1 + kStateFine - 1) / kStateFine);
     const size_t fl = align256((size_t)nrec * 8);
-    const size_t fr = align256((size_t)(nrec * cw) * sizeof(Fwd));
+    const size_t fr = align256((size_t)(nrec * cw) * sizeof(FwdRec));
     const size_t rr = align256((size_t)(nrec * cw) * sizeof(RevRec));
     const size_t cr = align256((size_t)(ncoarse * cw) * sizeof(Fwd));
     g.flags_c = reinterpret_cast<uint64_t*>(at), at += align256((size_t)ncoarse * 8);

@@ -26,7 +26,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kCkptSlab = 56;  // steps between kept sums: the gradient kernel's slab (7 x 8)
 
 struct WkvCkptArgs : WkvArgs {
-    uint32_t* ckpt;  // (B*ngrp, nck, 10 dwords, 64 lanes) kept sums
+    uint32_t* ckpt;  // (B*ngrp, nck, 5 dwords, 64 lanes) kept sums (FwdRec)
     int64_t nck;     // records per channel group: ceil(T / 56)
 };
 
@@ -100,7 +100,7 @@ struct WkvCkptOpT {
         const int64_t mb = row > 0 ? ((row + kCkptSlab - 1) / kCkptSlab) * kCkptSlab : kCkptSlab;
         R.js = (mb < g.T) ? (int)(mb - row) : -1;
         R.m = mb / kCkptSlab - 1;
-        R.rec = A.ckpt + (b * g.ngrp + col0 / 64) * A.nck * (64 * kDwords<Fwd>);
+        R.rec = A.ckpt + (b * g.ngrp + col0 / 64) * A.nck * (64 * kDwords<FwdRec>);
         return R;
     }
     template <int VEC>
@@ -194,7 +194,7 @@ struct WkvCkptOpT {
             // nothing: its offset names no entry.
             const unsigned slot = voff >> 2;
             if (slot < 64) {
-                Fwd x[1] = {st};
+                const FwdRec x[1] = {fwd_to_rec(st)};
                 store_record<1>(R.rec, R.m, (int)slot, x);
             }
         }
@@ -230,7 +230,7 @@ constexpr int kCkptNW = 8, kCkptL = 16;
 
 size_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C) {
     const int64_t nck = (T + kCkptSlab - 1) / kCkptSlab;
-    return (size_t)(B * ((C + 63) / 64) * nck * 64) * sizeof(Fwd);
+    return (size_t)(B * ((C + 63) / 64) * nck * 64) * sizeof(FwdRec);
 }
 
 size_t wkv_ckpt_forward_ws_bytes(int64_t B, int64_t T, int64_t C) {

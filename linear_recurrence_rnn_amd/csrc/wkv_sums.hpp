@@ -9,7 +9,10 @@
 //
 // The gradient kernel starts each slab from these sums at the slab's start.  They are found
 // either by the backward's own state kernel or, in a training step, by the forward pass that
-// keeps them (the checkpointing forward), and both write them in the same record layout.
+// keeps them (the checkpointing forward), and both write them in the same record layout: as
+// float32 mantissas with the exponent (FwdRec), 20 bytes instead of 36.  The gradient kernel
+// scales the slab's starting sums by an exact power of two into float32 for its chunk frame
+// anyway, so its fast path sees the same values; its exact path starts from these.
 #pragma once
 
 #include "device_common.hpp"
@@ -21,6 +24,14 @@ namespace linrec {
 struct Fwd { double a, b, ad, bd; float p; };
 
 __device__ __forceinline__ Fwd fwd_identity() { return {0.0, 0.0, 0.0, 0.0, kEmpty}; }
+
+// The sums kept at a slab boundary (see above).
+struct FwdRec { float a, b, ad, bd, p; };
+
+__device__ __forceinline__ FwdRec fwd_to_rec(const Fwd& s) {
+    return {(float)s.a, (float)s.b, (float)s.ad, (float)s.bd, s.p};
+}
+__device__ __forceinline__ Fwd fwd_from_rec(const FwdRec& r) { return {r.a, r.b, r.ad, r.bd, r.p}; }
 
 // State s1, then a span s2 of n2 steps:
 //   A = eps^n2 A1 + A2,   A' = eps^n2 (A'1 + n2 A1) + A'2   (B, B' likewise).

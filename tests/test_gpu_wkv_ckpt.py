@@ -138,10 +138,10 @@ def test_ckpt_step_is_deterministic_and_buffers_reusable(L):
     y1b, g1b, c1b = ckpt_step(L, d1)
 
     def sums(c):
-        # records of 10 dwords per lane (four float64 sums, the exponent, one padding dword)
-        # per slab and channel group of 64; the last slab's record is never written
-        r = c.view(np.uint32).reshape(2 * 2, 17, 10, 64)
-        return r[:, :16, :9, :]
+        # records of 5 dwords per lane (four float32 sums and the exponent) per slab and
+        # channel group of 64; the last slab's record is never written
+        r = c.view(np.uint32).reshape(2 * 2, 17, 5, 64)
+        return r[:, :16, :, :]
 
     assert np.array_equal(y1, y1b) and np.array_equal(sums(c1), sums(c1b))
     for a, b in zip(g1, g1b):
