@@ -48,20 +48,21 @@ namespace {
 __device__ __forceinline__ float gate_sigmoid(float r) { return __builtin_amdgcn_rcpf(1.f + fast_exp2(-r * kLog2e)); }
 
 // Reverse sums: G-like = x 2^r, H-like = h 2^r; z 2^r is the sum of the (positive) weights,
-// which x and h can cancel below, and sets the exponent.
-struct Rev { double x, h, z; float r; };
+// which x and h can cancel below, and sets the exponent.  z only picks exponents, so float32
+// is enough for it (a record is 24 bytes instead of 32).
+struct Rev { double x, h; float z, r; };
 // Reverse look-back record: the reverse sums of a run of slabs and their dL/dw, dL/du sums.
 struct RevRec { Rev st; double sw, su; };
 
-__device__ __forceinline__ Rev rev_identity() { return {0.0, 0.0, 0.0, kEmpty}; }
+__device__ __forceinline__ Rev rev_identity() { return {0.0, 0.0, 0.f, kEmpty}; }
 
 // Reverse sums: s1 is the state at the end of an earlier span s2 of n2 steps; the result is
 // the state at the start of s2:  X = s2 + eps^n2 s1.
 __device__ __forceinline__ Rev rev_combine(float om, const Rev& s1, const Rev& s2, int64_t n2) {
     float r, f1, f2;
-    merge_scales(s1.r, (float)s1.z, s2.r, (float)s2.z, mul_split((float)n2, om), r, f1, f2);
+    merge_scales(s1.r, s1.z, s2.r, s2.z, mul_split((float)n2, om), r, f1, f2);
     const double g1 = f1, g2 = f2;
-    return {fma(s1.x, g1, s2.x * g2), fma(s1.h, g1, s2.h * g2), fma(s1.z, g1, s2.z * g2), r};
+    return {fma(s1.x, g1, s2.x * g2), fma(s1.h, g1, s2.h * g2), fmaf(s1.z, f1, s2.z * f2), r};
 }
 
 // (A, B, A', B') of a chunk of n steps from the empty state: with m_j = kk_j - (n-1-j) om,
@@ -213,13 +214,14 @@ __device__ __forceinline__ void rev_step(float om, float mu, Rev& s, float kj, f
     const float dgv = c * fast_exp2((kj - q) + mu);  // g_t beta_t / D_t
     gv = (float)fma(s.x, (double)sc, (double)dgv);
     gk = fmaf(dgv, vmy, sc * (float)fma((double)vj, s.x, -s.h));
-    const float r2 = ceilf(fmaxf(mag(s.r, (float)s.z) - om, -q));
-    const double f1 = fast_exp2((s.r - r2) - om);
+    const float r2 = ceilf(fmaxf(mag(s.r, s.z) - om, -q));
+    const float f1f = fast_exp2((s.r - r2) - om);
+    const double f1 = f1f;
     const float w2 = fast_exp2(-q - r2);
     const double f2 = w2 * c;
     s.x = fma(s.x, f1, f2);
     s.h = fma(s.h, f1, f2 * y);
-    s.z = fma(s.z, f1, (double)w2);
+    s.z = fmaf(s.z, f1f, w2);
     s.r = r2;
 }
 
@@ -264,7 +266,7 @@ __device__ __forceinline__ Rev rev_state_out(const WkvBwdArgs& A, const BwdGeom&
     const float P = ceilf(np * kLog2e);
     const float rem = fmaf(-P, kLn2Lo, fmaf(-P, kLn2Hi, np));
     const double sc = (double)fast_exp2(rem * kLog2e);
-    return {ga * sc, -(double)gb * sc, (fabs((double)ga) + fabs((double)gb)) * sc, P};
+    return {ga * sc, -(double)gb * sc, (float)((fabs((double)ga) + fabs((double)gb)) * sc), P};
 }
 
 // dL/dw's share of the state after the last token: -(dL/dA_T A'_T + dL/dB_T B'_T), with the
@@ -543,7 +545,7 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const StepOut o = fwd_step(om[e], mu[e], fs[e], kt.v[e] * kLog2e, vt.v[e], gt.v[e], x[e].sw, x[e].su);
-            const Rev one{(double)o.c, (double)o.c * (double)o.y, 1.0, -o.q};
+            const Rev one{(double)o.c, (double)o.c * (double)o.y, 1.f, -o.q};
             x[e].st = rev_combine(om[e], one, x[e].st, t);
         }
     }
