@@ -581,9 +581,9 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
 // work better than the compiler's own choice (~90 VGPRs, two workgroups).
 template <int L, bool GATE, bool STATE>
 constexpr int grad_waves_per_eu() {
-    // The gate's r_j take 8 more registers, the state's terms a few: 5 waves (96 VGPRs), 4
-    // with both (no spills).
-    return L <= 8 ? ((GATE && STATE) ? 4 : (GATE || STATE) ? 5 : 6) : 1;
+    // The gate's r_j take 8 more registers: 5 waves (96 VGPRs, two workgroups per CU), with
+    // or without the state.  The state's terms fit the plain kernel's budget (no spills).
+    return L <= 8 ? (GATE ? 5 : 6) : 1;
 }
 
 // GATE: the output is sigma(r) wkv (eq. (15)); dL/dwkv = gy sigma(r) drives every sum, and
@@ -665,6 +665,16 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         // this wave itself (the waves' folds run side by side, none waits for another).
         Fwd cin = sh_cin[lane];
         for (int x = 0; x < w; ++x) cin = fwd_combine(om[0], cin, shf[x][lane], chunk_len<L>(x, slab_n));
+        if constexpr (STATE) {
+            // The last slab: dL/dw's share of the final state takes the sums at the slab's
+            // end, which the last wave extends its own carry-in to (the same fold as the
+            // other waves').  The coordinator adds it to the slab's record after B3.
+            if (q == 0 && w == NW - 1) {
+                sh_mine[lane].sw =
+                    active ? sw_state_out(A, g, b, c0, fwd_combine(om[0], cin, shf[w][lane], chunk_len<L>(w, slab_n)))
+                           : 0.0;
+            }
+        }
 
         const float lift = ceilf(fmaxf(fmaxf(om[0], mu[0]), 0.f));
         ChunkFrame fr = chunk_frame(om[0], mu[0], lift, cin, p_chunk, m0, n, gmax, n > 0 && !g.exact_only);
@@ -846,20 +856,6 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         for (int e = 0; e < VEC; ++e) sh_cin[lane * VEC + e] = cin[e];
     }
     __syncthreads();  // B1
-    if constexpr (STATE) {
-        // The last slab: dL/dw's share of the final state, from the sums at the slab's end,
-        // parked in LDS until the record.
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            double v = 0.0;
-            if (q == 0 && active) {
-                Fwd c = sh_cin[lane * VEC + e];
-                for (int x = 0; x < NW; ++x) c = fwd_combine(om[e], c, shf[x][lane * VEC + e], chunk_len<L>(x, slab_n));
-                v = sw_state_out(A, g, b, c0 + e, c);
-            }
-            sh_mine[lane * VEC + e].sw = v;
-        }
-    }
     const Chain<RevRec> chn{g.flags_r + gi * g.nslab,
                             reinterpret_cast<uint32_t*>(g.agg_r) + gi * g.nslab * (CW * kDwords<RevRec>),
                             reinterpret_cast<uint32_t*>(g.incl_r) + gi * g.nslab * (CW * kDwords<RevRec>), g.tag_r,
@@ -912,13 +908,13 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         double sw = 0.0, su = 0.0;
         // The last slab's record also holds the final state's gradient, so that every chain
         // starts from the empty carry.
-        if (STATE && q == 0 && active) a = rev_state_out(A, g, b, c0 + e);
+        if (STATE && q == 0 && active) a = sh_rend[lane * VEC + e];  // set by slab_end (q = 0 is early)
         for (int x = NW - 1; x >= 0; --x) a = rev_combine(om[e], a, shr[x][lane * VEC + e], chunk_len<L>(x, slab_n));
         for (int x = 0; x < NW; ++x) {
             sw += shwu[x][lane * VEC + e][0];
             su += shwu[x][lane * VEC + e][1];
         }
-        if constexpr (STATE) sw += sh_mine[lane * VEC + e].sw;
+        if (STATE && q == 0) sw += sh_mine[lane * VEC + e].sw;  // the final state's share (last wave)
         mine[e] = {a, sw, su};
         sh_mine[lane * VEC + e] = mine[e];  // kept in LDS across the look-back (registers)
     }
