@@ -581,9 +581,10 @@ __device__ __forceinline__ void rev_record_from_inputs(const WkvBwdArgs& A, cons
 // work better than the compiler's own choice (~90 VGPRs, two workgroups).
 template <int L, bool GATE, bool STATE>
 constexpr int grad_waves_per_eu() {
-    // The gate's r_j take 8 more registers: 5 waves (96 VGPRs, two workgroups per CU), with
-    // or without the state.  The state's terms fit the plain kernel's budget (no spills).
-    return L <= 8 ? (GATE ? 5 : 6) : 1;
+    // Every instance fits: the gate's r_j live only until the fast path has written dL/dr
+    // (the exact path reads r again), and the state's terms are formed where few chunk
+    // values are live.
+    return L <= 8 ? 6 : 1;
 }
 
 // GATE: the output is sigma(r) wkv (eq. (15)); dL/dwkv = gy sigma(r) drives every sum, and
@@ -635,10 +636,10 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
         float sa[L], vv[L], sc[L], sy[L], sd[L];
         float rr[GATE ? L : 1];  // r_j
         const rsrc_t rgr = make_rsrc(GATE ? A.gr + base : A.gk + base, GATE ? nbytes : 0);
+        const rsrc_t rrs = make_rsrc(GATE ? A.r + base : A.k + base, GATE ? nbytes : 0);
         float gmax = 0.f;
         {
             const rsrc_t rv = make_rsrc(A.v + base, nbytes);
-            const rsrc_t rrs = make_rsrc(GATE ? A.r + base : A.k + base, GATE ? nbytes : 0);
 #pragma unroll
             for (int j = 0; j < L; ++j) {
                 float kt = 0.f, vt = 0.f, gt = 0.f;
@@ -730,19 +731,21 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
             }
         }
         if (!fr.fast && n > 0) {
-            // Exact per-step path (wkv_math.hpp exponents); k and dL/dy are read again.
+            // Exact per-step path (wkv_math.hpp exponents); k, dL/dy and r are read again, so
+            // that no register holds r past the fast path.
             Fwd st = cin;
 #pragma unroll
             for (int j = 0; j < L; ++j) {
                 if (j < n) {
                     const float kj = ldb<1>(rk, voff, j * rowb).v[0] * kLog2e;
                     float gj = ldb<1>(rg, voff, j * rowb).v[0];
-                    if constexpr (GATE) gj *= gate_sigmoid(rr[j]);
+                    const float rj = GATE ? ldb<1>(rrs, voff, j * rowb).v[0] : 0.f;
+                    if constexpr (GATE) gj *= gate_sigmoid(rj);
                     const StepOut o = fwd_step(om[0], mu[0], st, kj, vv[j], gj, sw, su);
                     if constexpr (GATE) {
                         // Overwrites the fast path's value when that path was abandoned.
                         FV<1> og;
-                        og.v[0] = gj * o.y * gate_sigmoid(-rr[j]);
+                        og.v[0] = gj * o.y * gate_sigmoid(-rj);
                         stb<1>(rgr, voff, j * rowb, og);
                     }
                     sa[j] = o.q;
