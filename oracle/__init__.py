@@ -67,6 +67,8 @@ def _bind(path: str):
     lib.oracle_wkv4_backward_gated.restype = None
     lib.oracle_wkv4_backward_ex.argtypes = [_I64, _I64, _I64] + [_F32P] * 9 + [_F64P] * 6
     lib.oracle_wkv4_backward_ex.restype = None
+    lib.oracle_wkv4_backward_cond.argtypes = [_I64, _I64, _I64] + [_F32P] * 9 + [_F64P] * 8
+    lib.oracle_wkv4_backward_cond.restype = None
     lib.oracle_scan_mingru.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_scan_minlstm.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F32P, _F64P]
     lib.oracle_scan_real_decay.argtypes = [_I64, _I64, _I64, _F32P, _F32P, _F32P, _F64P]
@@ -453,3 +455,27 @@ def wkv4_backward_ex(w, u, k, v, gy, r=None, s_in=None, s_out=None, gs_out=None,
                                              opt(so, _p32), _p32(gy), opt(go, _p32), _p64(gw), _p64(gu), _p64(gk),
                                              _p64(gv), opt(gr, _p64), opt(gsi, _p64))
     return gw, gu, gk, gv, gr, gsi
+
+
+def wkv4_backward_cond(w, u, k, v, gy, r=None, s_in=None, s_out=None, gs_out=None, lib=None):
+    """wkv4_backward_ex's outputs followed by (cw, cu): per channel, the sums over b and t of
+    the magnitudes of the products in each term of dL/dw and dL/du (their conditioning; see
+    oracle_wkv4_backward_cond).  gs_in is returned when s_in or gs_out is given."""
+    k = _f32(k)
+    B, T, C = k.shape
+    v, gy = _f32(v, (B, T, C)), _f32(gy, (B, T, C))
+    w, u = _f32(w, (C,)), _f32(u, (C,))
+    ra = None if r is None else _f32(r, (B, T, C))
+    si = None if s_in is None else _f32(s_in, (B, C, 3))
+    so = None if s_out is None else _f32(s_out, (B, C, 3))
+    go = None if gs_out is None else _f32(gs_out, (B, C, 2))
+    gw, gu, cw, cu = np.empty(C), np.empty(C), np.empty(C), np.empty(C)
+    gk, gv = np.empty((B, T, C)), np.empty((B, T, C))
+    gr = None if ra is None else np.empty((B, T, C))
+    gsi = np.empty((B, C, 2)) if (si is not None or go is not None) else None
+    opt = lambda a, f: None if a is None else f(a)  # noqa: E731
+    (lib or _load()).oracle_wkv4_backward_cond(B, T, C, _p32(w), _p32(u), _p32(k), _p32(v), opt(ra, _p32),
+                                               opt(si, _p32), opt(so, _p32), _p32(gy), opt(go, _p32), _p64(gw),
+                                               _p64(gu), _p64(gk), _p64(gv), opt(gr, _p64), opt(gsi, _p64),
+                                               _p64(cw), _p64(cu))
+    return gw, gu, gk, gv, gr, gsi, cw, cu

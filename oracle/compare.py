@@ -11,6 +11,11 @@ oracle output over the time axis of the same (batch, channel) sequence:
 For per-channel vectors (the w and u gradients) the floor is the RMS over channels.
 Complex values use the modulus.  ``quantiles`` reports the plain element-wise relative
 error distribution alongside, for transparency.
+
+The w and u gradients are also held channel by channel (``chan_ratio``): each channel's
+error against tol times its own value, floored by kappa times the sum of the magnitudes of
+the products its terms are made of (its conditioning, ``wkv4_backward_cond``), which bounds
+what float32 evaluation of those terms can resolve.
 """
 
 from __future__ import annotations
@@ -42,6 +47,36 @@ def rel_err(out, ref, time_axis: int | None = 1) -> float:
     if not np.all(np.isfinite(e)):
         return float("inf")
     return float(np.max(e))
+
+
+# kappa of chan_ratio: a term of dL/dw or dL/du evaluated in float32 passes through about a
+# dozen roundings (the weights' exponentials and their float32 arguments, the reciprocal of
+# the denominator, the products, the in-chunk float32 partial sums), each of at most 2^-24
+# relative to the magnitudes of the products involved.
+KAPPA_F32_TERMS = 2.0 ** -20
+
+
+def chan_ratio(out, ref, cond, tol: float, kappa: float = KAPPA_F32_TERMS) -> float:
+    """max_c |out_c - ref_c| / max(tol |ref_c|, kappa cond_c): at most 1 when every channel
+    is within tol of its own value or within kappa of its conditioning sum cond_c."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    cond = np.asarray(cond, np.float64)
+    if ref.size == 0:
+        return 0.0
+    bound = np.maximum(np.maximum(tol * np.abs(ref), kappa * cond), 1e-300)
+    e = np.abs(out - ref) / bound
+    return float(np.max(e)) if np.all(np.isfinite(e)) else float("inf")
+
+
+def plain_rel(out, ref) -> float:
+    """max |out - ref| / |ref| (no floor), reported next to the floored metrics."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        e = np.abs(out - ref) / np.abs(ref)
+    e = e[np.isfinite(e)]
+    return float(np.max(e)) if e.size else 0.0
 
 
 def quantiles(out, ref) -> dict:

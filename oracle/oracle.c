@@ -168,10 +168,13 @@ static void wkv4_backward_impl(int64_t B, int64_t T, int64_t C,
                                const float *w, const float *u,
                                const float *k, const float *v, const float *r, const float *gy,
                                double *gw, double *gu, double *gk, double *gv, double *gr,
-                               const float *s_in, const float *s_out, const float *gs_out, double *gs_in)
+                               const float *s_in, const float *s_out, const float *gs_out, double *gs_in,
+                               double *cw, double *cu)
 {
     double *gw_bc = (double *)calloc((size_t)(B * C), sizeof(double));
     double *gu_bc = (double *)calloc((size_t)(B * C), sizeof(double));
+    double *cw_bc = (double *)calloc((size_t)(B * C), sizeof(double));
+    double *cu_bc = (double *)calloc((size_t)(B * C), sizeof(double));
 #pragma omp parallel
     {
         double *D = (double *)malloc((size_t)T * sizeof(double));
@@ -198,6 +201,8 @@ static void wkv4_backward_impl(int64_t B, int64_t T, int64_t C,
             double A = s_in ? (double)s_in[3 * bc] * exp(p0 - K) : 0.0;
             double Bs = s_in ? (double)s_in[3 * bc + 1] * exp(p0 - K) : 0.0;
             double Ad = 0.0, Bd = 0.0, sgw = 0.0, sgu = 0.0;
+            /* Magnitude sums (cw, cu): A and A' with |v| in place of v. */
+            double Aabs = s_in ? fabs((double)s_in[3 * bc]) * exp(p0 - K) : 0.0, Adabs = 0.0, cgw = 0.0, cgu = 0.0;
             for (int64_t t = 0; t < T; ++t) {
                 const int64_t o = base + t * C;
                 const double kt = (double)k[o], vt = (double)v[o];
@@ -214,6 +219,10 @@ static void wkv4_backward_impl(int64_t B, int64_t T, int64_t C,
                 }
                 sgu += g * beta * (vt - yt) / Dt;
                 sgw -= g * (Ad - yt * Bd) / Dt;
+                cgu += fabs(g) * beta * (fabs(vt) + fabs(yt)) / Dt;
+                cgw += fabs(g) * (Adabs + fabs(yt) * Bd) / Dt;
+                Adabs = eps * (Adabs + Aabs);
+                Aabs = eps * Aabs + alpha * fabs(vt);
                 Ad = eps * (Ad + A);
                 Bd = eps * (Bd + Bs);
                 A = eps * A + alpha * vt;
@@ -224,8 +233,11 @@ static void wkv4_backward_impl(int64_t B, int64_t T, int64_t C,
             const double gA = gs_out ? (double)gs_out[2 * bc] * so : 0.0;   /* dL/dA_T e^K */
             const double gB = gs_out ? (double)gs_out[2 * bc + 1] * so : 0.0;
             sgw -= gA * Ad + gB * Bd;
+            cgw += fabs(gA) * Adabs + fabs(gB) * Bd;
             gw_bc[bc] = sgw;
             gu_bc[bc] = sgu;
+            cw_bc[bc] = cgw;
+            cu_bc[bc] = cgu;
             double G = gA, H = -gB; /* G_{T-1}, H_{T-1} */
             for (int64_t s = T - 1; s >= 0; --s) {
                 const int64_t o = base + s * C;
@@ -255,9 +267,20 @@ static void wkv4_backward_impl(int64_t B, int64_t T, int64_t C,
         }
         gw[c] = sw;
         gu[c] = su;
+        if (cw) {
+            double a = 0.0, b2 = 0.0;
+            for (int64_t b = 0; b < B; ++b) {
+                a += cw_bc[b * C + c];
+                b2 += cu_bc[b * C + c];
+            }
+            cw[c] = a;
+            cu[c] = b2;
+        }
     }
     free(gw_bc);
     free(gu_bc);
+    free(cw_bc);
+    free(cu_bc);
 }
 
 void oracle_wkv4_backward(int64_t B, int64_t T, int64_t C,
@@ -265,7 +288,7 @@ void oracle_wkv4_backward(int64_t B, int64_t T, int64_t C,
                           const float *k, const float *v, const float *gy,
                           double *gw, double *gu, double *gk, double *gv)
 {
-    wkv4_backward_impl(B, T, C, w, u, k, v, NULL, gy, gw, gu, gk, gv, NULL, NULL, NULL, NULL, NULL);
+    wkv4_backward_impl(B, T, C, w, u, k, v, NULL, gy, gw, gu, gk, gv, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
 }
 
 /*
@@ -278,7 +301,7 @@ void oracle_wkv4_backward_gated(int64_t B, int64_t T, int64_t C,
                                 const float *r, const float *gy,
                                 double *gw, double *gu, double *gk, double *gv, double *gr)
 {
-    wkv4_backward_impl(B, T, C, w, u, k, v, r, gy, gw, gu, gk, gv, gr, NULL, NULL, NULL, NULL);
+    wkv4_backward_impl(B, T, C, w, u, k, v, r, gy, gw, gu, gk, gv, gr, NULL, NULL, NULL, NULL, NULL, NULL);
 }
 
 /*
@@ -291,7 +314,24 @@ void oracle_wkv4_backward_ex(int64_t B, int64_t T, int64_t C, const float *w, co
                              const float *gy, const float *gs_out, double *gw, double *gu, double *gk, double *gv,
                              double *gr, double *gs_in)
 {
-    wkv4_backward_impl(B, T, C, w, u, k, v, r, gy, gw, gu, gk, gv, gr, s_in, s_out, gs_out, gs_in);
+    wkv4_backward_impl(B, T, C, w, u, k, v, r, gy, gw, gu, gk, gv, gr, s_in, s_out, gs_out, gs_in, NULL, NULL);
+}
+
+/*
+ * As oracle_wkv4_backward_ex, also returning per channel the sums over b and t of the
+ * magnitudes of the products that make up each term of dL/dw and dL/du (test
+ * infrastructure: the conditioning of those sums, for their per-channel tolerance):
+ *   cu[c] = sum_{b,t} |g_t| beta_t (|v_t| + |y_t|) / D_t
+ *   cw[c] = sum_{b,t} |g_t| (|A'|_t + |y_t| B'_t) / D_t  + |dL/dA_T| |A'|_T + |dL/dB_T| B'_T
+ * with |A'| the sum A' taken over |v_i|.  An evaluation that rounds every product and
+ * partial sum to float32 is off by a few float32 ulps of these, whatever the sums cancel to.
+ */
+void oracle_wkv4_backward_cond(int64_t B, int64_t T, int64_t C, const float *w, const float *u, const float *k,
+                               const float *v, const float *r, const float *s_in, const float *s_out,
+                               const float *gy, const float *gs_out, double *gw, double *gu, double *gk, double *gv,
+                               double *gr, double *gs_in, double *cw, double *cu)
+{
+    wkv4_backward_impl(B, T, C, w, u, k, v, r, gy, gw, gu, gk, gv, gr, s_in, s_out, gs_out, gs_in, cw, cu);
 }
 
 /*

@@ -236,3 +236,46 @@ def lru_normalized_torch(lam, u, x0=None):
     import torch
     gamma = torch.sqrt(1.0 - lam.abs() ** 2)
     return scan_torch(lam, gamma * u, x0)
+
+
+def wkv4_cond_sums(w, u, k, v, gy, r=None, s_in=None, gs_out=None):
+    """(gw, gu, cw, cu, s_out) of WKV-4 (RWKV-LLM page, eq. (14), its chain rule; the gate of
+    eq. (15); a carried state (a, b, p) decayed with the sums), every sum over the earlier
+    steps written out: dL/dw, dL/du, and per channel the sums of the magnitudes of the
+    products in their terms (cw with |A'| = A' over |v_i|).  s_out is (A_T, B_T, 0), the
+    state after the last token at exponent 0.  No rescaling: for tiny inputs only."""
+    B, T, C = k.shape
+    f = lambda x: np.asarray(x, dtype=np.float64)  # noqa: E731
+    w, u, k, v, gy = f(w), f(u), f(k), f(v), f(gy)
+    gw, gu, cw, cu = np.zeros(C), np.zeros(C), np.zeros(C), np.zeros(C)
+    s_out = np.zeros((B, C, 3))
+    for b in range(B):
+        for c in range(C):
+            eps = np.exp(-w[c])
+            a0, b0, p0 = (f(s_in[b, c]) if s_in is not None else (0.0, 0.0, 0.0))
+            for t in range(T + 1):
+                i = np.arange(t)
+                e = eps ** (t - 1 - i) * np.exp(k[b, i, c])
+                d = (t - 1 - i).astype(np.float64)
+                st = eps ** t * np.exp(p0)  # the carried state, decayed to step t
+                A = np.sum(e * v[b, i, c]) + st * a0
+                Bs = np.sum(e) + st * b0
+                Ad = np.sum(d * e * v[b, i, c]) + t * st * a0
+                Adabs = np.sum(d * e * np.abs(v[b, i, c])) + t * st * abs(a0)
+                Bd = np.sum(d * e) + t * st * b0
+                if t == T:
+                    s_out[b, c] = (A, Bs, 0.0)
+                    if gs_out is not None:
+                        gA, gB = f(gs_out[b, c])
+                        gw[c] -= gA * Ad + gB * Bd
+                        cw[c] += abs(gA) * Adabs + abs(gB) * Bd
+                    break
+                beta = np.exp(u[c] + k[b, t, c])
+                D = Bs + beta
+                y = (A + beta * v[b, t, c]) / D
+                g = gy[b, t, c] * (1.0 / (1.0 + np.exp(-f(r[b, t, c]))) if r is not None else 1.0)
+                gu[c] += g * beta * (v[b, t, c] - y) / D
+                gw[c] -= g * (Ad - y * Bd) / D
+                cu[c] += abs(g) * beta * (abs(v[b, t, c]) + abs(y)) / D
+                cw[c] += abs(g) * (Adabs + abs(y) * Bd) / D
+    return gw, gu, cw, cu, s_out

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.compare import rel_err
+from oracle.compare import chan_ratio, plain_rel, rel_err
 from linear_recurrence_rnn_amd import workloads
 
 pytestmark = pytest.mark.gpu
@@ -65,7 +65,17 @@ def worst(out, ref, time_axis=1):
     return {"index": tuple(int(x) for x in i), "got": float(out[i]), "ref": float(ref[i])}
 
 
-def check_bwd(got, ref, tol=TOL):
+def ref_bwd(d):
+    """The oracle's (gw, gu, gk, gv) and the conditioning sums (cw, cu) of gw and gu."""
+    r = oracle.wkv4_backward_cond(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    return list(r[:4]), (r[6], r[7])
+
+
+def check_bwd(got, ref, cond=None, tol=TOL):
+    """Parity of (gw, gu, gk, gv).  gk, gv: RMS-floored per sequence.  gw, gu: RMS-floored
+    over channels and, given their conditioning sums cond = (cw, cu), channel by channel:
+    |err_c| <= max(tol |ref_c|, 2^-20 cond_c) (the plain per-channel relative error is
+    reported alongside)."""
     gw, gu, gk, gv = got
     rw, ru, rk, rv = ref
     T = gk.shape[1]
@@ -84,6 +94,10 @@ def check_bwd(got, ref, tol=TOL):
               for k, o, r in (("gw", gw, rw), ("gu", gu, ru), ("gk", gk, rk), ("gv", gv, rv))
               if errs[k] > tol}
     assert all(e <= tol for e in errs.values()), (errs, detail)
+    if cond is not None:
+        chan = {"gw": chan_ratio(gw, rw, cond[0], tol), "gu": chan_ratio(gu, ru, cond[1], tol)}
+        plain = {"gw": plain_rel(gw, rw), "gu": plain_rel(gu, ru)}
+        assert all(v <= 1.0 for v in chan.values()), (chan, plain)
     return errs
 
 
@@ -112,8 +126,8 @@ def test_wkv_workload3_backward(L, wl3):
     announce("wkv4_backward workload 3 B=8 T=4096 C=2560")
     d = wl3
     got = gpu_wkv_bwd(L, d)
-    ref = oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
-    check_bwd(got, ref)
+    ref, cond = ref_bwd(d)
+    check_bwd(got, ref, cond)
 
 
 def test_scan_real_workload4(L):
@@ -150,7 +164,7 @@ def test_wkv_forward_shapes(L, shape):
 def test_wkv_backward_shapes(L, shape):
     announce("wkv4_backward shape %s" % (shape,))
     d = workloads.make_inputs(3, seed=8, shape=shape)
-    check_bwd(gpu_wkv_bwd(L, d), oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+    check_bwd(gpu_wkv_bwd(L, d), *ref_bwd(d))
 
 
 def test_wkv_unaligned_views(L):
@@ -172,7 +186,7 @@ def test_wkv_unaligned_views(L):
     outs = L.wkv4_backward(dev(d["w"]), dev(d["u"]), k, v, gy,
                            out=(dev(np.zeros(C, np.float32)), dev(np.zeros(C, np.float32)),
                                 shifted(np.zeros_like(d["k"])), shifted(np.zeros_like(d["k"]))))
-    check_bwd([host(t) for t in outs], oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+    check_bwd([host(t) for t in outs], *ref_bwd(d))
 
 
 def test_wkv_stress_spikes(L):
@@ -186,7 +200,7 @@ def test_wkv_stress_spikes(L):
     d["w"][1] = 1e4
     err = rel_err(gpu_wkv(L, d), oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"]))
     assert err <= TOL, err
-    check_bwd(gpu_wkv_bwd(L, d), oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+    check_bwd(gpu_wkv_bwd(L, d), *ref_bwd(d))
 
 
 @pytest.mark.parametrize("wid", [2, 3])
@@ -250,12 +264,12 @@ def test_backward_exact_path_matches_fast_path(L, monkeypatch, wid):
     d = workloads.make_inputs(wid, seed=22, shape=(2, 1500, 96))
     if "gy" not in d:
         d["gy"] = np.random.default_rng(5).standard_normal(d["k"].shape).astype(np.float32)
-    ref = oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    ref, cond = ref_bwd(d)
     fast = gpu_wkv_bwd(L, d)
     monkeypatch.setenv("LINREC_WKV_EXACT", "1")
     exact = gpu_wkv_bwd(L, d)
-    check_bwd(fast, ref)
-    check_bwd(exact, ref)
+    check_bwd(fast, ref, cond)
+    check_bwd(exact, ref, cond)
     for name, a, b in zip(("gw", "gu", "gk", "gv"), fast, exact):
         ax = None if name in ("gw", "gu") else 1
         assert rel_err(a, b.astype(np.float64), ax) <= 2 * TOL, name
@@ -273,7 +287,7 @@ def test_backward_launch_shapes(L, monkeypatch, nw, lc):
     monkeypatch.setenv("LINREC_BWD_L", lc)
     for shape in [(2, 1001, 150), (3, 40, 70)]:
         d = workloads.make_inputs(3, seed=13, shape=shape)
-        check_bwd(gpu_wkv_bwd(L, d), oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+        check_bwd(gpu_wkv_bwd(L, d), *ref_bwd(d))
 
 
 @pytest.mark.parametrize("spin", ["0", "1"])
@@ -284,14 +298,14 @@ def test_backward_lookback_recompute_path(L, monkeypatch, spin):
     monkeypatch.setenv("LINREC_SPIN", spin)
     d = workloads.make_inputs(3, seed=14, shape=(2, 1300, 130))
     d["k"][1, 600, 7] = 140.0
-    check_bwd(gpu_wkv_bwd(L, d), oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+    check_bwd(gpu_wkv_bwd(L, d), *ref_bwd(d))
 
 
 def test_backward_long_single_sequence(L):
     # Many slabs in one chain (look-back windows of more than 64 slabs).
     announce("wkv4_backward B=1 T=20000 C=64")
     d = workloads.make_inputs(3, seed=15, shape=(1, 20000, 64))
-    check_bwd(gpu_wkv_bwd(L, d), oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+    check_bwd(gpu_wkv_bwd(L, d), *ref_bwd(d))
 
 
 def test_forward_determinism_and_vec1(L, monkeypatch):

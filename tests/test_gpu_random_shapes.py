@@ -6,7 +6,8 @@ other parity tests cite: eq. (14) of the RWKV-LLM page ("Time-mixing block") and
 rule, the token shift of eqs. (11)-(13), the real and complex scans of the LRU write-up and
 the minGRU page, and their gated forms.  Tolerance: 1e-4 RMS-floored relative error
 (`oracle.compare.rel_err`), per sequence for (B,T,C) outputs, over the vector for (C,) and
-(B,C) ones.
+(B,C) ones; dL/dw and dL/du are also held channel by channel against their conditioning
+sums (`oracle.compare.chan_ratio`).
 """
 
 import math
@@ -16,7 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.compare import rel_err
+from oracle.compare import chan_ratio, plain_rel, rel_err
 from linear_recurrence_rnn_amd import workloads
 
 pytestmark = pytest.mark.gpu
@@ -75,6 +76,14 @@ def check(pairs):
     assert not bad, errs
 
 
+def check_chan(got_w, got_u, ref):
+    """dL/dw, dL/du channel by channel against the oracle's conditioning sums
+    (``wkv4_backward_cond`` outputs): |err_c| <= max(TOL |ref_c|, 2^-20 cond_c)."""
+    gw, gu = host(got_w), host(got_u)
+    chan = {"gw": chan_ratio(gw, ref[0], ref[6], TOL), "gu": chan_ratio(gu, ref[1], ref[7], TOL)}
+    assert all(v <= 1.0 for v in chan.values()), (chan, {"gw": plain_rel(gw, ref[0]), "gu": plain_rel(gu, ref[1])})
+
+
 def state(B, C, seed):
     rng = np.random.default_rng(seed)
     return np.stack([rng.standard_normal((B, C)), rng.uniform(0.2, 3.0, (B, C)), rng.uniform(-5.0, 20.0, (B, C))],
@@ -88,12 +97,15 @@ def test_wkv_forward_and_backward(L, shape):
     d = workloads.make_inputs(3, seed=300 + T, shape=shape)
     w, u, k, v, gy = (dev(d[n]) for n in ("w", "u", "k", "v", "gy"))
     check([("y", L.wkv4_forward(w, u, k, v), oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"]), 1)])
-    ref = oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    full = oracle.wkv4_backward_cond(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    ref = full[:4]
     got = L.wkv4_backward(w, u, k, v, gy)
     check([(n, g, r, None if n in ("gw", "gu") else 1) for n, g, r in zip(("gw", "gu", "gk", "gv"), got, ref)])
+    check_chan(got[0], got[1], full)
     y, ck = L.wkv4_forward_ckpt(w, u, k, v)
     got = L.wkv4_backward_ckpt(w, u, k, v, gy, ck)
     check([(n, g, r, None if n in ("gw", "gu") else 1) for n, g, r in zip(("gw", "gu", "gk", "gv"), got, ref)])
+    check_chan(got[0], got[1], full)
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=str)
@@ -109,16 +121,19 @@ def test_wkv_state_and_gate(L, shape):
     w, u, k, v, gy = (dev(d[n]) for n in ("w", "u", "k", "v", "gy"))
     y, _ = L.wkv4_forward_ex(w, u, k, v, r=dev(r), state=dev(s_in))
     check([("y", y, y_ref, 1)])
-    ref = oracle.wkv4_backward_ex(d["w"], d["u"], d["k"], d["v"], d["gy"], r=r, s_in=s_in, s_out=s_out,
-                                  gs_out=gs_out)
+    full = oracle.wkv4_backward_cond(d["w"], d["u"], d["k"], d["v"], d["gy"], r=r, s_in=s_in, s_out=s_out,
+                                     gs_out=gs_out)
+    ref = full[:6]
     names = ("gw", "gu", "gk", "gv", "gr", "gs_in")
     axes = {"gw": None, "gu": None, "gs_in": None}
     got = L.wkv4_backward_ex(w, u, k, v, gy, r=dev(r), s_in=dev(s_in), s_out=dev(s_out), gs_out=dev(gs_out))
     check([(n, g, rf, axes.get(n, 1)) for n, g, rf in zip(names, got, ref)])
+    check_chan(got[0], got[1], full)
     _, ck, _ = L.wkv4_forward_ckpt_ex(w, u, k, v, r=dev(r), state=dev(s_in))
     got = L.wkv4_backward_ckpt_ex(w, u, k, v, gy, ck, r=dev(r), s_in=dev(s_in), s_out=dev(s_out),
                                   gs_out=dev(gs_out))
     check([(n, g, rf, axes.get(n, 1)) for n, g, rf in zip(names, got, ref)])
+    check_chan(got[0], got[1], full)
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=str)

@@ -13,7 +13,7 @@ import oracle
 from oracle.compare import rel_err
 from linear_recurrence_rnn_amd import workloads
 
-from test_gpu_parity import TOL, announce, check_bwd, dev, host, gpu_wkv_bwd
+from test_gpu_parity import TOL, announce, check_bwd, dev, host, gpu_wkv_bwd, ref_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -36,10 +36,10 @@ def ckpt_step(L, d):
 
 def check_step(L, d, compare_plain=True):
     ref_y = oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])
-    ref_g = oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
+    ref_g, cond = ref_bwd(d)
     y, g, _ = ckpt_step(L, d)
     assert rel_err(y, ref_y) <= TOL, rel_err(y, ref_y)
-    check_bwd(g, ref_g)
+    check_bwd(g, ref_g, cond)
     if compare_plain and d["k"].shape[1] > 1:
         plain = gpu_wkv_bwd(L, d)
         for name, a, b in zip(("gw", "gu", "gk", "gv"), g, plain):
@@ -154,7 +154,7 @@ def test_ckpt_step_is_deterministic_and_buffers_reusable(L):
     y2, _ = L.wkv4_forward_ckpt(w, u, k, v, out=(torch.empty_like(k), ck), workspace=fws)
     g2 = L.wkv4_backward_ckpt(w, u, k, v, dev(d2["gy"]), ck)
     assert rel_err(host(y2), oracle.wkv4_forward(d2["w"], d2["u"], d2["k"], d2["v"])) <= TOL
-    check_bwd([host(t) for t in g2], oracle.wkv4_backward(d2["w"], d2["u"], d2["k"], d2["v"], d2["gy"]))
+    check_bwd([host(t) for t in g2], *ref_bwd(d2))
 
 
 def test_ckpt_backward_empty_sequence(L):
@@ -209,7 +209,7 @@ def test_ckpt_serves_gated_and_plain_backward(L):
     w, u, k, v = dev(d["w"]), dev(d["u"]), dev(d["k"]), dev(d["v"])
     _, ck = L.wkv4_forward_ckpt(w, u, k, v, r=dev(r))
     got = [host(t) for t in L.wkv4_backward_ckpt(w, u, k, v, dev(d["gy"]), ck)]
-    check_bwd(got, oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"]))
+    check_bwd(got, *ref_bwd(d))
 
 
 def test_ckpt_step_gated_lookback_recompute(L, monkeypatch):

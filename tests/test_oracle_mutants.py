@@ -98,6 +98,10 @@ MUTANTS = [
     ("lru_norm_bwd_gamma_term_sign", "glam[2 * c] = re - k * creal(L);", "glam[2 * c] = re + k * creal(L);"),
     ("lru_norm_bwd_gu_unscaled", "gu[2 * o] = gamma * creal(s);", "gu[2 * o] = creal(s);"),
     ("shift_bwd_gx_prev_weight", "if (T > 0) gp += (1.0 - mm) * (double)gm[base];", "if (T > 0) gp += mm * (double)gm[base];"),
+    ("cond_w_signed_past", "Aabs = eps * Aabs + alpha * fabs(vt);", "Aabs = eps * Aabs + alpha * vt;"),
+    ("cond_u_y_dropped", "cgu += fabs(g) * beta * (fabs(vt) + fabs(yt)) / Dt;", "cgu += fabs(g) * beta * fabs(vt) / Dt;"),
+    ("cond_state_term_dropped", "cgw += fabs(gA) * Adabs + fabs(gB) * Bd;", ""),
+    ("cond_w_derivative_sum", "Adabs = eps * (Adabs + Aabs);", "Adabs = eps * Adabs + Aabs;"),
 ]
 
 
@@ -266,6 +270,20 @@ def _pins_pass(lib) -> bool:
     rl, _, r0 = brute.scan_complex_backward_sums(lu["lam"][edge], gu_[..., edge], rot[..., edge], lu["x0"][:, edge])
     ok &= np.allclose(gl[edge], rl, rtol=1e-10, atol=1e-10) and np.allclose(g0[:, edge], r0, rtol=1e-11, atol=1e-11)
     ok &= bool(np.all(gq[..., edge] == 0))
+
+    # Conditioning sums of dL/dw, dL/du (plain, and with a carried state) against their
+    # brute-force sums.
+    wc, uc, kc, vc = d["w"], d["u"], d["k"], d["v"]
+    gc = rng.standard_normal(kc.shape).astype(np.float32)
+    sc_in = np.stack([rng.standard_normal(kc.shape[::2]), rng.uniform(0.2, 3.0, kc.shape[::2]),
+                      rng.uniform(-2.0, 2.0, kc.shape[::2])], axis=-1).astype(np.float32)
+    gsc = rng.standard_normal(kc.shape[::2] + (2,)).astype(np.float32)
+    for kw in ({}, {"s_in": sc_in, "gs_out": gsc}):
+        ref = brute.wkv4_cond_sums(wc, uc, kc, vc, gc, **kw)
+        if kw:
+            kw = dict(kw, s_out=ref[4].astype(np.float32))
+        got = oracle.wkv4_backward_cond(wc, uc, kc, vc, gc, lib=lib, **kw)
+        ok &= np.allclose(got[6], ref[2], rtol=1e-9) and np.allclose(got[7], ref[3], rtol=1e-9)
     return bool(ok)
 
 
