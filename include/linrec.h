@@ -264,8 +264,9 @@ int wkv4_backward_ex(int64_t B, int64_t T, int64_t C,
  *   (The sums do not depend on r: one ckpt serves the gated and the plain backward.)
  *
  *   ckpt  device buffer of at least wkv4_checkpoint_size(B, T, C) bytes, 16-byte aligned,
- *         owned by the caller.  Its contents are opaque (float64 sums with an integer
- *         exponent per channel and slab); they are valid only for the B, T, C, w and k, v of
+ *         owned by the caller.  Its contents are opaque (float32 mantissas of the sums with
+ *         an integer exponent, 20 bytes per channel and slab); they are valid only for the
+ *         B, T, C, w and k, v of
  *         the forward that wrote them, and only after that forward has completed in stream
  *         order.  The backward only reads it.
  *   r     (B,T,C) float32 receptance, or NULL: with r the output is the gated sigma(r) wkv

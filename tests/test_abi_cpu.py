@@ -300,9 +300,9 @@ def test_wkv4_checkpoint_argument_checks(lib):
     nck = lib.wkv4_checkpoint_size(B, T, C)
     nfw = lib.wkv4_forward_ckpt_workspace_size(B, T, C)
     nbw = lib.wkv4_backward_ckpt_workspace_size(B, T, C)
-    # one record (4 float64 sums and an exponent, padded to 40 bytes) per slab of 56 steps,
+    # one record (4 float32 mantissas and their exponent, 20 bytes) per slab of 56 steps,
     # channel and batch row; the backward's workspace drops the state pass
-    assert nck == B * C * ((T + 55) // 56) * 40
+    assert nck == B * C * ((T + 55) // 56) * 20
     assert 0 < nbw < lib.wkv4_backward_workspace_size(B, T, C)
     assert nfw > 0
     assert lib.wkv4_checkpoint_size(0, T, C) == 0 and lib.wkv4_checkpoint_size(-1, T, C) == 0
