@@ -31,15 +31,29 @@ constexpr uint64_t kStateIncl = 2;
 template <class Agg>
 constexpr int kDwords = (int)(sizeof(Agg) / 4);
 
+// The form a record takes in memory: the aggregate itself, unless its type names a narrower
+// one (a specialisation of RecordOf) that every publisher and every reader converts through,
+// so that all of them fold the same values.
+template <class Agg>
+struct RecordOf {
+    using type = Agg;
+    __device__ __forceinline__ static Agg to(const Agg& a) { return a; }
+    __device__ __forceinline__ static Agg from(const Agg& r) { return r; }
+};
+template <class Agg>
+constexpr int kRecDwords = kDwords<typename RecordOf<Agg>::type>;
+
 // This wave's VEC entries per lane of slab q's record (rec: dwords, field-major).
 template <int VEC, class Agg>
 __device__ __forceinline__ void store_record(uint32_t* rec, int64_t q, int lane, const Agg (&x)[VEC]) {
-    static_assert(sizeof(Agg) % 4 == 0, "record must be whole dwords");
-    constexpr int ND = kDwords<Agg>;
+    using Rec = typename RecordOf<Agg>::type;
+    static_assert(sizeof(Rec) % 4 == 0, "record must be whole dwords");
+    constexpr int ND = kDwords<Rec>;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
         uint32_t w[ND];
-        __builtin_memcpy(w, &x[e], sizeof(Agg));
+        const Rec r = RecordOf<Agg>::to(x[e]);
+        __builtin_memcpy(w, &r, sizeof(Rec));
 #pragma unroll
         for (int i = 0; i < ND; ++i)
             __hip_atomic_store(rec + ((q * ND + i) * VEC + e) * 64 + lane, w[i], __ATOMIC_RELAXED,
@@ -49,7 +63,8 @@ __device__ __forceinline__ void store_record(uint32_t* rec, int64_t q, int lane,
 
 template <int VEC, class Agg>
 __device__ __forceinline__ void load_record(const uint32_t* rec, int64_t q, int lane, Agg (&x)[VEC]) {
-    constexpr int ND = kDwords<Agg>;
+    using Rec = typename RecordOf<Agg>::type;
+    constexpr int ND = kDwords<Rec>;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
         uint32_t w[ND];
@@ -57,7 +72,9 @@ __device__ __forceinline__ void load_record(const uint32_t* rec, int64_t q, int 
         for (int i = 0; i < ND; ++i)
             w[i] = __hip_atomic_load(rec + ((q * ND + i) * VEC + e) * 64 + lane, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_memcpy(&x[e], w, sizeof(Agg));
+        Rec r;
+        __builtin_memcpy(&r, w, sizeof(Rec));
+        x[e] = RecordOf<Agg>::from(r);
     }
 }
 

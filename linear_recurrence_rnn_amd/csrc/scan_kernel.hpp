@@ -122,8 +122,8 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     // this lane's bytes in the row (out of range for an inactive lane of a uniform-step operator)
     const unsigned voff = (UN && !active) ? kOutOfRange : (unsigned)(lane * VEC * EF * 4);
     const Chain<Agg> chn{g.flags + gi * g.nslab,
-                         reinterpret_cast<uint32_t*>(g.rec_agg) + gi * g.nslab * (CW * kDwords<Agg>),
-                         reinterpret_cast<uint32_t*>(g.rec_incl) + gi * g.nslab * (CW * kDwords<Agg>), g.tag, g.spin};
+                         reinterpret_cast<uint32_t*>(g.rec_agg) + gi * g.nslab * (CW * kRecDwords<Agg>),
+                         reinterpret_cast<uint32_t*>(g.rec_incl) + gi * g.nslab * (CW * kRecDwords<Agg>), g.tag, g.spin};
     const bool has_succ = s + 1 < g.nslab;
 
     // Coordination, by one whole wave after B1: the slab aggregate (published), the carry
@@ -162,9 +162,11 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
                     for (int e = 0; e < VEC; ++e) x[e] = Op::step(ch[e], x[e], xi[e]);
                 }
             }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) x[e] = RecordOf<Agg>::from(RecordOf<Agg>::to(x[e]));  // as if read
         };
         // Records in flight per lane: fewer for the wide (float64) aggregates.
-        constexpr int KB = (VEC >= 4 || kDwords<Agg> > 4) ? 2 : (VEC == 2 ? 4 : 8);
+        constexpr int KB = (VEC >= 4 || kRecDwords<Agg> > 4) ? 2 : (VEC == 2 ? 4 : 8);
         look_back<VEC, KB>(chn, s, lane, carry, fold, recompute, first);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {

@@ -356,7 +356,7 @@ __global__ __launch_bounds__(64 * (kStateFine + 1)) __attribute__((amdgpu_waves_
 void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
     constexpr int SLAB = NW * L;
     constexpr int F = kStateFine;
-    constexpr int kRec = 64 * kDwords<Fwd>;  // dwords per coarse-chain record
+    constexpr int kRec = 64 * kRecDwords<Fwd>;  // dwords per coarse-chain record
     __shared__ Fwd shf[2][F][64];
 
     const int tid = threadIdx.x;
@@ -497,6 +497,7 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
                     fwd_advance(om[0], x[0], kj, (double)vj, mag(x[0].p, (float)x[0].b));
                 }
             }
+            x[0] = RecordOf<Fwd>::from(RecordOf<Fwd>::to(x[0]));  // in the records' form, as if read
         };
         look_back<1, 2>(chn, it.q, lane, carry, fold, recompute, first);
         // The sums at the end of every fine slab of the item (read by the gradient kernel).
@@ -1070,7 +1071,7 @@ BwdPlan wkv_backward_plan(int vec, int64_t B, int64_t T, int64_t C, int nw_overr
     if (p.nslab > 1) {
         const int64_t ncoarse = B * ((C + cw - 1) / cw) * ((p.nslab - 1 + kStateFine - 1) / kStateFine);
         bytes += align256((size_t)ncoarse * 8);                            // coarse flags
-        bytes += 2 * align256((size_t)(ncoarse * cw) * sizeof(Fwd));       // coarse records
+        bytes += 2 * align256((size_t)(ncoarse * cw) * sizeof(RecordOf<Fwd>::type));  // coarse records
         bytes += align256((size_t)(nrec * cw) * sizeof(FwdRec));           // sums at fine slab ends
         bytes += align256((size_t)nrec * 8);                               // reverse flags
         bytes += 2 * align256((size_t)(nrec * cw) * sizeof(RevRec));       // reverse records
@@ -1092,7 +1093,7 @@ void wkv_backward_layout(const BwdPlan& p, int64_t B, int64_t C, void* ws, BwdGe
     const size_t fl = align256((size_t)nrec * 8);
     const size_t fr = align256((size_t)(nrec * cw) * sizeof(FwdRec));
     const size_t rr = align256((size_t)(nrec * cw) * sizeof(RevRec));
-    const size_t cr = align256((size_t)(ncoarse * cw) * sizeof(Fwd));
+    const size_t cr = align256((size_t)(ncoarse * cw) * sizeof(RecordOf<Fwd>::type));
     g.flags_c = reinterpret_cast<uint64_t*>(at), at += align256((size_t)ncoarse * 8);
     g.agg_c = at, at += cr;
     g.incl_c = at, at += cr;

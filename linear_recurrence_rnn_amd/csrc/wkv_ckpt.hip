@@ -237,7 +237,7 @@ size_t wkv_ckpt_forward_ws_bytes(int64_t B, int64_t T, int64_t C) {
     const int64_t nslab = (T + kCkptNW * kCkptL - 1) / (kCkptNW * kCkptL);
     if (nslab <= 1) return 0;
     const int64_t nwg = B * ((C + 63) / 64) * nslab;
-    return align256((size_t)nwg * 8) + 2 * align256((size_t)(nwg * 64) * sizeof(Fwd));
+    return align256((size_t)nwg * 8) + 2 * align256((size_t)(nwg * 64) * sizeof(RecordOf<Fwd>::type));
 }
 
 hipError_t run_wkv_forward_ckpt(const WkvArgs& A, int64_t B, int64_t T, int64_t C, void* ckpt, void* ws,
@@ -259,7 +259,7 @@ hipError_t run_wkv_forward_ckpt(const WkvArgs& A, int64_t B, int64_t T, int64_t 
     g.spin = spin;
     if (g.nslab > 1) {
         const int64_t nwg = B * g.ngrp * g.nslab;
-        const size_t rec = align256((size_t)(nwg * 64) * sizeof(Fwd));
+        const size_t rec = align256((size_t)(nwg * 64) * sizeof(RecordOf<Fwd>::type));
         g.flags = reinterpret_cast<uint64_t*>(ws);
         g.rec_agg = (char*)ws + align256((size_t)nwg * 8);
         g.rec_incl = (char*)g.rec_agg + rec;

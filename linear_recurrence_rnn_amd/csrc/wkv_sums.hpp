@@ -16,6 +16,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "lookback.hpp"
 #include "wkv_math.hpp"
 
 namespace linrec {
@@ -32,6 +33,15 @@ __device__ __forceinline__ FwdRec fwd_to_rec(const Fwd& s) {
     return {(float)s.a, (float)s.b, (float)s.ad, (float)s.bd, s.p};
 }
 __device__ __forceinline__ Fwd fwd_from_rec(const FwdRec& r) { return {r.a, r.b, r.ad, r.bd, r.p}; }
+
+// Look-back records of these sums (the checkpointing forward's slabs, the state kernel's
+// coarse chain) take the same form; the folds stay in float64.
+template <>
+struct RecordOf<Fwd> {
+    using type = FwdRec;
+    __device__ __forceinline__ static FwdRec to(const Fwd& s) { return fwd_to_rec(s); }
+    __device__ __forceinline__ static Fwd from(const FwdRec& r) { return fwd_from_rec(r); }
+};
 
 // State s1, then a span s2 of n2 steps:
 //   A = eps^n2 A1 + A2,   A' = eps^n2 (A'1 + n2 A1) + A'2   (B, B' likewise).
