@@ -23,7 +23,7 @@
 //                    sequence ends with the sums of the whole row;
 //   a third kernel sums the rows over the batch in order.
 // HBM traffic: k, v twice, g once, dL/dk, dL/dv once (28 bytes per element; 20 algorithmic),
-// plus the slab-end sums and the reverse look-back records (about 4 more at 56-step slabs).
+// plus the slab-end sums and the reverse look-back records (about 2.5 more at 56-step slabs).
 //
 // The sums are float64 mantissas times 2^p with p an integer exponent (wkv_math.hpp).  The
 // gradients are differences of long sums (v G - H, A' - y B'): float64 mantissas keep their
