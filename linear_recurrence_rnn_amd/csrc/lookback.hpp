@@ -4,9 +4,13 @@
 // (q = 0 first: time order for a forward scan, reverse time order for a backward one).  Each
 // slab publishes its aggregate (AGG), then -- once it knows its carry-in -- its inclusive
 // prefix (INCL); a slab that knows its carry before its aggregate is formed may publish
-// INCL alone (its flag never reads AGG, so no reader looks for the missing record).  A slab's carry is the nearest published INCL folded with the aggregates
-// of the slabs after it, in chain order: the association a strictly chained scan would use,
-// so the result does not depend on timing.
+// INCL alone (its flag never reads AGG, so no reader looks for the missing record).  A slab's
+// carry is the nearest published INCL folded with the aggregates of the slabs after it, in
+// chain order: the association a strictly chained scan would use, so the result does not
+// depend on timing.  That needs every INCL_q to equal, bit for bit, INCL_{q-1} folded with
+// AGG_q as a reader would fold them: a publisher forms INCL as its carry folded with the
+// very aggregate it publishes, and where records are narrower than the aggregates every
+// chain value (aggregate, each fold, INCL) is taken in the record's form (as_record).
 //
 // Records are written and read with device-scope relaxed atomics, which the hardware keeps
 // coherent across the XCDs' L2 caches (they write through), and a publication flag is
@@ -42,6 +46,12 @@ struct RecordOf {
 };
 template <class Agg>
 constexpr int kRecDwords = kDwords<typename RecordOf<Agg>::type>;
+
+// x as a record holds it (x itself unless Agg has a narrower record form); idempotent.
+template <class Agg>
+__device__ __forceinline__ Agg as_record(const Agg& x) {
+    return RecordOf<Agg>::from(RecordOf<Agg>::to(x));
+}
 
 // This wave's VEC entries per lane of slab q's record (rec: dwords, field-major).
 template <int VEC, class Agg>

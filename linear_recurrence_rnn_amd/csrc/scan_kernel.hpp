@@ -139,12 +139,13 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
                 sh[x][lane * VEC + e] = mine[e];
                 mine[e] = Op::combine(ch[e], mine[e], chunk, chunk_len(x));
             }
-            carry[e] = active ? Op::init(A, g, b, c0 + e) : Op::identity();
+            mine[e] = as_record(mine[e]);  // chain values in the records' form (lookback.hpp)
+            carry[e] = as_record(active ? Op::init(A, g, b, c0 + e) : Op::identity());
         }
         if (has_succ) publish<VEC>(chn, s, lane, mine, false);
         auto fold = [&](Agg (&c)[VEC], const Agg (&x)[VEC], int64_t) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) c[e] = Op::combine(ch[e], c[e], x[e], SLAB);
+            for (int e = 0; e < VEC; ++e) c[e] = as_record(Op::combine(ch[e], c[e], x[e], SLAB));
         };
         // A slab whose aggregate was not published in time is recomputed from its inputs.
         auto recompute = [&](int64_t jj, Agg (&x)[VEC]) {
@@ -163,7 +164,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
                 }
             }
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) x[e] = RecordOf<Agg>::from(RecordOf<Agg>::to(x[e]));  // as if read
+            for (int e = 0; e < VEC; ++e) x[e] = as_record(x[e]);  // as if read
         };
         // Records in flight per lane: fewer for the wide (float64) aggregates.
         constexpr int KB = (VEC >= 4 || kRecDwords<Agg> > 4) ? 2 : (VEC == 2 ? 4 : 8);
@@ -171,7 +172,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             sh_carry[lane * VEC + e] = carry[e];
-            incl[e] = Op::combine(ch[e], carry[e], mine[e], slab_n);
+            incl[e] = as_record(Op::combine(ch[e], carry[e], mine[e], slab_n));
         }
     };
     // Hands the inclusive prefix on: published for the next slab, or, in the last slab, the

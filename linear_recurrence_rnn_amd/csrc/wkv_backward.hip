@@ -477,14 +477,18 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
         const int nvalid = (int)((nfine - f0) < F ? (nfine - f0) : F);
         __syncthreads();
         const uint64_t first = prefetch_window(chn, it.q, lane);  // overlaps the fold below
+        // Chain values (the item's aggregate, each fold, the inclusive sums) are taken in the
+        // records' form, and the inclusive sums are the carry folded with that aggregate, so
+        // that every look-back path folds the same values (lookback.hpp).
         Fwd mine[1], carry[1];
         mine[0] = shf[ib][0][lane];
         for (int x = 1; x < nvalid; ++x) mine[0] = fwd_combine(om[0], mine[0], shf[ib][x][lane], SLAB);
-        carry[0] = it.active ? fwd_state_in(A, g, it.b, it.c0) : fwd_identity();
+        mine[0] = as_record(mine[0]);
+        carry[0] = as_record(it.active ? fwd_state_in(A, g, it.b, it.c0) : fwd_identity());
         const bool has_succ = it.q + 1 < nitem;
         if (has_succ) publish<1>(chn, it.q, lane, mine, false);
         auto fold = [&](Fwd (&c)[1], const Fwd (&x)[1], int64_t) {
-            c[0] = fwd_combine(om[0], c[0], x[0], (int64_t)F * SLAB);  // earlier items are full
+            c[0] = as_record(fwd_combine(om[0], c[0], x[0], (int64_t)F * SLAB));  // earlier items are full
         };
         auto recompute = [&](int64_t jj, Fwd (&x)[1]) {
             const int64_t bj = (it.b * g.T + jj * F * SLAB) * g.C + it.grp * 64;
@@ -497,9 +501,13 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
                     fwd_advance(om[0], x[0], kj, (double)vj, mag(x[0].p, (float)x[0].b));
                 }
             }
-            x[0] = RecordOf<Fwd>::from(RecordOf<Fwd>::to(x[0]));  // in the records' form, as if read
+            x[0] = as_record(x[0]);  // as if read
         };
         look_back<1, 2>(chn, it.q, lane, carry, fold, recompute, first);
+        if (has_succ) {
+            const Fwd incl[1] = {as_record(fwd_combine(om[0], carry[0], mine[0], (int64_t)F * SLAB))};
+            publish<1>(chn, it.q, lane, incl, true);
+        }
         // The sums at the end of every fine slab of the item (read by the gradient kernel).
         uint32_t* fine = reinterpret_cast<uint32_t*>(g.incl_f) + it.gi * g.nslab * (64 * kDwords<FwdRec>);
         for (int x = 0; x < nvalid; ++x) {
@@ -507,7 +515,6 @@ void wkv_bwd_state_kernel(WkvBwdArgs A, BwdGeom g) {
             const FwdRec r[1] = {fwd_to_rec(carry[0])};
             store_record<1>(fine, f0 + x, lane, r);
         }
-        if (has_succ) publish<1>(chn, it.q, lane, carry, true);
     }
 }
 

@@ -1,7 +1,8 @@
 """Calls captured into a HIP graph and replayed, through the C ABI: every replay gives, bit
 for bit, what an eager call on the replay's inputs gives, and stays within the oracle's
-tolerance (WKV-4 forward and backward: eq. (14) of the RWKV-LLM page, "Time-mixing block";
-the decay adjoint with its glambda sums: the LRU write-up's diagonal recurrence).
+tolerance (WKV-4 forward, backward and the checkpointed training step: eq. (14) of the
+RWKV-LLM page, "Time-mixing block"; the decay adjoint with its glambda sums: the LRU
+write-up's diagonal recurrence).
 
 A captured call keeps its host-drawn look-back tag on every replay; while the stream is
 capturing, the library also records a fill kernel that clears the call's flags, so each
@@ -131,4 +132,43 @@ def test_decay_adjoint_graph_replays(L):
             assert np.array_equal(a, b), seed
         ref = oracle.scan_real_decay_backward(d["lam"], x, d["gx"], d["x0"], want_gx0=True)
         errs = [rel_err(got[0], ref[0], None), rel_err(got[1], ref[1], 1), rel_err(got[2], ref[2], None)]
+        assert max(errs) <= TOL, (seed, errs)
+
+
+def test_ckpt_step_graph_replays(L):
+    # The checkpointed training step captured whole: the forward's look-back and kept sums,
+    # then the backward from them (RWKV-LLM page, eq. (14), "Time-mixing block", and its
+    # chain rule).  10 forward slabs of 128 steps and 22 kept sums every 56.
+    import torch
+    B, T, C = 2, 1200, 130
+    announce("wkv4_forward_ckpt + wkv4_backward_ckpt captured and replayed B=%d T=%d C=%d" % (B, T, C))
+    d0 = workloads.make_inputs(3, seed=213, shape=(B, T, C))
+    ins = [torch.from_numpy(d0[n]).cuda() for n in ("w", "u", "k", "v", "gy")]
+    w, u, k, v, gy = ins
+    lib = L.load()
+    y = torch.empty_like(k)
+    ck = torch.empty(L.wkv4_checkpoint_size(B, T, C), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(lib.wkv4_forward_ckpt_workspace_size(B, T, C), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(lib.wkv4_backward_ckpt_workspace_size(B, T, C), dtype=torch.uint8, device="cuda")
+    outs = (torch.empty(C, device="cuda"), torch.empty(C, device="cuda"), torch.empty_like(k), torch.empty_like(k))
+
+    def step():
+        L.wkv4_forward_ckpt(w, u, k, v, out=(y, ck), workspace=fws)
+        return L.wkv4_backward_ckpt(w, u, k, v, gy, ck, out=outs, workspace=bws)
+
+    g, _ = capture(step)
+    for seed in (214, 215, 216):
+        d = workloads.make_inputs(3, seed=seed, shape=(B, T, C))
+        load(ins, [d[n] for n in ("w", "u", "k", "v", "gy")])
+        g.replay()
+        got_y = host(y)
+        got = [host(t) for t in outs]
+        ey, eck = L.wkv4_forward_ckpt(w, u, k, v)
+        eager = [host(t) for t in L.wkv4_backward_ckpt(w, u, k, v, gy, eck)]
+        assert np.array_equal(got_y, host(ey)), seed
+        for a, b in zip(got, eager):
+            assert np.array_equal(a, b), seed
+        assert rel_err(got_y, oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])) <= TOL, seed
+        ref = oracle.wkv4_backward(d["w"], d["u"], d["k"], d["v"], d["gy"])
+        errs = [rel_err(got[i], ref[i], None if i < 2 else 1) for i in range(4)]
         assert max(errs) <= TOL, (seed, errs)
