@@ -230,14 +230,19 @@ __device__ __forceinline__ void look_back(const Chain<Agg>& ch, int64_t q, int l
 // look_back does -- same records, same association, so the same bits -- and returns true.
 // Returns false, with `carry` untouched, as soon as give_up() holds or after ch.spin polls;
 // the caller then publishes its aggregate and calls look_back.  Chains longer than 64 slabs
-// without an inclusive prefix in that window always end that way.
+// without an inclusive prefix in that window always end that way.  With `first` (the
+// prefetched window of prefetch_window), the first round reads those flags instead of
+// polling again.
 template <int VEC, class Agg, class Fold, class GiveUp>
 __device__ __forceinline__ bool try_look_back(const Chain<Agg>& ch, int64_t q, int lane, Agg (&carry)[VEC],
-                                              Fold&& fold, GiveUp&& give_up) {
+                                              Fold&& fold, GiveUp&& give_up, const uint64_t* first = nullptr) {
     if (q == 0) return true;
     const int64_t j = q - 1 - lane;  // lane i watches slab q-1-i
     for (int it = 0;; ++it) {
-        const uint64_t f = j >= 0 ? __hip_atomic_load(ch.flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        const uint64_t f = j < 0 ? 0
+                           : (it == 0 && first) ? *first
+                                                : __hip_atomic_load(ch.flags + j, __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_AGENT);
         const uint64_t incl_mask = __ballot(j >= 0 && f == ch.tag * 4 + kStateIncl);
         const uint64_t pub_mask = __ballot(j >= 0 && (f >> 2) == ch.tag);
         bool ready = false;

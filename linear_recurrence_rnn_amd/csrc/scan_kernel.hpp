@@ -131,6 +131,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     // Returns the inclusive prefix, carry followed by the slab.
     auto coordinate = [&](uint64_t first, Agg (&incl)[VEC]) {
         Agg mine[VEC], carry[VEC];
+        bool early_carry = false;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             mine[e] = sh[0][lane * VEC + e];
@@ -142,11 +143,20 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
             mine[e] = as_record(mine[e]);  // chain values in the records' form (lookback.hpp)
             carry[e] = as_record(active ? Op::init(A, g, b, c0 + e) : Op::identity());
         }
-        if (has_succ) publish<VEC>(chn, s, lane, mine, false);
         auto fold = [&](Agg (&c)[VEC], const Agg (&x)[VEC], int64_t) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) c[e] = as_record(Op::combine(ch[e], c[e], x[e], SLAB));
         };
+        // When the flags prefetched before B1 already resolve the carry (every predecessor,
+        // or all of them from the nearest inclusive prefix on, published), the slab publishes
+        // its inclusive prefix alone: no aggregate, so one store round trip fewer.  The same
+        // records in the same association as look_back, so the same bits.  Coordination in
+        // wave 0 only: with a coordinator wave of its own (long chains) it measured slower.
+        if (!SEP && try_look_back<VEC>(chn, s, lane, carry, fold, [] { return true; }, &first)) {
+            early_carry = true;
+        } else if (has_succ) {
+            publish<VEC>(chn, s, lane, mine, false);
+        }
         // A slab whose aggregate was not published in time is recomputed from its inputs.
         auto recompute = [&](int64_t jj, Agg (&x)[VEC]) {
             int64_t rowj;
@@ -168,7 +178,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
         };
         // Records in flight per lane: fewer for the wide (float64) aggregates.
         constexpr int KB = (VEC >= 4 || kRecDwords<Agg> > 4) ? 2 : (VEC == 2 ? 4 : 8);
-        look_back<VEC, KB>(chn, s, lane, carry, fold, recompute, first);
+        if (!early_carry) look_back<VEC, KB>(chn, s, lane, carry, fold, recompute, first);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             sh_carry[lane * VEC + e] = carry[e];
