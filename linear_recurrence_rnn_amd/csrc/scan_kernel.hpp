@@ -28,6 +28,7 @@
 // a per-call tag, so stale flags from earlier calls read as "not published".
 #pragma once
 
+#include <cstdlib>
 #include <type_traits>
 
 #include "chunk_scan.hpp"
@@ -56,6 +57,7 @@ struct uniform_steps : std::false_type {};
 template <class Op>
 struct uniform_steps<Op, std::void_t<decltype(Op::kUniformSteps)>> : std::bool_constant<Op::kUniformSteps> {};
 constexpr unsigned kOutOfRange = 0x80000000u;
+constexpr int64_t kGridYZMax = 65535;  // grid extent in y and z
 
 template <class Op, int VEC, int L>
 constexpr int scan_waves_per_eu() {
@@ -103,19 +105,41 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int64_t G = g.B * g.ngrp;
-    const int64_t s = (int64_t)blockIdx.x / G;  // slab in the recurrence's order: predecessors come first
-    const int64_t gi = (int64_t)blockIdx.x - s * G;
-    const int64_t b = gi / g.ngrp, grp = gi - b * g.ngrp;
+    // Slab s (in the recurrence's order: predecessors are dispatched first), batch row b and
+    // channel group grp.  A 3-D grid (ngrp, B, nslab) hands them over directly; the flat grid
+    // (sizes beyond the 3-D grid's limits) divides the block index, a long scalar sequence
+    // that every wave ran before its first load.
+    int64_t s, b, grp;
+    if (g.grid3) {
+        s = blockIdx.z;
+        b = blockIdx.y;
+        grp = blockIdx.x;
+    } else {
+        const int64_t G = g.B * g.ngrp;
+        s = (int64_t)blockIdx.x / G;
+        const int64_t gq = (int64_t)blockIdx.x - s * G;
+        b = gq / g.ngrp;
+        grp = gq - b * g.ngrp;
+    }
+    const int64_t gi = b * g.ngrp + grp;
     const int64_t c0 = grp * CW + (int64_t)lane * VEC;
     const bool active = c0 < g.C;  // C is a multiple of VEC
     const int64_t t_slab = s * SLAB;
     const int slab_n = (int)((g.T - t_slab) < SLAB ? (g.T - t_slab) : SLAB);
     auto chunk_len = [&](int x) { return max(0, min(L, slab_n - x * L)); };
 
+    // The channels' constants (for WKV w and u; for the complex scans lambda and lambda^L).
+    // They are formed after the chunk's loads are issued: formed first, their wait held the
+    // chunk's loads back by one memory round trip.  A lane past the last channel reads the
+    // first channels' (no branch around the loads) and keeps the empty constants.
     Chan ch[VEC];
+    auto form_chan = [&]() {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) ch[e] = active ? Op::template chan<L>(A, c0 + e) : Chan{};
+        for (int e = 0; e < VEC; ++e) {
+            const Chan x = Op::template chan<L>(A, active ? c0 + e : (int64_t)e);
+            ch[e] = active ? x : Chan{};
+        }
+    };
 
     const unsigned rowb = (unsigned)(g.C * EF * 4);           // bytes per time step
     constexpr bool UN = uniform_steps<Op>::value;
@@ -212,6 +236,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     if constexpr (SEP) {
         if (w == NW) {
             // ---- the coordinator wave ----
+            form_chan();
             __syncthreads();  // B1: chunk aggregates are in sh
             Agg incl[VEC];
             coordinate(prefetch_window(chn, s, lane), incl);
@@ -243,6 +268,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
             else Op::template zero<VEC>(in[j]);
         }
     }
+    form_chan();
     Local loc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) sh[w][lane * VEC + e] = Op::template reduce<L, VEC>(ch[e], in, e, n, loc[e]);
@@ -294,14 +320,20 @@ template <class Op, int VEC, int NW, int L>
 hipError_t launch(const typename Op::Args& A, const ScanGeom& g, bool sep, hipStream_t st) {
     const int64_t nb = g.B * g.ngrp * g.nslab;
     if (const hipError_t e = clear_flags_if_capturing(g.flags, nb, st)) return e;
+    // The 3-D grid numbers blocks x fastest, then y, then z: the same slab-major order as the
+    // flat one.  Its y and z extents are kept within 65535.
+    // LINREC_FLAT_GRID=1 takes the flat grid at any size (tests).
+    const char* flat = std::getenv("LINREC_FLAT_GRID");
+    ScanGeom g3 = g;
+    g3.grid3 = g.B <= kGridYZMax && g.nslab <= kGridYZMax && !(flat && flat[0] == '1');
+    const dim3 grid = g3.grid3 ? dim3((unsigned)g.ngrp, (unsigned)g.B, (unsigned)g.nslab) : dim3((unsigned)nb);
     if constexpr (VEC == 1) {
         if (sep) {
-            hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, true>), dim3((unsigned)nb), dim3(64 * (NW + 1)),
-                               0, st, A, g);
+            hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, true>), grid, dim3(64 * (NW + 1)), 0, st, A, g3);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, false>), dim3((unsigned)nb), dim3(64 * NW), 0, st, A, g);
+    hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, false>), grid, dim3(64 * NW), 0, st, A, g3);
     return hipGetLastError();
 }
 

@@ -377,3 +377,32 @@ def test_scan_special_cases(L):
     assert rel_err(x, np.cumsum(b.astype(np.float64), axis=1)) <= TOL
     x = host(L.scan_real(dev(np.zeros_like(b)), dev(b)))
     np.testing.assert_array_equal(x, b)
+
+
+def test_flat_grid_matches_3d_grid(L, monkeypatch):
+    # The scan kernels run on a 3-D grid (channel groups, batch rows, slabs) whenever the
+    # rows and slabs fit its y and z extents, and on a flat grid, whose block index is
+    # divided into the same three, otherwise.  Both number the blocks alike, so the results
+    # must agree bit for bit (forward WKV, real and complex scans, a reverse-time adjoint),
+    # and with the oracle.
+    announce("flat grid (LINREC_FLAT_GRID=1) vs 3-D grid")
+    d = workloads.make_inputs(3, seed=31, shape=(3, 1100, 200))
+    r = workloads.make_inputs(4, seed=31, shape=(3, 900, 260))
+    c = workloads.make_inputs(5, seed=31, shape=(2, 1300, 130))
+    gx = np.random.default_rng(31).standard_normal(r["a"].shape).astype(np.float32)
+
+    def run():
+        y = gpu_wkv(L, d)
+        xr = L.scan_real(dev(r["a"]), dev(r["b"]))
+        ga, gb, _ = L.scan_real_backward(dev(r["a"]), xr, dev(gx))
+        xc = host(L.scan_complex(dev(c["lam"]), dev(c["u"])))
+        return [y, host(xr), host(ga), host(gb), xc]
+
+    base = run()
+    monkeypatch.setenv("LINREC_FLAT_GRID", "1")
+    flat = run()
+    for a, f in zip(base, flat):
+        assert a.tobytes() == f.tobytes()
+    assert rel_err(flat[0], oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])) <= TOL
+    assert rel_err(flat[1], oracle.scan_real(r["a"], r["b"])) <= TOL
+    assert rel_err(flat[4], oracle.scan_complex(c["lam"], c["u"])) <= TOL
