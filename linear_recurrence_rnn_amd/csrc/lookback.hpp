@@ -223,6 +223,51 @@ __device__ __forceinline__ void look_back(const Chain<Agg>& ch, int64_t q, int l
     }
 }
 
+// Look-back over a short chain (q <= KB: all predecessors in one batch), in which every slab
+// publishes its aggregate alone and a slab's carry is the entry state folded with the
+// aggregates of all its predecessors, in chain order (the same association whatever the
+// timing).  The slab's own record stores (when it has a successor) and its predecessors'
+// record loads are in flight together, so a slab whose predecessors had published when
+// their flags were prefetched (`first`, see prefetch_window) pays one memory round trip
+// where publishing an inclusive prefix after the carry costs two.  When some predecessor
+// has not published yet, the slab raises its own flag first, then polls.
+template <int VEC, int KB, class Agg, class Fold, class Recompute>
+__device__ __forceinline__ void look_back_short(const Chain<Agg>& ch, int64_t q, int lane, const Agg (&mine)[VEC],
+                                                bool publish_mine, Agg (&carry)[VEC], Fold&& fold,
+                                                Recompute&& recompute, uint64_t first) {
+    static_assert(KB < 64, "one window of flags");
+    auto raise = [&]() {
+        wait_memory();  // the records have been performed before the flag is stored
+        if (lane == 0)
+            __hip_atomic_store(ch.flags + q, ch.tag * 4 + kStateAgg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if (publish_mine) store_record<VEC>(ch.agg, q, lane, mine);
+    const int64_t j = q - 1 - lane;  // lane i watches slab q-1-i
+    const uint64_t need = (1ull << q) - 1;
+    uint64_t f = (j >= 0) ? first : 0;
+    uint64_t pub = __ballot(j >= 0 && (f >> 2) == ch.tag);
+    bool raised = false;
+    if ((pub & need) != need) {
+        if (publish_mine) raise();
+        raised = true;
+        if (j >= 0 && (f >> 2) != ch.tag) f = poll_flag(ch.flags + j, ch.tag, ch.spin);
+        pub = __ballot(j >= 0 && (f >> 2) == ch.tag);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // record loads stay after the polls
+    Agg xb[KB][VEC];
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+        if (k < q && ((pub >> (q - 1 - k)) & 1)) load_record<VEC>(ch.agg, k, lane, xb[k]);
+    if (publish_mine && !raised) raise();
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        if (k < q) {
+            if (!((pub >> (q - 1 - k)) & 1)) recompute((int64_t)k, xb[k]);  // not published in time
+            fold(carry, xb[k], (int64_t)k);
+        }
+    }
+}
+
 // A non-blocking attempt at look_back's result, for a coordinator that would otherwise sit
 // idle while its workgroup's other waves work: polls the flags of the 64 nearest
 // predecessors until they hold a published inclusive prefix with every aggregate after it

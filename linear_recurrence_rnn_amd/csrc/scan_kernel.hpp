@@ -149,6 +149,11 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
                          reinterpret_cast<uint32_t*>(g.rec_agg) + gi * g.nslab * (CW * kRecDwords<Agg>),
                          reinterpret_cast<uint32_t*>(g.rec_incl) + gi * g.nslab * (CW * kRecDwords<Agg>), g.tag, g.spin};
     const bool has_succ = s + 1 < g.nslab;
+    // Records in flight per lane in a look-back: fewer for the wide (float64) aggregates.
+    constexpr int KB = (VEC >= 4 || kRecDwords<Agg> > 4) ? 2 : (VEC == 2 ? 4 : 8);
+    // A chain whose predecessors all fit one batch of records publishes aggregates only
+    // (look_back_short); coordination in wave 0 only.
+    const bool short_chain = !SEP && g.nslab - 1 <= KB;
 
     // Coordination, by one whole wave after B1: the slab aggregate (published), the carry
     // into the slab (look-back; into sh_carry), sh[x] = the chunks before x combined (x >= 1).
@@ -176,7 +181,10 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
         // its inclusive prefix alone: no aggregate, so one store round trip fewer.  The same
         // records in the same association as look_back, so the same bits.  Coordination in
         // wave 0 only: with a coordinator wave of its own (long chains) it measured slower.
-        if (!SEP && try_look_back<VEC>(chn, s, lane, carry, fold, [] { return true; }, &first)) {
+        // A short chain publishes aggregates only and folds all of them (look_back_short).
+        if (short_chain) {
+            early_carry = true;  // carry formed below
+        } else if (!SEP && try_look_back<VEC>(chn, s, lane, carry, fold, [] { return true; }, &first)) {
             early_carry = true;
         } else if (has_succ) {
             publish<VEC>(chn, s, lane, mine, false);
@@ -200,9 +208,8 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) x[e] = as_record(x[e]);  // as if read
         };
-        // Records in flight per lane: fewer for the wide (float64) aggregates.
-        constexpr int KB = (VEC >= 4 || kRecDwords<Agg> > 4) ? 2 : (VEC == 2 ? 4 : 8);
-        if (!early_carry) look_back<VEC, KB>(chn, s, lane, carry, fold, recompute, first);
+        if (short_chain) look_back_short<VEC, KB>(chn, s, lane, mine, has_succ, carry, fold, recompute, first);
+        else if (!early_carry) look_back<VEC, KB>(chn, s, lane, carry, fold, recompute, first);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             sh_carry[lane * VEC + e] = carry[e];
@@ -212,7 +219,12 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     // Hands the inclusive prefix on: published for the next slab, or, in the last slab, the
     // state after the whole sequence for operators that return it.
     auto hand_on = [&](const Agg (&incl)[VEC]) {
-        if (has_succ) {
+        if (short_chain) {
+            if (!has_succ && active) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) Op::finish(A, g, b, c0 + e, incl[e]);
+            }
+        } else if (has_succ) {
             publish<VEC>(chn, s, lane, incl, true);
         } else if (active) {
 #pragma unroll

@@ -254,6 +254,11 @@ def test_lookback_recompute_path(L, monkeypatch, spin):
     xc0 = (np.ones((1, 128)) + 0.5j).astype(np.complex64)
     assert rel_err(host(L.scan_complex(dev(c["lam"]), dev(c["u"]), dev(xc0))),
                    oracle.scan_complex(c["lam"], c["u"], xc0)) <= TOL
+    # Short chains (at most 9 slabs of 128 steps: aggregates only) take the same fallback.
+    d = workloads.make_inputs(3, seed=13, shape=(2, 1100, 320))
+    assert rel_err(gpu_wkv(L, d), oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])) <= TOL
+    r = workloads.make_inputs(4, seed=13, shape=(2, 1000, 256))
+    assert rel_err(host(L.scan_real(dev(r["a"]), dev(r["b"]), dev(x0))), oracle.scan_real(r["a"], r["b"], x0)) <= TOL
 
 
 @pytest.mark.parametrize("wid", [2, 3])
