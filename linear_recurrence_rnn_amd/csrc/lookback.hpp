@@ -248,6 +248,9 @@ __device__ __forceinline__ void look_back_short(const Chain<Agg>& ch, int64_t q,
     uint64_t pub = __ballot(j >= 0 && (f >> 2) == ch.tag);
     bool raised = false;
     if ((pub & need) != need) {
+        // The missing flags are read again while this slab's records are being stored (one
+        // round trip for both), then polled if still missing.
+        if (j >= 0 && (f >> 2) != ch.tag) f = __hip_atomic_load(ch.flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (publish_mine) raise();
         raised = true;
         if (j >= 0 && (f >> 2) != ch.tag) f = poll_flag(ch.flags + j, ch.tag, ch.spin);
