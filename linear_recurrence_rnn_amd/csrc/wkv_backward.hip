@@ -33,6 +33,7 @@
 // Every sum over slabs is a fold in chain order (look-back), and dL/dw, dL/du are summed over
 // the batch in ascending row order: the results do not depend on scheduling.
 #include <atomic>
+#include <cstdlib>
 
 #include "chunk_scan.hpp"
 #include "device_common.hpp"
@@ -617,11 +618,23 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int64_t G = g.B * g.ngrp;
-    const int64_t q = (int64_t)blockIdx.x / G;  // chain position: later slabs first
-    const int64_t gi = (int64_t)blockIdx.x - q * G;
+    // Chain position q (later slabs first), batch row b and channel group grp: from a 3-D
+    // grid (ngrp, B, nslab) directly, or by dividing the flat grid's block index (sizes
+    // beyond the 3-D grid's limits), a long scalar sequence ahead of the first load.
+    int64_t q, b, grp;
+    if (g.grid3) {
+        q = blockIdx.z;
+        b = blockIdx.y;
+        grp = blockIdx.x;
+    } else {
+        const int64_t G = g.B * g.ngrp;
+        q = (int64_t)blockIdx.x / G;
+        const int64_t gq = (int64_t)blockIdx.x - q * G;
+        b = gq / g.ngrp;
+        grp = gq - b * g.ngrp;
+    }
+    const int64_t gi = b * g.ngrp + grp;
     const int64_t s = g.nslab - 1 - q;
-    const int64_t b = gi / g.ngrp, grp = gi - b * g.ngrp;
     const int64_t c0 = grp * CW + (int64_t)lane * VEC;
     const bool active = c0 < g.C;
     const int64_t t_slab = s * SLAB;
@@ -1028,15 +1041,21 @@ hipError_t launch(const WkvBwdArgs& A, const BwdGeom& g, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     const bool state = A.s_in || A.gs_out || A.gs_in;
-    const dim3 grid((unsigned)(G * g.nslab)), block(64 * (NW + 1));
+    // The 3-D grid numbers blocks x fastest, then y, then z: the flat grid's order.
+    const char* flat = std::getenv("LINREC_FLAT_GRID");  // 1: the flat grid at any size (tests)
+    BwdGeom g3 = g;
+    g3.grid3 = g.B <= 65535 && g.nslab <= 65535 && !(flat && flat[0] == '1');
+    const dim3 grid = g3.grid3 ? dim3((unsigned)g.ngrp, (unsigned)g.B, (unsigned)g.nslab)
+                               : dim3((unsigned)(G * g.nslab)),
+               block(64 * (NW + 1));
     if (A.r && state) {
-        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true, true>), grid, block, 0, st, A, g);
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true, true>), grid, block, 0, st, A, g3);
     } else if (A.r) {
-        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true, false>), grid, block, 0, st, A, g);
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true, false>), grid, block, 0, st, A, g3);
     } else if (state) {
-        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false, true>), grid, block, 0, st, A, g);
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false, true>), grid, block, 0, st, A, g3);
     } else {
-        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false, false>), grid, block, 0, st, A, g);
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false, false>), grid, block, 0, st, A, g3);
     }
     return hipGetLastError();
 }

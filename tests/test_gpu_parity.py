@@ -385,11 +385,11 @@ def test_scan_special_cases(L):
 
 
 def test_flat_grid_matches_3d_grid(L, monkeypatch):
-    # The scan kernels run on a 3-D grid (channel groups, batch rows, slabs) whenever the
-    # rows and slabs fit its y and z extents, and on a flat grid, whose block index is
-    # divided into the same three, otherwise.  Both number the blocks alike, so the results
-    # must agree bit for bit (forward WKV, real and complex scans, a reverse-time adjoint),
-    # and with the oracle.
+    # The scan kernels and the WKV gradient kernel run on a 3-D grid (channel groups, batch
+    # rows, slabs) whenever the rows and slabs fit its y and z extents, and on a flat grid,
+    # whose block index is divided into the same three, otherwise.  Both number the blocks
+    # alike, so the results must agree bit for bit (forward WKV, real and complex scans, a
+    # reverse-time adjoint, the WKV backward), and with the oracle.
     announce("flat grid (LINREC_FLAT_GRID=1) vs 3-D grid")
     d = workloads.make_inputs(3, seed=31, shape=(3, 1100, 200))
     r = workloads.make_inputs(4, seed=31, shape=(3, 900, 260))
@@ -401,7 +401,7 @@ def test_flat_grid_matches_3d_grid(L, monkeypatch):
         xr = L.scan_real(dev(r["a"]), dev(r["b"]))
         ga, gb, _ = L.scan_real_backward(dev(r["a"]), xr, dev(gx))
         xc = host(L.scan_complex(dev(c["lam"]), dev(c["u"])))
-        return [y, host(xr), host(ga), host(gb), xc]
+        return [y, host(xr), host(ga), host(gb), xc] + gpu_wkv_bwd(L, d)
 
     base = run()
     monkeypatch.setenv("LINREC_FLAT_GRID", "1")
