@@ -248,9 +248,12 @@ hipError_t run_token_shift(const TokenShiftArgs& A, int64_t B, int64_t T, int64_
     return hipGetLastError();
 }
 
-// Backward spans: 16 steps for one channel per lane, 8 for two (the gradient rows of every
-// mix stay in registers).
-constexpr int shift_bwd_ts(int vec) { return vec == 2 ? 8 : kShiftTS; }
+// Backward spans: 16 steps for one channel per lane, 4 for two (the gradient rows of every
+// mix stay in registers).  With two channels per lane, 4-step spans hold 66 VGPRs, so three
+// 8-wave blocks share a CU (B8 T1024 C768, 3 mixes: 30.9 -> 30.3 us with the dL/dmu sum);
+// 8-step spans held 106 (two blocks per CU), 6-step spans ran 34.9 us (ragged blocks), and
+// capping 8-step spans at 80 VGPRs spilled (56.2 us).
+constexpr int shift_bwd_ts(int vec) { return vec == 2 ? 4 : kShiftTS; }
 
 size_t token_shift_backward_ws_bytes(int64_t B, int64_t T, int64_t C, int M, int vec) {
     const int ts = shift_bwd_ts(vec);
