@@ -143,7 +143,6 @@ struct ScanGeom {
     double* part;       // (B*ngrp*nslab, 64*vec, 2) per-slab sums of operators that have them
     double* part2;      // (B*nk, C, 2) their first-stage sums (see run_scan_complex_backward)
     int64_t nk;         // ceil(nslab / kPartBlock): first-stage blocks per row
-    int grid3;          // set by the launch: the grid is (ngrp, B, nslab) instead of (B*ngrp*nslab)
 };
 
 struct ScanPlan {

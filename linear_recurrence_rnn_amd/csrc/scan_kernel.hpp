@@ -57,6 +57,15 @@ struct uniform_steps : std::false_type {};
 template <class Op>
 struct uniform_steps<Op, std::void_t<decltype(Op::kUniformSteps)>> : std::bool_constant<Op::kUniformSteps> {};
 constexpr unsigned kOutOfRange = 0x80000000u;
+
+// Operators that declare kChanLate form their channel constants after the chunk's loads are
+// issued (their constants are loads whose wait would hold the chunk's loads back); the
+// others form them first (the complex scans' lambda^L, a float64 power, would otherwise wait
+// for the whole chunk).
+template <class Op, class = void>
+struct chan_late : std::false_type {};
+template <class Op>
+struct chan_late<Op, std::void_t<decltype(Op::kChanLate)>> : std::bool_constant<Op::kChanLate> {};
 constexpr int64_t kGridYZMax = 65535;  // grid extent in y and z
 
 template <class Op, int VEC, int L>
@@ -84,7 +93,8 @@ __device__ __forceinline__ void run_rows(int64_t T, int64_t tl, int n, unsigned 
 // publishes the inclusive prefix while the chunks re-run.  The first packs more chunks onto
 // a CU (it holds about 24 such waves); the second keeps the publication off the chunks'
 // path, which pays for long look-back chains of register-heavy operators.
-template <class Op, int VEC, int NW, int L, bool SEP>
+// G3 selects the grid: (ngrp, B, nslab), or a flat one (sizes beyond the 3-D grid's limits).
+template <class Op, int VEC, int NW, int L, bool SEP, bool G3>
 __global__ __launch_bounds__(64 * (NW + SEP)) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<Op, VEC, L>())))
 void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     using Agg = typename Op::Agg;
@@ -107,10 +117,10 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     const int lane = tid & 63;
     // Slab s (in the recurrence's order: predecessors are dispatched first), batch row b and
     // channel group grp.  A 3-D grid (ngrp, B, nslab) hands them over directly; the flat grid
-    // (sizes beyond the 3-D grid's limits) divides the block index, a long scalar sequence
-    // that every wave ran before its first load.
+    // divides the block index, a long scalar sequence that every wave ran before its first
+    // load (and whose registers, compiled beside the 3-D path, made the kernels spill SGPRs).
     int64_t s, b, grp;
-    if (g.grid3) {
+    if constexpr (G3) {
         s = blockIdx.z;
         b = blockIdx.y;
         grp = blockIdx.x;
@@ -129,9 +139,10 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     auto chunk_len = [&](int x) { return max(0, min(L, slab_n - x * L)); };
 
     // The channels' constants (for WKV w and u; for the complex scans lambda and lambda^L).
-    // They are formed after the chunk's loads are issued: formed first, their wait held the
-    // chunk's loads back by one memory round trip.  A lane past the last channel reads the
-    // first channels' (no branch around the loads) and keeps the empty constants.
+    // WKV forms them after the chunk's loads are issued: formed first, their wait held the
+    // chunk's loads back by one memory round trip (chan_late).  A lane past the last channel
+    // reads the first channels' (no branch around the loads) and keeps the empty constants.
+    constexpr bool LATE = chan_late<Op>::value;
     Chan ch[VEC];
     auto form_chan = [&]() {
 #pragma unroll
@@ -140,6 +151,10 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
             ch[e] = active ? x : Chan{};
         }
     };
+    if constexpr (!LATE) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ch[e] = active ? Op::template chan<L>(A, c0 + e) : Chan{};
+    }
 
     const unsigned rowb = (unsigned)(g.C * EF * 4);           // bytes per time step
     constexpr bool UN = uniform_steps<Op>::value;
@@ -248,7 +263,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
     if constexpr (SEP) {
         if (w == NW) {
             // ---- the coordinator wave ----
-            form_chan();
+            if constexpr (LATE) form_chan();
             __syncthreads();  // B1: chunk aggregates are in sh
             Agg incl[VEC];
             coordinate(prefetch_window(chn, s, lane), incl);
@@ -280,7 +295,7 @@ void lookback_scan_kernel(typename Op::Args A, ScanGeom g) {
             else Op::template zero<VEC>(in[j]);
         }
     }
-    form_chan();
+    if constexpr (LATE) form_chan();
     Local loc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) sh[w][lane * VEC + e] = Op::template reduce<L, VEC>(ch[e], in, e, n, loc[e]);
@@ -336,16 +351,23 @@ hipError_t launch(const typename Op::Args& A, const ScanGeom& g, bool sep, hipSt
     // flat one.  Its y and z extents are kept within 65535.
     // LINREC_FLAT_GRID=1 takes the flat grid at any size (tests).
     const char* flat = std::getenv("LINREC_FLAT_GRID");
-    ScanGeom g3 = g;
-    g3.grid3 = g.B <= kGridYZMax && g.nslab <= kGridYZMax && !(flat && flat[0] == '1');
-    const dim3 grid = g3.grid3 ? dim3((unsigned)g.ngrp, (unsigned)g.B, (unsigned)g.nslab) : dim3((unsigned)nb);
+    const bool g3 = g.B <= kGridYZMax && g.nslab <= kGridYZMax && !(flat && flat[0] == '1');
+    const dim3 grid3((unsigned)g.ngrp, (unsigned)g.B, (unsigned)g.nslab), grid1((unsigned)nb);
     if constexpr (VEC == 1) {
         if (sep) {
-            hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, true>), grid, dim3(64 * (NW + 1)), 0, st, A, g3);
+            if (g3)
+                hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, true, true>), grid3, dim3(64 * (NW + 1)), 0,
+                                   st, A, g);
+            else
+                hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, true, false>), grid1, dim3(64 * (NW + 1)), 0,
+                                   st, A, g);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, false>), grid, dim3(64 * NW), 0, st, A, g3);
+    if (g3)
+        hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, false, true>), grid3, dim3(64 * NW), 0, st, A, g);
+    else
+        hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, false, false>), grid1, dim3(64 * NW), 0, st, A, g);
     return hipGetLastError();
 }
 

@@ -59,6 +59,7 @@ struct WkvOpT {
     // over the same step count and drop an inactive lane's accesses by an out-of-range offset
     // (see scan_kernel.hpp).
     static constexpr bool kUniformSteps = true;
+    static constexpr bool kChanLate = true;  // w, u are read after the chunk's loads are issued
     using Part = NoPart;
     struct Chan { float om, mu, lift, fast_lo; };  // lift = ceil(max(om, mu, 0))
     // kk becomes g_j after phase 1.  The gated instance also loads r with the chunk, so that

@@ -600,7 +600,8 @@ constexpr int grad_waves_per_eu() {
 // dL/dr = dL/dwkv wkv sigma(-r) is written where wkv is formed.  STATE: a carried state
 // s_in starts the forward sums, the final state's gradient gs_out starts the reverse ones and
 // gs_in is written.  Separate instances, so the plain kernel's registers are unchanged.
-template <int VEC, int NW, int L, bool GATE, bool STATE>
+// G3: the grid is (ngrp, B, nslab); otherwise flat (sizes beyond the 3-D grid's limits).
+template <int VEC, int NW, int L, bool GATE, bool STATE, bool G3>
 __global__ __launch_bounds__(64 * (NW + 1))
 __attribute__((amdgpu_waves_per_eu(grad_waves_per_eu<L, GATE, STATE>())))
 void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
@@ -619,10 +620,10 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     // Chain position q (later slabs first), batch row b and channel group grp: from a 3-D
-    // grid (ngrp, B, nslab) directly, or by dividing the flat grid's block index (sizes
-    // beyond the 3-D grid's limits), a long scalar sequence ahead of the first load.
+    // grid (ngrp, B, nslab) directly, or by dividing the flat grid's block index, a long
+    // scalar sequence ahead of the first load.
     int64_t q, b, grp;
-    if (g.grid3) {
+    if constexpr (G3) {
         q = blockIdx.z;
         b = blockIdx.y;
         grp = blockIdx.x;
@@ -1018,6 +1019,21 @@ hipError_t resident_blocks(const void* kernel, int threads, std::atomic<int> (&c
     return hipSuccess;
 }
 
+template <int VEC, int NW, int L, bool G3>
+hipError_t launch_grad(const WkvBwdArgs& A, const BwdGeom& g, bool state, dim3 grid, hipStream_t st) {
+    const dim3 block(64 * (NW + 1));
+    if (A.r && state) {
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true, true, G3>), grid, block, 0, st, A, g);
+    } else if (A.r) {
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true, false, G3>), grid, block, 0, st, A, g);
+    } else if (state) {
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false, true, G3>), grid, block, 0, st, A, g);
+    } else {
+        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false, false, G3>), grid, block, 0, st, A, g);
+    }
+    return hipGetLastError();
+}
+
 template <int VEC, int NW, int L>
 hipError_t launch(const WkvBwdArgs& A, const BwdGeom& g, hipStream_t st) {
     const int64_t G = g.B * g.ngrp;
@@ -1043,21 +1059,9 @@ hipError_t launch(const WkvBwdArgs& A, const BwdGeom& g, hipStream_t st) {
     const bool state = A.s_in || A.gs_out || A.gs_in;
     // The 3-D grid numbers blocks x fastest, then y, then z: the flat grid's order.
     const char* flat = std::getenv("LINREC_FLAT_GRID");  // 1: the flat grid at any size (tests)
-    BwdGeom g3 = g;
-    g3.grid3 = g.B <= 65535 && g.nslab <= 65535 && !(flat && flat[0] == '1');
-    const dim3 grid = g3.grid3 ? dim3((unsigned)g.ngrp, (unsigned)g.B, (unsigned)g.nslab)
-                               : dim3((unsigned)(G * g.nslab)),
-               block(64 * (NW + 1));
-    if (A.r && state) {
-        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true, true>), grid, block, 0, st, A, g3);
-    } else if (A.r) {
-        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, true, false>), grid, block, 0, st, A, g3);
-    } else if (state) {
-        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false, true>), grid, block, 0, st, A, g3);
-    } else {
-        hipLaunchKernelGGL((wkv_bwd_grad_kernel<VEC, NW, L, false, false>), grid, block, 0, st, A, g3);
-    }
-    return hipGetLastError();
+    const bool g3 = g.B <= 65535 && g.nslab <= 65535 && !(flat && flat[0] == '1');
+    if (g3) return launch_grad<VEC, NW, L, true>(A, g, state, dim3((unsigned)g.ngrp, (unsigned)g.B, (unsigned)g.nslab), st);
+    return launch_grad<VEC, NW, L, false>(A, g, state, dim3((unsigned)(G * g.nslab)), st);
 }
 
 // Kernels that exist (one channel per lane): (nw, L) in {(3, 16), (4, 16), (7, 8), (8, 8), (7, 16)}.

@@ -45,7 +45,6 @@ struct BwdGeom {
     double* part;           // (B, C, 2) dL/dw, dL/du of each batch row
     int exact_only;         // 1: the gradient kernel never takes its frame fast path (tests)
     int from_ckpt;          // 1: incl_f holds a checkpointing forward's sums; no state kernel
-    int grid3;              // set by the launch: the gradient kernel's grid is (ngrp, B, nslab)
 };
 
 struct BwdPlan {

@@ -56,6 +56,7 @@ struct WkvCkptOpT {
     using Base = typename std::conditional<GATED || STATE, WkvExtOp, WkvOp>::type;
     static constexpr bool kReverse = false;
     static constexpr bool kParts = false;
+    static constexpr bool kChanLate = true;  // w, u are read after the chunk's loads are issued
     using Part = NoPart;
     using Chan = typename Base::Chan;
     using In = typename Base::In;
