@@ -348,19 +348,18 @@ hipError_t launch(const typename Op::Args& A, const ScanGeom& g, bool sep, hipSt
     const int64_t nb = g.B * g.ngrp * g.nslab;
     if (const hipError_t e = clear_flags_if_capturing(g.flags, nb, st)) return e;
     // The 3-D grid numbers blocks x fastest, then y, then z: the same slab-major order as the
-    // flat one.  Its y and z extents are kept within 65535.
+    // flat one.  Its y and z extents are kept within 65535.  Kernels with a coordinator wave of
+    // their own (the complex scans: long chains, many rounds of workgroups) keep the flat grid,
+    // which measured faster for them (B1 T262144 C1024 LRU scan 764 vs 776 us); for the others
+    // the 3-D grid saves the prologue's divisions.
     // LINREC_FLAT_GRID=1 takes the flat grid at any size (tests).
     const char* flat = std::getenv("LINREC_FLAT_GRID");
     const bool g3 = g.B <= kGridYZMax && g.nslab <= kGridYZMax && !(flat && flat[0] == '1');
     const dim3 grid3((unsigned)g.ngrp, (unsigned)g.B, (unsigned)g.nslab), grid1((unsigned)nb);
     if constexpr (VEC == 1) {
         if (sep) {
-            if (g3)
-                hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, true, true>), grid3, dim3(64 * (NW + 1)), 0,
-                                   st, A, g);
-            else
-                hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, true, false>), grid1, dim3(64 * (NW + 1)), 0,
-                                   st, A, g);
+            hipLaunchKernelGGL((lookback_scan_kernel<Op, VEC, NW, L, true, false>), grid1, dim3(64 * (NW + 1)), 0, st,
+                               A, g);
             return hipGetLastError();
         }
     }
