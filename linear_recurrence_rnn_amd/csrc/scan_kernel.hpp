@@ -15,14 +15,18 @@
 //             timing), and publishes the slab's own inclusive prefix;
 //   re-run    each wave combines the slab's carry with the chunks before its own (prepared
 //             by the coordinator) and re-runs its chunk straight from registers.
+// In a chain short enough that all predecessors' records fit one batch (at most 1 + KB slabs)
+// no inclusive prefix is published: every slab publishes its aggregate and folds all its
+// predecessors' aggregates (look_back_short), one memory round trip instead of two.
 // The waves meet at two barriers only.  Parking wave 0's chunk keeps the look-back's
 // registers from adding to the chunk's, and having no wave without a chunk lets 3
 // workgroups of 8 waves share a CU (the CU holds about 24 of these waves).  The combine of
 // two spans is associative, which is what lets a sequence be cut into chunks and slabs (the
 // two-halves split of the LRU write-up, parallelisation section).
 //
-// Progress: workgroups are numbered slab-major, so a slab's predecessors have smaller block
-// indices and are dispatched first.  A wait is bounded all the same: if a predecessor has
+// Progress: workgroups are numbered slab-major (a 3-D grid (groups, rows, slabs), or a flat
+// one of the same order), so a slab's predecessors have smaller block indices and are
+// dispatched first.  A wait is bounded all the same: if a predecessor has
 // not published after g.spin polls, the waiting wave recomputes that slab's aggregate from
 // its inputs.  No wait depends on dispatch order or on the workspace contents; flags carry
 // a per-call tag, so stale flags from earlier calls read as "not published".
