@@ -90,6 +90,15 @@ def test_wkv_forward_and_ckpt_step_bits_independent_of_timing(L):
     check_same(runs, "checkpointed step")
 
 
+def test_wkv_forward_short_chain_bits_independent_of_timing(L):
+    # The bench shape: chains of 8 slabs, which publish aggregates only and fold all of them.
+    B, T, C = 8, 1024, 768
+    announce("wkv4 forward (short chains), %d runs, B=%d T=%d C=%d" % (RUNS, B, T, C))
+    d = workloads.make_inputs(2, seed=73, shape=(B, T, C))
+    w, u, k, v = (dev(d[n]) for n in ("w", "u", "k", "v"))
+    check_same(repeat(lambda: [L.wkv4_forward(w, u, k, v)]), "wkv4_forward")
+
+
 def test_wkv_backward_bits_independent_of_timing(L):
     B, T, C = 4, 6000, 200  # 108 slabs of 56 steps; the state kernel's chain over them
     announce("wkv4_backward, %d runs, B=%d T=%d C=%d" % (RUNS, B, T, C))

@@ -66,9 +66,11 @@ def load(dst, arrays):
         t.copy_(torch.from_numpy(np.ascontiguousarray(a)))
 
 
-def test_forward_graph_replays(L):
+# 12 slabs per row (the look-back runs, with inclusive prefixes); 8 slabs per row at the
+# bench shape (a short chain: aggregates only)
+@pytest.mark.parametrize("B,T,C", [(2, 1500, 200), (8, 1024, 768)], ids=["long_chain", "short_chain"])
+def test_forward_graph_replays(L, B, T, C):
     import torch
-    B, T, C = 2, 1500, 200  # 12 slabs per row: the look-back runs
     announce("wkv4_forward captured and replayed B=%d T=%d C=%d" % (B, T, C))
     d0 = workloads.make_inputs(1, seed=201, shape=(B, T, C))
     w, u, k, v = (torch.from_numpy(d0[n]).cuda() for n in ("w", "u", "k", "v"))
