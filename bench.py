@@ -729,8 +729,10 @@ def measure(lib, wid, kind, steps, warmup, cpu_budget, shape=None, cpu_slice=Non
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="the headline's warm-up goes on (in batches of --warmup) for at least this long")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle CPU baseline (0 skips it)")
     ap.add_argument("--no-copy-probe", action="store_true")
@@ -764,7 +766,7 @@ def main():
                 sys.exit(2)
             print(json.dumps(measure(lib, int(wid), kind, args.steps, args.warmup, 0)), flush=True)
         return
-    res = measure(lib, 2, "wkv4_forward", args.steps, args.warmup, args.cpu_seconds)
+    res = measure(lib, 2, "wkv4_forward", args.steps, args.warmup, args.cpu_seconds, min_warm_s=args.warm_seconds)
     line = {
         "metric": METRIC,
         "value": res["elements_per_s"],
