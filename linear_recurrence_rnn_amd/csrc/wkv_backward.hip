@@ -976,16 +976,29 @@ void wkv_bwd_grad_kernel(WkvBwdArgs A, BwdGeom g) {
     }
 }
 
-// gw[c] = sum_b part[b, c].w, gu likewise, in ascending b.
+// gw[c] = sum_b part[b, c].w, gu likewise, in ascending b.  The rows are loaded 8 at a time
+// (one 16-byte load per row) and then added in order: one memory round trip per 8 rows
+// where a load feeding each add cost one per row (B = 8: 4.7 us).  The same association,
+// so the same bits.
 __global__ __launch_bounds__(256) void wkv_bwd_wu_kernel(const double* __restrict__ part, int64_t B,
                                                          int64_t C, float* __restrict__ gw,
                                                          float* __restrict__ gu) {
+    constexpr int K = 8;
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= C) return;
+    const double2* p2 = reinterpret_cast<const double2*>(part);
     double sw = 0.0, su = 0.0;
-    for (int64_t b = 0; b < B; ++b) {
-        sw += part[2 * (b * C + c)];
-        su += part[2 * (b * C + c) + 1];
+    for (int64_t b0 = 0; b0 < B; b0 += K) {
+        double2 x[K];
+#pragma unroll
+        for (int i = 0; i < K; ++i) x[i] = (b0 + i < B) ? p2[(b0 + i) * C + c] : double2{0.0, 0.0};
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            if (b0 + i < B) {
+                sw += x[i].x;
+                su += x[i].y;
+            }
+        }
     }
     gw[c] = (float)sw;
     gu[c] = (float)su;
