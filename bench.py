@@ -790,6 +790,9 @@ def main():
         line["cpu_baseline"] = res["cpu_baseline"]
     if not args.no_copy_probe:
         line["stream_ceiling"] = stream_ceiling(8, 1024, 768, res["rotations"], args.steps, args.warmup)
+        # the headline's HIP-event time per launch against the ceiling's, both timed the same way
+        line["stream_ceiling"]["headline_vs_ceiling"] = round(
+            line["stream_ceiling"]["us_per_launch"] / (res["event_ms_per_step"] * 1e3), 4)
         line["copy_probe_GBps"] = copy_probe()
     if not args.no_workloads:
         # The other workloads, measured in the same run with a few launches each: the WKV
