@@ -237,6 +237,13 @@ def test_forward_launch_shapes(L, monkeypatch, nw, lc, vec):
     assert rel_err(host(L.scan_real(dev(r["a"]), dev(r["b"]), dev(x0))), oracle.scan_real(r["a"], r["b"], x0)) <= TOL
     c = workloads.make_inputs(5, seed=11, shape=(2, 900, 130))
     assert rel_err(host(L.scan_complex(dev(c["lam"]), dev(c["u"]))), oracle.scan_complex(c["lam"], c["u"])) <= TOL
+    # Short sequences: chains of at most 1 + KB slabs (KB = 8, 4 or 2 records in flight for
+    # 1, 2 or 4 channels per lane) publish aggregates only.
+    d = workloads.make_inputs(3, seed=12, shape=(2, 300, 296))
+    assert rel_err(gpu_wkv(L, d), oracle.wkv4_forward(d["w"], d["u"], d["k"], d["v"])) <= TOL
+    r = workloads.make_inputs(4, seed=12, shape=(3, 250, 260))
+    x0 = np.random.default_rng(5).standard_normal((3, 260)).astype(np.float32)
+    assert rel_err(host(L.scan_real(dev(r["a"]), dev(r["b"]), dev(x0))), oracle.scan_real(r["a"], r["b"], x0)) <= TOL
 
 
 @pytest.mark.parametrize("spin", ["0", "1"])
